@@ -1,0 +1,168 @@
+"""ctypes binding of ``libgma.so`` (C ABI in ``include/gma.h``).
+
+Argument marshalling only: tensors are passed to the library as raw device pointers
+together with their sizes, and every step of the computation runs in the library's
+HIP kernels.  The functions carry the ABI's names.  If ``libgma.so`` has not been
+built, loading fails with an error; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgma.so")
+
+GMA_OK = 0
+STATUS_NAMES = ["GMA_OK", "GMA_ERR_NULL_POINTER", "GMA_ERR_BAD_SHAPE", "GMA_ERR_BAD_VALUE",
+                "GMA_ERR_UNSUPPORTED", "GMA_ERR_MISALIGNED", "GMA_ERR_WORKSPACE_TOO_SMALL",
+                "GMA_ERR_HIP"]
+GMA_F32, GMA_BF16 = 0, 1
+GMA_OP_RESPONSIBILITIES, GMA_OP_BIDIR, GMA_OP_CAUSAL = 0, 1, 2
+EXPORTED = ["gma_status_string", "gma_workspace_size", "gma_responsibilities", "gma_forward_bidir",
+            "gma_forward_causal"]
+
+
+class GmaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__("%s returned %s" % (where, name))
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("d_r", ctypes.c_int64), ("d_v", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libgma.so from the package directory (raises if it is not built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError("libgma.so not found at %s; build it with "
+                                   "`python -m gaussian_mixture_sequence_amd.build`" % LIB_PATH)
+            lib = ctypes.CDLL(LIB_PATH)
+            vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+            shp = ctypes.POINTER(Shape)
+            lib.gma_status_string.argtypes = [i32]
+            lib.gma_status_string.restype = ctypes.c_char_p
+            lib.gma_workspace_size.argtypes = [i32, shp, i32, i32, ctypes.POINTER(sz)]
+            lib.gma_workspace_size.restype = i32
+            lib.gma_responsibilities.argtypes = [vp, i32, vp, vp, vp, vp, i32, shp, vp, sz, vp]
+            lib.gma_responsibilities.restype = i32
+            lib.gma_forward_bidir.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, shp, vp, sz, vp]
+            lib.gma_forward_bidir.restype = i32
+            lib.gma_forward_causal.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, shp, i32, vp, sz, vp]
+            lib.gma_forward_causal.restype = i32
+            _lib = lib
+    return _lib
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return GMA_F32
+    if t == torch.bfloat16:
+        return GMA_BF16
+    raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(status: int, where: str) -> None:
+    if status != GMA_OK:
+        raise GmaError(status, where)
+
+
+def gma_status_string(status: int) -> str:
+    return load().gma_status_string(status).decode()
+
+
+def gma_workspace_size(op: int, B: int, H: int, N: int, d_r: int, d_v: int, K: int,
+                       io_dtype: int, chunk: int = 64) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().gma_workspace_size(op, ctypes.byref(Shape(B, H, N, d_r, d_v, K)), io_dtype, chunk,
+                                     ctypes.byref(out)), "gma_workspace_size")
+    return int(out.value)
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise GmaError(6, "workspace")
+    return workspace
+
+
+def gma_responsibilities(x: torch.Tensor, mu: torch.Tensor, sigma2: torch.Tensor, pi: torch.Tensor,
+                         gamma_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Gamma [B,H,N,K] of routing vectors x [B,H,N,d_r] (Eq. 3 / 3b)."""
+    B, H, N, dr = x.shape
+    K = mu.shape[1]
+    io = _dtype_code(x.dtype)
+    if out is None:
+        out = torch.empty(B, H, N, K, dtype=gamma_dtype, device=x.device)
+    ws = _workspace(gma_workspace_size(GMA_OP_RESPONSIBILITIES, B, H, N, dr, 1, K, io), x.device, workspace)
+    _check(load().gma_responsibilities(_ptr(x), io, _ptr(mu), _ptr(sigma2), _ptr(pi), _ptr(out),
+                                       _dtype_code(out.dtype), ctypes.byref(Shape(B, H, N, dr, 1, K)),
+                                       _ptr(ws), ws.numel(), _stream(stream)), "gma_responsibilities")
+    return out
+
+
+def gma_forward_bidir(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, mu: torch.Tensor,
+                      sigma2: torch.Tensor, pi: torch.Tensor, eps: float = 1e-6,
+                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Bidirectional GMA O [B,H,N,d_v] (Eq. 5-8)."""
+    B, H, N, dr = xq.shape
+    dv = v.shape[-1]
+    K = mu.shape[1]
+    io = _dtype_code(xq.dtype)
+    if out is None:
+        out = torch.empty(B, H, N, dv, dtype=xq.dtype, device=xq.device)
+    ws = _workspace(gma_workspace_size(GMA_OP_BIDIR, B, H, N, dr, dv, K, io), xq.device, workspace)
+    _check(load().gma_forward_bidir(_ptr(xq), _ptr(xk), _ptr(v), io, _ptr(mu), _ptr(sigma2), _ptr(pi),
+                                    float(eps), _ptr(out), ctypes.byref(Shape(B, H, N, dr, dv, K)),
+                                    _ptr(ws), ws.numel(), _stream(stream)), "gma_forward_bidir")
+    return out
+
+
+def gma_forward_causal(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, mu: torch.Tensor,
+                       sigma2: torch.Tensor, pi: torch.Tensor, eps: float = 1e-6, chunk: int = 64,
+                       out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Causal GMA O [B,H,N,d_v] (Eq. 6b/8b), chunked scan with `chunk` positions per chunk."""
+    B, H, N, dr = xq.shape
+    dv = v.shape[-1]
+    K = mu.shape[1]
+    io = _dtype_code(xq.dtype)
+    if out is None:
+        out = torch.empty(B, H, N, dv, dtype=xq.dtype, device=xq.device)
+    ws = _workspace(gma_workspace_size(GMA_OP_CAUSAL, B, H, N, dr, dv, K, io, chunk), xq.device, workspace)
+    _check(load().gma_forward_causal(_ptr(xq), _ptr(xk), _ptr(v), io, _ptr(mu), _ptr(sigma2), _ptr(pi),
+                                     float(eps), _ptr(out), ctypes.byref(Shape(B, H, N, dr, dv, K)),
+                                     int(chunk), _ptr(ws), ws.numel(), _stream(stream)),
+           "gma_forward_causal")
+    return out

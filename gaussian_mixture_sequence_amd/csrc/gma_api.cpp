@@ -1,0 +1,194 @@
+// C-ABI front end of libgma.so: argument validation, workspace planning and
+// dispatch to the fp32 (VALU) or bf16 (MFMA) kernel launchers.  Declarations and
+// the contract of every entry point are in include/gma.h.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "gma_internal.h"
+
+namespace gma {
+
+namespace {
+
+constexpr int64_t kTokenTile = 64;      // tokens per tile in every kernel family
+constexpr int64_t kBidirBlocks = 1024;  // target workgroups for the split-N write
+constexpr int64_t kCausalBlocks = 512;  // target workgroups for the segmented scan
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+gma_status_t check_dims(gma_op_t op, const gma_shape_t& s, gma_dtype_t io) {
+    if (s.B < 0 || s.H < 0 || s.N < 0) return GMA_ERR_BAD_SHAPE;
+    if (s.d_r < 1 || s.K < 1) return GMA_ERR_UNSUPPORTED;
+    if (op != GMA_OP_RESPONSIBILITIES && s.d_v < 1) return GMA_ERR_UNSUPPORTED;
+    if (s.K > 256) return GMA_ERR_UNSUPPORTED;
+    if (io == GMA_F32) {
+        if (s.d_r > 128) return GMA_ERR_UNSUPPORTED;
+        if (op != GMA_OP_RESPONSIBILITIES && s.d_v > 128) return GMA_ERR_UNSUPPORTED;
+    } else {
+        if (s.d_r != 16 && s.d_r != 32 && s.d_r != 64 && s.d_r != 128) return GMA_ERR_UNSUPPORTED;
+        if (op != GMA_OP_RESPONSIBILITIES && s.d_v != 32 && s.d_v != 64 && s.d_v != 128)
+            return GMA_ERR_UNSUPPORTED;
+    }
+    // guard the int64 products used for sizes
+    const int64_t lim = int64_t(1) << 40;
+    if (s.B > lim || s.H > lim || s.N > lim || (s.B * s.H) > lim || (s.B * s.H) * s.N > lim)
+        return GMA_ERR_BAD_SHAPE;
+    return GMA_OK;
+}
+
+}  // namespace
+
+gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_t chunk, Plan* pl) {
+    if (op != GMA_OP_RESPONSIBILITIES && op != GMA_OP_BIDIR && op != GMA_OP_CAUSAL)
+        return GMA_ERR_BAD_VALUE;
+    if (io != GMA_F32 && io != GMA_BF16) return GMA_ERR_BAD_VALUE;
+    gma_status_t st = check_dims(op, s, io);
+    if (st != GMA_OK) return st;
+    if (op == GMA_OP_CAUSAL && chunk != 16 && chunk != 32 && chunk != 64) return GMA_ERR_UNSUPPORTED;
+
+    Plan p{};
+    p.op = op;
+    p.io = io;
+    p.B = s.B; p.H = s.H; p.N = s.N; p.dr = s.d_r; p.dv = (op == GMA_OP_RESPONSIBILITIES) ? 0 : s.d_v;
+    p.K = s.K;
+    p.P = s.B * s.H;
+    p.Kp = (io == GMA_BF16) ? round_up(size_t(s.K), 32) : s.K;
+    p.chunk = (op == GMA_OP_CAUSAL) ? chunk : 0;
+
+    // parameter tables: fp32 path keeps 1/sigma2 and the score constant in fp64; the bf16 path
+    // keeps four bf16 operand planes (a hi/lo, b hi/lo) and the constant.
+    if (io == GMA_F32)
+        p.params_bytes = round_up(size_t(p.H * p.K) * 8, 256) + round_up(size_t(p.H * p.K * p.dr) * 8, 256);
+    else
+        p.params_bytes = round_up(size_t(p.H * p.Kp) * 4, 256) +
+                         round_up(size_t(p.H * p.Kp * 4 * p.dr) * 2, 256);
+
+    p.G = 1;
+    p.seg = round_up(size_t(std::max<int64_t>(p.N, 1)), kTokenTile);
+    if (op == GMA_OP_BIDIR && p.P > 0 && p.N > 0) {
+        int64_t g = std::min(cdiv(kBidirBlocks, p.P), cdiv(p.N, 256));
+        g = std::max<int64_t>(g, 1);
+        p.seg = round_up(size_t(cdiv(p.N, g)), kTokenTile);
+        p.G = cdiv(p.N, p.seg);
+    } else if (op == GMA_OP_CAUSAL && p.P > 0 && p.N > 0) {
+        int64_t g = std::min(cdiv(kCausalBlocks, p.P), cdiv(p.N, 512));
+        g = std::max<int64_t>(g, 1);
+        p.seg = round_up(size_t(cdiv(p.N, g)), kTokenTile);
+        p.G = cdiv(p.N, p.seg);
+    }
+    const size_t mem_elems = size_t(p.Kp) * size_t(p.dv + 1);
+    p.partials_bytes = (op == GMA_OP_RESPONSIBILITIES) ? 0 : round_up(size_t(p.P * p.G) * mem_elems * 4, 256);
+    p.memory_bytes = (op == GMA_OP_BIDIR) ? round_up(size_t(p.P) * mem_elems * 4, 256) : 0;
+    p.off_params = 0;
+    p.off_partials = p.off_params + p.params_bytes;
+    p.off_memory = p.off_partials + p.partials_bytes;
+    p.total = p.off_memory + p.memory_bytes;
+    *pl = p;
+    return GMA_OK;
+}
+
+}  // namespace gma
+
+using gma::Plan;
+
+extern "C" {
+
+const char* gma_status_string(gma_status_t s) {
+    switch (s) {
+        case GMA_OK: return "GMA_OK";
+        case GMA_ERR_NULL_POINTER: return "GMA_ERR_NULL_POINTER";
+        case GMA_ERR_BAD_SHAPE: return "GMA_ERR_BAD_SHAPE";
+        case GMA_ERR_BAD_VALUE: return "GMA_ERR_BAD_VALUE";
+        case GMA_ERR_UNSUPPORTED: return "GMA_ERR_UNSUPPORTED";
+        case GMA_ERR_MISALIGNED: return "GMA_ERR_MISALIGNED";
+        case GMA_ERR_WORKSPACE_TOO_SMALL: return "GMA_ERR_WORKSPACE_TOO_SMALL";
+        case GMA_ERR_HIP: return "GMA_ERR_HIP";
+    }
+    return "GMA_ERR_UNKNOWN";
+}
+
+gma_status_t gma_workspace_size(gma_op_t op, const gma_shape_t* shape, gma_dtype_t io_dtype,
+                                int32_t chunk, size_t* bytes_out) {
+    if (!shape || !bytes_out) return GMA_ERR_NULL_POINTER;
+    Plan p;
+    gma_status_t st = gma::make_plan(op, *shape, io_dtype, chunk, &p);
+    if (st != GMA_OK) return st;
+    *bytes_out = p.total;
+    return GMA_OK;
+}
+
+static gma_status_t check_ws(const Plan& p, const void* ws, size_t ws_bytes) {
+    if (p.total > 0 && !ws) return GMA_ERR_NULL_POINTER;
+    if (ws_bytes < p.total) return GMA_ERR_WORKSPACE_TOO_SMALL;
+    if (ws && !gma::aligned16(ws)) return GMA_ERR_MISALIGNED;
+    return GMA_OK;
+}
+
+static gma_status_t launch_status(hipError_t e) { return e == hipSuccess ? GMA_OK : GMA_ERR_HIP; }
+
+gma_status_t gma_responsibilities(const void* X, gma_dtype_t x_dtype, const float* mu,
+                                  const float* sigma2, const float* pi, void* Gamma,
+                                  gma_dtype_t gamma_dtype, const gma_shape_t* shape,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!X || !mu || !sigma2 || !pi || !Gamma || !shape) return GMA_ERR_NULL_POINTER;
+    if (gamma_dtype != GMA_F32 && gamma_dtype != GMA_BF16) return GMA_ERR_BAD_VALUE;
+    Plan p;
+    gma_status_t st = gma::make_plan(GMA_OP_RESPONSIBILITIES, *shape, x_dtype, 0, &p);
+    if (st != GMA_OK) return st;
+    for (const void* q : {X, (const void*)mu, (const void*)sigma2, (const void*)pi, (const void*)Gamma})
+        if (!gma::aligned16(q)) return GMA_ERR_MISALIGNED;
+    if ((st = check_ws(p, workspace, workspace_bytes)) != GMA_OK) return st;
+    if (p.P == 0 || p.N == 0) return GMA_OK;
+    char* ws = static_cast<char*>(workspace);
+    if (x_dtype == GMA_F32)
+        return launch_status(gma::f32_responsibilities(p, static_cast<const float*>(X), mu, sigma2, pi,
+                                                       Gamma, gamma_dtype, ws, stream));
+    return launch_status(gma::bf16_responsibilities(p, X, mu, sigma2, pi, Gamma, gamma_dtype, ws, stream));
+}
+
+static gma_status_t forward_common(gma_op_t op, const void* XQ, const void* XK, const void* V,
+                                   gma_dtype_t io, const float* mu, const float* sigma2,
+                                   const float* pi, float eps, void* O, const gma_shape_t* shape,
+                                   int32_t chunk, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+    if (!XQ || !XK || !V || !mu || !sigma2 || !pi || !O || !shape) return GMA_ERR_NULL_POINTER;
+    Plan p;
+    gma_status_t st = gma::make_plan(op, *shape, io, chunk, &p);
+    if (st != GMA_OK) return st;
+    if (!(eps > 0.0f) || !std::isfinite(eps)) return GMA_ERR_BAD_VALUE;
+    for (const void* q : {XQ, XK, V, (const void*)mu, (const void*)sigma2, (const void*)pi, (const void*)O})
+        if (!gma::aligned16(q)) return GMA_ERR_MISALIGNED;
+    if ((st = check_ws(p, workspace, workspace_bytes)) != GMA_OK) return st;
+    if (p.P == 0 || p.N == 0) return GMA_OK;
+    char* ws = static_cast<char*>(workspace);
+    if (io == GMA_F32) {
+        const float *q = static_cast<const float*>(XQ), *k = static_cast<const float*>(XK),
+                    *v = static_cast<const float*>(V);
+        float* o = static_cast<float*>(O);
+        if (op == GMA_OP_BIDIR) return launch_status(gma::f32_bidir(p, q, k, v, mu, sigma2, pi, eps, o, ws, stream));
+        return launch_status(gma::f32_causal(p, q, k, v, mu, sigma2, pi, eps, o, ws, stream));
+    }
+    if (op == GMA_OP_BIDIR) return launch_status(gma::bf16_bidir(p, XQ, XK, V, mu, sigma2, pi, eps, O, ws, stream));
+    return launch_status(gma::bf16_causal(p, XQ, XK, V, mu, sigma2, pi, eps, O, ws, stream));
+}
+
+gma_status_t gma_forward_bidir(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                               const float* mu, const float* sigma2, const float* pi, float eps,
+                               void* O, const gma_shape_t* shape, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    return forward_common(GMA_OP_BIDIR, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, O, shape, 0,
+                          workspace, workspace_bytes, stream);
+}
+
+gma_status_t gma_forward_causal(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                                const float* mu, const float* sigma2, const float* pi, float eps,
+                                void* O, const gma_shape_t* shape, int32_t chunk, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    return forward_common(GMA_OP_CAUSAL, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, O, shape, chunk,
+                          workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

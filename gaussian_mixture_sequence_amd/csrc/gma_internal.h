@@ -1,0 +1,60 @@
+// Internal interface between the C-ABI front end (gma_api.cpp) and the kernel
+// launchers (gma_f32.hip, gma_bf16.hip).  Not installed; the public ABI is
+// include/gma.h.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <hip/hip_runtime.h>
+
+#include "gma.h"
+
+namespace gma {
+
+// Rounded-up size of one workspace region (256-byte granules keep every region
+// aligned for vector loads).
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Where each piece of scratch lives inside the caller's workspace, and how the
+// sequence is split.  Computed on the host from the shape alone (never from the
+// device), so workspace sizes and reduction orders are the same on every GPU.
+struct Plan {
+    gma_op_t op;
+    gma_dtype_t io;
+    int64_t B, H, N, dr, dv, K;
+    int64_t P;            // B * H independent (batch, head) problems
+    int64_t Kp;           // K padded to the MFMA component tile (bf16) or K (f32)
+    int64_t G;            // sequence splits per problem (write partials / causal segments)
+    int64_t seg;          // tokens per split (multiple of the token tile)
+    int32_t chunk;        // causal chunk length
+    // byte offsets into the workspace
+    size_t off_params, off_partials, off_memory, total;
+    size_t params_bytes, partials_bytes, memory_bytes;
+};
+
+// Fills `plan`; returns GMA_OK or the validation error for unsupported sizes.
+gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_t chunk, Plan* plan);
+
+// ---- fp32 path (gma_f32.hip) ---------------------------------------------------
+hipError_t f32_responsibilities(const Plan& p, const float* X, const float* mu, const float* s2,
+                                const float* pi, void* Gamma, gma_dtype_t gamma_dtype, char* ws,
+                                hipStream_t st);
+hipError_t f32_bidir(const Plan& p, const float* XQ, const float* XK, const float* V,
+                     const float* mu, const float* s2, const float* pi, float eps, float* O,
+                     char* ws, hipStream_t st);
+hipError_t f32_causal(const Plan& p, const float* XQ, const float* XK, const float* V,
+                      const float* mu, const float* s2, const float* pi, float eps, float* O,
+                      char* ws, hipStream_t st);
+
+// ---- bf16 MFMA path (gma_bf16.hip) ---------------------------------------------
+hipError_t bf16_responsibilities(const Plan& p, const void* X, const float* mu, const float* s2,
+                                 const float* pi, void* Gamma, gma_dtype_t gamma_dtype, char* ws,
+                                 hipStream_t st);
+hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void* V,
+                      const float* mu, const float* s2, const float* pi, float eps, void* O,
+                      char* ws, hipStream_t st);
+hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void* V,
+                       const float* mu, const float* s2, const float* pi, float eps, void* O,
+                       char* ws, hipStream_t st);
+
+}  // namespace gma

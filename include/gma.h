@@ -1,0 +1,146 @@
+/*
+ * gma.h -- C ABI of libgma.so, the MI355X (gfx950) forward pass of Gaussian
+ * Mixture Attention (GMA), after "Gaussian Mixture Attention: Linear-Time Sequence
+ * Mixing via Probabilistic Latent Routing" (Huang & Raza).
+ *
+ * Problem statement (Sec. 3.2-3.5 of that paper).  For every batch entry b and head h
+ * there are N routing vectors of dimension d_r for queries (X_Q) and keys (X_K), N
+ * value vectors of dimension d_v (V), and one diagonal Gaussian mixture with K
+ * components shared by queries and keys of that head (Fig. 1, "Shared GMM
+ * Parameters"): means mu, variances sigma2 (the diagonal of Sigma_k) and priors pi.
+ *   responsibilities   Gamma = softmax_k(s),  s_k = log pi_k + log N(x | mu_k, Sigma_k)
+ *                      (Sec. 3.2 Eq. 2-3, Sec. 4.1 Eq. 16 and Eq. 3b)
+ *   bidirectional      Vt = Gamma_K^T V,  Z = Gamma_K^T 1           (Sec. 3.3 Eq. 5-6)
+ *                      O  = Gamma_Q Vt / (Gamma_Q Z + eps)           (Eq. 7-8)
+ *   causal             Vt, Z replaced by prefix sums over j <= i     (Sec. 3.5 Eq. 6b, 8b)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout      All tensors are dense, contiguous and row-major:
+ *               X, X_Q, X_K [B, H, N, d_r]   V, O [B, H, N, d_v]   Gamma [B, H, N, K]
+ *               mu, sigma2  [H, K, d_r]      pi   [H, K]
+ *             Parameters are per head and broadcast over the batch.
+ * Dtypes      X_Q, X_K, V and O share one I/O dtype (GMA_F32 or GMA_BF16).  The
+ *             parameters mu, sigma2, pi are always fp32.  eps is fp32.
+ * Memory      Every pointer is a device pointer (HBM) owned by the caller.  The library
+ *             never allocates or frees device memory and keeps no state between calls;
+ *             scratch space is the caller's workspace (size from gma_workspace_size).
+ *             O and Gamma must not overlap any input or the workspace.
+ * Alignment   Tensor pointers and the workspace must be 16-byte aligned
+ *             (GMA_ERR_MISALIGNED otherwise).
+ * Streams     Work is enqueued on `stream` (NULL = the device's null stream) and the call
+ *             returns without waiting.  Calls on different streams may run concurrently
+ *             if they use different workspaces.
+ * Errors      Arguments are validated on the host before any HIP call; a non-OK status
+ *             means nothing was enqueued.  GMA_ERR_HIP reports a failed launch.  Faults
+ *             inside a kernel surface at the caller's next synchronisation.  Device-side
+ *             preconditions that are not checked: sigma2 > 0, pi > 0, finite inputs
+ *             (violations propagate NaN or infinities into the outputs).
+ * Sizes       B, H, N >= 0; a problem with B*H*N == 0 is valid and enqueues nothing.
+ *             d_r, d_v, K must lie in the supported set (GMA_ERR_UNSUPPORTED otherwise):
+ *               GMA_F32  : 1 <= d_r <= 128, 1 <= d_v <= 128, 1 <= K <= 256
+ *               GMA_BF16 : d_r in {16, 32, 64, 128}, d_v in {32, 64, 128}, 1 <= K <= 256
+ * Numerics    Scores and softmax in fp32, accumulations in fp32.  bf16 I/O uses bf16
+ *             MFMA with split (hi + lo) operands for the scores and for the latent
+ *             memory, and rounds O to bf16 (nearest-even).  Results are bitwise
+ *             reproducible for a fixed shape and chunk length (no atomics, fixed
+ *             reduction order).
+ */
+#ifndef GMA_H
+#define GMA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GMA_OK = 0,
+    GMA_ERR_NULL_POINTER = 1,        /* a required pointer is NULL                        */
+    GMA_ERR_BAD_SHAPE = 2,           /* negative size                                     */
+    GMA_ERR_BAD_VALUE = 3,           /* eps <= 0 or not finite; unknown dtype or op       */
+    GMA_ERR_UNSUPPORTED = 4,         /* d_r, d_v, K or chunk outside the supported set    */
+    GMA_ERR_MISALIGNED = 5,          /* pointer not 16-byte aligned                       */
+    GMA_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes < gma_workspace_size(...)         */
+    GMA_ERR_HIP = 7                  /* a HIP runtime call or kernel launch failed        */
+} gma_status_t;
+
+typedef enum { GMA_F32 = 0, GMA_BF16 = 1 } gma_dtype_t;
+
+typedef enum {
+    GMA_OP_RESPONSIBILITIES = 0,
+    GMA_OP_BIDIR = 1,
+    GMA_OP_CAUSAL = 2
+} gma_op_t;
+
+/* Problem sizes: batch B, heads H, sequence length N, routing dim d_r, value dim d_v,
+ * number of mixture components K (Sec. 3.2-3.3 notation). */
+typedef struct {
+    int64_t B, H, N, d_r, d_v, K;
+} gma_shape_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* gma_status_string(gma_status_t status);
+
+/*
+ * Workspace bytes that `op` needs for `shape` with I/O dtype `io_dtype` (and causal
+ * chunk length `chunk`, ignored for other ops).  Depends only on its arguments, never
+ * on the device.  For GMA_OP_RESPONSIBILITIES d_v is ignored.  Writes *bytes_out on
+ * success; same validation and error codes as the op itself.
+ */
+gma_status_t gma_workspace_size(gma_op_t op, const gma_shape_t* shape, gma_dtype_t io_dtype,
+                                int32_t chunk, size_t* bytes_out);
+
+/*
+ * Responsibilities Gamma[b,h,n,:] of every routing vector X[b,h,n,:] under head h's
+ * mixture: Sec. 3.2 Eq. 3, evaluated as the softmax of Eq. 3b over the scores of
+ * Sec. 4.1 Eq. 16 (the k-independent -(d_r/2) log 2 pi is dropped; it cancels).
+ *   X       [B,H,N,d_r] in x_dtype          mu, sigma2 [H,K,d_r] fp32, pi [H,K] fp32
+ *   Gamma   [B,H,N,K] out, in gamma_dtype (GMA_F32 or GMA_BF16)
+ * shape->d_v is ignored.  Every output row is non-negative and sums to 1 up to the
+ * output rounding.
+ */
+gma_status_t gma_responsibilities(const void* X, gma_dtype_t x_dtype,
+                                  const float* mu, const float* sigma2, const float* pi,
+                                  void* Gamma, gma_dtype_t gamma_dtype,
+                                  const gma_shape_t* shape,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bidirectional GMA forward, Sec. 3.3 Eq. 5-8:
+ *   Vt = Gamma_K^T V,  Z = Gamma_K^T 1_N,  O_i = (Gamma_Q Vt)_i / ((Gamma_Q Z)_i + eps)
+ * with Gamma_Q, Gamma_K the responsibilities of X_Q and X_K (see gma_responsibilities).
+ * eps > 0 is added once to each row denominator (footnote 4 of Sec. 3.3).  Gamma is
+ * never written to memory; Vt and Z live in the workspace.
+ *   XQ, XK [B,H,N,d_r], V [B,H,N,d_v], O [B,H,N,d_v] out, all in io_dtype.
+ */
+gma_status_t gma_forward_bidir(const void* XQ, const void* XK, const void* V,
+                               gma_dtype_t io_dtype,
+                               const float* mu, const float* sigma2, const float* pi,
+                               float eps, void* O, const gma_shape_t* shape,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Causal GMA forward, Sec. 3.5 Eq. 6b and 8b:
+ *   Vt^(i) = sum_{j<=i} gammaK_j V_j^T,  Z^(i) = sum_{j<=i} gammaK_j   (inclusive of i)
+ *   O_i    = gammaQ_i Vt^(i) / (gammaQ_i Z^(i) + eps)
+ * computed as a chunked scan: the sequence is cut into chunks of `chunk` positions;
+ * inside a chunk the masked product (Gamma_Q Gamma_K^T restricted to j <= i) is formed
+ * on chip and the K x (d_v+1) running memory carries the prefix across chunks.
+ * `chunk` must be 16, 32 or 64 (GMA_ERR_UNSUPPORTED otherwise).  Output row i depends
+ * only on inputs at positions <= i.  Arguments as for gma_forward_bidir.
+ */
+gma_status_t gma_forward_causal(const void* XQ, const void* XK, const void* V,
+                                gma_dtype_t io_dtype,
+                                const float* mu, const float* sigma2, const float* pi,
+                                float eps, void* O, const gma_shape_t* shape, int32_t chunk,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GMA_H */

@@ -26,3 +26,11 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_runtest_setup(item):
+    # Name each GPU case on stderr (unbuffered) before it runs, so a failing or hanging
+    # GPU step can be attributed from the tail of the output.
+    if "gpu" in item.keywords:
+        sys.stderr.write("\n[gpu-case] %s\n" % item.nodeid)
+        sys.stderr.flush()

@@ -1,0 +1,134 @@
+"""Host-side checks of libgma.so: it loads without a GPU, exports every entry point that
+include/gma.h declares, and rejects invalid arguments before making any HIP call.
+No test here launches work (fake device pointers never reach a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gaussian_mixture_sequence_amd import binding as gb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gma.h")
+OK, NULLP, SHAPE, VALUE, UNSUP, MISAL, WS, HIP = range(8)
+FAKE = 0x10000  # aligned, never dereferenced: validation fails before any HIP call
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gb.LIB_PATH):
+        from gaussian_mixture_sequence_amd import build
+        build.build()
+    return gb.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gma_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(gb.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in enumerate(gb.STATUS_NAMES):
+        assert gb.gma_status_string(code) == name
+    assert gb.gma_status_string(99) == "GMA_ERR_UNKNOWN"
+
+
+def ws_size(op, B, H, N, dr, dv, K, io, chunk=64):
+    out = ctypes.c_size_t(0)
+    st = gb.load().gma_workspace_size(op, ctypes.byref(gb.Shape(B, H, N, dr, dv, K)), io, chunk, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size_validation(lib):
+    F, BF = gb.GMA_F32, gb.GMA_BF16
+    R, Bd, C = gb.GMA_OP_RESPONSIBILITIES, gb.GMA_OP_BIDIR, gb.GMA_OP_CAUSAL
+    assert ws_size(Bd, 1, 1, 256, 16, 32, 8, F)[0] == OK
+    assert ws_size(Bd, 8, 8, 4096, 64, 64, 64, BF)[0] == OK
+    assert ws_size(C, 2, 16, 32768, 64, 128, 256, BF)[0] == OK
+    assert ws_size(Bd, -1, 1, 8, 16, 32, 8, F)[0] == SHAPE
+    assert ws_size(Bd, 1, 1, -8, 16, 32, 8, F)[0] == SHAPE
+    assert ws_size(Bd, 1, 1, 8, 16, 32, 257, F)[0] == UNSUP
+    assert ws_size(Bd, 1, 1, 8, 16, 32, 0, F)[0] == UNSUP
+    assert ws_size(Bd, 1, 1, 8, 129, 32, 8, F)[0] == UNSUP
+    assert ws_size(Bd, 1, 1, 8, 24, 32, 8, BF)[0] == UNSUP      # bf16 d_r set
+    assert ws_size(Bd, 1, 1, 8, 16, 48, 8, BF)[0] == UNSUP      # bf16 d_v set
+    assert ws_size(R, 1, 1, 8, 16, 0, 8, BF)[0] == OK            # d_v ignored
+    assert ws_size(C, 1, 1, 8, 16, 32, 8, F, chunk=24)[0] == UNSUP
+    assert ws_size(C, 1, 1, 8, 16, 32, 8, F, chunk=128)[0] == UNSUP
+    assert ws_size(7, 1, 1, 8, 16, 32, 8, F)[0] == VALUE
+    assert ws_size(Bd, 1, 1, 8, 16, 32, 8, 5)[0] == VALUE
+    assert gb.load().gma_workspace_size(Bd, None, F, 64, ctypes.byref(ctypes.c_size_t())) == NULLP
+
+
+def test_workspace_is_bounded_in_sequence_length(lib):
+    """Scratch is O(K d_v) per problem and split: it stops growing with N (linear total
+    memory in N comes only from the caller's inputs and output)."""
+    for op in (gb.GMA_OP_BIDIR, gb.GMA_OP_CAUSAL):
+        sizes = [ws_size(op, 4, 4, n, 32, 64, 128, gb.GMA_BF16)[1] for n in (65536, 1 << 18, 1 << 20)]
+        assert sizes[0] == sizes[1] == sizes[2], sizes
+
+
+def call_bidir(lib, xq=FAKE, xk=FAKE, v=FAKE, io=gb.GMA_F32, mu=FAKE, s2=FAKE, pi=FAKE, eps=1e-6, o=FAKE,
+               shape=(1, 1, 64, 16, 32, 8), ws=FAKE, ws_bytes=None, causal=False, chunk=64):
+    sh = gb.Shape(*shape)
+    op = gb.GMA_OP_CAUSAL if causal else gb.GMA_OP_BIDIR
+    if ws_bytes is None:
+        st, ws_bytes = ws_size(op, *shape, io, chunk)
+    if causal:
+        return lib.gma_forward_causal(xq, xk, v, io, mu, s2, pi, eps, o, ctypes.byref(sh), chunk, ws, ws_bytes, None)
+    return lib.gma_forward_bidir(xq, xk, v, io, mu, s2, pi, eps, o, ctypes.byref(sh), ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_argument_errors(lib, causal):
+    c = dict(causal=causal)
+    assert call_bidir(lib, xq=None, **c) == NULLP
+    assert call_bidir(lib, o=None, **c) == NULLP
+    assert call_bidir(lib, pi=None, **c) == NULLP
+    assert call_bidir(lib, ws=None, **c) == NULLP
+    assert call_bidir(lib, eps=0.0, **c) == VALUE
+    assert call_bidir(lib, eps=-1.0, **c) == VALUE
+    assert call_bidir(lib, eps=float("nan"), **c) == VALUE
+    assert call_bidir(lib, eps=float("inf"), **c) == VALUE
+    assert call_bidir(lib, io=3, **c) == VALUE
+    assert call_bidir(lib, shape=(1, -1, 64, 16, 32, 8), **c) == SHAPE
+    assert call_bidir(lib, shape=(1, 1, 64, 16, 32, 300), **c) == UNSUP
+    assert call_bidir(lib, xk=FAKE + 2, **c) == MISAL
+    assert call_bidir(lib, o=FAKE + 8, **c) == MISAL
+    assert call_bidir(lib, ws=FAKE + 4, **c) == MISAL
+    st, need = ws_size(gb.GMA_OP_CAUSAL if causal else gb.GMA_OP_BIDIR, 1, 1, 64, 16, 32, 8, gb.GMA_F32)
+    assert need > 0
+    assert call_bidir(lib, ws_bytes=need - 1, **c) == WS
+    if causal:
+        assert call_bidir(lib, chunk=48, **c) == UNSUP
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_empty_problems_enqueue_nothing(lib, causal):
+    """B*H*N == 0 is valid and returns before any HIP call."""
+    for shape in [(1, 1, 0, 16, 32, 8), (0, 4, 128, 16, 32, 8), (2, 0, 128, 16, 32, 8)]:
+        assert call_bidir(lib, shape=shape, causal=causal) == OK
+        assert call_bidir(lib, shape=shape, causal=causal, io=gb.GMA_BF16) == OK
+
+
+def test_responsibilities_argument_errors(lib):
+    sh = gb.Shape(1, 1, 64, 16, 1, 8)
+    st, need = ws_size(gb.GMA_OP_RESPONSIBILITIES, 1, 1, 64, 16, 1, 8, gb.GMA_F32)
+    f = lib.gma_responsibilities
+    assert f(None, 0, FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(sh), FAKE, need, None) == NULLP
+    assert f(FAKE, 0, FAKE, FAKE, FAKE, FAKE, 9, ctypes.byref(sh), FAKE, need, None) == VALUE
+    assert f(FAKE, 0, FAKE, FAKE, FAKE, FAKE + 2, 0, ctypes.byref(sh), FAKE, need, None) == MISAL
+    assert f(FAKE, 0, FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(sh), FAKE, need - 1, None) == WS
+    empty = gb.Shape(1, 1, 0, 16, 1, 8)
+    assert f(FAKE, 0, FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(empty), FAKE, need, None) == OK

@@ -1,0 +1,84 @@
+"""GPU parity: libgma.so (through the C ABI) against the fp64 oracle, element by element,
+on the same seeded inputs.  Tolerances (row-scaled error, see gma_testutil): 1e-5 for
+fp32 I/O, 2e-2 for bf16 I/O with fp32 accumulation."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gaussian_mixture_sequence_amd import binding as gb
+from gaussian_mixture_sequence_amd.inputs import WORKLOADS, Workload, make_inputs
+from gma_testutil import TOL, row_scaled_error, to_device, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(w: Workload, inp, chunk=None):
+    d = to_device(inp)
+    if w.causal:
+        out = gb.gma_forward_causal(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps,
+                                    chunk=chunk or w.chunk)
+    else:
+        out = gb.gma_forward_bidir(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps)
+    torch.cuda.synchronize()
+    return out
+
+
+def run_oracle(w: Workload, inp):
+    fn = oracle.forward_causal if w.causal else oracle.forward_bidir
+    return fn(inp["xq"], inp["xk"], inp["v"], inp["mu"], inp["sigma2"], inp["pi"], w.eps)
+
+
+def small(name, **kw):
+    return WORKLOADS[name].with_(**kw)
+
+
+F32_CASES = [
+    WORKLOADS["bidir_small_f32"],                                        # the fp32 workload itself
+    small("bidir_small_f32", B=2, H=3, N=200, seed=11),                 # ragged tail, several heads
+    small("bidir_small_f32", B=1, H=2, N=1000, d_r=7, d_v=5, K=13, seed=12),
+    small("bidir_small_f32", N=1, d_r=3, d_v=2, K=1, seed=13),          # single token, K = 1
+    small("bidir_small_f32", N=130, d_r=128, d_v=128, K=256, seed=14),  # maximum dims
+    small("bidir_small_f32", causal=True, B=2, H=2, N=300, seed=15),
+    small("bidir_small_f32", causal=True, N=777, d_r=5, d_v=9, K=6, chunk=16, seed=16),
+    small("bidir_small_f32", causal=True, N=1500, K=20, chunk=32, seed=17),  # several segments
+    small("bidir_small_f32", causal=True, N=100, d_r=128, d_v=128, K=256, seed=18),
+]
+
+
+@pytest.mark.parametrize("w", F32_CASES, ids=lambda w: "%s-%s-B%dH%dN%d-dr%d-dv%d-K%d" % (
+    "causal" if w.causal else "bidir", w.dtype, w.B, w.H, w.N, w.d_r, w.d_v, w.K))
+def test_f32_parity(w):
+    inp = make_inputs(w)
+    out = run_gpu(w, inp)
+    assert out.dtype == torch.float32 and out.shape == (w.B, w.H, w.N, w.d_v)
+    err = row_scaled_error(to_np(out), run_oracle(w, inp))
+    assert err <= TOL["f32"], err
+
+
+@pytest.mark.parametrize("gamma_dtype", [torch.float32, torch.bfloat16])
+def test_f32_responsibilities(gamma_dtype):
+    w = small("bidir_small_f32", B=2, H=3, N=333, K=40, seed=21)
+    inp = make_inputs(w)
+    d = to_device(inp)
+    g = gb.gma_responsibilities(d["xq"], d["mu"], d["sigma2"], d["pi"], gamma_dtype=gamma_dtype)
+    torch.cuda.synchronize()
+    ref = oracle.responsibilities(inp["xq"], inp["mu"], inp["sigma2"], inp["pi"])
+    err = np.abs(to_np(g) - ref).max()
+    assert err <= (2e-6 if gamma_dtype == torch.float32 else 4e-3), err
+    assert np.abs(to_np(g).sum(-1) - 1).max() <= (1e-5 if gamma_dtype == torch.float32 else 2e-2)
+
+
+def test_f32_deterministic_and_prefix_invariant():
+    w = small("bidir_small_f32", causal=True, B=1, H=2, N=700, seed=22)
+    inp = make_inputs(w)
+    a = to_np(run_gpu(w, inp))
+    b = to_np(run_gpu(w, inp))
+    assert np.array_equal(a, b)
+    i = 345
+    pert = {k: v.clone() for k, v in inp.items()}
+    g = torch.Generator().manual_seed(5)
+    for k in ("xq", "xk", "v"):
+        pert[k][:, :, i + 1:] += torch.randn(pert[k][:, :, i + 1:].shape, generator=g).to(pert[k].dtype)
+    c = to_np(run_gpu(w, pert))
+    assert np.array_equal(c[:, :, :i + 1], a[:, :, :i + 1])
