@@ -79,6 +79,12 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
         p.seg = round_up(size_t(cdiv(p.N, g)), kTokenTile);
         p.G = cdiv(p.N, p.seg);
     }
+    p.read_rows = 0;
+    if (io == GMA_BF16 && op == GMA_OP_BIDIR && p.P > 0 && p.N > 0) {
+        const int64_t round = bf16_round_tokens(int(p.dr), p.Kp);
+        const int64_t per_problem = std::max<int64_t>(1, cdiv(kBidirBlocks, p.P));
+        p.read_rows = round_up(size_t(cdiv(p.N, per_problem)), size_t(round));
+    }
     const size_t mem_elems = size_t(p.Kp) * size_t(p.dv + 1);
     p.partials_bytes = (op == GMA_OP_RESPONSIBILITIES) ? 0 : round_up(size_t(p.P * p.G) * mem_elems * 4, 256);
     p.memory_bytes = (op == GMA_OP_BIDIR) ? round_up(size_t(p.P) * mem_elems * 4, 256) : 0;

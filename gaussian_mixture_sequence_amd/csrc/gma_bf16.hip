@@ -1,11 +1,508 @@
-// bf16 I/O path of the GMA forward (MFMA kernels).  Placeholder: not implemented yet.
+// bf16 I/O path of the GMA forward: MFMA kernels for gfx950.
+//
+// Kernel sequence on the caller's stream:
+//   params    per head: four bf16 operand planes (a hi/lo, b hi/lo) and the score
+//             constant c (fp64 arithmetic, scaled by log2 e, shifted by max_k c)
+//   write     per (problem, split): partial [Vt | Z] = Gamma_K^T [V | 1] over the split
+//             (Sec. 3.3 Eq. 5-6 of "Gaussian Mixture Attention"); Gamma_K never leaves
+//             the chip: scores -> softmax in registers -> bf16 tile in LDS -> MFMA
+//   combine   bidirectional: fixed-order sum of the partials, then Vt split into hi + lo
+//             bf16 planes stored transposed (the A operand of the read) and Z in fp32
+//   prefix    causal: exclusive prefix of the segment aggregates (starting memories)
+//   read      O = Gamma_Q Vt / (Gamma_Q Z + eps) (Eq. 7-8): computed as O^T = Vt^T Gamma_Q^T
+//             with hi + lo Vt, the denominator in fp32 on the VALU during the softmax
+//   scan      causal chunked scan (gma_bf16_scan.hip)
+#include <cmath>
+#include <cstdint>
+#include <type_traits>
+
+#include "gma_bf16_common.h"
 #include "gma_internal.h"
 
 namespace gma {
-hipError_t bf16_responsibilities(const Plan&, const void*, const float*, const float*, const float*, void*,
-                                 gma_dtype_t, char*, hipStream_t) { return hipErrorNotSupported; }
-hipError_t bf16_bidir(const Plan&, const void*, const void*, const void*, const float*, const float*,
-                      const float*, float, void*, char*, hipStream_t) { return hipErrorNotSupported; }
-hipError_t bf16_causal(const Plan&, const void*, const void*, const void*, const float*, const float*,
-                       const float*, float, void*, char*, hipStream_t) { return hipErrorNotSupported; }
+namespace bf {
+
+// ---------------------------------------------------------------------------- params
+
+__global__ void __launch_bounds__(256) params_kernel(const float* __restrict__ mu, const float* __restrict__ s2,
+                                                     const float* __restrict__ pi, int K, int Kp, int dr,
+                                                     uint16_t* __restrict__ planes, float* __restrict__ cvec) {
+    const int h = blockIdx.x;
+    __shared__ double cd[256];
+    __shared__ double red[4];
+    const double L2E = 1.4426950408889634;
+    uint16_t* ph = planes + size_t(h) * 4 * Kp * dr;
+    for (int idx = threadIdx.x; idx < Kp * dr; idx += 256) {
+        const int k = idx / dr, d = idx - k * dr;
+        double a = 0.0, b = 0.0;
+        if (k < K) {
+            const double inv = 1.0 / double(s2[(size_t(h) * K + k) * dr + d]);
+            a = double(mu[(size_t(h) * K + k) * dr + d]) * inv * L2E;
+            b = -0.5 * inv * L2E;
+        }
+        const uint16_t ah = f32_to_bf16_bits(float(a)), bh = f32_to_bf16_bits(float(b));
+        const uint16_t al = f32_to_bf16_bits(float(a - double(bf16_bits_to_f32(ah))));
+        const uint16_t bl = f32_to_bf16_bits(float(b - double(bf16_bits_to_f32(bh))));
+        ph[(size_t(0) * Kp + k) * dr + d] = ah;
+        ph[(size_t(1) * Kp + k) * dr + d] = al;
+        ph[(size_t(2) * Kp + k) * dr + d] = bh;
+        ph[(size_t(3) * Kp + k) * dr + d] = bl;
+    }
+    double local_max = -INFINITY;
+    for (int k = threadIdx.x; k < K; k += 256) {
+        double acc = log(double(pi[size_t(h) * K + k]));
+        for (int d = 0; d < dr; ++d) {
+            const double v = double(s2[(size_t(h) * K + k) * dr + d]);
+            const double m = double(mu[(size_t(h) * K + k) * dr + d]);
+            acc -= 0.5 * (log(v) + m * m / v);
+        }
+        cd[k] = acc * L2E;
+        local_max = fmax(local_max, cd[k]);
+    }
+    for (int o = 32; o >= 1; o >>= 1) local_max = fmax(local_max, __shfl_xor(local_max, o, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = local_max;
+    __syncthreads();
+    const double mx = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
+    for (int k = threadIdx.x; k < Kp; k += 256) cvec[size_t(h) * Kp + k] = (k < K) ? float(cd[k] - mx) : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------- softmax across waves
+
+// Per-round softmax statistics shared by the CS waves of one token subtile.
+struct Stats {
+    float m, L, D;
+};
+
+// Combines this wave's (m, L, D) with those of the other component groups of its
+// token subtile (published in `st` before the barrier).  Returns the factor that turns
+// this wave's exp2(s - m_w) into probabilities, and the full D / L.
+template <int CS>
+__device__ __forceinline__ float combine_stats(const Stats* st, int ts, int cs, int j, float m, float L, float D,
+                                               float& DoverL) {
+    if (CS == 1) {
+        DoverL = D / L;
+        return 1.0f / L;
+    }
+    float mm = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < CS; ++c) mm = fmaxf(mm, st[(ts * CS + c) * 32 + j].m);
+    float Lt = 0.0f, Dt = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CS; ++c) {
+        const Stats s = st[(ts * CS + c) * 32 + j];
+        const float f = __builtin_amdgcn_exp2f(s.m - mm);
+        Lt = fmaf(s.L, f, Lt);
+        Dt = fmaf(s.D, f, Dt);
+    }
+    (void)cs;
+    DoverL = Dt / Lt;
+    return __builtin_amdgcn_exp2f(m - mm) / Lt;
+}
+
+// ---------------------------------------------------------------------------- responsibilities
+
+template <int DR, int KT>
+__global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) resp_kernel(const uint16_t* __restrict__ X, int64_t N,
+                                                                       int H, int K, const uint16_t* planes,
+                                                                       const float* cvec, void* Gamma,
+                                                                       int gamma_bf16) {
+    using S = Split<DR, KT>;
+    constexpr int Kp = KT * 32;
+    __shared__ Stats st[S::TS * S::CS * 32];
+    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
+    const int cs = wave % S::CS, ts = wave / S::CS;
+    const int64_t p = blockIdx.y;
+    const int h = int(p % H);
+    WaveParams<DR, S::CTW> P;
+    P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * S::CTW);
+    const uint16_t* Xp = X + size_t(p) * N * DR;
+    const int64_t n0 = int64_t(blockIdx.x) * S::ROUND + ts * 32;
+    const int valid = int(max<int64_t>(0, min<int64_t>(32, N - n0)));
+    f32x16 acc[S::CTW];
+    scores<DR, S::CTW>(P, Xp, n0, valid, acc);
+    float m, L, D;
+    float zr[S::CTW][16];
+    local_softmax<S::CTW, false>(acc, zr, m, L, D);
+    if (S::CS > 1) {
+        if (lh == 0) st[(ts * S::CS + cs) * 32 + j] = Stats{m, L, 0.0f};
+        __syncthreads();
+    }
+    float dl;
+    const float scale = combine_stats<S::CS>(st, ts, cs, j, m, L, 0.0f, dl);
+    if (j >= valid) return;
+    const size_t rowoff = (size_t(p) * N + n0 + j) * K;
+#pragma unroll
+    for (int ct = 0; ct < S::CTW; ++ct)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int comp = (cs * S::CTW + ct) * 32 + 8 * q + 4 * lh;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (comp + e < K) {
+                    const float g = acc[ct][4 * q + e] * scale;
+                    if (gamma_bf16)
+                        static_cast<uint16_t*>(Gamma)[rowoff + comp + e] = f32_to_bf16_bits(g);
+                    else
+                        static_cast<float*>(Gamma)[rowoff + comp + e] = g;
+                }
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------- write (Gamma_K^T [V | 1])
+
+template <int DR, int KT, int VT>
+__global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const uint16_t* __restrict__ XK,
+                                                                        const uint16_t* __restrict__ V, int64_t N,
+                                                                        int H, int64_t seg, int G,
+                                                                        const uint16_t* planes, const float* cvec,
+                                                                        float* __restrict__ partials) {
+    using S = Split<DR, KT>;
+    constexpr int Kp = KT * 32, DV = VT * 32;
+    constexpr int LDG = Kp + 8, LDV = DV + 8;
+    constexpr int PAIRS = KT * VT;
+    constexpr int PW = (PAIRS + S::NW - 1) / S::NW;
+    __shared__ Stats st[S::TS * S::CS * 32];
+    __shared__ __attribute__((aligned(16))) uint16_t Gs[S::ROUND * LDG];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[S::ROUND * LDV];
+
+    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
+    const int cs = wave % S::CS, ts = wave / S::CS;
+    const int64_t p = blockIdx.y;
+    const int g_idx = blockIdx.x;
+    const int h = int(p % H);
+    WaveParams<DR, S::CTW> P;
+    P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * S::CTW);
+    const uint16_t* Xp = XK + size_t(p) * N * DR;
+    const uint16_t* Vp = V + size_t(p) * N * DV;
+    const int64_t lo = int64_t(g_idx) * seg, hi = min<int64_t>(lo + seg, N);
+
+    f32x16 wacc[PW];
+    float zacc[PW];
+#pragma unroll
+    for (int q = 0; q < PW; ++q) {
+        zacc[q] = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) wacc[q][r] = 0.0f;
+    }
+    float zr[S::CTW][16];
+
+    for (int64_t nr = lo; nr < hi; nr += S::ROUND) {
+        const int64_t n0 = nr + ts * 32;
+        const int valid = int(max<int64_t>(0, min<int64_t>(32, hi - n0)));
+        f32x16 acc[S::CTW];
+        scores<DR, S::CTW>(P, Xp, n0, valid, acc);
+        float m, L, D;
+        local_softmax<S::CTW, false>(acc, zr, m, L, D);
+        if (S::CS > 1 && lh == 0) st[(ts * S::CS + cs) * 32 + j] = Stats{m, L, 0.0f};
+        __syncthreads();  // B1: stats published; previous round's LDS tiles consumed
+        // value tile of the round -> LDS (rows past the split read as zero)
+        for (int c = threadIdx.x; c < S::ROUND * DV / 8; c += S::NW * 64) {
+            const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (nr + row < hi) v = *reinterpret_cast<const u32x4*>(Vp + (nr + row) * DV + col);
+            *reinterpret_cast<u32x4*>(Vs + row * LDV + col) = v;
+        }
+        float dl;
+        float scale = combine_stats<S::CS>(st, ts, cs, j, m, L, 0.0f, dl);
+        if (j >= valid) scale = 0.0f;
+        store_gamma_lds<S::CTW>(acc, scale, Gs, LDG, ts * 32 + j, cs * S::CTW);
+        __syncthreads();  // B2: Gamma_K and V tiles of the round complete
+#pragma unroll
+        for (int q = 0; q < PW; ++q) {
+            const int pair = wave + q * S::NW;
+            if (pair < PAIRS) {
+                const int ct = pair / VT, vt = pair - ct * VT;
+#pragma unroll
+                for (int ks = 0; ks < S::ROUND / 16; ++ks) {
+                    bf16x8 a = read_colfrag(Gs, LDG, 16 * ks, ct * 32);
+                    bf16x8 b = read_colfrag(Vs, LDV, 16 * ks, vt * 32);
+                    wacc[q] = mfma(a, b, wacc[q]);
+                    if (vt == 0) {
+#pragma unroll
+                        for (int v = 0; v < 8; ++v) zacc[q] += float(a[v]);
+                    }
+                }
+            }
+        }
+    }
+    // partial of this split: Vt [Kp][DV] then Z [Kp]
+    float* mem = partials + (size_t(p) * G + g_idx) * size_t(Kp) * (DV + 1);
+#pragma unroll
+    for (int q = 0; q < PW; ++q) {
+        const int pair = wave + q * S::NW;
+        if (pair < PAIRS) {
+            const int ct = pair / VT, vt = pair - ct * VT;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int comp = ct * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                mem[size_t(comp) * DV + vt * 32 + j] = wacc[q][r];
+            }
+            if (vt == 0) {
+                const float z = xsum32(zacc[q]);
+                if (lh == 0) mem[size_t(Kp) * DV + ct * 32 + j] = z;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------- combine / prefix
+
+// Bidirectional: memory = sum_g partial_g (increasing g), then the read operands:
+// VtT_hi, VtT_lo [DV][Kp] bf16 (Vt transposed, hi + lo split) and Z [Kp] fp32.
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ partials, int G, int Kp, int DV,
+                                                      uint16_t* __restrict__ memory) {
+    const int64_t p = blockIdx.y;
+    const int E = Kp * (DV + 1);
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= E) return;
+    const float* src = partials + size_t(p) * G * E + e;
+    float acc = 0.0f;
+    for (int g = 0; g < G; ++g) acc += src[size_t(g) * E];
+    uint16_t* base = memory + size_t(p) * E * 2;  // E floats of room per problem
+    if (e < Kp * DV) {
+        const int k = e / DV, c = e - k * DV;
+        const uint16_t hi = f32_to_bf16_bits(acc);
+        const uint16_t lo = f32_to_bf16_bits(acc - bf16_bits_to_f32(hi));
+        base[size_t(c) * Kp + k] = hi;
+        base[size_t(DV) * Kp + size_t(c) * Kp + k] = lo;
+    } else {
+        reinterpret_cast<float*>(base + size_t(2) * DV * Kp)[e - Kp * DV] = acc;
+    }
+}
+
+__global__ void __launch_bounds__(256) prefix_kernel(float* __restrict__ partials, int G, int E) {
+    const int64_t p = blockIdx.y;
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= E) return;
+    float* src = partials + size_t(p) * G * E + e;
+    float run = 0.0f;
+    for (int g = 0; g < G; ++g) {
+        const float a = src[size_t(g) * E];
+        src[size_t(g) * E] = run;
+        run += a;
+    }
+}
+
+// ---------------------------------------------------------------------------- read
+
+template <int DR, int KT, int VT>
+__global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const uint16_t* __restrict__ XQ, int64_t N,
+                                                                       int H, int64_t rows_per_block,
+                                                                       const uint16_t* planes, const float* cvec,
+                                                                       const uint16_t* __restrict__ memory, float eps,
+                                                                       uint16_t* __restrict__ O) {
+    using S = Split<DR, KT>;
+    constexpr int Kp = KT * 32, DV = VT * 32;
+    constexpr int LDG = Kp + 8, LDM = Kp + 8;
+    constexpr int PAIRS = S::TS * VT;
+    constexpr int PW = (PAIRS + S::NW - 1) / S::NW;
+    __shared__ Stats st[S::TS * S::CS * 32];
+    __shared__ __attribute__((aligned(16))) uint16_t Gs[S::ROUND * LDG];
+    // VtT hi/lo staged in LDS when it fits next to the Gamma tile; otherwise read from L2
+    constexpr bool MS_LDS = (2 * DV * LDM + S::ROUND * LDG) * 2 <= 150 * 1024;
+    __shared__ __attribute__((aligned(16))) uint16_t Ms[MS_LDS ? 2 * DV * LDM : 8];
+    __shared__ float den_s[S::ROUND];
+
+    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
+    const int cs = wave % S::CS, ts = wave / S::CS;
+    const int64_t p = blockIdx.y;
+    const int h = int(p % H);
+    WaveParams<DR, S::CTW> P;
+    P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * S::CTW);
+    // latent memory of this problem: VtT hi/lo -> LDS, Z -> registers in score-row order
+    const uint16_t* mp = memory + size_t(p) * Kp * (DV + 1) * 2;
+    if (MS_LDS)
+        for (int c = threadIdx.x; c < 2 * DV * Kp / 8; c += S::NW * 64) {
+            const int row = c / (Kp / 8), col = (c - row * (Kp / 8)) * 8;
+            *reinterpret_cast<u32x4*>(Ms + row * LDM + col) =
+                *reinterpret_cast<const u32x4*>(mp + size_t(row) * Kp + col);
+        }
+    const uint16_t* Msrc = MS_LDS ? Ms : mp;
+    constexpr int LDMS = MS_LDS ? LDM : Kp;
+    const float* Zp = reinterpret_cast<const float*>(mp + size_t(2) * DV * Kp);
+    float zr[S::CTW][16];
+#pragma unroll
+    for (int ct = 0; ct < S::CTW; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) zr[ct][r] = Zp[(cs * S::CTW + ct) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)];
+
+    const uint16_t* Xp = XQ + size_t(p) * N * DR;
+    const int64_t lo = int64_t(blockIdx.x) * rows_per_block, hi = min<int64_t>(lo + rows_per_block, N);
+    for (int64_t nr = lo; nr < hi; nr += S::ROUND) {
+        const int64_t n0 = nr + ts * 32;
+        const int valid = int(max<int64_t>(0, min<int64_t>(32, hi - n0)));
+        f32x16 acc[S::CTW];
+        scores<DR, S::CTW>(P, Xp, n0, valid, acc);
+        float m, L, D;
+        local_softmax<S::CTW, true>(acc, zr, m, L, D);
+        if (S::CS > 1 && lh == 0) st[(ts * S::CS + cs) * 32 + j] = Stats{m, L, D};
+        __syncthreads();  // B1
+        float dl;
+        const float scale = combine_stats<S::CS>(st, ts, cs, j, m, L, D, dl);
+        store_gamma_lds<S::CTW>(acc, scale, Gs, LDG, ts * 32 + j, cs * S::CTW);
+        if (cs == 0 && lh == 0) den_s[ts * 32 + j] = dl + eps;
+        __syncthreads();  // B2
+#pragma unroll
+        for (int q = 0; q < PW; ++q) {
+            const int pair = wave + q * S::NW;
+            if (pair < PAIRS) {
+                const int tsub = pair / VT, vt = pair - tsub * VT;
+                f32x16 o;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[r] = 0.0f;
+#pragma unroll
+                for (int ks = 0; ks < Kp / 16; ++ks) {
+                    bf16x8 b = read_rowfrag(Gs, LDG, tsub * 32 + j, 16 * ks);
+                    bf16x8 ah = read_rowfrag(Msrc, LDMS, vt * 32 + j, 16 * ks);
+                    bf16x8 al = read_rowfrag(Msrc + DV * LDMS, LDMS, vt * 32 + j, 16 * ks);
+                    o = mfma(ah, b, o);
+                    o = mfma(al, b, o);
+                }
+                const int64_t tok = nr + tsub * 32 + j;
+                if (tok < hi) {
+                    const float rden = 1.0f / den_s[tsub * 32 + j];
+                    uint16_t* orow = O + (size_t(p) * N + tok) * DV + vt * 32 + 4 * lh;
+#pragma unroll
+                    for (int qq = 0; qq < 4; ++qq) {
+                        u32x2 v;
+                        v[0] = pack_bf16x2(o[4 * qq + 0] * rden, o[4 * qq + 1] * rden);
+                        v[1] = pack_bf16x2(o[4 * qq + 2] * rden, o[4 * qq + 3] * rden);
+                        *reinterpret_cast<u32x2*>(orow + 8 * qq) = v;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------- dispatch
+
+template <typename F>
+hipError_t with_dr_kt(int dr, int kt, F&& f) {
+#define GMA_CASE(D, T) \
+    if (dr == D && kt == T) return f(std::integral_constant<int, D>(), std::integral_constant<int, T>());
+#define GMA_DR(D) GMA_CASE(D, 1) GMA_CASE(D, 2) GMA_CASE(D, 4) GMA_CASE(D, 8)
+    GMA_DR(16) GMA_DR(32) GMA_DR(64) GMA_DR(128)
+#undef GMA_DR
+#undef GMA_CASE
+    return hipErrorNotSupported;
+}
+
+template <typename F>
+hipError_t with_vt(int vt, F&& f) {
+    if (vt == 1) return f(std::integral_constant<int, 1>());
+    if (vt == 2) return f(std::integral_constant<int, 2>());
+    if (vt == 4) return f(std::integral_constant<int, 4>());
+    return hipErrorNotSupported;
+}
+
+}  // namespace bf
+
+namespace {
+
+struct Bf16Params {
+    uint16_t* planes;  // [H][4][Kp][dr]
+    float* cvec;       // [H][Kp]
+};
+
+Bf16Params bf16_params_view(const Plan& p, char* ws) {
+    Bf16Params v;
+    v.cvec = reinterpret_cast<float*>(ws + p.off_params);
+    v.planes = reinterpret_cast<uint16_t*>(ws + p.off_params + round_up(size_t(p.H * p.Kp) * 4, 256));
+    return v;
+}
+
+int kt_of(const Plan& p) { return int(p.Kp / 32); }
+
+hipError_t launch_params(const Plan& p, const float* mu, const float* s2, const float* pi, char* ws, hipStream_t st) {
+    Bf16Params v = bf16_params_view(p, ws);
+    hipLaunchKernelGGL(bf::params_kernel, dim3(unsigned(p.H)), dim3(256), 0, st, mu, s2, pi, int(p.K), int(p.Kp),
+                       int(p.dr), v.planes, v.cvec);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t bf16_round_tokens(int dr, int64_t Kp) {
+    int64_t out = 0;
+    (void)bf::with_dr_kt(dr, int(Kp / 32), [&](auto D, auto T) {
+        out = bf::Split<decltype(D)::value, decltype(T)::value>::ROUND;
+        return hipSuccess;
+    });
+    return out;
+}
+
+hipError_t bf16_responsibilities(const Plan& p, const void* X, const float* mu, const float* s2, const float* pi,
+                                 void* Gamma, gma_dtype_t gamma_dtype, char* ws, hipStream_t st) {
+    hipError_t e = launch_params(p, mu, s2, pi, ws, st);
+    if (e != hipSuccess) return e;
+    Bf16Params v = bf16_params_view(p, ws);
+    return bf::with_dr_kt(int(p.dr), kt_of(p), [&](auto D, auto T) {
+        constexpr int DR = decltype(D)::value, KT = decltype(T)::value;
+        using S = bf::Split<DR, KT>;
+        dim3 grid(unsigned((p.N + S::ROUND - 1) / S::ROUND), unsigned(p.P));
+        hipLaunchKernelGGL((bf::resp_kernel<DR, KT>), grid, dim3(S::NW * 64), 0, st,
+                           static_cast<const uint16_t*>(X), p.N, int(p.H), int(p.K), v.planes, v.cvec, Gamma,
+                           gamma_dtype == GMA_BF16 ? 1 : 0);
+        return hipGetLastError();
+    });
+}
+
+hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, char* ws, hipStream_t st) {
+    Bf16Params v = bf16_params_view(p, ws);
+    float* partials = reinterpret_cast<float*>(ws + p.off_partials);
+    return bf::with_dr_kt(int(p.dr), kt_of(p), [&](auto D, auto T) {
+        constexpr int DR = decltype(D)::value, KT = decltype(T)::value;
+        return bf::with_vt(int(p.dv / 32), [&](auto VV) {
+            constexpr int VT = decltype(VV)::value;
+            using S = bf::Split<DR, KT>;
+            hipLaunchKernelGGL((bf::write_kernel<DR, KT, VT>), dim3(unsigned(p.G), unsigned(p.P)), dim3(S::NW * 64), 0,
+                               st, static_cast<const uint16_t*>(XK), static_cast<const uint16_t*>(V), p.N, int(p.H),
+                               p.seg, int(p.G), v.planes, v.cvec, partials);
+            return hipGetLastError();
+        });
+    });
+}
+
+hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu, const float* s2,
+                      const float* pi, float eps, void* O, char* ws, hipStream_t st) {
+    hipError_t e = launch_params(p, mu, s2, pi, ws, st);
+    if (e != hipSuccess) return e;
+    if ((e = bf16_write_partials(p, XK, V, ws, st)) != hipSuccess) return e;
+    float* partials = reinterpret_cast<float*>(ws + p.off_partials);
+    uint16_t* memory = reinterpret_cast<uint16_t*>(ws + p.off_memory);
+    const int E = int(p.Kp * (p.dv + 1));
+    hipLaunchKernelGGL(bf::combine_kernel, dim3(unsigned((E + 255) / 256), unsigned(p.P)), dim3(256), 0, st, partials,
+                       int(p.G), int(p.Kp), int(p.dv), memory);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    Bf16Params v = bf16_params_view(p, ws);
+    return bf::with_dr_kt(int(p.dr), kt_of(p), [&](auto D, auto T) {
+        constexpr int DR = decltype(D)::value, KT = decltype(T)::value;
+        return bf::with_vt(int(p.dv / 32), [&](auto VV) {
+            constexpr int VT = decltype(VV)::value;
+            using S = bf::Split<DR, KT>;
+            dim3 grid(unsigned((p.N + p.read_rows - 1) / p.read_rows), unsigned(p.P));
+            hipLaunchKernelGGL((bf::read_kernel<DR, KT, VT>), grid, dim3(S::NW * 64), 0, st,
+                               static_cast<const uint16_t*>(XQ), p.N, int(p.H), p.read_rows, v.planes, v.cvec, memory,
+                               eps, static_cast<uint16_t*>(O));
+            return hipGetLastError();
+        });
+    });
+}
+
+hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu, const float* s2,
+                       const float* pi, float eps, void* O, char* ws, hipStream_t st) {
+    hipError_t e = launch_params(p, mu, s2, pi, ws, st);
+    if (e != hipSuccess) return e;
+    float* partials = reinterpret_cast<float*>(ws + p.off_partials);
+    if (p.G > 1 && (e = bf16_write_partials(p, XK, V, ws, st)) != hipSuccess) return e;
+    const int E = int(p.Kp * (p.dv + 1));
+    hipLaunchKernelGGL(bf::prefix_kernel, dim3(unsigned((E + 255) / 256), unsigned(p.P)), dim3(256), 0, st, partials,
+                       int(p.G), E);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    Bf16Params v = bf16_params_view(p, ws);
+    return bf16_scan(p, XQ, XK, V, v.planes, v.cvec, eps, O, ws, st);
+}
+
 }  // namespace gma

@@ -27,6 +27,7 @@ struct Plan {
     int64_t G;            // sequence splits per problem (write partials / causal segments)
     int64_t seg;          // tokens per split (multiple of the token tile)
     int32_t chunk;        // causal chunk length
+    int64_t read_rows;    // tokens per workgroup of the bf16 read kernel
     // byte offsets into the workspace
     size_t off_params, off_partials, off_memory, total;
     size_t params_bytes, partials_bytes, memory_bytes;
@@ -56,5 +57,11 @@ hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void*
 hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void* V,
                        const float* mu, const float* s2, const float* pi, float eps, void* O,
                        char* ws, hipStream_t st);
+// tokens one bf16 workgroup processes per round for (d_r, padded K); 0 if unsupported
+int64_t bf16_round_tokens(int dr, int64_t Kp);
+// causal chunked scan of every segment, starting from the prefix memories in the
+// workspace partials (gma_bf16_scan.hip)
+hipError_t bf16_scan(const Plan& p, const void* XQ, const void* XK, const void* V, const uint16_t* planes,
+                     const float* cvec, float eps, void* O, char* ws, hipStream_t st);
 
 }  // namespace gma

@@ -82,3 +82,80 @@ def test_f32_deterministic_and_prefix_invariant():
         pert[k][:, :, i + 1:] += torch.randn(pert[k][:, :, i + 1:].shape, generator=g).to(pert[k].dtype)
     c = to_np(run_gpu(w, pert))
     assert np.array_equal(c[:, :, :i + 1], a[:, :, :i + 1])
+
+
+# ----------------------------------------------------------------------------- bf16 MFMA path
+
+def bf16_case(causal=False, **kw):
+    base = WORKLOADS["causal_b8h12_n2048" if causal else "bidir_b8h8_n4096"]
+    return base.with_(**kw)
+
+
+BF16_RESP_CASES = [(64, 64), (32, 128), (16, 8), (128, 256), (64, 50), (16, 256), (128, 32)]
+
+
+@pytest.mark.parametrize("dr,K", BF16_RESP_CASES, ids=lambda v: str(v))
+@pytest.mark.parametrize("gamma_dtype", [torch.float32, torch.bfloat16])
+def test_bf16_responsibilities(dr, K, gamma_dtype):
+    w = bf16_case(B=2, H=3, N=333, d_r=dr, K=K, seed=31 + dr + K)
+    inp = make_inputs(w)
+    d = to_device(inp)
+    g = gb.gma_responsibilities(d["xq"], d["mu"], d["sigma2"], d["pi"], gamma_dtype=gamma_dtype)
+    torch.cuda.synchronize()
+    ref = oracle.responsibilities(inp["xq"], inp["mu"], inp["sigma2"], inp["pi"])
+    err = np.abs(to_np(g) - ref).max()
+    # score error of the split-operand MFMA (~1e-4 in Gamma) plus the output rounding
+    assert err <= (2e-3 if gamma_dtype == torch.float32 else 6e-3), err
+
+
+BF16_BIDIR_CASES = [
+    bf16_case(B=1, H=2, N=1000, seed=41),                                   # the B8H8 shapes, short
+    bf16_case(B=2, H=1, N=777, d_r=32, d_v=64, K=128, mu_std=1.5, seed=42),  # long-context dims
+    bf16_case(B=1, H=1, N=300, d_r=16, d_v=32, K=8, seed=43),               # K padded to 32
+    bf16_case(B=1, H=1, N=200, d_r=128, d_v=128, K=256, seed=44),           # maximum dims
+    bf16_case(B=1, H=3, N=1, seed=45),                                      # single token
+    bf16_case(B=1, H=1, N=129, d_r=64, d_v=32, K=50, seed=46),              # ragged everything
+    bf16_case(B=1, H=2, N=5000, d_r=64, d_v=128, K=256, seed=47),           # several splits
+]
+
+
+def case_id(w):
+    return "%s-B%dH%dN%d-dr%d-dv%d-K%d" % ("causal" if w.causal else "bidir", w.B, w.H, w.N, w.d_r, w.d_v, w.K)
+
+
+@pytest.mark.parametrize("w", BF16_BIDIR_CASES, ids=case_id)
+def test_bf16_bidir_parity(w):
+    inp = make_inputs(w)
+    out = run_gpu(w, inp)
+    assert out.dtype == torch.bfloat16 and out.shape == (w.B, w.H, w.N, w.d_v)
+    err = row_scaled_error(to_np(out), run_oracle(w, inp))
+    assert err <= TOL["bf16"], err
+
+
+def sampled_heads(w, inp, out, heads):
+    """Oracle on a few full (b, h) problems of a full-size run."""
+    from gaussian_mixture_sequence_amd.inputs import head_slice
+    worst = 0.0
+    for b, h in heads:
+        sl = head_slice(inp, b, h)
+        ref = run_oracle(w.with_(B=1, H=1), sl)[0, 0]
+        worst = max(worst, row_scaled_error(to_np(out[b, h]), ref))
+    return worst
+
+
+@pytest.mark.parametrize("name", ["bidir_b8h8_n4096", "bidir_long_n65536"])
+def test_bf16_bidir_full_size_sampled(name):
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    out = run_gpu(w, inp)
+    assert torch.isfinite(out.float()).all()
+    err = sampled_heads(w, inp, out, [(0, 0), (w.B - 1, w.H - 1)])
+    assert err <= TOL["bf16"], err
+
+
+def test_bf16_bidir_deterministic():
+    w = bf16_case(B=2, H=2, N=3000, seed=48)
+    inp = make_inputs(w)
+    a = to_np(run_gpu(w, inp))
+    b = to_np(run_gpu(w, inp))
+    assert np.array_equal(a, b)
