@@ -24,7 +24,7 @@ STATUS_NAMES = ["GMA_OK", "GMA_ERR_NULL_POINTER", "GMA_ERR_BAD_SHAPE", "GMA_ERR_
 GMA_F32, GMA_BF16 = 0, 1
 GMA_OP_RESPONSIBILITIES, GMA_OP_BIDIR, GMA_OP_CAUSAL = 0, 1, 2
 EXPORTED = ["gma_status_string", "gma_workspace_size", "gma_responsibilities", "gma_forward_bidir",
-            "gma_forward_causal"]
+            "gma_forward_causal", "gma_profiling", "gma_profiling_collect"]
 
 
 class GmaError(RuntimeError):
@@ -32,6 +32,10 @@ class GmaError(RuntimeError):
         self.status = status
         name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
         super().__init__("%s returned %s" % (where, name))
+
+
+class KernelStat(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int64), ("total_ms", ctypes.c_double)]
 
 
 class Shape(ctypes.Structure):
@@ -64,6 +68,10 @@ def load() -> ctypes.CDLL:
             lib.gma_forward_bidir.restype = i32
             lib.gma_forward_causal.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, shp, i32, vp, sz, vp]
             lib.gma_forward_causal.restype = i32
+            lib.gma_profiling.argtypes = [ctypes.c_int]
+            lib.gma_profiling.restype = i32
+            lib.gma_profiling_collect.argtypes = [ctypes.POINTER(KernelStat), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+            lib.gma_profiling_collect.restype = i32
             _lib = lib
     return _lib
 
@@ -166,3 +174,16 @@ def gma_forward_causal(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, mu: 
                                      int(chunk), _ptr(ws), ws.numel(), _stream(stream)),
            "gma_forward_causal")
     return out
+
+
+def gma_profiling(enable: bool) -> None:
+    """Turn per-kernel hipEvent timing of the library's launches on or off."""
+    _check(load().gma_profiling(1 if enable else 0), "gma_profiling")
+
+
+def gma_profiling_collect(capacity: int = 64):
+    """{kernel name: (launches, total milliseconds)} recorded since the last collect."""
+    buf = (KernelStat * capacity)()
+    n = ctypes.c_int(0)
+    _check(load().gma_profiling_collect(buf, capacity, ctypes.byref(n)), "gma_profiling_collect")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n.value, capacity))}

@@ -4,6 +4,10 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
 
 #include "gma_internal.h"
 
@@ -94,6 +98,51 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
     p.total = p.off_memory + p.memory_bytes;
     *pl = p;
     return GMA_OK;
+}
+
+// ---- kernel timing ----------------------------------------------------------------
+
+namespace {
+
+struct PendingLaunch {
+    const char* name;
+    hipEvent_t start, stop;
+};
+
+std::mutex g_trace_mu;
+bool g_trace_on = false;
+std::vector<PendingLaunch> g_pending;
+PendingLaunch g_open{nullptr, nullptr, nullptr};
+
+void drop_pending() {
+    for (auto& p : g_pending) {
+        (void)hipEventDestroy(p.start);
+        (void)hipEventDestroy(p.stop);
+    }
+    g_pending.clear();
+}
+
+}  // namespace
+
+void trace_begin(hipStream_t st, const char* name) {
+    std::lock_guard<std::mutex> lk(g_trace_mu);
+    if (!g_trace_on) return;
+    PendingLaunch p{name, nullptr, nullptr};
+    if (hipEventCreate(&p.start) != hipSuccess) return;
+    if (hipEventCreate(&p.stop) != hipSuccess) {
+        (void)hipEventDestroy(p.start);
+        return;
+    }
+    (void)hipEventRecord(p.start, st);
+    g_open = p;
+}
+
+void trace_end(hipStream_t st) {
+    std::lock_guard<std::mutex> lk(g_trace_mu);
+    if (!g_trace_on || !g_open.name) return;
+    (void)hipEventRecord(g_open.stop, st);
+    g_pending.push_back(g_open);
+    g_open = PendingLaunch{nullptr, nullptr, nullptr};
 }
 
 }  // namespace gma
@@ -195,6 +244,51 @@ gma_status_t gma_forward_causal(const void* XQ, const void* XK, const void* V, g
                                 size_t workspace_bytes, hipStream_t stream) {
     return forward_common(GMA_OP_CAUSAL, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, O, shape, chunk,
                           workspace, workspace_bytes, stream);
+}
+
+gma_status_t gma_profiling(int enable) {
+    std::lock_guard<std::mutex> lk(gma::g_trace_mu);
+    gma::g_trace_on = enable != 0;
+    if (!gma::g_trace_on) gma::drop_pending();
+    return GMA_OK;
+}
+
+gma_status_t gma_profiling_collect(gma_kernel_stat_t* stats, int capacity, int* count) {
+    if (!count || (capacity > 0 && !stats)) return GMA_ERR_NULL_POINTER;
+    std::lock_guard<std::mutex> lk(gma::g_trace_mu);
+    std::map<std::string, std::pair<int64_t, double>> agg;
+    std::vector<std::string> order;
+    gma_status_t status = GMA_OK;
+    for (auto& p : gma::g_pending) {
+        float ms = 0.0f;
+        if (hipEventSynchronize(p.stop) != hipSuccess || hipEventElapsedTime(&ms, p.start, p.stop) != hipSuccess) {
+            status = GMA_ERR_HIP;
+            continue;
+        }
+        auto it = agg.find(p.name);
+        if (it == agg.end()) {
+            order.push_back(p.name);
+            agg[p.name] = {1, double(ms)};
+        } else {
+            it->second.first += 1;
+            it->second.second += ms;
+        }
+    }
+    // names are the launchers' string literals; map them back to those static pointers
+    std::map<std::string, const char*> names;
+    for (auto& p : gma::g_pending) names[p.name] = p.name;
+    gma::drop_pending();
+    int n = 0;
+    for (const auto& name : order) {
+        if (n < capacity) {
+            stats[n].name = names[name];
+            stats[n].launches = agg[name].first;
+            stats[n].total_ms = agg[name].second;
+        }
+        ++n;
+    }
+    *count = n;
+    return status;
 }
 
 }  // extern "C"

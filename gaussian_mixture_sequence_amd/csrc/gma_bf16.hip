@@ -417,7 +417,7 @@ int kt_of(const Plan& p) { return int(p.Kp / 32); }
 
 hipError_t launch_params(const Plan& p, const float* mu, const float* s2, const float* pi, char* ws, hipStream_t st) {
     Bf16Params v = bf16_params_view(p, ws);
-    hipLaunchKernelGGL(bf::params_kernel, dim3(unsigned(p.H)), dim3(256), 0, st, mu, s2, pi, int(p.K), int(p.Kp),
+    GMA_LAUNCH("bf16_params", bf::params_kernel, dim3(unsigned(p.H)), dim3(256), 0, st, mu, s2, pi, int(p.K), int(p.Kp),
                        int(p.dr), v.planes, v.cvec);
     return hipGetLastError();
 }
@@ -442,7 +442,7 @@ hipError_t bf16_responsibilities(const Plan& p, const void* X, const float* mu, 
         constexpr int DR = decltype(D)::value, KT = decltype(T)::value;
         using S = bf::Split<DR, KT>;
         dim3 grid(unsigned((p.N + S::ROUND - 1) / S::ROUND), unsigned(p.P));
-        hipLaunchKernelGGL((bf::resp_kernel<DR, KT>), grid, dim3(S::NW * 64), 0, st,
+        GMA_LAUNCH("bf16_resp", (bf::resp_kernel<DR, KT>), grid, dim3(S::NW * 64), 0, st,
                            static_cast<const uint16_t*>(X), p.N, int(p.H), int(p.K), v.planes, v.cvec, Gamma,
                            gamma_dtype == GMA_BF16 ? 1 : 0);
         return hipGetLastError();
@@ -457,7 +457,7 @@ hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, cha
         return bf::with_vt(int(p.dv / 32), [&](auto VV) {
             constexpr int VT = decltype(VV)::value;
             using S = bf::Split<DR, KT>;
-            hipLaunchKernelGGL((bf::write_kernel<DR, KT, VT>), dim3(unsigned(p.G), unsigned(p.P)), dim3(S::NW * 64), 0,
+            GMA_LAUNCH("bf16_write", (bf::write_kernel<DR, KT, VT>), dim3(unsigned(p.G), unsigned(p.P)), dim3(S::NW * 64), 0,
                                st, static_cast<const uint16_t*>(XK), static_cast<const uint16_t*>(V), p.N, int(p.H),
                                p.seg, int(p.G), v.planes, v.cvec, partials);
             return hipGetLastError();
@@ -473,7 +473,7 @@ hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void*
     float* partials = reinterpret_cast<float*>(ws + p.off_partials);
     uint16_t* memory = reinterpret_cast<uint16_t*>(ws + p.off_memory);
     const int E = int(p.Kp * (p.dv + 1));
-    hipLaunchKernelGGL(bf::combine_kernel, dim3(unsigned((E + 255) / 256), unsigned(p.P)), dim3(256), 0, st, partials,
+    GMA_LAUNCH("bf16_combine", bf::combine_kernel, dim3(unsigned((E + 255) / 256), unsigned(p.P)), dim3(256), 0, st, partials,
                        int(p.G), int(p.Kp), int(p.dv), memory);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     Bf16Params v = bf16_params_view(p, ws);
@@ -483,7 +483,7 @@ hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void*
             constexpr int VT = decltype(VV)::value;
             using S = bf::Split<DR, KT>;
             dim3 grid(unsigned((p.N + p.read_rows - 1) / p.read_rows), unsigned(p.P));
-            hipLaunchKernelGGL((bf::read_kernel<DR, KT, VT>), grid, dim3(S::NW * 64), 0, st,
+            GMA_LAUNCH("bf16_read", (bf::read_kernel<DR, KT, VT>), grid, dim3(S::NW * 64), 0, st,
                                static_cast<const uint16_t*>(XQ), p.N, int(p.H), p.read_rows, v.planes, v.cvec, memory,
                                eps, static_cast<uint16_t*>(O));
             return hipGetLastError();
@@ -498,7 +498,7 @@ hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void
     float* partials = reinterpret_cast<float*>(ws + p.off_partials);
     if (p.G > 1 && (e = bf16_write_partials(p, XK, V, ws, st)) != hipSuccess) return e;
     const int E = int(p.Kp * (p.dv + 1));
-    hipLaunchKernelGGL(bf::prefix_kernel, dim3(unsigned((E + 255) / 256), unsigned(p.P)), dim3(256), 0, st, partials,
+    GMA_LAUNCH("bf16_prefix", bf::prefix_kernel, dim3(unsigned((E + 255) / 256), unsigned(p.P)), dim3(256), 0, st, partials,
                        int(p.G), E);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     Bf16Params v = bf16_params_view(p, ws);

@@ -1,9 +1,333 @@
-// Causal chunked scan of the bf16 path (placeholder until the MFMA scan lands).
+// Causal GMA of the bf16 path: chunked scan over one segment per workgroup.
+//
+// Sec. 3.5 of "Gaussian Mixture Attention" defines the prefix memory (Eq. 6b) and the
+// output (Eq. 8b); the prefix sums run along the sequence.  A segment starts from the
+// memory of all earlier positions (the exclusive prefix of the segment aggregates,
+// computed by the write + prefix kernels) and advances it chunk by chunk.  For a chunk
+// of CH positions with responsibilities Gq, Gk (bf16, in LDS) and values Vc:
+//   S    = Gq Gk^T, kept for key positions j <= query position i      (Eq. 9b support)
+//   num  = S Vc + Gq Vt,   den = S 1 + Gq Z + eps                      (Eq. 8b split at the chunk)
+//   Vt  += Gk^T Vc,  Z += Gk^T 1                                       (Eq. 6b advanced by the chunk)
+// Phases per chunk (barriers between them):
+//   L  scores + softmax of the chunk's query and key rows -> Gq, Gk tiles; Gq Z on the VALU
+//   S  lower-triangular 32x32 tiles of S^T on MFMA, masked, stored bf16; fp32 row sums
+//   O  each wave owns 16-wide value columns of the K x d_v memory (fp32 registers, held
+//      across chunks): intra part V^T S^T, inter part Vt^T Gq^T (Vt split hi + lo),
+//      divide, store; then the memory update Gk^T Vc on MFMA.  Z lives in LDS.
+// 16x16x32 MFMA layouts (lane l, g = l / 16): A row i = l % 16, k = 8 g + v; B col j =
+// l % 16, k = 8 g + v; D row i = 4 g + r, col j = l % 16.
+#include <cstdint>
+#include <type_traits>
+
+#include "gma_bf16_common.h"
 #include "gma_internal.h"
 
 namespace gma {
-hipError_t bf16_scan(const Plan&, const void*, const void*, const void*, const uint16_t*, const float*, float, void*,
-                     char*, hipStream_t) {
+namespace bf {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16x32 fragment with k down a column of a row-major LDS tile:
+// lane (g, i) gets tile[row0 + 8 g + v][col0 + i], v = 0..7.  Within each 16-lane group
+// the transposing read hands output lane q, element v, the value at offset q % 4 of the
+// 8 bytes addressed by source lane 4 v + q / 4; source lane m therefore addresses row
+// (m / 4), columns 4 (m % 4) .. + 3.
+__device__ __forceinline__ bf16x8 read_colfrag16(const uint16_t* tile, int ld, int row0, int col0) {
+    const int l = threadIdx.x & 63;
+    const int g = l >> 4, m = l & 15;
+    const uint16_t* base = tile + (row0 + 8 * g + (m >> 2)) * ld + col0 + 4 * (m & 3);
+    i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+    i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 4 * ld));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+struct ScanStats {
+    float m, L, D;
+};
+
+template <int DR, int KT, int VT, int CH>
+__global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
+    scan_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
+                int64_t N, int H, int64_t seg, int G, const uint16_t* planes, const float* cvec,
+                const float* __restrict__ prefix, float eps, uint16_t* __restrict__ O) {
+    using S = Split<DR, KT>;
+    constexpr int Kp = KT * 32, DV = VT * 32;
+    constexpr int NW = S::NW, CS = S::CS, TS = S::TS, CTW = S::CTW;
+    constexpr int LDG = Kp + 8, LDV = DV + 8, LDSS = CH + 8;
+    constexpr int SUB = CH / 32;                  // 32-token subtiles per chunk
+    constexpr int JOBS = 2 * SUB;                 // query subtiles, then key subtiles
+    constexpr int JPW = (JOBS + TS - 1) / TS;     // jobs per token slot
+    constexpr int JG = (CS >= 8) ? 1 : JPW;       // jobs whose scores are held at once
+    constexpr int C16 = DV / 16;                  // 16-wide value column tiles
+    constexpr int CPW = (C16 + NW - 1) / NW;      // column tiles per wave
+    constexpr int KT16 = Kp / 16;                 // 16-row component tiles of the memory
+    constexpr int STILES = SUB * (SUB + 1) / 2;   // lower-triangular tiles of S^T
+
+    __shared__ ScanStats st[JPW][TS * CS * 32];
+    __shared__ __attribute__((aligned(16))) uint16_t Gq[CH * LDG];
+    __shared__ __attribute__((aligned(16))) uint16_t Gk[CH * LDG];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[CH * LDV];
+    __shared__ __attribute__((aligned(16))) uint16_t Ss[CH * LDSS];
+    __shared__ float den_inter[CH];
+    __shared__ float den_part[SUB][CH];
+    __shared__ float Zs[Kp];
+
+    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
+    const int g4 = l >> 4, i16 = l & 15;
+    const int cs = wave % CS, ts = wave / CS;
+    const int64_t p = blockIdx.y;
+    const int seg_idx = blockIdx.x;
+    const int h = int(p % H);
+
+    WaveParams<DR, CTW> P;
+    P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * CTW);
+    const uint16_t* Xq = XQ + size_t(p) * N * DR;
+    const uint16_t* Xk = XK + size_t(p) * N * DR;
+    const uint16_t* Vp = V + size_t(p) * N * DV;
+    const int64_t lo = int64_t(seg_idx) * seg, hi = min<int64_t>(lo + seg, N);
+
+    // starting memory of the segment
+    const float* pre = prefix + (size_t(p) * G + seg_idx) * size_t(Kp) * (DV + 1);
+    f32x4 mem[CPW][KT16];
+#pragma unroll
+    for (int cc = 0; cc < CPW; ++cc) {
+        const int c16 = wave + cc * NW;
+#pragma unroll
+        for (int kt = 0; kt < KT16; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                mem[cc][kt][r] = (c16 < C16) ? pre[size_t(kt * 16 + 4 * g4 + r) * DV + c16 * 16 + i16] : 0.0f;
+    }
+    for (int k = threadIdx.x; k < Kp; k += NW * 64) Zs[k] = pre[size_t(Kp) * DV + k];
+
+    for (int64_t nc = lo; nc < hi; nc += CH) {
+        __syncthreads();  // B0: previous chunk's tiles consumed, Zs updated
+        // ---- phase L: scores and softmax of the chunk's query and key rows
+        float zr[CTW][16];
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) zr[ct][r] = Zs[(cs * CTW + ct) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)];
+        // value rows of the chunk -> LDS (rows past the segment read as zero)
+        for (int c = threadIdx.x; c < CH * DV / 8; c += NW * 64) {
+            const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (nc + row < hi) v = *reinterpret_cast<const u32x4*>(Vp + (nc + row) * DV + col);
+            *reinterpret_cast<u32x4*>(Vs + row * LDV + col) = v;
+        }
+        // score jobs in groups of JG (one statistics barrier per group)
+#pragma unroll
+        for (int jg = 0; jg < JPW; jg += JG) {
+            f32x16 acc[JG][CTW];
+            float sm[JG], sL[JG], sD[JG];
+            int valid_j[JG];
+#pragma unroll
+            for (int u = 0; u < JG; ++u) {
+                const int jj = jg + u;
+                const int job = ts + jj * TS;
+                const bool is_q = job < SUB;
+                const int sub = is_q ? job : job - SUB;
+                const int64_t n0 = nc + sub * 32;
+                valid_j[u] = (jj < JPW && job < JOBS) ? int(max<int64_t>(0, min<int64_t>(32, hi - n0))) : 0;
+                scores<DR, CTW>(P, is_q ? Xq : Xk, n0, valid_j[u], acc[u]);
+                local_softmax<CTW, true>(acc[u], zr, sm[u], sL[u], sD[u]);
+                if (CS > 1 && lh == 0 && jj < JPW) st[jj][(ts * CS + cs) * 32 + j] = ScanStats{sm[u], sL[u], sD[u]};
+            }
+            if (CS > 1) __syncthreads();  // B1: this group's softmax statistics published
+#pragma unroll
+            for (int u = 0; u < JG; ++u) {
+                const int jj = jg + u;
+                const int job = ts + jj * TS;
+                if (jj >= JPW || job >= JOBS) continue;
+                const bool is_q = job < SUB;
+                const int sub = is_q ? job : job - SUB;
+                float scale, dl;
+                if (CS == 1) {
+                    scale = 1.0f / sL[u];
+                    dl = sD[u] / sL[u];
+                } else {
+                    float mm = -INFINITY;
+#pragma unroll
+                    for (int c = 0; c < CS; ++c) mm = fmaxf(mm, st[jj][(ts * CS + c) * 32 + j].m);
+                    float Lt = 0.0f, Dt = 0.0f;
+#pragma unroll
+                    for (int c = 0; c < CS; ++c) {
+                        const ScanStats s = st[jj][(ts * CS + c) * 32 + j];
+                        const float f = __builtin_amdgcn_exp2f(s.m - mm);
+                        Lt = fmaf(s.L, f, Lt);
+                        Dt = fmaf(s.D, f, Dt);
+                    }
+                    scale = __builtin_amdgcn_exp2f(sm[u] - mm) / Lt;
+                    dl = Dt / Lt;
+                }
+                if (j >= valid_j[u]) scale = 0.0f;
+                store_gamma_lds<CTW>(acc[u], scale, is_q ? Gq : Gk, LDG, sub * 32 + j, cs * CTW);
+                if (is_q && cs == 0 && lh == 0) den_inter[sub * 32 + j] = dl;
+            }
+        }
+        __syncthreads();  // B2: Gq, Gk, Vs complete
+        // ---- phase S: S^T tiles (rows = key positions, cols = query positions)
+        if (wave < STILES) {
+            int qt = 0, kt = wave;
+            while (kt > qt) { kt -= qt + 1; ++qt; }
+            f32x16 s;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < Kp / 16; ++ks) {
+                bf16x8 a = read_rowfrag(Gk, LDG, kt * 32 + j, 16 * ks);
+                bf16x8 b = read_rowfrag(Gq, LDG, qt * 32 + j, 16 * ks);
+                s = mfma(a, b, s);
+            }
+            float rs = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = kt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (kk > qt * 32 + j) s[r] = 0.0f;  // j > i is outside the causal support
+                rs += s[r];
+            }
+            rs = xsum32(rs);
+            if (lh == 0) den_part[kt][qt * 32 + j] = rs;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                u32x2 v;
+                v[0] = pack_bf16x2(s[4 * q + 0], s[4 * q + 1]);
+                v[1] = pack_bf16x2(s[4 * q + 2], s[4 * q + 3]);
+                *reinterpret_cast<u32x2*>(Ss + (qt * 32 + j) * LDSS + kt * 32 + 8 * q + 4 * lh) = v;
+            }
+        }
+        __syncthreads();  // B3: S tiles and row sums complete
+        // ---- phase O: outputs of this wave's value columns, then the memory update
+#pragma unroll
+        for (int cc = 0; cc < CPW; ++cc) {
+            const int c16 = wave + cc * NW;
+            if (c16 >= C16) continue;
+            f32x4 o[CH / 16];
+#pragma unroll
+            for (int t16 = 0; t16 < CH / 16; ++t16) {
+                o[t16] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                // intra-chunk part: V^T S^T over key positions up to this query tile
+#pragma unroll
+                for (int ks = 0; ks < (t16 * 16 + 16 + 31) / 32; ++ks) {
+                    bf16x8 a = read_colfrag16(Vs, LDV, 32 * ks, c16 * 16);
+                    bf16x8 b = *reinterpret_cast<const bf16x8*>(Ss + (t16 * 16 + i16) * LDSS + 32 * ks + 8 * g4);
+                    o[t16] = mfma16(a, b, o[t16]);
+                }
+            }
+            // inter-chunk part: memory^T Gq^T, memory split into hi + lo bf16 once per k-step
+#pragma unroll
+            for (int m2 = 0; m2 < Kp / 32; ++m2) {
+                u32x4 ah, al;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int v0 = 2 * q, v1 = 2 * q + 1;
+                    const float x0 = mem[cc][2 * m2 + (v0 >> 2)][v0 & 3];
+                    const float x1 = mem[cc][2 * m2 + (v1 >> 2)][v1 & 3];
+                    const uint16_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
+                    ah[q] = uint32_t(h0) | (uint32_t(h1) << 16);
+                    al[q] = pack_bf16x2(x0 - bf16_bits_to_f32(h0), x1 - bf16_bits_to_f32(h1));
+                }
+#pragma unroll
+                for (int t16 = 0; t16 < CH / 16; ++t16) {
+                    const int qrow = t16 * 16 + i16;
+                    const u32x2 b0 = *reinterpret_cast<const u32x2*>(Gq + qrow * LDG + 32 * m2 + 4 * g4);
+                    const u32x2 b1 = *reinterpret_cast<const u32x2*>(Gq + qrow * LDG + 32 * m2 + 16 + 4 * g4);
+                    const bf16x8 b = __builtin_bit_cast(bf16x8, u32x4{b0[0], b0[1], b1[0], b1[1]});
+                    o[t16] = mfma16(__builtin_bit_cast(bf16x8, ah), b, o[t16]);
+                    o[t16] = mfma16(__builtin_bit_cast(bf16x8, al), b, o[t16]);
+                }
+            }
+#pragma unroll
+            for (int t16 = 0; t16 < CH / 16; ++t16) {
+                const int qrow = t16 * 16 + i16;
+                const int64_t tok = nc + qrow;
+                if (tok < hi) {
+                    float den = den_inter[qrow] + eps;
+#pragma unroll
+                    for (int kt = 0; kt < SUB; ++kt)
+                        if (kt * 32 <= qrow) den += den_part[kt][qrow];
+                    const float rden = 1.0f / den;
+                    u32x2 v;
+                    v[0] = pack_bf16x2(o[t16][0] * rden, o[t16][1] * rden);
+                    v[1] = pack_bf16x2(o[t16][2] * rden, o[t16][3] * rden);
+                    *reinterpret_cast<u32x2*>(O + (size_t(p) * N + tok) * DV + c16 * 16 + 4 * g4) = v;
+                }
+            }
+        }
+        // memory update: Vt += Gk^T Vc (every wave its columns), Z += Gk^T 1 (wave 0)
+        float zacc[KT16];
+#pragma unroll
+        for (int kt = 0; kt < KT16; ++kt) zacc[kt] = 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < KT16; ++kt)
+#pragma unroll
+            for (int ks = 0; ks < CH / 32; ++ks) {
+                const bf16x8 a = read_colfrag16(Gk, LDG, 32 * ks, kt * 16);
+                if (wave == 0) {
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) zacc[kt] += float(a[v]);
+                }
+#pragma unroll
+                for (int cc = 0; cc < CPW; ++cc) {
+                    const int c16 = wave + cc * NW;
+                    if (c16 < C16) {
+                        const bf16x8 b = read_colfrag16(Vs, LDV, 32 * ks, c16 * 16);
+                        mem[cc][kt] = mfma16(a, b, mem[cc][kt]);
+                    }
+                }
+            }
+        if (wave == 0) {
+#pragma unroll
+            for (int kt = 0; kt < KT16; ++kt) {
+                float z = zacc[kt];
+                z += __shfl_xor(z, 16, 64);
+                z += __shfl_xor(z, 32, 64);
+                if (g4 == 0) Zs[kt * 16 + i16] += z;
+            }
+        }
+    }
+}
+
+template <typename F>
+hipError_t with_all(int dr, int kt, int vt, int ch, F&& f) {
+#define GMA_SCAN_CH(D, T, W)                                                                                    \
+    if (dr == D && kt == T && vt == W && ch == 32)                                                              \
+        return f(std::integral_constant<int, D>(), std::integral_constant<int, T>(), std::integral_constant<int, W>(), \
+                 std::integral_constant<int, 32>());                                                            \
+    if (dr == D && kt == T && vt == W && ch == 64)                                                              \
+        return f(std::integral_constant<int, D>(), std::integral_constant<int, T>(), std::integral_constant<int, W>(), \
+                 std::integral_constant<int, 64>());
+#define GMA_SCAN_VT(D, T) GMA_SCAN_CH(D, T, 1) GMA_SCAN_CH(D, T, 2) GMA_SCAN_CH(D, T, 4)
+#define GMA_SCAN_KT(D) GMA_SCAN_VT(D, 1) GMA_SCAN_VT(D, 2) GMA_SCAN_VT(D, 4) GMA_SCAN_VT(D, 8)
+    GMA_SCAN_KT(16) GMA_SCAN_KT(32) GMA_SCAN_KT(64) GMA_SCAN_KT(128)
+#undef GMA_SCAN_KT
+#undef GMA_SCAN_VT
+#undef GMA_SCAN_CH
     return hipErrorNotSupported;
 }
+
+}  // namespace bf
+
+// The bf16 scan works on 32-position score subtiles, so a requested chunk of 16
+// positions runs as 32 (the chunk length only changes the order of the sums).
+hipError_t bf16_scan(const Plan& p, const void* XQ, const void* XK, const void* V, const uint16_t* planes,
+                     const float* cvec, float eps, void* O, char* ws, hipStream_t st) {
+    const float* prefix = reinterpret_cast<const float*>(ws + p.off_partials);
+    const int ch = p.chunk < 32 ? 32 : p.chunk;
+    return bf::with_all(int(p.dr), int(p.Kp / 32), int(p.dv / 32), ch, [&](auto D, auto T, auto W, auto C) {
+        constexpr int DR = decltype(D)::value, KT = decltype(T)::value, VT = decltype(W)::value,
+                      CH = decltype(C)::value;
+        using S = bf::Split<DR, KT>;
+        GMA_LAUNCH("bf16_scan", (bf::scan_kernel<DR, KT, VT, CH>), dim3(unsigned(p.G), unsigned(p.P)),
+                   dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
+                   static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), planes, cvec, prefix, eps,
+                   static_cast<uint16_t*>(O));
+        return hipGetLastError();
+    });
+}
+
 }  // namespace gma

@@ -342,7 +342,7 @@ hipError_t launch_params(const Plan& p, const float* s2, const float* pi, char* 
     hipError_t e0 = allow_lds();
     if (e0 != hipSuccess) return e0;
     F32Params v = f32_params_view(p, ws);
-    hipLaunchKernelGGL(f32_params_kernel, dim3(unsigned(p.H)), dim3(kThreads), 0, st, s2, pi, int(p.K),
+    GMA_LAUNCH("f32_params", f32_params_kernel, dim3(unsigned(p.H)), dim3(kThreads), 0, st, s2, pi, int(p.K),
                        int(p.dr), const_cast<double*>(v.c), const_cast<double*>(v.inv));
     return hipGetLastError();
 }
@@ -357,7 +357,7 @@ hipError_t f32_responsibilities(const Plan& p, const float* X, const float* mu, 
     F32Params v = f32_params_view(p, ws);
     size_t lds = size_t(kTile) * (p.dr + p.K) * sizeof(float);
     dim3 grid(unsigned((p.N + kTile - 1) / kTile), unsigned(p.P));
-    hipLaunchKernelGGL(f32_resp_kernel, grid, dim3(kThreads), lds, st, X, p.N, int(p.H), int(p.dr),
+    GMA_LAUNCH("f32_resp", f32_resp_kernel, grid, dim3(kThreads), lds, st, X, p.N, int(p.H), int(p.dr),
                        int(p.K), v.c, v.inv, mu, Gamma, gamma_dtype == GMA_BF16 ? 1 : 0);
     return hipGetLastError();
 }
@@ -371,15 +371,15 @@ hipError_t f32_bidir(const Plan& p, const float* XQ, const float* XK, const floa
     float* memory = reinterpret_cast<float*>(ws + p.off_memory);
     const int E = int(p.K * (p.dv + 1));
     size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
-    hipLaunchKernelGGL(f32_write_kernel, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads), lds_w, st, XK, V,
+    GMA_LAUNCH("f32_write", f32_write_kernel, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads), lds_w, st, XK, V,
                        p.N, int(p.H), int(p.dr), int(p.dv), int(p.K), p.seg, int(p.G), v.c, v.inv, mu,
                        partials);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(f32_combine_kernel, dim3(unsigned((E + kThreads - 1) / kThreads), unsigned(p.P)),
+    GMA_LAUNCH("f32_combine", f32_combine_kernel, dim3(unsigned((E + kThreads - 1) / kThreads), unsigned(p.P)),
                        dim3(kThreads), 0, st, partials, int(p.G), E, memory);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     size_t lds_r = size_t(kTile) * (p.dr + p.K + 1) * sizeof(float);
-    hipLaunchKernelGGL(f32_read_kernel, dim3(unsigned((p.N + kTile - 1) / kTile), unsigned(p.P)),
+    GMA_LAUNCH("f32_read", f32_read_kernel, dim3(unsigned((p.N + kTile - 1) / kTile), unsigned(p.P)),
                        dim3(kThreads), lds_r, st, XQ, p.N, int(p.H), int(p.dr), int(p.dv), int(p.K), v.c,
                        v.inv, mu, memory, eps, O);
     return hipGetLastError();
@@ -394,20 +394,20 @@ hipError_t f32_causal(const Plan& p, const float* XQ, const float* XK, const flo
     const int E = int(p.K * (p.dv + 1));
     if (p.G > 1) {
         size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
-        hipLaunchKernelGGL(f32_write_kernel, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads), lds_w, st, XK,
+        GMA_LAUNCH("f32_write", f32_write_kernel, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads), lds_w, st, XK,
                            V, p.N, int(p.H), int(p.dr), int(p.dv), int(p.K), p.seg, int(p.G), v.c, v.inv, mu,
                            partials);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // With one segment the aggregate pass is skipped: the prefix kernel writes the
     // starting memory of segment 0 as zeros without reading the aggregate.
-    hipLaunchKernelGGL(f32_prefix_kernel, dim3(unsigned((E + kThreads - 1) / kThreads), unsigned(p.P)),
+    GMA_LAUNCH("f32_prefix", f32_prefix_kernel, dim3(unsigned((E + kThreads - 1) / kThreads), unsigned(p.P)),
                        dim3(kThreads), 0, st, partials, int(p.G), E);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // The chunk length is a tiling choice; halve it until the chunk's tiles fit in LDS.
     int C = p.chunk;
     while (C > 8 && scan_lds_bytes(C, int(p.dr), int(p.dv), int(p.K)) > kMaxLds) C /= 2;
-    hipLaunchKernelGGL(f32_scan_kernel, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads),
+    GMA_LAUNCH("f32_scan", f32_scan_kernel, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads),
                        scan_lds_bytes(C, int(p.dr), int(p.dv), int(p.K)), st, XQ, XK, V, p.N, int(p.H),
                        int(p.dr), int(p.dv), int(p.K), p.seg, int(p.G), C, v.c, v.inv, mu, partials, eps, O);
     return hipGetLastError();

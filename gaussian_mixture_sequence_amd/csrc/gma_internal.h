@@ -33,6 +33,19 @@ struct Plan {
     size_t params_bytes, partials_bytes, memory_bytes;
 };
 
+// Kernel timing hooks (see gma_profiling in gma.h).  Launchers bracket each launch with
+// trace_begin / trace_end; both are no-ops unless profiling is enabled.
+void trace_begin(hipStream_t st, const char* name);
+void trace_end(hipStream_t st);
+
+// hipLaunchKernelGGL bracketed by the timing hooks; `name` must be a string literal.
+#define GMA_LAUNCH(name, kernel, grid, block, lds, stream, ...)                   \
+    do {                                                                         \
+        ::gma::trace_begin(stream, name);                                        \
+        hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);       \
+        ::gma::trace_end(stream);                                                \
+    } while (0)
+
 // Fills `plan`; returns GMA_OK or the validation error for unsupported sizes.
 gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_t chunk, Plan* plan);
 

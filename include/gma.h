@@ -23,8 +23,9 @@
  * Dtypes      X_Q, X_K, V and O share one I/O dtype (GMA_F32 or GMA_BF16).  The
  *             parameters mu, sigma2, pi are always fp32.  eps is fp32.
  * Memory      Every pointer is a device pointer (HBM) owned by the caller.  The library
- *             never allocates or frees device memory and keeps no state between calls;
- *             scratch space is the caller's workspace (size from gma_workspace_size).
+ *             never allocates or frees device memory and keeps no state between calls
+ *             (apart from the optional kernel-timing record, gma_profiling); scratch
+ *             space is the caller's workspace (size from gma_workspace_size).
  *             O and Gamma must not overlap any input or the workspace.
  * Alignment   Tensor pointers and the workspace must be 16-byte aligned
  *             (GMA_ERR_MISALIGNED otherwise).
@@ -138,6 +139,26 @@ gma_status_t gma_forward_causal(const void* XQ, const void* XK, const void* V,
                                 const float* mu, const float* sigma2, const float* pi,
                                 float eps, void* O, const gma_shape_t* shape, int32_t chunk,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Kernel timing (optional tracing).  While enabled, every kernel the library launches is
+ * bracketed by a pair of hipEvents recorded on the launch stream; gma_profiling_collect
+ * waits for the recorded events, adds each launch's elapsed time to a per-kernel total,
+ * writes up to `capacity` entries (kernel name, launches, total milliseconds) and
+ * clears the record.  Names are static strings owned by the library.  Events are host
+ * objects created and destroyed by the library (no device memory).  Recording adds one
+ * event packet before and after each launch.  Not thread-safe against concurrent calls
+ * from other host threads while enabled.
+ *   gma_profiling(1) enables, gma_profiling(0) disables and drops anything uncollected.
+ */
+typedef struct {
+    const char* name;
+    int64_t launches;
+    double total_ms;
+} gma_kernel_stat_t;
+
+gma_status_t gma_profiling(int enable);
+gma_status_t gma_profiling_collect(gma_kernel_stat_t* stats, int capacity, int* count);
 
 #ifdef __cplusplus
 }

@@ -159,3 +159,69 @@ def test_bf16_bidir_deterministic():
     a = to_np(run_gpu(w, inp))
     b = to_np(run_gpu(w, inp))
     assert np.array_equal(a, b)
+
+
+BF16_CAUSAL_CASES = [
+    bf16_case(causal=True, B=1, H=2, N=700, seed=51),                                   # B8H12 dims, short
+    bf16_case(causal=True, B=1, H=1, N=600, d_r=64, d_v=128, K=256, seed=52),           # long-causal dims
+    bf16_case(causal=True, B=1, H=2, N=300, d_r=16, d_v=32, K=8, chunk=32, seed=53),    # K padded, chunk 32
+    bf16_case(causal=True, B=1, H=1, N=1, seed=54),                                     # single token
+    bf16_case(causal=True, B=2, H=1, N=3001, d_r=32, d_v=64, K=128, chunk=64, seed=55),  # several segments
+    bf16_case(causal=True, B=1, H=1, N=260, d_r=128, d_v=128, K=256, seed=56),          # maximum dims
+    bf16_case(causal=True, B=1, H=1, N=777, d_r=64, d_v=32, K=50, chunk=16, seed=57),   # ragged, chunk 16
+]
+
+
+@pytest.mark.parametrize("w", BF16_CAUSAL_CASES, ids=case_id)
+def test_bf16_causal_parity(w):
+    inp = make_inputs(w)
+    out = run_gpu(w, inp)
+    assert out.dtype == torch.bfloat16 and out.shape == (w.B, w.H, w.N, w.d_v)
+    err = row_scaled_error(to_np(out), run_oracle(w, inp))
+    assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("name,heads", [("causal_b8h12_n2048", [(0, 0), (7, 11)]),
+                                        ("causal_long_n32768", [(1, 15)])])
+def test_bf16_causal_full_size_sampled(name, heads):
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    out = run_gpu(w, inp)
+    assert torch.isfinite(out.float()).all()
+    err = sampled_heads(w, inp, out, heads)
+    assert err <= TOL["bf16"], err
+
+
+def test_bf16_causal_prefix_invariance_and_determinism():
+    """Output rows <= i are bit-identical when inputs after i change (Sec. 3.5 causality);
+    two runs on the same inputs are bit-identical."""
+    w = bf16_case(causal=True, B=1, H=2, N=2500, seed=58)
+    inp = make_inputs(w)
+    a = to_np(run_gpu(w, inp))
+    assert np.array_equal(a, to_np(run_gpu(w, inp)))
+    for i in (100, 1337):
+        pert = {k: v.clone() for k, v in inp.items()}
+        g = torch.Generator().manual_seed(i)
+        for k in ("xq", "xk", "v"):
+            pert[k][:, :, i + 1:] = torch.randn(pert[k][:, :, i + 1:].shape, generator=g).to(pert[k].dtype)
+        c = to_np(run_gpu(w, pert))
+        assert np.array_equal(c[:, :, :i + 1], a[:, :, :i + 1])
+        assert not np.array_equal(c[:, :, i + 1:], a[:, :, i + 1:])
+
+
+def test_bf16_causal_chunk_invariance():
+    """The chunk length only reorders sums: results for chunk 32 and 64 agree to tolerance."""
+    w = bf16_case(causal=True, B=1, H=2, N=1000, seed=59)
+    inp = make_inputs(w)
+    a = to_np(run_gpu(w, inp, chunk=32))
+    b = to_np(run_gpu(w, inp, chunk=64))
+    assert row_scaled_error(a, b) <= 1e-2
+
+
+def test_bf16_causal_last_row_matches_bidir():
+    """At the last position the causal prefix memory is the full memory (Eq. 6b vs Eq. 6)."""
+    w = bf16_case(causal=True, B=1, H=2, N=1500, seed=60)
+    inp = make_inputs(w)
+    c = to_np(run_gpu(w, inp))
+    b = to_np(run_gpu(w.with_(causal=False), inp))
+    assert row_scaled_error(c[:, :, -1:], b[:, :, -1:]) <= 1e-2
