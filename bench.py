@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Throughput benchmark of the GMA forward (bidirectional and causal) on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input: the
+bidirectional forward on the B=8, H=8, N=4096 workload (d_r=64, d_v=64, K=64) and the
+causal forward on the B=8, H=12, N=2048 workload (d_r=64, d_v=64, K=32, chunk 64), both
+bf16 I/O with fp32 accumulation.  Inputs are resident in HBM before timing starts and
+rotate over several independent input sets (more bytes than the 256 MB Infinity Cache)
+so that every step reads from HBM.
+
+Output: one JSON line with the whole-step throughput (tokens/s), the roofline fraction
+of the dominant kernel (per-kernel times from the library's hipEvent hooks, taken in a
+second pass over the same steps) and the oracle timed on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GMA forward tokens/s (bidir & causal) + achieved HBM GB/s / MFMA % of peak"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+DEFAULT_STEP = ["bidir_b8h8_n4096", "causal_b8h12_n2048"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=3, help="independent input sets rotated over the steps")
+    ap.add_argument("--workloads", default=",".join(DEFAULT_STEP),
+                    help="comma-separated workload names that make up one step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def alg_bytes_per_token_head(w, kernel: str) -> float:
+    """Algorithmic HBM bytes per (token, head) that a kernel must move."""
+    e = 2 if w.dtype == "bf16" else 4
+    if kernel.endswith("_write") or kernel.endswith("_causal_aggregate"):
+        return e * (w.d_r + w.d_v)          # X_K and V in
+    if kernel.endswith("_read"):
+        return e * (w.d_r + w.d_v)          # X_Q in, O out
+    if kernel.endswith("_scan"):
+        return e * (2 * w.d_r + 2 * w.d_v)  # X_Q, X_K, V in, O out
+    return 0.0
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this implementation runs on a single GPU; --gpus %d is not supported "
+              "(multi-GPU sharding is a design note only)" % args.gpus, file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+    from gaussian_mixture_sequence_amd import binding as gb
+    from gaussian_mixture_sequence_amd.inputs import WORKLOADS, make_inputs
+
+    gb.load()  # raises if libgma.so is missing: there is no fallback path
+    names = [n for n in args.workloads.split(",") if n]
+    ws_list = [WORKLOADS[n] for n in names]
+    dev = torch.device("cuda:0")
+
+    # ---- inputs resident in HBM: `sets` independent input sets per workload
+    sets = []   # sets[s][i] = dict of device tensors for workload i
+    for s in range(args.sets):
+        row = []
+        for w in ws_list:
+            inp = make_inputs(w, seed=w.seed + 1000 * s)
+            row.append({k: v.to(dev) for k, v in inp.items()})
+        sets.append(row)
+    outs, wss = [], []
+    for i, w in enumerate(ws_list):
+        dt = sets[0][i]["xq"].dtype
+        outs.append([torch.empty(w.B, w.H, w.N, w.d_v, dtype=dt, device=dev) for _ in range(args.sets)])
+        op = gb.GMA_OP_CAUSAL if w.causal else gb.GMA_OP_BIDIR
+        io = gb.GMA_BF16 if w.dtype == "bf16" else gb.GMA_F32
+        nbytes = gb.gma_workspace_size(op, w.B, w.H, w.N, w.d_r, w.d_v, w.K, io, w.chunk)
+        wss.append(torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev))
+    stream = torch.cuda.current_stream()
+
+    def step(k: int) -> None:
+        s = k % args.sets
+        for i, w in enumerate(ws_list):
+            d = sets[s][i]
+            if w.causal:
+                gb.gma_forward_causal(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps,
+                                      chunk=w.chunk, out=outs[i][s], workspace=wss[i], stream=stream)
+            else:
+                gb.gma_forward_bidir(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps,
+                                     out=outs[i][s], workspace=wss[i], stream=stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps between two synchronisations
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for k in range(args.steps):
+        step(k)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dev_ms = ev0.elapsed_time(ev1)
+    tokens_per_step = sum(w.B * w.N for w in ws_list)
+    value = tokens_per_step * args.steps / wall
+
+    # ---- per-kernel durations: the same steps again with the library's hipEvent hooks
+    gb.gma_profiling(True)
+    torch.cuda.synchronize()
+    tp0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    prof_wall = time.perf_counter() - tp0
+    kstats = gb.gma_profiling_collect()
+    gb.gma_profiling(False)
+
+    # which workload launches which kernel (names are unique per op)
+    kernel_of = {}
+    for w in ws_list:
+        pre = "bf16" if w.dtype == "bf16" else "f32"
+        ks = ["params", "scan", "causal_aggregate", "prefix"] if w.causal else ["params", "write", "combine", "read"]
+        for k in ks:
+            kernel_of.setdefault("%s_%s" % (pre, k), []).append(w)
+    kernels = {}
+    for name, (launches, total_ms) in kstats.items():
+        avg_us = 1000.0 * total_ms / max(launches, 1)
+        entry = {"launches": launches, "avg_us": round(avg_us, 3)}
+        owners = kernel_of.get(name, [])
+        if len(owners) == 1:
+            w = owners[0]
+            per_launch = alg_bytes_per_token_head(w, name) * w.B * w.H * w.N
+            if per_launch:
+                entry["alg_bytes_per_launch"] = int(per_launch)
+                entry["alg_GBps"] = round(per_launch / (avg_us * 1e-6) / 1e9, 1)
+        kernels[name] = entry
+    dominant = max(kstats.items(), key=lambda kv: kv[1][1])[0] if kstats else None
+    roofline = None
+    if dominant and "alg_GBps" in kernels[dominant]:
+        ach = kernels[dominant]["alg_GBps"]
+        roofline = {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "avg_us": kernels[dominant]["avg_us"],
+                    "alg_bytes_per_launch": kernels[dominant]["alg_bytes_per_launch"]}
+
+    # ---- sanity: outputs finite
+    for i in range(len(ws_list)):
+        if not torch.isfinite(outs[i][0].float()).all():
+            print("bench.py: non-finite output in %s" % names[i], file=sys.stderr)
+            return 1
+
+    step_bytes = sum(w.B * w.H * w.N * alg_bytes_per_token_head(w, "bf16_scan") for w in ws_list)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1000.0 * wall / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; mu~N(0,1), sigma2=softplus(N(0,1))+1e-3, pi=softmax(N(0,1)), "
+                "X_Q,X_K,V~N(0,1); %d rotating input sets)" % args.sets,
+        "config": {
+            "workload": " + ".join("%s (%s B=%d H=%d N=%d d_r=%d d_v=%d K=%d%s)" % (
+                w.name, "causal" if w.causal else "bidir", w.B, w.H, w.N, w.d_r, w.d_v, w.K,
+                ", chunk=%d" % w.chunk if w.causal else "") for w in ws_list),
+            "tokens_per_step": tokens_per_step,
+            "eps": 1e-6,
+        },
+        "device_ms_per_step": round(dev_ms / args.steps, 4),
+        "step_alg_hbm_GBps": round(step_bytes / (wall / args.steps) / 1e9, 1),
+        "step_alg_hbm_frac": round(step_bytes / (wall / args.steps) / 1e9 / HBM_PEAK_GBPS, 4),
+        "roofline": roofline,
+        "kernels": kernels,
+        "profiled_ms_per_step": round(1000.0 * prof_wall / args.steps, 4),
+    }
+
+    # ---- the oracle on the host cores, same workload (first input set), fp64
+    if not args.no_cpu_baseline:
+        import oracle
+        cpu_inputs = []
+        for w in ws_list:
+            inp = make_inputs(w)
+            cpu_inputs.append((w, {k: oracle._f64(v) for k, v in inp.items()}))
+        tc = time.perf_counter()
+        for w, d in cpu_inputs:
+            fn = oracle.forward_causal if w.causal else oracle.forward_bidir
+            fn(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps)
+        cpu_s = time.perf_counter() - tc
+        result["cpu_baseline"] = {
+            "value": round(tokens_per_step / cpu_s, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "one full step (all %d tokens of every workload), fp64 C oracle with OpenMP over "
+                      "(batch, head); %.2f s wall" % (tokens_per_step, cpu_s)}
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

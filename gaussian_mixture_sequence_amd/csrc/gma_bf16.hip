@@ -457,7 +457,7 @@ hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, cha
         return bf::with_vt(int(p.dv / 32), [&](auto VV) {
             constexpr int VT = decltype(VV)::value;
             using S = bf::Split<DR, KT>;
-            GMA_LAUNCH("bf16_write", (bf::write_kernel<DR, KT, VT>), dim3(unsigned(p.G), unsigned(p.P)), dim3(S::NW * 64), 0,
+            GMA_LAUNCH(p.op == GMA_OP_CAUSAL ? "bf16_causal_aggregate" : "bf16_write", (bf::write_kernel<DR, KT, VT>), dim3(unsigned(p.G), unsigned(p.P)), dim3(S::NW * 64), 0,
                                st, static_cast<const uint16_t*>(XK), static_cast<const uint16_t*>(V), p.N, int(p.H),
                                p.seg, int(p.G), v.planes, v.cvec, partials);
             return hipGetLastError();

@@ -394,7 +394,7 @@ hipError_t f32_causal(const Plan& p, const float* XQ, const float* XK, const flo
     const int E = int(p.K * (p.dv + 1));
     if (p.G > 1) {
         size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
-        GMA_LAUNCH("f32_write", f32_write_kernel, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads), lds_w, st, XK,
+        GMA_LAUNCH("f32_causal_aggregate", f32_write_kernel, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads), lds_w, st, XK,
                            V, p.N, int(p.H), int(p.dr), int(p.dv), int(p.K), p.seg, int(p.G), v.c, v.inv, mu,
                            partials);
         if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -38,7 +38,7 @@ struct Plan {
 void trace_begin(hipStream_t st, const char* name);
 void trace_end(hipStream_t st);
 
-// hipLaunchKernelGGL bracketed by the timing hooks; `name` must be a string literal.
+// hipLaunchKernelGGL bracketed by the timing hooks; `name` must be a static string.
 #define GMA_LAUNCH(name, kernel, grid, block, lds, stream, ...)                   \
     do {                                                                         \
         ::gma::trace_begin(stream, name);                                        \
