@@ -8,10 +8,11 @@
 //             the chip: scores -> softmax in registers -> bf16 tile in LDS -> MFMA
 //   combine   bidirectional: fixed-order sum of the partials, then Vt split into hi + lo
 //             bf16 planes stored transposed (the A operand of the read) and Z in fp32
-//   prefix    causal: exclusive prefix of the segment aggregates (starting memories)
 //   read      O = Gamma_Q Vt / (Gamma_Q Z + eps) (Eq. 7-8): computed as O^T = Vt^T Gamma_Q^T
 //             with hi + lo Vt, the denominator in fp32 on the VALU during the softmax
-//   scan      causal chunked scan (gma_bf16_scan.hip)
+//   aggregate causal: the write kernel over segments 0 .. G-2 (segment aggregates)
+//   scan      causal chunked scan (gma_bf16_scan.hip); segment s starts from the sum of
+//             the aggregates of segments 0 .. s-1
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -24,20 +25,41 @@ namespace bf {
 
 // ---------------------------------------------------------------------------- params
 
+// One wave per component k (grid: (Kp / 4, H), 4 waves per block).  Planes of row k and
+// c_k = log2(e) * (log pi_k - 1/2 sum_d (log sigma2_kd + mu_kd^2 / sigma2_kd)) in fp64,
+// shifted by c_0 of the same head: a k-independent shift, exact in the softmax, that
+// removes the common offset before the value is rounded to fp32.  Padded components
+// (k >= K) get zero planes and c = -inf, i.e. responsibility exactly 0.
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ double score_constant(const float* mu_k, const float* s2_k, float pi_k, int dr) {
+    double acc = 0.0;
+    for (int d = threadIdx.x & 63; d < dr; d += 64) {
+        const double v = double(s2_k[d]), m = double(mu_k[d]);
+        acc += log(v) + m * m / v;
+    }
+    return log(double(pi_k)) - 0.5 * wave_sum_f64(acc);
+}
+
 __global__ void __launch_bounds__(256) params_kernel(const float* __restrict__ mu, const float* __restrict__ s2,
                                                      const float* __restrict__ pi, int K, int Kp, int dr,
                                                      uint16_t* __restrict__ planes, float* __restrict__ cvec) {
-    const int h = blockIdx.x;
-    __shared__ double cd[256];
-    __shared__ double red[4];
     const double L2E = 1.4426950408889634;
+    const int h = blockIdx.y;
+    const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (k >= Kp) return;
     uint16_t* ph = planes + size_t(h) * 4 * Kp * dr;
-    for (int idx = threadIdx.x; idx < Kp * dr; idx += 256) {
-        const int k = idx / dr, d = idx - k * dr;
+    const float* mu_h = mu + size_t(h) * K * dr;
+    const float* s2_h = s2 + size_t(h) * K * dr;
+    for (int d = threadIdx.x & 63; d < dr; d += 64) {
         double a = 0.0, b = 0.0;
         if (k < K) {
-            const double inv = 1.0 / double(s2[(size_t(h) * K + k) * dr + d]);
-            a = double(mu[(size_t(h) * K + k) * dr + d]) * inv * L2E;
+            const double inv = 1.0 / double(s2_h[size_t(k) * dr + d]);
+            a = double(mu_h[size_t(k) * dr + d]) * inv * L2E;
             b = -0.5 * inv * L2E;
         }
         const uint16_t ah = f32_to_bf16_bits(float(a)), bh = f32_to_bf16_bits(float(b));
@@ -48,22 +70,13 @@ __global__ void __launch_bounds__(256) params_kernel(const float* __restrict__ m
         ph[(size_t(2) * Kp + k) * dr + d] = bh;
         ph[(size_t(3) * Kp + k) * dr + d] = bl;
     }
-    double local_max = -INFINITY;
-    for (int k = threadIdx.x; k < K; k += 256) {
-        double acc = log(double(pi[size_t(h) * K + k]));
-        for (int d = 0; d < dr; ++d) {
-            const double v = double(s2[(size_t(h) * K + k) * dr + d]);
-            const double m = double(mu[(size_t(h) * K + k) * dr + d]);
-            acc -= 0.5 * (log(v) + m * m / v);
-        }
-        cd[k] = acc * L2E;
-        local_max = fmax(local_max, cd[k]);
+    if (k < K) {
+        const double ck = score_constant(mu_h + size_t(k) * dr, s2_h + size_t(k) * dr, pi[size_t(h) * K + k], dr);
+        const double c0 = score_constant(mu_h, s2_h, pi[size_t(h) * K], dr);
+        if ((threadIdx.x & 63) == 0) cvec[size_t(h) * Kp + k] = float((ck - c0) * L2E);
+    } else if ((threadIdx.x & 63) == 0) {
+        cvec[size_t(h) * Kp + k] = -INFINITY;
     }
-    for (int o = 32; o >= 1; o >>= 1) local_max = fmax(local_max, __shfl_xor(local_max, o, 64));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = local_max;
-    __syncthreads();
-    const double mx = fmax(fmax(red[0], red[1]), fmax(red[2], red[3]));
-    for (int k = threadIdx.x; k < Kp; k += 256) cvec[size_t(h) * Kp + k] = (k < K) ? float(cd[k] - mx) : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------- softmax across waves
@@ -186,22 +199,54 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
         for (int r = 0; r < 16; ++r) wacc[q][r] = 0.0f;
     }
     float zr[S::CTW][16];
-
+    // value tile of a round: VCH 16-byte chunks per thread
+    constexpr int VCH = (S::ROUND * DV / 8 + S::NW * 64 - 1) / (S::NW * 64);
+    auto load_v = [&](int64_t nr, u32x4 (&vr)[VCH]) {
+#pragma unroll
+        for (int u = 0; u < VCH; ++u) {
+            const int c = threadIdx.x + u * S::NW * 64;
+            const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
+            vr[u] = u32x4{0u, 0u, 0u, 0u};
+            if (c < S::ROUND * DV / 8 && nr + row < hi)
+                vr[u] = *reinterpret_cast<const u32x4*>(Vp + (nr + row) * DV + col);
+        }
+    };
+    // software pipeline: the next round's X fragments and V chunks are loaded into
+    // registers while the current round is computed
+    bf16x8 xn[S::KS];
+    u32x4 vn[VCH];
+    {
+        const int64_t n0 = lo + ts * 32;
+        load_x<DR>(Xp, n0, int(max<int64_t>(0, min<int64_t>(32, hi - n0))), xn);
+        load_v(lo, vn);
+    }
     for (int64_t nr = lo; nr < hi; nr += S::ROUND) {
         const int64_t n0 = nr + ts * 32;
         const int valid = int(max<int64_t>(0, min<int64_t>(32, hi - n0)));
+        bf16x8 xc[S::KS];
+        u32x4 vc[VCH];
+#pragma unroll
+        for (int ks = 0; ks < S::KS; ++ks) xc[ks] = xn[ks];
+#pragma unroll
+        for (int u = 0; u < VCH; ++u) vc[u] = vn[u];
+        if (nr + S::ROUND < hi) {
+            const int64_t n1 = n0 + S::ROUND;
+            load_x<DR>(Xp, n1, int(max<int64_t>(0, min<int64_t>(32, hi - n1))), xn);
+            load_v(nr + S::ROUND, vn);
+        }
         f32x16 acc[S::CTW];
-        scores<DR, S::CTW>(P, Xp, n0, valid, acc);
+        scores_x<DR, S::CTW>(P, xc, acc);
         float m, L, D;
         local_softmax<S::CTW, false>(acc, zr, m, L, D);
         if (S::CS > 1 && lh == 0) st[(ts * S::CS + cs) * 32 + j] = Stats{m, L, 0.0f};
         __syncthreads();  // B1: stats published; previous round's LDS tiles consumed
-        // value tile of the round -> LDS (rows past the split read as zero)
-        for (int c = threadIdx.x; c < S::ROUND * DV / 8; c += S::NW * 64) {
-            const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (nr + row < hi) v = *reinterpret_cast<const u32x4*>(Vp + (nr + row) * DV + col);
-            *reinterpret_cast<u32x4*>(Vs + row * LDV + col) = v;
+#pragma unroll
+        for (int u = 0; u < VCH; ++u) {
+            const int c = threadIdx.x + u * S::NW * 64;
+            if (c < S::ROUND * DV / 8) {
+                const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
+                *reinterpret_cast<u32x4*>(Vs + row * LDV + col) = vc[u];
+            }
         }
         float dl;
         float scale = combine_stats<S::CS>(st, ts, cs, j, m, L, 0.0f, dl);
@@ -226,7 +271,7 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
             }
         }
     }
-    // partial of this split: Vt [Kp][DV] then Z [Kp]
+    // partial of this split: VtT [DV][Kp] (Vt transposed) then Z [Kp]
     float* mem = partials + (size_t(p) * G + g_idx) * size_t(Kp) * (DV + 1);
 #pragma unroll
     for (int q = 0; q < PW; ++q) {
@@ -234,9 +279,10 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
         if (pair < PAIRS) {
             const int ct = pair / VT, vt = pair - ct * VT;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int comp = ct * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                mem[size_t(comp) * DV + vt * 32 + j] = wacc[q][r];
+            for (int qq = 0; qq < 4; ++qq) {
+                const int comp = ct * 32 + 8 * qq + 4 * lh;
+                *reinterpret_cast<float4*>(mem + size_t(vt * 32 + j) * Kp + comp) =
+                    make_float4(wacc[q][4 * qq + 0], wacc[q][4 * qq + 1], wacc[q][4 * qq + 2], wacc[q][4 * qq + 3]);
             }
             if (vt == 0) {
                 const float z = xsum32(zacc[q]);
@@ -249,7 +295,8 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
 // ---------------------------------------------------------------------------- combine / prefix
 
 // Bidirectional: memory = sum_g partial_g (increasing g), then the read operands:
-// VtT_hi, VtT_lo [DV][Kp] bf16 (Vt transposed, hi + lo split) and Z [Kp] fp32.
+// VtT_hi, VtT_lo [DV][Kp] bf16 (Vt transposed, hi + lo split) and Z [Kp] fp32.  The
+// partials use the same [DV][Kp] + [Kp] order, so every access is coalesced.
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ partials, int G, int Kp, int DV,
                                                       uint16_t* __restrict__ memory) {
     const int64_t p = blockIdx.y;
@@ -261,26 +308,11 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     for (int g = 0; g < G; ++g) acc += src[size_t(g) * E];
     uint16_t* base = memory + size_t(p) * E * 2;  // E floats of room per problem
     if (e < Kp * DV) {
-        const int k = e / DV, c = e - k * DV;
         const uint16_t hi = f32_to_bf16_bits(acc);
-        const uint16_t lo = f32_to_bf16_bits(acc - bf16_bits_to_f32(hi));
-        base[size_t(c) * Kp + k] = hi;
-        base[size_t(DV) * Kp + size_t(c) * Kp + k] = lo;
+        base[e] = hi;
+        base[size_t(DV) * Kp + e] = f32_to_bf16_bits(acc - bf16_bits_to_f32(hi));
     } else {
         reinterpret_cast<float*>(base + size_t(2) * DV * Kp)[e - Kp * DV] = acc;
-    }
-}
-
-__global__ void __launch_bounds__(256) prefix_kernel(float* __restrict__ partials, int G, int E) {
-    const int64_t p = blockIdx.y;
-    const int e = blockIdx.x * 256 + threadIdx.x;
-    if (e >= E) return;
-    float* src = partials + size_t(p) * G * E + e;
-    float run = 0.0f;
-    for (int g = 0; g < G; ++g) {
-        const float a = src[size_t(g) * E];
-        src[size_t(g) * E] = run;
-        run += a;
     }
 }
 
@@ -329,11 +361,23 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
 
     const uint16_t* Xp = XQ + size_t(p) * N * DR;
     const int64_t lo = int64_t(blockIdx.x) * rows_per_block, hi = min<int64_t>(lo + rows_per_block, N);
+    bf16x8 xn[S::KS];  // next round's query fragments, loaded while this round computes
+    {
+        const int64_t n0 = lo + ts * 32;
+        load_x<DR>(Xp, n0, int(max<int64_t>(0, min<int64_t>(32, hi - n0))), xn);
+    }
     for (int64_t nr = lo; nr < hi; nr += S::ROUND) {
         const int64_t n0 = nr + ts * 32;
         const int valid = int(max<int64_t>(0, min<int64_t>(32, hi - n0)));
+        bf16x8 xc[S::KS];
+#pragma unroll
+        for (int ks = 0; ks < S::KS; ++ks) xc[ks] = xn[ks];
+        if (nr + S::ROUND < hi) {
+            const int64_t n1 = n0 + S::ROUND;
+            load_x<DR>(Xp, n1, int(max<int64_t>(0, min<int64_t>(32, hi - n1))), xn);
+        }
         f32x16 acc[S::CTW];
-        scores<DR, S::CTW>(P, Xp, n0, valid, acc);
+        scores_x<DR, S::CTW>(P, xc, acc);
         float m, L, D;
         local_softmax<S::CTW, true>(acc, zr, m, L, D);
         if (S::CS > 1 && lh == 0) st[(ts * S::CS + cs) * 32 + j] = Stats{m, L, D};
@@ -417,7 +461,8 @@ int kt_of(const Plan& p) { return int(p.Kp / 32); }
 
 hipError_t launch_params(const Plan& p, const float* mu, const float* s2, const float* pi, char* ws, hipStream_t st) {
     Bf16Params v = bf16_params_view(p, ws);
-    GMA_LAUNCH("bf16_params", bf::params_kernel, dim3(unsigned(p.H)), dim3(256), 0, st, mu, s2, pi, int(p.K), int(p.Kp),
+    GMA_LAUNCH("bf16_params", bf::params_kernel, dim3(unsigned((p.Kp + 3) / 4), unsigned(p.H)), dim3(256), 0, st, mu,
+               s2, pi, int(p.K), int(p.Kp),
                        int(p.dr), v.planes, v.cvec);
     return hipGetLastError();
 }
@@ -449,7 +494,7 @@ hipError_t bf16_responsibilities(const Plan& p, const void* X, const float* mu, 
     });
 }
 
-hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, char* ws, hipStream_t st) {
+hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, char* ws, hipStream_t st, int64_t splits) {
     Bf16Params v = bf16_params_view(p, ws);
     float* partials = reinterpret_cast<float*>(ws + p.off_partials);
     return bf::with_dr_kt(int(p.dr), kt_of(p), [&](auto D, auto T) {
@@ -457,7 +502,7 @@ hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, cha
         return bf::with_vt(int(p.dv / 32), [&](auto VV) {
             constexpr int VT = decltype(VV)::value;
             using S = bf::Split<DR, KT>;
-            GMA_LAUNCH(p.op == GMA_OP_CAUSAL ? "bf16_causal_aggregate" : "bf16_write", (bf::write_kernel<DR, KT, VT>), dim3(unsigned(p.G), unsigned(p.P)), dim3(S::NW * 64), 0,
+            GMA_LAUNCH(p.op == GMA_OP_CAUSAL ? "bf16_causal_aggregate" : "bf16_write", (bf::write_kernel<DR, KT, VT>), dim3(unsigned(splits), unsigned(p.P)), dim3(S::NW * 64), 0,
                                st, static_cast<const uint16_t*>(XK), static_cast<const uint16_t*>(V), p.N, int(p.H),
                                p.seg, int(p.G), v.planes, v.cvec, partials);
             return hipGetLastError();
@@ -469,7 +514,7 @@ hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void*
                       const float* pi, float eps, void* O, char* ws, hipStream_t st) {
     hipError_t e = launch_params(p, mu, s2, pi, ws, st);
     if (e != hipSuccess) return e;
-    if ((e = bf16_write_partials(p, XK, V, ws, st)) != hipSuccess) return e;
+    if ((e = bf16_write_partials(p, XK, V, ws, st, p.G)) != hipSuccess) return e;
     float* partials = reinterpret_cast<float*>(ws + p.off_partials);
     uint16_t* memory = reinterpret_cast<uint16_t*>(ws + p.off_memory);
     const int E = int(p.Kp * (p.dv + 1));
@@ -495,12 +540,9 @@ hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void
                        const float* pi, float eps, void* O, char* ws, hipStream_t st) {
     hipError_t e = launch_params(p, mu, s2, pi, ws, st);
     if (e != hipSuccess) return e;
-    float* partials = reinterpret_cast<float*>(ws + p.off_partials);
-    if (p.G > 1 && (e = bf16_write_partials(p, XK, V, ws, st)) != hipSuccess) return e;
-    const int E = int(p.Kp * (p.dv + 1));
-    GMA_LAUNCH("bf16_prefix", bf::prefix_kernel, dim3(unsigned((E + 255) / 256), unsigned(p.P)), dim3(256), 0, st, partials,
-                       int(p.G), E);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // aggregates of segments 0 .. G-2 (the last segment's aggregate is never read); the
+    // scan workgroup of segment s sums aggregates 0 .. s-1 itself
+    if (p.G > 1 && (e = bf16_write_partials(p, XK, V, ws, st, p.G - 1)) != hipSuccess) return e;
     Bf16Params v = bf16_params_view(p, ws);
     return bf16_scan(p, XQ, XK, V, v.planes, v.cvec, eps, O, ws, st);
 }

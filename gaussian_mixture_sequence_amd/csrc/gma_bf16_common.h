@@ -137,18 +137,24 @@ struct WaveParams {
     }
 };
 
-// S^T for one 32-token subtile starting at row `n0` of X (row-major [N][DR] bf16 of one
-// problem); rows >= `valid` read as zero.  acc[ct] holds scores of component tile ct.
-template <int DR, int CTW>
-__device__ __forceinline__ void scores(const WaveParams<DR, CTW>& P, const uint16_t* __restrict__ X, int64_t n0,
-                                       int valid, f32x16 (&acc)[CTW]) {
+// B fragments of one 32-token subtile starting at row `n0` of X (row-major [N][DR] bf16
+// of one problem): lane (lh, j) gets x[n0 + j][16 ks + 8 lh .. + 7].  Rows >= `valid`
+// read as zero (no memory access).
+template <int DR>
+__device__ __forceinline__ void load_x(const uint16_t* __restrict__ X, int64_t n0, int valid, bf16x8 (&xs)[DR / 16]) {
     const int l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
-    bf16x8 xs[DR / 16];
     const bool ok = j < valid;
-    const uint16_t* row = X + (n0 + j) * DR + 8 * lh;
+    const uint16_t* row = X + (n0 + (ok ? j : 0)) * DR + 8 * lh;
 #pragma unroll
     for (int ks = 0; ks < DR / 16; ++ks)
         xs[ks] = ok ? *reinterpret_cast<const bf16x8*>(row + 16 * ks) : zero_bf16x8();
+}
+
+// S^T for one 32-token subtile from its B fragments: acc[ct] holds the scores of
+// component tile ct (rows = components, cols = tokens).
+template <int DR, int CTW>
+__device__ __forceinline__ void scores_x(const WaveParams<DR, CTW>& P, const bf16x8 (&xs)[DR / 16],
+                                         f32x16 (&acc)[CTW]) {
 #pragma unroll
     for (int ct = 0; ct < CTW; ++ct)
 #pragma unroll
@@ -166,6 +172,15 @@ __device__ __forceinline__ void scores(const WaveParams<DR, CTW>& P, const uint1
             acc[ct] = mfma(P.w[ct][ks][2], x2l, acc[ct]);
         }
     }
+}
+
+// load_x + scores_x.
+template <int DR, int CTW>
+__device__ __forceinline__ void scores(const WaveParams<DR, CTW>& P, const uint16_t* __restrict__ X, int64_t n0,
+                                       int valid, f32x16 (&acc)[CTW]) {
+    bf16x8 xs[DR / 16];
+    load_x<DR>(X, n0, valid, xs);
+    scores_x<DR, CTW>(P, xs, acc);
 }
 
 // Softmax statistics of one wave's components for its lane's token: max m, sum of

@@ -90,19 +90,34 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
     const uint16_t* Vp = V + size_t(p) * N * DV;
     const int64_t lo = int64_t(seg_idx) * seg, hi = min<int64_t>(lo + seg, N);
 
-    // starting memory of the segment
-    const float* pre = prefix + (size_t(p) * G + seg_idx) * size_t(Kp) * (DV + 1);
+    // starting memory of the segment: the sum of the aggregates of segments 0 .. seg_idx-1
+    // (each stored as VtT [DV][Kp] then Z [Kp]), added in increasing segment order
+    const size_t E = size_t(Kp) * (DV + 1);
+    const float* agg = prefix + size_t(p) * G * E;
     f32x4 mem[CPW][KT16];
 #pragma unroll
-    for (int cc = 0; cc < CPW; ++cc) {
-        const int c16 = wave + cc * NW;
+    for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
-        for (int kt = 0; kt < KT16; ++kt)
+        for (int kt = 0; kt < KT16; ++kt) mem[cc][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = threadIdx.x; k < Kp; k += NW * 64) Zs[k] = 0.0f;
+    for (int gs = 0; gs < seg_idx; ++gs) {
+        const float* a = agg + size_t(gs) * E;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                mem[cc][kt][r] = (c16 < C16) ? pre[size_t(kt * 16 + 4 * g4 + r) * DV + c16 * 16 + i16] : 0.0f;
+        for (int cc = 0; cc < CPW; ++cc) {
+            const int c16 = wave + cc * NW;
+            if (c16 < C16) {
+#pragma unroll
+                for (int kt = 0; kt < KT16; ++kt) {
+                    const float4 v = *reinterpret_cast<const float4*>(a + size_t(c16 * 16 + i16) * Kp + kt * 16 + 4 * g4);
+                    mem[cc][kt][0] += v.x;
+                    mem[cc][kt][1] += v.y;
+                    mem[cc][kt][2] += v.z;
+                    mem[cc][kt][3] += v.w;
+                }
+            }
+        }
+        for (int k = threadIdx.x; k < Kp; k += NW * 64) Zs[k] += a[size_t(Kp) * DV + k];
     }
-    for (int k = threadIdx.x; k < Kp; k += NW * 64) Zs[k] = pre[size_t(Kp) * DV + k];
 
     for (int64_t nc = lo; nc < hi; nc += CH) {
         __syncthreads();  // B0: previous chunk's tiles consumed, Zs updated

@@ -72,8 +72,8 @@ hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void
                        char* ws, hipStream_t st);
 // tokens one bf16 workgroup processes per round for (d_r, padded K); 0 if unsupported
 int64_t bf16_round_tokens(int dr, int64_t Kp);
-// causal chunked scan of every segment, starting from the prefix memories in the
-// workspace partials (gma_bf16_scan.hip)
+// causal chunked scan of every segment; segment s starts from the sum of the aggregates
+// of segments 0 .. s-1 in the workspace partials (gma_bf16_scan.hip)
 hipError_t bf16_scan(const Plan& p, const void* XQ, const void* XK, const void* V, const uint16_t* planes,
                      const float* cvec, float eps, void* O, char* ws, hipStream_t st);
 
