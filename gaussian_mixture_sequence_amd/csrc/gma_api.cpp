@@ -16,7 +16,8 @@ namespace gma {
 namespace {
 
 constexpr int64_t kTokenTile = 64;      // tokens per tile in every kernel family
-constexpr int64_t kBidirBlocks = 1024;  // target workgroups for the split-N write
+constexpr int64_t kBidirBlocks = 512;   // target workgroups for the split-N write and the read
+                                        // (two resident per CU: one wave of workgroups)
 constexpr int64_t kCausalBlocks = 512;  // target workgroups for the segmented scan
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -73,7 +74,7 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
     p.G = 1;
     p.seg = round_up(size_t(std::max<int64_t>(p.N, 1)), kTokenTile);
     if (op == GMA_OP_BIDIR && p.P > 0 && p.N > 0) {
-        int64_t g = std::min(cdiv(kBidirBlocks, p.P), cdiv(p.N, 256));
+        int64_t g = std::min(cdiv(kBidirBlocks, p.P), cdiv(p.N, 512));
         g = std::max<int64_t>(g, 1);
         p.seg = round_up(size_t(cdiv(p.N, g)), kTokenTile);
         p.G = cdiv(p.N, p.seg);

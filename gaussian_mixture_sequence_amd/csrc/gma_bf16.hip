@@ -164,6 +164,12 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) resp_kernel(const ui
 
 // ---------------------------------------------------------------------------- write (Gamma_K^T [V | 1])
 
+// Rows [lo, hi) of one problem.  Per round of ROUND tokens:
+//   scores of this wave's (token subtile, component group) from the shared x tile
+//   -> softmax statistics -> B1 -> Gamma_K (bf16) and the V tile into LDS; the next
+//   round's x tile is split into LDS and the loads of the round after are issued
+//   -> B2 -> MFMA: Vt^T partial += V^T Gamma_K and Z += Gamma_K^T 1 (ones column).
+// Loads go through buffer resources ending at `hi`, so tails read zeros without branches.
 template <int DR, int KT, int VT>
 __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const uint16_t* __restrict__ XK,
                                                                         const uint16_t* __restrict__ V, int64_t N,
@@ -171,11 +177,15 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
                                                                         const uint16_t* planes, const float* cvec,
                                                                         float* __restrict__ partials) {
     using S = Split<DR, KT>;
+    constexpr int NT = S::NW * 64;
     constexpr int Kp = KT * 32, DV = VT * 32;
     constexpr int LDG = Kp + 8, LDV = DV + 8;
-    constexpr int PAIRS = KT * VT;
+    constexpr int PAIRS = KT * (VT + 1);  // value column tiles plus the ones column (Z)
     constexpr int PW = (PAIRS + S::NW - 1) / S::NW;
+    using XT = XTile<DR, S::ROUND, NT>;
+    constexpr int VCH = (S::ROUND * DV / 8 + NT - 1) / NT;
     __shared__ Stats st[S::TS * S::CS * 32];
+    __shared__ __attribute__((aligned(16))) u32x4 Xt[XT::LDS_BYTES / 16];
     __shared__ __attribute__((aligned(16))) uint16_t Gs[S::ROUND * LDG];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[S::ROUND * LDV];
 
@@ -184,89 +194,71 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
     const int64_t p = blockIdx.y;
     const int g_idx = blockIdx.x;
     const int h = int(p % H);
+    const int64_t lo = int64_t(g_idx) * seg, hi = min<int64_t>(lo + seg, N);
     WaveParams<DR, S::CTW> P;
     P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * S::CTW);
-    const uint16_t* Xp = XK + size_t(p) * N * DR;
-    const uint16_t* Vp = V + size_t(p) * N * DV;
-    const int64_t lo = int64_t(g_idx) * seg, hi = min<int64_t>(lo + seg, N);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(XK + (size_t(p) * N + lo) * DR, (hi - lo) * DR * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t(p) * N + lo) * DV, (hi - lo) * DV * 2);
 
-    f32x16 wacc[PW];
-    float zacc[PW];
-#pragma unroll
-    for (int q = 0; q < PW; ++q) {
-        zacc[q] = 0.0f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) wacc[q][r] = 0.0f;
-    }
-    float zr[S::CTW][16];
-    // value tile of a round: VCH 16-byte chunks per thread
-    constexpr int VCH = (S::ROUND * DV / 8 + S::NW * 64 - 1) / (S::NW * 64);
-    auto load_v = [&](int64_t nr, u32x4 (&vr)[VCH]) {
+    XT xt;
+    u32x4 vr[VCH];
+    auto load_v = [&](int64_t row0) {
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
-            const int c = threadIdx.x + u * S::NW * 64;
-            const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
-            vr[u] = u32x4{0u, 0u, 0u, 0u};
-            if (c < S::ROUND * DV / 8 && nr + row < hi)
-                vr[u] = *reinterpret_cast<const u32x4*>(Vp + (nr + row) * DV + col);
+            const int c = threadIdx.x + u * NT;
+            vr[u] = (c < S::ROUND * DV / 8) ? buf_load16(rv, uint32_t((row0 * DV + int64_t(c) * 8) * 2))
+                                            : u32x4{0u, 0u, 0u, 0u};
         }
     };
-    // software pipeline: the next round's X fragments and V chunks are loaded into
-    // registers while the current round is computed
-    bf16x8 xn[S::KS];
-    u32x4 vn[VCH];
-    {
-        const int64_t n0 = lo + ts * 32;
-        load_x<DR>(Xp, n0, int(max<int64_t>(0, min<int64_t>(32, hi - n0))), xn);
-        load_v(lo, vn);
-    }
-    for (int64_t nr = lo; nr < hi; nr += S::ROUND) {
-        const int64_t n0 = nr + ts * 32;
-        const int valid = int(max<int64_t>(0, min<int64_t>(32, hi - n0)));
-        bf16x8 xc[S::KS];
-        u32x4 vc[VCH];
+    // prologue: x tile of round 0 into LDS; V of round 0 and x of round 1 in flight
+    xt.load(rx, 0);
+    load_v(0);
+    xt.commit(Xt);
+    xt.load(rx, S::ROUND);
+    __syncthreads();
+
+    f32x16 wacc[PW];
 #pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks) xc[ks] = xn[ks];
+    for (int q = 0; q < PW; ++q)
 #pragma unroll
-        for (int u = 0; u < VCH; ++u) vc[u] = vn[u];
-        if (nr + S::ROUND < hi) {
-            const int64_t n1 = n0 + S::ROUND;
-            load_x<DR>(Xp, n1, int(max<int64_t>(0, min<int64_t>(32, hi - n1))), xn);
-            load_v(nr + S::ROUND, vn);
-        }
+        for (int r = 0; r < 16; ++r) wacc[q][r] = 0.0f;
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+    float zr[S::CTW][16];
+
+    for (int64_t r0 = 0; r0 < hi - lo; r0 += S::ROUND) {
+        const int valid = int(max<int64_t>(0, min<int64_t>(32, hi - lo - r0 - ts * 32)));
         f32x16 acc[S::CTW];
-        scores_x<DR, S::CTW>(P, xc, acc);
+        scores_lds<DR, S::CTW>(P, Xt, ts, acc);
         float m, L, D;
         local_softmax<S::CTW, false>(acc, zr, m, L, D);
         if (S::CS > 1 && lh == 0) st[(ts * S::CS + cs) * 32 + j] = Stats{m, L, 0.0f};
-        __syncthreads();  // B1: stats published; previous round's LDS tiles consumed
-#pragma unroll
-        for (int u = 0; u < VCH; ++u) {
-            const int c = threadIdx.x + u * S::NW * 64;
-            if (c < S::ROUND * DV / 8) {
-                const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
-                *reinterpret_cast<u32x4*>(Vs + row * LDV + col) = vc[u];
-            }
-        }
+        __syncthreads();  // B1: statistics published; this round's x tile and last round's tiles consumed
         float dl;
         float scale = combine_stats<S::CS>(st, ts, cs, j, m, L, 0.0f, dl);
         if (j >= valid) scale = 0.0f;
         store_gamma_lds<S::CTW>(acc, scale, Gs, LDG, ts * 32 + j, cs * S::CTW);
-        __syncthreads();  // B2: Gamma_K and V tiles of the round complete
+#pragma unroll
+        for (int u = 0; u < VCH; ++u) {
+            const int c = threadIdx.x + u * NT;
+            if (c < S::ROUND * DV / 8) {
+                const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
+                *reinterpret_cast<u32x4*>(Vs + row * LDV + col) = vr[u];
+            }
+        }
+        load_v(r0 + S::ROUND);
+        xt.commit(Xt);
+        xt.load(rx, r0 + 2 * S::ROUND);
+        __syncthreads();  // B2: Gamma_K, V and the next x tile are in LDS
 #pragma unroll
         for (int q = 0; q < PW; ++q) {
             const int pair = wave + q * S::NW;
             if (pair < PAIRS) {
-                const int ct = pair / VT, vt = pair - ct * VT;
+                const int ct = pair / (VT + 1), vt = pair - ct * (VT + 1);
 #pragma unroll
                 for (int ks = 0; ks < S::ROUND / 16; ++ks) {
-                    bf16x8 a = read_colfrag(Gs, LDG, 16 * ks, ct * 32);
-                    bf16x8 b = read_colfrag(Vs, LDV, 16 * ks, vt * 32);
+                    const bf16x8 a = read_colfrag(Gs, LDG, 16 * ks, ct * 32);
+                    const bf16x8 b = (vt < VT) ? read_colfrag(Vs, LDV, 16 * ks, vt * 32) : ones;
                     wacc[q] = mfma(a, b, wacc[q]);
-                    if (vt == 0) {
-#pragma unroll
-                        for (int v = 0; v < 8; ++v) zacc[q] += float(a[v]);
-                    }
                 }
             }
         }
@@ -277,16 +269,19 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
     for (int q = 0; q < PW; ++q) {
         const int pair = wave + q * S::NW;
         if (pair < PAIRS) {
-            const int ct = pair / VT, vt = pair - ct * VT;
+            const int ct = pair / (VT + 1), vt = pair - ct * (VT + 1);
+            if (vt < VT) {
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int comp = ct * 32 + 8 * qq + 4 * lh;
-                *reinterpret_cast<float4*>(mem + size_t(vt * 32 + j) * Kp + comp) =
-                    make_float4(wacc[q][4 * qq + 0], wacc[q][4 * qq + 1], wacc[q][4 * qq + 2], wacc[q][4 * qq + 3]);
-            }
-            if (vt == 0) {
-                const float z = xsum32(zacc[q]);
-                if (lh == 0) mem[size_t(Kp) * DV + ct * 32 + j] = z;
+                for (int qq = 0; qq < 4; ++qq) {
+                    const int comp = ct * 32 + 8 * qq + 4 * lh;
+                    *reinterpret_cast<float4*>(mem + size_t(vt * 32 + j) * Kp + comp) = make_float4(
+                        wacc[q][4 * qq + 0], wacc[q][4 * qq + 1], wacc[q][4 * qq + 2], wacc[q][4 * qq + 3]);
+                }
+            } else if (j == 0) {  // every column of the ones-column tile holds Z
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq)
+                    *reinterpret_cast<float4*>(mem + size_t(Kp) * DV + ct * 32 + 8 * qq + 4 * lh) = make_float4(
+                        wacc[q][4 * qq + 0], wacc[q][4 * qq + 1], wacc[q][4 * qq + 2], wacc[q][4 * qq + 3]);
             }
         }
     }
@@ -318,6 +313,10 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 
 // ---------------------------------------------------------------------------- read
 
+// Rows [lo, hi) of one problem.  The softmax normalisation cancels between numerator
+// and denominator of Eq. 7: with e_k = exp2(s_k - m) and L = sum_k e_k,
+//   O = sum_k e_k Vt_k / (sum_k e_k Z_k + eps L),
+// so the MFMA takes e (bf16) directly and the denominator D + eps L is formed in fp32.
 template <int DR, int KT, int VT>
 __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const uint16_t* __restrict__ XQ, int64_t N,
                                                                        int H, int64_t rows_per_block,
@@ -325,14 +324,17 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
                                                                        const uint16_t* __restrict__ memory, float eps,
                                                                        uint16_t* __restrict__ O) {
     using S = Split<DR, KT>;
+    constexpr int NT = S::NW * 64;
     constexpr int Kp = KT * 32, DV = VT * 32;
     constexpr int LDG = Kp + 8, LDM = Kp + 8;
     constexpr int PAIRS = S::TS * VT;
     constexpr int PW = (PAIRS + S::NW - 1) / S::NW;
+    using XT = XTile<DR, S::ROUND, NT>;
+    // VtT hi/lo staged in LDS when it fits; otherwise read from L2
+    constexpr bool MS_LDS = (2 * DV * LDM + S::ROUND * LDG) * 2 + XT::LDS_BYTES <= 150 * 1024;
     __shared__ Stats st[S::TS * S::CS * 32];
+    __shared__ __attribute__((aligned(16))) u32x4 Xt[XT::LDS_BYTES / 16];
     __shared__ __attribute__((aligned(16))) uint16_t Gs[S::ROUND * LDG];
-    // VtT hi/lo staged in LDS when it fits next to the Gamma tile; otherwise read from L2
-    constexpr bool MS_LDS = (2 * DV * LDM + S::ROUND * LDG) * 2 <= 150 * 1024;
     __shared__ __attribute__((aligned(16))) uint16_t Ms[MS_LDS ? 2 * DV * LDM : 8];
     __shared__ float den_s[S::ROUND];
 
@@ -340,12 +342,17 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
     const int cs = wave % S::CS, ts = wave / S::CS;
     const int64_t p = blockIdx.y;
     const int h = int(p % H);
+    const int64_t lo = int64_t(blockIdx.x) * rows_per_block, hi = min<int64_t>(lo + rows_per_block, N);
     WaveParams<DR, S::CTW> P;
     P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * S::CTW);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(XQ + (size_t(p) * N + lo) * DR, (hi - lo) * DR * 2);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + (size_t(p) * N + lo) * DV, (hi - lo) * DV * 2);
+    XT xt;
+    xt.load(rx, 0);
     // latent memory of this problem: VtT hi/lo -> LDS, Z -> registers in score-row order
     const uint16_t* mp = memory + size_t(p) * Kp * (DV + 1) * 2;
     if (MS_LDS)
-        for (int c = threadIdx.x; c < 2 * DV * Kp / 8; c += S::NW * 64) {
+        for (int c = threadIdx.x; c < 2 * DV * Kp / 8; c += NT) {
             const int row = c / (Kp / 8), col = (c - row * (Kp / 8)) * 8;
             *reinterpret_cast<u32x4*>(Ms + row * LDM + col) =
                 *reinterpret_cast<const u32x4*>(mp + size_t(row) * Kp + col);
@@ -358,34 +365,40 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
     for (int ct = 0; ct < S::CTW; ++ct)
 #pragma unroll
         for (int r = 0; r < 16; ++r) zr[ct][r] = Zp[(cs * S::CTW + ct) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)];
+    xt.commit(Xt);
+    xt.load(rx, S::ROUND);
+    __syncthreads();
 
-    const uint16_t* Xp = XQ + size_t(p) * N * DR;
-    const int64_t lo = int64_t(blockIdx.x) * rows_per_block, hi = min<int64_t>(lo + rows_per_block, N);
-    bf16x8 xn[S::KS];  // next round's query fragments, loaded while this round computes
-    {
-        const int64_t n0 = lo + ts * 32;
-        load_x<DR>(Xp, n0, int(max<int64_t>(0, min<int64_t>(32, hi - n0))), xn);
-    }
-    for (int64_t nr = lo; nr < hi; nr += S::ROUND) {
-        const int64_t n0 = nr + ts * 32;
-        const int valid = int(max<int64_t>(0, min<int64_t>(32, hi - n0)));
-        bf16x8 xc[S::KS];
-#pragma unroll
-        for (int ks = 0; ks < S::KS; ++ks) xc[ks] = xn[ks];
-        if (nr + S::ROUND < hi) {
-            const int64_t n1 = n0 + S::ROUND;
-            load_x<DR>(Xp, n1, int(max<int64_t>(0, min<int64_t>(32, hi - n1))), xn);
-        }
+    for (int64_t r0 = 0; r0 < hi - lo; r0 += S::ROUND) {
         f32x16 acc[S::CTW];
-        scores_x<DR, S::CTW>(P, xc, acc);
+        scores_lds<DR, S::CTW>(P, Xt, ts, acc);
         float m, L, D;
         local_softmax<S::CTW, true>(acc, zr, m, L, D);
         if (S::CS > 1 && lh == 0) st[(ts * S::CS + cs) * 32 + j] = Stats{m, L, D};
         __syncthreads();  // B1
-        float dl;
-        const float scale = combine_stats<S::CS>(st, ts, cs, j, m, L, D, dl);
-        store_gamma_lds<S::CTW>(acc, scale, Gs, LDG, ts * 32 + j, cs * S::CTW);
-        if (cs == 0 && lh == 0) den_s[ts * 32 + j] = dl + eps;
+        float scale = 1.0f, den = D + eps * L;
+        if (S::CS > 1) {
+            float mm = -INFINITY;
+#pragma unroll
+            for (int c = 0; c < S::CS; ++c) mm = fmaxf(mm, st[(ts * S::CS + c) * 32 + j].m);
+            float Lt = 0.0f, Dt = 0.0f;
+#pragma unroll
+            for (int c = 0; c < S::CS; ++c) {
+                const Stats sc = st[(ts * S::CS + c) * 32 + j];
+                const float f = __builtin_amdgcn_exp2f(sc.m - mm);
+                Lt = fmaf(sc.L, f, Lt);
+                Dt = fmaf(sc.D, f, Dt);
+            }
+            scale = __builtin_amdgcn_exp2f(m - mm);
+            den = Dt + eps * Lt;
+        }
+        if (S::CS > 1)
+            store_gamma_lds<S::CTW>(acc, scale, Gs, LDG, ts * 32 + j, cs * S::CTW);
+        else
+            store_gamma_lds<S::CTW>(acc, 1.0f, Gs, LDG, ts * 32 + j, cs * S::CTW);
+        if (cs == 0 && lh == 0) den_s[ts * 32 + j] = den;
+        xt.commit(Xt);
+        xt.load(rx, r0 + 2 * S::ROUND);
         __syncthreads();  // B2
 #pragma unroll
         for (int q = 0; q < PW; ++q) {
@@ -397,23 +410,20 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
                 for (int r = 0; r < 16; ++r) o[r] = 0.0f;
 #pragma unroll
                 for (int ks = 0; ks < Kp / 16; ++ks) {
-                    bf16x8 b = read_rowfrag(Gs, LDG, tsub * 32 + j, 16 * ks);
-                    bf16x8 ah = read_rowfrag(Msrc, LDMS, vt * 32 + j, 16 * ks);
-                    bf16x8 al = read_rowfrag(Msrc + DV * LDMS, LDMS, vt * 32 + j, 16 * ks);
+                    const bf16x8 b = read_rowfrag(Gs, LDG, tsub * 32 + j, 16 * ks);
+                    const bf16x8 ah = read_rowfrag(Msrc, LDMS, vt * 32 + j, 16 * ks);
+                    const bf16x8 al = read_rowfrag(Msrc + DV * LDMS, LDMS, vt * 32 + j, 16 * ks);
                     o = mfma(ah, b, o);
                     o = mfma(al, b, o);
                 }
-                const int64_t tok = nr + tsub * 32 + j;
-                if (tok < hi) {
-                    const float rden = 1.0f / den_s[tsub * 32 + j];
-                    uint16_t* orow = O + (size_t(p) * N + tok) * DV + vt * 32 + 4 * lh;
+                const float rden = 1.0f / den_s[tsub * 32 + j];
+                const uint32_t off = uint32_t(((r0 + tsub * 32 + j) * DV + vt * 32 + 4 * lh) * 2);
 #pragma unroll
-                    for (int qq = 0; qq < 4; ++qq) {
-                        u32x2 v;
-                        v[0] = pack_bf16x2(o[4 * qq + 0] * rden, o[4 * qq + 1] * rden);
-                        v[1] = pack_bf16x2(o[4 * qq + 2] * rden, o[4 * qq + 3] * rden);
-                        *reinterpret_cast<u32x2*>(orow + 8 * qq) = v;
-                    }
+                for (int qq = 0; qq < 4; ++qq) {
+                    u32x2 v;
+                    v[0] = pack_bf16x2(o[4 * qq + 0] * rden, o[4 * qq + 1] * rden);
+                    v[1] = pack_bf16x2(o[4 * qq + 2] * rden, o[4 * qq + 3] * rden);
+                    buf_store8(ro, off + 16 * qq, v);  // rows past hi are dropped by the range check
                 }
             }
         }

@@ -53,24 +53,105 @@ __device__ __forceinline__ void swap32(float x, float& a, float& b) {
 __device__ __forceinline__ float xmax32(float x) { float a, b; swap32(x, a, b); return fmaxf(a, b); }
 __device__ __forceinline__ float xsum32(float x) { float a, b; swap32(x, a, b); return a + b; }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Two floats -> packed bf16 pair (one v_cvt_pk_bf16_f32, round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return uint32_t(f32_to_bf16_bits(lo)) | (uint32_t(f32_to_bf16_bits(hi)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-// x^2 split into hi + lo bf16 (exact: the square of an 8-bit significand has 16 bits).
+// x^2 split into hi + lo bf16 for a packed pair of bf16 values (exact: the square of an
+// 8-bit significand has 16 bits, so x^2 - hi has at most 8 and is a bf16 value).
+__device__ __forceinline__ u32x2 square_split_pair(uint32_t x) {
+    const float x0 = __uint_as_float(x << 16), x1 = __uint_as_float(x & 0xffff0000u);
+    const float s0 = x0 * x0, s1 = x1 * x1;
+    const uint32_t hi = pack_bf16x2(s0, s1);
+    return u32x2{hi, pack_bf16x2(s0 - __uint_as_float(hi << 16), s1 - __uint_as_float(hi & 0xffff0000u))};
+}
+
 __device__ __forceinline__ void square_split(bf16x8 x, bf16x8& hi, bf16x8& lo) {
+    const u32x4 xv = __builtin_bit_cast(u32x4, x);
     u32x4 h, l;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        float f0 = float(x[2 * q]), f1 = float(x[2 * q + 1]);
-        float s0 = f0 * f0, s1 = f1 * f1;
-        uint16_t h0 = f32_to_bf16_bits(s0), h1 = f32_to_bf16_bits(s1);
-        float r0 = s0 - bf16_bits_to_f32(h0), r1 = s1 - bf16_bits_to_f32(h1);
-        h[q] = uint32_t(h0) | (uint32_t(h1) << 16);
-        l[q] = pack_bf16x2(r0, r1);
+        const u32x2 hl = square_split_pair(xv[q]);
+        h[q] = hl[0];
+        l[q] = hl[1];
     }
     hi = __builtin_bit_cast(bf16x8, h);
     lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// ---- buffer access: a resource covering [base, base + bytes); loads past the end
+// return zeros and stores past the end are dropped, so tiles need no guard branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+    const int32_t n = bytes <= 0 ? 0 : (bytes > 0x7fffffff ? 0x7fffffff : int32_t(bytes));
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v), r, off, 0, 0);
+}
+
+// ---- a tile of ROUND routing vectors, split once into the score MFMA's B fragments
+// (x, x^2 hi, x^2 lo) and shared through LDS by every wave that needs it.
+// LDS layout: frag[(ts * KS + ks) * 3 + piece][lane] of 16 bytes, lane = 32 * lh + j,
+// holding x[ts * 32 + j][16 ks + 8 lh .. + 7] (or its square pieces).  Each wave loads
+// whole fragments (lane l fetches exactly the 16 bytes lane l of the fragment needs), so
+// both the LDS stores and the 1 KiB fragment reads are conflict-free.
+template <int DR, int ROUND, int NTHREADS>
+struct XTile {
+    static constexpr int KS = DR / 16;
+    static constexpr int NW = NTHREADS / 64;
+    static constexpr int FRAGS = (ROUND / 32) * KS;
+    static constexpr int PER_WAVE = (FRAGS + NW - 1) / NW;
+    static constexpr int LDS_BYTES = FRAGS * 3 * 64 * 16;
+    u32x4 r[PER_WAVE];
+
+    // fragments of the tile that starts `row0` rows into the resource
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t row0) {
+        const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
+#pragma unroll
+        for (int u = 0; u < PER_WAVE; ++u) {
+            const int fi = wave + u * NW;
+            const int ts = fi / KS, ks = fi - ts * KS;
+            r[u] = (fi < FRAGS) ? buf_load16(rs, uint32_t(((row0 + ts * 32 + j) * DR + 16 * ks + 8 * lh) * 2))
+                                : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void commit(u32x4* lds) const {
+        const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+        for (int u = 0; u < PER_WAVE; ++u) {
+            const int fi = wave + u * NW;
+            if (fi < FRAGS) {
+                u32x4 h, lo;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x2 hl = square_split_pair(r[u][q]);
+                    h[q] = hl[0];
+                    lo[q] = hl[1];
+                }
+                u32x4* f = lds + fi * 3 * 64 + l;
+                f[0] = r[u];
+                f[64] = h;
+                f[128] = lo;
+            }
+        }
+    }
+};
+
+// B fragments of token subtile `ts` from an XTile in LDS.
+template <int DR>
+__device__ __forceinline__ void xtile_frags(const u32x4* lds, int ts, int ks, bf16x8& x, bf16x8& x2h, bf16x8& x2l) {
+    const int l = threadIdx.x & 63;
+    const u32x4* f = lds + ((ts * (DR / 16) + ks) * 3) * 64 + l;
+    x = __builtin_bit_cast(bf16x8, f[0]);
+    x2h = __builtin_bit_cast(bf16x8, f[64]);
+    x2l = __builtin_bit_cast(bf16x8, f[128]);
 }
 
 // Transposed fragment read from a row-major bf16 tile in LDS (ds_read_b64_tr_b16).
@@ -132,7 +213,13 @@ struct WaveParams {
                     w[ct][ks][pl] = *reinterpret_cast<const bf16x8*>(
                         planes + (size_t(pl) * Kp + comp) * DR + 16 * ks + 8 * lh);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) c[ct][r] = cvec[(ct0 + ct) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)];
+            for (int q = 0; q < 4; ++q) {
+                const float4 cv = *reinterpret_cast<const float4*>(cvec + (ct0 + ct) * 32 + 8 * q + 4 * lh);
+                c[ct][4 * q + 0] = cv.x;
+                c[ct][4 * q + 1] = cv.y;
+                c[ct][4 * q + 2] = cv.z;
+                c[ct][4 * q + 3] = cv.w;
+            }
         }
     }
 };
@@ -148,6 +235,16 @@ __device__ __forceinline__ void load_x(const uint16_t* __restrict__ X, int64_t n
 #pragma unroll
     for (int ks = 0; ks < DR / 16; ++ks)
         xs[ks] = ok ? *reinterpret_cast<const bf16x8*>(row + 16 * ks) : zero_bf16x8();
+}
+
+// B fragments of the 32-token subtile at row `row0` of a buffer resource over a
+// row-major [rows][DR] bf16 tile; rows past the resource's end read as zero.
+template <int DR>
+__device__ __forceinline__ void load_x_buf(__amdgpu_buffer_rsrc_t rs, int64_t row0, bf16x8 (&xs)[DR / 16]) {
+    const int l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
+    const uint32_t off = uint32_t(((row0 + j) * DR + 8 * lh) * 2);
+#pragma unroll
+    for (int ks = 0; ks < DR / 16; ++ks) xs[ks] = __builtin_bit_cast(bf16x8, buf_load16(rs, off + 32 * ks));
 }
 
 // S^T for one 32-token subtile from its B fragments: acc[ct] holds the scores of
@@ -167,6 +264,28 @@ __device__ __forceinline__ void scores_x(const WaveParams<DR, CTW>& P, const bf1
         for (int ct = 0; ct < CTW; ++ct) {
             acc[ct] = mfma(P.w[ct][ks][0], xs[ks], acc[ct]);
             acc[ct] = mfma(P.w[ct][ks][1], xs[ks], acc[ct]);
+            acc[ct] = mfma(P.w[ct][ks][2], x2h, acc[ct]);
+            acc[ct] = mfma(P.w[ct][ks][3], x2h, acc[ct]);
+            acc[ct] = mfma(P.w[ct][ks][2], x2l, acc[ct]);
+        }
+    }
+}
+
+// Scores of token subtile ts from an XTile in LDS.
+template <int DR, int CTW>
+__device__ __forceinline__ void scores_lds(const WaveParams<DR, CTW>& P, const u32x4* xt, int ts, f32x16 (&acc)[CTW]) {
+#pragma unroll
+    for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[ct][r] = P.c[ct][r];
+#pragma unroll
+    for (int ks = 0; ks < DR / 16; ++ks) {
+        bf16x8 x, x2h, x2l;
+        xtile_frags<DR>(xt, ts, ks, x, x2h, x2l);
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+            acc[ct] = mfma(P.w[ct][ks][0], x, acc[ct]);
+            acc[ct] = mfma(P.w[ct][ks][1], x, acc[ct]);
             acc[ct] = mfma(P.w[ct][ks][2], x2h, acc[ct]);
             acc[ct] = mfma(P.w[ct][ks][3], x2h, acc[ct]);
             acc[ct] = mfma(P.w[ct][ks][2], x2l, acc[ct]);

@@ -49,14 +49,34 @@ struct ScanStats {
     float m, L, D;
 };
 
+// LDS bytes of scan_kernel for a chunk of CH positions (mirrors the declarations below).
 template <int DR, int KT, int VT, int CH>
+constexpr int scan_lds_bytes() {
+    using S = Split<DR, KT>;
+    constexpr int Kp = KT * 32, DV = VT * 32, SUB = CH / 32;
+    constexpr int JPW = (2 * SUB + S::TS - 1) / S::TS;
+    constexpr int xt = S::CS > 1 ? 2 * XTile<DR, CH, S::NW * 64>::LDS_BYTES : 32;
+    return JPW * S::TS * S::CS * 32 * 12 + 2 * CH * (Kp + 8) * 2 + 2 * CH * (DV + 8) * 2 + CH * (CH + 8) * 2 + xt +
+           CH * 4 + SUB * CH * 4 + Kp * 4;
+}
+
+// The chunk actually used: the requested one, halved while its tiles exceed the 160 KiB of
+// LDS (the chunk length only changes the order of the sums).
+template <int DR, int KT, int VT, int CH_REQ>
+constexpr int scan_chunk() {
+    return (CH_REQ > 32 && scan_lds_bytes<DR, KT, VT, CH_REQ>() > 160 * 1024) ? CH_REQ / 2 : CH_REQ;
+}
+
+template <int DR, int KT, int VT, int CH_REQ>
 __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
     scan_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
                 int64_t N, int H, int64_t seg, int G, const uint16_t* planes, const float* cvec,
                 const float* __restrict__ prefix, float eps, uint16_t* __restrict__ O) {
+    constexpr int CH = scan_chunk<DR, KT, VT, CH_REQ>();
     using S = Split<DR, KT>;
+    constexpr int NT = S::NW * 64;
     constexpr int Kp = KT * 32, DV = VT * 32;
-    constexpr int NW = S::NW, CS = S::CS, TS = S::TS, CTW = S::CTW;
+    constexpr int NW = S::NW, CS = S::CS, TS = S::TS, CTW = S::CTW, KS = S::KS;
     constexpr int LDG = Kp + 8, LDV = DV + 8, LDSS = CH + 8;
     constexpr int SUB = CH / 32;                  // 32-token subtiles per chunk
     constexpr int JOBS = 2 * SUB;                 // query subtiles, then key subtiles
@@ -66,12 +86,19 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
     constexpr int CPW = (C16 + NW - 1) / NW;      // column tiles per wave
     constexpr int KT16 = Kp / 16;                 // 16-row component tiles of the memory
     constexpr int STILES = SUB * (SUB + 1) / 2;   // lower-triangular tiles of S^T
+    constexpr int VCH = (CH * DV / 8 + NT - 1) / NT;
+    // x tiles: split once and shared through LDS when several waves use the same token
+    // subtile (CS > 1); otherwise every wave prefetches its own fragments into registers
+    constexpr bool SHARE_X = CS > 1;
+    using XT = XTile<DR, CH, NT>;
 
     __shared__ ScanStats st[JPW][TS * CS * 32];
     __shared__ __attribute__((aligned(16))) uint16_t Gq[CH * LDG];
     __shared__ __attribute__((aligned(16))) uint16_t Gk[CH * LDG];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[CH * LDV];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][CH * LDV];
     __shared__ __attribute__((aligned(16))) uint16_t Ss[CH * LDSS];
+    __shared__ __attribute__((aligned(16))) u32x4 XtQ[SHARE_X ? XT::LDS_BYTES / 16 : 1];
+    __shared__ __attribute__((aligned(16))) u32x4 XtK[SHARE_X ? XT::LDS_BYTES / 16 : 1];
     __shared__ float den_inter[CH];
     __shared__ float den_part[SUB][CH];
     __shared__ float Zs[Kp];
@@ -82,13 +109,48 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
     const int64_t p = blockIdx.y;
     const int seg_idx = blockIdx.x;
     const int h = int(p % H);
+    const int64_t lo = int64_t(seg_idx) * seg, hi = min<int64_t>(lo + seg, N);
+    const int64_t rows = hi - lo;
 
     WaveParams<DR, CTW> P;
     P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * CTW);
-    const uint16_t* Xq = XQ + size_t(p) * N * DR;
-    const uint16_t* Xk = XK + size_t(p) * N * DR;
-    const uint16_t* Vp = V + size_t(p) * N * DV;
-    const int64_t lo = int64_t(seg_idx) * seg, hi = min<int64_t>(lo + seg, N);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(XQ + (size_t(p) * N + lo) * DR, rows * DR * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(XK + (size_t(p) * N + lo) * DR, rows * DR * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t(p) * N + lo) * DV, rows * DV * 2);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + (size_t(p) * N + lo) * DV, rows * DV * 2);
+
+    // ---- input pipeline: chunk c is consumed while chunk c+1 sits in LDS / registers and
+    // chunk c+2 is in flight
+    u32x4 vr[VCH];
+    auto load_v = [&](int64_t row0) {
+#pragma unroll
+        for (int u = 0; u < VCH; ++u) {
+            const int c = threadIdx.x + u * NT;
+            vr[u] = (c < CH * DV / 8) ? buf_load16(rv, uint32_t((row0 * DV + int64_t(c) * 8) * 2))
+                                      : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto commit_v = [&](uint16_t* dst) {
+#pragma unroll
+        for (int u = 0; u < VCH; ++u) {
+            const int c = threadIdx.x + u * NT;
+            if (c < CH * DV / 8) {
+                const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
+                *reinterpret_cast<u32x4*>(dst + row * LDV + col) = vr[u];
+            }
+        }
+    };
+    XT xq, xk;                      // SHARE_X: whole-tile chunks of the next chunk
+    bf16x8 xf[JPW][KS], xn[JPW][KS];  // !SHARE_X: this wave's fragments, this and next chunk
+    auto load_frags = [&](int64_t row0, bf16x8 (&dst)[JPW][KS]) {
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) {
+            const int job = ts + jj * TS;
+            const bool is_q = job < SUB;
+            const int sub = is_q ? job : job - SUB;
+            load_x_buf<DR>(is_q ? rq : rk, (job < JOBS) ? row0 + sub * 32 : int64_t(1) << 40, dst[jj]);
+        }
+    };
 
     // starting memory of the segment: the sum of the aggregates of segments 0 .. seg_idx-1
     // (each stored as VtT [DV][Kp] then Z [Kp]), added in increasing segment order
@@ -99,7 +161,16 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
     for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
         for (int kt = 0; kt < KT16; ++kt) mem[cc][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k = threadIdx.x; k < Kp; k += NW * 64) Zs[k] = 0.0f;
+    for (int k = threadIdx.x; k < Kp; k += NT) Zs[k] = 0.0f;
+
+    // prologue loads are issued before the prefix sum so they overlap it
+    load_v(0);
+    if (SHARE_X) {
+        xq.load(rq, 0);
+        xk.load(rk, 0);
+    } else {
+        load_frags(0, xf);
+    }
     for (int gs = 0; gs < seg_idx; ++gs) {
         const float* a = agg + size_t(gs) * E;
 #pragma unroll
@@ -116,25 +187,34 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
                 }
             }
         }
-        for (int k = threadIdx.x; k < Kp; k += NW * 64) Zs[k] += a[size_t(Kp) * DV + k];
+        for (int k = threadIdx.x; k < Kp; k += NT) Zs[k] += a[size_t(Kp) * DV + k];
+    }
+    commit_v(Vs[0]);
+    load_v(CH);
+    if (SHARE_X) {
+        xq.commit(XtQ);
+        xk.commit(XtK);
+        xq.load(rq, CH);
+        xk.load(rk, CH);
+    } else {
+        load_frags(CH, xn);
     }
 
-    for (int64_t nc = lo; nc < hi; nc += CH) {
-        __syncthreads();  // B0: previous chunk's tiles consumed, Zs updated
+    int vb = 0;
+    for (int64_t nc = 0; nc < rows; nc += CH, vb ^= 1) {
+        __syncthreads();  // B0: previous chunk consumed; this chunk's inputs and Zs visible
         // ---- phase L: scores and softmax of the chunk's query and key rows
         float zr[CTW][16];
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) zr[ct][r] = Zs[(cs * CTW + ct) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)];
-        // value rows of the chunk -> LDS (rows past the segment read as zero)
-        for (int c = threadIdx.x; c < CH * DV / 8; c += NW * 64) {
-            const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (nc + row < hi) v = *reinterpret_cast<const u32x4*>(Vp + (nc + row) * DV + col);
-            *reinterpret_cast<u32x4*>(Vs + row * LDV + col) = v;
-        }
-        // score jobs in groups of JG (one statistics barrier per group)
+            for (int q = 0; q < 4; ++q) {
+                const float4 z4 = *reinterpret_cast<const float4*>(Zs + (cs * CTW + ct) * 32 + 8 * q + 4 * lh);
+                zr[ct][4 * q + 0] = z4.x;
+                zr[ct][4 * q + 1] = z4.y;
+                zr[ct][4 * q + 2] = z4.z;
+                zr[ct][4 * q + 3] = z4.w;
+            }
 #pragma unroll
         for (int jg = 0; jg < JPW; jg += JG) {
             f32x16 acc[JG][CTW];
@@ -146,9 +226,11 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
                 const int job = ts + jj * TS;
                 const bool is_q = job < SUB;
                 const int sub = is_q ? job : job - SUB;
-                const int64_t n0 = nc + sub * 32;
-                valid_j[u] = (jj < JPW && job < JOBS) ? int(max<int64_t>(0, min<int64_t>(32, hi - n0))) : 0;
-                scores<DR, CTW>(P, is_q ? Xq : Xk, n0, valid_j[u], acc[u]);
+                valid_j[u] = (jj < JPW && job < JOBS) ? int(max<int64_t>(0, min<int64_t>(32, rows - nc - sub * 32))) : 0;
+                if (SHARE_X)
+                    scores_lds<DR, CTW>(P, is_q ? XtQ : XtK, sub, acc[u]);
+                else
+                    scores_x<DR, CTW>(P, xf[jj < JPW ? jj : 0], acc[u]);
                 local_softmax<CTW, true>(acc[u], zr, sm[u], sL[u], sD[u]);
                 if (CS > 1 && lh == 0 && jj < JPW) st[jj][(ts * CS + cs) * 32 + j] = ScanStats{sm[u], sL[u], sD[u]};
             }
@@ -171,10 +253,10 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
                     float Lt = 0.0f, Dt = 0.0f;
 #pragma unroll
                     for (int c = 0; c < CS; ++c) {
-                        const ScanStats s = st[jj][(ts * CS + c) * 32 + j];
-                        const float f = __builtin_amdgcn_exp2f(s.m - mm);
-                        Lt = fmaf(s.L, f, Lt);
-                        Dt = fmaf(s.D, f, Dt);
+                        const ScanStats sc = st[jj][(ts * CS + c) * 32 + j];
+                        const float f = __builtin_amdgcn_exp2f(sc.m - mm);
+                        Lt = fmaf(sc.L, f, Lt);
+                        Dt = fmaf(sc.D, f, Dt);
                     }
                     scale = __builtin_amdgcn_exp2f(sm[u] - mm) / Lt;
                     dl = Dt / Lt;
@@ -184,39 +266,57 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
                 if (is_q && cs == 0 && lh == 0) den_inter[sub * 32 + j] = dl;
             }
         }
-        __syncthreads();  // B2: Gq, Gk, Vs complete
+        if (!SHARE_X) {
+#pragma unroll
+            for (int jj = 0; jj < JPW; ++jj)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) xf[jj][ks] = xn[jj][ks];
+            load_frags(nc + 2 * CH, xn);
+        }
+        __syncthreads();  // B2: Gq, Gk complete; this chunk's x tiles consumed
+        // next chunk's inputs into the buffers that are now free; the loads of the one
+        // after are issued
+        commit_v(Vs[vb ^ 1]);
+        load_v(nc + 2 * CH);
+        if (SHARE_X) {
+            xq.commit(XtQ);
+            xk.commit(XtK);
+            xq.load(rq, nc + 2 * CH);
+            xk.load(rk, nc + 2 * CH);
+        }
         // ---- phase S: S^T tiles (rows = key positions, cols = query positions)
         if (wave < STILES) {
             int qt = 0, kt = wave;
             while (kt > qt) { kt -= qt + 1; ++qt; }
-            f32x16 s;
+            f32x16 sacc;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[r] = 0.0f;
+            for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < Kp / 16; ++ks) {
                 bf16x8 a = read_rowfrag(Gk, LDG, kt * 32 + j, 16 * ks);
                 bf16x8 b = read_rowfrag(Gq, LDG, qt * 32 + j, 16 * ks);
-                s = mfma(a, b, s);
+                sacc = mfma(a, b, sacc);
             }
             float rs = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int kk = kt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-                if (kk > qt * 32 + j) s[r] = 0.0f;  // j > i is outside the causal support
-                rs += s[r];
+                if (kk > qt * 32 + j) sacc[r] = 0.0f;  // j > i is outside the causal support
+                rs += sacc[r];
             }
             rs = xsum32(rs);
             if (lh == 0) den_part[kt][qt * 32 + j] = rs;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 u32x2 v;
-                v[0] = pack_bf16x2(s[4 * q + 0], s[4 * q + 1]);
-                v[1] = pack_bf16x2(s[4 * q + 2], s[4 * q + 3]);
+                v[0] = pack_bf16x2(sacc[4 * q + 0], sacc[4 * q + 1]);
+                v[1] = pack_bf16x2(sacc[4 * q + 2], sacc[4 * q + 3]);
                 *reinterpret_cast<u32x2*>(Ss + (qt * 32 + j) * LDSS + kt * 32 + 8 * q + 4 * lh) = v;
             }
         }
         __syncthreads();  // B3: S tiles and row sums complete
         // ---- phase O: outputs of this wave's value columns, then the memory update
+        const uint16_t* Vc = Vs[vb];
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc) {
             const int c16 = wave + cc * NW;
@@ -228,7 +328,7 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
                 // intra-chunk part: V^T S^T over key positions up to this query tile
 #pragma unroll
                 for (int ks = 0; ks < (t16 * 16 + 16 + 31) / 32; ++ks) {
-                    bf16x8 a = read_colfrag16(Vs, LDV, 32 * ks, c16 * 16);
+                    bf16x8 a = read_colfrag16(Vc, LDV, 32 * ks, c16 * 16);
                     bf16x8 b = *reinterpret_cast<const bf16x8*>(Ss + (t16 * 16 + i16) * LDSS + 32 * ks + 8 * g4);
                     o[t16] = mfma16(a, b, o[t16]);
                 }
@@ -242,9 +342,9 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
                     const int v0 = 2 * q, v1 = 2 * q + 1;
                     const float x0 = mem[cc][2 * m2 + (v0 >> 2)][v0 & 3];
                     const float x1 = mem[cc][2 * m2 + (v1 >> 2)][v1 & 3];
-                    const uint16_t h0 = f32_to_bf16_bits(x0), h1 = f32_to_bf16_bits(x1);
-                    ah[q] = uint32_t(h0) | (uint32_t(h1) << 16);
-                    al[q] = pack_bf16x2(x0 - bf16_bits_to_f32(h0), x1 - bf16_bits_to_f32(h1));
+                    const uint32_t hb = pack_bf16x2(x0, x1);
+                    ah[q] = hb;
+                    al[q] = pack_bf16x2(x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u));
                 }
 #pragma unroll
                 for (int t16 = 0; t16 < CH / 16; ++t16) {
@@ -259,18 +359,16 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
 #pragma unroll
             for (int t16 = 0; t16 < CH / 16; ++t16) {
                 const int qrow = t16 * 16 + i16;
-                const int64_t tok = nc + qrow;
-                if (tok < hi) {
-                    float den = den_inter[qrow] + eps;
+                float den = den_inter[qrow] + eps;
 #pragma unroll
-                    for (int kt = 0; kt < SUB; ++kt)
-                        if (kt * 32 <= qrow) den += den_part[kt][qrow];
-                    const float rden = 1.0f / den;
-                    u32x2 v;
-                    v[0] = pack_bf16x2(o[t16][0] * rden, o[t16][1] * rden);
-                    v[1] = pack_bf16x2(o[t16][2] * rden, o[t16][3] * rden);
-                    *reinterpret_cast<u32x2*>(O + (size_t(p) * N + tok) * DV + c16 * 16 + 4 * g4) = v;
-                }
+                for (int kt = 0; kt < SUB; ++kt)
+                    if (kt * 32 <= qrow) den += den_part[kt][qrow];
+                const float rden = 1.0f / den;
+                u32x2 v;
+                v[0] = pack_bf16x2(o[t16][0] * rden, o[t16][1] * rden);
+                v[1] = pack_bf16x2(o[t16][2] * rden, o[t16][3] * rden);
+                // rows past the segment fall outside the resource and are dropped
+                buf_store8(ro, uint32_t(((nc + qrow) * DV + c16 * 16 + 4 * g4) * 2), v);
             }
         }
         // memory update: Vt += Gk^T Vc (every wave its columns), Z += Gk^T 1 (wave 0)
@@ -290,7 +388,7 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
                 for (int cc = 0; cc < CPW; ++cc) {
                     const int c16 = wave + cc * NW;
                     if (c16 < C16) {
-                        const bf16x8 b = read_colfrag16(Vs, LDV, 32 * ks, c16 * 16);
+                        const bf16x8 b = read_colfrag16(Vc, LDV, 32 * ks, c16 * 16);
                         mem[cc][kt] = mfma16(a, b, mem[cc][kt]);
                     }
                 }
