@@ -50,7 +50,7 @@ __global__ void __launch_bounds__(256) params_kernel(const float* __restrict__ m
                                                      uint16_t* __restrict__ planes, float* __restrict__ cvec) {
     const double L2E = 1.4426950408889634;
     const int h = blockIdx.y;
-    const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int k = blockIdx.x * 4 + wave_id();
     if (k >= Kp) return;
     uint16_t* ph = planes + size_t(h) * 4 * Kp * dr;
     const float* mu_h = mu + size_t(h) * K * dr;
@@ -93,8 +93,9 @@ template <int CS>
 __device__ __forceinline__ float combine_stats(const Stats* st, int ts, int cs, int j, float m, float L, float D,
                                                float& DoverL) {
     if (CS == 1) {
-        DoverL = D / L;
-        return 1.0f / L;
+        const float r = __builtin_amdgcn_rcpf(L);
+        DoverL = D * r;
+        return r;
     }
     float mm = -INFINITY;
 #pragma unroll
@@ -108,8 +109,9 @@ __device__ __forceinline__ float combine_stats(const Stats* st, int ts, int cs, 
         Dt = fmaf(s.D, f, Dt);
     }
     (void)cs;
-    DoverL = Dt / Lt;
-    return __builtin_amdgcn_exp2f(m - mm) / Lt;
+    const float r = __builtin_amdgcn_rcpf(Lt);
+    DoverL = Dt * r;
+    return __builtin_amdgcn_exp2f(m - mm) * r;
 }
 
 // ---------------------------------------------------------------------------- responsibilities
@@ -122,7 +124,7 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) resp_kernel(const ui
     using S = Split<DR, KT>;
     constexpr int Kp = KT * 32;
     __shared__ Stats st[S::TS * S::CS * 32];
-    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
+    const int wave = wave_id(), l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
     const int cs = wave % S::CS, ts = wave / S::CS;
     const int64_t p = blockIdx.y;
     const int h = int(p % H);
@@ -183,13 +185,19 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
     constexpr int PAIRS = KT * (VT + 1);  // value column tiles plus the ones column (Z)
     constexpr int PW = (PAIRS + S::NW - 1) / S::NW;
     using XT = XTile<DR, S::ROUND, NT>;
-    constexpr int VCH = (S::ROUND * DV / 8 + NT - 1) / NT;
+    constexpr int VCHUNKS = S::ROUND * DV / 8;
+    constexpr int VCH = (VCHUNKS + NT - 1) / NT;
+    constexpr bool VEVEN = VCHUNKS % NT == 0;
     __shared__ Stats st[S::TS * S::CS * 32];
     __shared__ __attribute__((aligned(16))) u32x4 Xt[XT::LDS_BYTES / 16];
     __shared__ __attribute__((aligned(16))) uint16_t Gs[S::ROUND * LDG];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[S::ROUND * LDV];
+    // 32 bf16 ones: read with row stride 0 they form the all-ones B operand that turns
+    // the same MFMA into Z = Gamma_K^T 1, so every pair fetches its B operand the same
+    // way (no per-wave branch around the LDS reads)
+    __shared__ __attribute__((aligned(16))) uint16_t Ones[32];
 
-    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
+    const int wave = wave_id(), l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
     const int cs = wave % S::CS, ts = wave / S::CS;
     const int64_t p = blockIdx.y;
     const int g_idx = blockIdx.x;
@@ -206,13 +214,14 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
             const int c = threadIdx.x + u * NT;
-            vr[u] = (c < S::ROUND * DV / 8) ? buf_load16(rv, uint32_t((row0 * DV + int64_t(c) * 8) * 2))
-                                            : u32x4{0u, 0u, 0u, 0u};
+            vr[u] = (VEVEN || c < VCHUNKS) ? buf_load16(rv, uint32_t((row0 * DV + int64_t(c) * 8) * 2))
+                                           : u32x4{0u, 0u, 0u, 0u};
         }
     };
     // prologue: x tile of round 0 into LDS; V of round 0 and x of round 1 in flight
     xt.load(rx, 0);
     load_v(0);
+    if (threadIdx.x < 16) reinterpret_cast<uint32_t*>(Ones)[threadIdx.x] = 0x3f803f80u;
     xt.commit(Xt);
     xt.load(rx, S::ROUND);
     __syncthreads();
@@ -222,7 +231,6 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
     for (int q = 0; q < PW; ++q)
 #pragma unroll
         for (int r = 0; r < 16; ++r) wacc[q][r] = 0.0f;
-    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
     float zr[S::CTW][16];
 
     for (int64_t r0 = 0; r0 < hi - lo; r0 += S::ROUND) {
@@ -240,7 +248,7 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
             const int c = threadIdx.x + u * NT;
-            if (c < S::ROUND * DV / 8) {
+            if (VEVEN || c < VCHUNKS) {
                 const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
                 *reinterpret_cast<u32x4*>(Vs + row * LDV + col) = vr[u];
             }
@@ -254,10 +262,12 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
             const int pair = wave + q * S::NW;
             if (pair < PAIRS) {
                 const int ct = pair / (VT + 1), vt = pair - ct * (VT + 1);
+                const uint16_t* bt = (vt < VT) ? Vs + vt * 32 : Ones;
+                const int bld = (vt < VT) ? LDV : 0;
 #pragma unroll
                 for (int ks = 0; ks < S::ROUND / 16; ++ks) {
                     const bf16x8 a = read_colfrag(Gs, LDG, 16 * ks, ct * 32);
-                    const bf16x8 b = (vt < VT) ? read_colfrag(Vs, LDV, 16 * ks, vt * 32) : ones;
+                    const bf16x8 b = read_colfrag(bt, bld, 16 * ks, 0);
                     wacc[q] = mfma(a, b, wacc[q]);
                 }
             }
@@ -338,7 +348,7 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
     __shared__ __attribute__((aligned(16))) uint16_t Ms[MS_LDS ? 2 * DV * LDM : 8];
     __shared__ float den_s[S::ROUND];
 
-    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
+    const int wave = wave_id(), l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
     const int cs = wave % S::CS, ts = wave / S::CS;
     const int64_t p = blockIdx.y;
     const int h = int(p % H);
@@ -347,10 +357,17 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
     P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * S::CTW);
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(XQ + (size_t(p) * N + lo) * DR, (hi - lo) * DR * 2);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + (size_t(p) * N + lo) * DV, (hi - lo) * DV * 2);
+    // latent memory of this problem: Z -> registers in score-row order (loaded before the
+    // x tile, so the tile's wait covers it), VtT hi/lo -> LDS
+    const uint16_t* mp = memory + size_t(p) * Kp * (DV + 1) * 2;
+    const float* Zp = reinterpret_cast<const float*>(mp + size_t(2) * DV * Kp);
+    float zr[S::CTW][16];
+#pragma unroll
+    for (int ct = 0; ct < S::CTW; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) zr[ct][r] = Zp[(cs * S::CTW + ct) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)];
     XT xt;
     xt.load(rx, 0);
-    // latent memory of this problem: VtT hi/lo -> LDS, Z -> registers in score-row order
-    const uint16_t* mp = memory + size_t(p) * Kp * (DV + 1) * 2;
     if (MS_LDS)
         for (int c = threadIdx.x; c < 2 * DV * Kp / 8; c += NT) {
             const int row = c / (Kp / 8), col = (c - row * (Kp / 8)) * 8;
@@ -359,12 +376,6 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
         }
     const uint16_t* Msrc = MS_LDS ? Ms : mp;
     constexpr int LDMS = MS_LDS ? LDM : Kp;
-    const float* Zp = reinterpret_cast<const float*>(mp + size_t(2) * DV * Kp);
-    float zr[S::CTW][16];
-#pragma unroll
-    for (int ct = 0; ct < S::CTW; ++ct)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) zr[ct][r] = Zp[(cs * S::CTW + ct) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)];
     xt.commit(Xt);
     xt.load(rx, S::ROUND);
     __syncthreads();
@@ -416,7 +427,7 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
                     o = mfma(ah, b, o);
                     o = mfma(al, b, o);
                 }
-                const float rden = 1.0f / den_s[tsub * 32 + j];
+                const float rden = __builtin_amdgcn_rcpf(den_s[tsub * 32 + j]);
                 const uint32_t off = uint32_t(((r0 + tsub * 32 + j) * DV + vt * 32 + 4 * lh) * 2);
 #pragma unroll
                 for (int qq = 0; qq < 4; ++qq) {

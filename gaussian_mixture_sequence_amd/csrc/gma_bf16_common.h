@@ -36,6 +36,11 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Index of this wave in its workgroup, as a wave-uniform (scalar) value: without the
+// readfirstlane the compiler cannot prove uniformity, keeps everything derived from it in
+// VGPRs and turns buffer loads whose resource depends on it into per-lane waterfall loops.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)); }
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -108,26 +113,29 @@ struct XTile {
     static constexpr int NW = NTHREADS / 64;
     static constexpr int FRAGS = (ROUND / 32) * KS;
     static constexpr int PER_WAVE = (FRAGS + NW - 1) / NW;
+    static constexpr bool EVEN = FRAGS % NW == 0;
     static constexpr int LDS_BYTES = FRAGS * 3 * 64 * 16;
     u32x4 r[PER_WAVE];
 
     // fragments of the tile that starts `row0` rows into the resource
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t row0) {
-        const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
+        const int wave = wave_id(), l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
 #pragma unroll
         for (int u = 0; u < PER_WAVE; ++u) {
             const int fi = wave + u * NW;
             const int ts = fi / KS, ks = fi - ts * KS;
-            r[u] = (fi < FRAGS) ? buf_load16(rs, uint32_t(((row0 + ts * 32 + j) * DR + 16 * ks + 8 * lh) * 2))
-                                : u32x4{0u, 0u, 0u, 0u};
+            // EVEN: every wave owns exactly PER_WAVE fragments, so no load is predicated
+            // and the compiler can count outstanding loads exactly (no vmcnt(0) drains)
+            r[u] = (EVEN || fi < FRAGS) ? buf_load16(rs, uint32_t(((row0 + ts * 32 + j) * DR + 16 * ks + 8 * lh) * 2))
+                                        : u32x4{0u, 0u, 0u, 0u};
         }
     }
     __device__ __forceinline__ void commit(u32x4* lds) const {
-        const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+        const int wave = wave_id(), l = threadIdx.x & 63;
 #pragma unroll
         for (int u = 0; u < PER_WAVE; ++u) {
             const int fi = wave + u * NW;
-            if (fi < FRAGS) {
+            if (EVEN || fi < FRAGS) {
                 u32x4 h, lo;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {

@@ -103,7 +103,7 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
     __shared__ float den_part[SUB][CH];
     __shared__ float Zs[Kp];
 
-    const int wave = threadIdx.x >> 6, l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
+    const int wave = wave_id(), l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
     const int g4 = l >> 4, i16 = l & 15;
     const int cs = wave % CS, ts = wave / CS;
     const int64_t p = blockIdx.y;
@@ -200,8 +200,11 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
         load_frags(CH, xn);
     }
 
-    int vb = 0;
-    for (int64_t nc = 0; nc < rows; nc += CH, vb ^= 1) {
+    // One chunk.  `xc` holds this chunk's x fragments (!SHARE_X) and is refilled with the
+    // chunk after next once the scores are taken; the loop below alternates the two
+    // fragment buffers and the two V buffers statically, so no register copy (and no
+    // wait on loads still in flight) sits on the loop back-edge.
+    auto chunk = [&](const int64_t nc, const int vb, bf16x8 (&xc)[JPW][KS]) __attribute__((always_inline)) {
         __syncthreads();  // B0: previous chunk consumed; this chunk's inputs and Zs visible
         // ---- phase L: scores and softmax of the chunk's query and key rows
         float zr[CTW][16];
@@ -230,7 +233,7 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
                 if (SHARE_X)
                     scores_lds<DR, CTW>(P, is_q ? XtQ : XtK, sub, acc[u]);
                 else
-                    scores_x<DR, CTW>(P, xf[jj < JPW ? jj : 0], acc[u]);
+                    scores_x<DR, CTW>(P, xc[jj < JPW ? jj : 0], acc[u]);
                 local_softmax<CTW, true>(acc[u], zr, sm[u], sL[u], sD[u]);
                 if (CS > 1 && lh == 0 && jj < JPW) st[jj][(ts * CS + cs) * 32 + j] = ScanStats{sm[u], sL[u], sD[u]};
             }
@@ -266,13 +269,7 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
                 if (is_q && cs == 0 && lh == 0) den_inter[sub * 32 + j] = dl;
             }
         }
-        if (!SHARE_X) {
-#pragma unroll
-            for (int jj = 0; jj < JPW; ++jj)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) xf[jj][ks] = xn[jj][ks];
-            load_frags(nc + 2 * CH, xn);
-        }
+        if (!SHARE_X) load_frags(nc + 2 * CH, xc);
         __syncthreads();  // B2: Gq, Gk complete; this chunk's x tiles consumed
         // next chunk's inputs into the buffers that are now free; the loads of the one
         // after are issued
@@ -402,6 +399,13 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
                 if (g4 == 0) Zs[kt * 16 + i16] += z;
             }
         }
+    };
+    // Chunks run in pairs.  A chunk past the segment end (odd chunk count) is harmless:
+    // its loads read zeros, its rows get zero responsibilities (no memory update) and
+    // its stores fall outside the output resource.
+    for (int64_t nc = 0; nc < rows; nc += 2 * CH) {
+        chunk(nc, 0, xf);
+        chunk(nc + CH, 1, xn);
     }
 }
 
