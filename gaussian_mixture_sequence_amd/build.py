@@ -31,9 +31,6 @@ def hipcc() -> str:
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          # MFMA accumulators in ordinary VGPRs (gfx90a+ allows it): avoids the AGPR<->VGPR
-          # copies the default heuristic inserts around every softmax
-          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Wall", "-Wno-unused-result", "-Wno-unused-function"]
 
 

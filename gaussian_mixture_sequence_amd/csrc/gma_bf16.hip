@@ -65,10 +65,13 @@ __global__ void __launch_bounds__(256) params_kernel(const float* __restrict__ m
         const uint16_t ah = f32_to_bf16_bits(float(a)), bh = f32_to_bf16_bits(float(b));
         const uint16_t al = f32_to_bf16_bits(float(a - double(bf16_bits_to_f32(ah))));
         const uint16_t bl = f32_to_bf16_bits(float(b - double(bf16_bits_to_f32(bh))));
-        ph[(size_t(0) * Kp + k) * dr + d] = ah;
-        ph[(size_t(1) * Kp + k) * dr + d] = al;
-        ph[(size_t(2) * Kp + k) * dr + d] = bh;
-        ph[(size_t(3) * Kp + k) * dr + d] = bl;
+        // fragment-major: [ct][ks][plane][lane][8], lane = 32 * ((d / 8) % 2) + k % 32, so a
+        // wave fetches each of its MFMA A fragments as one contiguous 1 KiB block
+        const size_t f = ((size_t(k >> 5) * (dr / 16) + (d >> 4)) * 4) * 64 + 32 * ((d >> 3) & 1) + (k & 31);
+        ph[(f + 0 * 64) * 8 + (d & 7)] = ah;
+        ph[(f + 1 * 64) * 8 + (d & 7)] = al;
+        ph[(f + 2 * 64) * 8 + (d & 7)] = bh;
+        ph[(f + 3 * 64) * 8 + (d & 7)] = bl;
     }
     if (k < K) {
         const double ck = score_constant(mu_h + size_t(k) * dr, s2_h + size_t(k) * dr, pi[size_t(h) * K + k], dr);
@@ -166,12 +169,21 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) resp_kernel(const ui
 
 // ---------------------------------------------------------------------------- write (Gamma_K^T [V | 1])
 
-// Rows [lo, hi) of one problem.  Per round of ROUND tokens:
-//   scores of this wave's (token subtile, component group) from the shared x tile
-//   -> softmax statistics -> B1 -> Gamma_K (bf16) and the V tile into LDS; the next
-//   round's x tile is split into LDS and the loads of the round after are issued
-//   -> B2 -> MFMA: Vt^T partial += V^T Gamma_K and Z += Gamma_K^T 1 (ones column).
-// Loads go through buffer resources ending at `hi`, so tails read zeros without branches.
+// Rows [lo, hi) of one problem, in rounds of ROUND tokens, software-pipelined so that
+// every wave keeps the matrix cores and the vector ALU busy at the same time.
+// Iteration r, region A (one basic block, MFMA and VALU interleaved):
+//   MFMAs of round r+1's scores (x tile r+1, in LDS) and of round r-1's accumulation
+//   Vt^T += V^T Gamma_K, Z += Gamma_K^T 1 (Gamma_K and V tiles r-1, in LDS);
+//   VALU: softmax statistics of round r (scores issued in iteration r-1) and, with a
+//   double-buffered x tile, the split of x tile r+2 into its free buffer  -> B1
+// Region B: Gamma_K of round r (bf16) and V tile r into LDS (single x buffer: x tile r+2
+//   too); loads of V r+1 and x r+3 issued  -> B2
+// Every LDS overwrite follows a barrier that all reads of the old contents precede (a
+// wave's LDS reads complete before the MFMAs that use them issue).  Gamma_K and V start
+// zeroed, so round -1's accumulation adds nothing; round R's scores (x past the end
+// reads zero) are computed and discarded.  No branch splits region A.
+constexpr int gcd_i(int a, int b) { return b == 0 ? a : gcd_i(b, a % b); }
+
 template <int DR, int KT, int VT>
 __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const uint16_t* __restrict__ XK,
                                                                         const uint16_t* __restrict__ V, int64_t N,
@@ -179,23 +191,29 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
                                                                         const uint16_t* planes, const float* cvec,
                                                                         float* __restrict__ partials) {
     using S = Split<DR, KT>;
-    constexpr int NT = S::NW * 64;
+    constexpr int NW = S::NW, NT = NW * 64;
     constexpr int Kp = KT * 32, DV = VT * 32;
     constexpr int LDG = Kp + 8, LDV = DV + 8;
-    constexpr int PAIRS = KT * (VT + 1);  // value column tiles plus the ones column (Z)
-    constexpr int PW = (PAIRS + S::NW - 1) / S::NW;
     using XT = XTile<DR, S::ROUND, NT>;
     constexpr int VCHUNKS = S::ROUND * DV / 8;
     constexpr int VCH = (VCHUNKS + NT - 1) / NT;
     constexpr bool VEVEN = VCHUNKS % NT == 0;
+    // accumulation work, identical for every wave: V units are (component tile, value
+    // tile) pairs, split along the round's k-steps when there are fewer pairs than waves;
+    // Z units are component tiles times an all-ones operand, split the same way
+    constexpr int KSR = S::ROUND / 16;
+    constexpr int VPAIRS = KT * VT;
+    constexpr int VSPLIT = NW / gcd_i(VPAIRS, NW), VU = VPAIRS * VSPLIT / NW, VKS = KSR / VSPLIT;
+    constexpr int ZSPLIT = NW / gcd_i(KT, NW), ZU = KT * ZSPLIT / NW, ZKS = KSR / ZSPLIT;
+    static_assert(KSR % VSPLIT == 0 && KSR % ZSPLIT == 0, "round too short for the accumulation split");
+    constexpr int MF_A = 5 * S::CTW * S::KS + VU * VKS + ZU * ZKS;  // MFMAs of region A
+    constexpr int BASE_LDS = S::TS * S::CS * 32 * 12 + S::ROUND * (LDG + LDV) * 2;
+    constexpr int XB = (BASE_LDS + 2 * XT::LDS_BYTES <= 80 * 1024) ? 2 : 1;  // keep two workgroups per CU
     __shared__ Stats st[S::TS * S::CS * 32];
-    __shared__ __attribute__((aligned(16))) u32x4 Xt[XT::LDS_BYTES / 16];
+    __shared__ __attribute__((aligned(16))) u32x4 Xt[XB][XT::LDS_BYTES / 16];
     __shared__ __attribute__((aligned(16))) uint16_t Gs[S::ROUND * LDG];
     __shared__ __attribute__((aligned(16))) uint16_t Vs[S::ROUND * LDV];
-    // 32 bf16 ones: read with row stride 0 they form the all-ones B operand that turns
-    // the same MFMA into Z = Gamma_K^T 1, so every pair fetches its B operand the same
-    // way (no per-wave branch around the LDS reads)
-    __shared__ __attribute__((aligned(16))) uint16_t Ones[32];
+    __shared__ float Zred[KT * ZSPLIT * 32];
 
     const int wave = wave_id(), l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
     const int cs = wave % S::CS, ts = wave / S::CS;
@@ -203,10 +221,12 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
     const int g_idx = blockIdx.x;
     const int h = int(p % H);
     const int64_t lo = int64_t(g_idx) * seg, hi = min<int64_t>(lo + seg, N);
+    const int64_t rows = hi - lo;
+    const int64_t R = (rows + S::ROUND - 1) / S::ROUND;  // rounds of this split
     WaveParams<DR, S::CTW> P;
     P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * S::CTW);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(XK + (size_t(p) * N + lo) * DR, (hi - lo) * DR * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t(p) * N + lo) * DV, (hi - lo) * DV * 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(XK + (size_t(p) * N + lo) * DR, rows * DR * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t(p) * N + lo) * DV, rows * DV * 2);
 
     XT xt;
     u32x4 vr[VCH];
@@ -218,33 +238,91 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
                                            : u32x4{0u, 0u, 0u, 0u};
         }
     };
-    // prologue: x tile of round 0 into LDS; V of round 0 and x of round 1 in flight
-    xt.load(rx, 0);
-    load_v(0);
-    if (threadIdx.x < 16) reinterpret_cast<uint32_t*>(Ones)[threadIdx.x] = 0x3f803f80u;
-    xt.commit(Xt);
-    xt.load(rx, S::ROUND);
-    __syncthreads();
-
-    f32x16 wacc[PW];
+    f32x16 vacc[VU], zacc[ZU];
 #pragma unroll
-    for (int q = 0; q < PW; ++q)
+    for (int r = 0; r < 16; ++r) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) wacc[q][r] = 0.0f;
+        for (int i = 0; i < VU; ++i) vacc[i][r] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < ZU; ++i) zacc[i][r] = 0.0f;
+    }
+    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
     float zr[S::CTW][16];
+    f32x16 acc_a_init[S::CTW];  // round 0's scores when the x tile is single-buffered
+    auto accumulate = [&]() __attribute__((always_inline)) {  // Vt^T += V^T Gamma_K, Z += Gamma_K^T 1
+#pragma unroll
+        for (int i = 0; i < VU; ++i) {
+            const int q = wave + i * NW, pair = q / VSPLIT, part = q - pair * VSPLIT;
+            const int ct = pair / VT, vt = pair - ct * VT;
+#pragma unroll
+            for (int kk = 0; kk < VKS; ++kk) {
+                const int ks = part * VKS + kk;
+                vacc[i] = mfma(read_colfrag(Gs, LDG, 16 * ks, ct * 32), read_colfrag(Vs, LDV, 16 * ks, vt * 32), vacc[i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < ZU; ++i) {
+            const int q = wave + i * NW, ct = q / ZSPLIT, part = q - ct * ZSPLIT;
+#pragma unroll
+            for (int kk = 0; kk < ZKS; ++kk)
+                zacc[i] = mfma(read_colfrag(Gs, LDG, 16 * (part * ZKS + kk), ct * 32), ones, zacc[i]);
+        }
+    };
 
-    for (int64_t r0 = 0; r0 < hi - lo; r0 += S::ROUND) {
-        const int valid = int(max<int64_t>(0, min<int64_t>(32, hi - lo - r0 - ts * 32)));
-        f32x16 acc[S::CTW];
-        scores_lds<DR, S::CTW>(P, Xt, ts, acc);
+    // prologue: Gamma_K and V tiles zeroed; x tiles 0 and 1 fetched together (one memory
+    // round trip), 0 (and 1) split into LDS; scores of round 0 issued; V 0 and x tile 2
+    // in flight
+    {
+        XT xt1;
+        xt.load(rx, 0);
+        xt1.load(rx, S::ROUND);
+        load_v(0);
+        for (int c = threadIdx.x; c < S::ROUND * LDG / 8; c += NT) reinterpret_cast<u32x4*>(Gs)[c] = u32x4{0u, 0u, 0u, 0u};
+        for (int c = threadIdx.x; c < S::ROUND * LDV / 8; c += NT) reinterpret_cast<u32x4*>(Vs)[c] = u32x4{0u, 0u, 0u, 0u};
+        xt.commit(Xt[0]);
+        xt.load(rx, 2 * S::ROUND);
+        if (XB == 2) xt1.commit(Xt[XB - 1]);
+        __syncthreads();
+        if (XB == 1) {
+            scores_lds<DR, S::CTW>(P, Xt[0], ts, acc_a_init);
+            __syncthreads();  // x tile 0 consumed by every wave
+            xt1.commit(Xt[0]);
+            __syncthreads();
+        }
+    }
+    f32x16 acc_a[S::CTW], acc_b[S::CTW];
+    if (XB == 2) scores_lds<DR, S::CTW>(P, Xt[0], ts, acc_a);
+    else
+#pragma unroll
+        for (int ct = 0; ct < S::CTW; ++ct) acc_a[ct] = acc_a_init[ct];
+
+    // one pipelined iteration; `cur` holds round r's scores, `nxt` receives round r+1's
+    auto iteration = [&](const int64_t r, f32x16 (&cur)[S::CTW], f32x16 (&nxt)[S::CTW]) __attribute__((always_inline)) {
+        const int64_t r0 = r * S::ROUND;
+        const int xb1 = int((r + 1) % XB);
+        // ---- region A (the accumulation first: its transposing LDS reads bound the
+        // scheduling region, so everything after them can be interleaved)
+        accumulate();
+        scores_lds<DR, S::CTW>(P, Xt[xb1], ts, nxt);
+        if (XB == 2) {
+            xt.commit(Xt[xb1 ^ 1]);  // x tile r+2 into the buffer x tile r left
+            xt.load(rx, r0 + 3 * S::ROUND);
+        }
         float m, L, D;
-        local_softmax<S::CTW, false>(acc, zr, m, L, D);
-        if (S::CS > 1 && lh == 0) st[(ts * S::CS + cs) * 32 + j] = Stats{m, L, 0.0f};
-        __syncthreads();  // B1: statistics published; this round's x tile and last round's tiles consumed
+        local_softmax<S::CTW, false>(cur, zr, m, L, D);
+        if (S::CS > 1) st[(ts * S::CS + cs) * 32 + j] = Stats{m, L, 0.0f};  // both lane halves hold the same
+#pragma unroll
+        for (int i = 0; i < MF_A; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then up to five VALU
+        }
+        __syncthreads();  // B1: statistics published; x tile r+1 and tiles r-1 consumed
+        // ---- region B
+        const int valid = int(max<int64_t>(0, min<int64_t>(32, rows - r0 - ts * 32)));
         float dl;
         float scale = combine_stats<S::CS>(st, ts, cs, j, m, L, 0.0f, dl);
         if (j >= valid) scale = 0.0f;
-        store_gamma_lds<S::CTW>(acc, scale, Gs, LDG, ts * 32 + j, cs * S::CTW);
+        store_gamma_lds<S::CTW>(cur, scale, Gs, LDG, ts * 32 + j, cs * S::CTW);
 #pragma unroll
         for (int u = 0; u < VCH; ++u) {
             const int c = threadIdx.x + u * NT;
@@ -254,46 +332,65 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
             }
         }
         load_v(r0 + S::ROUND);
-        xt.commit(Xt);
-        xt.load(rx, r0 + 2 * S::ROUND);
-        __syncthreads();  // B2: Gamma_K, V and the next x tile are in LDS
+        if (XB == 1) {
+            xt.commit(Xt[0]);
+            xt.load(rx, r0 + 3 * S::ROUND);
+        }
+        __syncthreads();  // B2: Gamma_K r, V r and x tile r+2 are in LDS
+    };
+    // rounds in pairs (static accumulator roles, no register copies on the back-edge); a
+    // round past the end only exists for an odd count and is skipped
+    for (int64_t r = 0; r < R; r += 2) {
+        iteration(r, acc_a, acc_b);
+        if (r + 1 < R) iteration(r + 1, acc_b, acc_a);
+    }
+    accumulate();  // the last round
+
+    // ---- partial of this split: VtT [DV][Kp] (Vt transposed) then Z [Kp].  Parts of a
+    // split unit are summed through LDS in increasing part order (the x tile area is free).
+    float* mem = partials + (size_t(p) * G + g_idx) * size_t(Kp) * (DV + 1);
+    float* red = reinterpret_cast<float*>(&Xt[0][0]);
+    static_assert(VSPLIT == 1 || VPAIRS * 1024 * 4 <= XB * XT::LDS_BYTES, "x tile area too small for the reduction");
+    __syncthreads();  // every wave is done with the x tiles
 #pragma unroll
-        for (int q = 0; q < PW; ++q) {
-            const int pair = wave + q * S::NW;
-            if (pair < PAIRS) {
-                const int ct = pair / (VT + 1), vt = pair - ct * (VT + 1);
-                const uint16_t* bt = (vt < VT) ? Vs + vt * 32 : Ones;
-                const int bld = (vt < VT) ? LDV : 0;
+    for (int i = 0; i < VU; ++i) {
+        const int q = wave + i * NW, pair = q / VSPLIT, part = q - pair * VSPLIT;
+        const int ct = pair / VT, vt = pair - ct * VT;
 #pragma unroll
-                for (int ks = 0; ks < S::ROUND / 16; ++ks) {
-                    const bf16x8 a = read_colfrag(Gs, LDG, 16 * ks, ct * 32);
-                    const bf16x8 b = read_colfrag(bt, bld, 16 * ks, 0);
-                    wacc[q] = mfma(a, b, wacc[q]);
-                }
+        for (int pp = 0; pp < VSPLIT; ++pp) {
+            if (VSPLIT > 1) {
+                if (part == pp && pp > 0)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) vacc[i][r] += red[pair * 1024 + r * 64 + l];
+                if (part == pp && pp < VSPLIT - 1)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) red[pair * 1024 + r * 64 + l] = vacc[i][r];
+                __syncthreads();
+            }
+        }
+        if (part == VSPLIT - 1) {
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+                const int comp = ct * 32 + 8 * qq + 4 * lh;
+                *reinterpret_cast<float4*>(mem + size_t(vt * 32 + j) * Kp + comp) =
+                    make_float4(vacc[i][4 * qq + 0], vacc[i][4 * qq + 1], vacc[i][4 * qq + 2], vacc[i][4 * qq + 3]);
             }
         }
     }
-    // partial of this split: VtT [DV][Kp] (Vt transposed) then Z [Kp]
-    float* mem = partials + (size_t(p) * G + g_idx) * size_t(Kp) * (DV + 1);
 #pragma unroll
-    for (int q = 0; q < PW; ++q) {
-        const int pair = wave + q * S::NW;
-        if (pair < PAIRS) {
-            const int ct = pair / (VT + 1), vt = pair - ct * (VT + 1);
-            if (vt < VT) {
+    for (int i = 0; i < ZU; ++i) {
+        const int q = wave + i * NW, ct = q / ZSPLIT, part = q - ct * ZSPLIT;
+        if (j == 0)  // every column of the ones-operand tile holds the same sums
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    const int comp = ct * 32 + 8 * qq + 4 * lh;
-                    *reinterpret_cast<float4*>(mem + size_t(vt * 32 + j) * Kp + comp) = make_float4(
-                        wacc[q][4 * qq + 0], wacc[q][4 * qq + 1], wacc[q][4 * qq + 2], wacc[q][4 * qq + 3]);
-                }
-            } else if (j == 0) {  // every column of the ones-column tile holds Z
+            for (int r = 0; r < 16; ++r) Zred[(ct * ZSPLIT + part) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)] = zacc[i][r];
+    }
+    __syncthreads();
+    for (int k = threadIdx.x; k < Kp; k += NT) {
+        const int ct = k >> 5, i = k & 31;
+        float z = 0.0f;
 #pragma unroll
-                for (int qq = 0; qq < 4; ++qq)
-                    *reinterpret_cast<float4*>(mem + size_t(Kp) * DV + ct * 32 + 8 * qq + 4 * lh) = make_float4(
-                        wacc[q][4 * qq + 0], wacc[q][4 * qq + 1], wacc[q][4 * qq + 2], wacc[q][4 * qq + 3]);
-            }
-        }
+        for (int pp = 0; pp < ZSPLIT; ++pp) z += Zred[(ct * ZSPLIT + pp) * 32 + i];
+        mem[size_t(Kp) * DV + k] = z;
     }
 }
 
@@ -327,6 +424,12 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 // and denominator of Eq. 7: with e_k = exp2(s_k - m) and L = sum_k e_k,
 //   O = sum_k e_k Vt_k / (sum_k e_k Z_k + eps L),
 // so the MFMA takes e (bf16) directly and the denominator D + eps L is formed in fp32.
+// Software-pipelined like the write kernel.  Iteration r, region A (one basic block,
+// MFMA and VALU interleaved): MFMAs of round r-1's output O^T = Vt^T e^T (e of round r-1
+// in LDS, Vt hi + lo in LDS) and of round r+1's scores; VALU: softmax statistics of round
+// r (and, with a double-buffered x tile, the split of x tile r+2)  -> B1
+// Region B: round r-1's output scaled by 1 / den and stored; e of round r and its
+// denominator into LDS (single x buffer: x tile r+2 too)  -> B2
 template <int DR, int KT, int VT>
 __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const uint16_t* __restrict__ XQ, int64_t N,
                                                                        int H, int64_t rows_per_block,
@@ -334,31 +437,38 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
                                                                        const uint16_t* __restrict__ memory, float eps,
                                                                        uint16_t* __restrict__ O) {
     using S = Split<DR, KT>;
-    constexpr int NT = S::NW * 64;
+    constexpr int NW = S::NW, NT = NW * 64;
     constexpr int Kp = KT * 32, DV = VT * 32;
     constexpr int LDG = Kp + 8, LDM = Kp + 8;
-    constexpr int PAIRS = S::TS * VT;
-    constexpr int PW = (PAIRS + S::NW - 1) / S::NW;
+    constexpr int PAIRS = S::TS * VT;  // (token subtile, value tile) output tiles per round
+    constexpr int PW = (PAIRS + NW - 1) / NW;
+    constexpr bool PEVEN = PAIRS % NW == 0;
     using XT = XTile<DR, S::ROUND, NT>;
     // VtT hi/lo staged in LDS when it fits; otherwise read from L2
     constexpr bool MS_LDS = (2 * DV * LDM + S::ROUND * LDG) * 2 + XT::LDS_BYTES <= 150 * 1024;
+    constexpr int BASE_LDS = S::TS * S::CS * 32 * 12 + S::ROUND * LDG * 2 + (MS_LDS ? 2 * DV * LDM * 2 : 0) +
+                             2 * S::ROUND * 4;
+    constexpr int XB = (BASE_LDS + 2 * XT::LDS_BYTES <= 80 * 1024) ? 2 : 1;  // keep two workgroups per CU
+    constexpr int MF_A = 5 * S::CTW * S::KS + PW * 2 * (Kp / 16);
     __shared__ Stats st[S::TS * S::CS * 32];
-    __shared__ __attribute__((aligned(16))) u32x4 Xt[XT::LDS_BYTES / 16];
+    __shared__ __attribute__((aligned(16))) u32x4 Xt[XB][XT::LDS_BYTES / 16];
     __shared__ __attribute__((aligned(16))) uint16_t Gs[S::ROUND * LDG];
     __shared__ __attribute__((aligned(16))) uint16_t Ms[MS_LDS ? 2 * DV * LDM : 8];
-    __shared__ float den_s[S::ROUND];
+    __shared__ float den_s[2][S::ROUND];
 
     const int wave = wave_id(), l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
     const int cs = wave % S::CS, ts = wave / S::CS;
     const int64_t p = blockIdx.y;
     const int h = int(p % H);
     const int64_t lo = int64_t(blockIdx.x) * rows_per_block, hi = min<int64_t>(lo + rows_per_block, N);
+    const int64_t rows = hi - lo;
+    const int64_t R = (rows + S::ROUND - 1) / S::ROUND;
     WaveParams<DR, S::CTW> P;
     P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * S::CTW);
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(XQ + (size_t(p) * N + lo) * DR, (hi - lo) * DR * 2);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + (size_t(p) * N + lo) * DV, (hi - lo) * DV * 2);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(XQ + (size_t(p) * N + lo) * DR, rows * DR * 2);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + (size_t(p) * N + lo) * DV, rows * DV * 2);
     // latent memory of this problem: Z -> registers in score-row order (loaded before the
-    // x tile, so the tile's wait covers it), VtT hi/lo -> LDS
+    // x tiles, so their wait covers it), VtT hi/lo -> LDS
     const uint16_t* mp = memory + size_t(p) * Kp * (DV + 1) * 2;
     const float* Zp = reinterpret_cast<const float*>(mp + size_t(2) * DV * Kp);
     float zr[S::CTW][16];
@@ -366,27 +476,96 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
     for (int ct = 0; ct < S::CTW; ++ct)
 #pragma unroll
         for (int r = 0; r < 16; ++r) zr[ct][r] = Zp[(cs * S::CTW + ct) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)];
-    XT xt;
-    xt.load(rx, 0);
-    if (MS_LDS)
-        for (int c = threadIdx.x; c < 2 * DV * Kp / 8; c += NT) {
-            const int row = c / (Kp / 8), col = (c - row * (Kp / 8)) * 8;
-            *reinterpret_cast<u32x4*>(Ms + row * LDM + col) =
-                *reinterpret_cast<const u32x4*>(mp + size_t(row) * Kp + col);
-        }
     const uint16_t* Msrc = MS_LDS ? Ms : mp;
     constexpr int LDMS = MS_LDS ? LDM : Kp;
-    xt.commit(Xt);
-    xt.load(rx, S::ROUND);
-    __syncthreads();
 
-    for (int64_t r0 = 0; r0 < hi - lo; r0 += S::ROUND) {
-        f32x16 acc[S::CTW];
-        scores_lds<DR, S::CTW>(P, Xt, ts, acc);
+    XT xt;
+    f32x16 acc_a[S::CTW], acc_b[S::CTW], acc_a_init[S::CTW];
+    {
+        XT xt1;
+        xt.load(rx, 0);
+        xt1.load(rx, S::ROUND);
+        if (MS_LDS)
+            for (int c = threadIdx.x; c < 2 * DV * Kp / 8; c += NT) {
+                const int row = c / (Kp / 8), col = (c - row * (Kp / 8)) * 8;
+                *reinterpret_cast<u32x4*>(Ms + row * LDM + col) =
+                    *reinterpret_cast<const u32x4*>(mp + size_t(row) * Kp + col);
+            }
+        xt.commit(Xt[0]);
+        xt.load(rx, 2 * S::ROUND);
+        if (XB == 2) xt1.commit(Xt[XB - 1]);
+        __syncthreads();
+        if (XB == 1) {
+            scores_lds<DR, S::CTW>(P, Xt[0], ts, acc_a_init);
+            __syncthreads();  // x tile 0 consumed by every wave
+            xt1.commit(Xt[0]);
+            __syncthreads();
+        }
+    }
+    if (XB == 2) scores_lds<DR, S::CTW>(P, Xt[0], ts, acc_a);
+    else
+#pragma unroll
+        for (int ct = 0; ct < S::CTW; ++ct) acc_a[ct] = acc_a_init[ct];
+
+    f32x16 o[PW];
+    auto out_mfma = [&]() __attribute__((always_inline)) {  // O^T tiles of the round whose e is in LDS
+#pragma unroll
+        for (int q = 0; q < PW; ++q) {
+            const int pair = wave + q * NW;
+            if (PEVEN || pair < PAIRS) {
+                const int tsub = pair / VT, vt = pair - tsub * VT;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[q][r] = 0.0f;
+#pragma unroll
+                for (int ks = 0; ks < Kp / 16; ++ks) {
+                    const bf16x8 b = read_rowfrag(Gs, LDG, tsub * 32 + j, 16 * ks);
+                    const bf16x8 ah = read_rowfrag(Msrc, LDMS, vt * 32 + j, 16 * ks);
+                    const bf16x8 al = read_rowfrag(Msrc + DV * LDMS, LDMS, vt * 32 + j, 16 * ks);
+                    o[q] = mfma(ah, b, o[q]);
+                    o[q] = mfma(al, b, o[q]);
+                }
+            }
+        }
+    };
+    auto out_store = [&](const int64_t rr) __attribute__((always_inline)) {  // round rr's outputs
+#pragma unroll
+        for (int q = 0; q < PW; ++q) {
+            const int pair = wave + q * NW;
+            if (PEVEN || pair < PAIRS) {
+                const int tsub = pair / VT, vt = pair - tsub * VT;
+                const float rden = __builtin_amdgcn_rcpf(den_s[rr & 1][tsub * 32 + j]);
+                const uint32_t off = uint32_t(((rr * S::ROUND + tsub * 32 + j) * DV + vt * 32 + 4 * lh) * 2);
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) {
+                    u32x2 v;
+                    v[0] = pack_bf16x2(o[q][4 * qq + 0] * rden, o[q][4 * qq + 1] * rden);
+                    v[1] = pack_bf16x2(o[q][4 * qq + 2] * rden, o[q][4 * qq + 3] * rden);
+                    buf_store8(ro, off + 16 * qq, v);  // rows past hi are dropped by the range check
+                }
+            }
+        }
+    };
+
+    auto iteration = [&](const int64_t r, f32x16 (&cur)[S::CTW], f32x16 (&nxt)[S::CTW]) __attribute__((always_inline)) {
+        const int xb1 = int((r + 1) % XB);
+        // ---- region A
+        out_mfma();  // round r-1 (on zero-padded or stale e for r = 0: never stored)
+        scores_lds<DR, S::CTW>(P, Xt[xb1], ts, nxt);
+        if (XB == 2) {
+            xt.commit(Xt[xb1 ^ 1]);
+            xt.load(rx, (r + 3) * S::ROUND);
+        }
         float m, L, D;
-        local_softmax<S::CTW, true>(acc, zr, m, L, D);
-        if (S::CS > 1 && lh == 0) st[(ts * S::CS + cs) * 32 + j] = Stats{m, L, D};
+        local_softmax<S::CTW, true>(cur, zr, m, L, D);
+        if (S::CS > 1) st[(ts * S::CS + cs) * 32 + j] = Stats{m, L, D};  // both lane halves hold the same
+#pragma unroll
+        for (int i = 0; i < MF_A; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        }
         __syncthreads();  // B1
+        // ---- region B
+        if (r > 0) out_store(r - 1);
         float scale = 1.0f, den = D + eps * L;
         if (S::CS > 1) {
             float mm = -INFINITY;
@@ -403,42 +582,20 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
             scale = __builtin_amdgcn_exp2f(m - mm);
             den = Dt + eps * Lt;
         }
-        if (S::CS > 1)
-            store_gamma_lds<S::CTW>(acc, scale, Gs, LDG, ts * 32 + j, cs * S::CTW);
-        else
-            store_gamma_lds<S::CTW>(acc, 1.0f, Gs, LDG, ts * 32 + j, cs * S::CTW);
-        if (cs == 0 && lh == 0) den_s[ts * 32 + j] = den;
-        xt.commit(Xt);
-        xt.load(rx, r0 + 2 * S::ROUND);
-        __syncthreads();  // B2
-#pragma unroll
-        for (int q = 0; q < PW; ++q) {
-            const int pair = wave + q * S::NW;
-            if (pair < PAIRS) {
-                const int tsub = pair / VT, vt = pair - tsub * VT;
-                f32x16 o;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[r] = 0.0f;
-#pragma unroll
-                for (int ks = 0; ks < Kp / 16; ++ks) {
-                    const bf16x8 b = read_rowfrag(Gs, LDG, tsub * 32 + j, 16 * ks);
-                    const bf16x8 ah = read_rowfrag(Msrc, LDMS, vt * 32 + j, 16 * ks);
-                    const bf16x8 al = read_rowfrag(Msrc + DV * LDMS, LDMS, vt * 32 + j, 16 * ks);
-                    o = mfma(ah, b, o);
-                    o = mfma(al, b, o);
-                }
-                const float rden = __builtin_amdgcn_rcpf(den_s[tsub * 32 + j]);
-                const uint32_t off = uint32_t(((r0 + tsub * 32 + j) * DV + vt * 32 + 4 * lh) * 2);
-#pragma unroll
-                for (int qq = 0; qq < 4; ++qq) {
-                    u32x2 v;
-                    v[0] = pack_bf16x2(o[4 * qq + 0] * rden, o[4 * qq + 1] * rden);
-                    v[1] = pack_bf16x2(o[4 * qq + 2] * rden, o[4 * qq + 3] * rden);
-                    buf_store8(ro, off + 16 * qq, v);  // rows past hi are dropped by the range check
-                }
-            }
+        store_gamma_lds<S::CTW>(cur, scale, Gs, LDG, ts * 32 + j, cs * S::CTW);
+        if (cs == 0 && lh == 0) den_s[r & 1][ts * 32 + j] = den;
+        if (XB == 1) {
+            xt.commit(Xt[0]);
+            xt.load(rx, (r + 3) * S::ROUND);
         }
+        __syncthreads();  // B2
+    };
+    for (int64_t r = 0; r < R; r += 2) {
+        iteration(r, acc_a, acc_b);
+        if (r + 1 < R) iteration(r + 1, acc_b, acc_a);
     }
+    out_mfma();
+    out_store(R - 1);
 }
 
 // ---------------------------------------------------------------------------- dispatch

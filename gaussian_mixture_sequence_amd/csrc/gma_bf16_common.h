@@ -191,7 +191,9 @@ __device__ __forceinline__ bf16x8 read_rowfrag(const uint16_t* tile, int ld, int
 // registers), TS = NW / CS token subtiles of 32 tokens are processed side by side.
 template <int DR, int KT>
 struct Split {
-    static constexpr int CS0 = (KT * DR) / 64;  // keeps the register-resident planes <= 64 VGPRs
+    // register-resident planes <= 64 VGPRs per wave, and at most 2 component tiles per wave
+    // (the pipelined kernels hold two rounds of scores)
+    static constexpr int CS0 = (KT * DR) / 64 > KT / 2 ? (KT * DR) / 64 : KT / 2;
     static constexpr int CS = CS0 < 1 ? 1 : (CS0 > KT ? KT : CS0);
     static constexpr int CTW = KT / CS;         // component tiles per wave
     static constexpr int NW = CS > 4 ? CS : 4;  // waves per workgroup
@@ -207,19 +209,20 @@ struct WaveParams {
     bf16x8 w[CTW][DR / 16][4];
     float c[CTW][16];
 
-    // planes: [4][Kp][DR] bf16 of one head; cvec: [Kp] fp32 of one head; ct0: first tile
+    // planes: one head's fragment-major planes [Kp/32][DR/16][4][64 lanes][8] bf16 (every
+    // fragment one contiguous 1 KiB block); cvec: [Kp] fp32 of one head; ct0: first tile
     __device__ __forceinline__ void load(const uint16_t* __restrict__ planes, const float* __restrict__ cvec,
                                          int Kp, int ct0) {
-        const int l = threadIdx.x & 63, lh = l >> 5, i = l & 31;
+        const int l = threadIdx.x & 63, lh = l >> 5;
+        (void)Kp;
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
-            const int comp = (ct0 + ct) * 32 + i;
 #pragma unroll
             for (int ks = 0; ks < DR / 16; ++ks)
 #pragma unroll
                 for (int pl = 0; pl < 4; ++pl)
                     w[ct][ks][pl] = *reinterpret_cast<const bf16x8*>(
-                        planes + (size_t(pl) * Kp + comp) * DR + 16 * ks + 8 * lh);
+                        planes + ((size_t((ct0 + ct) * (DR / 16) + ks) * 4 + pl) * 64 + l) * 8);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const float4 cv = *reinterpret_cast<const float4*>(cvec + (ct0 + ct) * 32 + 8 * q + 4 * lh);
