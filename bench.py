@@ -41,7 +41,104 @@ def parse():
     ap.add_argument("--workloads", default=",".join(DEFAULT_STEP),
                     help="comma-separated workload names that make up one step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", choices=["copy", "step"], default=None,
+                    help="run only a workload for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE: a plain device copy of "
+                         "known size (calibration) or three steps of the benchmark")
+    ap.add_argument("--traffic-summarize", metavar="DIR", default=None,
+                    help="turn the counter CSVs of the four probe runs under DIR into profiles/traffic.json")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 29  # 512 MiB: larger than the 256 MiB Infinity Cache, so the copy streams HBM
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over every kernel source; a measured traffic figure is valid only for this hash."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gaussian_mixture_sequence_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def traffic_probe(mode: str, args) -> int:
+    import torch
+    if mode == "copy":
+        # an elementwise kernel (16-byte vector loads and stores, like the library's kernels)
+        # that reads and writes COPY_BYTES each; a device-to-device copy goes through a blit
+        # kernel whose FETCH_SIZE reads half its bytes, so it is not used for calibration
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        return 0
+    args.steps, args.warmup, args.no_cpu_baseline = 3, 0, True
+    return main(args, probe_only=True)
+
+
+def traffic_summarize(d: str) -> int:
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the copy and of the step kernels, from the CSVs
+    of four runs under d: copy_fetch, copy_write, step_fetch, step_write."""
+    import csv
+    import glob
+    import re
+
+    def per_kernel(run, counter):
+        out = {}
+        for f in glob.glob(os.path.join(d, run, "*_counter_collection.csv")):
+            for row in csv.DictReader(open(f)):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = re.sub(r"\(.*", "", row["Kernel_Name"]).replace("void ", "")
+                out.setdefault(name, {}).setdefault(row["Dispatch_Id"], 0.0)
+                out[name][row["Dispatch_Id"]] += float(row["Counter_Value"])
+        return {k: sum(v.values()) / len(v) * 1024.0 for k, v in out.items()}  # bytes per dispatch
+
+    cf, cw = per_kernel("copy_fetch", "FETCH_SIZE"), per_kernel("copy_write", "WRITE_SIZE")
+    copy_name = max(cf, key=cf.get)  # the copy kernel dominates its run
+    f_fetch, f_write = COPY_BYTES / cf[copy_name], COPY_BYTES / cw[copy_name]
+    sf, sw = per_kernel("step_fetch", "FETCH_SIZE"), per_kernel("step_write", "WRITE_SIZE")
+    kernels = {}
+    for k in sorted(set(sf) | set(sw)):
+        if not k.startswith("gma::"):
+            continue
+        fb, wb = sf.get(k, 0.0) * f_fetch, sw.get(k, 0.0) * f_write
+        kernels[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "hbm_bytes": round(fb + wb)}
+    res = {"source_sha256": kernel_source_hash(), "copy_kernel": copy_name, "copy_bytes": COPY_BYTES,
+           "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4), "kernels": kernels,
+           "commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/copy_fetch -o copy_fetch -- "
+                        "python bench.py --traffic-probe copy",
+                        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/copy_write -o copy_write -- "
+                        "python bench.py --traffic-probe copy",
+                        "rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/step_fetch -o step_fetch -- "
+                        "python bench.py --traffic-probe step",
+                        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/step_write -o step_write -- "
+                        "python bench.py --traffic-probe step",
+                        "python bench.py --traffic-summarize DIR"]}
+    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
+    with open(TRAFFIC_JSON, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res, indent=1))
+    return 0
+
+
+def measured_traffic(kernel_symbol_prefix: str):
+    """HBM bytes per launch of the kernel, from profiles/traffic.json when it matches the sources."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    for k, v in t.get("kernels", {}).items():
+        if k.startswith(kernel_symbol_prefix):
+            return v["hbm_bytes"]
+    return None
 
 
 def alg_bytes_per_token_head(w, kernel: str) -> float:
@@ -56,8 +153,16 @@ def alg_bytes_per_token_head(w, kernel: str) -> float:
     return 0.0
 
 
-def main() -> int:
-    args = parse()
+KERNEL_SYMBOL = {"bf16_scan": "gma::bf::scan_kernel", "bf16_write": "gma::bf::write_kernel<64, 2",
+                 "bf16_read": "gma::bf::read_kernel", "bf16_causal_aggregate": "gma::bf::write_kernel<64, 1"}
+
+
+def main(args=None, probe_only=False) -> int:
+    args = args or parse()
+    if args.traffic_summarize:
+        return traffic_summarize(args.traffic_summarize)
+    if args.traffic_probe and not probe_only:
+        return traffic_probe(args.traffic_probe, args)
     if args.gpus != 1:
         print("bench.py: this implementation runs on a single GPU; --gpus %d is not supported "
               "(multi-GPU sharding is a design note only)" % args.gpus, file=sys.stderr)
@@ -108,6 +213,11 @@ def main() -> int:
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
+    if probe_only:  # counters of exactly `steps` steps, nothing else launched
+        for k in range(args.steps):
+            step(k)
+        torch.cuda.synchronize()
+        return 0
 
     # ---- timed region: exactly `steps` steps between two synchronisations
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -157,8 +267,9 @@ def main() -> int:
     roofline = None
     if dominant and "alg_GBps" in kernels[dominant]:
         ach = kernels[dominant]["alg_GBps"]
+        traffic = measured_traffic(KERNEL_SYMBOL.get(dominant, "?"))
         roofline = {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None,
+                    "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
                     "avg_us": kernels[dominant]["avg_us"],
                     "alg_bytes_per_launch": kernels[dominant]["alg_bytes_per_launch"]}
 

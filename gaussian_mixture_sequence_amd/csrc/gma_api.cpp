@@ -79,9 +79,17 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
         p.seg = round_up(size_t(cdiv(p.N, g)), kTokenTile);
         p.G = cdiv(p.N, p.seg);
     } else if (op == GMA_OP_CAUSAL && p.P > 0 && p.N > 0) {
-        int64_t g = std::min(cdiv(kCausalBlocks, p.P), cdiv(p.N, 512));
-        g = std::max<int64_t>(g, 1);
-        p.seg = round_up(size_t(cdiv(p.N, g)), kTokenTile);
+        // segments per problem: every workgroup resident at once (two per CU), and the
+        // busiest CU's share of positions (ceil(P g / 256) segments of `seg`) smallest;
+        // ties go to fewer segments (less aggregate work)
+        int64_t best_g = 1, best_cost = -1;
+        for (int64_t g = 1; g <= std::min<int64_t>(16, cdiv(p.N, kTokenTile)); ++g) {
+            if (g > 1 && p.P * g > kCausalBlocks) break;
+            const int64_t seg = int64_t(round_up(size_t(cdiv(p.N, g)), kTokenTile));
+            const int64_t cost = cdiv(p.P * g, 256) * seg;
+            if (best_cost < 0 || cost < best_cost) best_cost = cost, best_g = g;
+        }
+        p.seg = round_up(size_t(cdiv(p.N, best_g)), kTokenTile);
         p.G = cdiv(p.N, p.seg);
     }
     p.read_rows = 0;

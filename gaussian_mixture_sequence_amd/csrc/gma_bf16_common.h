@@ -103,39 +103,44 @@ __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t of
 
 // ---- a tile of ROUND routing vectors, split once into the score MFMA's B fragments
 // (x, x^2 hi, x^2 lo) and shared through LDS by every wave that needs it.
-// LDS layout: frag[(ts * KS + ks) * 3 + piece][lane] of 16 bytes, lane = 32 * lh + j,
-// holding x[ts * 32 + j][16 ks + 8 lh .. + 7] (or its square pieces).  Each wave loads
-// whole fragments (lane l fetches exactly the 16 bytes lane l of the fragment needs), so
-// both the LDS stores and the 1 KiB fragment reads are conflict-free.
+// Global loads are fully coalesced: thread t fetches 16-byte chunk t (+ NTHREADS, ...) of
+// the row-major [ROUND][DR] tile, so every wave instruction reads whole 128-byte lines
+// (partial-line reads of the same line from several waves make L2 fetch it again).
+// LDS layout: fragment fi = (token subtile ts, k-step ks) holds, for each piece
+// (x, x^2 hi, x^2 lo), 64 lane slots of 16 bytes; lane (lh, j) of the MFMA B operand
+// needs x[ts * 32 + j][16 ks + 8 lh .. + 7].  Pieces are FS = 68 slots apart (4 of
+// padding) and lane slots are swizzled (slot = lane ^ 2 lh): with those, both the
+// scattered commit of a wave's chunks and the fragment reads are bank-conflict free
+// for d_r = 64 (at most 2-way otherwise).
 template <int DR, int ROUND, int NTHREADS>
 struct XTile {
     static constexpr int KS = DR / 16;
-    static constexpr int NW = NTHREADS / 64;
+    static constexpr int CPR = DR / 8;  // 16-byte chunks per row
+    static constexpr int CHUNKS = ROUND * CPR;
+    static constexpr int PER = (CHUNKS + NTHREADS - 1) / NTHREADS;
+    static constexpr bool EVEN = CHUNKS % NTHREADS == 0;
     static constexpr int FRAGS = (ROUND / 32) * KS;
-    static constexpr int PER_WAVE = (FRAGS + NW - 1) / NW;
-    static constexpr bool EVEN = FRAGS % NW == 0;
-    static constexpr int LDS_BYTES = FRAGS * 3 * 64 * 16;
-    u32x4 r[PER_WAVE];
+    static constexpr int FS = 68;
+    static constexpr int LDS_BYTES = FRAGS * 3 * FS * 16;
+    u32x4 r[PER];
 
-    // fragments of the tile that starts `row0` rows into the resource
+    // the tile that starts `row0` rows into the resource
     __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t row0) {
-        const int wave = wave_id(), l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
 #pragma unroll
-        for (int u = 0; u < PER_WAVE; ++u) {
-            const int fi = wave + u * NW;
-            const int ts = fi / KS, ks = fi - ts * KS;
-            // EVEN: every wave owns exactly PER_WAVE fragments, so no load is predicated
-            // and the compiler can count outstanding loads exactly (no vmcnt(0) drains)
-            r[u] = (EVEN || fi < FRAGS) ? buf_load16(rs, uint32_t(((row0 + ts * 32 + j) * DR + 16 * ks + 8 * lh) * 2))
+        for (int u = 0; u < PER; ++u) {
+            const int c = threadIdx.x + u * NTHREADS;
+            r[u] = (EVEN || c < CHUNKS) ? buf_load16(rs, uint32_t((row0 * DR + int64_t(c) * 8) * 2))
                                         : u32x4{0u, 0u, 0u, 0u};
         }
     }
     __device__ __forceinline__ void commit(u32x4* lds) const {
-        const int wave = wave_id(), l = threadIdx.x & 63;
 #pragma unroll
-        for (int u = 0; u < PER_WAVE; ++u) {
-            const int fi = wave + u * NW;
-            if (EVEN || fi < FRAGS) {
+        for (int u = 0; u < PER; ++u) {
+            const int c = threadIdx.x + u * NTHREADS;
+            if (EVEN || c < CHUNKS) {
+                const int row = c / CPR, cc = c - row * CPR;
+                const int lh = cc & 1;
+                const int slot = (32 * lh + (row & 31)) ^ (2 * lh);
                 u32x4 h, lo;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -143,23 +148,67 @@ struct XTile {
                     h[q] = hl[0];
                     lo[q] = hl[1];
                 }
-                u32x4* f = lds + fi * 3 * 64 + l;
+                u32x4* f = lds + ((row >> 5) * KS + (cc >> 1)) * 3 * FS + slot;
                 f[0] = r[u];
-                f[64] = h;
-                f[128] = lo;
+                f[FS] = h;
+                f[2 * FS] = lo;
             }
         }
     }
 };
 
+// ---- a row-major [ROWS][DR] bf16 tile staged through LDS unsplit, with the same coalesced
+// loads; rows are padded to DR + 8 elements, which makes the 16-byte row-fragment reads
+// bank-conflict free.  Used where one wave alone consumes each token subtile (it splits
+// its own fragments in registers).
+template <int DR, int ROWS, int NTHREADS>
+struct RawTile {
+    static constexpr int CPR = DR / 8;
+    static constexpr int CHUNKS = ROWS * CPR;
+    static constexpr int PER = (CHUNKS + NTHREADS - 1) / NTHREADS;
+    static constexpr bool EVEN = CHUNKS % NTHREADS == 0;
+    static constexpr int LD = DR + 8;
+    static constexpr int LDS_BYTES = ROWS * LD * 2;
+    u32x4 r[PER];
+
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int64_t row0) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int c = threadIdx.x + u * NTHREADS;
+            r[u] = (EVEN || c < CHUNKS) ? buf_load16(rs, uint32_t((row0 * DR + int64_t(c) * 8) * 2))
+                                        : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    __device__ __forceinline__ void commit(u32x4* lds) const {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int c = threadIdx.x + u * NTHREADS;
+            if (EVEN || c < CHUNKS) {
+                const int row = c / CPR, cc = c - row * CPR;
+                *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(lds) + row * LD + cc * 8) = r[u];
+            }
+        }
+    }
+};
+
+// B fragments (one per k-step) of 32-row subtile `sub` of a RawTile in LDS, unsplit.
+template <int DR>
+__device__ __forceinline__ void raw_frags(const u32x4* lds, int sub, bf16x8 (&xs)[DR / 16]) {
+    const int l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
+    const uint16_t* row = reinterpret_cast<const uint16_t*>(lds) + (sub * 32 + j) * (DR + 8) + 8 * lh;
+#pragma unroll
+    for (int ks = 0; ks < DR / 16; ++ks) xs[ks] = *reinterpret_cast<const bf16x8*>(row + 16 * ks);
+}
+
 // B fragments of token subtile `ts` from an XTile in LDS.
 template <int DR>
 __device__ __forceinline__ void xtile_frags(const u32x4* lds, int ts, int ks, bf16x8& x, bf16x8& x2h, bf16x8& x2l) {
+    constexpr int FS = 68;
     const int l = threadIdx.x & 63;
-    const u32x4* f = lds + ((ts * (DR / 16) + ks) * 3) * 64 + l;
+    const u32x4* f = lds + ((ts * (DR / 16) + ks) * 3) * FS + (l ^ (2 * (l >> 5)));
     x = __builtin_bit_cast(bf16x8, f[0]);
-    x2h = __builtin_bit_cast(bf16x8, f[64]);
-    x2l = __builtin_bit_cast(bf16x8, f[128]);
+    x2h = __builtin_bit_cast(bf16x8, f[FS]);
+    x2l = __builtin_bit_cast(bf16x8, f[2 * FS]);
 }
 
 // Transposed fragment read from a row-major bf16 tile in LDS (ds_read_b64_tr_b16).

@@ -2,18 +2,25 @@
 //
 // Sec. 3.5 of "Gaussian Mixture Attention" defines the prefix memory (Eq. 6b) and the
 // output (Eq. 8b); the prefix sums run along the sequence.  A segment starts from the
-// memory of all earlier positions (the exclusive prefix of the segment aggregates,
-// computed by the write + prefix kernels) and advances it chunk by chunk.  For a chunk
-// of CH positions with responsibilities Gq, Gk (bf16, in LDS) and values Vc:
+// memory of all earlier positions (the sum of the earlier segments' aggregates, computed
+// by the write kernel) and advances it chunk by chunk.  For a chunk of CH positions with
+// responsibilities Gq, Gk (bf16, in LDS) and values Vc:
 //   S    = Gq Gk^T, kept for key positions j <= query position i      (Eq. 9b support)
 //   num  = S Vc + Gq Vt,   den = S 1 + Gq Z + eps                      (Eq. 8b split at the chunk)
 //   Vt  += Gk^T Vc,  Z += Gk^T 1                                       (Eq. 6b advanced by the chunk)
-// Phases per chunk (barriers between them):
-//   L  scores + softmax of the chunk's query and key rows -> Gq, Gk tiles; Gq Z on the VALU
-//   S  lower-triangular 32x32 tiles of S^T on MFMA, masked, stored bf16; fp32 row sums
-//   O  each wave owns 16-wide value columns of the K x d_v memory (fp32 registers, held
-//      across chunks): intra part V^T S^T, inter part Vt^T Gq^T (Vt split hi + lo),
-//      divide, store; then the memory update Gk^T Vc on MFMA.  Z lives in LDS.
+// Only the memory (Vt, Z) chains one chunk to the next, so the chunks are software-
+// pipelined.  Iteration c (two barriers):
+//   region 1: V tile c+1 into LDS; lower-triangular 32x32 tiles of S^T(c) on MFMA, masked,
+//             stored bf16 with fp32 row sums; partial sums of Gq(c) Z(c) on the VALU; MFMAs
+//             of chunk c+2's scores; (several waves per token) local softmax statistics of
+//             chunk c+1                                                     -> B_Q
+//   region 2: local softmax of chunk c+1 (one wave per token), its Gq, Gk into the other
+//             LDS buffer; O(c): each wave owns 16-wide value columns, intra part V^T S^T and
+//             inter part Vt^T Gq^T (Vt split hi + lo), divided and stored; memory update
+//             Vt += Gk^T Vc (fp32 registers held across chunks), Z += Gk^T 1 on MFMA with a
+//             ones operand; x tiles of chunk c+3 into LDS                    -> B_P
+// x tiles are fetched with coalesced loads and staged through LDS: split once and shared
+// when several waves hold the components of a token, unsplit when one wave does.
 // 16x16x32 MFMA layouts (lane l, g = l / 16): A row i = l % 16, k = 8 g + v; B col j =
 // l % 16, k = 8 g + v; D row i = 4 g + r, col j = l % 16.
 #include <cstdint>
@@ -49,9 +56,392 @@ struct ScanStats {
     float m, L, D;
 };
 
+template <int DR, int KT, int CH>
+constexpr int scan_jpw() {  // 32-position score jobs per wave and chunk (query and key)
+    return (2 * (CH / 32) + Split<DR, KT>::TS - 1) / Split<DR, KT>::TS;
+}
+
 // LDS bytes of scan_kernel for a chunk of CH positions (mirrors the declarations below).
 template <int DR, int KT, int VT, int CH>
 constexpr int scan_lds_bytes() {
+    using S = Split<DR, KT>;
+    constexpr int Kp = KT * 32, DV = VT * 32, SUB = CH / 32;
+    constexpr int xt = S::CS > 1 ? 2 * XTile<DR, CH, S::NW * 64>::LDS_BYTES : 2 * RawTile<DR, CH, S::NW * 64>::LDS_BYTES;
+    return scan_jpw<DR, KT, CH>() * S::TS * S::CS * 32 * 12 + 4 * CH * (Kp + 8) * 2 + 2 * CH * (DV + 8) * 2 +
+           CH * (CH + 8) * 2 + xt + (S::NW * 64 / CH) * CH * 4 + SUB * CH * 4 + Kp * 4;
+}
+
+// The chunk actually used: the requested one, halved while its tiles exceed the 160 KiB of
+// LDS or the two chunks of scores the pipeline holds would exceed two 32x32 tiles per wave
+// (the chunk length only changes the order of the sums).
+template <int DR, int KT, int VT, int CH_REQ>
+constexpr int scan_chunk() {
+    return (CH_REQ > 32 && (scan_lds_bytes<DR, KT, VT, CH_REQ>() > 160 * 1024 ||
+                            scan_jpw<DR, KT, CH_REQ>() * Split<DR, KT>::CTW > 2))
+               ? CH_REQ / 2
+               : CH_REQ;
+}
+
+template <int DR, int KT, int VT, int CH_REQ>
+__global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
+    scan_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
+                int64_t N, int H, int64_t seg, int G, const uint16_t* planes, const float* cvec,
+                const float* __restrict__ prefix, float eps, uint16_t* __restrict__ O) {
+    constexpr int CH = scan_chunk<DR, KT, VT, CH_REQ>();
+    using S = Split<DR, KT>;
+    constexpr int NW = S::NW, NT = NW * 64;
+    constexpr int Kp = KT * 32, DV = VT * 32;
+    constexpr int CS = S::CS, TS = S::TS, CTW = S::CTW, KS = S::KS;
+    constexpr int LDG = Kp + 8, LDV = DV + 8, LDSS = CH + 8;
+    constexpr int SUB = CH / 32;                  // 32-position subtiles per chunk
+    constexpr int JOBS = 2 * SUB;                 // query subtiles, then key subtiles
+    constexpr int JPW = scan_jpw<DR, KT, CH>();   // jobs per wave
+    constexpr int C16 = DV / 16;                  // 16-wide value column tiles
+    constexpr int CPW = (C16 + NW - 1) / NW;      // column tiles per wave
+    constexpr int KT16 = Kp / 16;                 // 16-row component tiles of the memory
+    constexpr int ZPW = (KT16 + NW - 1) / NW;     // Z tiles per wave
+    constexpr int STILES = SUB * (SUB + 1) / 2;   // lower-triangular tiles of S^T
+    constexpr int VCHUNKS = CH * DV / 8, VCH = (VCHUNKS + NT - 1) / NT;
+    constexpr bool VEVEN = VCHUNKS % NT == 0;
+    constexpr int NPARTS = NW * 64 / CH, KPP = Kp / NPARTS;  // split of the Gq Z sums
+    static_assert(KPP % 4 == 0, "Gq Z partial sums read 4 components at a time");
+    // x tiles through LDS (coalesced loads): split once and shared when several waves use the
+    // same token subtile (CS > 1); otherwise staged unsplit, each wave splitting its own
+    constexpr bool SHARE_X = CS > 1;
+    using XT = typename std::conditional<SHARE_X, XTile<DR, CH, NT>, RawTile<DR, CH, NT>>::type;
+
+    __shared__ ScanStats st[JPW][TS * CS * 32];
+    __shared__ __attribute__((aligned(16))) uint16_t Gq[2][CH * LDG];
+    __shared__ __attribute__((aligned(16))) uint16_t Gk[2][CH * LDG];
+    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][CH * LDV];
+    __shared__ __attribute__((aligned(16))) uint16_t Ss[CH * LDSS];
+    __shared__ __attribute__((aligned(16))) u32x4 XtQ[XT::LDS_BYTES / 16];
+    __shared__ __attribute__((aligned(16))) u32x4 XtK[XT::LDS_BYTES / 16];
+    __shared__ float den_ip[NPARTS][CH];
+    __shared__ float den_part[SUB][CH];
+    __shared__ __attribute__((aligned(16))) float Zs[Kp];
+
+    const int wave = wave_id(), l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
+    const int g4 = l >> 4, i16 = l & 15;
+    const int cs = wave % CS, ts = wave / CS;
+    const int64_t p = blockIdx.y;
+    const int seg_idx = blockIdx.x;
+    const int h = int(p % H);
+    const int64_t lo = int64_t(seg_idx) * seg, hi = min<int64_t>(lo + seg, N);
+    const int64_t rows = hi - lo;
+    const int64_t C = (rows + CH - 1) / CH;  // chunks of this segment
+
+    WaveParams<DR, CTW> P;
+    P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * CTW);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(XQ + (size_t(p) * N + lo) * DR, rows * DR * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(XK + (size_t(p) * N + lo) * DR, rows * DR * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t(p) * N + lo) * DV, rows * DV * 2);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + (size_t(p) * N + lo) * DV, rows * DV * 2);
+
+    // ---- inputs: V tile c+1 in registers while tile c is in LDS; x fragments of chunk
+    // c+2 in registers (or, shared, x tile c+2 in LDS and c+3 in registers)
+    u32x4 vr[VCH];
+    auto load_v = [&](int64_t row0) {
+#pragma unroll
+        for (int u = 0; u < VCH; ++u) {
+            const int c = threadIdx.x + u * NT;
+            vr[u] = (VEVEN || c < VCHUNKS) ? buf_load16(rv, uint32_t((row0 * DV + int64_t(c) * 8) * 2))
+                                           : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    auto commit_v = [&](uint16_t* dst) {
+#pragma unroll
+        for (int u = 0; u < VCH; ++u) {
+            const int c = threadIdx.x + u * NT;
+            if (VEVEN || c < VCHUNKS) {
+                const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
+                *reinterpret_cast<u32x4*>(dst + row * LDV + col) = vr[u];
+            }
+        }
+    };
+    auto job_of = [&](int jj, bool& is_q, int& sub) {  // this wave's jj-th job; false if none
+        const int job = ts + jj * TS;
+        is_q = job < SUB;
+        sub = is_q ? job : job - SUB;
+        if (job >= JOBS) sub = 0;
+        return job < JOBS;
+    };
+    XT xq, xk;  // registers: the x tiles of the chunk after the one in LDS
+    auto scores_chunk = [&](f32x16 (&acc)[JPW][CTW]) __attribute__((always_inline)) {  // from the LDS tiles
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) {
+            bool is_q;
+            int sub;
+            job_of(jj, is_q, sub);
+            if constexpr (SHARE_X) {
+                scores_lds<DR, CTW>(P, is_q ? XtQ : XtK, sub, acc[jj]);
+            } else {
+                bf16x8 xs[KS];
+                raw_frags<DR>(is_q ? XtQ : XtK, sub, xs);
+                scores_x<DR, CTW>(P, xs, acc[jj]);
+            }
+        }
+    };
+    float zdummy[CTW][16];
+    float sm_m[JPW], sm_L[JPW];
+    auto softmax_local = [&](f32x16 (&acc)[JPW][CTW]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) {
+            float D;
+            local_softmax<CTW, false>(acc[jj], zdummy, sm_m[jj], sm_L[jj], D);
+            if (CS > 1) st[jj][(ts * CS + cs) * 32 + j] = ScanStats{sm_m[jj], sm_L[jj], 0.0f};  // both halves equal
+        }
+    };
+    // Gamma of the chunk starting at row0 into Gq[b], Gk[b] (after softmax_local)
+    auto store_gamma = [&](f32x16 (&acc)[JPW][CTW], int64_t row0, int b) __attribute__((always_inline)) {
+#pragma unroll
+        for (int jj = 0; jj < JPW; ++jj) {
+            bool is_q;
+            int sub;
+            if (!job_of(jj, is_q, sub)) continue;
+            float scale;
+            if (CS == 1) {
+                scale = __builtin_amdgcn_rcpf(sm_L[jj]);
+            } else {
+                float mm = -INFINITY;
+#pragma unroll
+                for (int c = 0; c < CS; ++c) mm = fmaxf(mm, st[jj][(ts * CS + c) * 32 + j].m);
+                float Lt = 0.0f;
+#pragma unroll
+                for (int c = 0; c < CS; ++c) {
+                    const ScanStats sc = st[jj][(ts * CS + c) * 32 + j];
+                    Lt = fmaf(sc.L, __builtin_amdgcn_exp2f(sc.m - mm), Lt);
+                }
+                scale = __builtin_amdgcn_exp2f(sm_m[jj] - mm) * __builtin_amdgcn_rcpf(Lt);
+            }
+            if (int64_t(sub) * 32 + j >= rows - row0) scale = 0.0f;  // positions past the segment
+            store_gamma_lds<CTW>(acc[jj], scale, is_q ? Gq[b] : Gk[b], LDG, sub * 32 + j, cs * CTW);
+        }
+    };
+
+    // ---- starting memory of the segment: the sum of the aggregates of segments
+    // 0 .. seg_idx-1 (each stored as VtT [DV][Kp] then Z [Kp]), in increasing segment order
+    const size_t E = size_t(Kp) * (DV + 1);
+    const float* agg = prefix + size_t(p) * G * E;
+    f32x4 mem[CPW][KT16];
+#pragma unroll
+    for (int cc = 0; cc < CPW; ++cc)
+#pragma unroll
+        for (int kt = 0; kt < KT16; ++kt) mem[cc][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = threadIdx.x; k < Kp; k += NT) Zs[k] = 0.0f;
+
+    // prologue loads first, so they overlap the prefix sum
+    load_v(0);
+    xq.load(rq, 0);
+    xk.load(rk, 0);
+#pragma unroll 2
+    for (int gs = 0; gs < seg_idx; ++gs) {
+        const float* a = agg + size_t(gs) * E;
+#pragma unroll
+        for (int cc = 0; cc < CPW; ++cc) {
+            const int c16 = wave + cc * NW;
+            if (c16 < C16) {
+#pragma unroll
+                for (int kt = 0; kt < KT16; ++kt) {
+                    const float4 v = *reinterpret_cast<const float4*>(a + size_t(c16 * 16 + i16) * Kp + kt * 16 + 4 * g4);
+                    mem[cc][kt][0] += v.x;
+                    mem[cc][kt][1] += v.y;
+                    mem[cc][kt][2] += v.z;
+                    mem[cc][kt][3] += v.w;
+                }
+            }
+        }
+        for (int k = threadIdx.x; k < Kp; k += NT) Zs[k] += a[size_t(Kp) * DV + k];
+    }
+    commit_v(Vs[0]);
+    load_v(CH);
+
+    // ---- prologue: Gamma of chunk 0 into Gq[0], Gk[0]; scores of chunk 1 held; x of
+    // chunks 2 (and 3) staged
+    f32x16 acc_a[JPW][CTW], acc_b[JPW][CTW];
+    xq.commit(XtQ);
+    xk.commit(XtK);
+    xq.load(rq, CH);
+    xk.load(rk, CH);
+    __syncthreads();
+    scores_chunk(acc_b);  // chunk 0
+    softmax_local(acc_b);
+    __syncthreads();      // statistics published; x tile 0 consumed
+    store_gamma(acc_b, 0, 0);
+    xq.commit(XtQ);
+    xk.commit(XtK);
+    xq.load(rq, 2 * CH);
+    xk.load(rk, 2 * CH);
+    __syncthreads();
+    scores_chunk(acc_a);  // chunk 1
+    __syncthreads();      // x tile 1 consumed
+    xq.commit(XtQ);
+    xk.commit(XtK);
+    xq.load(rq, 3 * CH);
+    xk.load(rk, 3 * CH);
+    __syncthreads();
+
+    // ---- one pipelined chunk: `cur` holds chunk c+1's scores, `nxt` receives chunk c+2's
+    // (x tiles of chunk c+2 in LDS, c+3 in registers); b = c % 2 selects the LDS buffers
+    auto chunk = [&](const int64_t c, const int b, f32x16 (&cur)[JPW][CTW], f32x16 (&nxt)[JPW][CTW])
+                     __attribute__((always_inline)) {
+        const int64_t nc = c * CH;
+        // ---- region 1
+        commit_v(Vs[b ^ 1]);  // V tile c+1
+        load_v(nc + 2 * CH);
+        if (wave < STILES) {  // S^T tile (rows = key positions, cols = query positions)
+            int qt = 0, kt = wave;
+            while (kt > qt) { kt -= qt + 1; ++qt; }
+            f32x16 sacc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < Kp / 16; ++ks)
+                sacc = mfma(read_rowfrag(Gk[b], LDG, kt * 32 + j, 16 * ks), read_rowfrag(Gq[b], LDG, qt * 32 + j, 16 * ks),
+                            sacc);
+            float rs = 0.0f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int kk = kt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+                if (kk > qt * 32 + j) sacc[r] = 0.0f;  // j > i is outside the causal support
+                rs += sacc[r];
+            }
+            rs = xsum32(rs);
+            if (lh == 0) den_part[kt][qt * 32 + j] = rs;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                u32x2 v;
+                v[0] = pack_bf16x2(sacc[4 * q + 0], sacc[4 * q + 1]);
+                v[1] = pack_bf16x2(sacc[4 * q + 2], sacc[4 * q + 3]);
+                *reinterpret_cast<u32x2*>(Ss + (qt * 32 + j) * LDSS + kt * 32 + 8 * q + 4 * lh) = v;
+            }
+        }
+        {  // partial sums of Gq(c) Z(c): part `pt` covers components pt*KPP .. +KPP-1
+            const int t = l % CH, pt = wave * (64 / CH) + l / CH;
+            float d = 0.0f;
+#pragma unroll
+            for (int k4 = 0; k4 < KPP / 4; ++k4) {
+                const int k = pt * KPP + 4 * k4;
+                const u32x2 gv = *reinterpret_cast<const u32x2*>(Gq[b] + t * LDG + k);
+                const float4 zv = *reinterpret_cast<const float4*>(Zs + k);
+                d = fmaf(__uint_as_float(gv[0] << 16), zv.x, d);
+                d = fmaf(__uint_as_float(gv[0] & 0xffff0000u), zv.y, d);
+                d = fmaf(__uint_as_float(gv[1] << 16), zv.z, d);
+                d = fmaf(__uint_as_float(gv[1] & 0xffff0000u), zv.w, d);
+            }
+            den_ip[pt][t] = d;
+        }
+        scores_chunk(nxt);  // chunk c+2
+        if (CS > 1) softmax_local(cur);
+        __syncthreads();  // B_Q: S(c), row sums, Gq Z partials, statistics of c+1 published
+        // ---- region 2
+        if (CS == 1) softmax_local(cur);
+        store_gamma(cur, nc + CH, b ^ 1);  // chunk c+1
+        const uint16_t* Vc = Vs[b];
+#pragma unroll
+        for (int cc = 0; cc < CPW; ++cc) {
+            const int c16 = wave + cc * NW;
+            if (c16 >= C16) continue;
+            f32x4 o[CH / 16];
+#pragma unroll
+            for (int t16 = 0; t16 < CH / 16; ++t16) {
+                o[t16] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                // intra-chunk part: V^T S^T over key positions up to this query tile
+#pragma unroll
+                for (int ks = 0; ks < (t16 * 16 + 16 + 31) / 32; ++ks) {
+                    bf16x8 a = read_colfrag16(Vc, LDV, 32 * ks, c16 * 16);
+                    bf16x8 bb = *reinterpret_cast<const bf16x8*>(Ss + (t16 * 16 + i16) * LDSS + 32 * ks + 8 * g4);
+                    o[t16] = mfma16(a, bb, o[t16]);
+                }
+            }
+            // inter-chunk part: memory^T Gq^T, memory split into hi + lo bf16 once per k-step
+#pragma unroll
+            for (int m2 = 0; m2 < Kp / 32; ++m2) {
+                u32x4 ah, al;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int v0 = 2 * q, v1 = 2 * q + 1;
+                    const float x0 = mem[cc][2 * m2 + (v0 >> 2)][v0 & 3];
+                    const float x1 = mem[cc][2 * m2 + (v1 >> 2)][v1 & 3];
+                    const uint32_t hb = pack_bf16x2(x0, x1);
+                    ah[q] = hb;
+                    al[q] = pack_bf16x2(x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u));
+                }
+#pragma unroll
+                for (int t16 = 0; t16 < CH / 16; ++t16) {
+                    const int qrow = t16 * 16 + i16;
+                    const u32x2 b0 = *reinterpret_cast<const u32x2*>(Gq[b] + qrow * LDG + 32 * m2 + 4 * g4);
+                    const u32x2 b1 = *reinterpret_cast<const u32x2*>(Gq[b] + qrow * LDG + 32 * m2 + 16 + 4 * g4);
+                    const bf16x8 bb = __builtin_bit_cast(bf16x8, u32x4{b0[0], b0[1], b1[0], b1[1]});
+                    o[t16] = mfma16(__builtin_bit_cast(bf16x8, ah), bb, o[t16]);
+                    o[t16] = mfma16(__builtin_bit_cast(bf16x8, al), bb, o[t16]);
+                }
+            }
+#pragma unroll
+            for (int t16 = 0; t16 < CH / 16; ++t16) {
+                const int qrow = t16 * 16 + i16;
+                float den = eps;
+#pragma unroll
+                for (int pt = 0; pt < NPARTS; ++pt) den += den_ip[pt][qrow];
+#pragma unroll
+                for (int kt = 0; kt < SUB; ++kt)
+                    if (kt * 32 <= qrow) den += den_part[kt][qrow];
+                const float rden = __builtin_amdgcn_rcpf(den);
+                u32x2 v;
+                v[0] = pack_bf16x2(o[t16][0] * rden, o[t16][1] * rden);
+                v[1] = pack_bf16x2(o[t16][2] * rden, o[t16][3] * rden);
+                // rows past the segment fall outside the resource and are dropped
+                buf_store8(ro, uint32_t(((nc + qrow) * DV + c16 * 16 + 4 * g4) * 2), v);
+            }
+        }
+        // memory update: Vt += Gk^T Vc (every wave its value columns), Z += Gk^T 1 (the
+        // component tiles kt = wave (mod NW), ones operand)
+        const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+        f32x4 zt[ZPW];
+#pragma unroll
+        for (int zi = 0; zi < ZPW; ++zi) zt[zi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kt = 0; kt < KT16; ++kt)
+#pragma unroll
+            for (int ks = 0; ks < CH / 32; ++ks) {
+                const bf16x8 a = read_colfrag16(Gk[b], LDG, 32 * ks, kt * 16);
+#pragma unroll
+                for (int cc = 0; cc < CPW; ++cc) {
+                    const int c16 = wave + cc * NW;
+                    if (c16 < C16) mem[cc][kt] = mfma16(a, read_colfrag16(Vc, LDV, 32 * ks, c16 * 16), mem[cc][kt]);
+                }
+                if (kt % NW == wave) zt[kt / NW] = mfma16(a, ones, zt[kt / NW]);
+            }
+        if (i16 == 0)
+#pragma unroll
+            for (int zi = 0; zi < ZPW; ++zi) {
+                const int kt = wave + zi * NW;
+                if (kt < KT16)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Zs[kt * 16 + 4 * g4 + r] += zt[zi][r];
+            }
+        // x tiles of chunk c+3 (chunk c+2's were read in region 1); loads of c+4 issued
+        xq.commit(XtQ);
+        xk.commit(XtK);
+        xq.load(rq, nc + 4 * CH);
+        xk.load(rk, nc + 4 * CH);
+        __syncthreads();  // B_P: Gamma(c+1), V(c+1), Z(c+1) visible; chunk c consumed
+    };
+    // chunks in pairs (static buffer roles), then the odd one
+    int64_t c = 0;
+    for (; c + 1 < C; c += 2) {
+        chunk(c, 0, acc_a, acc_b);
+        chunk(c + 1, 1, acc_b, acc_a);
+    }
+    if (c < C) chunk(c, 0, acc_a, acc_b);
+}
+
+// ---- serial variant: one chunk after another (four barriers per chunk), for the shapes
+// whose fp32 memory plus two chunks of scores would not fit the registers of the
+// pipelined kernel (many component tiles).
+// LDS bytes of serial_scan_kernel for a chunk of CH positions (mirrors the declarations below).
+template <int DR, int KT, int VT, int CH>
+constexpr int serial_scan_lds_bytes() {
     using S = Split<DR, KT>;
     constexpr int Kp = KT * 32, DV = VT * 32, SUB = CH / 32;
     constexpr int JPW = (2 * SUB + S::TS - 1) / S::TS;
@@ -63,16 +453,16 @@ constexpr int scan_lds_bytes() {
 // The chunk actually used: the requested one, halved while its tiles exceed the 160 KiB of
 // LDS (the chunk length only changes the order of the sums).
 template <int DR, int KT, int VT, int CH_REQ>
-constexpr int scan_chunk() {
-    return (CH_REQ > 32 && scan_lds_bytes<DR, KT, VT, CH_REQ>() > 160 * 1024) ? CH_REQ / 2 : CH_REQ;
+constexpr int serial_scan_chunk() {
+    return (CH_REQ > 32 && serial_scan_lds_bytes<DR, KT, VT, CH_REQ>() > 160 * 1024) ? CH_REQ / 2 : CH_REQ;
 }
 
 template <int DR, int KT, int VT, int CH_REQ>
 __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
-    scan_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
+    serial_scan_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
                 int64_t N, int H, int64_t seg, int G, const uint16_t* planes, const float* cvec,
                 const float* __restrict__ prefix, float eps, uint16_t* __restrict__ O) {
-    constexpr int CH = scan_chunk<DR, KT, VT, CH_REQ>();
+    constexpr int CH = serial_scan_chunk<DR, KT, VT, CH_REQ>();
     using S = Split<DR, KT>;
     constexpr int NT = S::NW * 64;
     constexpr int Kp = KT * 32, DV = VT * 32;
@@ -439,10 +829,19 @@ hipError_t bf16_scan(const Plan& p, const void* XQ, const void* XK, const void* 
         constexpr int DR = decltype(D)::value, KT = decltype(T)::value, VT = decltype(W)::value,
                       CH = decltype(C)::value;
         using S = bf::Split<DR, KT>;
-        GMA_LAUNCH("bf16_scan", (bf::scan_kernel<DR, KT, VT, CH>), dim3(unsigned(p.G), unsigned(p.P)),
-                   dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
-                   static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), planes, cvec, prefix, eps,
-                   static_cast<uint16_t*>(O));
+        // pipelined scan where its registers suffice (up to 4 component tiles and d_r * K <= 8192),
+        // the serial one otherwise
+        if constexpr (KT <= 4 && DR * KT <= 256) {
+            GMA_LAUNCH("bf16_scan", (bf::scan_kernel<DR, KT, VT, CH>), dim3(unsigned(p.G), unsigned(p.P)),
+                       dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
+                       static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), planes, cvec, prefix, eps,
+                       static_cast<uint16_t*>(O));
+        } else {
+            GMA_LAUNCH("bf16_scan", (bf::serial_scan_kernel<DR, KT, VT, CH>), dim3(unsigned(p.G), unsigned(p.P)),
+                       dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
+                       static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), planes, cvec, prefix, eps,
+                       static_cast<uint16_t*>(O));
+        }
         return hipGetLastError();
     });
 }
