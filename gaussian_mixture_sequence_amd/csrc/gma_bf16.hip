@@ -26,45 +26,47 @@ namespace bf {
 // ---------------------------------------------------------------------------- params
 
 // One wave per component k (grid: (Kp / 4, H), 4 waves per block).  Planes of row k and
-// c_k = log2(e) * (log pi_k - 1/2 sum_d (log sigma2_kd + mu_kd^2 / sigma2_kd)) in fp64,
-// shifted by c_0 of the same head: a k-independent shift, exact in the softmax, that
-// removes the common offset before the value is rounded to fp32.  Padded components
-// (k >= K) get zero planes and c = -inf, i.e. responsibility exactly 0.
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
-__device__ __forceinline__ double score_constant(const float* mu_k, const float* s2_k, float pi_k, int dr) {
-    double acc = 0.0;
-    for (int d = threadIdx.x & 63; d < dr; d += 64) {
-        const double v = double(s2_k[d]), m = double(mu_k[d]);
-        acc += log(v) + m * m / v;
-    }
-    return log(double(pi_k)) - 0.5 * wave_sum_f64(acc);
+// c_k = log2 pi_k - 1/2 sum_d (log2 sigma2_kd + log2(e) mu_kd^2 / sigma2_kd), i.e. the
+// constant of Eq. 16 in log2 units, all in fp32: the scores built from these planes are
+// accumulated in fp32 anyway, so fp32 here costs no accuracy the bf16 path keeps.
+// Padded components (k >= K) get zero planes and c = -inf, i.e. responsibility exactly 0.
+// Sum over the 64 lanes of a wave: within rows of 16 lanes by DPP, then across rows with
+// the lane-swap instructions; every lane ends with the total.
+__device__ __forceinline__ float wave_sum_f32(float x) {
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
+    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));  // row_mirror
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
 }
 
 __global__ void __launch_bounds__(256) params_kernel(const float* __restrict__ mu, const float* __restrict__ s2,
                                                      const float* __restrict__ pi, int K, int Kp, int dr,
                                                      uint16_t* __restrict__ planes, float* __restrict__ cvec) {
-    const double L2E = 1.4426950408889634;
+    const float L2E = 1.4426950408889634f;
     const int h = blockIdx.y;
     const int k = blockIdx.x * 4 + wave_id();
     if (k >= Kp) return;
+    const int lane = threadIdx.x & 63;
     uint16_t* ph = planes + size_t(h) * 4 * Kp * dr;
     const float* mu_h = mu + size_t(h) * K * dr;
     const float* s2_h = s2 + size_t(h) * K * dr;
-    for (int d = threadIdx.x & 63; d < dr; d += 64) {
-        double a = 0.0, b = 0.0;
+    float csum = 0.0f;
+    for (int d = lane; d < dr; d += 64) {
+        float a = 0.0f, b = 0.0f;
         if (k < K) {
-            const double inv = 1.0 / double(s2_h[size_t(k) * dr + d]);
-            a = double(mu_h[size_t(k) * dr + d]) * inv * L2E;
-            b = -0.5 * inv * L2E;
+            const float v = s2_h[size_t(k) * dr + d], m = mu_h[size_t(k) * dr + d];
+            const float inv = 1.0f / v;
+            a = m * inv * L2E;
+            b = -0.5f * inv * L2E;
+            csum += log2f(v) + m * m * inv * L2E;
         }
-        const uint16_t ah = f32_to_bf16_bits(float(a)), bh = f32_to_bf16_bits(float(b));
-        const uint16_t al = f32_to_bf16_bits(float(a - double(bf16_bits_to_f32(ah))));
-        const uint16_t bl = f32_to_bf16_bits(float(b - double(bf16_bits_to_f32(bh))));
+        const uint16_t ah = f32_to_bf16_bits(a), bh = f32_to_bf16_bits(b);
+        const uint16_t al = f32_to_bf16_bits(a - bf16_bits_to_f32(ah));
+        const uint16_t bl = f32_to_bf16_bits(b - bf16_bits_to_f32(bh));
         // fragment-major: [ct][ks][plane][lane][8], lane = 32 * ((d / 8) % 2) + k % 32, so a
         // wave fetches each of its MFMA A fragments as one contiguous 1 KiB block
         const size_t f = ((size_t(k >> 5) * (dr / 16) + (d >> 4)) * 4) * 64 + 32 * ((d >> 3) & 1) + (k & 31);
@@ -73,13 +75,8 @@ __global__ void __launch_bounds__(256) params_kernel(const float* __restrict__ m
         ph[(f + 2 * 64) * 8 + (d & 7)] = bh;
         ph[(f + 3 * 64) * 8 + (d & 7)] = bl;
     }
-    if (k < K) {
-        const double ck = score_constant(mu_h + size_t(k) * dr, s2_h + size_t(k) * dr, pi[size_t(h) * K + k], dr);
-        const double c0 = score_constant(mu_h, s2_h, pi[size_t(h) * K], dr);
-        if ((threadIdx.x & 63) == 0) cvec[size_t(h) * Kp + k] = float((ck - c0) * L2E);
-    } else if ((threadIdx.x & 63) == 0) {
-        cvec[size_t(h) * Kp + k] = -INFINITY;
-    }
+    const float t = wave_sum_f32(csum);
+    if (lane == 0) cvec[size_t(h) * Kp + k] = (k < K) ? log2f(pi[size_t(h) * K + k]) - 0.5f * t : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------- softmax across waves
@@ -401,20 +398,31 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
 // partials use the same [DV][Kp] + [Kp] order, so every access is coalesced.
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ partials, int G, int Kp, int DV,
                                                       uint16_t* __restrict__ memory) {
+    // four consecutive elements per thread (Kp * DV is a multiple of 4, so a group never
+    // straddles the VtT / Z boundary); the G loads are independent and issued together
     const int64_t p = blockIdx.y;
     const int E = Kp * (DV + 1);
-    const int e = blockIdx.x * 256 + threadIdx.x;
+    const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (e >= E) return;
     const float* src = partials + size_t(p) * G * E + e;
-    float acc = 0.0f;
-    for (int g = 0; g < G; ++g) acc += src[size_t(g) * E];
+    float4 acc = *reinterpret_cast<const float4*>(src);
+#pragma unroll 8
+    for (int g = 1; g < G; ++g) {
+        const float4 v = *reinterpret_cast<const float4*>(src + size_t(g) * E);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
     uint16_t* base = memory + size_t(p) * E * 2;  // E floats of room per problem
     if (e < Kp * DV) {
-        const uint16_t hi = f32_to_bf16_bits(acc);
-        base[e] = hi;
-        base[size_t(DV) * Kp + e] = f32_to_bf16_bits(acc - bf16_bits_to_f32(hi));
+        const uint32_t h01 = pack_bf16x2(acc.x, acc.y), h23 = pack_bf16x2(acc.z, acc.w);
+        const uint32_t l01 = pack_bf16x2(acc.x - __uint_as_float(h01 << 16), acc.y - __uint_as_float(h01 & 0xffff0000u));
+        const uint32_t l23 = pack_bf16x2(acc.z - __uint_as_float(h23 << 16), acc.w - __uint_as_float(h23 & 0xffff0000u));
+        *reinterpret_cast<u32x2*>(base + e) = u32x2{h01, h23};
+        *reinterpret_cast<u32x2*>(base + size_t(DV) * Kp + e) = u32x2{l01, l23};
     } else {
-        reinterpret_cast<float*>(base + size_t(2) * DV * Kp)[e - Kp * DV] = acc;
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(base + size_t(2) * DV * Kp) + (e - Kp * DV)) = acc;
     }
 }
 
@@ -696,7 +704,7 @@ hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void*
     float* partials = reinterpret_cast<float*>(ws + p.off_partials);
     uint16_t* memory = reinterpret_cast<uint16_t*>(ws + p.off_memory);
     const int E = int(p.Kp * (p.dv + 1));
-    GMA_LAUNCH("bf16_combine", bf::combine_kernel, dim3(unsigned((E + 255) / 256), unsigned(p.P)), dim3(256), 0, st, partials,
+    GMA_LAUNCH("bf16_combine", bf::combine_kernel, dim3(unsigned((E / 4 + 255) / 256), unsigned(p.P)), dim3(256), 0, st, partials,
                        int(p.G), int(p.Kp), int(p.dv), memory);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     Bf16Params v = bf16_params_view(p, ws);
