@@ -63,13 +63,12 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
     p.Kp = (io == GMA_BF16) ? round_up(size_t(s.K), 32) : s.K;
     p.chunk = (op == GMA_OP_CAUSAL) ? chunk : 0;
 
-    // parameter tables: fp32 path keeps 1/sigma2 and the score constant in fp64; the bf16 path
-    // keeps four bf16 operand planes (a hi/lo, b hi/lo) and the constant.
+    // parameter tables: the fp32 path keeps 1/sigma2 and the score constant in fp64; the bf16
+    // kernels build their operands from mu, sigma2 and pi in registers and keep none.
     if (io == GMA_F32)
         p.params_bytes = round_up(size_t(p.H * p.K) * 8, 256) + round_up(size_t(p.H * p.K * p.dr) * 8, 256);
     else
-        p.params_bytes = round_up(size_t(p.H * p.Kp) * 4, 256) +
-                         round_up(size_t(p.H * p.Kp * 4 * p.dr) * 2, 256);
+        p.params_bytes = 0;
 
     p.G = 1;
     p.seg = round_up(size_t(std::max<int64_t>(p.N, 1)), kTokenTile);

@@ -1,8 +1,6 @@
 // bf16 I/O path of the GMA forward: MFMA kernels for gfx950.
 //
 // Kernel sequence on the caller's stream:
-//   params    per head: four bf16 operand planes (a hi/lo, b hi/lo) and the score
-//             constant c (fp64 arithmetic, scaled by log2 e, shifted by max_k c)
 //   write     per (problem, split): partial [Vt | Z] = Gamma_K^T [V | 1] over the split
 //             (Sec. 3.3 Eq. 5-6 of "Gaussian Mixture Attention"); Gamma_K never leaves
 //             the chip: scores -> softmax in registers -> bf16 tile in LDS -> MFMA
@@ -13,6 +11,8 @@
 //   aggregate causal: the write kernel over segments 0 .. G-2 (segment aggregates)
 //   scan      causal chunked scan (gma_bf16_scan.hip); segment s starts from the sum of
 //             the aggregates of segments 0 .. s-1
+// Every kernel builds the score operands of its own component tiles from mu, sigma2 and
+// pi in registers (WaveParams::compute), so no launch is spent on the parameters.
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -22,62 +22,6 @@
 
 namespace gma {
 namespace bf {
-
-// ---------------------------------------------------------------------------- params
-
-// One wave per component k (grid: (Kp / 4, H), 4 waves per block).  Planes of row k and
-// c_k = log2 pi_k - 1/2 sum_d (log2 sigma2_kd + log2(e) mu_kd^2 / sigma2_kd), i.e. the
-// constant of Eq. 16 in log2 units, all in fp32: the scores built from these planes are
-// accumulated in fp32 anyway, so fp32 here costs no accuracy the bf16 path keeps.
-// Padded components (k >= K) get zero planes and c = -inf, i.e. responsibility exactly 0.
-// Sum over the 64 lanes of a wave: within rows of 16 lanes by DPP, then across rows with
-// the lane-swap instructions; every lane ends with the total.
-__device__ __forceinline__ float wave_sum_f32(float x) {
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false));  // row_half_mirror
-    x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false));  // row_mirror
-    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
-    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
-}
-
-__global__ void __launch_bounds__(256) params_kernel(const float* __restrict__ mu, const float* __restrict__ s2,
-                                                     const float* __restrict__ pi, int K, int Kp, int dr,
-                                                     uint16_t* __restrict__ planes, float* __restrict__ cvec) {
-    const float L2E = 1.4426950408889634f;
-    const int h = blockIdx.y;
-    const int k = blockIdx.x * 4 + wave_id();
-    if (k >= Kp) return;
-    const int lane = threadIdx.x & 63;
-    uint16_t* ph = planes + size_t(h) * 4 * Kp * dr;
-    const float* mu_h = mu + size_t(h) * K * dr;
-    const float* s2_h = s2 + size_t(h) * K * dr;
-    float csum = 0.0f;
-    for (int d = lane; d < dr; d += 64) {
-        float a = 0.0f, b = 0.0f;
-        if (k < K) {
-            const float v = s2_h[size_t(k) * dr + d], m = mu_h[size_t(k) * dr + d];
-            const float inv = 1.0f / v;
-            a = m * inv * L2E;
-            b = -0.5f * inv * L2E;
-            csum += log2f(v) + m * m * inv * L2E;
-        }
-        const uint16_t ah = f32_to_bf16_bits(a), bh = f32_to_bf16_bits(b);
-        const uint16_t al = f32_to_bf16_bits(a - bf16_bits_to_f32(ah));
-        const uint16_t bl = f32_to_bf16_bits(b - bf16_bits_to_f32(bh));
-        // fragment-major: [ct][ks][plane][lane][8], lane = 32 * ((d / 8) % 2) + k % 32, so a
-        // wave fetches each of its MFMA A fragments as one contiguous 1 KiB block
-        const size_t f = ((size_t(k >> 5) * (dr / 16) + (d >> 4)) * 4) * 64 + 32 * ((d >> 3) & 1) + (k & 31);
-        ph[(f + 0 * 64) * 8 + (d & 7)] = ah;
-        ph[(f + 1 * 64) * 8 + (d & 7)] = al;
-        ph[(f + 2 * 64) * 8 + (d & 7)] = bh;
-        ph[(f + 3 * 64) * 8 + (d & 7)] = bl;
-    }
-    const float t = wave_sum_f32(csum);
-    if (lane == 0) cvec[size_t(h) * Kp + k] = (k < K) ? log2f(pi[size_t(h) * K + k]) - 0.5f * t : -INFINITY;
-}
 
 // ---------------------------------------------------------------------------- softmax across waves
 
@@ -118,18 +62,16 @@ __device__ __forceinline__ float combine_stats(const Stats* st, int ts, int cs, 
 
 template <int DR, int KT>
 __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) resp_kernel(const uint16_t* __restrict__ X, int64_t N,
-                                                                       int H, int K, const uint16_t* planes,
-                                                                       const float* cvec, void* Gamma,
+                                                                       int H, Mixture mx, void* Gamma,
                                                                        int gamma_bf16) {
     using S = Split<DR, KT>;
-    constexpr int Kp = KT * 32;
     __shared__ Stats st[S::TS * S::CS * 32];
     const int wave = wave_id(), l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
     const int cs = wave % S::CS, ts = wave / S::CS;
     const int64_t p = blockIdx.y;
-    const int h = int(p % H);
+    const int h = int(p % H), K = mx.K;
     WaveParams<DR, S::CTW> P;
-    P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * S::CTW);
+    P.compute(mx, h, cs * S::CTW);
     const uint16_t* Xp = X + size_t(p) * N * DR;
     const int64_t n0 = int64_t(blockIdx.x) * S::ROUND + ts * 32;
     const int valid = int(max<int64_t>(0, min<int64_t>(32, N - n0)));
@@ -185,8 +127,7 @@ template <int DR, int KT, int VT>
 __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const uint16_t* __restrict__ XK,
                                                                         const uint16_t* __restrict__ V, int64_t N,
                                                                         int H, int64_t seg, int G,
-                                                                        const uint16_t* planes, const float* cvec,
-                                                                        float* __restrict__ partials) {
+                                                                        Mixture mx, float* __restrict__ partials) {
     using S = Split<DR, KT>;
     constexpr int NW = S::NW, NT = NW * 64;
     constexpr int Kp = KT * 32, DV = VT * 32;
@@ -220,8 +161,18 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
     const int64_t lo = int64_t(g_idx) * seg, hi = min<int64_t>(lo + seg, N);
     const int64_t rows = hi - lo;
     const int64_t R = (rows + S::ROUND - 1) / S::ROUND;  // rounds of this split
+    // mixture parameters staged through the x tile buffer when it is large enough
+    using MS = MixtureStage<DR, Kp, NT>;
+    constexpr bool STAGE = sizeof(Xt) >= MS::LDS_BYTES;
     WaveParams<DR, S::CTW> P;
-    P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * S::CTW);
+    typename WaveParams<DR, S::CTW>::Raw praw;
+    MS mstage;
+    if constexpr (STAGE) {
+        mstage.load(mx, h);
+        P.fetch_pi(mx, h, cs * S::CTW, praw);
+    } else {
+        P.fetch(mx, h, cs * S::CTW, praw);
+    }
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(XK + (size_t(p) * N + lo) * DR, rows * DR * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t(p) * N + lo) * DV, rows * DV * 2);
 
@@ -276,6 +227,15 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const u
         load_v(0);
         for (int c = threadIdx.x; c < S::ROUND * LDG / 8; c += NT) reinterpret_cast<u32x4*>(Gs)[c] = u32x4{0u, 0u, 0u, 0u};
         for (int c = threadIdx.x; c < S::ROUND * LDV / 8; c += NT) reinterpret_cast<u32x4*>(Vs)[c] = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (STAGE) {  // while the tiles are in flight
+            mstage.commit(reinterpret_cast<float*>(&Xt[0][0]));
+            __syncthreads();
+            P.template read_staged<Kp>(reinterpret_cast<const float*>(&Xt[0][0]), cs * S::CTW, praw);
+            P.build(praw, mx.K, cs * S::CTW);
+            __syncthreads();  // staging area free for the x tiles
+        } else {
+            P.build(praw, mx.K, cs * S::CTW);
+        }
         xt.commit(Xt[0]);
         xt.load(rx, 2 * S::ROUND);
         if (XB == 2) xt1.commit(Xt[XB - 1]);
@@ -441,8 +401,8 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 template <int DR, int KT, int VT>
 __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const uint16_t* __restrict__ XQ, int64_t N,
                                                                        int H, int64_t rows_per_block,
-                                                                       const uint16_t* planes, const float* cvec,
-                                                                       const uint16_t* __restrict__ memory, float eps,
+                                                                       Mixture mx, const uint16_t* __restrict__ memory,
+                                                                       float eps,
                                                                        uint16_t* __restrict__ O) {
     using S = Split<DR, KT>;
     constexpr int NW = S::NW, NT = NW * 64;
@@ -471,8 +431,17 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
     const int64_t lo = int64_t(blockIdx.x) * rows_per_block, hi = min<int64_t>(lo + rows_per_block, N);
     const int64_t rows = hi - lo;
     const int64_t R = (rows + S::ROUND - 1) / S::ROUND;
+    using MS = MixtureStage<DR, Kp, NT>;
+    constexpr bool STAGE = sizeof(Xt) >= MS::LDS_BYTES;
     WaveParams<DR, S::CTW> P;
-    P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * S::CTW);
+    typename WaveParams<DR, S::CTW>::Raw praw;
+    MS mstage;
+    if constexpr (STAGE) {
+        mstage.load(mx, h);
+        P.fetch_pi(mx, h, cs * S::CTW, praw);
+    } else {
+        P.fetch(mx, h, cs * S::CTW, praw);
+    }
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(XQ + (size_t(p) * N + lo) * DR, rows * DR * 2);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + (size_t(p) * N + lo) * DV, rows * DV * 2);
     // latent memory of this problem: Z -> registers in score-row order (loaded before the
@@ -493,6 +462,15 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
         XT xt1;
         xt.load(rx, 0);
         xt1.load(rx, S::ROUND);
+        if constexpr (STAGE) {  // while the tiles are in flight
+            mstage.commit(reinterpret_cast<float*>(&Xt[0][0]));
+            __syncthreads();
+            P.template read_staged<Kp>(reinterpret_cast<const float*>(&Xt[0][0]), cs * S::CTW, praw);
+            P.build(praw, mx.K, cs * S::CTW);
+            __syncthreads();  // staging area free for the x tiles
+        } else {
+            P.build(praw, mx.K, cs * S::CTW);
+        }
         if (MS_LDS)
             for (int c = threadIdx.x; c < 2 * DV * Kp / 8; c += NT) {
                 const int row = c / (Kp / 8), col = (c - row * (Kp / 8)) * 8;
@@ -631,27 +609,7 @@ hipError_t with_vt(int vt, F&& f) {
 
 namespace {
 
-struct Bf16Params {
-    uint16_t* planes;  // [H][4][Kp][dr]
-    float* cvec;       // [H][Kp]
-};
-
-Bf16Params bf16_params_view(const Plan& p, char* ws) {
-    Bf16Params v;
-    v.cvec = reinterpret_cast<float*>(ws + p.off_params);
-    v.planes = reinterpret_cast<uint16_t*>(ws + p.off_params + round_up(size_t(p.H * p.Kp) * 4, 256));
-    return v;
-}
-
 int kt_of(const Plan& p) { return int(p.Kp / 32); }
-
-hipError_t launch_params(const Plan& p, const float* mu, const float* s2, const float* pi, char* ws, hipStream_t st) {
-    Bf16Params v = bf16_params_view(p, ws);
-    GMA_LAUNCH("bf16_params", bf::params_kernel, dim3(unsigned((p.Kp + 3) / 4), unsigned(p.H)), dim3(256), 0, st, mu,
-               s2, pi, int(p.K), int(p.Kp),
-                       int(p.dr), v.planes, v.cvec);
-    return hipGetLastError();
-}
 
 }  // namespace
 
@@ -666,22 +624,21 @@ int64_t bf16_round_tokens(int dr, int64_t Kp) {
 
 hipError_t bf16_responsibilities(const Plan& p, const void* X, const float* mu, const float* s2, const float* pi,
                                  void* Gamma, gma_dtype_t gamma_dtype, char* ws, hipStream_t st) {
-    hipError_t e = launch_params(p, mu, s2, pi, ws, st);
-    if (e != hipSuccess) return e;
-    Bf16Params v = bf16_params_view(p, ws);
+    (void)ws;
+    const bf::Mixture mx{mu, s2, pi, int(p.K)};
     return bf::with_dr_kt(int(p.dr), kt_of(p), [&](auto D, auto T) {
         constexpr int DR = decltype(D)::value, KT = decltype(T)::value;
         using S = bf::Split<DR, KT>;
         dim3 grid(unsigned((p.N + S::ROUND - 1) / S::ROUND), unsigned(p.P));
         GMA_LAUNCH("bf16_resp", (bf::resp_kernel<DR, KT>), grid, dim3(S::NW * 64), 0, st,
-                           static_cast<const uint16_t*>(X), p.N, int(p.H), int(p.K), v.planes, v.cvec, Gamma,
+                           static_cast<const uint16_t*>(X), p.N, int(p.H), mx, Gamma,
                            gamma_dtype == GMA_BF16 ? 1 : 0);
         return hipGetLastError();
     });
 }
 
-hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, char* ws, hipStream_t st, int64_t splits) {
-    Bf16Params v = bf16_params_view(p, ws);
+hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, const bf::Mixture& mx, char* ws,
+                               hipStream_t st, int64_t splits) {
     float* partials = reinterpret_cast<float*>(ws + p.off_partials);
     return bf::with_dr_kt(int(p.dr), kt_of(p), [&](auto D, auto T) {
         constexpr int DR = decltype(D)::value, KT = decltype(T)::value;
@@ -690,7 +647,7 @@ hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, cha
             using S = bf::Split<DR, KT>;
             GMA_LAUNCH(p.op == GMA_OP_CAUSAL ? "bf16_causal_aggregate" : "bf16_write", (bf::write_kernel<DR, KT, VT>), dim3(unsigned(splits), unsigned(p.P)), dim3(S::NW * 64), 0,
                                st, static_cast<const uint16_t*>(XK), static_cast<const uint16_t*>(V), p.N, int(p.H),
-                               p.seg, int(p.G), v.planes, v.cvec, partials);
+                               p.seg, int(p.G), mx, partials);
             return hipGetLastError();
         });
     });
@@ -698,16 +655,15 @@ hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, cha
 
 hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu, const float* s2,
                       const float* pi, float eps, void* O, char* ws, hipStream_t st) {
-    hipError_t e = launch_params(p, mu, s2, pi, ws, st);
+    const bf::Mixture mx{mu, s2, pi, int(p.K)};
+    hipError_t e = bf16_write_partials(p, XK, V, mx, ws, st, p.G);
     if (e != hipSuccess) return e;
-    if ((e = bf16_write_partials(p, XK, V, ws, st, p.G)) != hipSuccess) return e;
     float* partials = reinterpret_cast<float*>(ws + p.off_partials);
     uint16_t* memory = reinterpret_cast<uint16_t*>(ws + p.off_memory);
     const int E = int(p.Kp * (p.dv + 1));
     GMA_LAUNCH("bf16_combine", bf::combine_kernel, dim3(unsigned((E / 4 + 255) / 256), unsigned(p.P)), dim3(256), 0, st, partials,
                        int(p.G), int(p.Kp), int(p.dv), memory);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    Bf16Params v = bf16_params_view(p, ws);
     return bf::with_dr_kt(int(p.dr), kt_of(p), [&](auto D, auto T) {
         constexpr int DR = decltype(D)::value, KT = decltype(T)::value;
         return bf::with_vt(int(p.dv / 32), [&](auto VV) {
@@ -715,7 +671,7 @@ hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void*
             using S = bf::Split<DR, KT>;
             dim3 grid(unsigned((p.N + p.read_rows - 1) / p.read_rows), unsigned(p.P));
             GMA_LAUNCH("bf16_read", (bf::read_kernel<DR, KT, VT>), grid, dim3(S::NW * 64), 0, st,
-                               static_cast<const uint16_t*>(XQ), p.N, int(p.H), p.read_rows, v.planes, v.cvec, memory,
+                               static_cast<const uint16_t*>(XQ), p.N, int(p.H), p.read_rows, mx, memory,
                                eps, static_cast<uint16_t*>(O));
             return hipGetLastError();
         });
@@ -724,13 +680,12 @@ hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void*
 
 hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu, const float* s2,
                        const float* pi, float eps, void* O, char* ws, hipStream_t st) {
-    hipError_t e = launch_params(p, mu, s2, pi, ws, st);
-    if (e != hipSuccess) return e;
+    const bf::Mixture mx{mu, s2, pi, int(p.K)};
+    hipError_t e = hipSuccess;
     // aggregates of segments 0 .. G-2 (the last segment's aggregate is never read); the
     // scan workgroup of segment s sums aggregates 0 .. s-1 itself
-    if (p.G > 1 && (e = bf16_write_partials(p, XK, V, ws, st, p.G - 1)) != hipSuccess) return e;
-    Bf16Params v = bf16_params_view(p, ws);
-    return bf16_scan(p, XQ, XK, V, v.planes, v.cvec, eps, O, ws, st);
+    if (p.G > 1 && (e = bf16_write_partials(p, XK, V, mx, ws, st, p.G - 1)) != hipSuccess) return e;
+    return bf16_scan(p, XQ, XK, V, mu, s2, pi, eps, O, ws, st);
 }
 
 }  // namespace gma

@@ -251,6 +251,48 @@ struct Split {
     static constexpr int KS = DR / 16;          // k-steps of the d contraction
 };
 
+// Mixture parameters of every head: mu, s2 [H][K][d_r] fp32 row-major, pi [H][K] fp32.
+struct Mixture {
+    const float* mu;
+    const float* s2;
+    const float* pi;
+    int K;
+};
+
+// One head's mu and sigma2 rows [KP][DR] (rows past K repeat row K - 1) fetched by the
+// whole workgroup with coalesced 16-byte loads and staged in LDS as fp32 rows of DR + 4
+// floats, so that the 16-byte reads of a fragment's 8 dims by 32 rows are conflict-free.
+// A strided per-lane fetch of the same values costs several times the L1 work, and every
+// wave of the workgroup would repeat it.
+template <int DR, int KP, int NT>
+struct MixtureStage {
+    static constexpr int LD = DR + 4;
+    static constexpr int LDS_BYTES = 2 * KP * LD * 4;
+    static constexpr int CPR = DR / 4, CHUNKS = 2 * KP * CPR, PER = (CHUNKS + NT - 1) / NT;
+    static constexpr bool EVEN = CHUNKS % NT == 0;
+    float4 r[PER];
+
+    __device__ __forceinline__ void load(const Mixture& mx, int h) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int c = threadIdx.x + u * NT;
+            const int arr = c / (KP * CPR), cc = c - arr * KP * CPR, row = cc / CPR, col = cc - row * CPR;
+            const int kr = row < mx.K ? row : mx.K - 1;
+            if (EVEN || c < CHUNKS)
+                r[u] = *reinterpret_cast<const float4*>((arr ? mx.s2 : mx.mu) + (size_t(h) * mx.K + kr) * DR + 4 * col);
+        }
+    }
+    // lds: [2][KP][LD] fp32 (mu rows, then sigma2 rows)
+    __device__ __forceinline__ void commit(float* lds) const {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int c = threadIdx.x + u * NT;
+            const int arr = c / (KP * CPR), cc = c - arr * KP * CPR, row = cc / CPR, col = cc - row * CPR;
+            if (EVEN || c < CHUNKS) *reinterpret_cast<float4*>(lds + (arr * KP + row) * LD + 4 * col) = r[u];
+        }
+    }
+};
+
 // Parameter planes of one wave: 4 bf16 planes (a_hi, a_lo, b_hi, b_lo) for its CTW
 // component tiles, as MFMA A fragments, and the score constants in D-row order.
 template <int DR, int CTW>
@@ -258,29 +300,120 @@ struct WaveParams {
     bf16x8 w[CTW][DR / 16][4];
     float c[CTW][16];
 
-    // planes: one head's fragment-major planes [Kp/32][DR/16][4][64 lanes][8] bf16 (every
-    // fragment one contiguous 1 KiB block); cvec: [Kp] fp32 of one head; ct0: first tile
-    __device__ __forceinline__ void load(const uint16_t* __restrict__ planes, const float* __restrict__ cvec,
-                                         int Kp, int ct0) {
-        const int l = threadIdx.x & 63, lh = l >> 5;
-        (void)Kp;
+    // Raw parameters behind this lane's fragments, fetched apart from the arithmetic so a
+    // kernel can put its first tile loads in flight before it waits for them.
+    struct Raw {
+        float4 m[CTW][DR / 16][2], v[CTW][DR / 16][2];
+        float pk[CTW];
+    };
+
+    // Lane (lh, j) owns component 32 tile + j and dims 16 ks + 8 lh .. + 7 of every k-step,
+    // which is exactly its A fragment.  mu, s2: [H][K][DR], pi: [H][K]; h: head; ct0: first
+    // component tile of this wave.  Lanes of padded components (k >= K) read row K - 1.
+    __device__ __forceinline__ static void fetch(const Mixture& mx, int h, int ct0, Raw& r) {
+        const int l = threadIdx.x & 63, lh = l >> 5, K = mx.K;
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
+            const int k = (ct0 + ct) * 32 + (l & 31);
+            const int kr = k < K ? k : K - 1;
+            const size_t row = (size_t(h) * K + kr) * DR + 8 * lh;
 #pragma unroll
             for (int ks = 0; ks < DR / 16; ++ks)
 #pragma unroll
-                for (int pl = 0; pl < 4; ++pl)
-                    w[ct][ks][pl] = *reinterpret_cast<const bf16x8*>(
-                        planes + ((size_t((ct0 + ct) * (DR / 16) + ks) * 4 + pl) * 64 + l) * 8);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float4 cv = *reinterpret_cast<const float4*>(cvec + (ct0 + ct) * 32 + 8 * q + 4 * lh);
-                c[ct][4 * q + 0] = cv.x;
-                c[ct][4 * q + 1] = cv.y;
-                c[ct][4 * q + 2] = cv.z;
-                c[ct][4 * q + 3] = cv.w;
-            }
+                for (int h4 = 0; h4 < 2; ++h4) {
+                    r.m[ct][ks][h4] = *reinterpret_cast<const float4*>(mx.mu + row + 16 * ks + 4 * h4);
+                    r.v[ct][ks][h4] = *reinterpret_cast<const float4*>(mx.s2 + row + 16 * ks + 4 * h4);
+                }
+            r.pk[ct] = mx.pi[size_t(h) * K + kr];
         }
+    }
+
+    // Mixing weights of this lane's components (the rest of Raw comes from read_staged).
+    __device__ __forceinline__ static void fetch_pi(const Mixture& mx, int h, int ct0, Raw& r) {
+        const int l = threadIdx.x & 63, K = mx.K;
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+            const int k = (ct0 + ct) * 32 + (l & 31);
+            r.pk[ct] = mx.pi[size_t(h) * K + (k < K ? k : K - 1)];
+        }
+    }
+
+    // This lane's fragment dims from a MixtureStage buffer of KP rows.
+    template <int KP>
+    __device__ __forceinline__ static void read_staged(const float* lds, int ct0, Raw& r) {
+        constexpr int LD = DR + 4;
+        const int l = threadIdx.x & 63, lh = l >> 5;
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+            const int row = (ct0 + ct) * 32 + (l & 31);
+#pragma unroll
+            for (int ks = 0; ks < DR / 16; ++ks)
+#pragma unroll
+                for (int h4 = 0; h4 < 2; ++h4) {
+                    r.m[ct][ks][h4] = *reinterpret_cast<const float4*>(lds + row * LD + 16 * ks + 8 * lh + 4 * h4);
+                    r.v[ct][ks][h4] = *reinterpret_cast<const float4*>(lds + (KP + row) * LD + 16 * ks + 8 * lh + 4 * h4);
+                }
+        }
+    }
+
+    // Builds the planes from the mixture parameters (Gaussian Mixture Attention, Eq. 16 with
+    // the square expanded, in log2 units):
+    //   a = log2(e) mu / sigma2,  b = -log2(e) / (2 sigma2),  each as a bf16 hi + lo pair,
+    //   c = log2 pi - (sum_d log2 sigma2 + log2(e) mu^2 / sigma2) / 2   (fp32).
+    // Padded components get zero planes (sigma2 taken as +inf) and c = -inf, so their
+    // responsibility is exactly 0.  sigma2 must be a positive normal float.
+    __device__ __forceinline__ void build(const Raw& r, int K, int ct0) {
+        const float L2E = 1.4426950408889634f;
+        const int l = threadIdx.x & 63, lh = l >> 5;
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+            const bool valid = (ct0 + ct) * 32 + (l & 31) < K;
+            float csum = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < DR / 16; ++ks) {
+                const float m[8] = {r.m[ct][ks][0].x, r.m[ct][ks][0].y, r.m[ct][ks][0].z, r.m[ct][ks][0].w,
+                                    r.m[ct][ks][1].x, r.m[ct][ks][1].y, r.m[ct][ks][1].z, r.m[ct][ks][1].w};
+                const float v[8] = {r.v[ct][ks][0].x, r.v[ct][ks][0].y, r.v[ct][ks][0].z, r.v[ct][ks][0].w,
+                                    r.v[ct][ks][1].x, r.v[ct][ks][1].y, r.v[ct][ks][1].z, r.v[ct][ks][1].w};
+                u32x4 ah, al, bh, bl;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float a2[2], b2[2];
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const float vv = v[2 * q + e];
+                        const float inv = __builtin_amdgcn_rcpf(valid ? vv : INFINITY);
+                        const float mi = m[2 * q + e] * inv;
+                        a2[e] = mi * L2E;
+                        b2[e] = (-0.5f * L2E) * inv;
+                        csum += __builtin_amdgcn_logf(vv) + mi * m[2 * q + e] * L2E;
+                    }
+                    ah[q] = pack_bf16x2(a2[0], a2[1]);
+                    bh[q] = pack_bf16x2(b2[0], b2[1]);
+                    al[q] = pack_bf16x2(a2[0] - __uint_as_float(ah[q] << 16), a2[1] - __uint_as_float(ah[q] & 0xffff0000u));
+                    bl[q] = pack_bf16x2(b2[0] - __uint_as_float(bh[q] << 16), b2[1] - __uint_as_float(bh[q] & 0xffff0000u));
+                }
+                w[ct][ks][0] = __builtin_bit_cast(bf16x8, ah);
+                w[ct][ks][1] = __builtin_bit_cast(bf16x8, al);
+                w[ct][ks][2] = __builtin_bit_cast(bf16x8, bh);
+                w[ct][ks][3] = __builtin_bit_cast(bf16x8, bl);
+            }
+            // the two halves of component k's dims sit in lanes j and j + 32
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(csum), __float_as_uint(csum), false, false);
+            const float ctot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            const float ck = valid ? __builtin_amdgcn_logf(r.pk[ct]) - 0.5f * ctot : -INFINITY;
+            // D rows of this lane: components 8 q + 4 lh + i of the tile
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) c[ct][4 * q + i] = __shfl(ck, 8 * q + 4 * lh + i);
+        }
+    }
+
+    __device__ __forceinline__ void compute(const Mixture& mx, int h, int ct0) {
+        Raw r;
+        fetch(mx, h, ct0, r);
+        build(r, mx.K, ct0);
     }
 };
 

@@ -85,7 +85,7 @@ constexpr int scan_chunk() {
 template <int DR, int KT, int VT, int CH_REQ>
 __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
     scan_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
-                int64_t N, int H, int64_t seg, int G, const uint16_t* planes, const float* cvec,
+                int64_t N, int H, int64_t seg, int G, Mixture mx,
                 const float* __restrict__ prefix, float eps, uint16_t* __restrict__ O) {
     constexpr int CH = scan_chunk<DR, KT, VT, CH_REQ>();
     using S = Split<DR, KT>;
@@ -131,8 +131,18 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
     const int64_t rows = hi - lo;
     const int64_t C = (rows + CH - 1) / CH;  // chunks of this segment
 
+    // mixture parameters staged through the V tile buffers when they are large enough
+    using MS = MixtureStage<DR, Kp, NT>;
+    constexpr bool STAGE = sizeof(Vs) >= MS::LDS_BYTES;
     WaveParams<DR, CTW> P;
-    P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * CTW);
+    typename WaveParams<DR, CTW>::Raw praw;
+    MS mstage;
+    if constexpr (STAGE) {
+        mstage.load(mx, h);
+        P.fetch_pi(mx, h, cs * CTW, praw);
+    } else {
+        P.fetch(mx, h, cs * CTW, praw);
+    }
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(XQ + (size_t(p) * N + lo) * DR, rows * DR * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(XK + (size_t(p) * N + lo) * DR, rows * DR * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t(p) * N + lo) * DV, rows * DV * 2);
@@ -230,10 +240,19 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
         for (int kt = 0; kt < KT16; ++kt) mem[cc][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int k = threadIdx.x; k < Kp; k += NT) Zs[k] = 0.0f;
 
-    // prologue loads first, so they overlap the prefix sum
+    // prologue loads first, so they overlap the operand build and the prefix sum
     load_v(0);
     xq.load(rq, 0);
     xk.load(rk, 0);
+    if constexpr (STAGE) {
+        mstage.commit(reinterpret_cast<float*>(&Vs[0][0]));
+        __syncthreads();
+        P.template read_staged<Kp>(reinterpret_cast<const float*>(&Vs[0][0]), cs * CTW, praw);
+        P.build(praw, mx.K, cs * CTW);
+        __syncthreads();  // staging area free for the V tiles
+    } else {
+        P.build(praw, mx.K, cs * CTW);
+    }
 #pragma unroll 2
     for (int gs = 0; gs < seg_idx; ++gs) {
         const float* a = agg + size_t(gs) * E;
@@ -460,7 +479,7 @@ constexpr int serial_scan_chunk() {
 template <int DR, int KT, int VT, int CH_REQ>
 __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
     serial_scan_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
-                int64_t N, int H, int64_t seg, int G, const uint16_t* planes, const float* cvec,
+                int64_t N, int H, int64_t seg, int G, Mixture mx,
                 const float* __restrict__ prefix, float eps, uint16_t* __restrict__ O) {
     constexpr int CH = serial_scan_chunk<DR, KT, VT, CH_REQ>();
     using S = Split<DR, KT>;
@@ -503,7 +522,7 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
     const int64_t rows = hi - lo;
 
     WaveParams<DR, CTW> P;
-    P.load(planes + size_t(h) * 4 * Kp * DR, cvec + size_t(h) * Kp, Kp, cs * CTW);
+    P.compute(mx, h, cs * CTW);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(XQ + (size_t(p) * N + lo) * DR, rows * DR * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(XK + (size_t(p) * N + lo) * DR, rows * DR * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t(p) * N + lo) * DV, rows * DV * 2);
@@ -821,8 +840,9 @@ hipError_t with_all(int dr, int kt, int vt, int ch, F&& f) {
 
 // The bf16 scan works on 32-position score subtiles, so a requested chunk of 16
 // positions runs as 32 (the chunk length only changes the order of the sums).
-hipError_t bf16_scan(const Plan& p, const void* XQ, const void* XK, const void* V, const uint16_t* planes,
-                     const float* cvec, float eps, void* O, char* ws, hipStream_t st) {
+hipError_t bf16_scan(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu,
+                     const float* s2, const float* pi, float eps, void* O, char* ws, hipStream_t st) {
+    const bf::Mixture mx{mu, s2, pi, int(p.K)};
     const float* prefix = reinterpret_cast<const float*>(ws + p.off_partials);
     const int ch = p.chunk < 32 ? 32 : p.chunk;
     return bf::with_all(int(p.dr), int(p.Kp / 32), int(p.dv / 32), ch, [&](auto D, auto T, auto W, auto C) {
@@ -834,12 +854,12 @@ hipError_t bf16_scan(const Plan& p, const void* XQ, const void* XK, const void* 
         if constexpr (KT <= 4 && DR * KT <= 256) {
             GMA_LAUNCH("bf16_scan", (bf::scan_kernel<DR, KT, VT, CH>), dim3(unsigned(p.G), unsigned(p.P)),
                        dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
-                       static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), planes, cvec, prefix, eps,
+                       static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), mx, prefix, eps,
                        static_cast<uint16_t*>(O));
         } else {
             GMA_LAUNCH("bf16_scan", (bf::serial_scan_kernel<DR, KT, VT, CH>), dim3(unsigned(p.G), unsigned(p.P)),
                        dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
-                       static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), planes, cvec, prefix, eps,
+                       static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), mx, prefix, eps,
                        static_cast<uint16_t*>(O));
         }
         return hipGetLastError();

@@ -74,7 +74,7 @@ hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void
 int64_t bf16_round_tokens(int dr, int64_t Kp);
 // causal chunked scan of every segment; segment s starts from the sum of the aggregates
 // of segments 0 .. s-1 in the workspace partials (gma_bf16_scan.hip)
-hipError_t bf16_scan(const Plan& p, const void* XQ, const void* XK, const void* V, const uint16_t* planes,
-                     const float* cvec, float eps, void* O, char* ws, hipStream_t st);
+hipError_t bf16_scan(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu,
+                     const float* s2, const float* pi, float eps, void* O, char* ws, hipStream_t st);
 
 }  // namespace gma
