@@ -148,13 +148,13 @@ def alg_bytes_per_token_head(w, kernel: str) -> float:
         return e * (w.d_r + w.d_v)          # X_K and V in
     if kernel.endswith("_read"):
         return e * (w.d_r + w.d_v)          # X_Q in, O out
-    if kernel.endswith("_scan"):
-        return e * (2 * w.d_r + 2 * w.d_v)  # X_Q, X_K, V in, O out
+    if kernel.endswith("_scan") or kernel.endswith("_bidir") or kernel.endswith("_causal"):
+        return e * (2 * w.d_r + 2 * w.d_v)  # X_Q, X_K, V in, O out (whole forward in one launch)
     return 0.0
 
 
-KERNEL_SYMBOL = {"bf16_scan": "gma::bf::scan_kernel", "bf16_write": "gma::bf::write_kernel<64, 2",
-                 "bf16_read": "gma::bf::read_kernel", "bf16_causal_aggregate": "gma::bf::write_kernel<64, 1"}
+KERNEL_SYMBOL = {"bf16_scan": "gma::bf::scan_kernel", "bf16_bidir": "gma::bf::bidir_kernel",
+                 "bf16_causal": "gma::bf::causal_kernel", "bf16_causal_aggregate": "gma::bf::write_kernel<64, 1"}
 
 
 def main(args=None, probe_only=False) -> int:
@@ -248,7 +248,8 @@ def main(args=None, probe_only=False) -> int:
     kernel_of = {}
     for w in ws_list:
         pre = "bf16" if w.dtype == "bf16" else "f32"
-        ks = ["params", "scan", "causal_aggregate", "prefix"] if w.causal else ["params", "write", "combine", "read"]
+        ks = ["params", "scan", "causal_aggregate", "causal", "prefix"] if w.causal else \
+            ["params", "write", "combine", "read", "bidir"]
         for k in ks:
             kernel_of.setdefault("%s_%s" % (pre, k), []).append(w)
     kernels = {}

@@ -2,10 +2,13 @@
 // dispatch to the fp32 (VALU) or bf16 (MFMA) kernel launchers.  Declarations and
 // the contract of every entry point are in include/gma.h.
 #include <algorithm>
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdint>
 #include <map>
 #include <mutex>
+#include <random>
 #include <string>
 #include <vector>
 
@@ -91,21 +94,36 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
         p.seg = round_up(size_t(cdiv(p.N, best_g)), kTokenTile);
         p.G = cdiv(p.N, p.seg);
     }
-    p.read_rows = 0;
-    if (io == GMA_BF16 && op == GMA_OP_BIDIR && p.P > 0 && p.N > 0) {
-        const int64_t round = bf16_round_tokens(int(p.dr), p.Kp);
-        const int64_t per_problem = std::max<int64_t>(1, cdiv(kBidirBlocks, p.P));
-        p.read_rows = round_up(size_t(cdiv(p.N, per_problem)), size_t(round));
-    }
     const size_t mem_elems = size_t(p.Kp) * size_t(p.dv + 1);
     p.partials_bytes = (op == GMA_OP_RESPONSIBILITIES) ? 0 : round_up(size_t(p.P * p.G) * mem_elems * 4, 256);
     p.memory_bytes = (op == GMA_OP_BIDIR) ? round_up(size_t(p.P) * mem_elems * 4, 256) : 0;
     p.off_params = 0;
     p.off_partials = p.off_params + p.params_bytes;
+    // hand-off words of the fused bf16 kernels: [P][2][G] (bidirectional), [P][G] (causal)
+    p.flags_bytes = 0;
+    if (io == GMA_BF16 && op == GMA_OP_BIDIR) p.flags_bytes = round_up(size_t(p.P * 2 * p.G) * 8, 256);
+    if (io == GMA_BF16 && op == GMA_OP_CAUSAL) p.flags_bytes = round_up(size_t(p.P * p.G) * 8, 256);
     p.off_memory = p.off_partials + p.partials_bytes;
-    p.total = p.off_memory + p.memory_bytes;
+    p.off_flags = p.off_memory + p.memory_bytes;
+    p.total = p.off_flags + p.flags_bytes;
     *pl = p;
     return GMA_OK;
+}
+
+// ---- launch tokens ----------------------------------------------------------------
+
+uint64_t launch_token() {
+    // splitmix64 over a per-process random seed plus a launch counter
+    static std::atomic<uint64_t> counter{0};
+    static const uint64_t seed = [] {
+        std::random_device rd;
+        return (uint64_t(rd()) << 32) ^ uint64_t(rd()) ^
+               uint64_t(std::chrono::high_resolution_clock::now().time_since_epoch().count());
+    }();
+    uint64_t z = seed + 0x9e3779b97f4a7c15ull * (counter.fetch_add(1, std::memory_order_relaxed) + 1);
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
 }
 
 // ---- kernel timing ----------------------------------------------------------------

@@ -18,45 +18,11 @@
 #include <type_traits>
 
 #include "gma_bf16_common.h"
+#include "gma_bf16_phases.h"
 #include "gma_internal.h"
 
 namespace gma {
 namespace bf {
-
-// ---------------------------------------------------------------------------- softmax across waves
-
-// Per-round softmax statistics shared by the CS waves of one token subtile.
-struct Stats {
-    float m, L, D;
-};
-
-// Combines this wave's (m, L, D) with those of the other component groups of its
-// token subtile (published in `st` before the barrier).  Returns the factor that turns
-// this wave's exp2(s - m_w) into probabilities, and the full D / L.
-template <int CS>
-__device__ __forceinline__ float combine_stats(const Stats* st, int ts, int cs, int j, float m, float L, float D,
-                                               float& DoverL) {
-    if (CS == 1) {
-        const float r = __builtin_amdgcn_rcpf(L);
-        DoverL = D * r;
-        return r;
-    }
-    float mm = -INFINITY;
-#pragma unroll
-    for (int c = 0; c < CS; ++c) mm = fmaxf(mm, st[(ts * CS + c) * 32 + j].m);
-    float Lt = 0.0f, Dt = 0.0f;
-#pragma unroll
-    for (int c = 0; c < CS; ++c) {
-        const Stats s = st[(ts * CS + c) * 32 + j];
-        const float f = __builtin_amdgcn_exp2f(s.m - mm);
-        Lt = fmaf(s.L, f, Lt);
-        Dt = fmaf(s.D, f, Dt);
-    }
-    (void)cs;
-    const float r = __builtin_amdgcn_rcpf(Lt);
-    DoverL = Dt * r;
-    return __builtin_amdgcn_exp2f(m - mm) * r;
-}
 
 // ---------------------------------------------------------------------------- responsibilities
 
@@ -106,283 +72,61 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) resp_kernel(const ui
         }
 }
 
-// ---------------------------------------------------------------------------- write (Gamma_K^T [V | 1])
+// ---------------------------------------------------------------------------- write (standalone)
 
-// Rows [lo, hi) of one problem, in rounds of ROUND tokens, software-pipelined so that
-// every wave keeps the matrix cores and the vector ALU busy at the same time.
-// Iteration r, region A (one basic block, MFMA and VALU interleaved):
-//   MFMAs of round r+1's scores (x tile r+1, in LDS) and of round r-1's accumulation
-//   Vt^T += V^T Gamma_K, Z += Gamma_K^T 1 (Gamma_K and V tiles r-1, in LDS);
-//   VALU: softmax statistics of round r (scores issued in iteration r-1) and, with a
-//   double-buffered x tile, the split of x tile r+2 into its free buffer  -> B1
-// Region B: Gamma_K of round r (bf16) and V tile r into LDS (single x buffer: x tile r+2
-//   too); loads of V r+1 and x r+3 issued  -> B2
-// Every LDS overwrite follows a barrier that all reads of the old contents precede (a
-// wave's LDS reads complete before the MFMAs that use them issue).  Gamma_K and V start
-// zeroed, so round -1's accumulation adds nothing; round R's scores (x past the end
-// reads zero) are computed and discarded.  No branch splits region A.
-constexpr int gcd_i(int a, int b) { return b == 0 ? a : gcd_i(b, a % b); }
-
+// Grid (G, P): split g of problem p into its partial.
 template <int DR, int KT, int VT>
-__global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) write_kernel(const uint16_t* __restrict__ XK,
+__global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
+__attribute__((amdgpu_waves_per_eu(waves_for_lds(WriteLds<DR, KT, VT>::bytes)))) write_kernel(const uint16_t* __restrict__ XK,
                                                                         const uint16_t* __restrict__ V, int64_t N,
                                                                         int H, int64_t seg, int G,
                                                                         Mixture mx, float* __restrict__ partials) {
-    using S = Split<DR, KT>;
-    constexpr int NW = S::NW, NT = NW * 64;
+    __shared__ __attribute__((aligned(16))) char smem[WriteLds<DR, KT, VT>::bytes];
     constexpr int Kp = KT * 32, DV = VT * 32;
-    constexpr int LDG = Kp + 8, LDV = DV + 8;
-    using XT = XTile<DR, S::ROUND, NT>;
-    constexpr int VCHUNKS = S::ROUND * DV / 8;
-    constexpr int VCH = (VCHUNKS + NT - 1) / NT;
-    constexpr bool VEVEN = VCHUNKS % NT == 0;
-    // accumulation work, identical for every wave: V units are (component tile, value
-    // tile) pairs, split along the round's k-steps when there are fewer pairs than waves;
-    // Z units are component tiles times an all-ones operand, split the same way
-    constexpr int KSR = S::ROUND / 16;
-    constexpr int VPAIRS = KT * VT;
-    constexpr int VSPLIT = NW / gcd_i(VPAIRS, NW), VU = VPAIRS * VSPLIT / NW, VKS = KSR / VSPLIT;
-    constexpr int ZSPLIT = NW / gcd_i(KT, NW), ZU = KT * ZSPLIT / NW, ZKS = KSR / ZSPLIT;
-    static_assert(KSR % VSPLIT == 0 && KSR % ZSPLIT == 0, "round too short for the accumulation split");
-    constexpr int MF_A = 5 * S::CTW * S::KS + VU * VKS + ZU * ZKS;  // MFMAs of region A
-    constexpr int BASE_LDS = S::TS * S::CS * 32 * 12 + S::ROUND * (LDG + LDV) * 2;
-    constexpr int XB = (BASE_LDS + 2 * XT::LDS_BYTES <= 80 * 1024) ? 2 : 1;  // keep two workgroups per CU
-    __shared__ Stats st[S::TS * S::CS * 32];
-    __shared__ __attribute__((aligned(16))) u32x4 Xt[XB][XT::LDS_BYTES / 16];
-    __shared__ __attribute__((aligned(16))) uint16_t Gs[S::ROUND * LDG];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[S::ROUND * LDV];
-    __shared__ float Zred[KT * ZSPLIT * 32];
-
-    const int wave = wave_id(), l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
-    const int cs = wave % S::CS, ts = wave / S::CS;
     const int64_t p = blockIdx.y;
-    const int g_idx = blockIdx.x;
-    const int h = int(p % H);
-    const int64_t lo = int64_t(g_idx) * seg, hi = min<int64_t>(lo + seg, N);
-    const int64_t rows = hi - lo;
-    const int64_t R = (rows + S::ROUND - 1) / S::ROUND;  // rounds of this split
-    // mixture parameters staged through the x tile buffer when it is large enough
-    using MS = MixtureStage<DR, Kp, NT>;
-    constexpr bool STAGE = sizeof(Xt) >= MS::LDS_BYTES;
-    WaveParams<DR, S::CTW> P;
-    typename WaveParams<DR, S::CTW>::Raw praw;
-    MS mstage;
-    if constexpr (STAGE) {
-        mstage.load(mx, h);
-        P.fetch_pi(mx, h, cs * S::CTW, praw);
-    } else {
-        P.fetch(mx, h, cs * S::CTW, praw);
-    }
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(XK + (size_t(p) * N + lo) * DR, rows * DR * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t(p) * N + lo) * DV, rows * DV * 2);
-
-    XT xt;
-    u32x4 vr[VCH];
-    auto load_v = [&](int64_t row0) {
-#pragma unroll
-        for (int u = 0; u < VCH; ++u) {
-            const int c = threadIdx.x + u * NT;
-            vr[u] = (VEVEN || c < VCHUNKS) ? buf_load16(rv, uint32_t((row0 * DV + int64_t(c) * 8) * 2))
-                                           : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    f32x16 vacc[VU], zacc[ZU];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-#pragma unroll
-        for (int i = 0; i < VU; ++i) vacc[i][r] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < ZU; ++i) zacc[i][r] = 0.0f;
-    }
-    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
-    float zr[S::CTW][16];
-    f32x16 acc_a_init[S::CTW];  // round 0's scores when the x tile is single-buffered
-    auto accumulate = [&]() __attribute__((always_inline)) {  // Vt^T += V^T Gamma_K, Z += Gamma_K^T 1
-#pragma unroll
-        for (int i = 0; i < VU; ++i) {
-            const int q = wave + i * NW, pair = q / VSPLIT, part = q - pair * VSPLIT;
-            const int ct = pair / VT, vt = pair - ct * VT;
-#pragma unroll
-            for (int kk = 0; kk < VKS; ++kk) {
-                const int ks = part * VKS + kk;
-                vacc[i] = mfma(read_colfrag(Gs, LDG, 16 * ks, ct * 32), read_colfrag(Vs, LDV, 16 * ks, vt * 32), vacc[i]);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < ZU; ++i) {
-            const int q = wave + i * NW, ct = q / ZSPLIT, part = q - ct * ZSPLIT;
-#pragma unroll
-            for (int kk = 0; kk < ZKS; ++kk)
-                zacc[i] = mfma(read_colfrag(Gs, LDG, 16 * (part * ZKS + kk), ct * 32), ones, zacc[i]);
-        }
-    };
-
-    // prologue: Gamma_K and V tiles zeroed; x tiles 0 and 1 fetched together (one memory
-    // round trip), 0 (and 1) split into LDS; scores of round 0 issued; V 0 and x tile 2
-    // in flight
-    {
-        XT xt1;
-        xt.load(rx, 0);
-        xt1.load(rx, S::ROUND);
-        load_v(0);
-        for (int c = threadIdx.x; c < S::ROUND * LDG / 8; c += NT) reinterpret_cast<u32x4*>(Gs)[c] = u32x4{0u, 0u, 0u, 0u};
-        for (int c = threadIdx.x; c < S::ROUND * LDV / 8; c += NT) reinterpret_cast<u32x4*>(Vs)[c] = u32x4{0u, 0u, 0u, 0u};
-        if constexpr (STAGE) {  // while the tiles are in flight
-            mstage.commit(reinterpret_cast<float*>(&Xt[0][0]));
-            __syncthreads();
-            P.template read_staged<Kp>(reinterpret_cast<const float*>(&Xt[0][0]), cs * S::CTW, praw);
-            P.build(praw, mx.K, cs * S::CTW);
-            __syncthreads();  // staging area free for the x tiles
-        } else {
-            P.build(praw, mx.K, cs * S::CTW);
-        }
-        xt.commit(Xt[0]);
-        xt.load(rx, 2 * S::ROUND);
-        if (XB == 2) xt1.commit(Xt[XB - 1]);
-        __syncthreads();
-        if (XB == 1) {
-            scores_lds<DR, S::CTW>(P, Xt[0], ts, acc_a_init);
-            __syncthreads();  // x tile 0 consumed by every wave
-            xt1.commit(Xt[0]);
-            __syncthreads();
-        }
-    }
-    f32x16 acc_a[S::CTW], acc_b[S::CTW];
-    if (XB == 2) scores_lds<DR, S::CTW>(P, Xt[0], ts, acc_a);
-    else
-#pragma unroll
-        for (int ct = 0; ct < S::CTW; ++ct) acc_a[ct] = acc_a_init[ct];
-
-    // one pipelined iteration; `cur` holds round r's scores, `nxt` receives round r+1's
-    auto iteration = [&](const int64_t r, f32x16 (&cur)[S::CTW], f32x16 (&nxt)[S::CTW]) __attribute__((always_inline)) {
-        const int64_t r0 = r * S::ROUND;
-        const int xb1 = int((r + 1) % XB);
-        // ---- region A (the accumulation first: its transposing LDS reads bound the
-        // scheduling region, so everything after them can be interleaved)
-        accumulate();
-        scores_lds<DR, S::CTW>(P, Xt[xb1], ts, nxt);
-        if (XB == 2) {
-            xt.commit(Xt[xb1 ^ 1]);  // x tile r+2 into the buffer x tile r left
-            xt.load(rx, r0 + 3 * S::ROUND);
-        }
-        float m, L, D;
-        local_softmax<S::CTW, false>(cur, zr, m, L, D);
-        if (S::CS > 1) st[(ts * S::CS + cs) * 32 + j] = Stats{m, L, 0.0f};  // both lane halves hold the same
-#pragma unroll
-        for (int i = 0; i < MF_A; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then up to five VALU
-        }
-        __syncthreads();  // B1: statistics published; x tile r+1 and tiles r-1 consumed
-        // ---- region B
-        const int valid = int(max<int64_t>(0, min<int64_t>(32, rows - r0 - ts * 32)));
-        float dl;
-        float scale = combine_stats<S::CS>(st, ts, cs, j, m, L, 0.0f, dl);
-        if (j >= valid) scale = 0.0f;
-        store_gamma_lds<S::CTW>(cur, scale, Gs, LDG, ts * 32 + j, cs * S::CTW);
-#pragma unroll
-        for (int u = 0; u < VCH; ++u) {
-            const int c = threadIdx.x + u * NT;
-            if (VEVEN || c < VCHUNKS) {
-                const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
-                *reinterpret_cast<u32x4*>(Vs + row * LDV + col) = vr[u];
-            }
-        }
-        load_v(r0 + S::ROUND);
-        if (XB == 1) {
-            xt.commit(Xt[0]);
-            xt.load(rx, r0 + 3 * S::ROUND);
-        }
-        __syncthreads();  // B2: Gamma_K r, V r and x tile r+2 are in LDS
-    };
-    // rounds in pairs (static accumulator roles, no register copies on the back-edge); a
-    // round past the end only exists for an odd count and is skipped
-    for (int64_t r = 0; r < R; r += 2) {
-        iteration(r, acc_a, acc_b);
-        if (r + 1 < R) iteration(r + 1, acc_b, acc_a);
-    }
-    accumulate();  // the last round
-
-    // ---- partial of this split: VtT [DV][Kp] (Vt transposed) then Z [Kp].  Parts of a
-    // split unit are summed through LDS in increasing part order (the x tile area is free).
-    float* mem = partials + (size_t(p) * G + g_idx) * size_t(Kp) * (DV + 1);
-    float* red = reinterpret_cast<float*>(&Xt[0][0]);
-    static_assert(VSPLIT == 1 || VPAIRS * 1024 * 4 <= XB * XT::LDS_BYTES, "x tile area too small for the reduction");
-    __syncthreads();  // every wave is done with the x tiles
-#pragma unroll
-    for (int i = 0; i < VU; ++i) {
-        const int q = wave + i * NW, pair = q / VSPLIT, part = q - pair * VSPLIT;
-        const int ct = pair / VT, vt = pair - ct * VT;
-#pragma unroll
-        for (int pp = 0; pp < VSPLIT; ++pp) {
-            if (VSPLIT > 1) {
-                if (part == pp && pp > 0)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) vacc[i][r] += red[pair * 1024 + r * 64 + l];
-                if (part == pp && pp < VSPLIT - 1)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) red[pair * 1024 + r * 64 + l] = vacc[i][r];
-                __syncthreads();
-            }
-        }
-        if (part == VSPLIT - 1) {
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-                const int comp = ct * 32 + 8 * qq + 4 * lh;
-                *reinterpret_cast<float4*>(mem + size_t(vt * 32 + j) * Kp + comp) =
-                    make_float4(vacc[i][4 * qq + 0], vacc[i][4 * qq + 1], vacc[i][4 * qq + 2], vacc[i][4 * qq + 3]);
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < ZU; ++i) {
-        const int q = wave + i * NW, ct = q / ZSPLIT, part = q - ct * ZSPLIT;
-        if (j == 0)  // every column of the ones-operand tile holds the same sums
-#pragma unroll
-            for (int r = 0; r < 16; ++r) Zred[(ct * ZSPLIT + part) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)] = zacc[i][r];
-    }
-    __syncthreads();
-    for (int k = threadIdx.x; k < Kp; k += NT) {
-        const int ct = k >> 5, i = k & 31;
-        float z = 0.0f;
-#pragma unroll
-        for (int pp = 0; pp < ZSPLIT; ++pp) z += Zred[(ct * ZSPLIT + pp) * 32 + i];
-        mem[size_t(Kp) * DV + k] = z;
-    }
+    const int g = blockIdx.x;
+    const int64_t lo = int64_t(g) * seg, hi = min<int64_t>(lo + seg, N);
+    WaveParams<DR, Split<DR, KT>::CTW> P;
+    write_body<DR, KT, VT, true>(smem, XK, V, N, p, int(p % H), lo, hi, mx, P,
+                                 partials + (size_t(p) * G + g) * size_t(Kp) * (DV + 1));
 }
 
-// ---------------------------------------------------------------------------- combine / prefix
+// ---------------------------------------------------------------------------- combine
 
 // Bidirectional: memory = sum_g partial_g (increasing g), then the read operands:
 // VtT_hi, VtT_lo [DV][Kp] bf16 (Vt transposed, hi + lo split) and Z [Kp] fp32.  The
 // partials use the same [DV][Kp] + [Kp] order, so every access is coalesced.
-__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ partials, int G, int Kp, int DV,
-                                                      uint16_t* __restrict__ memory) {
-    // four consecutive elements per thread (Kp * DV is a multiple of 4, so a group never
-    // straddles the VtT / Z boundary); the G loads are independent and issued together
-    const int64_t p = blockIdx.y;
-    const int E = Kp * (DV + 1);
-    const int e = (blockIdx.x * 256 + threadIdx.x) * 4;
-    if (e >= E) return;
-    const float* src = partials + size_t(p) * G * E + e;
-    float4 acc = *reinterpret_cast<const float4*>(src);
-#pragma unroll 8
-    for (int g = 1; g < G; ++g) {
-        const float4 v = *reinterpret_cast<const float4*>(src + size_t(g) * E);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
-    }
-    uint16_t* base = memory + size_t(p) * E * 2;  // E floats of room per problem
-    if (e < Kp * DV) {
-        const uint32_t h01 = pack_bf16x2(acc.x, acc.y), h23 = pack_bf16x2(acc.z, acc.w);
-        const uint32_t l01 = pack_bf16x2(acc.x - __uint_as_float(h01 << 16), acc.y - __uint_as_float(h01 & 0xffff0000u));
-        const uint32_t l23 = pack_bf16x2(acc.z - __uint_as_float(h23 << 16), acc.w - __uint_as_float(h23 & 0xffff0000u));
-        *reinterpret_cast<u32x2*>(base + e) = u32x2{h01, h23};
-        *reinterpret_cast<u32x2*>(base + size_t(DV) * Kp + e) = u32x2{l01, l23};
-    } else {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(base + size_t(2) * DV * Kp) + (e - Kp * DV)) = acc;
+//
+// 16-byte groups [c0, c1) of one problem's memory: the G partials summed in increasing
+// order, VtT split into hi + lo bf16 planes, Z kept in fp32, all through device-coherent
+// accesses.  Kp * DV is a multiple of 4, so a group never straddles the VtT / Z boundary.
+// part: the problem's G partials of E floats; base: its memory (E floats of room).
+__device__ __forceinline__ void combine_range(const float* __restrict__ part, int G, int E, int Kp, int DV, int c0,
+                                              int c1, uint16_t* __restrict__ base, int stride) {
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(part, int64_t(G) * E * 4);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(base, int64_t(E) * 4);
+    for (int c = c0 + int(threadIdx.x); c < c1; c += stride) {
+        const int e = 4 * c;
+        u32x4 v = buf_load16_dev(rp, uint32_t(e * 4));
+        float4 acc = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
+        for (int g = 1; g < G; ++g) {
+            v = buf_load16_dev(rp, uint32_t((size_t(g) * E + e) * 4));
+            acc.x += __uint_as_float(v[0]);
+            acc.y += __uint_as_float(v[1]);
+            acc.z += __uint_as_float(v[2]);
+            acc.w += __uint_as_float(v[3]);
+        }
+        if (e < Kp * DV) {
+            const uint32_t h01 = pack_bf16x2(acc.x, acc.y), h23 = pack_bf16x2(acc.z, acc.w);
+            const uint32_t l01 = pack_bf16x2(acc.x - __uint_as_float(h01 << 16), acc.y - __uint_as_float(h01 & 0xffff0000u));
+            const uint32_t l23 = pack_bf16x2(acc.z - __uint_as_float(h23 << 16), acc.w - __uint_as_float(h23 & 0xffff0000u));
+            buf_store8_dev(rb, uint32_t(e * 2), u32x2{h01, h23});
+            buf_store8_dev(rb, uint32_t((Kp * DV + e) * 2), u32x2{l01, l23});
+        } else {
+            buf_store16_dev(rb, uint32_t(4 * Kp * DV + (e - Kp * DV) * 4),
+                            u32x4{__float_as_uint(acc.x), __float_as_uint(acc.y), __float_as_uint(acc.z),
+                                  __float_as_uint(acc.w)});
+        }
     }
 }
 
@@ -398,13 +142,39 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 // r (and, with a double-buffered x tile, the split of x tile r+2)  -> B1
 // Region B: round r-1's output scaled by 1 / den and stored; e of round r and its
 // denominator into LDS (single x buffer: x tile r+2 too)  -> B2
+// LDS of read_body, carved in this order out of one workgroup buffer.
 template <int DR, int KT, int VT>
-__global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const uint16_t* __restrict__ XQ, int64_t N,
-                                                                       int H, int64_t rows_per_block,
-                                                                       Mixture mx, const uint16_t* __restrict__ memory,
-                                                                       float eps,
-                                                                       uint16_t* __restrict__ O) {
+struct ReadLds {
     using S = Split<DR, KT>;
+    static constexpr int NT = S::NW * 64, Kp = KT * 32, DV = VT * 32, LDG = Kp + 8, LDM = Kp + 8;
+    using XT = XTile<DR, S::ROUND, NT>;
+    // VtT hi/lo staged in LDS when it fits; otherwise read from L2
+    static constexpr bool MS_LDS = (2 * DV * LDM + S::ROUND * LDG) * 2 + XT::LDS_BYTES <= 150 * 1024;
+    static constexpr int BASE = S::TS * S::CS * 32 * 12 + S::ROUND * LDG * 2 + (MS_LDS ? 2 * DV * LDM * 2 : 0) +
+                                2 * S::ROUND * 4;
+    static constexpr int XB = (BASE + 2 * XT::LDS_BYTES <= 80 * 1024) ? 2 : 1;  // keep two workgroups per CU
+    using st_t = Stats[S::CS > 1 ? S::TS * S::CS * 32 : 1];  // unused with one component group
+    using xt_t = u32x4[XB][XT::LDS_BYTES / 16];
+    using gs_t = uint16_t[S::ROUND * LDG];
+    using ms_t = uint16_t[MS_LDS ? 2 * DV * LDM : 8];
+    using dn_t = float[2][S::ROUND];
+    static constexpr size_t o_st = 0, o_xt = lds_align(o_st + sizeof(st_t)), o_gs = lds_align(o_xt + sizeof(xt_t)),
+                            o_ms = lds_align(o_gs + sizeof(gs_t)), o_dn = lds_align(o_ms + sizeof(ms_t)),
+                            bytes = lds_align(o_dn + sizeof(dn_t));
+};
+
+// Rows [lo, hi) of problem p (head h): O = Gamma_Q Vt / (Gamma_Q Z + eps) from the problem's
+// latent memory `mp` (VtT hi, VtT lo [DV][Kp] bf16, then Z [Kp] fp32; read device-coherent,
+// as another workgroup of the launch writes it).  BUILD as in
+// write_body.  wait() runs once the first x tiles are in flight and before `mp` is read
+// (a fused kernel waits there for the memory to be complete).
+template <int DR, int KT, int VT, bool BUILD, typename WaitF>
+__device__ __forceinline__ void read_body(char* __restrict__ smem, const uint16_t* __restrict__ XQ, int64_t N,
+                                          int64_t p, int h, int64_t lo, int64_t hi, const Mixture& mx,
+                                          WaveParams<DR, Split<DR, KT>::CTW>& P, const uint16_t* mp, float eps,
+                                          uint16_t* __restrict__ O, WaitF&& wait) {
+    using S = Split<DR, KT>;
+    using LY = ReadLds<DR, KT, VT>;
     constexpr int NW = S::NW, NT = NW * 64;
     constexpr int Kp = KT * 32, DV = VT * 32;
     constexpr int LDG = Kp + 8, LDM = Kp + 8;
@@ -412,47 +182,37 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
     constexpr int PW = (PAIRS + NW - 1) / NW;
     constexpr bool PEVEN = PAIRS % NW == 0;
     using XT = XTile<DR, S::ROUND, NT>;
-    // VtT hi/lo staged in LDS when it fits; otherwise read from L2
-    constexpr bool MS_LDS = (2 * DV * LDM + S::ROUND * LDG) * 2 + XT::LDS_BYTES <= 150 * 1024;
-    constexpr int BASE_LDS = S::TS * S::CS * 32 * 12 + S::ROUND * LDG * 2 + (MS_LDS ? 2 * DV * LDM * 2 : 0) +
-                             2 * S::ROUND * 4;
-    constexpr int XB = (BASE_LDS + 2 * XT::LDS_BYTES <= 80 * 1024) ? 2 : 1;  // keep two workgroups per CU
+    constexpr bool MS_LDS = LY::MS_LDS;
+    constexpr int XB = LY::XB;
     constexpr int MF_A = 5 * S::CTW * S::KS + PW * 2 * (Kp / 16);
-    __shared__ Stats st[S::TS * S::CS * 32];
-    __shared__ __attribute__((aligned(16))) u32x4 Xt[XB][XT::LDS_BYTES / 16];
-    __shared__ __attribute__((aligned(16))) uint16_t Gs[S::ROUND * LDG];
-    __shared__ __attribute__((aligned(16))) uint16_t Ms[MS_LDS ? 2 * DV * LDM : 8];
-    __shared__ float den_s[2][S::ROUND];
+    typename LY::st_t& st = *reinterpret_cast<typename LY::st_t*>(smem + LY::o_st);
+    typename LY::xt_t& Xt = *reinterpret_cast<typename LY::xt_t*>(smem + LY::o_xt);
+    typename LY::gs_t& Gs = *reinterpret_cast<typename LY::gs_t*>(smem + LY::o_gs);
+    typename LY::ms_t& Ms = *reinterpret_cast<typename LY::ms_t*>(smem + LY::o_ms);
+    typename LY::dn_t& den_s = *reinterpret_cast<typename LY::dn_t*>(smem + LY::o_dn);
 
     const int wave = wave_id(), l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
     const int cs = wave % S::CS, ts = wave / S::CS;
-    const int64_t p = blockIdx.y;
-    const int h = int(p % H);
-    const int64_t lo = int64_t(blockIdx.x) * rows_per_block, hi = min<int64_t>(lo + rows_per_block, N);
     const int64_t rows = hi - lo;
     const int64_t R = (rows + S::ROUND - 1) / S::ROUND;
     using MS = MixtureStage<DR, Kp, NT>;
     constexpr bool STAGE = sizeof(Xt) >= MS::LDS_BYTES;
-    WaveParams<DR, S::CTW> P;
     typename WaveParams<DR, S::CTW>::Raw praw;
     MS mstage;
-    if constexpr (STAGE) {
-        mstage.load(mx, h);
-        P.fetch_pi(mx, h, cs * S::CTW, praw);
-    } else {
-        P.fetch(mx, h, cs * S::CTW, praw);
+    if constexpr (BUILD) {
+        if constexpr (STAGE) {
+            mstage.load(mx, h);
+            P.fetch_pi(mx, h, cs * S::CTW, praw);
+        } else {
+            P.fetch(mx, h, cs * S::CTW, praw);
+        }
     }
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(XQ + (size_t(p) * N + lo) * DR, rows * DR * 2);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + (size_t(p) * N + lo) * DV, rows * DV * 2);
-    // latent memory of this problem: Z -> registers in score-row order (loaded before the
-    // x tiles, so their wait covers it), VtT hi/lo -> LDS
-    const uint16_t* mp = memory + size_t(p) * Kp * (DV + 1) * 2;
-    const float* Zp = reinterpret_cast<const float*>(mp + size_t(2) * DV * Kp);
+    // latent memory of this problem (read after wait()): Z -> registers in score-row order,
+    // VtT hi/lo -> LDS
+    const __amdgpu_buffer_rsrc_t rmp = make_rsrc(mp, int64_t(Kp) * (DV + 1) * 4);
     float zr[S::CTW][16];
-#pragma unroll
-    for (int ct = 0; ct < S::CTW; ++ct)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) zr[ct][r] = Zp[(cs * S::CTW + ct) * 32 + 8 * (r >> 2) + 4 * lh + (r & 3)];
     const uint16_t* Msrc = MS_LDS ? Ms : mp;
     constexpr int LDMS = MS_LDS ? LDM : Kp;
 
@@ -462,21 +222,43 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
         XT xt1;
         xt.load(rx, 0);
         xt1.load(rx, S::ROUND);
-        if constexpr (STAGE) {  // while the tiles are in flight
+        wait();
+#pragma unroll
+        for (int ct = 0; ct < S::CTW; ++ct)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4 zv = buf_load16_dev(rmp, uint32_t(4 * Kp * DV + ((cs * S::CTW + ct) * 32 + 8 * q + 4 * lh) * 4));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) zr[ct][4 * q + i] = __uint_as_float(zv[i]);
+            }
+        // VtT hi/lo: all loads in flight before the first LDS store
+        constexpr int MCH = 2 * DV * Kp / 8, MPER = (MCH + NT - 1) / NT;
+        u32x4 mv[MS_LDS ? MPER : 1];
+        if constexpr (MS_LDS) {
+#pragma unroll
+            for (int u = 0; u < MPER; ++u) {
+                const int c = threadIdx.x + u * NT;
+                const int row = c / (Kp / 8), col = (c - row * (Kp / 8)) * 8;
+                if (MCH % NT == 0 || c < MCH) mv[u] = buf_load16_dev(rmp, uint32_t((row * Kp + col) * 2));
+            }
+        }
+        if constexpr (BUILD && STAGE) {  // while the tiles are in flight
             mstage.commit(reinterpret_cast<float*>(&Xt[0][0]));
             __syncthreads();
             P.template read_staged<Kp>(reinterpret_cast<const float*>(&Xt[0][0]), cs * S::CTW, praw);
             P.build(praw, mx.K, cs * S::CTW);
             __syncthreads();  // staging area free for the x tiles
-        } else {
+        } else if constexpr (BUILD) {
             P.build(praw, mx.K, cs * S::CTW);
         }
-        if (MS_LDS)
-            for (int c = threadIdx.x; c < 2 * DV * Kp / 8; c += NT) {
+        if constexpr (MS_LDS) {
+#pragma unroll
+            for (int u = 0; u < MPER; ++u) {
+                const int c = threadIdx.x + u * NT;
                 const int row = c / (Kp / 8), col = (c - row * (Kp / 8)) * 8;
-                *reinterpret_cast<u32x4*>(Ms + row * LDM + col) =
-                    *reinterpret_cast<const u32x4*>(mp + size_t(row) * Kp + col);
+                if (MCH % NT == 0 || c < MCH) *reinterpret_cast<u32x4*>(Ms + row * LDM + col) = mv[u];
             }
+        }
         xt.commit(Xt[0]);
         xt.load(rx, 2 * S::ROUND);
         if (XB == 2) xt1.commit(Xt[XB - 1]);
@@ -584,6 +366,51 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) read_kernel(const ui
     out_store(R - 1);
 }
 
+// ---------------------------------------------------------------------------- bidirectional forward
+
+// One launch for the whole bidirectional forward.  Grid (G, P); workgroup (g, p) owns rows
+// [g seg, (g + 1) seg) of problem p:
+//   1. write: the partial [Vt^T | Z] of its rows (write_body, operand planes built once);
+//   2. after all G partials of p are published: combine 1/G of p's memory (fixed order);
+//   3. after all G slices are published: read its rows (read_body, same planes, the first
+//      x tiles already in flight while it waits).
+// flags: [P][2][G] words (partials ready, memory slice ready), compared with `token`.  A
+// workgroup whose wait times out writes NaN over its output rows.
+template <int DR, int KT, int VT>
+__global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
+__attribute__((amdgpu_waves_per_eu(waves_for_lds(WriteLds<DR, KT, VT>::bytes > ReadLds<DR, KT, VT>::bytes
+                                                      ? WriteLds<DR, KT, VT>::bytes
+                                                      : ReadLds<DR, KT, VT>::bytes))))
+    bidir_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
+                 int64_t N, int H, int64_t seg, int G, Mixture mx, float* __restrict__ partials,
+                 uint16_t* __restrict__ memory, uint64_t* __restrict__ flags, uint64_t token, float eps,
+                 uint16_t* __restrict__ O) {
+    using WL = WriteLds<DR, KT, VT>;
+    using RL = ReadLds<DR, KT, VT>;
+    __shared__ __attribute__((aligned(16))) char smem[WL::bytes > RL::bytes ? WL::bytes : RL::bytes];
+    constexpr int Kp = KT * 32, DV = VT * 32, E = Kp * (DV + 1), NT = Split<DR, KT>::NW * 64;
+    const int64_t p = blockIdx.y;
+    const int g = blockIdx.x, h = int(p % H);
+    const int64_t lo = int64_t(g) * seg, hi = min<int64_t>(lo + seg, N);
+    float* part = partials + size_t(p) * G * E;
+    uint16_t* mem = memory + size_t(p) * E * 2;
+    uint64_t* fl = flags + size_t(p) * 2 * G;
+
+    WaveParams<DR, Split<DR, KT>::CTW> P;
+    write_body<DR, KT, VT, true>(smem, XK, V, N, p, h, lo, hi, mx, P, part + size_t(g) * E);
+    publish_token(fl + g, token);
+    bool ok = wait_tokens(fl, G, token);
+    const int per = (E / 4 + G - 1) / G;  // 16-byte groups per slice
+    combine_range(part, G, E, Kp, DV, min(g * per, E / 4), min((g + 1) * per, E / 4), mem, NT);
+    publish_token(fl + G + g, token);  // its barrier also frees the write phase's LDS
+    read_body<DR, KT, VT, false>(smem, XQ, N, p, h, lo, hi, mx, P, mem, eps, O,
+                                 [&] { ok = wait_tokens(fl + G, G, token) && ok; });
+    if (!ok) {  // the memory was never complete: make that visible in the output
+        uint16_t* op = O + (size_t(p) * N + lo) * DV;
+        for (int64_t e = threadIdx.x; e < (hi - lo) * DV; e += NT) op[e] = 0x7fc0u;
+    }
+}
+
 // ---------------------------------------------------------------------------- dispatch
 
 template <typename F>
@@ -612,15 +439,6 @@ namespace {
 int kt_of(const Plan& p) { return int(p.Kp / 32); }
 
 }  // namespace
-
-int64_t bf16_round_tokens(int dr, int64_t Kp) {
-    int64_t out = 0;
-    (void)bf::with_dr_kt(dr, int(Kp / 32), [&](auto D, auto T) {
-        out = bf::Split<decltype(D)::value, decltype(T)::value>::ROUND;
-        return hipSuccess;
-    });
-    return out;
-}
 
 hipError_t bf16_responsibilities(const Plan& p, const void* X, const float* mu, const float* s2, const float* pi,
                                  void* Gamma, gma_dtype_t gamma_dtype, char* ws, hipStream_t st) {
@@ -656,23 +474,19 @@ hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, con
 hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu, const float* s2,
                       const float* pi, float eps, void* O, char* ws, hipStream_t st) {
     const bf::Mixture mx{mu, s2, pi, int(p.K)};
-    hipError_t e = bf16_write_partials(p, XK, V, mx, ws, st, p.G);
-    if (e != hipSuccess) return e;
     float* partials = reinterpret_cast<float*>(ws + p.off_partials);
     uint16_t* memory = reinterpret_cast<uint16_t*>(ws + p.off_memory);
-    const int E = int(p.Kp * (p.dv + 1));
-    GMA_LAUNCH("bf16_combine", bf::combine_kernel, dim3(unsigned((E / 4 + 255) / 256), unsigned(p.P)), dim3(256), 0, st, partials,
-                       int(p.G), int(p.Kp), int(p.dv), memory);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    uint64_t* flags = reinterpret_cast<uint64_t*>(ws + p.off_flags);
+    const uint64_t token = launch_token();
     return bf::with_dr_kt(int(p.dr), kt_of(p), [&](auto D, auto T) {
         constexpr int DR = decltype(D)::value, KT = decltype(T)::value;
         return bf::with_vt(int(p.dv / 32), [&](auto VV) {
             constexpr int VT = decltype(VV)::value;
             using S = bf::Split<DR, KT>;
-            dim3 grid(unsigned((p.N + p.read_rows - 1) / p.read_rows), unsigned(p.P));
-            GMA_LAUNCH("bf16_read", (bf::read_kernel<DR, KT, VT>), grid, dim3(S::NW * 64), 0, st,
-                               static_cast<const uint16_t*>(XQ), p.N, int(p.H), p.read_rows, mx, memory,
-                               eps, static_cast<uint16_t*>(O));
+            GMA_LAUNCH("bf16_bidir", (bf::bidir_kernel<DR, KT, VT>), dim3(unsigned(p.G), unsigned(p.P)),
+                       dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
+                       static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), mx, partials, memory, flags,
+                       token, eps, static_cast<uint16_t*>(O));
             return hipGetLastError();
         });
     });

@@ -101,6 +101,23 @@ __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t of
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v), r, off, 0, 0);
 }
 
+// Device-coherent accesses (cache policy SC1) for data that another workgroup of the same
+// launch wrote or reads: they are performed at the coherence point every XCD shares, so no
+// cache-wide write-back or invalidate is needed around the hand-off.  Full 16-byte lanes
+// of a coalesced wave keep these at whole-line granularity.
+constexpr int kCoherent = 16;
+__device__ __forceinline__ u32x4 buf_load16_dev(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
+}
+__device__ __forceinline__ void buf_store16_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), r, off, 0,
+                                           kCoherent);
+}
+__device__ __forceinline__ void buf_store8_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v), r, off, 0,
+                                          kCoherent);
+}
+
 // ---- a tile of ROUND routing vectors, split once into the score MFMA's B fragments
 // (x, x^2 hi, x^2 lo) and shared through LDS by every wave that needs it.
 // Global loads are fully coalesced: thread t fetches 16-byte chunk t (+ NTHREADS, ...) of
@@ -250,6 +267,42 @@ struct Split {
     static constexpr int ROUND = 32 * TS;       // tokens per round
     static constexpr int KS = DR / 16;          // k-steps of the d contraction
 };
+
+constexpr size_t lds_align(size_t x) { return (x + 15) & ~size_t(15); }
+
+// Waves per SIMD a 4-wave workgroup of `lds` bytes can keep resident (160 KiB of LDS per
+// CU): kernels declare it so the register allocator keeps within that occupancy.
+constexpr int waves_for_lds(size_t lds) { return lds <= 80 * 1024 ? 2 : 1; }
+
+// ---- hand-off between workgroups of one launch
+// Data handed to another workgroup is written and read with the device-coherent accesses
+// above.  A workgroup publishes a 64-bit word once every such store of all its waves has
+// completed; waiters poll until each word they need holds the launch's token, a per-call
+// random value, so stale words from earlier calls never match.  Waiters only depend on
+// workgroups dispatched no later than themselves or alongside them, and the poll is
+// bounded: on time-out the waiter reports failure instead of hanging.
+constexpr uint32_t kSpinLimit = 1u << 18;
+
+__device__ __forceinline__ void publish_token(uint64_t* flag, uint64_t token) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
+    __syncthreads();                // ... and those of every wave of the workgroup
+    if (threadIdx.x == 0) __hip_atomic_store(flag, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every wave polls flags[0 .. n) itself (no LDS, no barrier); true when all hold `token`.
+__device__ __forceinline__ bool wait_tokens(const uint64_t* flags, int n, uint64_t token) {
+    const int l = threadIdx.x & 63;
+    bool done = false;
+    for (uint32_t it = 0; it < kSpinLimit; ++it) {
+        bool mine = true;
+        for (int i = l; i < n; i += 64)
+            mine = mine && (__hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == token);
+        done = __all(mine);
+        if (done) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    return done;
+}
 
 // Mixture parameters of every head: mu, s2 [H][K][d_r] fp32 row-major, pi [H][K] fp32.
 struct Mixture {

@@ -27,11 +27,14 @@ struct Plan {
     int64_t G;            // sequence splits per problem (write partials / causal segments)
     int64_t seg;          // tokens per split (multiple of the token tile)
     int32_t chunk;        // causal chunk length
-    int64_t read_rows;    // tokens per workgroup of the bf16 read kernel
     // byte offsets into the workspace
-    size_t off_params, off_partials, off_memory, total;
-    size_t params_bytes, partials_bytes, memory_bytes;
+    size_t off_params, off_partials, off_memory, off_flags, total;
+    size_t params_bytes, partials_bytes, memory_bytes, flags_bytes;
 };
+
+// A fresh 64-bit value per launch that hands data between workgroups (bf16 fused kernels):
+// flag words left in a workspace by earlier calls never equal it.
+uint64_t launch_token();
 
 // Kernel timing hooks (see gma_profiling in gma.h).  Launchers bracket each launch with
 // trace_begin / trace_end; both are no-ops unless profiling is enabled.
@@ -71,7 +74,6 @@ hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void
                        const float* mu, const float* s2, const float* pi, float eps, void* O,
                        char* ws, hipStream_t st);
 // tokens one bf16 workgroup processes per round for (d_r, padded K); 0 if unsupported
-int64_t bf16_round_tokens(int dr, int64_t Kp);
 // causal chunked scan of every segment; segment s starts from the sum of the aggregates
 // of segments 0 .. s-1 in the workspace partials (gma_bf16_scan.hip)
 hipError_t bf16_scan(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu,
