@@ -455,8 +455,9 @@ hipError_t bf16_responsibilities(const Plan& p, const void* X, const float* mu, 
     });
 }
 
-hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, const bf::Mixture& mx, char* ws,
-                               hipStream_t st, int64_t splits) {
+hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, const float* mu, const float* s2,
+                               const float* pi, char* ws, hipStream_t st, int64_t splits) {
+    const bf::Mixture mx{mu, s2, pi, int(p.K)};
     float* partials = reinterpret_cast<float*>(ws + p.off_partials);
     return bf::with_dr_kt(int(p.dr), kt_of(p), [&](auto D, auto T) {
         constexpr int DR = decltype(D)::value, KT = decltype(T)::value;
@@ -490,16 +491,6 @@ hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void*
             return hipGetLastError();
         });
     });
-}
-
-hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu, const float* s2,
-                       const float* pi, float eps, void* O, char* ws, hipStream_t st) {
-    const bf::Mixture mx{mu, s2, pi, int(p.K)};
-    hipError_t e = hipSuccess;
-    // aggregates of segments 0 .. G-2 (the last segment's aggregate is never read); the
-    // scan workgroup of segment s sums aggregates 0 .. s-1 itself
-    if (p.G > 1 && (e = bf16_write_partials(p, XK, V, mx, ws, st, p.G - 1)) != hipSuccess) return e;
-    return bf16_scan(p, XQ, XK, V, mu, s2, pi, eps, O, ws, st);
 }
 
 }  // namespace gma

@@ -27,6 +27,7 @@
 #include <type_traits>
 
 #include "gma_bf16_common.h"
+#include "gma_bf16_phases.h"
 #include "gma_internal.h"
 
 namespace gma {
@@ -61,7 +62,7 @@ constexpr int scan_jpw() {  // 32-position score jobs per wave and chunk (query 
     return (2 * (CH / 32) + Split<DR, KT>::TS - 1) / Split<DR, KT>::TS;
 }
 
-// LDS bytes of scan_kernel for a chunk of CH positions (mirrors the declarations below).
+// LDS bytes of scan_body for a chunk of CH positions (the ScanLds arrays, unaligned).
 template <int DR, int KT, int VT, int CH>
 constexpr int scan_lds_bytes() {
     using S = Split<DR, KT>;
@@ -82,12 +83,40 @@ constexpr int scan_chunk() {
                : CH_REQ;
 }
 
-template <int DR, int KT, int VT, int CH_REQ>
-__global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
-    scan_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
-                int64_t N, int H, int64_t seg, int G, Mixture mx,
-                const float* __restrict__ prefix, float eps, uint16_t* __restrict__ O) {
+// LDS of scan_body, carved in this order out of one workgroup buffer.
+template <int DR, int KT, int VT, int CH>
+struct ScanLds {
+    using S = Split<DR, KT>;
+    static constexpr int NT = S::NW * 64, Kp = KT * 32, DV = VT * 32, LDG = Kp + 8, LDV = DV + 8, LDSS = CH + 8;
+    static constexpr int SUB = CH / 32, JPW = scan_jpw<DR, KT, CH>(), NPARTS = NT / CH;
+    using XT = typename std::conditional<(S::CS > 1), XTile<DR, CH, NT>, RawTile<DR, CH, NT>>::type;
+    using st_t = ScanStats[JPW][S::TS * S::CS * 32];
+    using g_t = uint16_t[2][CH * LDG];
+    using v_t = uint16_t[2][CH * LDV];
+    using s_t = uint16_t[CH * LDSS];
+    using x_t = u32x4[XT::LDS_BYTES / 16];
+    using di_t = float[NPARTS][CH];
+    using dp_t = float[SUB][CH];
+    using z_t = float[Kp];
+    static constexpr size_t o_st = 0, o_gq = lds_align(o_st + sizeof(st_t)), o_gk = lds_align(o_gq + sizeof(g_t)),
+                            o_vs = lds_align(o_gk + sizeof(g_t)), o_ss = lds_align(o_vs + sizeof(v_t)),
+                            o_xq = lds_align(o_ss + sizeof(s_t)), o_xk = lds_align(o_xq + sizeof(x_t)),
+                            o_di = lds_align(o_xk + sizeof(x_t)), o_dp = lds_align(o_di + sizeof(di_t)),
+                            o_zs = lds_align(o_dp + sizeof(dp_t)), bytes = lds_align(o_zs + sizeof(z_t));
+};
+
+// Positions [lo, hi) (segment seg_idx) of problem p (head h).  The segment starts from the
+// sum of the aggregates 0 .. seg_idx-1 in `agg` (the problem's aggregates, E floats each,
+// read device-coherent); wait() runs once the first tiles are in flight and before they
+// are read.  BUILD as in write_body.  smem: ScanLds<DR, KT, VT, CH>::bytes of LDS.
+template <int DR, int KT, int VT, int CH_REQ, bool BUILD, typename WaitF>
+__device__ __forceinline__ void scan_body(char* __restrict__ smem, const uint16_t* __restrict__ XQ,
+                                          const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V, int64_t N,
+                                          int64_t p, int h, int seg_idx, int64_t lo, int64_t hi, const Mixture& mx,
+                                          WaveParams<DR, Split<DR, KT>::CTW>& P, const float* __restrict__ agg,
+                                          float eps, uint16_t* __restrict__ O, WaitF&& wait) {
     constexpr int CH = scan_chunk<DR, KT, VT, CH_REQ>();
+    using LY = ScanLds<DR, KT, VT, CH>;
     using S = Split<DR, KT>;
     constexpr int NW = S::NW, NT = NW * 64;
     constexpr int Kp = KT * 32, DV = VT * 32;
@@ -110,38 +139,36 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
     constexpr bool SHARE_X = CS > 1;
     using XT = typename std::conditional<SHARE_X, XTile<DR, CH, NT>, RawTile<DR, CH, NT>>::type;
 
-    __shared__ ScanStats st[JPW][TS * CS * 32];
-    __shared__ __attribute__((aligned(16))) uint16_t Gq[2][CH * LDG];
-    __shared__ __attribute__((aligned(16))) uint16_t Gk[2][CH * LDG];
-    __shared__ __attribute__((aligned(16))) uint16_t Vs[2][CH * LDV];
-    __shared__ __attribute__((aligned(16))) uint16_t Ss[CH * LDSS];
-    __shared__ __attribute__((aligned(16))) u32x4 XtQ[XT::LDS_BYTES / 16];
-    __shared__ __attribute__((aligned(16))) u32x4 XtK[XT::LDS_BYTES / 16];
-    __shared__ float den_ip[NPARTS][CH];
-    __shared__ float den_part[SUB][CH];
-    __shared__ __attribute__((aligned(16))) float Zs[Kp];
+    static_assert(std::is_same<XT, typename LY::XT>::value && NPARTS == LY::NPARTS && JPW == LY::JPW, "layout mismatch");
+    typename LY::st_t& st = *reinterpret_cast<typename LY::st_t*>(smem + LY::o_st);
+    typename LY::g_t& Gq = *reinterpret_cast<typename LY::g_t*>(smem + LY::o_gq);
+    typename LY::g_t& Gk = *reinterpret_cast<typename LY::g_t*>(smem + LY::o_gk);
+    typename LY::v_t& Vs = *reinterpret_cast<typename LY::v_t*>(smem + LY::o_vs);
+    typename LY::s_t& Ss = *reinterpret_cast<typename LY::s_t*>(smem + LY::o_ss);
+    typename LY::x_t& XtQ = *reinterpret_cast<typename LY::x_t*>(smem + LY::o_xq);
+    typename LY::x_t& XtK = *reinterpret_cast<typename LY::x_t*>(smem + LY::o_xk);
+    typename LY::di_t& den_ip = *reinterpret_cast<typename LY::di_t*>(smem + LY::o_di);
+    typename LY::dp_t& den_part = *reinterpret_cast<typename LY::dp_t*>(smem + LY::o_dp);
+    typename LY::z_t& Zs = *reinterpret_cast<typename LY::z_t*>(smem + LY::o_zs);
 
     const int wave = wave_id(), l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
     const int g4 = l >> 4, i16 = l & 15;
     const int cs = wave % CS, ts = wave / CS;
-    const int64_t p = blockIdx.y;
-    const int seg_idx = blockIdx.x;
-    const int h = int(p % H);
-    const int64_t lo = int64_t(seg_idx) * seg, hi = min<int64_t>(lo + seg, N);
     const int64_t rows = hi - lo;
     const int64_t C = (rows + CH - 1) / CH;  // chunks of this segment
 
     // mixture parameters staged through the V tile buffers when they are large enough
     using MS = MixtureStage<DR, Kp, NT>;
     constexpr bool STAGE = sizeof(Vs) >= MS::LDS_BYTES;
-    WaveParams<DR, CTW> P;
     typename WaveParams<DR, CTW>::Raw praw;
     MS mstage;
-    if constexpr (STAGE) {
-        mstage.load(mx, h);
-        P.fetch_pi(mx, h, cs * CTW, praw);
-    } else {
-        P.fetch(mx, h, cs * CTW, praw);
+    if constexpr (BUILD) {
+        if constexpr (STAGE) {
+            mstage.load(mx, h);
+            P.fetch_pi(mx, h, cs * CTW, praw);
+        } else {
+            P.fetch(mx, h, cs * CTW, praw);
+        }
     }
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(XQ + (size_t(p) * N + lo) * DR, rows * DR * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(XK + (size_t(p) * N + lo) * DR, rows * DR * 2);
@@ -232,7 +259,7 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
     // ---- starting memory of the segment: the sum of the aggregates of segments
     // 0 .. seg_idx-1 (each stored as VtT [DV][Kp] then Z [Kp]), in increasing segment order
     const size_t E = size_t(Kp) * (DV + 1);
-    const float* agg = prefix + size_t(p) * G * E;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(agg, int64_t(seg_idx) * int64_t(E) * 4);
     f32x4 mem[CPW][KT16];
 #pragma unroll
     for (int cc = 0; cc < CPW; ++cc)
@@ -244,33 +271,36 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
     load_v(0);
     xq.load(rq, 0);
     xk.load(rk, 0);
-    if constexpr (STAGE) {
+    if constexpr (BUILD && STAGE) {
         mstage.commit(reinterpret_cast<float*>(&Vs[0][0]));
         __syncthreads();
         P.template read_staged<Kp>(reinterpret_cast<const float*>(&Vs[0][0]), cs * CTW, praw);
         P.build(praw, mx.K, cs * CTW);
         __syncthreads();  // staging area free for the V tiles
-    } else {
+    } else if constexpr (BUILD) {
         P.build(praw, mx.K, cs * CTW);
     }
+    wait();
 #pragma unroll 2
     for (int gs = 0; gs < seg_idx; ++gs) {
-        const float* a = agg + size_t(gs) * E;
+        const uint32_t a = uint32_t(size_t(gs) * E * 4);
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc) {
             const int c16 = wave + cc * NW;
             if (c16 < C16) {
 #pragma unroll
                 for (int kt = 0; kt < KT16; ++kt) {
-                    const float4 v = *reinterpret_cast<const float4*>(a + size_t(c16 * 16 + i16) * Kp + kt * 16 + 4 * g4);
-                    mem[cc][kt][0] += v.x;
-                    mem[cc][kt][1] += v.y;
-                    mem[cc][kt][2] += v.z;
-                    mem[cc][kt][3] += v.w;
+                    const u32x4 v = buf_load16_dev(ra, a + uint32_t(((c16 * 16 + i16) * Kp + kt * 16 + 4 * g4) * 4));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mem[cc][kt][r] += __uint_as_float(v[r]);
                 }
             }
         }
-        for (int k = threadIdx.x; k < Kp; k += NT) Zs[k] += a[size_t(Kp) * DV + k];
+        for (int k = threadIdx.x * 4; k < Kp; k += NT * 4) {
+            const u32x4 v = buf_load16_dev(ra, a + uint32_t((Kp * DV + k) * 4));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Zs[k + r] += __uint_as_float(v[r]);
+        }
     }
     commit_v(Vs[0]);
     load_v(CH);
@@ -453,6 +483,50 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
         chunk(c + 1, 1, acc_b, acc_a);
     }
     if (c < C) chunk(c, 0, acc_a, acc_b);
+}
+
+// ---- the causal forward in one launch (shapes of the pipelined scan).  Grid (G, P);
+// workgroup (s, p) owns segment s of problem p.  Segments 0 .. G-2 first write their
+// aggregate (write_body over the segment) and publish it; every segment then waits for the
+// aggregates of the segments before it (only earlier-dispatched workgroups), sums them in
+// increasing order and scans.  The last segment's aggregate is never needed, so its
+// workgroup builds its operand planes and goes straight to the wait.  flags: [P][G] words
+// compared with `token`; a workgroup whose wait times out writes NaN over its positions.
+template <int DR, int KT, int VT, int CH_REQ>
+constexpr size_t causal_lds_bytes() {
+    constexpr size_t w = WriteLds<DR, KT, VT>::bytes;
+    constexpr size_t sc = ScanLds<DR, KT, VT, scan_chunk<DR, KT, VT, CH_REQ>()>::bytes;
+    return w > sc ? w : sc;
+}
+
+template <int DR, int KT, int VT, int CH_REQ>
+__global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
+__attribute__((amdgpu_waves_per_eu(waves_for_lds(causal_lds_bytes<DR, KT, VT, CH_REQ>()))))
+    causal_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
+                  int64_t N, int H, int64_t seg, int G, Mixture mx, float* __restrict__ aggregates,
+                  uint64_t* __restrict__ flags, uint64_t token, float eps, uint16_t* __restrict__ O) {
+    __shared__ __attribute__((aligned(16))) char smem[causal_lds_bytes<DR, KT, VT, CH_REQ>()];
+    using S = Split<DR, KT>;
+    constexpr int Kp = KT * 32, DV = VT * 32, E = Kp * (DV + 1), NT = S::NW * 64;
+    const int64_t p = blockIdx.y;
+    const int s = blockIdx.x, h = int(p % H);
+    const int64_t lo = int64_t(s) * seg, hi = min<int64_t>(lo + seg, N);
+    float* agg = aggregates + size_t(p) * G * E;
+    uint64_t* fl = flags + size_t(p) * G;
+    WaveParams<DR, S::CTW> P;
+    if (s + 1 < G) {
+        write_body<DR, KT, VT, true>(smem, XK, V, N, p, h, lo, hi, mx, P, agg + size_t(s) * E);
+        publish_token(fl + s, token);  // its barrier also frees the write phase's LDS
+    } else {
+        P.compute(mx, h, (wave_id() % S::CS) * S::CTW);
+    }
+    bool ok = true;
+    scan_body<DR, KT, VT, CH_REQ, false>(smem, XQ, XK, V, N, p, h, s, lo, hi, mx, P, agg, eps, O,
+                                         [&] { ok = wait_tokens(fl, s, token); });
+    if (!ok) {  // the starting memory was never complete: make that visible in the output
+        uint16_t* op = O + (size_t(p) * N + lo) * DV;
+        for (int64_t e = threadIdx.x; e < (hi - lo) * DV; e += NT) op[e] = 0x7fc0u;
+    }
 }
 
 // ---- serial variant: one chunk after another (four barriers per chunk), for the shapes
@@ -839,27 +913,34 @@ hipError_t with_all(int dr, int kt, int vt, int ch, F&& f) {
 }  // namespace bf
 
 // The bf16 scan works on 32-position score subtiles, so a requested chunk of 16
-// positions runs as 32 (the chunk length only changes the order of the sums).
-hipError_t bf16_scan(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu,
-                     const float* s2, const float* pi, float eps, void* O, char* ws, hipStream_t st) {
+// positions runs as 32 (the chunk length only changes the order of the sums).  Shapes
+// whose registers fit the pipelined scan run the fused causal kernel; the others run the
+// segment aggregates (write kernel) and then the serial scan.
+hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu, const float* s2,
+                       const float* pi, float eps, void* O, char* ws, hipStream_t st) {
     const bf::Mixture mx{mu, s2, pi, int(p.K)};
-    const float* prefix = reinterpret_cast<const float*>(ws + p.off_partials);
+    float* aggregates = reinterpret_cast<float*>(ws + p.off_partials);
+    uint64_t* flags = reinterpret_cast<uint64_t*>(ws + p.off_flags);
     const int ch = p.chunk < 32 ? 32 : p.chunk;
     return bf::with_all(int(p.dr), int(p.Kp / 32), int(p.dv / 32), ch, [&](auto D, auto T, auto W, auto C) {
         constexpr int DR = decltype(D)::value, KT = decltype(T)::value, VT = decltype(W)::value,
                       CH = decltype(C)::value;
         using S = bf::Split<DR, KT>;
-        // pipelined scan where its registers suffice (up to 4 component tiles and d_r * K <= 8192),
-        // the serial one otherwise
+        // pipelined scan where its registers suffice (up to 4 component tiles and d_r * K <= 8192)
         if constexpr (KT <= 4 && DR * KT <= 256) {
-            GMA_LAUNCH("bf16_scan", (bf::scan_kernel<DR, KT, VT, CH>), dim3(unsigned(p.G), unsigned(p.P)),
+            GMA_LAUNCH("bf16_causal", (bf::causal_kernel<DR, KT, VT, CH>), dim3(unsigned(p.G), unsigned(p.P)),
                        dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
-                       static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), mx, prefix, eps,
-                       static_cast<uint16_t*>(O));
+                       static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), mx, aggregates, flags,
+                       launch_token(), eps, static_cast<uint16_t*>(O));
         } else {
+            // aggregates of segments 0 .. G-2 (the last segment's aggregate is never read)
+            if (p.G > 1) {
+                hipError_t e = bf16_write_partials(p, XK, V, mu, s2, pi, ws, st, p.G - 1);
+                if (e != hipSuccess) return e;
+            }
             GMA_LAUNCH("bf16_scan", (bf::serial_scan_kernel<DR, KT, VT, CH>), dim3(unsigned(p.G), unsigned(p.P)),
                        dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
-                       static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), mx, prefix, eps,
+                       static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), mx, aggregates, eps,
                        static_cast<uint16_t*>(O));
         }
         return hipGetLastError();

@@ -73,10 +73,9 @@ hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void*
 hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void* V,
                        const float* mu, const float* s2, const float* pi, float eps, void* O,
                        char* ws, hipStream_t st);
-// tokens one bf16 workgroup processes per round for (d_r, padded K); 0 if unsupported
-// causal chunked scan of every segment; segment s starts from the sum of the aggregates
-// of segments 0 .. s-1 in the workspace partials (gma_bf16_scan.hip)
-hipError_t bf16_scan(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu,
-                     const float* s2, const float* pi, float eps, void* O, char* ws, hipStream_t st);
+// Segment aggregates (the first `splits` segments) into the partials region: the first
+// launch of the causal path for shapes the fused causal kernel does not take.
+hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, const float* mu, const float* s2,
+                               const float* pi, char* ws, hipStream_t st, int64_t splits);
 
 }  // namespace gma
