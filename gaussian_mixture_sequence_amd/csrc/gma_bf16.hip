@@ -105,16 +105,24 @@ __device__ __forceinline__ void combine_range(const float* __restrict__ part, in
                                               int c1, uint16_t* __restrict__ base, int stride) {
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(part, int64_t(G) * E * 4);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(base, int64_t(E) * 4);
+    constexpr int GB = 8;  // partials loaded together (one memory round trip per batch)
     for (int c = c0 + int(threadIdx.x); c < c1; c += stride) {
         const int e = 4 * c;
-        u32x4 v = buf_load16_dev(rp, uint32_t(e * 4));
-        float4 acc = make_float4(__uint_as_float(v[0]), __uint_as_float(v[1]), __uint_as_float(v[2]), __uint_as_float(v[3]));
-        for (int g = 1; g < G; ++g) {
-            v = buf_load16_dev(rp, uint32_t((size_t(g) * E + e) * 4));
-            acc.x += __uint_as_float(v[0]);
-            acc.y += __uint_as_float(v[1]);
-            acc.z += __uint_as_float(v[2]);
-            acc.w += __uint_as_float(v[3]);
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int g0 = 0; g0 < G; g0 += GB) {
+            u32x4 v[GB];
+#pragma unroll
+            for (int u = 0; u < GB; ++u)  // past the last partial: a repeat of it, not added
+                v[u] = buf_load16_dev(rp, uint32_t((size_t(min(g0 + u, G - 1)) * E + e) * 4));
+#pragma unroll
+            for (int u = 0; u < GB; ++u) {
+                if (g0 + u < G) {
+                    acc.x = g0 + u == 0 ? __uint_as_float(v[u][0]) : acc.x + __uint_as_float(v[u][0]);
+                    acc.y = g0 + u == 0 ? __uint_as_float(v[u][1]) : acc.y + __uint_as_float(v[u][1]);
+                    acc.z = g0 + u == 0 ? __uint_as_float(v[u][2]) : acc.z + __uint_as_float(v[u][2]);
+                    acc.w = g0 + u == 0 ? __uint_as_float(v[u][3]) : acc.w + __uint_as_float(v[u][3]);
+                }
+            }
         }
         if (e < Kp * DV) {
             const uint32_t h01 = pack_bf16x2(acc.x, acc.y), h23 = pack_bf16x2(acc.z, acc.w);
@@ -165,9 +173,9 @@ struct ReadLds {
 
 // Rows [lo, hi) of problem p (head h): O = Gamma_Q Vt / (Gamma_Q Z + eps) from the problem's
 // latent memory `mp` (VtT hi, VtT lo [DV][Kp] bf16, then Z [Kp] fp32; read device-coherent,
-// as another workgroup of the launch writes it).  BUILD as in
-// write_body.  wait() runs once the first x tiles are in flight and before `mp` is read
-// (a fused kernel waits there for the memory to be complete).
+// as another workgroup of the launch writes it).  BUILD as in write_body.  wait() runs
+// after the first x tiles are committed and round 0's scores issued, before `mp` is read:
+// a fused kernel completes the memory there, behind that work.
 template <int DR, int KT, int VT, bool BUILD, typename WaitF>
 __device__ __forceinline__ void read_body(char* __restrict__ smem, const uint16_t* __restrict__ XQ, int64_t N,
                                           int64_t p, int h, int64_t lo, int64_t hi, const Mixture& mx,
@@ -222,26 +230,6 @@ __device__ __forceinline__ void read_body(char* __restrict__ smem, const uint16_
         XT xt1;
         xt.load(rx, 0);
         xt1.load(rx, S::ROUND);
-        wait();
-#pragma unroll
-        for (int ct = 0; ct < S::CTW; ++ct)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const u32x4 zv = buf_load16_dev(rmp, uint32_t(4 * Kp * DV + ((cs * S::CTW + ct) * 32 + 8 * q + 4 * lh) * 4));
-#pragma unroll
-                for (int i = 0; i < 4; ++i) zr[ct][4 * q + i] = __uint_as_float(zv[i]);
-            }
-        // VtT hi/lo: all loads in flight before the first LDS store
-        constexpr int MCH = 2 * DV * Kp / 8, MPER = (MCH + NT - 1) / NT;
-        u32x4 mv[MS_LDS ? MPER : 1];
-        if constexpr (MS_LDS) {
-#pragma unroll
-            for (int u = 0; u < MPER; ++u) {
-                const int c = threadIdx.x + u * NT;
-                const int row = c / (Kp / 8), col = (c - row * (Kp / 8)) * 8;
-                if (MCH % NT == 0 || c < MCH) mv[u] = buf_load16_dev(rmp, uint32_t((row * Kp + col) * 2));
-            }
-        }
         if constexpr (BUILD && STAGE) {  // while the tiles are in flight
             mstage.commit(reinterpret_cast<float*>(&Xt[0][0]));
             __syncthreads();
@@ -250,14 +238,6 @@ __device__ __forceinline__ void read_body(char* __restrict__ smem, const uint16_
             __syncthreads();  // staging area free for the x tiles
         } else if constexpr (BUILD) {
             P.build(praw, mx.K, cs * S::CTW);
-        }
-        if constexpr (MS_LDS) {
-#pragma unroll
-            for (int u = 0; u < MPER; ++u) {
-                const int c = threadIdx.x + u * NT;
-                const int row = c / (Kp / 8), col = (c - row * (Kp / 8)) * 8;
-                if (MCH % NT == 0 || c < MCH) *reinterpret_cast<u32x4*>(Ms + row * LDM + col) = mv[u];
-            }
         }
         xt.commit(Xt[0]);
         xt.load(rx, 2 * S::ROUND);
@@ -274,6 +254,34 @@ __device__ __forceinline__ void read_body(char* __restrict__ smem, const uint16_
     else
 #pragma unroll
         for (int ct = 0; ct < S::CTW; ++ct) acc_a[ct] = acc_a_init[ct];
+
+    // the latent memory: only now (a fused kernel waits here for it to be complete)
+    wait();
+#pragma unroll
+    for (int ct = 0; ct < S::CTW; ++ct)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const u32x4 zv = buf_load16_dev(rmp, uint32_t(4 * Kp * DV + ((cs * S::CTW + ct) * 32 + 8 * q + 4 * lh) * 4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) zr[ct][4 * q + i] = __uint_as_float(zv[i]);
+        }
+    if constexpr (MS_LDS) {  // VtT hi/lo: all loads in flight before the first LDS store
+        constexpr int MCH = 2 * DV * Kp / 8, MPER = (MCH + NT - 1) / NT;
+        u32x4 mv[MPER];
+#pragma unroll
+        for (int u = 0; u < MPER; ++u) {
+            const int c = threadIdx.x + u * NT;
+            const int row = c / (Kp / 8), col = (c - row * (Kp / 8)) * 8;
+            if (MCH % NT == 0 || c < MCH) mv[u] = buf_load16_dev(rmp, uint32_t((row * Kp + col) * 2));
+        }
+#pragma unroll
+        for (int u = 0; u < MPER; ++u) {
+            const int c = threadIdx.x + u * NT;
+            const int row = c / (Kp / 8), col = (c - row * (Kp / 8)) * 8;
+            if (MCH % NT == 0 || c < MCH) *reinterpret_cast<u32x4*>(Ms + row * LDM + col) = mv[u];
+        }
+        __syncthreads();  // VtT in LDS for every wave
+    }
 
     f32x16 o[PW];
     auto out_mfma = [&]() __attribute__((always_inline)) {  // O^T tiles of the round whose e is in LDS
@@ -371,9 +379,10 @@ __device__ __forceinline__ void read_body(char* __restrict__ smem, const uint16_
 // One launch for the whole bidirectional forward.  Grid (G, P); workgroup (g, p) owns rows
 // [g seg, (g + 1) seg) of problem p:
 //   1. write: the partial [Vt^T | Z] of its rows (write_body, operand planes built once);
-//   2. after all G partials of p are published: combine 1/G of p's memory (fixed order);
-//   3. after all G slices are published: read its rows (read_body, same planes, the first
-//      x tiles already in flight while it waits).
+//   2. read phase (read_body, same planes): its first x tiles committed and round 0's
+//      scores issued, which need no memory;
+//   3. after all G partials of p are published: combine 1/G of p's memory (fixed order);
+//   4. after all G slices are published: the rest of the read phase.
 // flags: [P][2][G] words (partials ready, memory slice ready), compared with `token`.  A
 // workgroup whose wait times out writes NaN over its output rows.
 template <int DR, int KT, int VT>
@@ -398,13 +407,16 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(WriteLds<DR, KT, VT>::bytes > R
 
     WaveParams<DR, Split<DR, KT>::CTW> P;
     write_body<DR, KT, VT, true>(smem, XK, V, N, p, h, lo, hi, mx, P, part + size_t(g) * E);
-    publish_token(fl + g, token);
-    bool ok = wait_tokens(fl, G, token);
-    const int per = (E / 4 + G - 1) / G;  // 16-byte groups per slice
-    combine_range(part, G, E, Kp, DV, min(g * per, E / 4), min((g + 1) * per, E / 4), mem, NT);
-    publish_token(fl + G + g, token);  // its barrier also frees the write phase's LDS
-    read_body<DR, KT, VT, false>(smem, XQ, N, p, h, lo, hi, mx, P, mem, eps, O,
-                                 [&] { ok = wait_tokens(fl + G, G, token) && ok; });
+    publish_token(fl + g, token);  // its barrier also frees the write phase's LDS
+    bool ok = true;
+    read_body<DR, KT, VT, false>(smem, XQ, N, p, h, lo, hi, mx, P, mem, eps, O, [&] {
+        // behind the read phase's first tiles and scores: complete the memory
+        ok = wait_tokens(fl, G, token);
+        const int per = (E / 4 + G - 1) / G;  // 16-byte groups per slice
+        combine_range(part, G, E, Kp, DV, min(g * per, E / 4), min((g + 1) * per, E / 4), mem, NT);
+        publish_token(fl + G + g, token);
+        ok = wait_tokens(fl + G, G, token) && ok;
+    });
     if (!ok) {  // the memory was never complete: make that visible in the output
         uint16_t* op = O + (size_t(p) * N + lo) * DV;
         for (int64_t e = threadIdx.x; e < (hi - lo) * DV; e += NT) op[e] = 0x7fc0u;
