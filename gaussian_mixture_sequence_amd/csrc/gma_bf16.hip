@@ -324,7 +324,8 @@ __device__ __forceinline__ void read_body(char* __restrict__ smem, const uint16_
 
     auto iteration = [&](const int64_t r, f32x16 (&cur)[S::CTW], f32x16 (&nxt)[S::CTW]) __attribute__((always_inline)) {
         const int xb1 = int((r + 1) % XB);
-        // ---- region A
+        // ---- region A (raised priority while feeding the matrix cores, as in write_body)
+        __builtin_amdgcn_s_setprio(1);
         out_mfma();  // round r-1 (on zero-padded or stale e for r = 0: never stored)
         scores_lds<DR, S::CTW>(P, Xt[xb1], ts, nxt);
         if (XB == 2) {
@@ -339,6 +340,7 @@ __device__ __forceinline__ void read_body(char* __restrict__ smem, const uint16_
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
         }
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();  // B1
         // ---- region B
         if (r > 0) out_store(r - 1);

@@ -225,7 +225,10 @@ __device__ __forceinline__ void write_body(char* __restrict__ smem, const uint16
         const int64_t r0 = r * S::ROUND;
         const int xb1 = int((r + 1) % XB);
         // ---- region A (the accumulation first: its transposing LDS reads bound the
-        // scheduling region, so everything after them can be interleaved)
+        // scheduling region, so everything after them can be interleaved).  The wave runs
+        // at raised priority while it feeds the matrix cores, so the other wave on its SIMD
+        // fills the VALU around it rather than competing for issue.
+        __builtin_amdgcn_s_setprio(1);
         accumulate();
         scores_lds<DR, S::CTW>(P, Xt[xb1], ts, nxt);
         if (XB == 2) {
@@ -240,6 +243,7 @@ __device__ __forceinline__ void write_body(char* __restrict__ smem, const uint16
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // then up to five VALU
         }
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();  // B1: statistics published; x tile r+1 and tiles r-1 consumed
         // ---- region B
         const int valid = int(max<int64_t>(0, min<int64_t>(32, rows - r0 - ts * 32)));

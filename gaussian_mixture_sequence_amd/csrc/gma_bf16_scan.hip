@@ -335,7 +335,9 @@ __device__ __forceinline__ void scan_body(char* __restrict__ smem, const uint16_
     auto chunk = [&](const int64_t c, const int b, f32x16 (&cur)[JPW][CTW], f32x16 (&nxt)[JPW][CTW])
                      __attribute__((always_inline)) {
         const int64_t nc = c * CH;
-        // ---- region 1
+        // ---- region 1 (raised priority while the wave feeds the matrix cores: the other
+        // wave on its SIMD fills the VALU around it)
+        __builtin_amdgcn_s_setprio(1);
         commit_v(Vs[b ^ 1]);  // V tile c+1
         load_v(nc + 2 * CH);
         if (wave < STILES) {  // S^T tile (rows = key positions, cols = query positions)
@@ -382,10 +384,12 @@ __device__ __forceinline__ void scan_body(char* __restrict__ smem, const uint16_
         }
         scores_chunk(nxt);  // chunk c+2
         if (CS > 1) softmax_local(cur);
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();  // B_Q: S(c), row sums, Gq Z partials, statistics of c+1 published
         // ---- region 2
         if (CS == 1) softmax_local(cur);
         store_gamma(cur, nc + CH, b ^ 1);  // chunk c+1
+        __builtin_amdgcn_s_setprio(1);
         const uint16_t* Vc = Vs[b];
 #pragma unroll
         for (int cc = 0; cc < CPW; ++cc) {
@@ -474,6 +478,7 @@ __device__ __forceinline__ void scan_body(char* __restrict__ smem, const uint16_
         xk.commit(XtK);
         xq.load(rq, nc + 4 * CH);
         xk.load(rk, nc + 4 * CH);
+        __builtin_amdgcn_s_setprio(0);
         __syncthreads();  // B_P: Gamma(c+1), V(c+1), Z(c+1) visible; chunk c consumed
     };
     // chunks in pairs (static buffer roles), then the odd one
