@@ -24,7 +24,8 @@ STATUS_NAMES = ["GMA_OK", "GMA_ERR_NULL_POINTER", "GMA_ERR_BAD_SHAPE", "GMA_ERR_
 GMA_F32, GMA_BF16 = 0, 1
 GMA_OP_RESPONSIBILITIES, GMA_OP_BIDIR, GMA_OP_CAUSAL = 0, 1, 2
 EXPORTED = ["gma_status_string", "gma_workspace_size", "gma_responsibilities", "gma_forward_bidir",
-            "gma_forward_causal", "gma_profiling", "gma_profiling_collect"]
+            "gma_forward_causal", "gma_profiling", "gma_profiling_collect", "gma_set_wait_limit"]
+WAIT_LIMIT_DEFAULT = 1 << 18  # GMA_WAIT_LIMIT_DEFAULT
 
 
 class GmaError(RuntimeError):
@@ -72,6 +73,8 @@ def load() -> ctypes.CDLL:
             lib.gma_profiling.restype = i32
             lib.gma_profiling_collect.argtypes = [ctypes.POINTER(KernelStat), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
             lib.gma_profiling_collect.restype = i32
+            lib.gma_set_wait_limit.argtypes = [ctypes.c_uint32]
+            lib.gma_set_wait_limit.restype = i32
             _lib = lib
     return _lib
 
@@ -187,3 +190,8 @@ def gma_profiling_collect(capacity: int = 64):
     n = ctypes.c_int(0)
     _check(load().gma_profiling_collect(buf, capacity, ctypes.byref(n)), "gma_profiling_collect")
     return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(min(n.value, capacity))}
+
+
+def gma_set_wait_limit(polls: int) -> None:
+    """Bound on the hand-off waits of the single-launch bf16 forwards (see gma.h)."""
+    _check(load().gma_set_wait_limit(int(polls)), "gma_set_wait_limit")

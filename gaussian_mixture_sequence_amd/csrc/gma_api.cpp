@@ -126,6 +126,12 @@ uint64_t launch_token() {
     return z ^ (z >> 31);
 }
 
+namespace {
+std::atomic<uint32_t> g_wait_limit{GMA_WAIT_LIMIT_DEFAULT};
+}  // namespace
+
+uint32_t wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
+
 // ---- kernel timing ----------------------------------------------------------------
 
 namespace {
@@ -270,6 +276,11 @@ gma_status_t gma_forward_causal(const void* XQ, const void* XK, const void* V, g
                                 size_t workspace_bytes, hipStream_t stream) {
     return forward_common(GMA_OP_CAUSAL, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, O, shape, chunk,
                           workspace, workspace_bytes, stream);
+}
+
+gma_status_t gma_set_wait_limit(uint32_t polls) {
+    gma::g_wait_limit.store(polls, std::memory_order_relaxed);
+    return GMA_OK;
 }
 
 gma_status_t gma_profiling(int enable) {

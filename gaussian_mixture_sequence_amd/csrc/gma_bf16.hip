@@ -394,8 +394,8 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(WriteLds<DR, KT, VT>::bytes > R
                                                       : ReadLds<DR, KT, VT>::bytes))))
     bidir_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
                  int64_t N, int H, int64_t seg, int G, Mixture mx, float* __restrict__ partials,
-                 uint16_t* __restrict__ memory, uint64_t* __restrict__ flags, uint64_t token, float eps,
-                 uint16_t* __restrict__ O) {
+                 uint16_t* __restrict__ memory, uint64_t* __restrict__ flags, uint64_t token,
+                 uint32_t wait_limit, float eps, uint16_t* __restrict__ O) {
     using WL = WriteLds<DR, KT, VT>;
     using RL = ReadLds<DR, KT, VT>;
     __shared__ __attribute__((aligned(16))) char smem[WL::bytes > RL::bytes ? WL::bytes : RL::bytes];
@@ -413,13 +413,17 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(WriteLds<DR, KT, VT>::bytes > R
     bool ok = true;
     read_body<DR, KT, VT, false>(smem, XQ, N, p, h, lo, hi, mx, P, mem, eps, O, [&] {
         // behind the read phase's first tiles and scores: complete the memory
-        ok = wait_tokens(fl, G, token);
+        ok = wait_tokens(fl, G, token, wait_limit);
         const int per = (E / 4 + G - 1) / G;  // 16-byte groups per slice
         combine_range(part, G, E, Kp, DV, min(g * per, E / 4), min((g + 1) * per, E / 4), mem, NT);
         publish_token(fl + G + g, token);
-        ok = wait_tokens(fl + G, G, token) && ok;
+        ok = wait_tokens(fl + G, G, token, wait_limit) && ok;
     });
+    // waves poll on their own: agree on the outcome before acting on it
+    ok = workgroup_all(ok, reinterpret_cast<int*>(smem));
     if (!ok) {  // the memory was never complete: make that visible in the output
+        __builtin_amdgcn_s_waitcnt(0);  // the phase's own stores of these rows land first
+        __syncthreads();
         uint16_t* op = O + (size_t(p) * N + lo) * DV;
         for (int64_t e = threadIdx.x; e < (hi - lo) * DV; e += NT) op[e] = 0x7fc0u;
     }
@@ -501,7 +505,7 @@ hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void*
             GMA_LAUNCH("bf16_bidir", (bf::bidir_kernel<DR, KT, VT>), dim3(unsigned(p.G), unsigned(p.P)),
                        dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
                        static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), mx, partials, memory, flags,
-                       token, eps, static_cast<uint16_t*>(O));
+                       token, wait_limit(), eps, static_cast<uint16_t*>(O));
             return hipGetLastError();
         });
     });

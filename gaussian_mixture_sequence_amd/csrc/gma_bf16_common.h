@@ -280,8 +280,8 @@ constexpr int waves_for_lds(size_t lds) { return lds <= 80 * 1024 ? 2 : 1; }
 // completed; waiters poll until each word they need holds the launch's token, a per-call
 // random value, so stale words from earlier calls never match.  Waiters only depend on
 // workgroups dispatched no later than themselves or alongside them, and the poll is
-// bounded: on time-out the waiter reports failure instead of hanging.
-constexpr uint32_t kSpinLimit = 1u << 18;
+// bounded (`limit` polls, a launch argument): on time-out the waiter reports failure
+// instead of hanging.
 
 __device__ __forceinline__ void publish_token(uint64_t* flag, uint64_t token) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's stores have completed
@@ -289,11 +289,23 @@ __device__ __forceinline__ void publish_token(uint64_t* flag, uint64_t token) {
     if (threadIdx.x == 0) __hip_atomic_store(flag, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Every wave polls flags[0 .. n) itself (no LDS, no barrier); true when all hold `token`.
-__device__ __forceinline__ bool wait_tokens(const uint64_t* flags, int n, uint64_t token) {
+// AND of a per-wave flag over the workgroup, through NW ints of LDS that no wave uses any
+// more (`scratch`); every wave gets the same result.
+__device__ __forceinline__ bool workgroup_all(bool v, int* scratch) {
+    __syncthreads();  // scratch free
+    if ((threadIdx.x & 63) == 0) scratch[wave_id()] = v ? 1 : 0;
+    __syncthreads();
+    bool r = true;
+    for (int w = 0; w < int(blockDim.x >> 6); ++w) r = r && scratch[w] != 0;
+    return r;
+}
+
+// Every wave polls flags[0 .. n) itself (no LDS, no barrier); true when all hold `token`
+// within `limit` polls.
+__device__ __forceinline__ bool wait_tokens(const uint64_t* flags, int n, uint64_t token, uint32_t limit) {
     const int l = threadIdx.x & 63;
     bool done = false;
-    for (uint32_t it = 0; it < kSpinLimit; ++it) {
+    for (uint32_t it = 0; it < limit; ++it) {
         bool mine = true;
         for (int i = l; i < n; i += 64)
             mine = mine && (__hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == token);

@@ -509,7 +509,8 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
 __attribute__((amdgpu_waves_per_eu(waves_for_lds(causal_lds_bytes<DR, KT, VT, CH_REQ>()))))
     causal_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
                   int64_t N, int H, int64_t seg, int G, Mixture mx, float* __restrict__ aggregates,
-                  uint64_t* __restrict__ flags, uint64_t token, float eps, uint16_t* __restrict__ O) {
+                  uint64_t* __restrict__ flags, uint64_t token, uint32_t wait_limit, float eps,
+                  uint16_t* __restrict__ O) {
     __shared__ __attribute__((aligned(16))) char smem[causal_lds_bytes<DR, KT, VT, CH_REQ>()];
     using S = Split<DR, KT>;
     constexpr int Kp = KT * 32, DV = VT * 32, E = Kp * (DV + 1), NT = S::NW * 64;
@@ -527,8 +528,12 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(causal_lds_bytes<DR, KT, VT, CH
     }
     bool ok = true;
     scan_body<DR, KT, VT, CH_REQ, false>(smem, XQ, XK, V, N, p, h, s, lo, hi, mx, P, agg, eps, O,
-                                         [&] { ok = wait_tokens(fl, s, token); });
+                                         [&] { ok = wait_tokens(fl, s, token, wait_limit); });
+    // waves poll on their own: agree on the outcome before acting on it
+    ok = workgroup_all(ok, reinterpret_cast<int*>(smem));
     if (!ok) {  // the starting memory was never complete: make that visible in the output
+        __builtin_amdgcn_s_waitcnt(0);  // the phase's own stores of these rows land first
+        __syncthreads();
         uint16_t* op = O + (size_t(p) * N + lo) * DV;
         for (int64_t e = threadIdx.x; e < (hi - lo) * DV; e += NT) op[e] = 0x7fc0u;
     }
@@ -936,7 +941,7 @@ hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void
             GMA_LAUNCH("bf16_causal", (bf::causal_kernel<DR, KT, VT, CH>), dim3(unsigned(p.G), unsigned(p.P)),
                        dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
                        static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), mx, aggregates, flags,
-                       launch_token(), eps, static_cast<uint16_t*>(O));
+                       launch_token(), wait_limit(), eps, static_cast<uint16_t*>(O));
         } else {
             // aggregates of segments 0 .. G-2 (the last segment's aggregate is never read)
             if (p.G > 1) {

@@ -36,6 +36,10 @@ struct Plan {
 // flag words left in a workspace by earlier calls never equal it.
 uint64_t launch_token();
 
+// Polls a workgroup of the fused bf16 kernels makes before it gives up on a hand-off
+// (gma_set_wait_limit).
+uint32_t wait_limit();
+
 // Kernel timing hooks (see gma_profiling in gma.h).  Launchers bracket each launch with
 // trace_begin / trace_end; both are no-ops unless profiling is enabled.
 void trace_begin(hipStream_t st, const char* name);

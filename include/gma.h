@@ -44,8 +44,9 @@
  * Numerics    Scores and softmax in fp32, accumulations in fp32.  bf16 I/O uses bf16
  *             MFMA with split (hi + lo) operands for the scores and for the latent
  *             memory, and rounds O to bf16 (nearest-even).  Results are bitwise
- *             reproducible for a fixed shape and chunk length (no atomics, fixed
- *             reduction order).
+ *             reproducible for a fixed shape and chunk length: reductions run in a fixed
+ *             order, and the only atomics are the hand-off words between the phases of
+ *             one launch (see gma_set_wait_limit).
  */
 #ifndef GMA_H
 #define GMA_H
@@ -117,6 +118,9 @@ gma_status_t gma_responsibilities(const void* X, gma_dtype_t x_dtype,
  * eps > 0 is added once to each row denominator (footnote 4 of Sec. 3.3).  Gamma is
  * never written to memory; Vt and Z live in the workspace.
  *   XQ, XK [B,H,N,d_r], V [B,H,N,d_v], O [B,H,N,d_v] out, all in io_dtype.
+ * With bf16 I/O the whole forward is one kernel launch whose workgroups hand the split
+ * partials and the combined memory to one another through the workspace (flag words
+ * compared with a fresh per-call value, so the workspace may hold anything on entry).
  */
 gma_status_t gma_forward_bidir(const void* XQ, const void* XK, const void* V,
                                gma_dtype_t io_dtype,
@@ -132,7 +136,10 @@ gma_status_t gma_forward_bidir(const void* XQ, const void* XK, const void* V,
  * inside a chunk the masked product (Gamma_Q Gamma_K^T restricted to j <= i) is formed
  * on chip and the K x (d_v+1) running memory carries the prefix across chunks.
  * `chunk` must be 16, 32 or 64 (GMA_ERR_UNSUPPORTED otherwise).  Output row i depends
- * only on inputs at positions <= i.  Arguments as for gma_forward_bidir.
+ * only on inputs at positions <= i.  Arguments as for gma_forward_bidir.  With bf16 I/O
+ * and K <= 128 (d_r * K <= 8192) the forward is one launch: each segment's workgroup
+ * publishes its segment aggregate in the workspace and waits for those of the segments
+ * before it (same flag scheme as gma_forward_bidir); other shapes take two launches.
  */
 gma_status_t gma_forward_causal(const void* XQ, const void* XK, const void* V,
                                 gma_dtype_t io_dtype,
@@ -159,6 +166,21 @@ typedef struct {
 
 gma_status_t gma_profiling(int enable);
 gma_status_t gma_profiling_collect(gma_kernel_stat_t* stats, int capacity, int* count);
+
+/*
+ * Bound on the hand-off waits of the single-launch bf16 forwards.  Each of those launches
+ * runs several phases, and a workgroup waits for data that other workgroups of the same
+ * launch publish (the split partials and memory slices of a bidirectional problem; the
+ * aggregates of the earlier segments of a causal problem).  The waits poll at most `polls`
+ * times (each poll is a device-wide load followed by a short sleep).  A workgroup whose
+ * wait exceeds the bound stops waiting and writes NaN over its output rows, so a launch
+ * always terminates.  The default, GMA_WAIT_LIMIT_DEFAULT polls, is far above any wait of
+ * a healthy launch (well under a second in total).  0 makes every such wait fail at
+ * once.  That setting exists so that tests can exercise the failure path.  The value is
+ * process-wide and read when a forward is enqueued.
+ */
+#define GMA_WAIT_LIMIT_DEFAULT (1u << 18)
+gma_status_t gma_set_wait_limit(uint32_t polls);
 
 #ifdef __cplusplus
 }

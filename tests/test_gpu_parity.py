@@ -248,3 +248,20 @@ def test_bf16_workspace_reuse_and_garbage(causal):
             out = gb.gma_forward_bidir(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps, workspace=ws)
         torch.cuda.synchronize()
         assert np.array_equal(to_np(out), ref)
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["bidir", "causal"])
+def test_bf16_wait_timeout_gives_nan(causal):
+    """Failure path of the in-launch hand-off, forced from the host: with a wait bound of 0
+    every workgroup's wait fails at once, the launch still ends, and every output row is
+    NaN.  Restoring the default bound gives the normal result again."""
+    w = bf16_case(causal=causal, B=1, H=2, N=1500, seed=63)
+    inp = make_inputs(w)
+    ref = to_np(run_gpu(w, inp))
+    try:
+        gb.gma_set_wait_limit(0)
+        out = to_np(run_gpu(w, inp))
+    finally:
+        gb.gma_set_wait_limit(gb.WAIT_LIMIT_DEFAULT)
+    assert np.isnan(out).all()
+    assert np.array_equal(to_np(run_gpu(w, inp)), ref)
