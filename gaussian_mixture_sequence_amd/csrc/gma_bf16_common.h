@@ -313,6 +313,10 @@ __device__ __forceinline__ bool wait_tokens(const uint64_t* flags, int n, uint64
         if (done) break;
         __builtin_amdgcn_s_sleep(2);
     }
+    // The polls are relaxed atomics: keep the compiler from moving the caller's reads of the
+    // handed-off data above them (the hardware issues those reads only after the polls'
+    // values have returned, and the data reached the coherence point before the word did).
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
     return done;
 }
 
