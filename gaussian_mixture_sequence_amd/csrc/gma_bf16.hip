@@ -11,8 +11,9 @@
 //   aggregate causal: the write kernel over segments 0 .. G-2 (segment aggregates)
 //   scan      causal chunked scan (gma_bf16_scan.hip); segment s starts from the sum of
 //             the aggregates of segments 0 .. s-1
-// Every kernel builds the score operands of its own component tiles from mu, sigma2 and
-// pi in registers (WaveParams::compute), so no launch is spent on the parameters.
+// Every kernel builds the score operands from mu, sigma2 and pi itself (PlaneBuilder: each
+// (component, dim) pair once per workgroup, through LDS; WaveParams::compute per wave where
+// the planes do not fit), so no launch is spent on the parameters.
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -203,17 +204,13 @@ __device__ __forceinline__ void read_body(char* __restrict__ smem, const uint16_
     const int cs = wave % S::CS, ts = wave / S::CS;
     const int64_t rows = hi - lo;
     const int64_t R = (rows + S::ROUND - 1) / S::ROUND;
-    using MS = MixtureStage<DR, Kp, NT>;
-    constexpr bool STAGE = sizeof(Xt) >= MS::LDS_BYTES;
+    using PB = PlaneBuilder<DR, Kp, NT>;
+    constexpr bool COOP = sizeof(Xt) >= PB::LDS_BYTES;
     typename WaveParams<DR, S::CTW>::Raw praw;
-    MS mstage;
+    PB pb;
     if constexpr (BUILD) {
-        if constexpr (STAGE) {
-            mstage.load(mx, h);
-            P.fetch_pi(mx, h, cs * S::CTW, praw);
-        } else {
-            P.fetch(mx, h, cs * S::CTW, praw);
-        }
+        if constexpr (COOP) pb.load(mx, h);
+        else P.fetch(mx, h, cs * S::CTW, praw);
     }
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(XQ + (size_t(p) * N + lo) * DR, rows * DR * 2);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + (size_t(p) * N + lo) * DV, rows * DV * 2);
@@ -230,11 +227,10 @@ __device__ __forceinline__ void read_body(char* __restrict__ smem, const uint16_
         XT xt1;
         xt.load(rx, 0);
         xt1.load(rx, S::ROUND);
-        if constexpr (BUILD && STAGE) {  // while the tiles are in flight
-            mstage.commit(reinterpret_cast<float*>(&Xt[0][0]));
+        if constexpr (BUILD && COOP) {  // while the tiles are in flight
+            pb.build(reinterpret_cast<char*>(&Xt[0][0]), mx.K);
             __syncthreads();
-            P.template read_staged<Kp>(reinterpret_cast<const float*>(&Xt[0][0]), cs * S::CTW, praw);
-            P.build(praw, mx.K, cs * S::CTW);
+            P.template read_planes<Kp>(reinterpret_cast<const char*>(&Xt[0][0]), cs * S::CTW);
             __syncthreads();  // staging area free for the x tiles
         } else if constexpr (BUILD) {
             P.build(praw, mx.K, cs * S::CTW);

@@ -328,36 +328,87 @@ struct Mixture {
     int K;
 };
 
-// One head's mu and sigma2 rows [KP][DR] (rows past K repeat row K - 1) fetched by the
-// whole workgroup with coalesced 16-byte loads and staged in LDS as fp32 rows of DR + 4
-// floats, so that the 16-byte reads of a fragment's 8 dims by 32 rows are conflict-free.
-// A strided per-lane fetch of the same values costs several times the L1 work, and every
-// wave of the workgroup would repeat it.
+// One head's score operands built once per workgroup (Gaussian Mixture Attention, Eq. 16
+// with the square expanded, in log2 units):
+//   a = log2(e) mu / sigma2,  b = -log2(e) / (2 sigma2),  each as a bf16 hi + lo pair,
+//   c = log2 pi - (sum_d log2 sigma2 + log2(e) mu^2 / sigma2) / 2   (fp32).
+// Every thread fetches whole 16-byte chunks of mu and sigma2 rows (coalesced), computes the
+// planes of its chunks' 4 dims, and stores them in LDS in MFMA A-fragment order:
+//   planes [KP/32][DR/16][4: a_hi, a_lo, b_hi, b_lo][64 lanes] of 16 bytes
+// followed by c [KP] fp32.  Lane (lh, j) of component tile ct, k-step ks holds component
+// 32 ct + j, dims 16 ks + 8 lh .. + 7, so each wave then loads its fragments with one
+// conflict-free 16-byte read per plane (WaveParams::read_planes).  Each (component, dim)
+// pair is computed once per workgroup, not once per wave that needs it.  Components k >= K
+// (padding up to KP) get zero planes and c = -inf, so their responsibility is exactly 0.
+// sigma2 must be a positive normal float.
 template <int DR, int KP, int NT>
-struct MixtureStage {
-    static constexpr int LD = DR + 4;
-    static constexpr int LDS_BYTES = 2 * KP * LD * 4;
-    static constexpr int CPR = DR / 4, CHUNKS = 2 * KP * CPR, PER = (CHUNKS + NT - 1) / NT;
+struct PlaneBuilder {
+    static constexpr int KT = KP / 32, KS = DR / 16;
+    static constexpr int CPR = DR / 4;  // 16-byte chunks per parameter row
+    static constexpr int CHUNKS = KP * CPR, PER = (CHUNKS + NT - 1) / NT;
     static constexpr bool EVEN = CHUNKS % NT == 0;
-    float4 r[PER];
+    static constexpr int PLANE_BYTES = KT * KS * 4 * 64 * 16;
+    static constexpr int LDS_BYTES = PLANE_BYTES + KP * 4;
+    static_assert(NT % CPR == 0 && CPR <= 64, "a row's chunks must sit in consecutive lanes of one wave");
+    float4 m[PER], v[PER];
+    float pk[PER];
 
+    // Raw parameters of this thread's chunks (rows past K repeat row K - 1), fetched apart
+    // from the arithmetic so a kernel can put its first tile loads in flight before it
+    // waits for them.
     __device__ __forceinline__ void load(const Mixture& mx, int h) {
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
             const int c = threadIdx.x + u * NT;
-            const int arr = c / (KP * CPR), cc = c - arr * KP * CPR, row = cc / CPR, col = cc - row * CPR;
-            const int kr = row < mx.K ? row : mx.K - 1;
-            if (EVEN || c < CHUNKS)
-                r[u] = *reinterpret_cast<const float4*>((arr ? mx.s2 : mx.mu) + (size_t(h) * mx.K + kr) * DR + 4 * col);
+            if (EVEN || c < CHUNKS) {
+                const int row = c / CPR, col = c - row * CPR;
+                const size_t kr = size_t(h) * mx.K + (row < mx.K ? row : mx.K - 1);
+                m[u] = *reinterpret_cast<const float4*>(mx.mu + kr * DR + 4 * col);
+                v[u] = *reinterpret_cast<const float4*>(mx.s2 + kr * DR + 4 * col);
+                pk[u] = mx.pi[kr];
+            }
         }
     }
-    // lds: [2][KP][LD] fp32 (mu rows, then sigma2 rows)
-    __device__ __forceinline__ void commit(float* lds) const {
+
+    // Planes and constants into `lds` (LDS_BYTES); the caller synchronises before reading.
+    __device__ __forceinline__ void build(char* lds, int K) const {
+        const float L2E = 1.4426950408889634f;
+        float* cst = reinterpret_cast<float*>(lds + PLANE_BYTES);
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
             const int c = threadIdx.x + u * NT;
-            const int arr = c / (KP * CPR), cc = c - arr * KP * CPR, row = cc / CPR, col = cc - row * CPR;
-            if (EVEN || c < CHUNKS) *reinterpret_cast<float4*>(lds + (arr * KP + row) * LD + 4 * col) = r[u];
+            if (EVEN || c < CHUNKS) {  // uniform over the CPR lanes of a row
+                const int row = c / CPR, col = c - row * CPR;
+                const bool valid = row < K;
+                const float mm[4] = {m[u].x, m[u].y, m[u].z, m[u].w};
+                const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                float a[4], b[4], csum = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float inv2 = __builtin_amdgcn_rcpf(valid ? vv[e] : INFINITY) * L2E;
+                    a[e] = mm[e] * inv2;
+                    b[e] = -0.5f * inv2;
+                    csum += __builtin_amdgcn_logf(vv[e]) + mm[e] * a[e];
+                }
+                uint32_t w[4][2];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const uint32_t ah = pack_bf16x2(a[2 * q], a[2 * q + 1]);
+                    const uint32_t bh = pack_bf16x2(b[2 * q], b[2 * q + 1]);
+                    w[0][q] = ah;
+                    w[1][q] = pack_bf16x2(a[2 * q] - __uint_as_float(ah << 16), a[2 * q + 1] - __uint_as_float(ah & 0xffff0000u));
+                    w[2][q] = bh;
+                    w[3][q] = pack_bf16x2(b[2 * q] - __uint_as_float(bh << 16), b[2 * q + 1] - __uint_as_float(bh & 0xffff0000u));
+                }
+                const int d0 = 4 * col, ct = row >> 5, j = row & 31;
+                const int ks = d0 >> 4, lh = (d0 >> 3) & 1, half = (d0 >> 2) & 1;
+                char* dst = lds + (size_t((ct * KS + ks) * 4) * 64 + 32 * lh + j) * 16 + half * 8;
+#pragma unroll
+                for (int pl = 0; pl < 4; ++pl) *reinterpret_cast<u32x2*>(dst + pl * 64 * 16) = u32x2{w[pl][0], w[pl][1]};
+#pragma unroll
+                for (int o = CPR / 2; o >= 1; o >>= 1) csum += __shfl_xor(csum, o, kWave);
+                if (col == 0) cst[row] = valid ? __builtin_amdgcn_logf(pk[u]) - 0.5f * csum : -INFINITY;
+            }
         }
     }
 };
@@ -397,31 +448,27 @@ struct WaveParams {
         }
     }
 
-    // Mixing weights of this lane's components (the rest of Raw comes from read_staged).
-    __device__ __forceinline__ static void fetch_pi(const Mixture& mx, int h, int ct0, Raw& r) {
-        const int l = threadIdx.x & 63, K = mx.K;
-#pragma unroll
-        for (int ct = 0; ct < CTW; ++ct) {
-            const int k = (ct0 + ct) * 32 + (l & 31);
-            r.pk[ct] = mx.pi[size_t(h) * K + (k < K ? k : K - 1)];
-        }
-    }
-
-    // This lane's fragment dims from a MixtureStage buffer of KP rows.
+    // This wave's fragments and constants from a PlaneBuilder buffer of KP components.
     template <int KP>
-    __device__ __forceinline__ static void read_staged(const float* lds, int ct0, Raw& r) {
-        constexpr int LD = DR + 4;
+    __device__ __forceinline__ void read_planes(const char* lds, int ct0) {
         const int l = threadIdx.x & 63, lh = l >> 5;
+        const u32x4* pl = reinterpret_cast<const u32x4*>(lds);
+        const float* cst = reinterpret_cast<const float*>(lds + PlaneBuilder<DR, KP, 64>::PLANE_BYTES);
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
-            const int row = (ct0 + ct) * 32 + (l & 31);
 #pragma unroll
             for (int ks = 0; ks < DR / 16; ++ks)
 #pragma unroll
-                for (int h4 = 0; h4 < 2; ++h4) {
-                    r.m[ct][ks][h4] = *reinterpret_cast<const float4*>(lds + row * LD + 16 * ks + 8 * lh + 4 * h4);
-                    r.v[ct][ks][h4] = *reinterpret_cast<const float4*>(lds + (KP + row) * LD + 16 * ks + 8 * lh + 4 * h4);
-                }
+                for (int q = 0; q < 4; ++q)
+                    w[ct][ks][q] = __builtin_bit_cast(bf16x8, pl[(((ct0 + ct) * (DR / 16) + ks) * 4 + q) * 64 + l]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 cv = *reinterpret_cast<const float4*>(cst + (ct0 + ct) * 32 + 8 * q + 4 * lh);
+                c[ct][4 * q + 0] = cv.x;
+                c[ct][4 * q + 1] = cv.y;
+                c[ct][4 * q + 2] = cv.z;
+                c[ct][4 * q + 3] = cv.w;
+            }
         }
     }
 

@@ -127,18 +127,15 @@ __device__ __forceinline__ void write_body(char* __restrict__ smem, const uint16
     const int cs = wave % S::CS, ts = wave / S::CS;
     const int64_t rows = hi - lo;
     const int64_t R = (rows + S::ROUND - 1) / S::ROUND;  // rounds of this split
-    // mixture parameters staged through the x tile buffer when it is large enough
-    using MS = MixtureStage<DR, Kp, NT>;
-    constexpr bool STAGE = sizeof(Xt) >= MS::LDS_BYTES;
+    // operand planes built by the whole workgroup in the x tile buffer when it is large
+    // enough, else by every wave for itself
+    using PB = PlaneBuilder<DR, Kp, NT>;
+    constexpr bool COOP = sizeof(Xt) >= PB::LDS_BYTES;
     typename WaveParams<DR, S::CTW>::Raw praw;
-    MS mstage;
+    PB pb;
     if constexpr (BUILD) {
-        if constexpr (STAGE) {
-            mstage.load(mx, h);
-            P.fetch_pi(mx, h, cs * S::CTW, praw);
-        } else {
-            P.fetch(mx, h, cs * S::CTW, praw);
-        }
+        if constexpr (COOP) pb.load(mx, h);
+        else P.fetch(mx, h, cs * S::CTW, praw);
     }
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(XK + (size_t(p) * N + lo) * DR, rows * DR * 2);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t(p) * N + lo) * DV, rows * DV * 2);
@@ -194,11 +191,10 @@ __device__ __forceinline__ void write_body(char* __restrict__ smem, const uint16
         load_v(0);
         for (int c = threadIdx.x; c < S::ROUND * LDG / 8; c += NT) reinterpret_cast<u32x4*>(Gs)[c] = u32x4{0u, 0u, 0u, 0u};
         for (int c = threadIdx.x; c < S::ROUND * LDV / 8; c += NT) reinterpret_cast<u32x4*>(Vs)[c] = u32x4{0u, 0u, 0u, 0u};
-        if constexpr (BUILD && STAGE) {  // while the tiles are in flight
-            mstage.commit(reinterpret_cast<float*>(&Xt[0][0]));
+        if constexpr (BUILD && COOP) {  // while the tiles are in flight
+            pb.build(reinterpret_cast<char*>(&Xt[0][0]), mx.K);
             __syncthreads();
-            P.template read_staged<Kp>(reinterpret_cast<const float*>(&Xt[0][0]), cs * S::CTW, praw);
-            P.build(praw, mx.K, cs * S::CTW);
+            P.template read_planes<Kp>(reinterpret_cast<const char*>(&Xt[0][0]), cs * S::CTW);
             __syncthreads();  // staging area free for the x tiles
         } else if constexpr (BUILD) {
             P.build(praw, mx.K, cs * S::CTW);

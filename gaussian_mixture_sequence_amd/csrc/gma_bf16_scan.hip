@@ -157,18 +157,15 @@ __device__ __forceinline__ void scan_body(char* __restrict__ smem, const uint16_
     const int64_t rows = hi - lo;
     const int64_t C = (rows + CH - 1) / CH;  // chunks of this segment
 
-    // mixture parameters staged through the V tile buffers when they are large enough
-    using MS = MixtureStage<DR, Kp, NT>;
-    constexpr bool STAGE = sizeof(Vs) >= MS::LDS_BYTES;
+    // operand planes built by the whole workgroup in the V tile buffers when they are large
+    // enough, else by every wave for itself
+    using PB = PlaneBuilder<DR, Kp, NT>;
+    constexpr bool COOP = sizeof(Vs) >= PB::LDS_BYTES;
     typename WaveParams<DR, CTW>::Raw praw;
-    MS mstage;
+    PB pb;
     if constexpr (BUILD) {
-        if constexpr (STAGE) {
-            mstage.load(mx, h);
-            P.fetch_pi(mx, h, cs * CTW, praw);
-        } else {
-            P.fetch(mx, h, cs * CTW, praw);
-        }
+        if constexpr (COOP) pb.load(mx, h);
+        else P.fetch(mx, h, cs * CTW, praw);
     }
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(XQ + (size_t(p) * N + lo) * DR, rows * DR * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(XK + (size_t(p) * N + lo) * DR, rows * DR * 2);
@@ -271,11 +268,10 @@ __device__ __forceinline__ void scan_body(char* __restrict__ smem, const uint16_
     load_v(0);
     xq.load(rq, 0);
     xk.load(rk, 0);
-    if constexpr (BUILD && STAGE) {
-        mstage.commit(reinterpret_cast<float*>(&Vs[0][0]));
+    if constexpr (BUILD && COOP) {
+        pb.build(reinterpret_cast<char*>(&Vs[0][0]), mx.K);
         __syncthreads();
-        P.template read_staged<Kp>(reinterpret_cast<const float*>(&Vs[0][0]), cs * CTW, praw);
-        P.build(praw, mx.K, cs * CTW);
+        P.template read_planes<Kp>(reinterpret_cast<const char*>(&Vs[0][0]), cs * CTW);
         __syncthreads();  // staging area free for the V tiles
     } else if constexpr (BUILD) {
         P.build(praw, mx.K, cs * CTW);
@@ -523,6 +519,13 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(causal_lds_bytes<DR, KT, VT, CH
     if (s + 1 < G) {
         write_body<DR, KT, VT, true>(smem, XK, V, N, p, h, lo, hi, mx, P, agg + size_t(s) * E);
         publish_token(fl + s, token);  // its barrier also frees the write phase's LDS
+    } else if constexpr (PlaneBuilder<DR, Kp, NT>::LDS_BYTES <= sizeof(smem)) {  // the whole buffer is free here
+        PlaneBuilder<DR, Kp, NT> pb;
+        pb.load(mx, h);
+        pb.build(smem, mx.K);
+        __syncthreads();
+        P.template read_planes<Kp>(smem, (wave_id() % S::CS) * S::CTW);
+        __syncthreads();
     } else {
         P.compute(mx, h, (wave_id() % S::CS) * S::CTW);
     }
