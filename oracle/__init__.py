@@ -8,7 +8,8 @@ Two independent implementations live here, both written from "Gaussian Mixture
 Attention: Linear-Time Sequence Mixing via Probabilistic Latent Routing":
 
 * ``gma_oracle.c`` (loaded through ctypes): the associative form the method uses,
-  Sec. 3.3 Eq. 5-8 (bidirectional) and Sec. 3.5 Eq. 6b/8b (causal), with the
+  Sec. 3.3 Eq. 5-8 (bidirectional; with a separate context sequence for keys and
+  values, the cross-attention of Sec. 3) and Sec. 3.5 Eq. 6b/8b (causal), with the
   responsibilities of Sec. 3.2 Eq. 3 computed through the log-density scores of
   Sec. 4.1 Eq. 16 and the softmax of Eq. 3b.
 * ``brute.py`` (numpy): the explicit N x N affinity forms, Eq. 9-11 and Eq. 9b/10b,
@@ -59,8 +60,10 @@ def _load():
             fwd = [dp, dp, dp, i64, i64, i64, i64, i64, i64, dp, dp, dp, ctypes.c_double, dp]
             lib.oracle_forward_bidir.argtypes = fwd
             lib.oracle_forward_causal.argtypes = fwd
+            lib.oracle_forward_cross.argtypes = [dp, i64, dp, dp, i64, i64, i64, i64, i64, i64, dp, dp, dp,
+                                                 ctypes.c_double, dp]
             for f in (lib.oracle_log_scores, lib.oracle_responsibilities,
-                      lib.oracle_forward_bidir, lib.oracle_forward_causal):
+                      lib.oracle_forward_bidir, lib.oracle_forward_causal, lib.oracle_forward_cross):
                 f.restype = ctypes.c_int
             lib.oracle_num_threads.restype = ctypes.c_int
             lib.oracle_num_threads.argtypes = []
@@ -144,7 +147,24 @@ def forward_causal(XQ, XK, V, mu, sigma2, pi, eps) -> np.ndarray:
     return _forward(_load().oracle_forward_causal, XQ, XK, V, mu, sigma2, pi, eps)
 
 
+def forward_cross(XQ, XK, V, mu, sigma2, pi, eps) -> np.ndarray:
+    """Cross-attention GMA output O [B,H,Nq,d_v] (Sec. 3, "Cross-attention"): queries XQ
+    [B,H,Nq,d_r] read the latent memory written by a context XK [B,H,Nk,d_r], V [B,H,Nk,d_v]
+    through Eq. 5-8."""
+    XQ, XK, V = _f64(XQ), _f64(XK), _f64(V)
+    mu, sigma2, pi = _params(mu, sigma2, pi)
+    B, H, Nq, dr = XQ.shape
+    Nk, dv = XK.shape[2], V.shape[-1]
+    K = mu.shape[1]
+    if XK.shape[:2] != (B, H) or XK.shape[3] != dr or V.shape[:3] != XK.shape[:3]:
+        raise ValueError("XQ must be [B,H,Nq,d_r], XK [B,H,Nk,d_r] and V [B,H,Nk,d_v]")
+    O = np.empty((B, H, Nq, dv), np.float64)
+    _check(_load().oracle_forward_cross(_ptr(XQ), Nq, _ptr(XK), _ptr(V), Nk, B, H, dr, dv, K, _ptr(mu),
+                                        _ptr(sigma2), _ptr(pi), float(eps), _ptr(O)), "oracle_forward_cross")
+    return O
+
+
 from . import brute  # noqa: E402  (numpy explicit-affinity forms)
 
 __all__ = ["build", "num_threads", "log_scores", "responsibilities", "forward_bidir",
-           "forward_causal", "brute"]
+           "forward_causal", "forward_cross", "brute"]

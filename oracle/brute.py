@@ -51,7 +51,9 @@ def affinity(gq: np.ndarray, gk: np.ndarray, causal: bool) -> np.ndarray:
 
 
 def forward_one_head(xq, xk, v, mu, s2, pi, eps: float, causal: bool) -> np.ndarray:
-    """O [N, d_v] for one (batch, head) through the explicit affinity, Eq. 9-10 / 9b-10b."""
+    """O [Nq, d_v] for one (batch, head) through the explicit affinity, Eq. 9-10 / 9b-10b.
+    Without the causal mask the query and key sequences may differ in length (the
+    cross-attention of Sec. 3): A~ is then Nq x Nk."""
     gq = responsibilities(xq, mu, s2, pi)
     gk = responsibilities(xk, mu, s2, pi)
     a_tilde = affinity(gq, gk, causal)
@@ -70,6 +72,18 @@ def forward(XQ, XK, V, mu, sigma2, pi, eps: float, causal: bool) -> np.ndarray:
         for h in range(H):
             out[b, h] = forward_one_head(XQ[b, h], XK[b, h], V[b, h], mu[h], sigma2[h], pi[h],
                                          eps, causal)
+    return out
+
+
+def forward_cross(XQ, XK, V, mu, sigma2, pi, eps: float) -> np.ndarray:
+    """Batched explicit cross-attention: XQ [B,H,Nq,d_r], XK [B,H,Nk,d_r], V [B,H,Nk,d_v]."""
+    XQ, XK, V = (np.asarray(t, np.float64) for t in (XQ, XK, V))
+    mu, sigma2, pi = (np.asarray(t, np.float64) for t in (mu, sigma2, pi))
+    B, H, Nq, _ = XQ.shape
+    out = np.empty((B, H, Nq, V.shape[-1]), np.float64)
+    for b in range(B):
+        for h in range(H):
+            out[b, h] = forward_one_head(XQ[b, h], XK[b, h], V[b, h], mu[h], sigma2[h], pi[h], eps, False)
     return out
 
 

@@ -177,6 +177,66 @@ int oracle_forward_bidir(const double* XQ, const double* XK, const double* V,
 }
 
 /*
+ * Cross-attention GMA (Sec. 3, "Cross-attention"): queries come from a query-side
+ * sequence X of length Nq, keys and values from a separate context sequence Y of
+ * length Nk, and the routing of Sec. 3.3 is applied with Gamma^Q_X and Gamma^K_Y.
+ *   Latent aggregation over the context, Eq. 5-6:  Vt_k = sum_j gammaK_jk V_j,  Z_k = sum_j gammaK_jk
+ *   Normalised broadcasting to the queries, Eq. 7-8:
+ *        O_i = sum_k gammaQ_ik Vt_k / (sum_k gammaQ_ik Z_k + eps)
+ * Layout: XQ [B,H,Nq,d_r], XK [B,H,Nk,d_r], V [B,H,Nk,d_v], O [B,H,Nq,d_v].  An empty
+ * context (Nk = 0) leaves Vt = 0 and Z = 0, so every output is 0 / eps = 0.
+ */
+int oracle_forward_cross(const double* XQ, int64_t Nq, const double* XK, const double* V, int64_t Nk,
+                         int64_t B, int64_t H, int64_t dr, int64_t dv, int64_t K,
+                         const double* mu, const double* sigma2, const double* pi,
+                         double eps, double* O) {
+    if (!XQ || !XK || !V || !mu || !sigma2 || !pi || !O || dv < 1 || Nk < 0 ||
+        bad_sizes(B, H, Nq, dr, K))
+        return -1;
+    int64_t P = B * H;
+    int failed = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
+    for (int64_t p = 0; p < P; ++p) {
+        int64_t h = p % H;
+        const double* mu_h = mu + h * K * dr;
+        const double* s2_h = sigma2 + h * K * dr;
+        const double* pi_h = pi + h * K;
+        double* s = (double*)malloc((size_t)K * sizeof(double));
+        double* g = (double*)malloc((size_t)K * sizeof(double));
+        double* Vt = (double*)calloc((size_t)(K * dv), sizeof(double));
+        double* Z = (double*)calloc((size_t)K, sizeof(double));
+        if (!s || !g || !Vt || !Z) {
+            failed = 1;
+        } else {
+            /* write: Eq. 6 over the context positions */
+            for (int64_t j = 0; j < Nk; ++j) {
+                responsibilities_one(XK + (p * Nk + j) * dr, dr, mu_h, s2_h, pi_h, K, s, g);
+                const double* vj = V + (p * Nk + j) * dv;
+                for (int64_t k = 0; k < K; ++k) {
+                    for (int64_t c = 0; c < dv; ++c) Vt[k * dv + c] += g[k] * vj[c];
+                    Z[k] += g[k];
+                }
+            }
+            /* read: Eq. 8 for every query position */
+            for (int64_t i = 0; i < Nq; ++i) {
+                responsibilities_one(XQ + (p * Nq + i) * dr, dr, mu_h, s2_h, pi_h, K, s, g);
+                double den = 0.0;
+                for (int64_t k = 0; k < K; ++k) den += g[k] * Z[k];
+                den += eps;
+                double* oi = O + (p * Nq + i) * dv;
+                for (int64_t c = 0; c < dv; ++c) {
+                    double num = 0.0;
+                    for (int64_t k = 0; k < K; ++k) num += g[k] * Vt[k * dv + c];
+                    oi[c] = num / den;
+                }
+            }
+        }
+        free(s); free(g); free(Vt); free(Z);
+    }
+    return failed ? -2 : 0;
+}
+
+/*
  * Causal GMA (Sec. 3.5).
  *   Prefix memory, Eq. 6b:  Vt^(i)_k = sum_{j<=i} gammaK_jk V_j,  Z^(i)_k = sum_{j<=i} gammaK_jk
  *   Output, Eq. 8b:         O_i = sum_k gammaQ_ik Vt^(i)_k / (sum_k gammaQ_ik Z^(i)_k + eps)

@@ -343,3 +343,79 @@ def test_empty_sequence_is_noop():
     xq, xk, v, mu, s2, pi = rand_problem(rng, 1, 2, 0, 3, 4, 5)
     assert oracle.forward_bidir(xq, xk, v, mu, s2, pi, 1e-6).shape == (1, 2, 0, 4)
     assert oracle.forward_causal(xq, xk, v, mu, s2, pi, 1e-6).shape == (1, 2, 0, 4)
+
+
+# --------------------------------------------------------------------------- cross-attention
+
+def rand_cross(rng, B, H, Nq, Nk, dr, dv, K):
+    """Queries from one sequence (Nq rows), keys and values from a context (Nk rows)."""
+    xq, _, _, mu, s2, pi = rand_problem(rng, B, H, Nq, dr, dv, K)
+    _, xk, v, _, _, _ = rand_problem(rng, B, H, Nk, dr, dv, K)
+    return xq, xk, v, mu, s2, pi
+
+
+@pytest.mark.parametrize("sizes", [(1, 1, 5, 9, 2, 3, 2), (2, 3, 13, 4, 4, 5, 3), (1, 2, 1, 20, 3, 2, 6),
+                                   (2, 1, 17, 1, 2, 3, 4)])
+def test_cross_matches_explicit_affinity(sizes):
+    """Cross-attention (Sec. 3): the associative form (Eq. 5-8 with the context writing
+    and the queries reading) equals the explicit Nq x Nk normalised affinity (Eq. 9-11)
+    built through Eq. 2-3 directly."""
+    rng = np.random.default_rng(30)
+    xq, xk, v, mu, s2, pi = rand_cross(rng, *sizes)
+    for eps in (1e-6, 0.3):
+        O = oracle.forward_cross(xq, xk, v, mu, s2, pi, eps)
+        assert O.shape == xq.shape[:3] + (v.shape[-1],)
+        np.testing.assert_allclose(O, oracle.brute.forward_cross(xq, xk, v, mu, s2, pi, eps),
+                                   rtol=1e-11, atol=1e-13)
+
+
+@settings(max_examples=25, deadline=None)
+@given(B=st.integers(1, 2), H=st.integers(1, 3), Nq=st.integers(1, 12), Nk=st.integers(1, 12),
+       dr=st.integers(1, 4), dv=st.integers(1, 4), K=st.integers(1, 5), seed=st.integers(0, 10**6))
+def test_property_cross_equals_explicit(B, H, Nq, Nk, dr, dv, K, seed):
+    """Random tiny shapes with Nq != Nk in general: oracle == explicit form."""
+    rng = np.random.default_rng(seed)
+    xq, xk, v, mu, s2, pi = rand_cross(rng, B, H, Nq, Nk, dr, dv, K)
+    np.testing.assert_allclose(oracle.forward_cross(xq, xk, v, mu, s2, pi, 1e-6),
+                               oracle.brute.forward_cross(xq, xk, v, mu, s2, pi, 1e-6),
+                               rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.5])
+def test_cross_single_component_is_context_mean(eps):
+    """K = 1: Z = Nk and every query reads sum_j V_j / (Nk + eps), the context mean."""
+    rng = np.random.default_rng(31)
+    xq, xk, v, mu, s2, pi = rand_cross(rng, 2, 2, 9, 23, 3, 5, 1)
+    O = oracle.forward_cross(xq, xk, v, mu, s2, pi, eps)
+    ref = v.sum(axis=2, keepdims=True) / (23 + eps)
+    np.testing.assert_allclose(O, np.broadcast_to(ref, O.shape), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("eps", [1e-6, 2.5])
+def test_cross_constant_values_closed_form(eps):
+    """Constant context values c: Vt = Z c^T, so O_i = c s_i / (s_i + eps) with
+    s_i = gammaQ_i . Z and Z the context's responsibility mass (Eq. 6-7)."""
+    rng = np.random.default_rng(32)
+    B, H, Nq, Nk, dr, dv, K = 2, 2, 11, 30, 3, 4, 6
+    xq, xk, _, mu, s2, pi = rand_cross(rng, B, H, Nq, Nk, dr, dv, K)
+    c = rng.standard_normal(dv)
+    v = np.broadcast_to(c, (B, H, Nk, dv)).copy()
+    O = oracle.forward_cross(xq, xk, v, mu, s2, pi, eps)
+    s = np.einsum("bhnk,bhk->bhn", oracle.responsibilities(xq, mu, s2, pi),
+                  oracle.responsibilities(xk, mu, s2, pi).sum(axis=2))
+    np.testing.assert_allclose(O, c * (s / (s + eps))[..., None], rtol=1e-12, atol=1e-14)
+
+
+def test_cross_permutation_symmetries_and_empty_context():
+    """Query permutation permutes the output rows; a joint permutation of the context's
+    keys and values leaves O unchanged; an empty context gives Vt = 0, Z = 0, O = 0."""
+    rng = np.random.default_rng(33)
+    xq, xk, v, mu, s2, pi = rand_cross(rng, 1, 2, 8, 14, 3, 4, 5)
+    O = oracle.forward_cross(xq, xk, v, mu, s2, pi, 1e-6)
+    pq, pk = rng.permutation(8), rng.permutation(14)
+    np.testing.assert_allclose(oracle.forward_cross(xq[:, :, pq], xk, v, mu, s2, pi, 1e-6), O[:, :, pq],
+                               rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(oracle.forward_cross(xq, xk[:, :, pk], v[:, :, pk], mu, s2, pi, 1e-6), O,
+                               rtol=1e-11, atol=1e-13)
+    O0 = oracle.forward_cross(xq, xk[:, :, :0], v[:, :, :0], mu, s2, pi, 1e-6)
+    assert O0.shape == (1, 2, 8, 4) and not O0.any()
