@@ -24,7 +24,8 @@ STATUS_NAMES = ["GMA_OK", "GMA_ERR_NULL_POINTER", "GMA_ERR_BAD_SHAPE", "GMA_ERR_
 GMA_F32, GMA_BF16 = 0, 1
 GMA_OP_RESPONSIBILITIES, GMA_OP_BIDIR, GMA_OP_CAUSAL = 0, 1, 2
 EXPORTED = ["gma_status_string", "gma_workspace_size", "gma_responsibilities", "gma_forward_bidir",
-            "gma_forward_causal", "gma_profiling", "gma_profiling_collect", "gma_set_wait_limit"]
+            "gma_forward_causal", "gma_cross_workspace_size", "gma_forward_cross", "gma_profiling",
+            "gma_profiling_collect", "gma_set_wait_limit"]
 WAIT_LIMIT_DEFAULT = 1 << 18  # GMA_WAIT_LIMIT_DEFAULT
 
 
@@ -41,6 +42,11 @@ class KernelStat(ctypes.Structure):
 
 class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("d_r", ctypes.c_int64), ("d_v", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class CrossShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N_q", ctypes.c_int64), ("N_k", ctypes.c_int64),
                 ("d_r", ctypes.c_int64), ("d_v", ctypes.c_int64), ("K", ctypes.c_int64)]
 
 
@@ -69,6 +75,11 @@ def load() -> ctypes.CDLL:
             lib.gma_forward_bidir.restype = i32
             lib.gma_forward_causal.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, shp, i32, vp, sz, vp]
             lib.gma_forward_causal.restype = i32
+            xshp = ctypes.POINTER(CrossShape)
+            lib.gma_cross_workspace_size.argtypes = [xshp, i32, ctypes.POINTER(sz)]
+            lib.gma_cross_workspace_size.restype = i32
+            lib.gma_forward_cross.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, xshp, vp, sz, vp]
+            lib.gma_forward_cross.restype = i32
             lib.gma_profiling.argtypes = [ctypes.c_int]
             lib.gma_profiling.restype = i32
             lib.gma_profiling_collect.argtypes = [ctypes.POINTER(KernelStat), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
@@ -176,6 +187,33 @@ def gma_forward_causal(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, mu: 
                                      float(eps), _ptr(out), ctypes.byref(Shape(B, H, N, dr, dv, K)),
                                      int(chunk), _ptr(ws), ws.numel(), _stream(stream)),
            "gma_forward_causal")
+    return out
+
+
+def gma_cross_workspace_size(B: int, H: int, N_q: int, N_k: int, d_r: int, d_v: int, K: int, io_dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().gma_cross_workspace_size(ctypes.byref(CrossShape(B, H, N_q, N_k, d_r, d_v, K)), io_dtype,
+                                           ctypes.byref(out)), "gma_cross_workspace_size")
+    return int(out.value)
+
+
+def gma_forward_cross(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, mu: torch.Tensor,
+                      sigma2: torch.Tensor, pi: torch.Tensor, eps: float = 1e-6,
+                      out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Cross-attention GMA O [B,H,N_q,d_v]: queries xq [B,H,N_q,d_r] read the memory written by
+    the context xk [B,H,N_k,d_r], v [B,H,N_k,d_v] (Sec. 3, Eq. 5-8)."""
+    B, H, Nq, dr = xq.shape
+    Nk, dv = xk.shape[2], v.shape[-1]
+    K = mu.shape[1]
+    io = _dtype_code(xq.dtype)
+    if out is None:
+        out = torch.empty(B, H, Nq, dv, dtype=xq.dtype, device=xq.device)
+    shape = CrossShape(B, H, Nq, Nk, dr, dv, K)
+    ws = _workspace(gma_cross_workspace_size(B, H, Nq, Nk, dr, dv, K, io), xq.device, workspace)
+    _check(load().gma_forward_cross(_ptr(xq), _ptr(xk), _ptr(v), io, _ptr(mu), _ptr(sigma2), _ptr(pi),
+                                    float(eps), _ptr(out), ctypes.byref(shape), _ptr(ws), ws.numel(),
+                                    _stream(stream)), "gma_forward_cross")
     return out
 
 

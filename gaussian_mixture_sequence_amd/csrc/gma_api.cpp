@@ -42,12 +42,14 @@ gma_status_t check_dims(gma_op_t op, const gma_shape_t& s, gma_dtype_t io) {
     }
     // guard the int64 products used for sizes
     const int64_t lim = int64_t(1) << 40;
-    if (s.B > lim || s.H > lim || s.N > lim || (s.B * s.H) > lim || (s.B * s.H) * s.N > lim)
+    if (s.B > lim || s.H > lim || s.N > lim || (s.B * s.H) > lim || (s.B * s.H > 0 && s.N > lim / (s.B * s.H)))
         return GMA_ERR_BAD_SHAPE;
     return GMA_OK;
 }
 
 }  // namespace
+
+void layout(Plan* pl);
 
 gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_t chunk, Plan* pl) {
     if (op != GMA_OP_RESPONSIBILITIES && op != GMA_OP_BIDIR && op != GMA_OP_CAUSAL)
@@ -94,6 +96,18 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
         p.seg = round_up(size_t(cdiv(p.N, best_g)), kTokenTile);
         p.G = cdiv(p.N, p.seg);
     }
+    p.Nq = p.N;
+    p.seg_q = p.seg;
+    layout(&p);
+    *pl = p;
+    return GMA_OK;
+}
+
+// Workspace regions of a plan whose op, sizes and split are set.
+void layout(Plan* pl) {
+    Plan& p = *pl;
+    const gma_op_t op = p.op;
+    const gma_dtype_t io = p.io;
     const size_t mem_elems = size_t(p.Kp) * size_t(p.dv + 1);
     p.partials_bytes = (op == GMA_OP_RESPONSIBILITIES) ? 0 : round_up(size_t(p.P * p.G) * mem_elems * 4, 256);
     p.memory_bytes = (op == GMA_OP_BIDIR) ? round_up(size_t(p.P) * mem_elems * 4, 256) : 0;
@@ -106,6 +120,28 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
     p.off_memory = p.off_partials + p.partials_bytes;
     p.off_flags = p.off_memory + p.memory_bytes;
     p.total = p.off_flags + p.flags_bytes;
+}
+
+gma_status_t make_cross_plan(const gma_cross_shape_t& s, gma_dtype_t io, Plan* pl) {
+    const gma_shape_t sk{s.B, s.H, s.N_k, s.d_r, s.d_v, s.K};
+    Plan p;
+    gma_status_t st = make_plan(GMA_OP_BIDIR, sk, io, 0, &p);
+    if (st != GMA_OK) return st;
+    const int64_t lim = int64_t(1) << 40;
+    if (s.N_q < 0) return GMA_ERR_BAD_SHAPE;
+    if (s.N_q > lim || (p.P > 0 && s.N_q > lim / p.P)) return GMA_ERR_BAD_SHAPE;
+    // one split count for both sides, from the longer one; a split may be empty on one side
+    p.Nq = s.N_q;
+    p.G = 1;
+    if (p.P > 0) {
+        const int64_t n = std::max(p.N, p.Nq);
+        p.G = std::max<int64_t>(1, std::min(cdiv(kBidirBlocks, p.P), cdiv(std::max<int64_t>(n, 1), 512)));
+    }
+    p.seg = round_up(size_t(cdiv(std::max<int64_t>(p.N, 1), p.G)), kTokenTile);
+    p.seg_q = round_up(size_t(cdiv(std::max<int64_t>(p.Nq, 1), p.G)), kTokenTile);
+    // no split that is empty on both sides (with N_q = N_k this is the bidirectional plan)
+    p.G = std::max<int64_t>(1, std::max(cdiv(p.N, p.seg), cdiv(p.Nq, p.seg_q)));
+    layout(&p);
     *pl = p;
     return GMA_OK;
 }
@@ -276,6 +312,39 @@ gma_status_t gma_forward_causal(const void* XQ, const void* XK, const void* V, g
                                 size_t workspace_bytes, hipStream_t stream) {
     return forward_common(GMA_OP_CAUSAL, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, O, shape, chunk,
                           workspace, workspace_bytes, stream);
+}
+
+gma_status_t gma_cross_workspace_size(const gma_cross_shape_t* shape, gma_dtype_t io_dtype, size_t* bytes_out) {
+    if (!shape || !bytes_out) return GMA_ERR_NULL_POINTER;
+    Plan p;
+    gma_status_t st = gma::make_cross_plan(*shape, io_dtype, &p);
+    if (st != GMA_OK) return st;
+    *bytes_out = p.total;
+    return GMA_OK;
+}
+
+gma_status_t gma_forward_cross(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                               const float* mu, const float* sigma2, const float* pi, float eps, void* O,
+                               const gma_cross_shape_t* shape, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+    if (!mu || !sigma2 || !pi || !shape) return GMA_ERR_NULL_POINTER;
+    Plan p;
+    gma_status_t st = gma::make_cross_plan(*shape, io_dtype, &p);
+    if (st != GMA_OK) return st;
+    // a side without rows may come without storage
+    if ((!XQ || !O) && p.P > 0 && p.Nq > 0) return GMA_ERR_NULL_POINTER;
+    if ((!XK || !V) && p.P > 0 && p.N > 0) return GMA_ERR_NULL_POINTER;
+    if (!(eps > 0.0f) || !std::isfinite(eps)) return GMA_ERR_BAD_VALUE;
+    for (const void* q : {XQ, XK, V, (const void*)mu, (const void*)sigma2, (const void*)pi, (const void*)O})
+        if (!gma::aligned16(q)) return GMA_ERR_MISALIGNED;
+    if ((st = check_ws(p, workspace, workspace_bytes)) != GMA_OK) return st;
+    if (p.P == 0 || p.Nq == 0) return GMA_OK;  // no output rows (an empty context still yields zeros)
+    char* ws = static_cast<char*>(workspace);
+    if (io_dtype == GMA_F32)
+        return launch_status(gma::f32_bidir(p, static_cast<const float*>(XQ), static_cast<const float*>(XK),
+                                            static_cast<const float*>(V), mu, sigma2, pi, eps, static_cast<float*>(O),
+                                            ws, stream));
+    return launch_status(gma::bf16_bidir(p, XQ, XK, V, mu, sigma2, pi, eps, O, ws, stream));
 }
 
 gma_status_t gma_set_wait_limit(uint32_t polls) {

@@ -374,8 +374,10 @@ __device__ __forceinline__ void read_body(char* __restrict__ smem, const uint16_
 
 // ---------------------------------------------------------------------------- bidirectional forward
 
-// One launch for the whole bidirectional forward.  Grid (G, P); workgroup (g, p) owns rows
-// [g seg, (g + 1) seg) of problem p:
+// One launch for the whole bidirectional forward.  Grid (G, P); workgroup (g, p) owns key
+// rows [g seg, (g + 1) seg) and query rows [g seg_q, (g + 1) seg_q) of problem p (the same
+// rows unless the queries come from another sequence than the keys, as in cross-attention;
+// either range may then be empty):
 //   1. write: the partial [Vt^T | Z] of its rows (write_body, operand planes built once);
 //   2. read phase (read_body, same planes): its first x tiles committed and round 0's
 //      scores issued, which need no memory;
@@ -389,7 +391,7 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(WriteLds<DR, KT, VT>::bytes > R
                                                       ? WriteLds<DR, KT, VT>::bytes
                                                       : ReadLds<DR, KT, VT>::bytes))))
     bidir_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
-                 int64_t N, int H, int64_t seg, int G, Mixture mx, float* __restrict__ partials,
+                 int64_t N, int64_t Nq, int H, int64_t seg, int64_t seg_q, int G, Mixture mx, float* __restrict__ partials,
                  uint16_t* __restrict__ memory, uint64_t* __restrict__ flags, uint64_t token,
                  uint32_t wait_limit, float eps, uint16_t* __restrict__ O) {
     using WL = WriteLds<DR, KT, VT>;
@@ -398,7 +400,8 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(WriteLds<DR, KT, VT>::bytes > R
     constexpr int Kp = KT * 32, DV = VT * 32, E = Kp * (DV + 1), NT = Split<DR, KT>::NW * 64;
     const int64_t p = blockIdx.y;
     const int g = blockIdx.x, h = int(p % H);
-    const int64_t lo = int64_t(g) * seg, hi = min<int64_t>(lo + seg, N);
+    const int64_t lo = min<int64_t>(int64_t(g) * seg, N), hi = min<int64_t>(lo + seg, N);
+    const int64_t lo_q = min<int64_t>(int64_t(g) * seg_q, Nq), hi_q = min<int64_t>(lo_q + seg_q, Nq);
     float* part = partials + size_t(p) * G * E;
     uint16_t* mem = memory + size_t(p) * E * 2;
     uint64_t* fl = flags + size_t(p) * 2 * G;
@@ -407,7 +410,7 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(WriteLds<DR, KT, VT>::bytes > R
     write_body<DR, KT, VT, true>(smem, XK, V, N, p, h, lo, hi, mx, P, part + size_t(g) * E);
     publish_token(fl + g, token);  // its barrier also frees the write phase's LDS
     bool ok = true;
-    read_body<DR, KT, VT, false>(smem, XQ, N, p, h, lo, hi, mx, P, mem, eps, O, [&] {
+    read_body<DR, KT, VT, false>(smem, XQ, Nq, p, h, lo_q, hi_q, mx, P, mem, eps, O, [&] {
         // behind the read phase's first tiles and scores: complete the memory
         ok = wait_tokens(fl, G, token, wait_limit);
         const int per = (E / 4 + G - 1) / G;  // 16-byte groups per slice
@@ -420,8 +423,8 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(WriteLds<DR, KT, VT>::bytes > R
     if (!ok) {  // the memory was never complete: make that visible in the output
         __builtin_amdgcn_s_waitcnt(0);  // the phase's own stores of these rows land first
         __syncthreads();
-        uint16_t* op = O + (size_t(p) * N + lo) * DV;
-        for (int64_t e = threadIdx.x; e < (hi - lo) * DV; e += NT) op[e] = 0x7fc0u;
+        uint16_t* op = O + (size_t(p) * Nq + lo_q) * DV;
+        for (int64_t e = threadIdx.x; e < (hi_q - lo_q) * DV; e += NT) op[e] = 0x7fc0u;
     }
 }
 
@@ -500,7 +503,8 @@ hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void*
             using S = bf::Split<DR, KT>;
             GMA_LAUNCH("bf16_bidir", (bf::bidir_kernel<DR, KT, VT>), dim3(unsigned(p.G), unsigned(p.P)),
                        dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
-                       static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), mx, partials, memory, flags,
+                       static_cast<const uint16_t*>(V), p.N, p.Nq, int(p.H), p.seg, p.seg_q, int(p.G), mx, partials,
+                       memory, flags,
                        token, wait_limit(), eps, static_cast<uint16_t*>(O));
             return hipGetLastError();
         });

@@ -379,8 +379,8 @@ hipError_t f32_bidir(const Plan& p, const float* XQ, const float* XK, const floa
                        dim3(kThreads), 0, st, partials, int(p.G), E, memory);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     size_t lds_r = size_t(kTile) * (p.dr + p.K + 1) * sizeof(float);
-    GMA_LAUNCH("f32_read", f32_read_kernel, dim3(unsigned((p.N + kTile - 1) / kTile), unsigned(p.P)),
-                       dim3(kThreads), lds_r, st, XQ, p.N, int(p.H), int(p.dr), int(p.dv), int(p.K), v.c,
+    GMA_LAUNCH("f32_read", f32_read_kernel, dim3(unsigned((p.Nq + kTile - 1) / kTile), unsigned(p.P)),
+                       dim3(kThreads), lds_r, st, XQ, p.Nq, int(p.H), int(p.dr), int(p.dv), int(p.K), v.c,
                        v.inv, mu, memory, eps, O);
     return hipGetLastError();
 }

@@ -22,10 +22,12 @@ struct Plan {
     gma_op_t op;
     gma_dtype_t io;
     int64_t B, H, N, dr, dv, K;
+    int64_t Nq;           // query rows: N, except for cross-attention (N is then the context length)
     int64_t P;            // B * H independent (batch, head) problems
     int64_t Kp;           // K padded to the MFMA component tile (bf16) or K (f32)
     int64_t G;            // sequence splits per problem (write partials / causal segments)
     int64_t seg;          // tokens per split (multiple of the token tile)
+    int64_t seg_q;        // query rows per split of the read (seg, except for cross-attention)
     int32_t chunk;        // causal chunk length
     // byte offsets into the workspace
     size_t off_params, off_partials, off_memory, off_flags, total;
@@ -55,6 +57,9 @@ void trace_end(hipStream_t st);
 
 // Fills `plan`; returns GMA_OK or the validation error for unsupported sizes.
 gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_t chunk, Plan* plan);
+// Cross-attention plan: a bidirectional plan over the context (N = N_k) whose read covers
+// N_q query rows in the same number of splits.
+gma_status_t make_cross_plan(const gma_cross_shape_t& s, gma_dtype_t io, Plan* plan);
 
 // ---- fp32 path (gma_f32.hip) ---------------------------------------------------
 hipError_t f32_responsibilities(const Plan& p, const float* X, const float* mu, const float* s2,

@@ -9,8 +9,8 @@ Draw order for one input set (one ``torch.Generator`` seeded once):
   2. omega  = randn(H, K, d_r);  sigma2 = softplus(omega) + 1e-3
   3. alpha  = randn(H, K);       pi = softmax(alpha) per head
   4. XQ = randn(B, H, N, d_r)
-  5. XK = randn(B, H, N, d_r)
-  6. V  = randn(B, H, N, d_v)
+  5. XK = randn(B, H, N, d_r)      (N_k = n_ctx rows instead of N for cross-attention)
+  6. V  = randn(B, H, N, d_v)      (likewise)
 Parameters stay fp32; XQ, XK, V are rounded to the I/O dtype (round-to-nearest-even
 for bf16).  Every tensor is contiguous and on the CPU.
 """
@@ -40,6 +40,7 @@ class Workload:
     mu_std: float = 1.0
     seed: int = 0
     chunk: int = 64     # causal chunk length (ignored by the bidirectional variant)
+    n_ctx: int = -1     # cross-attention: context length N_k of XK and V (N is then N_q); -1: self
 
     @property
     def tokens(self) -> int:
@@ -48,6 +49,14 @@ class Workload:
     @property
     def head_rows(self) -> int:
         return self.B * self.H * self.N
+
+    @property
+    def cross(self) -> bool:
+        return self.n_ctx >= 0
+
+    @property
+    def n_keys(self) -> int:
+        return self.n_ctx if self.cross else self.N
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -63,6 +72,10 @@ WORKLOADS: Dict[str, Workload] = {
                                   mu_std=1.5, seed=3),
     "causal_long_n32768": Workload("causal_long_n32768", True, 2, 16, 32768, 64, 128, 256, "bf16",
                                    seed=4),
+    # cross-attention (no workload is given for it): the B=8, H=8 bidirectional dims with
+    # 4096 queries reading a context four times as long
+    "cross_b8h8_q4096_k16384": Workload("cross_b8h8_q4096_k16384", False, 8, 8, 4096, 64, 64, 64, "bf16",
+                                        seed=5, n_ctx=16384),
 }
 WORKLOAD_ORDER = ["bidir_small_f32", "bidir_b8h8_n4096", "causal_b8h12_n2048",
                   "bidir_long_n65536", "causal_long_n32768"]
@@ -88,8 +101,9 @@ def make_inputs(w: Workload, seed: int | None = None) -> Dict[str, torch.Tensor]
     mu, sigma2, pi = make_params(w.H, w.K, w.d_r, w.mu_std, gen)
     dt = torch_dtype(w.dtype)
     xq = torch.randn(w.B, w.H, w.N, w.d_r, generator=gen, dtype=torch.float32).to(dt)
-    xk = torch.randn(w.B, w.H, w.N, w.d_r, generator=gen, dtype=torch.float32).to(dt)
-    v = torch.randn(w.B, w.H, w.N, w.d_v, generator=gen, dtype=torch.float32).to(dt)
+    nk = w.n_keys  # the context length for cross-attention
+    xk = torch.randn(w.B, w.H, nk, w.d_r, generator=gen, dtype=torch.float32).to(dt)
+    v = torch.randn(w.B, w.H, nk, w.d_v, generator=gen, dtype=torch.float32).to(dt)
     return {"xq": xq.contiguous(), "xk": xk.contiguous(), "v": v.contiguous(),
             "mu": mu, "sigma2": sigma2, "pi": pi}
 

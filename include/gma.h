@@ -148,6 +148,30 @@ gma_status_t gma_forward_causal(const void* XQ, const void* XK, const void* V,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Cross-attention (Sec. 3, "Cross-attention"): queries are formed from a query-side
+ * sequence X and keys and values from a separate context sequence Y; the routing of
+ * Sec. 3.3 is applied with Gamma^Q of X and Gamma^K of Y, through the same mixture:
+ *   Vt = Gamma_K^T V,  Z = Gamma_K^T 1_{Nk},  O_i = (Gamma_Q Vt)_i / ((Gamma_Q Z)_i + eps)
+ * Sizes are given by gma_cross_shape_t: N_q query rows, N_k context rows.
+ *   XQ [B,H,N_q,d_r], XK [B,H,N_k,d_r], V [B,H,N_k,d_v], O [B,H,N_q,d_v] out, in io_dtype.
+ * N_q, N_k >= 0.  An empty context (N_k = 0, N_q > 0) is valid: Vt = 0 and Z = 0, so every
+ * output row is 0.  XK and V may be NULL when N_k = 0, XQ and O when N_q = 0.  With N_q = N_k = N this is gma_forward_bidir.  Conventions, dtypes,
+ * supported d_r, d_v, K, errors and the workspace contract are those of gma_forward_bidir;
+ * the workspace size comes from gma_cross_workspace_size.  With bf16 I/O the forward is one
+ * launch (same hand-off scheme as gma_forward_bidir).
+ */
+typedef struct {
+    int64_t B, H, N_q, N_k, d_r, d_v, K;
+} gma_cross_shape_t;
+
+gma_status_t gma_cross_workspace_size(const gma_cross_shape_t* shape, gma_dtype_t io_dtype, size_t* bytes_out);
+
+gma_status_t gma_forward_cross(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                               const float* mu, const float* sigma2, const float* pi, float eps,
+                               void* O, const gma_cross_shape_t* shape,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Kernel timing (optional tracing).  While enabled, every kernel the library launches is
  * bracketed by a pair of hipEvents recorded on the launch stream; gma_profiling_collect
  * waits for the recorded events, adds each launch's elapsed time to a per-kernel total,

@@ -132,3 +132,62 @@ def test_responsibilities_argument_errors(lib):
     assert f(FAKE, 0, FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(sh), FAKE, need - 1, None) == WS
     empty = gb.Shape(1, 1, 0, 16, 1, 8)
     assert f(FAKE, 0, FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(empty), FAKE, need, None) == OK
+
+
+def cross_ws(B, H, Nq, Nk, dr, dv, K, io):
+    out = ctypes.c_size_t(0)
+    st = gb.load().gma_cross_workspace_size(ctypes.byref(gb.CrossShape(B, H, Nq, Nk, dr, dv, K)), io,
+                                            ctypes.byref(out))
+    return st, out.value
+
+
+def call_cross(lib, xq=FAKE, xk=FAKE, v=FAKE, io=gb.GMA_F32, eps=1e-6, o=FAKE, shape=(1, 1, 64, 96, 16, 32, 8),
+               ws=FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = cross_ws(*shape, io)[1]
+    return lib.gma_forward_cross(xq, xk, v, io, FAKE, FAKE, FAKE, eps, o, ctypes.byref(gb.CrossShape(*shape)), ws,
+                                 ws_bytes, None)
+
+
+def test_cross_workspace_size_validation(lib):
+    F, BF = gb.GMA_F32, gb.GMA_BF16
+    assert cross_ws(8, 8, 4096, 16384, 64, 64, 64, BF)[0] == OK
+    assert cross_ws(1, 1, 0, 0, 16, 32, 8, F)[0] == OK
+    assert cross_ws(1, 1, -1, 8, 16, 32, 8, F)[0] == SHAPE
+    assert cross_ws(1, 1, 8, -1, 16, 32, 8, F)[0] == SHAPE
+    assert cross_ws(1, 1, 1 << 41, 8, 16, 32, 8, F)[0] == SHAPE
+    assert cross_ws(1 << 20, 1 << 10, 1 << 11, 8, 16, 32, 8, F)[0] == SHAPE   # B*H*N_q beyond 2^40
+    assert cross_ws(1, 1, 8, 8, 24, 32, 8, BF)[0] == UNSUP
+    assert cross_ws(1, 1, 8, 8, 16, 32, 0, F)[0] == UNSUP
+    assert lib.gma_cross_workspace_size(None, F, ctypes.byref(ctypes.c_size_t())) == NULLP
+    # with N_q = N_k the plan is the bidirectional one
+    assert cross_ws(4, 4, 4096, 4096, 32, 64, 128, BF)[1] == ws_size(gb.GMA_OP_BIDIR, 4, 4, 4096, 32, 64, 128, BF)[1]
+    # scratch stops growing with either length
+    sizes = [cross_ws(4, 4, nq, nk, 32, 64, 128, BF)[1] for nq, nk in ((65536, 1 << 18), (1 << 20, 65536), (1 << 20, 1 << 20))]
+    assert sizes[0] == sizes[1] == sizes[2], sizes
+
+
+def test_cross_argument_errors(lib):
+    assert call_cross(lib, xq=None) == NULLP
+    assert call_cross(lib, xk=None) == NULLP
+    assert call_cross(lib, o=None) == NULLP
+    assert call_cross(lib, ws=None) == NULLP
+    assert call_cross(lib, eps=0.0) == VALUE
+    assert call_cross(lib, eps=float("nan")) == VALUE
+    assert call_cross(lib, io=3) == VALUE
+    assert call_cross(lib, shape=(1, 1, -3, 96, 16, 32, 8), ws_bytes=1 << 20) == SHAPE
+    assert call_cross(lib, shape=(1, 1, 64, 96, 16, 32, 300), ws_bytes=1 << 20) == UNSUP
+    assert call_cross(lib, v=FAKE + 4) == MISAL
+    need = cross_ws(1, 1, 64, 96, 16, 32, 8, gb.GMA_F32)[1]
+    assert need > 0 and call_cross(lib, ws_bytes=need - 1) == WS
+
+
+def test_cross_without_output_rows_enqueues_nothing(lib):
+    """No query rows (or no problems) is valid and returns before any HIP call."""
+    for shape in [(1, 1, 0, 96, 16, 32, 8), (0, 2, 64, 96, 16, 32, 8), (1, 1, 0, 0, 16, 32, 8)]:
+        for io in (gb.GMA_F32, gb.GMA_BF16):
+            assert call_cross(lib, shape=shape, io=io) == OK
+    # a side without rows may come without storage; a side with rows may not
+    assert call_cross(lib, xq=None, o=None, shape=(1, 1, 0, 96, 16, 32, 8)) == OK
+    assert call_cross(lib, xk=None, v=None, shape=(1, 1, 0, 0, 16, 32, 8)) == OK
+    assert call_cross(lib, xk=None, shape=(1, 1, 0, 96, 16, 32, 8)) == NULLP
