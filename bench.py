@@ -46,11 +46,22 @@ def parse():
                          "known size (calibration) or three steps of the benchmark")
     ap.add_argument("--traffic-summarize", metavar="DIR", default=None,
                     help="turn the counter CSVs of the four probe runs under DIR into profiles/traffic.json")
+    ap.add_argument("--trace-summarize", metavar="DIR", default=None,
+                    help="summarise the library kernels of a rocprofv3 --kernel-trace --stats run of this script "
+                         "(CSV output under DIR) into --trace-out")
+    ap.add_argument("--trace-out", metavar="FILE", default=None)
+    ap.add_argument("--trace-command", default=None, help="the command that produced DIR, recorded in the summary")
     return ap.parse_args()
 
 
 COPY_BYTES = 1 << 29  # 512 MiB: larger than the 256 MiB Infinity Cache, so the copy streams HBM
-TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def traffic_json(workloads: str) -> str:
+    """Where the calibrated HBM traffic of a workload set is kept (one file per set)."""
+    if workloads == ",".join(DEFAULT_STEP):
+        return os.path.join(ROOT, "profiles", "traffic.json")
+    return os.path.join(ROOT, "profiles", "traffic_%s.json" % workloads.replace(",", "+"))
 
 
 def kernel_source_hash() -> str:
@@ -80,7 +91,7 @@ def traffic_probe(mode: str, args) -> int:
     return main(args, probe_only=True)
 
 
-def traffic_summarize(d: str) -> int:
+def traffic_summarize(d: str, workloads: str) -> int:
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the copy and of the step kernels, from the CSVs
     of four runs under d: copy_fetch, copy_write, step_fetch, step_write."""
     import csv
@@ -108,7 +119,8 @@ def traffic_summarize(d: str) -> int:
             continue
         fb, wb = sf.get(k, 0.0) * f_fetch, sw.get(k, 0.0) * f_write
         kernels[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb), "hbm_bytes": round(fb + wb)}
-    res = {"source_sha256": kernel_source_hash(), "copy_kernel": copy_name, "copy_bytes": COPY_BYTES,
+    res = {"source_sha256": kernel_source_hash(), "workloads": workloads, "copy_kernel": copy_name,
+           "copy_bytes": COPY_BYTES,
            "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4), "kernels": kernels,
            "commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/copy_fetch -o copy_fetch -- "
                         "python bench.py --traffic-probe copy",
@@ -119,17 +131,61 @@ def traffic_summarize(d: str) -> int:
                         "rocprofv3 --pmc WRITE_SIZE --output-format csv -d DIR/step_write -o step_write -- "
                         "python bench.py --traffic-probe step",
                         "python bench.py --traffic-summarize DIR"]}
-    os.makedirs(os.path.dirname(TRAFFIC_JSON), exist_ok=True)
-    with open(TRAFFIC_JSON, "w") as f:
+    if workloads != ",".join(DEFAULT_STEP):
+        res["commands"] = [c.replace("--traffic-probe step", "--traffic-probe step --workloads " + workloads)
+                           .replace("--traffic-summarize DIR", "--traffic-summarize DIR --workloads " + workloads)
+                           for c in res["commands"]]
+    path = traffic_json(workloads)
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as f:
         json.dump(res, f, indent=1)
     print(json.dumps(res, indent=1))
     return 0
 
 
-def measured_traffic(kernel_symbol_prefix: str):
-    """HBM bytes per launch of the kernel, from profiles/traffic.json when it matches the sources."""
+def trace_summarize(d: str, out: str, workloads: str, command: str) -> int:
+    """Per-kernel launch statistics (microseconds, from rocprofv3 kernel timestamps) of the library's
+    kernels in a kernel-trace run under d, cross-checked against rocprofv3's own stats file."""
+    import csv
+    import glob
+    import re
+    import statistics
+    durs = {}
+    for f in glob.glob(os.path.join(d, "**", "*_kernel_trace.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            name = re.sub(r"\(.*", "", row["Kernel_Name"]).replace("void ", "")
+            if name.startswith("gma::"):
+                durs.setdefault(name, []).append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1000.0)
+    stats = {}
+    for f in glob.glob(os.path.join(d, "**", "*_kernel_stats.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            name = re.sub(r"\(.*", "", row["Name"]).replace("void ", "")
+            if name.startswith("gma::"):
+                stats[name] = float(row["AverageNs"]) / 1000.0
+    if not durs:
+        print("no library kernels in %s" % d, file=sys.stderr)
+        return 1
+    total = sum(sum(v) for v in durs.values())
+    lines = ["# Kernel trace summary: %s (bf16 unless the kernel name says otherwise)" % workloads,
+             "# command (run from the repository root on one MI355X):", "#   " + (command or "?"),
+             "# durations in microseconds from rocprofv3 kernel timestamps; library kernels only",
+             "%-44s %6s %9s %9s %9s %9s %7s" % ("kernel", "calls", "avg_us", "median_us", "min_us", "max_us", "pct")]
+    for name, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        lines.append("%-44s %6d %9.2f %9.2f %9.2f %9.2f %7.2f" % (
+            name, len(v), statistics.mean(v), statistics.median(v), min(v), max(v), 100.0 * sum(v) / total))
+    lines.append("# stats.csv averages (us): " + ", ".join("%s %.2f" % kv for kv in sorted(stats.items())))
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
+def measured_traffic(kernel_symbol_prefix: str, workloads: str):
+    """HBM bytes per launch of the kernel, from the workload set's traffic record when that record
+    was taken on the current kernel sources."""
     try:
-        with open(TRAFFIC_JSON) as f:
+        with open(traffic_json(workloads)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -142,8 +198,11 @@ def measured_traffic(kernel_symbol_prefix: str):
 
 
 def alg_bytes_per_token_head(w, kernel: str) -> float:
-    """Algorithmic HBM bytes per (token, head) that a kernel must move."""
+    """Algorithmic HBM bytes per (token, head) that a kernel must move (per query row for
+    cross-attention, with the context rows' share folded in)."""
     e = 2 if w.dtype == "bf16" else 4
+    if w.cross:  # X_K and V of N_k context rows in; X_Q of N_q rows in and O out
+        return e * (w.d_r + w.d_v) * (w.n_ctx + w.N) / max(w.N, 1)
     if kernel.endswith("_write") or kernel.endswith("_causal_aggregate"):
         return e * (w.d_r + w.d_v)          # X_K and V in
     if kernel.endswith("_read"):
@@ -154,13 +213,16 @@ def alg_bytes_per_token_head(w, kernel: str) -> float:
 
 
 KERNEL_SYMBOL = {"bf16_scan": "gma::bf::scan_kernel", "bf16_bidir": "gma::bf::bidir_kernel",
+                 "bf16_cross": "gma::bf::bidir_kernel",
                  "bf16_causal": "gma::bf::causal_kernel", "bf16_causal_aggregate": "gma::bf::write_kernel<64, 1"}
 
 
 def main(args=None, probe_only=False) -> int:
     args = args or parse()
     if args.traffic_summarize:
-        return traffic_summarize(args.traffic_summarize)
+        return traffic_summarize(args.traffic_summarize, args.workloads)
+    if args.trace_summarize:
+        return trace_summarize(args.trace_summarize, args.trace_out, args.workloads, args.trace_command)
     if args.traffic_probe and not probe_only:
         return traffic_probe(args.traffic_probe, args)
     if args.gpus != 1:
@@ -195,7 +257,10 @@ def main(args=None, probe_only=False) -> int:
         outs.append([torch.empty(w.B, w.H, w.N, w.d_v, dtype=dt, device=dev) for _ in range(args.sets)])
         op = gb.GMA_OP_CAUSAL if w.causal else gb.GMA_OP_BIDIR
         io = gb.GMA_BF16 if w.dtype == "bf16" else gb.GMA_F32
-        nbytes = gb.gma_workspace_size(op, w.B, w.H, w.N, w.d_r, w.d_v, w.K, io, w.chunk)
+        if w.cross:
+            nbytes = gb.gma_cross_workspace_size(w.B, w.H, w.N, w.n_ctx, w.d_r, w.d_v, w.K, io)
+        else:
+            nbytes = gb.gma_workspace_size(op, w.B, w.H, w.N, w.d_r, w.d_v, w.K, io, w.chunk)
         wss.append(torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev))
     stream = torch.cuda.current_stream()
 
@@ -206,6 +271,9 @@ def main(args=None, probe_only=False) -> int:
             if w.causal:
                 gb.gma_forward_causal(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps,
                                       chunk=w.chunk, out=outs[i][s], workspace=wss[i], stream=stream)
+            elif w.cross:
+                gb.gma_forward_cross(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps,
+                                     out=outs[i][s], workspace=wss[i], stream=stream)
             else:
                 gb.gma_forward_bidir(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps,
                                      out=outs[i][s], workspace=wss[i], stream=stream)
@@ -249,6 +317,7 @@ def main(args=None, probe_only=False) -> int:
     for w in ws_list:
         pre = "bf16" if w.dtype == "bf16" else "f32"
         ks = ["params", "scan", "causal_aggregate", "causal", "prefix"] if w.causal else \
+            ["params", "cross_write", "cross_combine", "cross_read", "cross"] if w.cross else \
             ["params", "write", "combine", "read", "bidir"]
         for k in ks:
             kernel_of.setdefault("%s_%s" % (pre, k), []).append(w)
@@ -268,7 +337,7 @@ def main(args=None, probe_only=False) -> int:
     roofline = None
     if dominant and "alg_GBps" in kernels[dominant]:
         ach = kernels[dominant]["alg_GBps"]
-        traffic = measured_traffic(KERNEL_SYMBOL.get(dominant, "?"))
+        traffic = measured_traffic(KERNEL_SYMBOL.get(dominant, "?"), args.workloads)
         roofline = {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
                     "avg_us": kernels[dominant]["avg_us"],
@@ -296,8 +365,9 @@ def main(args=None, probe_only=False) -> int:
         "data": "synthetic (seeded; mu~N(0,1), sigma2=softplus(N(0,1))+1e-3, pi=softmax(N(0,1)), "
                 "X_Q,X_K,V~N(0,1); %d rotating input sets)" % args.sets,
         "config": {
-            "workload": " + ".join("%s (%s B=%d H=%d N=%d d_r=%d d_v=%d K=%d%s)" % (
-                w.name, "causal" if w.causal else "bidir", w.B, w.H, w.N, w.d_r, w.d_v, w.K,
+            "workload": " + ".join("%s (%s B=%d H=%d %s d_r=%d d_v=%d K=%d%s)" % (
+                w.name, "causal" if w.causal else "cross" if w.cross else "bidir", w.B, w.H,
+                "N_q=%d N_k=%d" % (w.N, w.n_ctx) if w.cross else "N=%d" % w.N, w.d_r, w.d_v, w.K,
                 ", chunk=%d" % w.chunk if w.causal else "") for w in ws_list),
             "tokens_per_step": tokens_per_step,
             "eps": 1e-6,
@@ -319,7 +389,7 @@ def main(args=None, probe_only=False) -> int:
             cpu_inputs.append((w, {k: oracle._f64(v) for k, v in inp.items()}))
         tc = time.perf_counter()
         for w, d in cpu_inputs:
-            fn = oracle.forward_causal if w.causal else oracle.forward_bidir
+            fn = oracle.forward_causal if w.causal else oracle.forward_cross if w.cross else oracle.forward_bidir
             fn(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps)
         cpu_s = time.perf_counter() - tc
         result["cpu_baseline"] = {

@@ -132,6 +132,7 @@ gma_status_t make_cross_plan(const gma_cross_shape_t& s, gma_dtype_t io, Plan* p
     if (s.N_q > lim || (p.P > 0 && s.N_q > lim / p.P)) return GMA_ERR_BAD_SHAPE;
     // one split count for both sides, from the longer one; a split may be empty on one side
     p.Nq = s.N_q;
+    p.cross = true;
     p.G = 1;
     if (p.P > 0) {
         const int64_t n = std::max(p.N, p.Nq);

@@ -501,7 +501,7 @@ hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void*
         return bf::with_vt(int(p.dv / 32), [&](auto VV) {
             constexpr int VT = decltype(VV)::value;
             using S = bf::Split<DR, KT>;
-            GMA_LAUNCH("bf16_bidir", (bf::bidir_kernel<DR, KT, VT>), dim3(unsigned(p.G), unsigned(p.P)),
+            GMA_LAUNCH(p.cross ? "bf16_cross" : "bf16_bidir", (bf::bidir_kernel<DR, KT, VT>), dim3(unsigned(p.G), unsigned(p.P)),
                        dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
                        static_cast<const uint16_t*>(V), p.N, p.Nq, int(p.H), p.seg, p.seg_q, int(p.G), mx, partials,
                        memory, flags,

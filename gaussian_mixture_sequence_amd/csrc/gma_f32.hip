@@ -371,15 +371,15 @@ hipError_t f32_bidir(const Plan& p, const float* XQ, const float* XK, const floa
     float* memory = reinterpret_cast<float*>(ws + p.off_memory);
     const int E = int(p.K * (p.dv + 1));
     size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
-    GMA_LAUNCH("f32_write", f32_write_kernel, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads), lds_w, st, XK, V,
+    GMA_LAUNCH(p.cross ? "f32_cross_write" : "f32_write", f32_write_kernel, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads), lds_w, st, XK, V,
                        p.N, int(p.H), int(p.dr), int(p.dv), int(p.K), p.seg, int(p.G), v.c, v.inv, mu,
                        partials);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    GMA_LAUNCH("f32_combine", f32_combine_kernel, dim3(unsigned((E + kThreads - 1) / kThreads), unsigned(p.P)),
+    GMA_LAUNCH(p.cross ? "f32_cross_combine" : "f32_combine", f32_combine_kernel, dim3(unsigned((E + kThreads - 1) / kThreads), unsigned(p.P)),
                        dim3(kThreads), 0, st, partials, int(p.G), E, memory);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     size_t lds_r = size_t(kTile) * (p.dr + p.K + 1) * sizeof(float);
-    GMA_LAUNCH("f32_read", f32_read_kernel, dim3(unsigned((p.Nq + kTile - 1) / kTile), unsigned(p.P)),
+    GMA_LAUNCH(p.cross ? "f32_cross_read" : "f32_read", f32_read_kernel, dim3(unsigned((p.Nq + kTile - 1) / kTile), unsigned(p.P)),
                        dim3(kThreads), lds_r, st, XQ, p.Nq, int(p.H), int(p.dr), int(p.dv), int(p.K), v.c,
                        v.inv, mu, memory, eps, O);
     return hipGetLastError();

@@ -23,6 +23,7 @@ struct Plan {
     gma_dtype_t io;
     int64_t B, H, N, dr, dv, K;
     int64_t Nq;           // query rows: N, except for cross-attention (N is then the context length)
+    bool cross;           // cross-attention plan (queries and keys from different sequences)
     int64_t P;            // B * H independent (batch, head) problems
     int64_t Kp;           // K padded to the MFMA component tile (bf16) or K (f32)
     int64_t G;            // sequence splits per problem (write partials / causal segments)
