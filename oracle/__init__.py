@@ -60,6 +60,9 @@ def _load():
             fwd = [dp, dp, dp, i64, i64, i64, i64, i64, i64, dp, dp, dp, ctypes.c_double, dp]
             lib.oracle_forward_bidir.argtypes = fwd
             lib.oracle_forward_causal.argtypes = fwd
+            lib.oracle_forward_causal_state.argtypes = [dp, dp, dp, i64, i64, i64, i64, i64, i64, dp, dp, dp,
+                                                        ctypes.c_double, dp, dp, dp]
+            lib.oracle_forward_causal_state.restype = ctypes.c_int
             lib.oracle_forward_cross.argtypes = [dp, i64, dp, dp, i64, i64, i64, i64, i64, i64, dp, dp, dp,
                                                  ctypes.c_double, dp]
             for f in (lib.oracle_log_scores, lib.oracle_responsibilities,
@@ -147,6 +150,31 @@ def forward_causal(XQ, XK, V, mu, sigma2, pi, eps) -> np.ndarray:
     return _forward(_load().oracle_forward_causal, XQ, XK, V, mu, sigma2, pi, eps)
 
 
+def forward_causal_state(XQ, XK, V, mu, sigma2, pi, eps, state_in=None):
+    """Causal GMA continued from a carried memory (Sec. 3.5 Eq. 6b as a recurrence).
+    state_in [B,H,K,d_v+1] (row k: Vt_k then Z_k) is the memory before position 0, None for
+    an empty one.  Returns (O [B,H,N,d_v], state_out [B,H,K,d_v+1]): the outputs and the
+    memory after the last position."""
+    XQ, XK, V = _f64(XQ), _f64(XK), _f64(V)
+    mu, sigma2, pi = _params(mu, sigma2, pi)
+    B, H, N, dr = XQ.shape
+    dv, K = V.shape[-1], mu.shape[1]
+    if XK.shape != XQ.shape or V.shape[:3] != XQ.shape[:3]:
+        raise ValueError("XQ, XK must be [B,H,N,d_r] and V [B,H,N,d_v]")
+    sin = None
+    if state_in is not None:
+        sin = _f64(state_in)
+        if sin.shape != (B, H, K, dv + 1):
+            raise ValueError("state_in must be [B,H,K,d_v+1]")
+    O = np.empty((B, H, N, dv), np.float64)
+    S = np.empty((B, H, K, dv + 1), np.float64)
+    _check(_load().oracle_forward_causal_state(_ptr(XQ), _ptr(XK), _ptr(V), B, H, N, dr, dv, K, _ptr(mu),
+                                               _ptr(sigma2), _ptr(pi), float(eps),
+                                               _ptr(sin) if sin is not None else None, _ptr(O), _ptr(S)),
+           "oracle_forward_causal_state")
+    return O, S
+
+
 def forward_cross(XQ, XK, V, mu, sigma2, pi, eps) -> np.ndarray:
     """Cross-attention GMA output O [B,H,Nq,d_v] (Sec. 3, "Cross-attention"): queries XQ
     [B,H,Nq,d_r] read the latent memory written by a context XK [B,H,Nk,d_r], V [B,H,Nk,d_v]
@@ -167,4 +195,4 @@ def forward_cross(XQ, XK, V, mu, sigma2, pi, eps) -> np.ndarray:
 from . import brute  # noqa: E402  (numpy explicit-affinity forms)
 
 __all__ = ["build", "num_threads", "log_scores", "responsibilities", "forward_bidir",
-           "forward_causal", "forward_cross", "brute"]
+           "forward_causal", "forward_causal_state", "forward_cross", "brute"]

@@ -87,6 +87,31 @@ def forward_cross(XQ, XK, V, mu, sigma2, pi, eps: float) -> np.ndarray:
     return out
 
 
+def forward_causal_state(XQ, XK, V, mu, sigma2, pi, eps: float, state_in):
+    """Explicit causal form continued from a carried memory (Vt0, Z0) = state_in [B,H,K,d_v+1]:
+    O_i = (gammaQ_i Vt0 + sum_{j<=i} A~_ij V_j) / (gammaQ_i Z0 + sum_{j<=i} A~_ij + eps), with
+    A~ the masked affinity of Eq. 9b; the memory after the last position is
+    (Vt0 + Gamma_K^T V, Z0 + Gamma_K^T 1).  Returns (O, state_out)."""
+    XQ, XK, V, S0 = (np.asarray(t, np.float64) for t in (XQ, XK, V, state_in))
+    mu, sigma2, pi = (np.asarray(t, np.float64) for t in (mu, sigma2, pi))
+    B, H, N, _ = XQ.shape
+    dv = V.shape[-1]
+    out = np.empty((B, H, N, dv), np.float64)
+    s_out = np.empty(S0.shape, np.float64)
+    for b in range(B):
+        for h in range(H):
+            gq = responsibilities(XQ[b, h], mu[h], sigma2[h], pi[h])
+            gk = responsibilities(XK[b, h], mu[h], sigma2[h], pi[h])
+            a = affinity(gq, gk, True)
+            vt0, z0 = S0[b, h, :, :dv], S0[b, h, :, dv]
+            num = gq @ vt0 + a @ V[b, h]
+            den = gq @ z0 + a.sum(axis=1) + eps
+            out[b, h] = num / den[:, None]
+            s_out[b, h, :, :dv] = vt0 + gk.T @ V[b, h]
+            s_out[b, h, :, dv] = z0 + gk.sum(axis=0)
+    return out, s_out
+
+
 def affinity_matrix(XQ1, XK1, mu1, s21, pi1, causal: bool = False) -> np.ndarray:
     """Unnormalised affinity A~ of one head, for rank checks (Sec. 4.2 Eq. 23)."""
     gq = responsibilities(XQ1, mu1, s21, pi1)

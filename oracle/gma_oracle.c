@@ -242,11 +242,17 @@ int oracle_forward_cross(const double* XQ, int64_t Nq, const double* XK, const d
  *   Output, Eq. 8b:         O_i = sum_k gammaQ_ik Vt^(i)_k / (sum_k gammaQ_ik Z^(i)_k + eps)
  * The prefix sums are kept as a running sum along the sequence (the cumulative-sum
  * reading given at the end of Sec. 3.5); position i is included before O_i is read.
+ *
+ * Carried memory: the running sum is Eq. 6b as a recurrence (memory after i = memory
+ * after i-1 + gammaK_i [V_i | 1]), so a sequence may be continued from the memory of the
+ * positions before it.  state_in [B,H,K,d_v+1] (row k: Vt_k then Z_k) is that starting
+ * memory (NULL: empty); state_out receives the memory after the last position (NULL: not
+ * wanted).
  */
-int oracle_forward_causal(const double* XQ, const double* XK, const double* V,
-                          int64_t B, int64_t H, int64_t N, int64_t dr, int64_t dv, int64_t K,
-                          const double* mu, const double* sigma2, const double* pi,
-                          double eps, double* O) {
+int oracle_forward_causal_state(const double* XQ, const double* XK, const double* V,
+                                int64_t B, int64_t H, int64_t N, int64_t dr, int64_t dv, int64_t K,
+                                const double* mu, const double* sigma2, const double* pi,
+                                double eps, const double* state_in, double* O, double* state_out) {
     if (!XQ || !XK || !V || !mu || !sigma2 || !pi || !O || dv < 1 ||
         bad_sizes(B, H, N, dr, K))
         return -1;
@@ -265,6 +271,13 @@ int oracle_forward_causal(const double* XQ, const double* XK, const double* V,
         if (!s || !g || !Vt || !Z) {
             failed = 1;
         } else {
+            if (state_in) {
+                const double* st = state_in + p * K * (dv + 1);
+                for (int64_t k = 0; k < K; ++k) {
+                    for (int64_t c = 0; c < dv; ++c) Vt[k * dv + c] = st[k * (dv + 1) + c];
+                    Z[k] = st[k * (dv + 1) + dv];
+                }
+            }
             for (int64_t i = 0; i < N; ++i) {
                 /* add token i to the prefix memory (j <= i is inclusive) */
                 responsibilities_one(XK + (p * N + i) * dr, dr, mu_h, s2_h, pi_h, K, s, g);
@@ -285,10 +298,25 @@ int oracle_forward_causal(const double* XQ, const double* XK, const double* V,
                     oi[c] = num / den;
                 }
             }
+            if (state_out) {
+                double* st = state_out + p * K * (dv + 1);
+                for (int64_t k = 0; k < K; ++k) {
+                    for (int64_t c = 0; c < dv; ++c) st[k * (dv + 1) + c] = Vt[k * dv + c];
+                    st[k * (dv + 1) + dv] = Z[k];
+                }
+            }
         }
         free(s); free(g); free(Vt); free(Z);
     }
     return failed ? -2 : 0;
+}
+
+/* Causal GMA from an empty memory. */
+int oracle_forward_causal(const double* XQ, const double* XK, const double* V,
+                          int64_t B, int64_t H, int64_t N, int64_t dr, int64_t dv, int64_t K,
+                          const double* mu, const double* sigma2, const double* pi,
+                          double eps, double* O) {
+    return oracle_forward_causal_state(XQ, XK, V, B, H, N, dr, dv, K, mu, sigma2, pi, eps, NULL, O, NULL);
 }
 
 #ifdef _OPENMP

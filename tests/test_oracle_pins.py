@@ -419,3 +419,73 @@ def test_cross_permutation_symmetries_and_empty_context():
                                rtol=1e-11, atol=1e-13)
     O0 = oracle.forward_cross(xq, xk[:, :, :0], v[:, :, :0], mu, s2, pi, 1e-6)
     assert O0.shape == (1, 2, 8, 4) and not O0.any()
+
+
+# --------------------------------------------------------------------------- carried causal memory
+
+def rand_state(rng, B, H, K, dv):
+    """A plausible carried memory: Vt of any sign, Z > 0 (a responsibility mass)."""
+    s = np.empty((B, H, K, dv + 1))
+    s[..., :dv] = rng.standard_normal((B, H, K, dv)) * 3.0
+    s[..., dv] = rng.uniform(0.5, 20.0, (B, H, K))
+    return s
+
+
+def test_causal_state_matches_explicit_form():
+    """Eq. 6b as a recurrence from a starting memory equals the explicit masked affinity
+    (Eq. 9b) plus the starting memory's share, and the final memory is the starting one
+    plus Gamma_K^T [V | 1] (Eq. 6), both built through the density ratio of Eq. 2-3."""
+    rng = np.random.default_rng(40)
+    for shape in [(1, 1, 9, 2, 3, 2), (2, 2, 16, 3, 2, 5)]:
+        xq, xk, v, mu, s2, pi = rand_problem(rng, *shape)
+        B, H, N, dr, dv, K = shape
+        s0 = rand_state(rng, B, H, K, dv)
+        for eps in (1e-6, 0.4):
+            O, S = oracle.forward_causal_state(xq, xk, v, mu, s2, pi, eps, s0)
+            Ob, Sb = oracle.brute.forward_causal_state(xq, xk, v, mu, s2, pi, eps, s0)
+            np.testing.assert_allclose(O, Ob, rtol=1e-11, atol=1e-13)
+            np.testing.assert_allclose(S, Sb, rtol=1e-12, atol=1e-12)
+
+
+def test_causal_state_pieces_equal_whole_bitwise():
+    """Continuing a sequence from the previous piece's final memory reproduces the outputs
+    and the final memory of one pass over the whole sequence exactly (the running sum
+    adds the same terms in the same order); pieces of one position are decoding steps."""
+    rng = np.random.default_rng(41)
+    N = 23
+    xq, xk, v, mu, s2, pi = rand_problem(rng, 2, 2, N, 3, 4, 5)
+    O, S = oracle.forward_causal_state(xq, xk, v, mu, s2, pi, 1e-6)
+    assert np.array_equal(O, oracle.forward_causal(xq, xk, v, mu, s2, pi, 1e-6))
+    for cuts in ([0, 10, N], [0, 1, 2, 7, 8, 9, 22, N], list(range(N + 1))):
+        state, outs = None, []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            o, state = oracle.forward_causal_state(xq[:, :, a:b], xk[:, :, a:b], v[:, :, a:b], mu, s2, pi, 1e-6,
+                                                   state)
+            outs.append(o)
+        assert np.array_equal(np.concatenate(outs, axis=2), O)
+        assert np.array_equal(state, S)
+
+
+@pytest.mark.parametrize("eps", [1e-6, 0.5])
+def test_causal_state_single_component_closed_form(eps):
+    """K = 1 with starting memory (Vt0, Z0): O_i = (Vt0 + sum_{j<=i} V_j) / (Z0 + i + 1 + eps),
+    and the final memory is (Vt0 + sum V, Z0 + N)."""
+    rng = np.random.default_rng(42)
+    N, dv = 13, 4
+    xq, xk, v, mu, s2, pi = rand_problem(rng, 1, 2, N, 3, dv, 1)
+    s0 = rand_state(rng, 1, 2, 1, dv)
+    O, S = oracle.forward_causal_state(xq, xk, v, mu, s2, pi, eps, s0)
+    vt0, z0 = s0[:, :, 0, :dv][:, :, None], s0[:, :, 0, dv][:, :, None, None]
+    ref = (vt0 + np.cumsum(v, axis=2)) / (z0 + np.arange(1, N + 1)[None, None, :, None] + eps)
+    np.testing.assert_allclose(O, ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(S[:, :, 0, :dv], s0[:, :, 0, :dv] + v.sum(axis=2), rtol=1e-12)
+    np.testing.assert_allclose(S[:, :, 0, dv], s0[:, :, 0, dv] + N, rtol=1e-12)
+
+
+def test_causal_state_empty_call_passes_memory_through():
+    rng = np.random.default_rng(43)
+    xq, xk, v, mu, s2, pi = rand_problem(rng, 1, 2, 0, 3, 4, 5)
+    s0 = rand_state(rng, 1, 2, 5, 4)
+    O, S = oracle.forward_causal_state(xq, xk, v, mu, s2, pi, 1e-6, s0)
+    assert O.shape == (1, 2, 0, 4) and np.array_equal(S, s0)
+    assert not oracle.forward_causal_state(xq, xk, v, mu, s2, pi, 1e-6)[1].any()
