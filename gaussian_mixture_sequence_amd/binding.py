@@ -24,7 +24,7 @@ STATUS_NAMES = ["GMA_OK", "GMA_ERR_NULL_POINTER", "GMA_ERR_BAD_SHAPE", "GMA_ERR_
 GMA_F32, GMA_BF16 = 0, 1
 GMA_OP_RESPONSIBILITIES, GMA_OP_BIDIR, GMA_OP_CAUSAL = 0, 1, 2
 EXPORTED = ["gma_status_string", "gma_workspace_size", "gma_responsibilities", "gma_forward_bidir",
-            "gma_forward_causal", "gma_cross_workspace_size", "gma_forward_cross", "gma_profiling",
+            "gma_forward_causal", "gma_forward_causal_state", "gma_cross_workspace_size", "gma_forward_cross", "gma_profiling",
             "gma_profiling_collect", "gma_set_wait_limit"]
 WAIT_LIMIT_DEFAULT = 1 << 18  # GMA_WAIT_LIMIT_DEFAULT
 
@@ -75,6 +75,9 @@ def load() -> ctypes.CDLL:
             lib.gma_forward_bidir.restype = i32
             lib.gma_forward_causal.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, shp, i32, vp, sz, vp]
             lib.gma_forward_causal.restype = i32
+            lib.gma_forward_causal_state.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, shp, i32, vp, vp, vp, sz,
+                                                     vp]
+            lib.gma_forward_causal_state.restype = i32
             xshp = ctypes.POINTER(CrossShape)
             lib.gma_cross_workspace_size.argtypes = [xshp, i32, ctypes.POINTER(sz)]
             lib.gma_cross_workspace_size.restype = i32
@@ -188,6 +191,33 @@ def gma_forward_causal(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, mu: 
                                      int(chunk), _ptr(ws), ws.numel(), _stream(stream)),
            "gma_forward_causal")
     return out
+
+
+def gma_forward_causal_state(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, mu: torch.Tensor,
+                             sigma2: torch.Tensor, pi: torch.Tensor, eps: float = 1e-6, chunk: int = 64,
+                             state_in: Optional[torch.Tensor] = None, state_out: Optional[torch.Tensor] = None,
+                             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                             stream=None):
+    """Causal GMA continued from a carried memory (Eq. 6b as a recurrence).  state_in, state_out:
+    [B,H,K,d_v+1] float32 (row k: Vt_k then Z_k); state_in None is an empty memory, state_out is
+    allocated when None.  Returns (O [B,H,N,d_v], state_out)."""
+    B, H, N, dr = xq.shape
+    dv = v.shape[-1]
+    K = mu.shape[1]
+    io = _dtype_code(xq.dtype)
+    if out is None:
+        out = torch.empty(B, H, N, dv, dtype=xq.dtype, device=xq.device)
+    if state_out is None:
+        state_out = torch.empty(B, H, K, dv + 1, dtype=torch.float32, device=xq.device)
+    for s in (state_in, state_out):
+        if s is not None and (s.dtype != torch.float32 or tuple(s.shape) != (B, H, K, dv + 1)):
+            raise ValueError("states must be float32 [B,H,K,d_v+1]")
+    ws = _workspace(gma_workspace_size(GMA_OP_CAUSAL, B, H, N, dr, dv, K, io, chunk), xq.device, workspace)
+    _check(load().gma_forward_causal_state(_ptr(xq), _ptr(xk), _ptr(v), io, _ptr(mu), _ptr(sigma2), _ptr(pi),
+                                           float(eps), _ptr(out), ctypes.byref(Shape(B, H, N, dr, dv, K)),
+                                           int(chunk), _ptr(state_in), _ptr(state_out), _ptr(ws), ws.numel(),
+                                           _stream(stream)), "gma_forward_causal_state")
+    return out, state_out
 
 
 def gma_cross_workspace_size(B: int, H: int, N_q: int, N_k: int, d_r: int, d_v: int, K: int, io_dtype: int) -> int:

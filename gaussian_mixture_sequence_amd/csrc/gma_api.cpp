@@ -277,26 +277,37 @@ static gma_status_t forward_common(gma_op_t op, const void* XQ, const void* XK, 
                                    gma_dtype_t io, const float* mu, const float* sigma2,
                                    const float* pi, float eps, void* O, const gma_shape_t* shape,
                                    int32_t chunk, void* workspace, size_t workspace_bytes,
-                                   hipStream_t stream) {
-    if (!XQ || !XK || !V || !mu || !sigma2 || !pi || !O || !shape) return GMA_ERR_NULL_POINTER;
+                                   hipStream_t stream, const float* state_in = nullptr,
+                                   float* state_out = nullptr) {
+    if (!mu || !sigma2 || !pi || !shape) return GMA_ERR_NULL_POINTER;
     Plan p;
     gma_status_t st = gma::make_plan(op, *shape, io, chunk, &p);
     if (st != GMA_OK) return st;
+    if ((!XQ || !XK || !V || !O) && p.P > 0 && p.N > 0) return GMA_ERR_NULL_POINTER;  // tensors with elements
     if (!(eps > 0.0f) || !std::isfinite(eps)) return GMA_ERR_BAD_VALUE;
     for (const void* q : {XQ, XK, V, (const void*)mu, (const void*)sigma2, (const void*)pi, (const void*)O})
         if (!gma::aligned16(q)) return GMA_ERR_MISALIGNED;
     if ((st = check_ws(p, workspace, workspace_bytes)) != GMA_OK) return st;
-    if (p.P == 0 || p.N == 0) return GMA_OK;
+    if (state_out) {  // carried memory (causal only): aligned and not overlapping its input
+        const size_t sb = size_t(p.P) * size_t(p.K) * size_t(p.dv + 1) * 4;
+        if (!gma::aligned16(state_out) || (state_in && !gma::aligned16(state_in))) return GMA_ERR_MISALIGNED;
+        const char *a = reinterpret_cast<const char*>(state_in), *b = reinterpret_cast<const char*>(state_out);
+        if (state_in && sb > 0 && a < b + sb && b < a + sb) return GMA_ERR_BAD_VALUE;
+    } else if (state_in && !gma::aligned16(state_in)) {
+        return GMA_ERR_MISALIGNED;
+    }
+    if (p.P == 0) return GMA_OK;
+    if (p.N == 0) return state_out ? launch_status(gma::copy_state(p, state_in, state_out, stream)) : GMA_OK;
     char* ws = static_cast<char*>(workspace);
     if (io == GMA_F32) {
         const float *q = static_cast<const float*>(XQ), *k = static_cast<const float*>(XK),
                     *v = static_cast<const float*>(V);
         float* o = static_cast<float*>(O);
         if (op == GMA_OP_BIDIR) return launch_status(gma::f32_bidir(p, q, k, v, mu, sigma2, pi, eps, o, ws, stream));
-        return launch_status(gma::f32_causal(p, q, k, v, mu, sigma2, pi, eps, o, ws, stream));
+        return launch_status(gma::f32_causal(p, q, k, v, mu, sigma2, pi, eps, o, ws, stream, state_in, state_out));
     }
     if (op == GMA_OP_BIDIR) return launch_status(gma::bf16_bidir(p, XQ, XK, V, mu, sigma2, pi, eps, O, ws, stream));
-    return launch_status(gma::bf16_causal(p, XQ, XK, V, mu, sigma2, pi, eps, O, ws, stream));
+    return launch_status(gma::bf16_causal(p, XQ, XK, V, mu, sigma2, pi, eps, O, ws, stream, state_in, state_out));
 }
 
 gma_status_t gma_forward_bidir(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
@@ -313,6 +324,15 @@ gma_status_t gma_forward_causal(const void* XQ, const void* XK, const void* V, g
                                 size_t workspace_bytes, hipStream_t stream) {
     return forward_common(GMA_OP_CAUSAL, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, O, shape, chunk,
                           workspace, workspace_bytes, stream);
+}
+
+gma_status_t gma_forward_causal_state(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                                      const float* mu, const float* sigma2, const float* pi, float eps,
+                                      void* O, const gma_shape_t* shape, int32_t chunk,
+                                      const float* state_in, float* state_out, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+    return forward_common(GMA_OP_CAUSAL, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, O, shape, chunk,
+                          workspace, workspace_bytes, stream, state_in, state_out);
 }
 
 gma_status_t gma_cross_workspace_size(const gma_cross_shape_t* shape, gma_dtype_t io_dtype, size_t* bytes_out) {

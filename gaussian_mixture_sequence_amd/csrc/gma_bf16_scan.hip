@@ -57,6 +57,54 @@ struct ScanStats {
     float m, L, D;
 };
 
+// The scans keep the memory as 16x16 MFMA accumulators: mem[cc][kt] holds Vt[k][c] for value
+// column c = 16 (wave + cc NW) + l % 16 and components k = 16 kt + 4 (l / 16) + r, r = 0..3
+// (Vt^T's D layout), and Z in LDS.  The carried memory of gma_forward_causal_state is
+// [K][DV + 1] fp32 (row k: Vt_k then Z_k); components k >= K (padding) are zero.  Thread t
+// initialises Z entries ZV t .. ZV t + ZV - 1 (+ ZV NT, ...): the same entries it later adds
+// the earlier segments' aggregates to, so no barrier is needed in between.
+template <int CPW, int KT16, int NW, int DV, int ZV>
+__device__ __forceinline__ void init_memory(f32x4 (&mem)[CPW][KT16], float* Zs, int Kp, int NT,
+                                            const float* __restrict__ state, int K) {
+    const int l = threadIdx.x & 63, g4 = l >> 4, i16 = l & 15, wave = wave_id();
+#pragma unroll
+    for (int cc = 0; cc < CPW; ++cc)
+#pragma unroll
+        for (int kt = 0; kt < KT16; ++kt) {
+            const int c = (wave + cc * NW) * 16 + i16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int k = kt * 16 + 4 * g4 + r;
+                mem[cc][kt][r] = (state && c < DV && k < K) ? state[size_t(k) * (DV + 1) + c] : 0.0f;
+            }
+        }
+    for (int k0 = threadIdx.x * ZV; k0 < Kp; k0 += NT * ZV)
+#pragma unroll
+        for (int r = 0; r < ZV; ++r) {
+            const int k = k0 + r;
+            Zs[k] = (state && k < K) ? state[size_t(k) * (DV + 1) + DV] : 0.0f;
+        }
+}
+
+// Writes the memory back in the carried layout; Zs must be complete (after a barrier).
+template <int CPW, int KT16, int NW, int DV>
+__device__ __forceinline__ void store_memory(const f32x4 (&mem)[CPW][KT16], const float* Zs, float* __restrict__ state,
+                                             int K) {
+    const int l = threadIdx.x & 63, g4 = l >> 4, i16 = l & 15, wave = wave_id();
+#pragma unroll
+    for (int cc = 0; cc < CPW; ++cc)
+#pragma unroll
+        for (int kt = 0; kt < KT16; ++kt) {
+            const int c = (wave + cc * NW) * 16 + i16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int k = kt * 16 + 4 * g4 + r;
+                if (c < DV && k < K) state[size_t(k) * (DV + 1) + c] = mem[cc][kt][r];
+            }
+        }
+    for (int k = threadIdx.x; k < K; k += int(blockDim.x)) state[size_t(k) * (DV + 1) + DV] = Zs[k];
+}
+
 template <int DR, int KT, int CH>
 constexpr int scan_jpw() {  // 32-position score jobs per wave and chunk (query and key)
     return (2 * (CH / 32) + Split<DR, KT>::TS - 1) / Split<DR, KT>::TS;
@@ -114,7 +162,8 @@ __device__ __forceinline__ void scan_body(char* __restrict__ smem, const uint16_
                                           const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V, int64_t N,
                                           int64_t p, int h, int seg_idx, int64_t lo, int64_t hi, const Mixture& mx,
                                           WaveParams<DR, Split<DR, KT>::CTW>& P, const float* __restrict__ agg,
-                                          float eps, uint16_t* __restrict__ O, WaitF&& wait) {
+                                          float eps, uint16_t* __restrict__ O, WaitF&& wait,
+                                          const float* __restrict__ state_in, float* __restrict__ state_out) {
     constexpr int CH = scan_chunk<DR, KT, VT, CH_REQ>();
     using LY = ScanLds<DR, KT, VT, CH>;
     using S = Split<DR, KT>;
@@ -258,11 +307,7 @@ __device__ __forceinline__ void scan_body(char* __restrict__ smem, const uint16_
     const size_t E = size_t(Kp) * (DV + 1);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(agg, int64_t(seg_idx) * int64_t(E) * 4);
     f32x4 mem[CPW][KT16];
-#pragma unroll
-    for (int cc = 0; cc < CPW; ++cc)
-#pragma unroll
-        for (int kt = 0; kt < KT16; ++kt) mem[cc][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k = threadIdx.x; k < Kp; k += NT) Zs[k] = 0.0f;
+    init_memory<CPW, KT16, NW, DV, 4>(mem, Zs, Kp, NT, state_in, mx.K);
 
     // prologue loads first, so they overlap the operand build and the prefix sum
     load_v(0);
@@ -484,6 +529,7 @@ __device__ __forceinline__ void scan_body(char* __restrict__ smem, const uint16_
         chunk(c + 1, 1, acc_b, acc_a);
     }
     if (c < C) chunk(c, 0, acc_a, acc_b);
+    if (state_out) store_memory<CPW, KT16, NW, DV>(mem, Zs, state_out, mx.K);  // after B_P of the last chunk
 }
 
 // ---- the causal forward in one launch (shapes of the pipelined scan).  Grid (G, P);
@@ -506,7 +552,7 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(causal_lds_bytes<DR, KT, VT, CH
     causal_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
                   int64_t N, int H, int64_t seg, int G, Mixture mx, float* __restrict__ aggregates,
                   uint64_t* __restrict__ flags, uint64_t token, uint32_t wait_limit, float eps,
-                  uint16_t* __restrict__ O) {
+                  uint16_t* __restrict__ O, const float* __restrict__ state_in, float* __restrict__ state_out) {
     __shared__ __attribute__((aligned(16))) char smem[causal_lds_bytes<DR, KT, VT, CH_REQ>()];
     using S = Split<DR, KT>;
     constexpr int Kp = KT * 32, DV = VT * 32, E = Kp * (DV + 1), NT = S::NW * 64;
@@ -530,8 +576,11 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(causal_lds_bytes<DR, KT, VT, CH
         P.compute(mx, h, (wave_id() % S::CS) * S::CTW);
     }
     bool ok = true;
+    const size_t SE = size_t(mx.K) * (DV + 1);  // one problem's carried memory
     scan_body<DR, KT, VT, CH_REQ, false>(smem, XQ, XK, V, N, p, h, s, lo, hi, mx, P, agg, eps, O,
-                                         [&] { ok = wait_tokens(fl, s, token, wait_limit); });
+                                         [&] { ok = wait_tokens(fl, s, token, wait_limit); },
+                                         state_in ? state_in + p * SE : nullptr,
+                                         (state_out && s == G - 1) ? state_out + p * SE : nullptr);
     // waves poll on their own: agree on the outcome before acting on it
     ok = workgroup_all(ok, reinterpret_cast<int*>(smem));
     if (!ok) {  // the starting memory was never complete: make that visible in the output
@@ -567,7 +616,8 @@ template <int DR, int KT, int VT, int CH_REQ>
 __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
     serial_scan_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
                 int64_t N, int H, int64_t seg, int G, Mixture mx,
-                const float* __restrict__ prefix, float eps, uint16_t* __restrict__ O) {
+                const float* __restrict__ prefix, float eps, uint16_t* __restrict__ O,
+                const float* __restrict__ state_in, float* __restrict__ state_out) {
     constexpr int CH = serial_scan_chunk<DR, KT, VT, CH_REQ>();
     using S = Split<DR, KT>;
     constexpr int NT = S::NW * 64;
@@ -652,12 +702,9 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
     // (each stored as VtT [DV][Kp] then Z [Kp]), added in increasing segment order
     const size_t E = size_t(Kp) * (DV + 1);
     const float* agg = prefix + size_t(p) * G * E;
+    const size_t SE = size_t(mx.K) * (DV + 1);  // one problem's carried memory
     f32x4 mem[CPW][KT16];
-#pragma unroll
-    for (int cc = 0; cc < CPW; ++cc)
-#pragma unroll
-        for (int kt = 0; kt < KT16; ++kt) mem[cc][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int k = threadIdx.x; k < Kp; k += NT) Zs[k] = 0.0f;
+    init_memory<CPW, KT16, NW, DV, 1>(mem, Zs, Kp, NT, state_in ? state_in + p * SE : nullptr, mx.K);
 
     // prologue loads are issued before the prefix sum so they overlap it
     load_v(0);
@@ -903,6 +950,10 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
         chunk(nc, 0, xf);
         chunk(nc + CH, 1, xn);
     }
+    if (state_out && seg_idx == G - 1) {
+        __syncthreads();  // the last chunk's Z update is visible
+        store_memory<CPW, KT16, NW, DV>(mem, Zs, state_out + p * SE, mx.K);
+    }
 }
 
 template <typename F>
@@ -930,7 +981,8 @@ hipError_t with_all(int dr, int kt, int vt, int ch, F&& f) {
 // whose registers fit the pipelined scan run the fused causal kernel; the others run the
 // segment aggregates (write kernel) and then the serial scan.
 hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu, const float* s2,
-                       const float* pi, float eps, void* O, char* ws, hipStream_t st) {
+                       const float* pi, float eps, void* O, char* ws, hipStream_t st, const float* state_in,
+                       float* state_out) {
     const bf::Mixture mx{mu, s2, pi, int(p.K)};
     float* aggregates = reinterpret_cast<float*>(ws + p.off_partials);
     uint64_t* flags = reinterpret_cast<uint64_t*>(ws + p.off_flags);
@@ -944,7 +996,7 @@ hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void
             GMA_LAUNCH("bf16_causal", (bf::causal_kernel<DR, KT, VT, CH>), dim3(unsigned(p.G), unsigned(p.P)),
                        dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
                        static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), mx, aggregates, flags,
-                       launch_token(), wait_limit(), eps, static_cast<uint16_t*>(O));
+                       launch_token(), wait_limit(), eps, static_cast<uint16_t*>(O), state_in, state_out);
         } else {
             // aggregates of segments 0 .. G-2 (the last segment's aggregate is never read)
             if (p.G > 1) {
@@ -954,7 +1006,7 @@ hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void
             GMA_LAUNCH("bf16_scan", (bf::serial_scan_kernel<DR, KT, VT, CH>), dim3(unsigned(p.G), unsigned(p.P)),
                        dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
                        static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), mx, aggregates, eps,
-                       static_cast<uint16_t*>(O));
+                       static_cast<uint16_t*>(O), state_in, state_out);
         }
         return hipGetLastError();
     });

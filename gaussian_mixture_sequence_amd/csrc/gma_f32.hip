@@ -203,14 +203,22 @@ __global__ void __launch_bounds__(kThreads) f32_combine_kernel(const float* __re
     out[size_t(p) * E + e] = acc;
 }
 
+// Index of partial-layout element e (Vt [K][dv] then Z [K]) in the carried-memory layout
+// [K][dv + 1] (row k: Vt_k then Z_k).
+__device__ __forceinline__ int state_index(int e, int K, int dv) {
+    return e < K * dv ? (e / dv) * (dv + 1) + e % dv : (e - K * dv) * (dv + 1) + dv;
+}
+
 // Causal: exclusive prefix over segments in place; segment g then holds the memory
-// accumulated over all positions before it.
-__global__ void __launch_bounds__(kThreads) f32_prefix_kernel(float* __restrict__ partials, int G, int E) {
+// accumulated over all positions before it, starting from the carried memory state_in
+// ([P][K][dv+1], or zero when NULL).
+__global__ void __launch_bounds__(kThreads) f32_prefix_kernel(float* __restrict__ partials, int G, int E,
+                                                              const float* __restrict__ state_in, int K, int dv) {
     const int64_t p = blockIdx.y;
     const int e = blockIdx.x * kThreads + threadIdx.x;
     if (e >= E) return;
     float* src = partials + size_t(p) * G * E + e;
-    float run = 0.0f;
+    float run = state_in ? state_in[size_t(p) * E + state_index(e, K, dv)] : 0.0f;
     for (int g = 0; g < G; ++g) {
         float a = src[size_t(g) * E];
         src[size_t(g) * E] = run;
@@ -261,7 +269,7 @@ __global__ void __launch_bounds__(kThreads) f32_scan_kernel(const float* __restr
                                                             int dr, int dv, int K, int64_t seg, int G,
                                                             int C, const double* c, const double* inv,
                                                             const float* mu, float* partials, float eps,
-                                                            float* __restrict__ O) {
+                                                            float* __restrict__ O, float* __restrict__ state_out) {
     extern __shared__ float lds[];
     const int64_t p = blockIdx.y;
     const int g_idx = blockIdx.x;
@@ -318,6 +326,16 @@ __global__ void __launch_bounds__(kThreads) f32_scan_kernel(const float* __restr
         }
         __syncthreads();  // state update visible to the whole block before the next chunk
     }
+    // the last segment's memory is the memory after the last position
+    if (state_out && g_idx == G - 1)
+        for (int e = threadIdx.x; e < K * (dv + 1); e += kThreads)
+            state_out[size_t(p) * K * (dv + 1) + state_index(e, K, dv)] = Vt[e];
+}
+
+__global__ void __launch_bounds__(kThreads) state_copy_kernel(const float* __restrict__ in, float* __restrict__ out,
+                                                              int E) {
+    const size_t i = size_t(blockIdx.y) * E + size_t(blockIdx.x) * kThreads + threadIdx.x;
+    if (int(blockIdx.x) * kThreads + int(threadIdx.x) < E) out[i] = in ? in[i] : 0.0f;
 }
 
 size_t scan_lds_bytes(int C, int dr, int dv, int K) {
@@ -385,8 +403,16 @@ hipError_t f32_bidir(const Plan& p, const float* XQ, const float* XK, const floa
     return hipGetLastError();
 }
 
+hipError_t copy_state(const Plan& p, const float* state_in, float* state_out, hipStream_t st) {
+    const int E = int(p.K * (p.dv + 1));
+    GMA_LAUNCH("state_copy", state_copy_kernel, dim3(unsigned((E + kThreads - 1) / kThreads), unsigned(p.P)),
+               dim3(kThreads), 0, st, state_in, state_out, E);
+    return hipGetLastError();
+}
+
 hipError_t f32_causal(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
-                      const float* s2, const float* pi, float eps, float* O, char* ws, hipStream_t st) {
+                      const float* s2, const float* pi, float eps, float* O, char* ws, hipStream_t st,
+                      const float* state_in, float* state_out) {
     hipError_t e = launch_params(p, s2, pi, ws, st);
     if (e != hipSuccess) return e;
     F32Params v = f32_params_view(p, ws);
@@ -402,14 +428,15 @@ hipError_t f32_causal(const Plan& p, const float* XQ, const float* XK, const flo
     // With one segment the aggregate pass is skipped: the prefix kernel writes the
     // starting memory of segment 0 as zeros without reading the aggregate.
     GMA_LAUNCH("f32_prefix", f32_prefix_kernel, dim3(unsigned((E + kThreads - 1) / kThreads), unsigned(p.P)),
-                       dim3(kThreads), 0, st, partials, int(p.G), E);
+                       dim3(kThreads), 0, st, partials, int(p.G), E, state_in, int(p.K), int(p.dv));
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // The chunk length is a tiling choice; halve it until the chunk's tiles fit in LDS.
     int C = p.chunk;
     while (C > 8 && scan_lds_bytes(C, int(p.dr), int(p.dv), int(p.K)) > kMaxLds) C /= 2;
     GMA_LAUNCH("f32_scan", f32_scan_kernel, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads),
                        scan_lds_bytes(C, int(p.dr), int(p.dv), int(p.K)), st, XQ, XK, V, p.N, int(p.H),
-                       int(p.dr), int(p.dv), int(p.K), p.seg, int(p.G), C, v.c, v.inv, mu, partials, eps, O);
+                       int(p.dr), int(p.dv), int(p.K), p.seg, int(p.G), C, v.c, v.inv, mu, partials, eps, O,
+                       state_out);
     return hipGetLastError();
 }
 

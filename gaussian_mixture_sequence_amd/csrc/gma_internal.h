@@ -69,9 +69,13 @@ hipError_t f32_responsibilities(const Plan& p, const float* X, const float* mu, 
 hipError_t f32_bidir(const Plan& p, const float* XQ, const float* XK, const float* V,
                      const float* mu, const float* s2, const float* pi, float eps, float* O,
                      char* ws, hipStream_t st);
+// state_in / state_out: [P][K][d_v+1] fp32 carried memory (gma_forward_causal_state), or NULL.
 hipError_t f32_causal(const Plan& p, const float* XQ, const float* XK, const float* V,
                       const float* mu, const float* s2, const float* pi, float eps, float* O,
-                      char* ws, hipStream_t st);
+                      char* ws, hipStream_t st, const float* state_in, float* state_out);
+// state_out = state_in (zeros if state_in is NULL) for the P problems of `p`: the carried
+// memory of a call without positions.
+hipError_t copy_state(const Plan& p, const float* state_in, float* state_out, hipStream_t st);
 
 // ---- bf16 MFMA path (gma_bf16.hip) ---------------------------------------------
 hipError_t bf16_responsibilities(const Plan& p, const void* X, const float* mu, const float* s2,
@@ -82,7 +86,7 @@ hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void*
                       char* ws, hipStream_t st);
 hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void* V,
                        const float* mu, const float* s2, const float* pi, float eps, void* O,
-                       char* ws, hipStream_t st);
+                       char* ws, hipStream_t st, const float* state_in, float* state_out);
 // Segment aggregates (the first `splits` segments) into the partials region: the first
 // launch of the causal path for shapes the fused causal kernel does not take.
 hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, const float* mu, const float* s2,

@@ -32,6 +32,8 @@
  * Streams     Work is enqueued on `stream` (NULL = the device's null stream) and the call
  *             returns without waiting.  Calls on different streams may run concurrently
  *             if they use different workspaces.
+ * Pointers    A tensor pointer may be NULL when the tensor has no elements (e.g. N = 0);
+ *             the parameters, the shape and a workspace of nonzero size may not.
  * Errors      Arguments are validated on the host before any HIP call; a non-OK status
  *             means nothing was enqueued.  GMA_ERR_HIP reports a failed launch.  Faults
  *             inside a kernel surface at the caller's next synchronisation.  Device-side
@@ -146,6 +148,30 @@ gma_status_t gma_forward_causal(const void* XQ, const void* XK, const void* V,
                                 const float* mu, const float* sigma2, const float* pi,
                                 float eps, void* O, const gma_shape_t* shape, int32_t chunk,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Causal GMA with a carried memory: Sec. 3.5 Eq. 6b read as a recurrence, the prefix memory
+ * after position i being the memory after position i-1 plus gammaK_i [V_i | 1].  A call
+ * continues the sequence from the memory of all positions before its first one:
+ *   state_in   [B,H,K,d_v+1] fp32, row k = Vt_k (d_v values) then Z_k: the memory before
+ *              position 0 of this call.  NULL means an empty memory (then this is
+ *              gma_forward_causal).
+ *   state_out  [B,H,K,d_v+1] fp32, same layout: the memory after this call's last position,
+ *              i.e. state_in plus gammaK_j [V_j | 1] summed over every position j of the call.
+ *              NULL skips it.  Must not overlap state_in.
+ *   O_i = gammaQ_i (Vt_in + sum_{j<=i} gammaK_j V_j^T) / (gammaQ_i (Z_in + sum_{j<=i} gammaK_j) + eps)
+ * Processing a sequence in consecutive pieces, each call's state_out being the next call's
+ * state_in, gives the outputs of one call over the whole sequence (up to the order of the
+ * sums); pieces of N = 1 are single-token decoding.  With N = 0 state_out receives state_in
+ * (zeros if state_in is NULL).  All other arguments, errors and the workspace (size from
+ * gma_workspace_size with GMA_OP_CAUSAL) are those of gma_forward_causal.  state_in and
+ * state_out must be 16-byte aligned.
+ */
+gma_status_t gma_forward_causal_state(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                                      const float* mu, const float* sigma2, const float* pi, float eps,
+                                      void* O, const gma_shape_t* shape, int32_t chunk,
+                                      const float* state_in, float* state_out,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Cross-attention (Sec. 3, "Cross-attention"): queries are formed from a query-side

@@ -191,3 +191,21 @@ def test_cross_without_output_rows_enqueues_nothing(lib):
     assert call_cross(lib, xq=None, o=None, shape=(1, 1, 0, 96, 16, 32, 8)) == OK
     assert call_cross(lib, xk=None, v=None, shape=(1, 1, 0, 0, 16, 32, 8)) == OK
     assert call_cross(lib, xk=None, shape=(1, 1, 0, 96, 16, 32, 8)) == NULLP
+
+
+def test_causal_state_argument_errors(lib):
+    """State pointers: optional, 16-byte aligned, state_out not overlapping state_in."""
+    shape = (1, 1, 64, 16, 32, 8)
+    sh = gb.Shape(*shape)
+    st, need = ws_size(gb.GMA_OP_CAUSAL, *shape, gb.GMA_F32)
+    f = lib.gma_forward_causal_state
+    args = lambda s_in, s_out, n=64: (FAKE, FAKE, FAKE, gb.GMA_F32, FAKE, FAKE, FAKE, 1e-6, FAKE,
+                                      ctypes.byref(gb.Shape(1, 1, n, 16, 32, 8)), 64, s_in, s_out, FAKE, need, None)
+    sbytes = 8 * 33 * 4
+    assert f(*args(FAKE + 4, None)) == MISAL
+    assert f(*args(None, FAKE + 8)) == MISAL
+    assert f(*args(FAKE, FAKE + sbytes - 16)) == VALUE          # overlap
+    assert f(*args(FAKE + sbytes - 16, FAKE)) == VALUE
+    assert f(FAKE, FAKE, FAKE, gb.GMA_F32, FAKE, FAKE, FAKE, 0.0, FAKE, ctypes.byref(sh), 64, None, None, FAKE, need,
+             None) == VALUE
+    assert f(*args(None, None, n=0)) == OK                       # no positions, no state: nothing to do

@@ -1,0 +1,113 @@
+"""GPU parity of the causal forward continued from a carried memory (Sec. 3.5 Eq. 6b as a
+recurrence) through the C ABI: piecewise passes and single-token decoding against one
+oracle pass over the whole sequence, and the final memory against the oracle's."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gaussian_mixture_sequence_amd import binding as gb
+from gaussian_mixture_sequence_amd.inputs import WORKLOADS, make_inputs
+from gma_testutil import TOL, row_scaled_error, to_device, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def state_error(s, ref):
+    """Row-scaled error of a memory [B,H,K,d_v+1]: each component row (Vt_k and Z_k) scaled by
+    its largest reference magnitude."""
+    return row_scaled_error(s, ref)
+
+
+def pieces(w, inp, cuts, chunk=None, state=None):
+    """Runs the sequence [cuts[0], cuts[-1]) as consecutive calls; returns (O of all pieces, state)."""
+    d = to_device(inp)
+    outs = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        sl = {k: (d[k][:, :, a:b].contiguous() if k in ("xq", "xk", "v") else d[k]) for k in d}
+        o, state = gb.gma_forward_causal_state(sl["xq"], sl["xk"], sl["v"], sl["mu"], sl["sigma2"], sl["pi"], w.eps,
+                                               chunk=chunk or w.chunk, state_in=state)
+        outs.append(o)
+    torch.cuda.synchronize()
+    return torch.cat(outs, dim=2), state
+
+
+def case(dtype, **kw):
+    base = WORKLOADS["bidir_small_f32"].with_(causal=True) if dtype == "f32" else WORKLOADS["causal_b8h12_n2048"]
+    return base.with_(**kw)
+
+
+CASES = [
+    (case("f32", B=1, H=2, N=700, seed=91), [0, 300, 301, 700]),
+    (case("bf16", B=1, H=2, N=2500, seed=92), [0, 900, 2500]),                            # fused scan, segments
+    (case("bf16", B=2, H=1, N=1300, d_r=32, d_v=64, K=128, seed=93), [0, 64, 65, 1300]),  # K = 128
+    (case("bf16", B=1, H=1, N=600, d_r=64, d_v=128, K=256, seed=94), [0, 250, 600]),      # serial scan
+    (case("bf16", B=1, H=2, N=300, d_r=16, d_v=32, K=8, chunk=32, seed=95), [0, 31, 300]),  # padded K
+]
+
+
+@pytest.mark.parametrize("w,cuts", CASES, ids=lambda x: getattr(x, "dtype", None) and "%s-N%d-dr%d-dv%d-K%d" % (
+    x.dtype, x.N, x.d_r, x.d_v, x.K))
+def test_pieces_match_whole_sequence(w, cuts):
+    inp = make_inputs(w)
+    O, S = pieces(w, inp, cuts)
+    ref_o, ref_s = oracle.forward_causal_state(inp["xq"], inp["xk"], inp["v"], inp["mu"], inp["sigma2"], inp["pi"],
+                                               w.eps)
+    tol = TOL[w.dtype]
+    assert row_scaled_error(to_np(O), ref_o) <= tol
+    assert state_error(to_np(S), ref_s) <= (1e-5 if w.dtype == "f32" else 1e-2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_steps_from_prefill(dtype):
+    """Prefill 700 positions with the state API, then decode 6 positions one at a time."""
+    w = case(dtype, B=2, H=2, N=706, seed=96)
+    inp = make_inputs(w)
+    O, S = pieces(w, inp, [0, 700, 701, 702, 703, 704, 705, 706])
+    ref_o, ref_s = oracle.forward_causal_state(inp["xq"], inp["xk"], inp["v"], inp["mu"], inp["sigma2"], inp["pi"],
+                                               w.eps)
+    assert row_scaled_error(to_np(O[:, :, 700:]), ref_o[:, :, 700:]) <= TOL[dtype]
+    assert row_scaled_error(to_np(O), ref_o) <= TOL[dtype]
+    assert state_error(to_np(S), ref_s) <= (1e-5 if dtype == "f32" else 1e-2)
+
+
+def test_starting_memory_is_used():
+    """A nonzero starting memory changes the outputs exactly as the oracle says."""
+    w = case("bf16", B=1, H=2, N=1000, seed=97)
+    inp = make_inputs(w)
+    g = np.random.default_rng(3)
+    s0 = np.empty((w.B, w.H, w.K, w.d_v + 1))
+    s0[..., :w.d_v] = g.standard_normal((w.B, w.H, w.K, w.d_v)) * 10
+    s0[..., w.d_v] = g.uniform(1.0, 50.0, (w.B, w.H, w.K))
+    d = to_device(inp)
+    st_in = torch.tensor(s0, dtype=torch.float32, device="cuda")
+    O, S = gb.gma_forward_causal_state(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps, chunk=w.chunk,
+                                       state_in=st_in)
+    torch.cuda.synchronize()
+    ref_o, ref_s = oracle.forward_causal_state(inp["xq"], inp["xk"], inp["v"], inp["mu"], inp["sigma2"], inp["pi"],
+                                               w.eps, state_in=to_np(st_in))
+    assert row_scaled_error(to_np(O), ref_o) <= TOL["bf16"]
+    assert state_error(to_np(S), ref_s) <= 1e-2
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_without_state_is_the_causal_forward(dtype):
+    """state_in = NULL is gma_forward_causal bit for bit."""
+    w = case(dtype, B=1, H=2, N=1500, seed=98)
+    inp = make_inputs(w)
+    d = to_device(inp)
+    O, _ = gb.gma_forward_causal_state(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps, chunk=w.chunk)
+    ref = gb.gma_forward_causal(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps, chunk=w.chunk)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_np(O), to_np(ref))
+
+
+def test_empty_call_copies_state():
+    w = case("bf16", B=2, H=3, N=0, seed=99)
+    inp = make_inputs(w)
+    d = to_device(inp)
+    s0 = torch.randn(w.B, w.H, w.K, w.d_v + 1, device="cuda")
+    _, S = gb.gma_forward_causal_state(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps, state_in=s0)
+    _, S0 = gb.gma_forward_causal_state(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps)
+    torch.cuda.synchronize()
+    assert torch.equal(S, s0) and not S0.any()
