@@ -298,6 +298,8 @@ static gma_status_t forward_common(gma_op_t op, const void* XQ, const void* XK, 
     }
     if (p.P == 0) return GMA_OK;
     if (p.N == 0) return state_out ? launch_status(gma::copy_state(p, state_in, state_out, stream)) : GMA_OK;
+    if (gma::decode_applies(p))
+        return launch_status(gma::causal_decode(p, XQ, XK, V, mu, sigma2, pi, eps, O, stream, state_in, state_out));
     char* ws = static_cast<char*>(workspace);
     if (io == GMA_F32) {
         const float *q = static_cast<const float*>(XQ), *k = static_cast<const float*>(XK),

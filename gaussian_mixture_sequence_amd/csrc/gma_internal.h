@@ -77,6 +77,15 @@ hipError_t f32_causal(const Plan& p, const float* XQ, const float* XK, const flo
 // memory of a call without positions.
 hipError_t copy_state(const Plan& p, const float* state_in, float* state_out, hipStream_t st);
 
+// ---- short causal calls (gma_decode.hip) --------------------------------------
+// Causal calls of at most this many positions (decoding steps) run one workgroup per problem
+// that walks its positions in order, instead of the chunked scan.
+constexpr int64_t kDecodeMaxPositions = 8;
+bool decode_applies(const Plan& p);
+hipError_t causal_decode(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu,
+                         const float* s2, const float* pi, float eps, void* O, hipStream_t st,
+                         const float* state_in, float* state_out);
+
 // ---- bf16 MFMA path (gma_bf16.hip) ---------------------------------------------
 hipError_t bf16_responsibilities(const Plan& p, const void* X, const float* mu, const float* s2,
                                  const float* pi, void* Gamma, gma_dtype_t gamma_dtype, char* ws,

@@ -41,6 +41,7 @@ class Workload:
     seed: int = 0
     chunk: int = 64     # causal chunk length (ignored by the bidirectional variant)
     n_ctx: int = -1     # cross-attention: context length N_k of XK and V (N is then N_q); -1: self
+    decode: bool = False  # causal decoding: one position per call, carrying the memory between calls
 
     @property
     def tokens(self) -> int:
@@ -74,6 +75,9 @@ WORKLOADS: Dict[str, Workload] = {
                                    seed=4),
     # cross-attention (no workload is given for it): the B=8, H=8 bidirectional dims with
     # 4096 queries reading a context four times as long
+    # single-token causal decoding with a carried memory: the B=8, H=12 causal dims, one
+    # position of each sequence per call (N positions are drawn and cycled through)
+    "decode_b8h12_k32": Workload("decode_b8h12_k32", True, 8, 12, 64, 64, 64, 32, "bf16", seed=6, decode=True),
     "cross_b8h8_q4096_k16384": Workload("cross_b8h8_q4096_k16384", False, 8, 8, 4096, 64, 64, 64, "bf16",
                                         seed=5, n_ctx=16384),
 }

@@ -111,3 +111,35 @@ def test_empty_call_copies_state():
     _, S0 = gb.gma_forward_causal_state(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps)
     torch.cuda.synchronize()
     assert torch.equal(S, s0) and not S0.any()
+
+
+SHORT = [
+    ("f32", dict(d_r=16, d_v=32, K=8)), ("f32", dict(d_r=7, d_v=5, K=13)), ("f32", dict(d_r=128, d_v=128, K=256)),
+    ("bf16", dict(d_r=64, d_v=64, K=32)), ("bf16", dict(d_r=32, d_v=64, K=128)), ("bf16", dict(d_r=128, d_v=128, K=256)),
+    ("bf16", dict(d_r=16, d_v=32, K=1)), ("bf16", dict(d_r=64, d_v=32, K=50)),
+]
+
+
+@pytest.mark.parametrize("n", [1, 3, 8])
+@pytest.mark.parametrize("dtype,dims", SHORT, ids=lambda v: str(v))
+def test_short_calls_match_oracle(dtype, dims, n):
+    """Calls of a few positions (decoding steps) from a nonzero starting memory: outputs and
+    final memory against the oracle."""
+    w = case(dtype, B=2, H=3, N=n, seed=100 + n, **dims)
+    inp = make_inputs(w)
+    g = np.random.default_rng(n)
+    s0 = np.empty((w.B, w.H, w.K, w.d_v + 1))
+    s0[..., :w.d_v] = g.standard_normal((w.B, w.H, w.K, w.d_v)) * 5
+    s0[..., w.d_v] = g.uniform(0.5, 30.0, (w.B, w.H, w.K))
+    d = to_device(inp)
+    st_in = torch.tensor(s0, dtype=torch.float32, device="cuda")
+    O, S = gb.gma_forward_causal_state(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps, chunk=w.chunk,
+                                       state_in=st_in)
+    O2 = gb.gma_forward_causal(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps, chunk=w.chunk)
+    torch.cuda.synchronize()
+    ref_o, ref_s = oracle.forward_causal_state(inp["xq"], inp["xk"], inp["v"], inp["mu"], inp["sigma2"], inp["pi"],
+                                               w.eps, state_in=to_np(st_in))
+    assert row_scaled_error(to_np(O), ref_o) <= TOL[dtype]
+    assert state_error(to_np(S), ref_s) <= (1e-5 if dtype == "f32" else 1e-2)
+    ref2 = oracle.forward_causal(inp["xq"], inp["xk"], inp["v"], inp["mu"], inp["sigma2"], inp["pi"], w.eps)
+    assert row_scaled_error(to_np(O2), ref2) <= TOL[dtype]
