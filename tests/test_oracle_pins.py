@@ -489,3 +489,78 @@ def test_causal_state_empty_call_passes_memory_through():
     O, S = oracle.forward_causal_state(xq, xk, v, mu, s2, pi, 1e-6, s0)
     assert O.shape == (1, 2, 0, 4) and np.array_equal(S, s0)
     assert not oracle.forward_causal_state(xq, xk, v, mu, s2, pi, 1e-6)[1].any()
+
+
+# --------------------------------------------------------------------------- diagnostics (Sec. 5.4)
+
+def test_diagnostics_match_sklearn_posteriors():
+    """Eq. 24-29 from responsibilities computed by sklearn's diagonal GaussianMixture
+    (predict_proba, one model per head) equal the oracle's diagnostics."""
+    from sklearn.mixture import GaussianMixture
+    rng = np.random.default_rng(50)
+    B, H, N, dr, K = 3, 4, 40, 5, 6
+    xq, _, _, mu, s2, pi = rand_problem(rng, B, H, N, dr, 1, K, x_std=1.5)
+    d = oracle.diagnostics.diagnostics(xq, mu, s2, pi)
+    G = np.empty((B, H, N, K))
+    for h in range(H):
+        gm = GaussianMixture(n_components=K, covariance_type="diag")
+        gm.weights_, gm.means_, gm.covariances_ = pi[h], mu[h], s2[h]
+        gm.precisions_cholesky_ = 1.0 / np.sqrt(s2[h])
+        for b in range(B):
+            G[b, h] = gm.predict_proba(xq[b, h])
+    gbar = G.mean(axis=1)
+    np.testing.assert_allclose(d["gbar"], gbar, rtol=1e-10, atol=1e-12)
+    p = gbar.reshape(-1, K).mean(axis=0)
+    np.testing.assert_allclose(d["usage"], p, rtol=1e-10)
+    np.testing.assert_allclose(d["h_usage"], -(p * np.log(p)).sum() / np.log(K), rtol=1e-10)
+    g = gbar.reshape(-1, K)
+    np.testing.assert_allclose(d["h_token"], (-(g * np.log(g)).sum(1)).mean() / np.log(K), rtol=1e-9)
+    np.testing.assert_allclose(d["r_max"], g.max(1).mean(), rtol=1e-10)
+    assert np.array_equal(d["argmax"].reshape(-1), g.argmax(1))
+
+
+def test_diagnostics_identical_components():
+    """Identical components in every head: gamma = pi_h for every token, so gbar is the head
+    mean of pi, usage = gbar, both entropies equal H(gbar) / log K and R_max = max gbar."""
+    rng = np.random.default_rng(51)
+    H, K, dr = 3, 5, 2
+    mu = np.repeat(rng.standard_normal((H, 1, dr)), K, axis=1)
+    s2 = np.repeat(np.abs(rng.standard_normal((H, 1, dr))) + 0.5, K, axis=1)
+    a = rng.standard_normal((H, K))
+    pi = np.exp(a) / np.exp(a).sum(1, keepdims=True)
+    x = rng.standard_normal((2, H, 7, dr))
+    d = oracle.diagnostics.diagnostics(x, mu, s2, pi)
+    gb = pi.mean(0)
+    np.testing.assert_allclose(d["usage"], gb, rtol=1e-12)
+    ent = -(gb * np.log(gb)).sum() / np.log(K)
+    np.testing.assert_allclose([d["h_usage"], d["h_token"], d["r_max"]], [ent, ent, gb.max()], rtol=1e-12)
+    assert (d["argmax"] == gb.argmax()).all()
+
+
+def test_diagnostics_sharp_routing_counts():
+    """Well separated components with small variances: each token sits on one mean, so its
+    responsibilities are one-hot (H_token ~ 0, R_max ~ 1), usage is the fraction of tokens on
+    each component and z_t is that component."""
+    rng = np.random.default_rng(52)
+    H, K, dr, N = 2, 4, 3, 50
+    centres = np.eye(K, dr) * 20.0 if K <= dr else rng.standard_normal((K, dr)) * 20.0
+    mu = np.repeat(centres[None], H, axis=0)
+    s2 = np.full((H, K, dr), 0.05)
+    pi = np.full((H, K), 1.0 / K)
+    lab = rng.integers(0, K, (1, N))
+    x = np.repeat(centres[lab][:, None], H, axis=1) + 0.01 * rng.standard_normal((1, H, N, dr))
+    d = oracle.diagnostics.diagnostics(x, mu, s2, pi)
+    assert d["h_token"] < 1e-6 and abs(d["r_max"] - 1.0) < 1e-9
+    np.testing.assert_allclose(d["usage"], np.bincount(lab[0], minlength=K) / N, atol=1e-9)
+    assert np.array_equal(d["argmax"], lab)
+
+
+def test_diagnostics_single_component_and_ties():
+    """K = 1: every gbar is 1, usage 1, both entropies reported as 0, R_max 1, z = 0.  Exactly
+    equal responsibilities pick the lowest component index."""
+    rng = np.random.default_rng(53)
+    x, _, _, mu, s2, pi = rand_problem(rng, 2, 2, 9, 3, 1, 1)
+    d = oracle.diagnostics.diagnostics(x, mu, s2, pi)
+    assert d["h_usage"] == 0.0 and d["h_token"] == 0.0 and d["r_max"] == 1.0 and not d["argmax"].any()
+    G = np.full((1, 2, 3, 4), 0.25)
+    assert (oracle.diagnostics.from_gamma(G)["argmax"] == 0).all()
