@@ -22,9 +22,9 @@ STATUS_NAMES = ["GMA_OK", "GMA_ERR_NULL_POINTER", "GMA_ERR_BAD_SHAPE", "GMA_ERR_
                 "GMA_ERR_UNSUPPORTED", "GMA_ERR_MISALIGNED", "GMA_ERR_WORKSPACE_TOO_SMALL",
                 "GMA_ERR_HIP"]
 GMA_F32, GMA_BF16 = 0, 1
-GMA_OP_RESPONSIBILITIES, GMA_OP_BIDIR, GMA_OP_CAUSAL = 0, 1, 2
+GMA_OP_RESPONSIBILITIES, GMA_OP_BIDIR, GMA_OP_CAUSAL, GMA_OP_DIAGNOSTICS = 0, 1, 2, 3
 EXPORTED = ["gma_status_string", "gma_workspace_size", "gma_responsibilities", "gma_forward_bidir",
-            "gma_forward_causal", "gma_forward_causal_state", "gma_cross_workspace_size", "gma_forward_cross", "gma_profiling",
+            "gma_forward_causal", "gma_forward_causal_state", "gma_cross_workspace_size", "gma_forward_cross", "gma_responsibility_diagnostics", "gma_profiling",
             "gma_profiling_collect", "gma_set_wait_limit"]
 WAIT_LIMIT_DEFAULT = 1 << 18  # GMA_WAIT_LIMIT_DEFAULT
 
@@ -78,6 +78,8 @@ def load() -> ctypes.CDLL:
             lib.gma_forward_causal_state.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, shp, i32, vp, vp, vp, sz,
                                                      vp]
             lib.gma_forward_causal_state.restype = i32
+            lib.gma_responsibility_diagnostics.argtypes = [vp, i32, vp, vp, vp, shp, vp, vp, vp, vp, vp, sz, vp]
+            lib.gma_responsibility_diagnostics.restype = i32
             xshp = ctypes.POINTER(CrossShape)
             lib.gma_cross_workspace_size.argtypes = [xshp, i32, ctypes.POINTER(sz)]
             lib.gma_cross_workspace_size.restype = i32
@@ -218,6 +220,27 @@ def gma_forward_causal_state(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor
                                            int(chunk), _ptr(state_in), _ptr(state_out), _ptr(ws), ws.numel(),
                                            _stream(stream)), "gma_forward_causal_state")
     return out, state_out
+
+
+def gma_responsibility_diagnostics(x: torch.Tensor, mu: torch.Tensor, sigma2: torch.Tensor, pi: torch.Tensor,
+                                   want_argmax: bool = True, want_gbar: bool = False,
+                                   workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Sec. 5.4 diagnostics of routing vectors x [B,H,N,d_r]: usage [K], H_usage, H_token, R_max
+    (Eq. 25-28, as 0-dim tensors), argmax [B,N] int32 (Eq. 29) and gbar [B,N,K] (Eq. 24) if asked."""
+    B, H, N, dr = x.shape
+    K = mu.shape[1]
+    io = _dtype_code(x.dtype)
+    dev = x.device
+    usage = torch.empty(K, dtype=torch.float32, device=dev)
+    stats = torch.empty(4, dtype=torch.float32, device=dev)  # 3 used; 16 bytes keeps the alignment rule
+    z = torch.empty(B, N, dtype=torch.int32, device=dev) if want_argmax else None
+    gbar = torch.empty(B, N, K, dtype=torch.float32, device=dev) if want_gbar else None
+    ws = _workspace(gma_workspace_size(GMA_OP_DIAGNOSTICS, B, H, N, dr, 0, K, io), dev, workspace)
+    _check(load().gma_responsibility_diagnostics(_ptr(x), io, _ptr(mu), _ptr(sigma2), _ptr(pi),
+                                                 ctypes.byref(Shape(B, H, N, dr, 0, K)), _ptr(usage), _ptr(stats),
+                                                 _ptr(z), _ptr(gbar), _ptr(ws), ws.numel(), _stream(stream)),
+           "gma_responsibility_diagnostics")
+    return {"usage": usage, "h_usage": stats[0], "h_token": stats[1], "r_max": stats[2], "argmax": z, "gbar": gbar}
 
 
 def gma_cross_workspace_size(B: int, H: int, N_q: int, N_k: int, d_r: int, d_v: int, K: int, io_dtype: int) -> int:

@@ -30,14 +30,15 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 gma_status_t check_dims(gma_op_t op, const gma_shape_t& s, gma_dtype_t io) {
     if (s.B < 0 || s.H < 0 || s.N < 0) return GMA_ERR_BAD_SHAPE;
     if (s.d_r < 1 || s.K < 1) return GMA_ERR_UNSUPPORTED;
-    if (op != GMA_OP_RESPONSIBILITIES && s.d_v < 1) return GMA_ERR_UNSUPPORTED;
+    const bool has_values = op == GMA_OP_BIDIR || op == GMA_OP_CAUSAL;
+    if (has_values && s.d_v < 1) return GMA_ERR_UNSUPPORTED;
     if (s.K > 256) return GMA_ERR_UNSUPPORTED;
     if (io == GMA_F32) {
         if (s.d_r > 128) return GMA_ERR_UNSUPPORTED;
-        if (op != GMA_OP_RESPONSIBILITIES && s.d_v > 128) return GMA_ERR_UNSUPPORTED;
+        if (has_values && s.d_v > 128) return GMA_ERR_UNSUPPORTED;
     } else {
         if (s.d_r != 16 && s.d_r != 32 && s.d_r != 64 && s.d_r != 128) return GMA_ERR_UNSUPPORTED;
-        if (op != GMA_OP_RESPONSIBILITIES && s.d_v != 32 && s.d_v != 64 && s.d_v != 128)
+        if (has_values && s.d_v != 32 && s.d_v != 64 && s.d_v != 128)
             return GMA_ERR_UNSUPPORTED;
     }
     // guard the int64 products used for sizes
@@ -52,7 +53,7 @@ gma_status_t check_dims(gma_op_t op, const gma_shape_t& s, gma_dtype_t io) {
 void layout(Plan* pl);
 
 gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_t chunk, Plan* pl) {
-    if (op != GMA_OP_RESPONSIBILITIES && op != GMA_OP_BIDIR && op != GMA_OP_CAUSAL)
+    if (op != GMA_OP_RESPONSIBILITIES && op != GMA_OP_BIDIR && op != GMA_OP_CAUSAL && op != GMA_OP_DIAGNOSTICS)
         return GMA_ERR_BAD_VALUE;
     if (io != GMA_F32 && io != GMA_BF16) return GMA_ERR_BAD_VALUE;
     gma_status_t st = check_dims(op, s, io);
@@ -62,7 +63,8 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
     Plan p{};
     p.op = op;
     p.io = io;
-    p.B = s.B; p.H = s.H; p.N = s.N; p.dr = s.d_r; p.dv = (op == GMA_OP_RESPONSIBILITIES) ? 0 : s.d_v;
+    p.B = s.B; p.H = s.H; p.N = s.N; p.dr = s.d_r;
+    p.dv = (op == GMA_OP_BIDIR || op == GMA_OP_CAUSAL) ? s.d_v : 0;
     p.K = s.K;
     p.P = s.B * s.H;
     p.Kp = (io == GMA_BF16) ? round_up(size_t(s.K), 32) : s.K;
@@ -99,6 +101,13 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
     p.Nq = p.N;
     p.seg_q = p.seg;
     layout(&p);
+    if (op == GMA_OP_DIAGNOSTICS) {  // responsibilities of every head, partial sums, and their plan's scratch
+        Plan r;
+        st = make_plan(GMA_OP_RESPONSIBILITIES, s, io, 0, &r);
+        if (st != GMA_OK) return st;
+        p.partials_bytes = p.memory_bytes = p.flags_bytes = 0;
+        p.total = diag_gamma_bytes(p) + diag_partials_bytes(p) + r.total;
+    }
     *pl = p;
     return GMA_OK;
 }
@@ -109,7 +118,7 @@ void layout(Plan* pl) {
     const gma_op_t op = p.op;
     const gma_dtype_t io = p.io;
     const size_t mem_elems = size_t(p.Kp) * size_t(p.dv + 1);
-    p.partials_bytes = (op == GMA_OP_RESPONSIBILITIES) ? 0 : round_up(size_t(p.P * p.G) * mem_elems * 4, 256);
+    p.partials_bytes = (op == GMA_OP_BIDIR || op == GMA_OP_CAUSAL) ? round_up(size_t(p.P * p.G) * mem_elems * 4, 256) : 0;
     p.memory_bytes = (op == GMA_OP_BIDIR) ? round_up(size_t(p.P) * mem_elems * 4, 256) : 0;
     p.off_params = 0;
     p.off_partials = p.off_params + p.params_bytes;
@@ -335,6 +344,24 @@ gma_status_t gma_forward_causal_state(const void* XQ, const void* XK, const void
                                       size_t workspace_bytes, hipStream_t stream) {
     return forward_common(GMA_OP_CAUSAL, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, O, shape, chunk,
                           workspace, workspace_bytes, stream, state_in, state_out);
+}
+
+gma_status_t gma_responsibility_diagnostics(const void* X, gma_dtype_t x_dtype, const float* mu, const float* sigma2,
+                                            const float* pi, const gma_shape_t* shape, float* usage, float* stats,
+                                            int32_t* argmax, float* gbar, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream) {
+    if (!mu || !sigma2 || !pi || !shape || !usage || !stats) return GMA_ERR_NULL_POINTER;
+    Plan p, r;
+    gma_status_t st = gma::make_plan(GMA_OP_DIAGNOSTICS, *shape, x_dtype, 0, &p);
+    if (st != GMA_OK) return st;
+    if ((st = gma::make_plan(GMA_OP_RESPONSIBILITIES, *shape, x_dtype, 0, &r)) != GMA_OK) return st;
+    if (!X && p.P > 0 && p.N > 0) return GMA_ERR_NULL_POINTER;
+    for (const void* q : {X, (const void*)mu, (const void*)sigma2, (const void*)pi, (const void*)usage, (const void*)stats,
+                          (const void*)argmax, (const void*)gbar})
+        if (!gma::aligned16(q)) return GMA_ERR_MISALIGNED;
+    if ((st = check_ws(p, workspace, workspace_bytes)) != GMA_OK) return st;
+    return launch_status(gma::diagnostics(p, r, X, mu, sigma2, pi, usage, stats, argmax, gbar,
+                                          static_cast<char*>(workspace), stream));
 }
 
 gma_status_t gma_cross_workspace_size(const gma_cross_shape_t* shape, gma_dtype_t io_dtype, size_t* bytes_out) {

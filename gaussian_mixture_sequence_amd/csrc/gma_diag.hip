@@ -1,0 +1,165 @@
+// Responsibility diagnostics (Sec. 5.4 of "Gaussian Mixture Attention", Eq. 24-29) of
+// routing vectors X [B,H,N,d_r]: B sequences of N positions, H heads with their own mixtures.
+//   1. Gamma [B,H,N,K] fp32 into the workspace by the responsibilities kernels (Eq. 3)
+//   2. token kernel, per block of 64 positions of one sequence: gbar = head mean of Gamma
+//      (Eq. 24, heads in order), each position's entropy -sum_k gbar log gbar, maximum and
+//      argmax (Eq. 27-29; the lowest k among equal maxima), and the block's fp64 partial sums of
+//      gbar (usage, Eq. 25), of the entropies and of the maxima
+//   3. final kernel: partials summed in block order; usage p_k = sum / T, H_usage = -sum p log p
+//      / log K (Eq. 26), H_token and R_max the means over the T = B N positions
+// Every sum runs in a fixed order, so results are bitwise reproducible.  0 log 0 is 0; with
+// K = 1 both normalised entropies are reported as 0.
+#include <cmath>
+#include <cstdint>
+
+#include "gma_device.h"
+#include "gma_internal.h"
+
+namespace gma {
+namespace diag {
+
+constexpr int kThreads = 256;
+constexpr int kTokens = 64;   // positions per block of the token kernel (16 per wave)
+constexpr int kMaxKPL = 4;    // components per lane (K <= 256)
+
+// (value, index) pair reduction over the wave: the larger value, the lower index on ties.
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(v, o, kWave);
+        const int oi = __shfl_xor(i, o, kWave);
+        if (ov > v || (ov == v && oi < i)) {
+            v = ov;
+            i = oi;
+        }
+    }
+}
+
+// Grid (blocks of kTokens positions, B).  Gamma: [B][H][N][K] fp32.  partials: per block
+// (b-major), K + 2 doubles: sum of gbar per component, sum of entropies, sum of maxima.
+__global__ void __launch_bounds__(kThreads)
+    diag_tokens_kernel(const float* __restrict__ Gamma, int64_t N, int H, int K, int32_t* __restrict__ argmax,
+                       float* __restrict__ gbar, double* __restrict__ partials) {
+    __shared__ double red[kThreads / 64][kMaxKPL * 64 + 2];
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t b = blockIdx.y;
+    const int64_t blk = int64_t(blockIdx.y) * gridDim.x + blockIdx.x;
+    const int KPL = (K + 63) / 64;
+    const float invH = 1.0f / float(H);
+    double acc[kMaxKPL] = {0.0, 0.0, 0.0, 0.0};
+    double ent_sum = 0.0, max_sum = 0.0;
+    for (int q = 0; q < kTokens / (kThreads / 64); ++q) {
+        const int64_t n = int64_t(blockIdx.x) * kTokens + w * (kTokens / (kThreads / 64)) + q;
+        if (n >= N) break;  // uniform over the wave
+        float g[kMaxKPL];
+#pragma unroll
+        for (int u = 0; u < kMaxKPL; ++u) g[u] = 0.0f;
+        for (int h = 0; h < H; ++h) {  // Eq. 24, heads in order
+            const float* row = Gamma + ((size_t(b) * H + h) * N + n) * K;
+#pragma unroll
+            for (int u = 0; u < kMaxKPL; ++u)
+                if (u < KPL && l + 64 * u < K) g[u] += row[l + 64 * u];
+        }
+        float ent = 0.0f, best = -1.0f;
+        int bi = 0;
+#pragma unroll
+        for (int u = 0; u < kMaxKPL; ++u) {
+            if (u < KPL && l + 64 * u < K) {
+                const float v = g[u] * invH;
+                g[u] = v;
+                // natural log; values below the smallest normal float (where the hardware log
+                // flushes to -inf) contribute less than 1e-35 and are skipped
+                if (v >= 1.17549435e-38f) ent -= v * (__builtin_amdgcn_logf(v) * 0.69314718055994530942f);
+                if (v > best) {  // k ascending within the lane: equal values keep the lower k
+                    best = v;
+                    bi = l + 64 * u;
+                }
+                acc[u] += double(v);
+                if (gbar) gbar[(size_t(b) * N + n) * K + l + 64 * u] = v;
+            }
+        }
+        for (int o = 32; o >= 1; o >>= 1) ent += __shfl_xor(ent, o, kWave);
+        wave_argmax(best, bi);
+        if (l == 0) {
+            if (argmax) argmax[size_t(b) * N + n] = bi;
+            ent_sum += double(ent);
+            max_sum += double(best);
+        }
+    }
+    // the block's partial sums: waves combined in wave order
+#pragma unroll
+    for (int u = 0; u < kMaxKPL; ++u) red[w][l + 64 * u] = acc[u];
+    if (l == 0) {
+        red[w][kMaxKPL * 64] = ent_sum;
+        red[w][kMaxKPL * 64 + 1] = max_sum;
+    }
+    __syncthreads();
+    double* out = partials + size_t(blk) * (K + 2);
+    for (int k = threadIdx.x; k < K + 2; k += kThreads) {
+        const int src = k < K ? k : kMaxKPL * 64 + (k - K);
+        double s = 0.0;
+        for (int ww = 0; ww < kThreads / 64; ++ww) s += red[ww][src];
+        out[k] = s;
+    }
+}
+
+// One block: usage [K], stats [3] = H_usage, H_token, R_max (T = 0 gives zeros).
+__global__ void __launch_bounds__(kThreads)
+    diag_final_kernel(const double* __restrict__ partials, int64_t nblk, int K, int64_t T, float* __restrict__ usage,
+                      float* __restrict__ stats) {
+    __shared__ double red[kThreads / 64];
+    const int t = threadIdx.x, l = t & 63, w = t >> 6;
+    double plogp = 0.0;
+    for (int k = t; k < K; k += kThreads) {
+        double s = 0.0;
+        for (int64_t i = 0; i < nblk; ++i) s += partials[size_t(i) * (K + 2) + k];
+        const double p = T > 0 ? s / double(T) : 0.0;
+        usage[k] = float(p);
+        if (p > 0.0) plogp += p * log(p);
+    }
+    for (int o = 32; o >= 1; o >>= 1) plogp += __shfl_xor(plogp, o, kWave);
+    if (l == 0) red[w] = plogp;
+    __syncthreads();
+    if (t == 0) {
+        double pl = 0.0;
+        for (int ww = 0; ww < kThreads / 64; ++ww) pl += red[ww];
+        double es = 0.0, ms = 0.0;
+        for (int64_t i = 0; i < nblk; ++i) {
+            es += partials[size_t(i) * (K + 2) + K];
+            ms += partials[size_t(i) * (K + 2) + K + 1];
+        }
+        const double logk = log(double(K));
+        stats[0] = (K > 1) ? float(-pl / logk) : 0.0f;
+        stats[1] = (K > 1 && T > 0) ? float(es / double(T) / logk) : 0.0f;
+        stats[2] = T > 0 ? float(ms / double(T)) : 0.0f;
+    }
+}
+
+}  // namespace diag
+
+size_t diag_gamma_bytes(const Plan& p) { return round_up(size_t(p.P) * size_t(p.N) * size_t(p.K) * 4, 256); }
+int64_t diag_blocks(const Plan& p) { return p.B * ((p.N + diag::kTokens - 1) / diag::kTokens); }
+size_t diag_partials_bytes(const Plan& p) { return round_up(size_t(diag_blocks(p)) * size_t(p.K + 2) * 8, 256); }
+
+hipError_t diagnostics(const Plan& p, const Plan& resp, const void* X, const float* mu, const float* s2,
+                       const float* pi, float* usage, float* stats, int32_t* argmax, float* gbar, char* ws,
+                       hipStream_t st) {
+    float* gamma = reinterpret_cast<float*>(ws);
+    double* partials = reinterpret_cast<double*>(ws + diag_gamma_bytes(p));
+    char* rws = ws + diag_gamma_bytes(p) + diag_partials_bytes(p);
+    const int64_t nblk = (p.P > 0 && p.N > 0) ? diag_blocks(p) : 0;
+    if (nblk > 0) {
+        hipError_t e = p.io == GMA_F32
+                           ? f32_responsibilities(resp, static_cast<const float*>(X), mu, s2, pi, gamma, GMA_F32, rws, st)
+                           : bf16_responsibilities(resp, X, mu, s2, pi, gamma, GMA_F32, rws, st);
+        if (e != hipSuccess) return e;
+        GMA_LAUNCH("diag_tokens", diag::diag_tokens_kernel,
+                   dim3(unsigned((p.N + diag::kTokens - 1) / diag::kTokens), unsigned(p.B)), dim3(diag::kThreads), 0,
+                   st, gamma, p.N, int(p.H), int(p.K), argmax, gbar, partials);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    GMA_LAUNCH("diag_final", diag::diag_final_kernel, dim3(1), dim3(diag::kThreads), 0, st, partials, nblk, int(p.K),
+               p.B * p.N, usage, stats);
+    return hipGetLastError();
+}
+
+}  // namespace gma

@@ -77,6 +77,15 @@ hipError_t f32_causal(const Plan& p, const float* XQ, const float* XK, const flo
 // memory of a call without positions.
 hipError_t copy_state(const Plan& p, const float* state_in, float* state_out, hipStream_t st);
 
+// ---- responsibility diagnostics (gma_diag.hip) ---------------------------------
+// Workspace: Gamma [B][H][N][K] fp32, then per-block partial sums, then the responsibilities
+// plan's own workspace.
+size_t diag_gamma_bytes(const Plan& p);
+size_t diag_partials_bytes(const Plan& p);
+hipError_t diagnostics(const Plan& p, const Plan& resp, const void* X, const float* mu, const float* s2,
+                       const float* pi, float* usage, float* stats, int32_t* argmax, float* gbar, char* ws,
+                       hipStream_t st);
+
 // ---- short causal calls (gma_decode.hip) --------------------------------------
 // Causal calls of at most this many positions (decoding steps) run one workgroup per problem
 // that walks its positions in order, instead of the chunked scan.

@@ -78,6 +78,9 @@ WORKLOADS: Dict[str, Workload] = {
     # single-token causal decoding with a carried memory: the B=8, H=12 causal dims, one
     # position of each sequence per call (N positions are drawn and cycled through)
     "decode_b8h12_k32": Workload("decode_b8h12_k32", True, 8, 12, 64, 64, 64, 32, "bf16", seed=6, decode=True),
+    # responsibility diagnostics in the paper's setting: 64 sequences of 1024 positions, 8 heads,
+    # K = 128, routing dim d_model / H = 64 (d_v unused)
+    "diag_s64_h8_l1024_k128": Workload("diag_s64_h8_l1024_k128", False, 64, 8, 1024, 64, 32, 128, "bf16", seed=7),
     "cross_b8h8_q4096_k16384": Workload("cross_b8h8_q4096_k16384", False, 8, 8, 4096, 64, 64, 64, "bf16",
                                         seed=5, n_ctx=16384),
 }

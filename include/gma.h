@@ -77,7 +77,8 @@ typedef enum { GMA_F32 = 0, GMA_BF16 = 1 } gma_dtype_t;
 typedef enum {
     GMA_OP_RESPONSIBILITIES = 0,
     GMA_OP_BIDIR = 1,
-    GMA_OP_CAUSAL = 2
+    GMA_OP_CAUSAL = 2,
+    GMA_OP_DIAGNOSTICS = 3
 } gma_op_t;
 
 /* Problem sizes: batch B, heads H, sequence length N, routing dim d_r, value dim d_v,
@@ -196,6 +197,30 @@ gma_status_t gma_forward_cross(const void* XQ, const void* XK, const void* V, gm
                                const float* mu, const float* sigma2, const float* pi, float eps,
                                void* O, const gma_cross_shape_t* shape,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Responsibility diagnostics (Sec. 5.4, Eq. 24-29) of routing vectors X [B,H,N,d_r] of B
+ * sequences of N positions (for instance the query projections of a layer), each head with
+ * its own mixture; T = B N token occurrences t = (b, n):
+ *   gbar[t,k] = (1/H) sum_h gamma[b,h,n,k]                       head-averaged responsibility (Eq. 24)
+ *   usage[k]  = (1/T) sum_t gbar[t,k]                            marginal component usage    (Eq. 25)
+ *   stats[0]  = H_usage = -sum_k usage_k log usage_k / log K     usage entropy               (Eq. 26)
+ *   stats[1]  = H_token = (1/T) sum_t (-sum_k gbar log gbar) / log K   mean token entropy    (Eq. 27)
+ *   stats[2]  = R_max   = (1/T) sum_t max_k gbar[t,k]            mean maximum responsibility (Eq. 28)
+ *   argmax[t] = argmax_k gbar[t,k], the lowest k among equal maxima      hard assignment     (Eq. 29)
+ * with gamma the responsibilities of gma_responsibilities.  0 log 0 is 0; with K = 1 both
+ * normalised entropies are reported as 0; T = 0 gives zeros.
+ *   usage  [K] fp32 out, stats [3] fp32 out (required);
+ *   argmax [B,N] int32 out and gbar [B,N,K] fp32 out (optional, NULL to skip).
+ * Workspace: gma_workspace_size(GMA_OP_DIAGNOSTICS, shape, x_dtype, 0, ...), which holds the
+ * responsibilities of every head (B H N K fp32) and per-block partial sums (shape->d_v is
+ * ignored).  Sums run in a fixed order (bitwise reproducible).  Sizes, dtypes and errors as
+ * for gma_responsibilities.
+ */
+gma_status_t gma_responsibility_diagnostics(const void* X, gma_dtype_t x_dtype, const float* mu, const float* sigma2,
+                                            const float* pi, const gma_shape_t* shape, float* usage, float* stats,
+                                            int32_t* argmax, float* gbar, void* workspace, size_t workspace_bytes,
+                                            hipStream_t stream);
 
 /*
  * Kernel timing (optional tracing).  While enabled, every kernel the library launches is

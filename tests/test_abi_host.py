@@ -209,3 +209,22 @@ def test_causal_state_argument_errors(lib):
     assert f(FAKE, FAKE, FAKE, gb.GMA_F32, FAKE, FAKE, FAKE, 0.0, FAKE, ctypes.byref(sh), 64, None, None, FAKE, need,
              None) == VALUE
     assert f(*args(None, None, n=0)) == OK                       # no positions, no state: nothing to do
+
+
+def test_diagnostics_argument_errors(lib):
+    F, BF = gb.GMA_F32, gb.GMA_BF16
+    D = gb.GMA_OP_DIAGNOSTICS
+    assert ws_size(D, 64, 8, 1024, 64, 0, 128, BF)[0] == OK
+    assert ws_size(D, 64, 8, 1024, 64, 0, 128, BF)[1] >= 64 * 8 * 1024 * 128 * 4   # every head's responsibilities
+    assert ws_size(D, 1, 1, 8, 24, 0, 8, BF)[0] == UNSUP
+    assert ws_size(D, 1, 1, -8, 16, 0, 8, F)[0] == SHAPE
+    shape = (2, 3, 64, 16, 0, 8)
+    need = ws_size(D, *shape, F)[1]
+    f = lib.gma_responsibility_diagnostics
+    sh = ctypes.byref(gb.Shape(*shape))
+    assert f(FAKE, F, FAKE, FAKE, FAKE, sh, None, FAKE, FAKE, FAKE, FAKE, need, None) == NULLP   # usage
+    assert f(FAKE, F, FAKE, FAKE, FAKE, sh, FAKE, None, FAKE, FAKE, FAKE, need, None) == NULLP   # stats
+    assert f(None, F, FAKE, FAKE, FAKE, sh, FAKE, FAKE, None, None, FAKE, need, None) == NULLP
+    assert f(FAKE, F, FAKE, FAKE, FAKE, sh, FAKE, FAKE, FAKE + 4, None, FAKE, need, None) == MISAL
+    assert f(FAKE, F, FAKE, FAKE, FAKE, sh, FAKE, FAKE, None, None, FAKE, need - 1, None) == WS
+    assert f(FAKE, 7, FAKE, FAKE, FAKE, sh, FAKE, FAKE, None, None, FAKE, need, None) == VALUE
