@@ -205,6 +205,8 @@ def alg_bytes_per_token_head(w, kernel: str) -> float:
         return e * (w.d_r + w.d_v) * (w.n_ctx + w.N) / max(w.N, 1)
     if w.decode:  # one position: X_Q, X_K, V in, O out, and the fp32 memory read and written
         return e * (2 * w.d_r + 2 * w.d_v) + 2 * 4 * w.K * (w.d_v + 1)
+    if w.diagnostics:  # the routing vectors in; the outputs (per token, not per head) are negligible
+        return e * w.d_r
     if kernel.endswith("_write") or kernel.endswith("_causal_aggregate"):
         return e * (w.d_r + w.d_v)          # X_K and V in
     if kernel.endswith("_read"):
@@ -215,7 +217,8 @@ def alg_bytes_per_token_head(w, kernel: str) -> float:
 
 
 KERNEL_SYMBOL = {"bf16_scan": "gma::bf::scan_kernel", "bf16_bidir": "gma::bf::bidir_kernel",
-                 "bf16_cross": "gma::bf::bidir_kernel",
+                 "bf16_cross": "gma::bf::bidir_kernel", "bf16_resp": "gma::bf::resp_kernel",
+                 "bf16_decode": "gma::dec::decode_kernel",
                  "bf16_causal": "gma::bf::causal_kernel", "bf16_causal_aggregate": "gma::bf::write_kernel<64, 1"}
 
 
@@ -268,6 +271,8 @@ def main(args=None, probe_only=False) -> int:
         io = gb.GMA_BF16 if w.dtype == "bf16" else gb.GMA_F32
         if w.cross:
             nbytes = gb.gma_cross_workspace_size(w.B, w.H, w.N, w.n_ctx, w.d_r, w.d_v, w.K, io)
+        elif w.diagnostics:
+            nbytes = gb.gma_workspace_size(gb.GMA_OP_DIAGNOSTICS, w.B, w.H, w.N, w.d_r, 0, w.K, io)
         else:
             nbytes = gb.gma_workspace_size(op, w.B, w.H, 1 if w.decode else w.N, w.d_r, w.d_v, w.K, io, w.chunk)
         wss.append(torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev))
@@ -277,7 +282,10 @@ def main(args=None, probe_only=False) -> int:
         s = k % args.sets
         for i, w in enumerate(ws_list):
             d = sets[s][i]
-            if w.decode:
+            if w.diagnostics:
+                gb.gma_responsibility_diagnostics(d["xq"], d["mu"], d["sigma2"], d["pi"], workspace=wss[i],
+                                                  stream=stream)
+            elif w.decode:
                 t = (k // args.sets) % w.N
                 gb.gma_forward_causal_state(d["xq_t"][t], d["xk_t"][t], d["v_t"][t], d["mu"], d["sigma2"], d["pi"],
                                             w.eps, chunk=w.chunk, state_in=d["state"][t % 2],
@@ -331,7 +339,8 @@ def main(args=None, probe_only=False) -> int:
     kernel_of = {}
     for w in ws_list:
         pre = "bf16" if w.dtype == "bf16" else "f32"
-        ks = ["params", "scan", "causal_aggregate", "causal", "prefix", "decode"] if w.causal else \
+        ks = ["resp", "params"] if w.diagnostics else \
+            ["params", "scan", "causal_aggregate", "causal", "prefix", "decode"] if w.causal else \
             ["params", "cross_write", "cross_combine", "cross_read", "cross"] if w.cross else \
             ["params", "write", "combine", "read", "bidir"]
         for k in ks:
@@ -411,6 +420,9 @@ def main(args=None, probe_only=False) -> int:
         tc = time.perf_counter()
         while True:
             for w, d in cpu_inputs:
+                if w.diagnostics:
+                    oracle.diagnostics.diagnostics(d["xq"], d["mu"], d["sigma2"], d["pi"])
+                    continue
                 fn = oracle.forward_causal if w.causal else oracle.forward_cross if w.cross else oracle.forward_bidir
                 fn(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps)
             reps += 1

@@ -14,6 +14,7 @@
 // Every kernel builds the score operands from mu, sigma2 and pi itself (PlaneBuilder: each
 // (component, dim) pair once per workgroup, through LDS; WaveParams::compute per wave where
 // the planes do not fit), so no launch is spent on the parameters.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -27,50 +28,89 @@ namespace bf {
 
 // ---------------------------------------------------------------------------- responsibilities
 
+// Grid (G, P): workgroup (g, p) computes Gamma for rounds [g RPW, (g + 1) RPW) of problem p
+// (ROUND tokens each), so the operand planes, built once per workgroup, serve RPW rounds.
+template <int DR, int KT>
+constexpr size_t resp_plane_bytes() {
+    return PlaneBuilder<DR, KT * 32, Split<DR, KT>::NW * 64>::LDS_BYTES <= 96 * 1024
+               ? PlaneBuilder<DR, KT * 32, Split<DR, KT>::NW * 64>::LDS_BYTES
+               : 16;
+}
+
 template <int DR, int KT>
 __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) resp_kernel(const uint16_t* __restrict__ X, int64_t N,
-                                                                       int H, Mixture mx, void* Gamma,
+                                                                       int H, int RPW, Mixture mx, void* Gamma,
                                                                        int gamma_bf16) {
     using S = Split<DR, KT>;
+    constexpr int NT = S::NW * 64, Kp = KT * 32;
+    using PB = PlaneBuilder<DR, Kp, NT>;
+    constexpr bool COOP = resp_plane_bytes<DR, KT>() > 16;
     __shared__ Stats st[S::TS * S::CS * 32];
+    __shared__ __attribute__((aligned(16))) char planes[resp_plane_bytes<DR, KT>()];
     const int wave = wave_id(), l = threadIdx.x & 63, lh = l >> 5, j = l & 31;
     const int cs = wave % S::CS, ts = wave / S::CS;
     const int64_t p = blockIdx.y;
     const int h = int(p % H), K = mx.K;
     WaveParams<DR, S::CTW> P;
-    P.compute(mx, h, cs * S::CTW);
-    const uint16_t* Xp = X + size_t(p) * N * DR;
-    const int64_t n0 = int64_t(blockIdx.x) * S::ROUND + ts * 32;
-    const int valid = int(max<int64_t>(0, min<int64_t>(32, N - n0)));
-    f32x16 acc[S::CTW];
-    scores<DR, S::CTW>(P, Xp, n0, valid, acc);
-    float m, L, D;
-    float zr[S::CTW][16];
-    local_softmax<S::CTW, false>(acc, zr, m, L, D);
-    if (S::CS > 1) {
-        if (lh == 0) st[(ts * S::CS + cs) * 32 + j] = Stats{m, L, 0.0f};
+    if constexpr (COOP) {  // each (component, dim) pair once per workgroup
+        PB pb;
+        pb.load(mx, h);
+        pb.build(planes, K);
         __syncthreads();
+        P.template read_planes<Kp>(planes, cs * S::CTW);
+    } else {
+        P.compute(mx, h, cs * S::CTW);
     }
-    float dl;
-    const float scale = combine_stats<S::CS>(st, ts, cs, j, m, L, 0.0f, dl);
-    if (j >= valid) return;
-    const size_t rowoff = (size_t(p) * N + n0 + j) * K;
+    const uint16_t* Xp = X + size_t(p) * N * DR;
+    const bool vec = (K & 3) == 0;  // whole groups of 4 components: 16- or 8-byte stores
+    for (int r = 0; r < RPW; ++r) {
+        const int64_t n0 = (int64_t(blockIdx.x) * RPW + r) * S::ROUND + ts * 32;
+        if (n0 - ts * 32 >= N) break;  // uniform over the workgroup
+        const int valid = int(max<int64_t>(0, min<int64_t>(32, N - n0)));
+        f32x16 acc[S::CTW];
+        scores<DR, S::CTW>(P, Xp, n0, valid, acc);
+        float m, L, D;
+        float zr[S::CTW][16];
+        local_softmax<S::CTW, false>(acc, zr, m, L, D);
+        if (S::CS > 1) {
+            __syncthreads();  // the previous round's statistics are read
+            if (lh == 0) st[(ts * S::CS + cs) * 32 + j] = Stats{m, L, 0.0f};
+            __syncthreads();
+        }
+        float dl;
+        const float scale = combine_stats<S::CS>(st, ts, cs, j, m, L, 0.0f, dl);
+        if (j >= valid) continue;
+        const size_t rowoff = (size_t(p) * N + n0 + j) * K;
 #pragma unroll
-    for (int ct = 0; ct < S::CTW; ++ct)
+        for (int ct = 0; ct < S::CTW; ++ct)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int comp = (cs * S::CTW + ct) * 32 + 8 * q + 4 * lh;
+            for (int q = 0; q < 4; ++q) {
+                const int comp = (cs * S::CTW + ct) * 32 + 8 * q + 4 * lh;
+                const float g0 = acc[ct][4 * q] * scale, g1 = acc[ct][4 * q + 1] * scale;
+                const float g2 = acc[ct][4 * q + 2] * scale, g3 = acc[ct][4 * q + 3] * scale;
+                if (vec) {
+                    if (comp < K) {
+                        if (gamma_bf16)
+                            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(Gamma) + rowoff + comp) =
+                                u32x2{pack_bf16x2(g0, g1), pack_bf16x2(g2, g3)};
+                        else
+                            *reinterpret_cast<float4*>(static_cast<float*>(Gamma) + rowoff + comp) =
+                                make_float4(g0, g1, g2, g3);
+                    }
+                } else {
+                    const float gg[4] = {g0, g1, g2, g3};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (comp + e < K) {
-                    const float g = acc[ct][4 * q + e] * scale;
-                    if (gamma_bf16)
-                        static_cast<uint16_t*>(Gamma)[rowoff + comp + e] = f32_to_bf16_bits(g);
-                    else
-                        static_cast<float*>(Gamma)[rowoff + comp + e] = g;
+                    for (int e = 0; e < 4; ++e) {
+                        if (comp + e < K) {
+                            if (gamma_bf16)
+                                static_cast<uint16_t*>(Gamma)[rowoff + comp + e] = f32_to_bf16_bits(gg[e]);
+                            else
+                                static_cast<float*>(Gamma)[rowoff + comp + e] = gg[e];
+                        }
+                    }
                 }
             }
-        }
+    }
 }
 
 // ---------------------------------------------------------------------------- write (standalone)
@@ -464,9 +504,12 @@ hipError_t bf16_responsibilities(const Plan& p, const void* X, const float* mu, 
     return bf::with_dr_kt(int(p.dr), kt_of(p), [&](auto D, auto T) {
         constexpr int DR = decltype(D)::value, KT = decltype(T)::value;
         using S = bf::Split<DR, KT>;
-        dim3 grid(unsigned((p.N + S::ROUND - 1) / S::ROUND), unsigned(p.P));
+        // rounds per workgroup: about 2048 workgroups in all (several waves of them on 256 CUs)
+        const int64_t rounds = (p.N + S::ROUND - 1) / S::ROUND;
+        const int64_t rpw = std::max<int64_t>(1, (p.P * rounds + 2047) / 2048);
+        dim3 grid(unsigned((rounds + rpw - 1) / rpw), unsigned(p.P));
         GMA_LAUNCH("bf16_resp", (bf::resp_kernel<DR, KT>), grid, dim3(S::NW * 64), 0, st,
-                           static_cast<const uint16_t*>(X), p.N, int(p.H), mx, Gamma,
+                           static_cast<const uint16_t*>(X), p.N, int(p.H), int(rpw), mx, Gamma,
                            gamma_dtype == GMA_BF16 ? 1 : 0);
         return hipGetLastError();
     });

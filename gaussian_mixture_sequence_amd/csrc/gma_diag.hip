@@ -5,8 +5,9 @@
 //      (Eq. 24, heads in order), each position's entropy -sum_k gbar log gbar, maximum and
 //      argmax (Eq. 27-29; the lowest k among equal maxima), and the block's fp64 partial sums of
 //      gbar (usage, Eq. 25), of the entropies and of the maxima
-//   3. final kernel: partials summed in block order; usage p_k = sum / T, H_usage = -sum p log p
-//      / log K (Eq. 26), H_token and R_max the means over the T = B N positions
+//   3. column kernel: each of the K + 2 partial columns summed over the blocks in a fixed order;
+//      final kernel: usage p_k = sum / T, H_usage = -sum p log p / log K (Eq. 26), H_token and
+//      R_max the means over the T = B N positions
 // Every sum runs in a fixed order, so results are bitwise reproducible.  0 log 0 is 0; with
 // K = 1 both normalised entropies are reported as 0.
 #include <cmath>
@@ -43,7 +44,10 @@ __global__ void __launch_bounds__(kThreads)
     const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t b = blockIdx.y;
     const int64_t blk = int64_t(blockIdx.y) * gridDim.x + blockIdx.x;
+    // lane l holds components l KPL .. l KPL + KPL - 1 (consecutive: one vector load per row
+    // when KPL is 2 or 4 and divides K)
     const int KPL = (K + 63) / 64;
+    const bool v2 = KPL == 2 && (K & 1) == 0, v4 = KPL == 4 && (K & 3) == 0;
     const float invH = 1.0f / float(H);
     double acc[kMaxKPL] = {0.0, 0.0, 0.0, 0.0};
     double ent_sum = 0.0, max_sum = 0.0;
@@ -54,16 +58,28 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int u = 0; u < kMaxKPL; ++u) g[u] = 0.0f;
         for (int h = 0; h < H; ++h) {  // Eq. 24, heads in order
-            const float* row = Gamma + ((size_t(b) * H + h) * N + n) * K;
+            const float* row = Gamma + ((size_t(b) * H + h) * N + n) * K + l * KPL;
+            if (v4) {
+                if (l * 4 < K) {
+                    const float4 x = *reinterpret_cast<const float4*>(row);
+                    g[0] += x.x; g[1] += x.y; g[2] += x.z; g[3] += x.w;
+                }
+            } else if (v2) {
+                if (l * 2 < K) {
+                    const float2 x = *reinterpret_cast<const float2*>(row);
+                    g[0] += x.x; g[1] += x.y;
+                }
+            } else {
 #pragma unroll
-            for (int u = 0; u < kMaxKPL; ++u)
-                if (u < KPL && l + 64 * u < K) g[u] += row[l + 64 * u];
+                for (int u = 0; u < kMaxKPL; ++u)
+                    if (u < KPL && l * KPL + u < K) g[u] += row[u];
+            }
         }
         float ent = 0.0f, best = -1.0f;
         int bi = 0;
 #pragma unroll
         for (int u = 0; u < kMaxKPL; ++u) {
-            if (u < KPL && l + 64 * u < K) {
+            if (u < KPL && l * KPL + u < K) {
                 const float v = g[u] * invH;
                 g[u] = v;
                 // natural log; values below the smallest normal float (where the hardware log
@@ -71,10 +87,10 @@ __global__ void __launch_bounds__(kThreads)
                 if (v >= 1.17549435e-38f) ent -= v * (__builtin_amdgcn_logf(v) * 0.69314718055994530942f);
                 if (v > best) {  // k ascending within the lane: equal values keep the lower k
                     best = v;
-                    bi = l + 64 * u;
+                    bi = l * KPL + u;
                 }
                 acc[u] += double(v);
-                if (gbar) gbar[(size_t(b) * N + n) * K + l + 64 * u] = v;
+                if (gbar) gbar[(size_t(b) * N + n) * K + l * KPL + u] = v;
             }
         }
         for (int o = 32; o >= 1; o >>= 1) ent += __shfl_xor(ent, o, kWave);
@@ -87,7 +103,7 @@ __global__ void __launch_bounds__(kThreads)
     }
     // the block's partial sums: waves combined in wave order
 #pragma unroll
-    for (int u = 0; u < kMaxKPL; ++u) red[w][l + 64 * u] = acc[u];
+    for (int u = 0; u < kMaxKPL; ++u) red[w][l * kMaxKPL + u] = acc[u];
     if (l == 0) {
         red[w][kMaxKPL * 64] = ent_sum;
         red[w][kMaxKPL * 64 + 1] = max_sum;
@@ -95,24 +111,40 @@ __global__ void __launch_bounds__(kThreads)
     __syncthreads();
     double* out = partials + size_t(blk) * (K + 2);
     for (int k = threadIdx.x; k < K + 2; k += kThreads) {
-        const int src = k < K ? k : kMaxKPL * 64 + (k - K);
+        const int src = k < K ? (k / KPL) * kMaxKPL + k % KPL : kMaxKPL * 64 + (k - K);
         double s = 0.0;
         for (int ww = 0; ww < kThreads / 64; ++ww) s += red[ww][src];
         out[k] = s;
     }
 }
 
-// One block: usage [K], stats [3] = H_usage, H_token, R_max (T = 0 gives zeros).
+// Grid (K + 2): column c of the block partials summed over the nblk blocks, each thread a
+// fixed strided subset in order, then a fixed-shape tree over the threads.
 __global__ void __launch_bounds__(kThreads)
-    diag_final_kernel(const double* __restrict__ partials, int64_t nblk, int K, int64_t T, float* __restrict__ usage,
+    diag_columns_kernel(const double* __restrict__ partials, int64_t nblk, int K, double* __restrict__ cols) {
+    __shared__ double red[kThreads];
+    const int c = blockIdx.x, t = threadIdx.x;
+    double s = 0.0;
+    for (int64_t i = t; i < nblk; i += kThreads) s += partials[size_t(i) * (K + 2) + c];
+    red[t] = s;
+    __syncthreads();
+    for (int o = kThreads / 2; o >= 1; o >>= 1) {
+        if (t < o) red[t] += red[t + o];
+        __syncthreads();
+    }
+    if (t == 0) cols[c] = red[0];
+}
+
+// One block: usage [K], stats [3] = H_usage, H_token, R_max from the K + 2 column sums
+// (T = 0 gives zeros).
+__global__ void __launch_bounds__(kThreads)
+    diag_final_kernel(const double* __restrict__ cols, int K, int64_t T, float* __restrict__ usage,
                       float* __restrict__ stats) {
     __shared__ double red[kThreads / 64];
     const int t = threadIdx.x, l = t & 63, w = t >> 6;
     double plogp = 0.0;
     for (int k = t; k < K; k += kThreads) {
-        double s = 0.0;
-        for (int64_t i = 0; i < nblk; ++i) s += partials[size_t(i) * (K + 2) + k];
-        const double p = T > 0 ? s / double(T) : 0.0;
+        const double p = T > 0 ? cols[k] / double(T) : 0.0;
         usage[k] = float(p);
         if (p > 0.0) plogp += p * log(p);
     }
@@ -122,11 +154,7 @@ __global__ void __launch_bounds__(kThreads)
     if (t == 0) {
         double pl = 0.0;
         for (int ww = 0; ww < kThreads / 64; ++ww) pl += red[ww];
-        double es = 0.0, ms = 0.0;
-        for (int64_t i = 0; i < nblk; ++i) {
-            es += partials[size_t(i) * (K + 2) + K];
-            ms += partials[size_t(i) * (K + 2) + K + 1];
-        }
+        const double es = T > 0 ? cols[K] : 0.0, ms = T > 0 ? cols[K + 1] : 0.0;
         const double logk = log(double(K));
         stats[0] = (K > 1) ? float(-pl / logk) : 0.0f;
         stats[1] = (K > 1 && T > 0) ? float(es / double(T) / logk) : 0.0f;
@@ -138,13 +166,17 @@ __global__ void __launch_bounds__(kThreads)
 
 size_t diag_gamma_bytes(const Plan& p) { return round_up(size_t(p.P) * size_t(p.N) * size_t(p.K) * 4, 256); }
 int64_t diag_blocks(const Plan& p) { return p.B * ((p.N + diag::kTokens - 1) / diag::kTokens); }
-size_t diag_partials_bytes(const Plan& p) { return round_up(size_t(diag_blocks(p)) * size_t(p.K + 2) * 8, 256); }
+size_t diag_partials_bytes(const Plan& p) {  // block partials, then the K + 2 column sums
+    return round_up(size_t(diag_blocks(p)) * size_t(p.K + 2) * 8, 256) + round_up(size_t(p.K + 2) * 8, 256);
+}
 
 hipError_t diagnostics(const Plan& p, const Plan& resp, const void* X, const float* mu, const float* s2,
                        const float* pi, float* usage, float* stats, int32_t* argmax, float* gbar, char* ws,
                        hipStream_t st) {
     float* gamma = reinterpret_cast<float*>(ws);
     double* partials = reinterpret_cast<double*>(ws + diag_gamma_bytes(p));
+    double* cols = reinterpret_cast<double*>(ws + diag_gamma_bytes(p) +
+                                             round_up(size_t(diag_blocks(p)) * size_t(p.K + 2) * 8, 256));
     char* rws = ws + diag_gamma_bytes(p) + diag_partials_bytes(p);
     const int64_t nblk = (p.P > 0 && p.N > 0) ? diag_blocks(p) : 0;
     if (nblk > 0) {
@@ -156,9 +188,12 @@ hipError_t diagnostics(const Plan& p, const Plan& resp, const void* X, const flo
                    dim3(unsigned((p.N + diag::kTokens - 1) / diag::kTokens), unsigned(p.B)), dim3(diag::kThreads), 0,
                    st, gamma, p.N, int(p.H), int(p.K), argmax, gbar, partials);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        GMA_LAUNCH("diag_columns", diag::diag_columns_kernel, dim3(unsigned(p.K + 2)), dim3(diag::kThreads), 0, st,
+                   partials, nblk, int(p.K), cols);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    GMA_LAUNCH("diag_final", diag::diag_final_kernel, dim3(1), dim3(diag::kThreads), 0, st, partials, nblk, int(p.K),
-               p.B * p.N, usage, stats);
+    GMA_LAUNCH("diag_final", diag::diag_final_kernel, dim3(1), dim3(diag::kThreads), 0, st, cols, int(p.K),
+               nblk > 0 ? p.B * p.N : int64_t(0), usage, stats);
     return hipGetLastError();
 }
 

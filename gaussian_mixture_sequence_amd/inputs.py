@@ -42,6 +42,7 @@ class Workload:
     chunk: int = 64     # causal chunk length (ignored by the bidirectional variant)
     n_ctx: int = -1     # cross-attention: context length N_k of XK and V (N is then N_q); -1: self
     decode: bool = False  # causal decoding: one position per call, carrying the memory between calls
+    diagnostics: bool = False  # responsibility diagnostics of X_Q (Sec. 5.4); V and X_K unused
 
     @property
     def tokens(self) -> int:
@@ -80,7 +81,8 @@ WORKLOADS: Dict[str, Workload] = {
     "decode_b8h12_k32": Workload("decode_b8h12_k32", True, 8, 12, 64, 64, 64, 32, "bf16", seed=6, decode=True),
     # responsibility diagnostics in the paper's setting: 64 sequences of 1024 positions, 8 heads,
     # K = 128, routing dim d_model / H = 64 (d_v unused)
-    "diag_s64_h8_l1024_k128": Workload("diag_s64_h8_l1024_k128", False, 64, 8, 1024, 64, 32, 128, "bf16", seed=7),
+    "diag_s64_h8_l1024_k128": Workload("diag_s64_h8_l1024_k128", False, 64, 8, 1024, 64, 32, 128, "bf16", seed=7,
+                                       diagnostics=True),
     "cross_b8h8_q4096_k16384": Workload("cross_b8h8_q4096_k16384", False, 8, 8, 4096, 64, 64, 64, "bf16",
                                         seed=5, n_ctx=16384),
 }
