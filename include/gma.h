@@ -212,9 +212,10 @@ gma_status_t gma_forward_cross(const void* XQ, const void* XK, const void* V, gm
  * normalised entropies are reported as 0; T = 0 gives zeros.
  *   usage  [K] fp32 out, stats [3] fp32 out (required);
  *   argmax [B,N] int32 out and gbar [B,N,K] fp32 out (optional, NULL to skip).
- * Workspace: gma_workspace_size(GMA_OP_DIAGNOSTICS, shape, x_dtype, 0, ...), which holds the
- * responsibilities of every head (B H N K fp32) and per-block partial sums (shape->d_v is
- * ignored).  Sums run in a fixed order (bitwise reproducible).  Sizes, dtypes and errors as
+ * Workspace: gma_workspace_size(GMA_OP_DIAGNOSTICS, shape, x_dtype, 0, ...) (shape->d_v is
+ * ignored): per-block partial sums, and for fp32 input the responsibilities of every head
+ * (B H N K fp32); bf16 input (except d_r = 128 with K > 128) is processed by one fused kernel that
+ * needs only per-head operand tables.  Sums run in a fixed order (bitwise reproducible).  Sizes, dtypes and errors as
  * for gma_responsibilities.
  */
 gma_status_t gma_responsibility_diagnostics(const void* X, gma_dtype_t x_dtype, const float* mu, const float* sigma2,
