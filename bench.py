@@ -51,6 +51,9 @@ def parse():
                          "(CSV output under DIR) into --trace-out")
     ap.add_argument("--trace-out", metavar="FILE", default=None)
     ap.add_argument("--trace-command", default=None, help="the command that produced DIR, recorded in the summary")
+    ap.add_argument("--counters-summarize", metavar="DIR", default=None,
+                    help="summarise rocprofv3 --pmc runs of --traffic-probe step (one subdirectory per pass under DIR) "
+                         "into utilisation figures per library kernel, written to --trace-out")
     return ap.parse_args()
 
 
@@ -181,6 +184,55 @@ def trace_summarize(d: str, out: str, workloads: str, command: str) -> int:
     return 0
 
 
+def counters_summarize(d: str, out: str, workloads: str, command: str) -> int:
+    """SQ counters per library kernel (mean per dispatch, summed over the device) and the
+    derived figures rocprofv3 defines: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD
+    x 1024 SIMDs); VALU busy = SQ_ACTIVE_INST_VALU / 256 CUs / GRBM_GUI_ACTIVE per XCD; LDS bank
+    conflict = SQ_LDS_BANK_CONFLICT / 256 / GRBM_GUI_ACTIVE per XCD; wait and issue fractions of
+    SQ_WAVE_CYCLES."""
+    import csv
+    import glob
+    import re
+    vals = {}
+    for f in glob.glob(os.path.join(d, "**", "*_counter_collection.csv"), recursive=True):
+        per = {}
+        for row in csv.DictReader(open(f)):
+            name = re.sub(r"\(.*", "", row["Kernel_Name"].replace("(anonymous namespace)::", "")).replace("void ", "")
+            if not name.startswith("gma::"):
+                continue
+            key = (name, row["Counter_Name"], row["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+        for (name, ctr, _), v in per.items():
+            vals.setdefault(name, {}).setdefault(ctr, []).append(v)
+    if not vals:
+        print("no library kernels in %s" % d, file=sys.stderr)
+        return 1
+    lines = ["# SQ counter summary: %s" % workloads, "# commands (run from the repository root on one MI355X):"]
+    lines += ["#   " + c for c in (command or "?").split(" ;; ")]
+    for name, ctrs in sorted(vals.items()):
+        m = {c: sum(v) / len(v) for c, v in ctrs.items()}
+        lines.append("%s" % name)
+        for c in sorted(m):
+            lines.append("  %-28s %16.0f" % (c, m[c]))
+        g = m.get("GRBM_GUI_ACTIVE", 0.0) / 8.0  # per XCD
+        if g > 0:
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                lines.append("  %-28s %15.1f%%" % ("MFMA busy", 100.0 * m["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * 1024)))
+            if "SQ_ACTIVE_INST_VALU" in m:
+                lines.append("  %-28s %15.1f%%" % ("VALU busy", 100.0 * m["SQ_ACTIVE_INST_VALU"] / 256 / g))
+            if "SQ_LDS_BANK_CONFLICT" in m:
+                lines.append("  %-28s %15.1f%%" % ("LDS bank-conflict stall", 100.0 * m["SQ_LDS_BANK_CONFLICT"] / 256 / g))
+        if m.get("SQ_WAVE_CYCLES"):
+            for c, label in (("SQ_WAIT_ANY", "waiting on a counter"), ("SQ_WAIT_INST_ANY", "waiting for issue"),
+                             ("SQ_ACTIVE_INST_ANY", "issuing")):
+                if c in m:
+                    lines.append("  %-28s %15.1f%%" % (label + " (of wave time)", 100.0 * m[c] / m["SQ_WAVE_CYCLES"]))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
 def measured_traffic(kernel_symbol_prefix: str, workloads: str):
     """HBM bytes per launch of the kernel, from the workload set's traffic record when that record
     was taken on the current kernel sources."""
@@ -218,7 +270,7 @@ def alg_bytes_per_token_head(w, kernel: str) -> float:
 
 KERNEL_SYMBOL = {"bf16_scan": "gma::bf::scan_kernel", "bf16_bidir": "gma::bf::bidir_kernel",
                  "bf16_cross": "gma::bf::bidir_kernel", "bf16_resp": "gma::bf::resp_kernel",
-                 "bf16_decode": "gma::dec::decode_kernel",
+                 "bf16_decode": "gma::dec::decode_kernel", "bf16_diag": "gma::diag::diag_fused_kernel",
                  "bf16_causal": "gma::bf::causal_kernel", "bf16_causal_aggregate": "gma::bf::write_kernel<64, 1"}
 
 
@@ -228,6 +280,8 @@ def main(args=None, probe_only=False) -> int:
         return traffic_summarize(args.traffic_summarize, args.workloads)
     if args.trace_summarize:
         return trace_summarize(args.trace_summarize, args.trace_out, args.workloads, args.trace_command)
+    if args.counters_summarize:
+        return counters_summarize(args.counters_summarize, args.trace_out, args.workloads, args.trace_command)
     if args.traffic_probe and not probe_only:
         return traffic_probe(args.traffic_probe, args)
     if args.gpus != 1:
@@ -339,7 +393,7 @@ def main(args=None, probe_only=False) -> int:
     kernel_of = {}
     for w in ws_list:
         pre = "bf16" if w.dtype == "bf16" else "f32"
-        ks = ["resp", "params"] if w.diagnostics else \
+        ks = ["diag", "resp", "params"] if w.diagnostics else \
             ["params", "scan", "causal_aggregate", "causal", "prefix", "decode"] if w.causal else \
             ["params", "cross_write", "cross_combine", "cross_read", "cross"] if w.cross else \
             ["params", "write", "combine", "read", "bidir"]
