@@ -194,6 +194,7 @@ def forward_cross(XQ, XK, V, mu, sigma2, pi, eps) -> np.ndarray:
 
 from . import brute  # noqa: E402  (numpy explicit-affinity forms)
 from . import diagnostics  # noqa: E402  (responsibility diagnostics, Sec. 5.4)
+from . import backward  # noqa: E402  (backward pass of the bidirectional forward, Sec. 4.1)
 
 __all__ = ["build", "num_threads", "log_scores", "responsibilities", "forward_bidir",
-           "forward_causal", "forward_causal_state", "forward_cross", "brute", "diagnostics"]
+           "forward_causal", "forward_causal_state", "forward_cross", "brute", "diagnostics", "backward"]

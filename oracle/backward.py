@@ -1,0 +1,65 @@
+"""Backward pass of the bidirectional forward, in numpy fp64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+"Gaussian Mixture Attention: Linear-Time Sequence Mixing via Probabilistic Latent Routing",
+Sec. 4.1: the loss gradient reaches the responsibilities (g = dL/dgamma), passes the softmax
+Jacobian of Eq. 17 as the responsibility-weighted, mean-centred gradient of Eq. 18,
+dL/ds_ik = gamma_ik (g_ik - sum_j gamma_ij g_ij), and reaches every parameter that enters the
+score through the chain rule of Eq. 19.  For the score of Eq. 16 with Sigma_k = diag(sigma2_k):
+  ds/dmu_kd     = (x_d - mu_kd) / sigma2_kd                                   (Eq. 20)
+  ds/dsigma2_kd = ((x_d - mu_kd)^2 / sigma2_kd^2 - 1 / sigma2_kd) / 2
+  ds/dpi_k      = 1 / pi_k      (pi as given at the boundary; Eq. 15 lies upstream)
+  ds/dx_d       = -(x_d - mu_kd) / sigma2_kd
+The upstream gradients g come from Eq. 5-8 (O = N / D, N = Gamma_Q Vt, D = Gamma_Q Z + eps,
+Vt = Gamma_K^T V, Z = Gamma_K^T 1): with a_i = dO_i . O_i,
+  g^Q_ik = (dO_i . Vt_k - a_i Z_k) / D_i,   dVt_k = sum_i gamma^Q_ik dO_i / D_i,
+  dZ_k = -sum_i gamma^Q_ik a_i / D_i,       dV_j = sum_k gamma^K_jk dVt_k,
+  g^K_jk = dVt_k . V_j + dZ_k.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _score_grads(x, ds, mu, s2, pi):
+    """Contributions of one side's score gradients ds [N,K] to dx [N,d], dmu, dsigma2 [K,d], dpi [K]."""
+    diff = x[:, None, :] - mu[None]                 # [N,K,d]
+    w = ds[:, :, None] * diff / s2[None]            # ds_ik (x_id - mu_kd) / sigma2_kd
+    dx = -w.sum(axis=1)
+    dmu = w.sum(axis=0)
+    ds2 = (ds[:, :, None] * 0.5 * (diff * diff / (s2 * s2)[None] - 1.0 / s2[None])).sum(axis=0)
+    dpi = ds.sum(axis=0) / pi
+    return dx, dmu, ds2, dpi
+
+
+def backward_bidir(XQ, XK, V, mu, sigma2, pi, eps, dO) -> dict:
+    """Gradients of <dO, O> for the bidirectional forward O (Sec. 3.3): dXQ, dXK [B,H,N,d_r],
+    dV [B,H,N,d_v], dmu, dsigma2 [H,K,d_r], dpi [H,K]."""
+    from . import _f64, responsibilities
+    XQ, XK, V, dO = (_f64(t) for t in (XQ, XK, V, dO))
+    mu, s2, pi = (_f64(t) for t in (mu, sigma2, pi))
+    GQ, GK = responsibilities(XQ, mu, s2, pi), responsibilities(XK, mu, s2, pi)
+    B, H, N, dr = XQ.shape
+    out = {"dXQ": np.zeros_like(XQ), "dXK": np.zeros_like(XK), "dV": np.zeros_like(V),
+           "dmu": np.zeros_like(mu), "dsigma2": np.zeros_like(s2), "dpi": np.zeros_like(pi)}
+    for b in range(B):
+        for h in range(H):
+            gq, gk, v, do = GQ[b, h], GK[b, h], V[b, h], dO[b, h]
+            vt, z = gk.T @ v, gk.sum(axis=0)                       # Eq. 5-6
+            n_, d_ = gq @ vt, gq @ z + eps                         # Eq. 7-8
+            o = n_ / d_[:, None]
+            a = (do * o).sum(axis=1)
+            g_q = (do @ vt.T - a[:, None] * z[None, :]) / d_[:, None]
+            dvt = gq.T @ (do / d_[:, None])
+            dz = -(gq.T @ (a / d_))
+            out["dV"][b, h] = gk @ dvt
+            g_k = v @ dvt.T + dz[None, :]
+            for x, g, gam, key in ((XQ[b, h], g_q, gq, "dXQ"), (XK[b, h], g_k, gk, "dXK")):
+                ds = gam * (g - (gam * g).sum(axis=1, keepdims=True))   # Eq. 18
+                dx, dmu, ds2, dpi = _score_grads(x, ds, mu[h], s2[h], pi[h])
+                out[key][b, h] = dx
+                out["dmu"][h] += dmu
+                out["dsigma2"][h] += ds2
+                out["dpi"][h] += dpi
+    return out

@@ -564,3 +564,67 @@ def test_diagnostics_single_component_and_ties():
     assert d["h_usage"] == 0.0 and d["h_token"] == 0.0 and d["r_max"] == 1.0 and not d["argmax"].any()
     G = np.full((1, 2, 3, 4), 0.25)
     assert (oracle.diagnostics.from_gamma(G)["argmax"] == 0).all()
+
+
+# --------------------------------------------------------------------------- backward (Sec. 4.1)
+
+def _backward_problem(rng, B=2, H=2, N=9, dr=3, dv=4, K=5):
+    xq, xk, v, mu, s2, pi = rand_problem(rng, B, H, N, dr, dv, K)
+    return xq, xk, v, mu, s2, pi, rng.standard_normal((B, H, N, dv))
+
+
+def test_backward_matches_finite_differences():
+    """<grad, u> equals the central difference of <dO, O> along a random direction u, for
+    every input, with O from the (pinned) forward oracle."""
+    rng = np.random.default_rng(60)
+    xq, xk, v, mu, s2, pi, do = _backward_problem(rng)
+    eps = 1e-3
+    g = oracle.backward.backward_bidir(xq, xk, v, mu, s2, pi, eps, do)
+    args = {"dXQ": xq, "dXK": xk, "dV": v, "dmu": mu, "dsigma2": s2, "dpi": pi}
+    order = ["dXQ", "dXK", "dV", "dmu", "dsigma2", "dpi"]
+    for key in order:
+        u = rng.standard_normal(args[key].shape)
+        h = 1e-6 * (np.abs(args[key]).max() + 1.0)
+        def loss(sign):
+            a = [args[k].copy() for k in order]
+            a[order.index(key)] = a[order.index(key)] + sign * h * u
+            return float((do * oracle.forward_bidir(a[0], a[1], a[2], a[3], a[4], a[5], eps)).sum())
+        fd = (loss(1.0) - loss(-1.0)) / (2 * h)
+        np.testing.assert_allclose((g[key] * u).sum(), fd, rtol=2e-6, atol=1e-9, err_msg=key)
+
+
+def test_backward_matches_torch_autograd():
+    """Every gradient equals torch.autograd in fp64 through a forward built from
+    torch.distributions.Normal log-densities (Eq. 2-3) and Eq. 5-8."""
+    import torch
+    rng = np.random.default_rng(61)
+    xq, xk, v, mu, s2, pi, do = _backward_problem(rng, B=2, H=3, N=11, dr=4, dv=3, K=6)
+    eps = 0.05
+    T = {k: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+         for k, a in dict(xq=xq, xk=xk, v=v, mu=mu, s2=s2, pi=pi).items()}
+
+    def resp(x):
+        # log pi_k + sum_d log Normal(x_d; mu_kd, sqrt(sigma2_kd)), softmax over k
+        lp = torch.distributions.Normal(T["mu"][None, :, None], T["s2"].sqrt()[None, :, None]).log_prob(
+            x[:, :, :, None, :]).sum(-1) + torch.log(T["pi"])[None, :, None]
+        return torch.softmax(lp, dim=-1)
+
+    gq, gk = resp(T["xq"]), resp(T["xk"])
+    vt = gk.transpose(-1, -2) @ T["v"]
+    z = gk.sum(dim=2)
+    o = (gq @ vt) / ((gq * z[:, :, None, :]).sum(-1, keepdim=True) + eps)
+    (o * torch.tensor(do)).sum().backward()
+    g = oracle.backward.backward_bidir(xq, xk, v, mu, s2, pi, eps, do)
+    for key, name in (("dXQ", "xq"), ("dXK", "xk"), ("dV", "v"), ("dmu", "mu"), ("dsigma2", "s2"), ("dpi", "pi")):
+        np.testing.assert_allclose(g[key], T[name].grad.numpy(), rtol=1e-9, atol=1e-12, err_msg=key)
+
+
+def test_backward_values_gradient_closed_form():
+    """K = 1: every responsibility is 1, so O_i = sum_j V_j / (N + eps) and dV_j =
+    sum_i dO_i / (N + eps); routing vectors get no gradient."""
+    rng = np.random.default_rng(62)
+    xq, xk, v, mu, s2, pi, do = _backward_problem(rng, K=1)
+    g = oracle.backward.backward_bidir(xq, xk, v, mu, s2, pi, 0.5, do)
+    ref = do.sum(axis=2, keepdims=True) / (9 + 0.5)
+    np.testing.assert_allclose(g["dV"], np.broadcast_to(ref, g["dV"].shape), rtol=1e-12)
+    assert np.abs(g["dXQ"]).max() < 1e-12 and np.abs(g["dXK"]).max() < 1e-12
