@@ -30,7 +30,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 gma_status_t check_dims(gma_op_t op, const gma_shape_t& s, gma_dtype_t io) {
     if (s.B < 0 || s.H < 0 || s.N < 0) return GMA_ERR_BAD_SHAPE;
     if (s.d_r < 1 || s.K < 1) return GMA_ERR_UNSUPPORTED;
-    const bool has_values = op == GMA_OP_BIDIR || op == GMA_OP_CAUSAL;
+    const bool has_values = op == GMA_OP_BIDIR || op == GMA_OP_CAUSAL || op == GMA_OP_BACKWARD_BIDIR;
     if (has_values && s.d_v < 1) return GMA_ERR_UNSUPPORTED;
     if (s.K > 256) return GMA_ERR_UNSUPPORTED;
     if (io == GMA_F32) {
@@ -53,11 +53,19 @@ gma_status_t check_dims(gma_op_t op, const gma_shape_t& s, gma_dtype_t io) {
 void layout(Plan* pl);
 
 gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_t chunk, Plan* pl) {
-    if (op != GMA_OP_RESPONSIBILITIES && op != GMA_OP_BIDIR && op != GMA_OP_CAUSAL && op != GMA_OP_DIAGNOSTICS)
+    if (op != GMA_OP_RESPONSIBILITIES && op != GMA_OP_BIDIR && op != GMA_OP_CAUSAL && op != GMA_OP_DIAGNOSTICS &&
+        op != GMA_OP_BACKWARD_BIDIR)
         return GMA_ERR_BAD_VALUE;
     if (io != GMA_F32 && io != GMA_BF16) return GMA_ERR_BAD_VALUE;
     gma_status_t st = check_dims(op, s, io);
     if (st != GMA_OK) return st;
+    if (op == GMA_OP_BACKWARD_BIDIR) {  // the forward's plan (fp32 only), then the gradient scratch
+        if (io != GMA_F32) return GMA_ERR_UNSUPPORTED;
+        if ((st = make_plan(GMA_OP_BIDIR, s, io, 0, pl)) != GMA_OK) return st;
+        pl->op = op;
+        pl->total += f32_backward_extra_bytes(*pl);
+        return GMA_OK;
+    }
     if (op == GMA_OP_CAUSAL && chunk != 16 && chunk != 32 && chunk != 64) return GMA_ERR_UNSUPPORTED;
 
     Plan p{};
@@ -362,6 +370,27 @@ gma_status_t gma_responsibility_diagnostics(const void* X, gma_dtype_t x_dtype, 
     if ((st = check_ws(p, workspace, workspace_bytes)) != GMA_OK) return st;
     return launch_status(gma::diagnostics(p, r, X, mu, sigma2, pi, usage, stats, argmax, gbar,
                                           static_cast<char*>(workspace), stream));
+}
+
+gma_status_t gma_backward_bidir(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                                const float* mu, const float* sigma2, const float* pi, float eps, const void* dO,
+                                void* dXQ, void* dXK, void* dV, float* dmu, float* dsigma2, float* dpi,
+                                const gma_shape_t* shape, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!mu || !sigma2 || !pi || !shape) return GMA_ERR_NULL_POINTER;
+    Plan p;
+    gma_status_t st = gma::make_plan(GMA_OP_BACKWARD_BIDIR, *shape, io_dtype, 0, &p);
+    if (st != GMA_OK) return st;
+    if ((!dmu || !dsigma2 || !dpi) && p.H > 0) return GMA_ERR_NULL_POINTER;
+    if ((!XQ || !XK || !V || !dO || !dXQ || !dXK || !dV) && p.P > 0 && p.N > 0) return GMA_ERR_NULL_POINTER;
+    if (!(eps > 0.0f) || !std::isfinite(eps)) return GMA_ERR_BAD_VALUE;
+    for (const void* q : {XQ, XK, V, (const void*)mu, (const void*)sigma2, (const void*)pi, dO, (const void*)dXQ,
+                          (const void*)dXK, (const void*)dV, (const void*)dmu, (const void*)dsigma2, (const void*)dpi})
+        if (!gma::aligned16(q)) return GMA_ERR_MISALIGNED;
+    if ((st = check_ws(p, workspace, workspace_bytes)) != GMA_OK) return st;
+    return launch_status(gma::f32_backward_bidir(
+        p, static_cast<const float*>(XQ), static_cast<const float*>(XK), static_cast<const float*>(V), mu, sigma2,
+        pi, eps, static_cast<const float*>(dO), static_cast<float*>(dXQ), static_cast<float*>(dXK),
+        static_cast<float*>(dV), dmu, dsigma2, dpi, static_cast<char*>(workspace), stream));
 }
 
 gma_status_t gma_cross_workspace_size(const gma_cross_shape_t* shape, gma_dtype_t io_dtype, size_t* bytes_out) {

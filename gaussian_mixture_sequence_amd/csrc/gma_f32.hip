@@ -440,4 +440,240 @@ hipError_t f32_causal(const Plan& p, const float* XQ, const float* XK, const flo
     return hipGetLastError();
 }
 
+// ============================================================================ backward
+// Gradients of <dO, O> for the bidirectional forward (Sec. 4.1 of "Gaussian Mixture
+// Attention": the softmax Jacobian of Eq. 17, the centred score gradient of Eq. 18 and the
+// chain rule of Eq. 19-20 through the direct-form score of Eq. 16), fp32 with the fp64 score
+// tables of the forward.  With a_i = dO_i . O_i and D_i = gamma^Q_i . Z + eps:
+//   g^Q_ik = (dO_i . Vt_k - a_i Z_k) / D_i,      dVt_k = sum_i gamma^Q_ik dO_i / D_i,
+//   dZ_k = -sum_i gamma^Q_ik a_i / D_i,          dV_j = sum_k gamma^K_jk dVt_k,
+//   g^K_jk = dVt_k . V_j + dZ_k,                  ds_ik = gamma_ik (g_ik - sum_l gamma_il g_il),
+//   dx_id = -sum_k ds_ik (x_id - mu_kd) / sigma2_kd,
+//   dmu_kd += ds_ik (x_id - mu_kd) / sigma2_kd,   dsigma2_kd += ds_ik ((x_id - mu_kd)^2 / sigma2_kd^2
+//   - 1 / sigma2_kd) / 2,                         dpi_k += ds_ik / pi_k.
+namespace {
+
+// LDS floats of one side's tile of T rows.
+size_t bwd_lds_bytes(int T, int dr, int dv, int K) { return size_t(T) * (dr + 2 * K + dv + 2) * sizeof(float); }
+
+// Grid (G, P): rows [g seg, (g + 1) seg) of problem p in tiles of T.  QUERY: the query side
+// (reads the memory mem = [Vt | Z], writes dX_Q and the partial [dVt | dZ] of its rows);
+// otherwise the key side (reads dmem = [dVt | dZ], writes dV and dX_K).  Both add their rows'
+// parameter gradients into the block's partial record pp = [dmu (K dr) | dsigma2 (K dr) | dpi
+// (K)] (first tile writes, later tiles add: each entry has one owner thread).
+template <bool QUERY>
+__global__ void __launch_bounds__(kThreads)
+    f32_bwd_side_kernel(const float* __restrict__ X, const float* __restrict__ Y, int64_t N, int H, int dr, int dv,
+                        int K, int64_t seg, int G, int T, const double* c, const double* inv, const float* mu,
+                        const float* __restrict__ pi, const float* __restrict__ mem, float eps,
+                        float* __restrict__ dX, float* __restrict__ dY, float* __restrict__ mem_part,
+                        float* __restrict__ param_part) {
+    extern __shared__ float lds[];
+    const int64_t p = blockIdx.y;
+    const int gi = blockIdx.x, h = int(p % H);
+    float* xs = lds;          // T*dr: the tile's routing vectors (left by gamma_tile)
+    float* gm = xs + T * dr;  // T*K: responsibilities
+    float* gg = gm + T * K;   // T*K: upstream gradient, then the score gradient
+    float* ys = gg + T * K;   // T*dv: dO (query side) or V (key side)
+    float* dd = ys + T * dv;  // T: D_i
+    float* aa = dd + T;       // T: a_i
+    const double *ch = c + size_t(h) * K, *ih = inv + size_t(h) * K * dr;
+    const float* mh = mu + size_t(h) * K * dr;
+    const float* Vt = mem + size_t(p) * K * (dv + 1);  // [K][dv], then Z (or dVt, dZ)
+    const float* Z = Vt + size_t(K) * dv;
+    const int E = K * (dv + 1), PE = 2 * K * dr + K;
+    float* mp = mem_part ? mem_part + (size_t(p) * G + gi) * E : nullptr;
+    float* pp = param_part + (size_t(p) * G + gi) * PE;
+    const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    bool first = true;
+    for (int64_t n0 = lo; n0 < hi; n0 += T) {
+        const int rows = int(min<int64_t>(T, hi - n0));
+        gamma_tile(X + p * N * dr, n0, rows, T, dr, K, ch, ih, mh, xs, gm);
+        for (int i = threadIdx.x; i < T * dv; i += kThreads) {
+            const int t = i / dv;
+            ys[i] = t < rows ? Y[(p * N + n0) * dv + i] : 0.0f;
+        }
+        __syncthreads();
+        if (QUERY) {  // D_t and a_t = dO_t . O_t, one wave per row
+            for (int t = wave; t < rows; t += kThreads / kWave) {
+                float d = 0.0f;
+                for (int k = lane; k < K; k += kWave) d = fmaf(gm[t * K + k], Z[k], d);
+                d = wave_sum(d) + eps;
+                float a = 0.0f;
+                for (int cc = lane; cc < dv; cc += kWave) {
+                    float nn = 0.0f;
+                    for (int k = 0; k < K; ++k) nn = fmaf(gm[t * K + k], Vt[size_t(k) * dv + cc], nn);
+                    a = fmaf(ys[t * dv + cc], nn / d, a);
+                }
+                a = wave_sum(a);
+                if (lane == 0) {
+                    dd[t] = d;
+                    aa[t] = a;
+                }
+            }
+            __syncthreads();
+        } else {  // dV_tc = sum_k gamma^K_tk dVt_kc
+            for (int i = threadIdx.x; i < rows * dv; i += kThreads) {
+                const int t = i / dv, cc = i - t * dv;
+                float acc = 0.0f;
+                for (int k = 0; k < K; ++k) acc = fmaf(gm[t * K + k], Vt[size_t(k) * dv + cc], acc);
+                dY[(p * N + n0) * dv + i] = acc;
+            }
+        }
+        // upstream gradient at the responsibilities
+        for (int i = threadIdx.x; i < T * K; i += kThreads) {
+            const int t = i / K, k = i - t * K;
+            float acc = 0.0f;
+            if (t < rows) {
+                for (int cc = 0; cc < dv; ++cc) acc = fmaf(ys[t * dv + cc], Vt[size_t(k) * dv + cc], acc);
+                acc = QUERY ? (acc - aa[t] * Z[k]) / dd[t] : acc + Z[k];
+            }
+            gg[i] = acc;
+        }
+        __syncthreads();
+        // Eq. 18: ds = gamma (g - gamma . g), one wave per row
+        for (int t = wave; t < T; t += kThreads / kWave) {
+            float w = 0.0f;
+            for (int k = lane; k < K; k += kWave) w = fmaf(gm[t * K + k], gg[t * K + k], w);
+            w = wave_sum(w);
+            for (int k = lane; k < K; k += kWave) gg[t * K + k] = gm[t * K + k] * (gg[t * K + k] - w);
+        }
+        __syncthreads();
+        // routing-vector gradient
+        for (int i = threadIdx.x; i < rows * dr; i += kThreads) {
+            const int t = i / dr, d = i - t * dr;
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k)
+                acc = fmaf(gg[t * K + k], float((double(xs[t * dr + d]) - double(mh[size_t(k) * dr + d])) * ih[size_t(k) * dr + d]), acc);
+            dX[(p * N + n0) * dr + i] = -acc;
+        }
+        // parameter gradients of these rows (Eq. 19-20)
+        for (int e = threadIdx.x; e < K * dr; e += kThreads) {
+            const int k = e / dr, d = e - k * dr;
+            const double m = double(mh[e]), iv = ih[e];
+            double am = 0.0, as = 0.0;
+            for (int t = 0; t < rows; ++t) {
+                const double df = double(xs[t * dr + d]) - m, s = double(gg[t * K + k]);
+                am += s * df * iv;
+                as += s * 0.5 * (df * df * iv * iv - iv);
+            }
+            pp[e] = first ? float(am) : pp[e] + float(am);
+            pp[K * dr + e] = first ? float(as) : pp[K * dr + e] + float(as);
+        }
+        for (int k = threadIdx.x; k < K; k += kThreads) {
+            float acc = 0.0f;
+            for (int t = 0; t < rows; ++t) acc += gg[t * K + k];
+            acc /= pi[size_t(h) * K + k];
+            pp[2 * K * dr + k] = first ? acc : pp[2 * K * dr + k] + acc;
+        }
+        if (QUERY) {  // partial [dVt | dZ] of these rows, in the memory's layout
+            for (int e = threadIdx.x; e < E; e += kThreads) {
+                float acc = 0.0f;
+                if (e < K * dv) {
+                    const int k = e / dv, cc = e - k * dv;
+                    for (int t = 0; t < rows; ++t) acc = fmaf(gm[t * K + k], ys[t * dv + cc] / dd[t], acc);
+                } else {
+                    const int k = e - K * dv;
+                    for (int t = 0; t < rows; ++t) acc -= gm[t * K + k] * aa[t] / dd[t];
+                }
+                mp[e] = first ? acc : mp[e] + acc;
+            }
+        }
+        first = false;
+        __syncthreads();  // the tile's LDS is free
+    }
+    if (first) {  // empty block
+        for (int e = threadIdx.x; e < PE; e += kThreads) pp[e] = 0.0f;
+        if (QUERY)
+            for (int e = threadIdx.x; e < E; e += kThreads) mp[e] = 0.0f;
+    }
+}
+
+// Grid (ceil(PE / kThreads), H): the parameter gradients of head h, one entry per thread, summed
+// over the query and key sides, the batch and the splits in that fixed order.  With B == 0 it
+// writes zeros (no rows, no gradient).
+__global__ void __launch_bounds__(kThreads)
+    f32_bwd_param_reduce_kernel(const float* __restrict__ param_part, int B, int H, int G, int K, int dr,
+                                float* __restrict__ dmu, float* __restrict__ ds2, float* __restrict__ dpi) {
+    const int h = blockIdx.y, PE = 2 * K * dr + K;
+    const int e = blockIdx.x * kThreads + threadIdx.x;
+    if (e >= PE) return;
+    const size_t P = size_t(B) * H;
+    float acc = 0.0f;
+    for (int side = 0; side < 2; ++side)
+        for (int b = 0; b < B; ++b)
+            for (int g = 0; g < G; ++g) acc += param_part[((side * P + size_t(b) * H + h) * G + g) * PE + e];
+    if (e < K * dr) dmu[size_t(h) * K * dr + e] = acc;
+    else if (e < 2 * K * dr) ds2[size_t(h) * K * dr + e - K * dr] = acc;
+    else dpi[size_t(h) * K + e - 2 * K * dr] = acc;
+}
+
+}  // namespace
+
+size_t f32_backward_extra_bytes(const Plan& p) {
+    const size_t E = size_t(p.K) * size_t(p.dv + 1);
+    return round_up(size_t(p.P * p.G) * E * 4, 256) + round_up(size_t(p.P) * E * 4, 256) +
+           round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256);
+}
+
+namespace {
+hipError_t reduce_params(const Plan& p, const float* ppart, int B, float* dmu, float* ds2, float* dpi, hipStream_t st) {
+    const int PE = int(2 * p.K * p.dr + p.K);
+    GMA_LAUNCH("f32_bwd_params", f32_bwd_param_reduce_kernel, dim3(unsigned((PE + kThreads - 1) / kThreads), unsigned(p.H)),
+               dim3(kThreads), 0, st, ppart, B, int(p.H), int(p.G), int(p.K), int(p.dr), dmu, ds2, dpi);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
+                              const float* s2, const float* pi, float eps, const float* dO, float* dXQ, float* dXK,
+                              float* dV, float* dmu, float* ds2, float* dpi, char* ws, hipStream_t st) {
+    if (p.H == 0) return hipSuccess;
+    if (p.P == 0 || p.N == 0) return reduce_params(p, nullptr, 0, dmu, ds2, dpi, st);  // zero gradients
+    static const hipError_t attr = [] {
+        const void* fns[] = {(const void*)f32_bwd_side_kernel<true>, (const void*)f32_bwd_side_kernel<false>};
+        for (const void* f : fns) {
+            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }();
+    if (attr != hipSuccess) return attr;
+    hipError_t e = launch_params(p, s2, pi, ws, st);
+    if (e != hipSuccess) return e;
+    F32Params v = f32_params_view(p, ws);
+    float* partials = reinterpret_cast<float*>(ws + p.off_partials);
+    float* memory = reinterpret_cast<float*>(ws + p.off_memory);
+    const size_t E = size_t(p.K) * size_t(p.dv + 1);
+    char* extra = ws + p.total - f32_backward_extra_bytes(p);
+    float* dpart = reinterpret_cast<float*>(extra);
+    float* dmem = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256));
+    float* ppart = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256) + round_up(size_t(p.P) * E * 4, 256));
+    // the forward's memory
+    size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
+    GMA_LAUNCH("f32_bwd_write", f32_write_kernel, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads), lds_w, st, XK, V,
+               p.N, int(p.H), int(p.dr), int(p.dv), int(p.K), p.seg, int(p.G), v.c, v.inv, mu, partials);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int Ei = int(E);
+    GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, dim3(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P)),
+               dim3(kThreads), 0, st, partials, int(p.G), Ei, memory);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    int T = kTile;
+    while (T > 8 && bwd_lds_bytes(T, int(p.dr), int(p.dv), int(p.K)) > kMaxLds) T /= 2;
+    const size_t lds = bwd_lds_bytes(T, int(p.dr), int(p.dv), int(p.K));
+    GMA_LAUNCH("f32_bwd_query", f32_bwd_side_kernel<true>, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads), lds, st,
+               XQ, dO, p.N, int(p.H), int(p.dr), int(p.dv), int(p.K), p.seg, int(p.G), T, v.c, v.inv, mu, pi, memory,
+               eps, dXQ, static_cast<float*>(nullptr), dpart, ppart);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, dim3(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P)),
+               dim3(kThreads), 0, st, dpart, int(p.G), Ei, dmem);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    GMA_LAUNCH("f32_bwd_key", f32_bwd_side_kernel<false>, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads), lds, st,
+               XK, V, p.N, int(p.H), int(p.dr), int(p.dv), int(p.K), p.seg, int(p.G), T, v.c, v.inv, mu, pi, dmem,
+               eps, dXK, dV, static_cast<float*>(nullptr), ppart + size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return reduce_params(p, ppart, int(p.B), dmu, ds2, dpi, st);
+}
+
 }  // namespace gma

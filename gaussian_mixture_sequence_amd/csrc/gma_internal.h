@@ -77,6 +77,13 @@ hipError_t f32_causal(const Plan& p, const float* XQ, const float* XK, const flo
 // memory of a call without positions.
 hipError_t copy_state(const Plan& p, const float* state_in, float* state_out, hipStream_t st);
 
+// Backward of the bidirectional forward (fp32): workspace beyond the bidirectional plan's
+// own (placed at its end), and the launcher.
+size_t f32_backward_extra_bytes(const Plan& p);
+hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
+                              const float* s2, const float* pi, float eps, const float* dO, float* dXQ, float* dXK,
+                              float* dV, float* dmu, float* ds2, float* dpi, char* ws, hipStream_t st);
+
 // ---- responsibility diagnostics (gma_diag.hip) ---------------------------------
 // Workspace: Gamma [B][H][N][K] fp32, then per-block partial sums, then the responsibilities
 // plan's own workspace.

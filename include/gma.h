@@ -78,7 +78,8 @@ typedef enum {
     GMA_OP_RESPONSIBILITIES = 0,
     GMA_OP_BIDIR = 1,
     GMA_OP_CAUSAL = 2,
-    GMA_OP_DIAGNOSTICS = 3
+    GMA_OP_DIAGNOSTICS = 3,
+    GMA_OP_BACKWARD_BIDIR = 4
 } gma_op_t;
 
 /* Problem sizes: batch B, heads H, sequence length N, routing dim d_r, value dim d_v,
@@ -222,6 +223,35 @@ gma_status_t gma_responsibility_diagnostics(const void* X, gma_dtype_t x_dtype, 
                                             const float* pi, const gma_shape_t* shape, float* usage, float* stats,
                                             int32_t* argmax, float* gbar, void* workspace, size_t workspace_bytes,
                                             hipStream_t stream);
+
+/*
+ * Backward pass of the bidirectional forward (gma_forward_bidir) for the loss gradient dO:
+ * the gradients of <dO, O> with respect to every input, Sec. 4.1 Eq. 17-20.  With the
+ * forward's Vt, Z, D_i = (Gamma_Q Z)_i + eps and a_i = dO_i . O_i, the upstream gradients at
+ * the responsibilities are
+ *   g^Q_ik = (dO_i . Vt_k - a_i Z_k) / D_i                 (query side)
+ *   g^K_jk = dVt_k . V_j + dZ_k                            (key side)
+ * with dVt_k = sum_i Gamma_Q[i,k] dO_i / D_i and dZ_k = -sum_i Gamma_Q[i,k] a_i / D_i; they pass
+ * the softmax Jacobian as ds_ik = gamma_ik (g_ik - sum_l gamma_il g_il) (Eq. 18) and reach the
+ * routing vectors and the mixture parameters through the score of Eq. 16 (Eq. 19-20):
+ *   dX[i,d] = -sum_k ds_ik (x_id - mu_kd) / sigma2_kd, dmu[k,d] = sum_i ds_ik (x_id - mu_kd) / sigma2_kd,
+ *   dsigma2[k,d] = sum_i ds_ik ((x_id - mu_kd)^2 / sigma2_kd^2 - 1 / sigma2_kd) / 2,
+ *   dpi[k] = sum_i ds_ik / pi_k      (pi as passed in; its parameterisation lies upstream),
+ * the parameter sums running over both sides, every sequence and every position.  Also
+ *   dV[j,:] = sum_k Gamma_K[j,k] dVt_k.
+ *   XQ, XK, dXQ, dXK [B,H,N,d_r]; V, dO, dV [B,H,N,d_v]; mu, sigma2, dmu, dsigma2 [H,K,d_r];
+ *   pi, dpi [H,K].  Every tensor fp32 (io_dtype must be GMA_F32; GMA_BF16 is
+ *   GMA_ERR_UNSUPPORTED).  The gradient outputs are overwritten, not accumulated into.
+ * Workspace: gma_workspace_size(GMA_OP_BACKWARD_BIDIR, shape, GMA_F32, 0, ...): the forward's
+ * memory and its split partials, the same for (dVt, dZ), and per-split parameter partials,
+ * reduced in a fixed order (bitwise reproducible).  Sizes, alignment and errors as for
+ * gma_forward_bidir; with no rows (B N = 0) the parameter gradients are zeros.
+ */
+gma_status_t gma_backward_bidir(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                                const float* mu, const float* sigma2, const float* pi, float eps,
+                                const void* dO, void* dXQ, void* dXK, void* dV, float* dmu, float* dsigma2,
+                                float* dpi, const gma_shape_t* shape, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream);
 
 /*
  * Kernel timing (optional tracing).  While enabled, every kernel the library launches is

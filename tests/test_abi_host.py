@@ -231,3 +231,39 @@ def test_diagnostics_argument_errors(lib):
     assert f(FAKE, F, FAKE, FAKE, FAKE, sh, FAKE, FAKE, FAKE + 4, None, FAKE, need, None) == MISAL
     assert f(FAKE, F, FAKE, FAKE, FAKE, sh, FAKE, FAKE, None, None, FAKE, need - 1, None) == WS
     assert f(FAKE, 7, FAKE, FAKE, FAKE, sh, FAKE, FAKE, None, None, FAKE, need, None) == VALUE
+
+
+def test_backward_argument_errors(lib):
+    F, BF = gb.GMA_F32, gb.GMA_BF16
+    Bw = gb.GMA_OP_BACKWARD_BIDIR
+    assert ws_size(Bw, 8, 8, 4096, 64, 64, 64, F)[0] == OK
+    assert ws_size(Bw, 8, 8, 4096, 64, 64, 64, BF)[0] == UNSUP   # fp32 only
+    assert ws_size(Bw, 1, 1, 8, 16, 0, 8, F)[0] == UNSUP          # needs values
+    assert ws_size(Bw, 1, 1, 8, 129, 32, 8, F)[0] == UNSUP
+    assert ws_size(Bw, 1, -1, 8, 16, 32, 8, F)[0] == SHAPE
+    # more scratch than the forward: the gradient memory and the parameter partials
+    assert ws_size(Bw, 8, 8, 4096, 64, 64, 64, F)[1] > ws_size(gb.GMA_OP_BIDIR, 8, 8, 4096, 64, 64, 64, F)[1]
+    shape = (2, 3, 64, 16, 32, 8)
+    need = ws_size(Bw, *shape, F)[1]
+    sh = ctypes.byref(gb.Shape(*shape))
+
+    def call(xq=FAKE, io=F, pi=FAKE, eps=1e-6, d_o=FAKE, dxk=FAKE, dmu=FAKE, dpi=FAKE, ws=FAKE, nb=need, s=sh):
+        return lib.gma_backward_bidir(xq, FAKE, FAKE, io, FAKE, FAKE, pi, eps, d_o, FAKE, dxk, FAKE, dmu, FAKE, dpi,
+                                      s, ws, nb, None)
+
+    assert call(xq=None) == NULLP
+    assert call(d_o=None) == NULLP
+    assert call(dxk=None) == NULLP
+    assert call(dmu=None) == NULLP
+    assert call(pi=None) == NULLP
+    assert call(ws=None) == NULLP
+    assert call(io=BF) == UNSUP
+    assert call(io=9) == VALUE
+    assert call(eps=0.0) == VALUE
+    assert call(eps=float("nan")) == VALUE
+    assert call(d_o=FAKE + 4) == MISAL
+    assert call(dpi=FAKE + 8) == MISAL
+    assert call(nb=need - 1) == WS
+    # no heads: nothing to write, returns before any HIP call
+    sh0 = gb.Shape(2, 0, 64, 16, 32, 8)
+    assert call(s=ctypes.byref(sh0), nb=ws_size(Bw, 2, 0, 64, 16, 32, 8, F)[1], dmu=None, dpi=None) == OK

@@ -1,0 +1,146 @@
+"""GPU parity of the backward pass of the bidirectional forward (Sec. 4.1, Eq. 17-20) through
+the C ABI, against the fp64 oracle's backward on the same seeded inputs and upstream gradient.
+
+Error measure: per output tensor, max |g - g*| / max |g*| (tensor-scaled).  The gradients are
+sums of responsibility-weighted terms of both signs (the centring of Eq. 18 makes every row of
+ds sum to zero), so single entries can be far below the tensor's scale and an elementwise
+relative error is ill-posed.  Bound: the kernels evaluate the scores in fp64 and everything
+after the softmax in fp32 (sums over K, d_v and the positions of a split), so the error is a
+few hundred fp32 roundings of the tensor's scale; 1e-4 leaves a margin of about 10x over what
+the longest reductions here (N up to 5000, K up to 256) accumulate."""
+import numpy as np
+import pytest
+import torch
+
+import oracle.backward
+from gaussian_mixture_sequence_amd import binding as gb
+from gaussian_mixture_sequence_amd.inputs import WORKLOADS, Workload, head_slice, make_inputs
+from gma_testutil import to_device, to_np
+
+pytestmark = pytest.mark.gpu
+
+TOL_BWD = 1e-4
+KEYS = ("dXQ", "dXK", "dV", "dmu", "dsigma2", "dpi")
+
+
+def upstream(w: Workload, seed: int) -> torch.Tensor:
+    """dO [B,H,N,d_v]: standard normal, seeded (the loss gradient is an input of the pass)."""
+    gen = torch.Generator().manual_seed(seed)
+    return torch.randn(w.B, w.H, w.N, w.d_v, generator=gen, dtype=torch.float32)
+
+
+def tensor_error(out, ref) -> float:
+    out, ref = np.asarray(out, np.float64), np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    return float(np.abs(out - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def run_gpu(w: Workload, inp, d_o):
+    d = to_device(inp)
+    g = gb.gma_backward_bidir(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], d_o.cuda(), w.eps)
+    torch.cuda.synchronize()
+    return {k: to_np(v) for k, v in g.items()}
+
+
+def run_oracle(w: Workload, inp, d_o):
+    return oracle.backward.backward_bidir(inp["xq"], inp["xk"], inp["v"], inp["mu"], inp["sigma2"], inp["pi"],
+                                          w.eps, d_o)
+
+
+def case(N, seed, **kw):
+    base = WORKLOADS["bidir_small_f32"]
+    return base.with_(name="bwd", N=N, seed=seed, **dict(dict(B=1, H=2), **kw))
+
+
+def cid(w):
+    return "B%dH%d-N%d-dr%d-dv%d-K%d" % (w.B, w.H, w.N, w.d_r, w.d_v, w.K)
+
+
+CASES = [
+    WORKLOADS["bidir_small_f32"],
+    case(1000, 91, B=2, H=3, d_r=7, d_v=5, K=13),       # ragged dims and tail
+    case(2, 92),                                        # two positions, one tile
+    case(5000, 93, d_r=32, d_v=64, K=64),              # several splits per problem
+    case(300, 94, B=1, H=1, d_r=128, d_v=128, K=256),  # maximum dims (half-height tiles)
+    case(700, 95, B=3, H=2, d_r=64, d_v=32, K=128, mu_std=1.5),
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=cid)
+def test_backward_parity(w):
+    inp = make_inputs(w)
+    d_o = upstream(w, w.seed + 1000)
+    got, ref = run_gpu(w, inp, d_o), run_oracle(w, inp, d_o)
+    for k in KEYS:
+        assert got[k].shape == ref[k].shape, k
+        assert np.isfinite(got[k]).all(), k
+        err = tensor_error(got[k], ref[k])
+        assert err <= TOL_BWD, (k, err)
+
+
+def test_backward_single_position():
+    """N = 1: the one key is the whole memory, so O = v r / (r + eps) with r = gamma_Q . gamma_K;
+    the routing enters only through the eps term.  dV = dO r / (r + eps) is well conditioned
+    and must match; the routing and parameter gradients are O(eps) exact values that any
+    fp32 evaluation of (dO . Vt - a Z) / D obtains by cancellation, so they are only required
+    to be finite."""
+    w = case(1, 92)
+    inp = make_inputs(w)
+    d_o = upstream(w, 1092)
+    got, ref = run_gpu(w, inp, d_o), run_oracle(w, inp, d_o)
+    assert tensor_error(got["dV"], ref["dV"]) <= TOL_BWD
+    for k in KEYS:
+        assert got[k].shape == ref[k].shape and np.isfinite(got[k]).all(), k
+
+
+def test_backward_deterministic():
+    """Fixed reduction orders: two calls give bit-identical gradients."""
+    w = case(3000, 96, B=2, H=2)
+    inp = make_inputs(w)
+    d_o = upstream(w, 1096)
+    a, b = run_gpu(w, inp, d_o), run_gpu(w, inp, d_o)
+    for k in KEYS:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_backward_no_rows_gives_zero_parameter_gradients():
+    """N = 0: no term reaches the mixture parameters; their gradients are overwritten with 0."""
+    w = case(0, 97)
+    inp = make_inputs(w)
+    d = to_device(inp)
+    g = gb.gma_backward_bidir(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"],
+                              torch.empty(w.B, w.H, 0, w.d_v, device="cuda"), w.eps)
+    torch.cuda.synchronize()
+    for k in ("dmu", "dsigma2", "dpi"):
+        assert not to_np(g[k]).any(), k
+    assert g["dXQ"].numel() == 0 and g["dV"].numel() == 0
+
+
+def test_backward_bf16_unsupported():
+    w = WORKLOADS["bidir_small_f32"]
+    inp = {k: (v.bfloat16() if k in ("xq", "xk", "v") else v) for k, v in make_inputs(w).items()}
+    d = to_device(inp)
+    with pytest.raises(gb.GmaError) as e:
+        gb.gma_backward_bidir(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"],
+                              torch.zeros(w.B, w.H, w.N, w.d_v, dtype=torch.bfloat16, device="cuda"), w.eps)
+    assert "UNSUPPORTED" in str(e.value)
+
+
+def test_backward_full_size_sampled_heads():
+    """The B=8, H=8, N=4096, d_r=d_v=K=64 dims in fp32 (the split plan of the bench's backward
+    step): the per-position gradients of sampled (batch, head) problems against the oracle run
+    on that problem alone (each problem's dX and dV depend only on its own rows)."""
+    w = WORKLOADS["bidir_b8h8_n4096"].with_(dtype="f32", name="bwd_full")
+    inp = make_inputs(w)
+    d_o = upstream(w, 2001)
+    got = run_gpu(w, inp, d_o)
+    for b, h in ((0, 0), (3, 5), (7, 7)):
+        sl = head_slice(inp, b, h)
+        ref = oracle.backward.backward_bidir(sl["xq"], sl["xk"], sl["v"], sl["mu"], sl["sigma2"], sl["pi"], w.eps,
+                                             d_o[b:b + 1, h:h + 1])
+        for k in ("dXQ", "dXK", "dV"):
+            err = tensor_error(got[k][b:b + 1, h:h + 1], ref[k])
+            assert err <= TOL_BWD, (b, h, k, err)
+    for k in ("dmu", "dsigma2", "dpi"):
+        assert np.isfinite(got[k]).all(), k
