@@ -259,6 +259,16 @@ def alg_bytes_per_token_head(w, kernel: str) -> float:
         return e * (2 * w.d_r + 2 * w.d_v) + 2 * 4 * w.K * (w.d_v + 1)
     if w.diagnostics:  # the routing vectors in; the outputs (per token, not per head) are negligible
         return e * w.d_r
+    if w.backward:
+        if kernel.endswith("_bwd_write"):
+            return e * (w.d_r + w.d_v)          # X_K and V in
+        if kernel.endswith("_bwd_query"):
+            return e * (2 * w.d_r + w.d_v)      # X_Q and dO in, dX_Q out
+        if kernel.endswith("_bwd_key"):
+            return e * (2 * w.d_r + 2 * w.d_v)  # X_K and V in, dX_K and dV out
+        if kernel == "step":
+            return e * (4 * w.d_r + 3 * w.d_v)  # X_Q, X_K, V, dO in; dX_Q, dX_K, dV out
+        return 0.0
     if kernel.endswith("_write") or kernel.endswith("_causal_aggregate"):
         return e * (w.d_r + w.d_v)          # X_K and V in
     if kernel.endswith("_read"):
@@ -271,7 +281,35 @@ def alg_bytes_per_token_head(w, kernel: str) -> float:
 KERNEL_SYMBOL = {"bf16_scan": "gma::bf::scan_kernel", "bf16_bidir": "gma::bf::bidir_kernel",
                  "bf16_cross": "gma::bf::bidir_kernel", "bf16_resp": "gma::bf::resp_kernel",
                  "bf16_decode": "gma::dec::decode_kernel", "bf16_diag": "gma::diag::diag_fused_kernel",
+                 "f32_bwd_query": "gma::f32_bwd_side_kernel<true>",
+                 "f32_bwd_key": "gma::f32_bwd_side_kernel<false>",
                  "bf16_causal": "gma::bf::causal_kernel", "bf16_causal_aggregate": "gma::bf::write_kernel<64, 1"}
+
+
+def cpu_backward_sample(cpu_inputs):
+    """The oracle's backward (numpy fp64) on successive (batch, head) problems of the workload until
+    about 10 s have been timed; a problem of N positions is N / H tokens of the whole workload."""
+    import oracle.backward
+    w, d = cpu_inputs[0]
+    done = 0
+    tc = time.perf_counter()
+    while True:
+        b, h = divmod(done % (w.B * w.H), w.H)
+        sl = {k: (v[b:b + 1, h:h + 1] if k in ("xq", "xk", "v", "d_o") else v[h:h + 1]) for k, v in d.items()}
+        oracle.backward.backward_bidir(sl["xq"], sl["xk"], sl["v"], sl["mu"], sl["sigma2"], sl["pi"], w.eps, sl["d_o"])
+        done += 1
+        cpu_s = time.perf_counter() - tc
+        if cpu_s >= 10.0:
+            break
+    try:  # numpy's BLAS pool runs the matrix products; everything else is one thread
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except ImportError:
+        threads = 1
+    return {"value": round(done * w.N / w.H / cpu_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d (batch, head) problems of %d positions (the first of the workload's %d, in order), "
+                      "numpy fp64 backward oracle (BLAS pool for the matrix products); %.2f s wall; a problem is N / H = %g tokens"
+                      % (done, w.N, w.B * w.H, cpu_s, w.N / w.H)}
 
 
 def main(args=None, probe_only=False) -> int:
@@ -319,14 +357,23 @@ def main(args=None, probe_only=False) -> int:
     outs, wss = [], []
     for i, w in enumerate(ws_list):
         dt = sets[0][i]["xq"].dtype
-        outs.append([torch.empty(w.B, w.H, 1 if w.decode else w.N, w.d_v, dtype=dt, device=dev)
-                     for _ in range(args.sets)])
+        if w.backward:
+            d0 = sets[0][i]
+            outs.append([{"dXQ": torch.empty_like(d0["xq"]), "dXK": torch.empty_like(d0["xk"]),
+                          "dV": torch.empty_like(d0["v"]), "dmu": torch.empty_like(d0["mu"]),
+                          "dsigma2": torch.empty_like(d0["sigma2"]), "dpi": torch.empty_like(d0["pi"])}
+                         for _ in range(args.sets)])
+        else:
+            outs.append([torch.empty(w.B, w.H, 1 if w.decode else w.N, w.d_v, dtype=dt, device=dev)
+                         for _ in range(args.sets)])
         op = gb.GMA_OP_CAUSAL if w.causal else gb.GMA_OP_BIDIR
         io = gb.GMA_BF16 if w.dtype == "bf16" else gb.GMA_F32
         if w.cross:
             nbytes = gb.gma_cross_workspace_size(w.B, w.H, w.N, w.n_ctx, w.d_r, w.d_v, w.K, io)
         elif w.diagnostics:
             nbytes = gb.gma_workspace_size(gb.GMA_OP_DIAGNOSTICS, w.B, w.H, w.N, w.d_r, 0, w.K, io)
+        elif w.backward:
+            nbytes = gb.gma_workspace_size(gb.GMA_OP_BACKWARD_BIDIR, w.B, w.H, w.N, w.d_r, w.d_v, w.K, io)
         else:
             nbytes = gb.gma_workspace_size(op, w.B, w.H, 1 if w.decode else w.N, w.d_r, w.d_v, w.K, io, w.chunk)
         wss.append(torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev))
@@ -339,6 +386,9 @@ def main(args=None, probe_only=False) -> int:
             if w.diagnostics:
                 gb.gma_responsibility_diagnostics(d["xq"], d["mu"], d["sigma2"], d["pi"], workspace=wss[i],
                                                   stream=stream)
+            elif w.backward:
+                gb.gma_backward_bidir(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], d["d_o"], w.eps,
+                                      out=outs[i][s], workspace=wss[i], stream=stream)
             elif w.decode:
                 t = (k // args.sets) % w.N
                 gb.gma_forward_causal_state(d["xq_t"][t], d["xk_t"][t], d["v_t"][t], d["mu"], d["sigma2"], d["pi"],
@@ -393,7 +443,8 @@ def main(args=None, probe_only=False) -> int:
     kernel_of = {}
     for w in ws_list:
         pre = "bf16" if w.dtype == "bf16" else "f32"
-        ks = ["diag", "resp", "params"] if w.diagnostics else \
+        ks = ["params", "bwd_write", "bwd_combine", "bwd_query", "bwd_key", "bwd_params"] if w.backward else \
+            ["diag", "resp", "params"] if w.diagnostics else \
             ["params", "scan", "causal_aggregate", "causal", "prefix", "decode"] if w.causal else \
             ["params", "cross_write", "cross_combine", "cross_read", "cross"] if w.cross else \
             ["params", "write", "combine", "read", "bidir"]
@@ -423,12 +474,13 @@ def main(args=None, probe_only=False) -> int:
 
     # ---- sanity: outputs finite
     for i in range(len(ws_list)):
-        if not torch.isfinite(outs[i][0].float()).all():
+        o = outs[i][0]
+        if not all(torch.isfinite(t.float()).all() for t in (o.values() if isinstance(o, dict) else [o])):
             print("bench.py: non-finite output in %s" % names[i], file=sys.stderr)
             return 1
 
-    step_bytes = sum(w.B * w.H * (1 if w.decode else w.N) * alg_bytes_per_token_head(w, "bf16_scan")
-                     for w in ws_list)
+    step_bytes = sum(w.B * w.H * (1 if w.decode else w.N) *
+                     alg_bytes_per_token_head(w, "step" if w.backward else "bf16_scan") for w in ws_list)
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -440,12 +492,13 @@ def main(args=None, probe_only=False) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if any(w.dtype == "bf16" for w in ws_list) else "f32",
         "data": "synthetic (seeded; mu~N(0,1), sigma2=softplus(N(0,1))+1e-3, pi=softmax(N(0,1)), "
                 "X_Q,X_K,V~N(0,1); %d rotating input sets)" % args.sets,
         "config": {
             "workload": " + ".join("%s (%s B=%d H=%d %s d_r=%d d_v=%d K=%d%s)" % (
-                w.name, "causal" if w.causal else "cross" if w.cross else "bidir", w.B, w.H,
+                w.name, "causal" if w.causal else "cross" if w.cross else "bidir backward" if w.backward else "bidir",
+                w.B, w.H,
                 "N_q=%d N_k=%d" % (w.N, w.n_ctx) if w.cross else "N=%d" % w.N, w.d_r, w.d_v, w.K,
                 ", chunk=%d" % w.chunk if w.causal else "") for w in ws_list),
             "tokens_per_step": tokens_per_step,
@@ -469,25 +522,28 @@ def main(args=None, probe_only=False) -> int:
         # the oracle over every position of every workload (for decoding: all N positions, which
         # equals N one-position steps with the memory carried), repeated until about 10 s of CPU
         # work have been timed
-        cpu_tokens = sum(w.B * w.N for w in ws_list)
-        reps = 0
-        tc = time.perf_counter()
-        while True:
-            for w, d in cpu_inputs:
-                if w.diagnostics:
-                    oracle.diagnostics.diagnostics(d["xq"], d["mu"], d["sigma2"], d["pi"])
-                    continue
-                fn = oracle.forward_causal if w.causal else oracle.forward_cross if w.cross else oracle.forward_bidir
-                fn(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps)
-            reps += 1
-            cpu_s = time.perf_counter() - tc
-            if cpu_s >= 10.0 or reps >= 100000:
-                break
-        result["cpu_baseline"] = {
-            "value": round(cpu_tokens * reps / cpu_s, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "the whole workload (%d tokens: every position of every sequence) %d times, fp64 C oracle "
-                      "with OpenMP over (batch, head); %.2f s wall" % (cpu_tokens, reps, cpu_s)}
+        if any(w.backward for w in ws_list):
+            result["cpu_baseline"] = cpu_backward_sample([c for c in cpu_inputs if c[0].backward])
+        else:
+            cpu_tokens = sum(w.B * w.N for w in ws_list)
+            reps = 0
+            tc = time.perf_counter()
+            while True:
+                for w, d in cpu_inputs:
+                    if w.diagnostics:
+                        oracle.diagnostics.diagnostics(d["xq"], d["mu"], d["sigma2"], d["pi"])
+                        continue
+                    fn = oracle.forward_causal if w.causal else oracle.forward_cross if w.cross else oracle.forward_bidir
+                    fn(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps)
+                reps += 1
+                cpu_s = time.perf_counter() - tc
+                if cpu_s >= 10.0 or reps >= 100000:
+                    break
+            result["cpu_baseline"] = {
+                "value": round(cpu_tokens * reps / cpu_s, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
+                "kind": "oracle",
+                "sample": "the whole workload (%d tokens: every position of every sequence) %d times, fp64 C oracle "
+                          "with OpenMP over (batch, head); %.2f s wall" % (cpu_tokens, reps, cpu_s)}
     print(json.dumps(result))
     return 0
 

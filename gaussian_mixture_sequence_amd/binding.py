@@ -249,16 +249,18 @@ def gma_responsibility_diagnostics(x: torch.Tensor, mu: torch.Tensor, sigma2: to
 
 def gma_backward_bidir(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, mu: torch.Tensor,
                        sigma2: torch.Tensor, pi: torch.Tensor, d_o: torch.Tensor, eps: float = 1e-6,
-                       workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+                       out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
     """Gradients of <d_o, O> for the bidirectional forward O (Sec. 4.1, Eq. 17-20), fp32:
-    dXQ, dXK [B,H,N,d_r], dV [B,H,N,d_v], dmu, dsigma2 [H,K,d_r], dpi [H,K]."""
+    dXQ, dXK [B,H,N,d_r], dV [B,H,N,d_v], dmu, dsigma2 [H,K,d_r], dpi [H,K] (into `out` when given,
+    a dict with those keys)."""
     B, H, N, dr = xq.shape
     dv = v.shape[-1]
     K = mu.shape[1]
     io = _dtype_code(xq.dtype)
     dev = xq.device
-    out = {"dXQ": torch.empty_like(xq), "dXK": torch.empty_like(xk), "dV": torch.empty_like(v),
-           "dmu": torch.empty_like(mu), "dsigma2": torch.empty_like(sigma2), "dpi": torch.empty_like(pi)}
+    if out is None:
+        out = {"dXQ": torch.empty_like(xq), "dXK": torch.empty_like(xk), "dV": torch.empty_like(v),
+               "dmu": torch.empty_like(mu), "dsigma2": torch.empty_like(sigma2), "dpi": torch.empty_like(pi)}
     ws = _workspace(gma_workspace_size(GMA_OP_BACKWARD_BIDIR, B, H, N, dr, dv, K, io), dev, workspace)
     _check(load().gma_backward_bidir(_ptr(xq), _ptr(xk), _ptr(v), io, _ptr(mu), _ptr(sigma2), _ptr(pi),
                                      float(eps), _ptr(d_o), _ptr(out["dXQ"]), _ptr(out["dXK"]), _ptr(out["dV"]),

@@ -44,28 +44,32 @@ F32Params f32_params_view(const Plan& p, char* ws) {
 
 // One block per head.  c_k = log pi_k - 1/2 sum_d log sigma2_kd in fp64, then shifted by
 // its maximum over k (a k-independent shift, exact in the softmax) so the fp32 value is small.
+// Each wave takes one component at a time, its lanes over d.
 __global__ void __launch_bounds__(kThreads) f32_params_kernel(const float* __restrict__ s2,
                                                               const float* __restrict__ pi, int K,
                                                               int dr, double* __restrict__ c_out,
                                                               double* __restrict__ inv_out) {
     const int h = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     __shared__ double cd[256];
     __shared__ double red[kThreads / kWave];
     const float* s2h = s2 + size_t(h) * K * dr;
-    double local_max = -INFINITY;
-    for (int k = threadIdx.x; k < K; k += kThreads) {
-        double acc = log(double(pi[size_t(h) * K + k]));
-        for (int d = 0; d < dr; ++d) {
-            double v = double(s2h[size_t(k) * dr + d]);
-            acc -= 0.5 * log(v);
+    for (int k = wave; k < K; k += kThreads / kWave) {
+        double acc = 0.0;
+        for (int d = lane; d < dr; d += kWave) {
+            const double v = double(s2h[size_t(k) * dr + d]);
+            acc += log(v);
             inv_out[(size_t(h) * K + k) * dr + d] = 1.0 / v;
         }
-        cd[k] = acc;
-        local_max = fmax(local_max, acc);
+        for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+        if (lane == 0) cd[k] = log(double(pi[size_t(h) * K + k])) - 0.5 * acc;
     }
+    __syncthreads();
+    double local_max = -INFINITY;
+    for (int k = threadIdx.x; k < K; k += kThreads) local_max = fmax(local_max, cd[k]);
     // block max
     for (int o = 32; o >= 1; o >>= 1) local_max = fmax(local_max, __shfl_xor(local_max, o, kWave));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = local_max;
+    if (lane == 0) red[wave] = local_max;
     __syncthreads();
     double m = red[0];
     for (int w = 1; w < kThreads / kWave; ++w) m = fmax(m, red[w]);
@@ -443,31 +447,32 @@ hipError_t f32_causal(const Plan& p, const float* XQ, const float* XK, const flo
 // ============================================================================ backward
 // Gradients of <dO, O> for the bidirectional forward (Sec. 4.1 of "Gaussian Mixture
 // Attention": the softmax Jacobian of Eq. 17, the centred score gradient of Eq. 18 and the
-// chain rule of Eq. 19-20 through the direct-form score of Eq. 16), fp32 with the fp64 score
-// tables of the forward.  With a_i = dO_i . O_i and D_i = gamma^Q_i . Z + eps:
-//   g^Q_ik = (dO_i . Vt_k - a_i Z_k) / D_i,      dVt_k = sum_i gamma^Q_ik dO_i / D_i,
-//   dZ_k = -sum_i gamma^Q_ik a_i / D_i,          dV_j = sum_k gamma^K_jk dVt_k,
+// chain rule of Eq. 19-20 through the direct-form score of Eq. 16), fp32.  With
+// D_i = gamma^Q_i . Z + eps, dO'_i = dO_i / D_i and a'_i = dO_i . O_i / D_i:
+//   g^Q_ik = dO'_i . Vt_k - a'_i Z_k,            dVt_k = sum_i gamma^Q_ik dO'_i,
+//   dZ_k = -sum_i gamma^Q_ik a'_i,                dV_j = sum_k gamma^K_jk dVt_k,
 //   g^K_jk = dVt_k . V_j + dZ_k,                  ds_ik = gamma_ik (g_ik - sum_l gamma_il g_il),
-//   dx_id = -sum_k ds_ik (x_id - mu_kd) / sigma2_kd,
-//   dmu_kd += ds_ik (x_id - mu_kd) / sigma2_kd,   dsigma2_kd += ds_ik ((x_id - mu_kd)^2 / sigma2_kd^2
-//   - 1 / sigma2_kd) / 2,                         dpi_k += ds_ik / pi_k.
+//   dx_id = -sum_k ds_ik (x_id - mu_kd) / sigma2_kd.
+// The mixture parameters see every row of both sides through three moments per split,
+//   S0_k = sum_i ds_ik,  S1_kd = sum_i ds_ik (x_id - mu_kd),  S2_kd = sum_i ds_ik (x_id - mu_kd)^2,
+// kept in the direct (centred) form, from which dmu_kd = S1_kd / sigma2_kd,
+// dsigma2_kd = (S2_kd / sigma2_kd^2 - S0_k / sigma2_kd) / 2 and dpi_k = S0_k / pi_k.
+// Partial records per (problem, split): [S1 (K d_r) | S2 (K d_r) | S0 (K)].
 namespace {
 
-// LDS floats of one side's tile of T rows.
+// ---- general sizes: one thread per output element, LDS tiles of T rows
 size_t bwd_lds_bytes(int T, int dr, int dv, int K) { return size_t(T) * (dr + 2 * K + dv + 2) * sizeof(float); }
 
 // Grid (G, P): rows [g seg, (g + 1) seg) of problem p in tiles of T.  QUERY: the query side
 // (reads the memory mem = [Vt | Z], writes dX_Q and the partial [dVt | dZ] of its rows);
-// otherwise the key side (reads dmem = [dVt | dZ], writes dV and dX_K).  Both add their rows'
-// parameter gradients into the block's partial record pp = [dmu (K dr) | dsigma2 (K dr) | dpi
-// (K)] (first tile writes, later tiles add: each entry has one owner thread).
+// otherwise the key side (reads dmem = [dVt | dZ], writes dV and dX_K).  Both write the
+// block's moment record pp (first tile writes, later tiles add: each entry has one owner).
 template <bool QUERY>
 __global__ void __launch_bounds__(kThreads)
     f32_bwd_side_kernel(const float* __restrict__ X, const float* __restrict__ Y, int64_t N, int H, int dr, int dv,
                         int K, int64_t seg, int G, int T, const double* c, const double* inv, const float* mu,
-                        const float* __restrict__ pi, const float* __restrict__ mem, float eps,
-                        float* __restrict__ dX, float* __restrict__ dY, float* __restrict__ mem_part,
-                        float* __restrict__ param_part) {
+                        const float* __restrict__ mem, float eps, float* __restrict__ dX, float* __restrict__ dY,
+                        float* __restrict__ mem_part, float* __restrict__ param_part) {
     extern __shared__ float lds[];
     const int64_t p = blockIdx.y;
     const int gi = blockIdx.x, h = int(p % H);
@@ -548,23 +553,22 @@ __global__ void __launch_bounds__(kThreads)
                 acc = fmaf(gg[t * K + k], float((double(xs[t * dr + d]) - double(mh[size_t(k) * dr + d])) * ih[size_t(k) * dr + d]), acc);
             dX[(p * N + n0) * dr + i] = -acc;
         }
-        // parameter gradients of these rows (Eq. 19-20)
+        // moments of these rows
         for (int e = threadIdx.x; e < K * dr; e += kThreads) {
             const int k = e / dr, d = e - k * dr;
-            const double m = double(mh[e]), iv = ih[e];
-            double am = 0.0, as = 0.0;
+            const double m = double(mh[e]);
+            double a1 = 0.0, a2 = 0.0;
             for (int t = 0; t < rows; ++t) {
-                const double df = double(xs[t * dr + d]) - m, s = double(gg[t * K + k]);
-                am += s * df * iv;
-                as += s * 0.5 * (df * df * iv * iv - iv);
+                const double df = double(xs[t * dr + d]) - m, w = double(gg[t * K + k]) * df;
+                a1 += w;
+                a2 += w * df;
             }
-            pp[e] = first ? float(am) : pp[e] + float(am);
-            pp[K * dr + e] = first ? float(as) : pp[K * dr + e] + float(as);
+            pp[e] = first ? float(a1) : pp[e] + float(a1);
+            pp[K * dr + e] = first ? float(a2) : pp[K * dr + e] + float(a2);
         }
         for (int k = threadIdx.x; k < K; k += kThreads) {
             float acc = 0.0f;
             for (int t = 0; t < rows; ++t) acc += gg[t * K + k];
-            acc /= pi[size_t(h) * K + k];
             pp[2 * K * dr + k] = first ? acc : pp[2 * K * dr + k] + acc;
         }
         if (QUERY) {  // partial [dVt | dZ] of these rows, in the memory's layout
@@ -590,23 +594,486 @@ __global__ void __launch_bounds__(kThreads)
     }
 }
 
-// Grid (ceil(PE / kThreads), H): the parameter gradients of head h, one entry per thread, summed
-// over the query and key sides, the batch and the splits in that fixed order.  With B == 0 it
-// writes zeros (no rows, no gradient).
+// ---- register-tiled passes for K, d_r, d_v <= 64 (multiples of 4)
+// 256 threads as 16 row groups x 16 column groups: thread (tr, mc) owns rows r0 = 4 tr .. r0 + 3
+// and columns m0 = 4 mc .. m0 + 3 of every 64 x 64 product of a tile; operands are read from
+// LDS as 16-byte vectors.  The 16 threads of a row group are 16 adjacent lanes of one wave,
+// so row reductions are 16-lane shuffles.
+constexpr int kBT = 64;        // rows per tile
+constexpr int kLDT = kBT + 4;  // row stride of the transposed ([L][T]) tiles
+enum { BWD_WRITE = 0, BWD_QUERY = 1, BWD_KEY = 2 };
+
+bool bwd_tiled_applies(const Plan& p) {
+    return p.K % 4 == 0 && p.dr % 4 == 0 && p.dv % 4 == 0 && p.K <= 64 && p.dr <= 64 && p.dv <= 64;
+}
+
+size_t bwd_tiled_lds_bytes(int mode, int K, int dr, int dv) {
+    const bool qk = mode != BWD_WRITE;
+    size_t f = size_t(2 * dr * (K + 4) + K);                 // mu^T, (1/sigma2)^T, c
+    if (qk) f += size_t(2 * K * dv + K);                     // memory (or its gradient), transposed, and Z
+    if (qk) f += size_t(dr * kLDT) + size_t(K * kLDT) + size_t(kBT * K);  // X^T, gamma^T (then ds^T), gamma (then ds)
+    else f += size_t(max(dr * kLDT, kBT * K));               // X^T, then gamma in the same space
+    if (mode != BWD_KEY) f += size_t(kBT * dv);              // V (write) or dO / D (query)
+    if (qk) f += size_t(dv * kLDT);                          // (dO / D)^T (query) or V^T (key)
+    if (mode == BWD_QUERY) f += 2 * kBT;                     // D, a'
+    return f * sizeof(float);
+}
+
+__device__ __forceinline__ float4 lds4(const float* q) { return *reinterpret_cast<const float4*>(q); }
+__device__ __forceinline__ void put4(float* q, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(q) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void unpack(const float4 v, float (&a)[4]) {
+    a[0] = v.x, a[1] = v.y, a[2] = v.z, a[3] = v.w;
+}
+__device__ __forceinline__ float sum16(float v) {
+    for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 16);
+    return v;
+}
+__device__ __forceinline__ float max16(float v) {
+    for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 16));
+    return v;
+}
+
+// Grid (G, P), one split of one problem per workgroup.
+//   WRITE: X = X_K, Y = V; mem_part gets the split's [Vt | Z] (the forward's memory, Eq. 5-6).
+//   QUERY: X = X_Q, Y = dO, mem = [Vt | Z]; writes dX_Q, mem_part gets the split's [dVt | dZ].
+//   KEY:   X = X_K, Y = V, mem = [dVt | dZ]; writes dX_K and dY = dV.
+// QUERY and KEY write the split's moment record to param_part.
+template <int MODE>
 __global__ void __launch_bounds__(kThreads)
-    f32_bwd_param_reduce_kernel(const float* __restrict__ param_part, int B, int H, int G, int K, int dr,
+    f32_bwd_tiled_kernel(const float* __restrict__ X, const float* __restrict__ Y, int64_t N, int H, int dr, int dv,
+                         int K, int64_t seg, int G, const double* __restrict__ c, const double* __restrict__ inv,
+                         const float* __restrict__ mu, const float* __restrict__ mem, float eps,
+                         float* __restrict__ dX, float* __restrict__ dY, float* __restrict__ mem_part,
+                         float* __restrict__ param_part) {
+    constexpr bool QK = MODE != BWD_WRITE;
+    extern __shared__ float lds[];
+    const int64_t p = blockIdx.y;
+    const int gi = blockIdx.x, h = int(p % H);
+    const int tid = threadIdx.x, tr = tid >> 4, mc = tid & 15, r0 = tr * 4, m0 = mc * 4;
+    const int LDK = K + 4;
+    float* muT = lds;                              // [dr][LDK]
+    float* ivT = muT + dr * LDK;                   // [dr][LDK]
+    float* cK = ivT + dr * LDK;                    // [K]
+    float* M = cK + K;                             // [K][dv]   Vt (query) or dVt (key)
+    float* MT = M + (QK ? K * dv : 0);             // [dv][K]
+    float* Zm = MT + (QK ? dv * K : 0);            // [K]       Z or dZ
+    float* xT = Zm + (QK ? K : 0);                 // [dr][kLDT]
+    float* gT = xT + dr * kLDT;                    // [K][kLDT] gamma^T, then ds^T
+    float* g = QK ? gT + K * kLDT : xT;            // [kBT][K]  gamma, then ds (write: in the space of X^T)
+    float* Yr = QK ? g + kBT * K : xT + max(dr * kLDT, kBT * K);  // [kBT][dv] V (write) or dO / D (query)
+    float* YT = Yr + (MODE != BWD_KEY ? kBT * dv : 0);  // [dv][kLDT]
+    float* Dv = YT + (QK ? dv * kLDT : 0);         // [kBT]
+    float* Av = Dv + kBT;                          // [kBT]
+
+    {   // per-head tables and (query, key) the problem's memory
+        const double *ch = c + size_t(h) * K, *ih = inv + size_t(h) * K * dr;
+        const float* mh = mu + size_t(h) * K * dr;
+        for (int i = tid; i < K * dr; i += kThreads) {
+            const int k = i / dr, d = i - k * dr;
+            muT[d * LDK + k] = mh[i];
+            ivT[d * LDK + k] = float(ih[i]);
+        }
+        for (int k = tid; k < K; k += kThreads) cK[k] = float(ch[k]);
+        if (QK) {
+            const float* src = mem + size_t(p) * K * (dv + 1);
+            for (int i = tid; i < K * dv; i += kThreads) {
+                const int k = i / dv, cc = i - k * dv;
+                const float v = src[i];
+                M[i] = v;
+                MT[cc * K + k] = v;
+            }
+            for (int k = tid; k < K; k += kThreads) Zm[k] = src[K * dv + k];
+        }
+    }
+    __syncthreads();
+    // moment accumulators (rows d = r0 + i, columns k = m0 + j) and their mu
+    float mreg[4][4], s1[4][4] = {}, s2[4][4] = {}, s0[4] = {};
+    // memory-like accumulators (rows k = r0 + i, columns c = m0 + j): Vt, Z (write) or dVt, dZ (query)
+    float mv[4][4] = {}, mz[4] = {};
+    const bool mom = QK && r0 < dr && m0 < K;
+    if (mom)
+        for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j) mreg[i][j] = muT[(r0 + i) * LDK + m0 + j];
+
+    const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
+    const float* Xp = X + size_t(p) * N * dr;
+    const float* Yp = Y + size_t(p) * N * dv;
+    for (int64_t n0 = lo; n0 < hi; n0 += kBT) {
+        const int rows = int(min<int64_t>(kBT, hi - n0));
+        __syncthreads();  // the previous tile's reads are done
+        for (int i = tid; i < kBT * (dr / 4); i += kThreads) {
+            const int t = i / (dr / 4), d = (i - t * (dr / 4)) * 4;
+            const float4 v = t < rows ? *reinterpret_cast<const float4*>(Xp + (n0 + t) * dr + d) : make_float4(0, 0, 0, 0);
+            xT[(d + 0) * kLDT + t] = v.x;
+            xT[(d + 1) * kLDT + t] = v.y;
+            xT[(d + 2) * kLDT + t] = v.z;
+            xT[(d + 3) * kLDT + t] = v.w;
+        }
+        for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
+            const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
+            const float4 v = t < rows ? *reinterpret_cast<const float4*>(Yp + (n0 + t) * dv + cc) : make_float4(0, 0, 0, 0);
+            if (MODE == BWD_KEY) {
+                YT[(cc + 0) * kLDT + t] = v.x;
+                YT[(cc + 1) * kLDT + t] = v.y;
+                YT[(cc + 2) * kLDT + t] = v.z;
+                YT[(cc + 3) * kLDT + t] = v.w;
+            } else {
+                *reinterpret_cast<float4*>(Yr + t * dv + cc) = v;
+            }
+        }
+        __syncthreads();
+
+        // responsibilities (rows t, columns k): direct-form score of Eq. 16, softmax of Eq. 3b
+        float gam[4][4];
+        {
+            float q[4][4] = {};
+            if (m0 < K) {
+#pragma unroll 4
+                for (int d = 0; d < dr; ++d) {
+                    float xa[4], ma[4], ia[4];
+                    unpack(lds4(xT + d * kLDT + r0), xa);
+                    unpack(lds4(muT + d * LDK + m0), ma);
+                    unpack(lds4(ivT + d * LDK + m0), ia);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const float df = xa[i] - ma[j];
+                            q[i][j] = fmaf(df * df, ia[j], q[i][j]);
+                        }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float sc[4], m = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    sc[j] = m0 < K ? cK[m0 + j] - 0.5f * q[i][j] : -INFINITY;
+                    m = fmaxf(m, sc[j]);
+                }
+                m = max16(m);
+                float e[4], sum = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    e[j] = m0 < K ? expf(sc[j] - m) : 0.0f;
+                    sum += e[j];
+                }
+                sum = sum16(sum);
+                const float r = r0 + i < rows ? 1.0f / sum : 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) gam[i][j] = e[j] * r;
+            }
+        }
+        if (MODE == BWD_WRITE) __syncthreads();  // gamma overwrites X^T
+        if (m0 < K) {
+            if (MODE != BWD_KEY)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) put4(g + (r0 + i) * K + m0, gam[i][0], gam[i][1], gam[i][2], gam[i][3]);
+            if (QK)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) put4(gT + (m0 + j) * kLDT + r0, gam[0][j], gam[1][j], gam[2][j], gam[3][j]);
+        }
+        __syncthreads();
+
+        if (MODE == BWD_WRITE) {  // Vt += gamma^T V, Z += gamma^T 1 (rows k, columns c)
+            if (r0 < K && m0 < dv)
+#pragma unroll 4
+                for (int t = 0; t < rows; ++t) {
+                    float ga[4], ya[4];
+                    unpack(lds4(g + t * K + r0), ga);
+                    unpack(lds4(Yr + t * dv + m0), ya);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        mz[i] += ga[i];
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) mv[i][j] = fmaf(ga[i], ya[j], mv[i][j]);
+                    }
+                }
+            continue;
+        }
+
+        float gg[4][4] = {};  // upstream gradient at the responsibilities (rows t, columns k)
+        if (MODE == BWD_QUERY) {
+            // N = gamma Vt (rows t, columns c); D = gamma Z + eps; dO . N
+            float nv[4][4] = {};
+            if (m0 < dv)
+#pragma unroll 4
+                for (int k = 0; k < K; ++k) {
+                    float ga[4], va[4];
+                    unpack(lds4(gT + k * kLDT + r0), ga);
+                    unpack(lds4(M + k * dv + m0), va);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ga[i], va[j], nv[i][j]);
+                }
+            float Dt[4], An[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float dp = 0.0f, ap = 0.0f;
+                if (m0 < K)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) dp = fmaf(gam[i][j], Zm[m0 + j], dp);
+                if (m0 < dv) {
+                    float ya[4];
+                    unpack(lds4(Yr + (r0 + i) * dv + m0), ya);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ap = fmaf(ya[j], nv[i][j], ap);
+                }
+                Dt[i] = sum16(dp) + eps;
+                An[i] = sum16(ap);
+            }
+            // dO' = dO / D in both layouts (each thread rescales its own entries), D and a' = dO . N / D^2
+            float sy[4][4];
+            if (m0 < dv) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float ya[4];
+                    unpack(lds4(Yr + (r0 + i) * dv + m0), ya);
+                    const float rD = 1.0f / Dt[i];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sy[i][j] = ya[j] * rD;
+                    put4(Yr + (r0 + i) * dv + m0, sy[i][0], sy[i][1], sy[i][2], sy[i][3]);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) put4(YT + (m0 + j) * kLDT + r0, sy[0][j], sy[1][j], sy[2][j], sy[3][j]);
+            }
+            if (mc == 0)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    Dv[r0 + i] = Dt[i];
+                    Av[r0 + i] = An[i] / (Dt[i] * Dt[i]);
+                }
+            __syncthreads();
+            // dVt += gamma^T dO', dZ -= gamma^T a' (rows k, columns c)
+            if (r0 < K && m0 < dv)
+#pragma unroll 4
+                for (int t = 0; t < rows; ++t) {
+                    float ga[4], ya[4];
+                    unpack(lds4(g + t * K + r0), ga);
+                    unpack(lds4(Yr + t * dv + m0), ya);
+                    const float at = Av[t];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        mz[i] = fmaf(-ga[i], at, mz[i]);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) mv[i][j] = fmaf(ga[i], ya[j], mv[i][j]);
+                    }
+                }
+            // g = dO' Vt^T - a' Z
+            if (m0 < K) {
+#pragma unroll 4
+                for (int cc = 0; cc < dv; ++cc) {
+                    float ya[4], va[4];
+                    unpack(lds4(YT + cc * kLDT + r0), ya);
+                    unpack(lds4(MT + cc * K + m0), va);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(ya[i], va[j], gg[i][j]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(-Av[r0 + i], Zm[m0 + j], gg[i][j]);
+            }
+        } else {
+            // dV = gamma dVt (rows t, columns c)
+            if (m0 < dv) {
+                float nv[4][4] = {};
+#pragma unroll 4
+                for (int k = 0; k < K; ++k) {
+                    float ga[4], va[4];
+                    unpack(lds4(gT + k * kLDT + r0), ga);
+                    unpack(lds4(M + k * dv + m0), va);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ga[i], va[j], nv[i][j]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (r0 + i < rows)
+                        *reinterpret_cast<float4*>(dY + (size_t(p) * N + n0 + r0 + i) * dv + m0) =
+                            make_float4(nv[i][0], nv[i][1], nv[i][2], nv[i][3]);
+            }
+            // g = V dVt^T + dZ
+            if (m0 < K) {
+#pragma unroll 4
+                for (int cc = 0; cc < dv; ++cc) {
+                    float ya[4], va[4];
+                    unpack(lds4(YT + cc * kLDT + r0), ya);
+                    unpack(lds4(MT + cc * K + m0), va);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(ya[i], va[j], gg[i][j]);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) gg[i][j] += Zm[m0 + j];
+            }
+        }
+        // Eq. 18: ds = gamma (g - gamma . g)
+        float ds[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float w = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w = fmaf(gam[i][j], gg[i][j], w);
+            w = sum16(w);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ds[i][j] = gam[i][j] * (gg[i][j] - w);
+        }
+        __syncthreads();  // every read of gamma is done
+        if (m0 < K) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) put4(g + (r0 + i) * K + m0, ds[i][0], ds[i][1], ds[i][2], ds[i][3]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) put4(gT + (m0 + j) * kLDT + r0, ds[0][j], ds[1][j], ds[2][j], ds[3][j]);
+        }
+        __syncthreads();
+        // dX (rows d, columns t): dx_td = -sum_k ds_tk (x_td - mu_kd) / sigma2_kd
+        if (r0 < dr) {
+            float xa[4][4], acc[4][4] = {};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) unpack(lds4(xT + (r0 + i) * kLDT + m0), xa[i]);
+#pragma unroll 4
+            for (int k = 0; k < K; ++k) {
+                float da[4], ma[4], ia[4];
+                unpack(lds4(gT + k * kLDT + m0), da);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ma[i] = muT[(r0 + i) * LDK + k];
+                    ia[i] = ivT[(r0 + i) * LDK + k];
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(da[j] * ia[i], xa[i][j] - ma[i], acc[i][j]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (m0 + j < rows)
+                    *reinterpret_cast<float4*>(dX + (size_t(p) * N + n0 + m0 + j) * dr + r0) =
+                        make_float4(-acc[0][j], -acc[1][j], -acc[2][j], -acc[3][j]);
+        }
+        // moments (rows d, columns k)
+        if (mom)
+#pragma unroll 4
+            for (int t = 0; t < rows; ++t) {
+                float da[4], xa[4];
+                unpack(lds4(g + t * K + m0), da);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xa[i] = xT[(r0 + i) * kLDT + t];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s0[j] += da[j];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float df = xa[i] - mreg[i][j], w = da[j] * df;
+                        s1[i][j] += w;
+                        s2[i][j] = fmaf(w, df, s2[i][j]);
+                    }
+            }
+    }
+    // the split's records (zeros for a split without rows)
+    if (MODE != BWD_KEY && r0 < K && m0 < dv) {
+        float* mp = mem_part + (size_t(p) * G + gi) * size_t(K) * (dv + 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<float4*>(mp + (r0 + i) * dv + m0) = make_float4(mv[i][0], mv[i][1], mv[i][2], mv[i][3]);
+        if (mc == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mp[K * dv + r0 + i] = mz[i];
+    }
+    if (mom) {
+        float* pp = param_part + (size_t(p) * G + gi) * size_t(2 * K * dr + K);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                pp[(m0 + j) * dr + r0 + i] = s1[i][j];
+                pp[K * dr + (m0 + j) * dr + r0 + i] = s2[i][j];
+            }
+        if (tr == 0)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pp[2 * K * dr + m0 + j] = s0[j];
+    }
+}
+
+// Grid (ceil((K d_r + K) / kThreads), H): the parameter gradients of head h from the moments,
+// summed in fp64 over the query and key sides, the batch and the splits in that fixed order.
+// With B == 0 it writes zeros (no rows, no gradient) and reads neither moments nor tables.
+__global__ void __launch_bounds__(kThreads)
+    f32_bwd_param_reduce_kernel(const float* __restrict__ part, int B, int H, int G, int K, int dr,
+                                const double* __restrict__ inv, const float* __restrict__ pi,
                                 float* __restrict__ dmu, float* __restrict__ ds2, float* __restrict__ dpi) {
     const int h = blockIdx.y, PE = 2 * K * dr + K;
     const int e = blockIdx.x * kThreads + threadIdx.x;
-    if (e >= PE) return;
+    if (e >= K * dr + K) return;
     const size_t P = size_t(B) * H;
-    float acc = 0.0f;
-    for (int side = 0; side < 2; ++side)
-        for (int b = 0; b < B; ++b)
-            for (int g = 0; g < G; ++g) acc += param_part[((side * P + size_t(b) * H + h) * G + g) * PE + e];
-    if (e < K * dr) dmu[size_t(h) * K * dr + e] = acc;
-    else if (e < 2 * K * dr) ds2[size_t(h) * K * dr + e - K * dr] = acc;
-    else dpi[size_t(h) * K + e - 2 * K * dr] = acc;
+    const int k = e < K * dr ? e / dr : e - K * dr;
+    const int i1 = e < K * dr ? e : 2 * K * dr + k;  // S1 (or S0 for dpi)
+    // records in (side, b, g) order, loads issued eight records at a time, sums in that order
+    double s1 = 0.0, s2 = 0.0, s0 = 0.0;
+    const int R = 2 * B * G;
+    for (int r = 0; r < R; r += 8) {
+        float v1[8], v2[8], v0[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            v1[u] = v2[u] = v0[u] = 0.0f;
+            const int q = r + u;
+            if (q < R) {
+                const int side = q / (B * G), b = (q / G) % B, g = q % G;
+                const float* rec = part + ((side * P + size_t(b) * H + h) * G + g) * PE;
+                v1[u] = rec[i1];
+                if (e < K * dr) {
+                    v2[u] = rec[K * dr + e];
+                    v0[u] = rec[2 * K * dr + k];
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            s1 += double(v1[u]);
+            s2 += double(v2[u]);
+            s0 += double(v0[u]);
+        }
+    }
+    if (e < K * dr) {
+        const double iv = B > 0 ? inv[size_t(h) * K * dr + e] : 0.0;
+        dmu[size_t(h) * K * dr + e] = float(iv * s1);
+        ds2[size_t(h) * K * dr + e] = float(0.5 * (iv * iv * s2 - iv * s0));
+    } else {
+        dpi[size_t(h) * K + k] = B > 0 ? float(s1 / double(pi[size_t(h) * K + k])) : 0.0f;
+    }
+}
+
+hipError_t reduce_params(const Plan& p, const float* part, int B, const double* inv, const float* pi, float* dmu,
+                         float* ds2, float* dpi, hipStream_t st) {
+    const int n = int(p.K * p.dr + p.K);
+    GMA_LAUNCH("f32_bwd_params", f32_bwd_param_reduce_kernel, dim3(unsigned((n + kThreads - 1) / kThreads), unsigned(p.H)),
+               dim3(kThreads), 0, st, part, B, int(p.H), int(p.G), int(p.K), int(p.dr), inv, pi, dmu, ds2, dpi);
+    return hipGetLastError();
+}
+
+hipError_t bwd_allow_lds() {
+    static const hipError_t e = [] {
+        const void* fns[] = {(const void*)f32_bwd_side_kernel<true>, (const void*)f32_bwd_side_kernel<false>,
+                             (const void*)f32_bwd_tiled_kernel<BWD_WRITE>, (const void*)f32_bwd_tiled_kernel<BWD_QUERY>,
+                             (const void*)f32_bwd_tiled_kernel<BWD_KEY>};
+        for (const void* f : fns) {
+            hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
+            if (r != hipSuccess) return r;
+        }
+        return hipSuccess;
+    }();
+    return e;
 }
 
 }  // namespace
@@ -617,31 +1084,14 @@ size_t f32_backward_extra_bytes(const Plan& p) {
            round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256);
 }
 
-namespace {
-hipError_t reduce_params(const Plan& p, const float* ppart, int B, float* dmu, float* ds2, float* dpi, hipStream_t st) {
-    const int PE = int(2 * p.K * p.dr + p.K);
-    GMA_LAUNCH("f32_bwd_params", f32_bwd_param_reduce_kernel, dim3(unsigned((PE + kThreads - 1) / kThreads), unsigned(p.H)),
-               dim3(kThreads), 0, st, ppart, B, int(p.H), int(p.G), int(p.K), int(p.dr), dmu, ds2, dpi);
-    return hipGetLastError();
-}
-}  // namespace
-
 hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
                               const float* s2, const float* pi, float eps, const float* dO, float* dXQ, float* dXK,
                               float* dV, float* dmu, float* ds2, float* dpi, char* ws, hipStream_t st) {
     if (p.H == 0) return hipSuccess;
-    if (p.P == 0 || p.N == 0) return reduce_params(p, nullptr, 0, dmu, ds2, dpi, st);  // zero gradients
-    static const hipError_t attr = [] {
-        const void* fns[] = {(const void*)f32_bwd_side_kernel<true>, (const void*)f32_bwd_side_kernel<false>};
-        for (const void* f : fns) {
-            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
-            if (e != hipSuccess) return e;
-        }
-        return hipSuccess;
-    }();
-    if (attr != hipSuccess) return attr;
-    hipError_t e = launch_params(p, s2, pi, ws, st);
+    if (p.P == 0 || p.N == 0) return reduce_params(p, nullptr, 0, nullptr, pi, dmu, ds2, dpi, st);  // zero gradients
+    hipError_t e = bwd_allow_lds();
     if (e != hipSuccess) return e;
+    if ((e = launch_params(p, s2, pi, ws, st)) != hipSuccess) return e;
     F32Params v = f32_params_view(p, ws);
     float* partials = reinterpret_cast<float*>(ws + p.off_partials);
     float* memory = reinterpret_cast<float*>(ws + p.off_memory);
@@ -650,30 +1100,51 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     float* dpart = reinterpret_cast<float*>(extra);
     float* dmem = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256));
     float* ppart = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256) + round_up(size_t(p.P) * E * 4, 256));
-    // the forward's memory
-    size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
-    GMA_LAUNCH("f32_bwd_write", f32_write_kernel, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads), lds_w, st, XK, V,
-               p.N, int(p.H), int(p.dr), int(p.dv), int(p.K), p.seg, int(p.G), v.c, v.inv, mu, partials);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    float* ppart_key = ppart + size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K);
+    const dim3 grid(unsigned(p.G), unsigned(p.P));
     const int Ei = int(E);
-    GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, dim3(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P)),
-               dim3(kThreads), 0, st, partials, int(p.G), Ei, memory);
+    const dim3 cgrid(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P));
+    const int H = int(p.H), dr = int(p.dr), dv = int(p.dv), K = int(p.K), G = int(p.G);
+    if (bwd_tiled_applies(p)) {
+        GMA_LAUNCH("f32_bwd_write", f32_bwd_tiled_kernel<BWD_WRITE>, grid, dim3(kThreads),
+                   bwd_tiled_lds_bytes(BWD_WRITE, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
+                   static_cast<const float*>(nullptr), eps, static_cast<float*>(nullptr),
+                   static_cast<float*>(nullptr), partials, static_cast<float*>(nullptr));
+    } else {
+        const size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
+        GMA_LAUNCH("f32_bwd_write", f32_write_kernel, grid, dim3(kThreads), lds_w, st, XK, V, p.N, H, dr, dv, K,
+                   p.seg, G, v.c, v.inv, mu, partials);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    int T = kTile;
-    while (T > 8 && bwd_lds_bytes(T, int(p.dr), int(p.dv), int(p.K)) > kMaxLds) T /= 2;
-    const size_t lds = bwd_lds_bytes(T, int(p.dr), int(p.dv), int(p.K));
-    GMA_LAUNCH("f32_bwd_query", f32_bwd_side_kernel<true>, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads), lds, st,
-               XQ, dO, p.N, int(p.H), int(p.dr), int(p.dv), int(p.K), p.seg, int(p.G), T, v.c, v.inv, mu, pi, memory,
-               eps, dXQ, static_cast<float*>(nullptr), dpart, ppart);
+    GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, partials, G, Ei, memory);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, dim3(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P)),
-               dim3(kThreads), 0, st, dpart, int(p.G), Ei, dmem);
+    if (bwd_tiled_applies(p)) {
+        GMA_LAUNCH("f32_bwd_query", f32_bwd_tiled_kernel<BWD_QUERY>, grid, dim3(kThreads),
+                   bwd_tiled_lds_bytes(BWD_QUERY, K, dr, dv), st, XQ, dO, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
+                   static_cast<const float*>(memory), eps, dXQ, static_cast<float*>(nullptr), dpart, ppart);
+    } else {
+        int T = kTile;
+        while (T > 8 && bwd_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
+        GMA_LAUNCH("f32_bwd_query", f32_bwd_side_kernel<true>, grid, dim3(kThreads), bwd_lds_bytes(T, dr, dv, K), st,
+                   XQ, dO, p.N, H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, static_cast<const float*>(memory), eps, dXQ,
+                   static_cast<float*>(nullptr), dpart, ppart);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    GMA_LAUNCH("f32_bwd_key", f32_bwd_side_kernel<false>, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads), lds, st,
-               XK, V, p.N, int(p.H), int(p.dr), int(p.dv), int(p.K), p.seg, int(p.G), T, v.c, v.inv, mu, pi, dmem,
-               eps, dXK, dV, static_cast<float*>(nullptr), ppart + size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K));
+    GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, dpart, G, Ei, dmem);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    return reduce_params(p, ppart, int(p.B), dmu, ds2, dpi, st);
+    if (bwd_tiled_applies(p)) {
+        GMA_LAUNCH("f32_bwd_key", f32_bwd_tiled_kernel<BWD_KEY>, grid, dim3(kThreads),
+                   bwd_tiled_lds_bytes(BWD_KEY, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
+                   static_cast<const float*>(dmem), eps, dXK, dV, static_cast<float*>(nullptr), ppart_key);
+    } else {
+        int T = kTile;
+        while (T > 8 && bwd_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
+        GMA_LAUNCH("f32_bwd_key", f32_bwd_side_kernel<false>, grid, dim3(kThreads), bwd_lds_bytes(T, dr, dv, K), st,
+                   XK, V, p.N, H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, static_cast<const float*>(dmem), eps, dXK, dV,
+                   static_cast<float*>(nullptr), ppart_key);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
 }
 
 }  // namespace gma

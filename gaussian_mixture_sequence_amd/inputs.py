@@ -43,6 +43,7 @@ class Workload:
     n_ctx: int = -1     # cross-attention: context length N_k of XK and V (N is then N_q); -1: self
     decode: bool = False  # causal decoding: one position per call, carrying the memory between calls
     diagnostics: bool = False  # responsibility diagnostics of X_Q (Sec. 5.4); V and X_K unused
+    backward: bool = False  # backward pass of the bidirectional forward for a seeded upstream gradient dO
 
     @property
     def tokens(self) -> int:
@@ -83,6 +84,9 @@ WORKLOADS: Dict[str, Workload] = {
     # K = 128, routing dim d_model / H = 64 (d_v unused)
     "diag_s64_h8_l1024_k128": Workload("diag_s64_h8_l1024_k128", False, 64, 8, 1024, 64, 32, 128, "bf16", seed=7,
                                        diagnostics=True),
+    # backward of the bidirectional forward (Sec. 4.1), fp32: the B=8, H=8, N=4096 bidirectional dims
+    "bwd_b8h8_n4096_f32": Workload("bwd_b8h8_n4096_f32", False, 8, 8, 4096, 64, 64, 64, "f32", seed=8,
+                                   backward=True),
     "cross_b8h8_q4096_k16384": Workload("cross_b8h8_q4096_k16384", False, 8, 8, 4096, 64, 64, 64, "bf16",
                                         seed=5, n_ctx=16384),
 }
@@ -113,8 +117,10 @@ def make_inputs(w: Workload, seed: int | None = None) -> Dict[str, torch.Tensor]
     nk = w.n_keys  # the context length for cross-attention
     xk = torch.randn(w.B, w.H, nk, w.d_r, generator=gen, dtype=torch.float32).to(dt)
     v = torch.randn(w.B, w.H, nk, w.d_v, generator=gen, dtype=torch.float32).to(dt)
-    return {"xq": xq.contiguous(), "xk": xk.contiguous(), "v": v.contiguous(),
-            "mu": mu, "sigma2": sigma2, "pi": pi}
+    out = {"xq": xq.contiguous(), "xk": xk.contiguous(), "v": v.contiguous(), "mu": mu, "sigma2": sigma2, "pi": pi}
+    if w.backward:  # the loss gradient at O, drawn last so the forward inputs match the forward's
+        out["d_o"] = torch.randn(w.B, w.H, w.N, w.d_v, generator=gen, dtype=torch.float32).to(dt).contiguous()
+    return out
 
 
 def head_slice(inp: Dict[str, torch.Tensor], b: int, h: int) -> Dict[str, torch.Tensor]:
