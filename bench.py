@@ -278,11 +278,31 @@ def alg_bytes_per_token_head(w, kernel: str) -> float:
     return 0.0
 
 
+# fp32 vector peak without packed-fp32 instructions (the library is built with them disabled):
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flops per FMA x 2.4 GHz
+F32_VALU_PEAK_TFLOPS = 78.6
+
+
+def alg_flops_per_token_head(w, kernel: str) -> float:
+    """Algorithmic fp32 flops per (row, head) of the backward passes (an FMA counts 2): per (k, d)
+    the direct-form score 3 (difference, then a fused square-scale-add), dX 4 and the three moments
+    5; per (k, c) each product with the memory 2; per k the softmax 3, Eq. 18 4, D / Z terms 2 each."""
+    if not w.backward:
+        return 0.0
+    K, dr, dv = w.K, w.d_r, w.d_v
+    if kernel.endswith("_bwd_write"):
+        return 3 * K * dr + 2 * K * dv + 4 * K
+    if kernel.endswith("_bwd_query"):
+        return 12 * K * dr + 6 * K * dv + 12 * K + 2 * dv
+    if kernel.endswith("_bwd_key"):
+        return 12 * K * dr + 4 * K * dv + 8 * K
+    return 0.0
+
+
 KERNEL_SYMBOL = {"bf16_scan": "gma::bf::scan_kernel", "bf16_bidir": "gma::bf::bidir_kernel",
                  "bf16_cross": "gma::bf::bidir_kernel", "bf16_resp": "gma::bf::resp_kernel",
                  "bf16_decode": "gma::dec::decode_kernel", "bf16_diag": "gma::diag::diag_fused_kernel",
-                 "f32_bwd_query": "gma::f32_bwd_side_kernel<true>",
-                 "f32_bwd_key": "gma::f32_bwd_side_kernel<false>",
+                 "f32_bwd_query": "gma::f32_bwd_tiled_kernel<1>", "f32_bwd_key": "gma::f32_bwd_tiled_kernel<2>",
                  "bf16_causal": "gma::bf::causal_kernel", "bf16_causal_aggregate": "gma::bf::write_kernel<64, 1"}
 
 
@@ -461,10 +481,22 @@ def main(args=None, probe_only=False) -> int:
             if per_launch:
                 entry["alg_bytes_per_launch"] = int(per_launch)
                 entry["alg_GBps"] = round(per_launch / (avg_us * 1e-6) / 1e9, 1)
+            flops = alg_flops_per_token_head(w, name) * w.B * w.H * w.N
+            if flops:
+                entry["alg_flops_per_launch"] = int(flops)
+                entry["alg_TFLOPs"] = round(flops / (avg_us * 1e-6) / 1e12, 2)
         kernels[name] = entry
     dominant = max(kstats.items(), key=lambda kv: kv[1][1])[0] if kstats else None
     roofline = None
-    if dominant and "alg_GBps" in kernels[dominant]:
+    if dominant and "alg_TFLOPs" in kernels[dominant]:  # the fp32 backward: bound by vector ALU issue
+        ach = kernels[dominant]["alg_TFLOPs"]
+        traffic = measured_traffic(KERNEL_SYMBOL.get(dominant, "?"), args.workloads)
+        roofline = {"kernel": dominant, "bound": "alu", "achieved": ach, "peak": F32_VALU_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / F32_VALU_PEAK_TFLOPS, 4), "traffic": traffic,
+                    "avg_us": kernels[dominant]["avg_us"],
+                    "alg_flops_per_launch": kernels[dominant]["alg_flops_per_launch"],
+                    "alg_bytes_per_launch": kernels[dominant].get("alg_bytes_per_launch")}
+    elif dominant and "alg_GBps" in kernels[dominant]:
         ach = kernels[dominant]["alg_GBps"]
         traffic = measured_traffic(KERNEL_SYMBOL.get(dominant, "?"), args.workloads)
         roofline = {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
