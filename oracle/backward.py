@@ -63,3 +63,44 @@ def backward_bidir(XQ, XK, V, mu, sigma2, pi, eps, dO) -> dict:
                 out["dsigma2"][h] += ds2
                 out["dpi"][h] += dpi
     return out
+
+
+def backward_causal(XQ, XK, V, mu, sigma2, pi, eps, dO) -> dict:
+    """Gradients of <dO, O> for the causal forward O (Sec. 3.5, Eq. 6b and 8b): position i reads
+    the prefix memory Vt^(i) = sum_{j<=i} gamma^K_j V_j^T, Z^(i) = sum_{j<=i} gamma^K_j.  With
+    D_i = gamma^Q_i . Z^(i) + eps and a_i = dO_i . O_i,
+      g^Q_ik = (dO_i . Vt^(i)_k - a_i Z^(i)_k) / D_i;
+    the memory that position i reads receives gamma^Q_i dO_i^T / D_i and -gamma^Q_i a_i / D_i, and
+    key position j enters every memory Vt^(i) with i >= j, so its gradients are suffix sums:
+      dVt_j = sum_{i>=j} gamma^Q_i dO_i^T / D_i,  dZ_j = -sum_{i>=j} gamma^Q_i a_i / D_i,
+      dV_j = sum_k gamma^K_jk dVt_j[k],            g^K_jk = dVt_j[k] . V_j + dZ_j[k].
+    The rest (Eq. 18-20) is as for the bidirectional backward.  Shapes as backward_bidir."""
+    from . import _f64, responsibilities
+    XQ, XK, V, dO = (_f64(t) for t in (XQ, XK, V, dO))
+    mu, s2, pi = (_f64(t) for t in (mu, sigma2, pi))
+    GQ, GK = responsibilities(XQ, mu, s2, pi), responsibilities(XK, mu, s2, pi)
+    B, H, N, dr = XQ.shape
+    out = {"dXQ": np.zeros_like(XQ), "dXK": np.zeros_like(XK), "dV": np.zeros_like(V),
+           "dmu": np.zeros_like(mu), "dsigma2": np.zeros_like(s2), "dpi": np.zeros_like(pi)}
+    for b in range(B):
+        for h in range(H):
+            gq, gk, v, do = GQ[b, h], GK[b, h], V[b, h], dO[b, h]
+            vt = np.cumsum(gk[:, :, None] * v[:, None, :], axis=0)   # Vt^(i), [N,K,d_v] (Eq. 6b)
+            z = np.cumsum(gk, axis=0)                                  # Z^(i), [N,K]
+            n_ = np.einsum("ik,ikc->ic", gq, vt)                       # Eq. 8b numerator
+            d_ = np.einsum("ik,ik->i", gq, z) + eps
+            o = n_ / d_[:, None]
+            a = (do * o).sum(axis=1)
+            g_q = (np.einsum("ic,ikc->ik", do, vt) - a[:, None] * z) / d_[:, None]
+            dvt = np.cumsum((gq[:, :, None] * (do / d_[:, None])[:, None, :])[::-1], axis=0)[::-1]
+            dz = -np.cumsum((gq * (a / d_)[:, None])[::-1], axis=0)[::-1]
+            out["dV"][b, h] = np.einsum("jk,jkc->jc", gk, dvt)
+            g_k = np.einsum("jc,jkc->jk", v, dvt) + dz
+            for x, g, gam, key in ((XQ[b, h], g_q, gq, "dXQ"), (XK[b, h], g_k, gk, "dXK")):
+                ds = gam * (g - (gam * g).sum(axis=1, keepdims=True))   # Eq. 18
+                dx, dmu, ds2, dpi = _score_grads(x, ds, mu[h], s2[h], pi[h])
+                out[key][b, h] = dx
+                out["dmu"][h] += dmu
+                out["dsigma2"][h] += ds2
+                out["dpi"][h] += dpi
+    return out

@@ -628,3 +628,74 @@ def test_backward_values_gradient_closed_form():
     ref = do.sum(axis=2, keepdims=True) / (9 + 0.5)
     np.testing.assert_allclose(g["dV"], np.broadcast_to(ref, g["dV"].shape), rtol=1e-12)
     assert np.abs(g["dXQ"]).max() < 1e-12 and np.abs(g["dXK"]).max() < 1e-12
+
+
+def test_backward_causal_matches_finite_differences():
+    """<grad, u> equals the central difference of <dO, O> along a random direction u for every
+    input, with O from the causal forward oracle (Eq. 6b, 8b)."""
+    rng = np.random.default_rng(63)
+    xq, xk, v, mu, s2, pi, do = _backward_problem(rng)
+    eps = 1e-3
+    g = oracle.backward.backward_causal(xq, xk, v, mu, s2, pi, eps, do)
+    args = {"dXQ": xq, "dXK": xk, "dV": v, "dmu": mu, "dsigma2": s2, "dpi": pi}
+    order = ["dXQ", "dXK", "dV", "dmu", "dsigma2", "dpi"]
+    for key in order:
+        u = rng.standard_normal(args[key].shape)
+        h = 1e-6 * (np.abs(args[key]).max() + 1.0)
+        def loss(sign):
+            a = [args[k].copy() for k in order]
+            a[order.index(key)] = a[order.index(key)] + sign * h * u
+            return float((do * oracle.forward_causal(a[0], a[1], a[2], a[3], a[4], a[5], eps)).sum())
+        fd = (loss(1.0) - loss(-1.0)) / (2 * h)
+        np.testing.assert_allclose((g[key] * u).sum(), fd, rtol=2e-6, atol=1e-9, err_msg=key)
+
+
+def test_backward_causal_matches_torch_autograd():
+    """Every gradient equals torch.autograd in fp64 through a causal forward assembled from
+    torch.distributions.Normal log-densities (Eq. 2-3) and cumulative sums over positions."""
+    import torch
+    rng = np.random.default_rng(64)
+    xq, xk, v, mu, s2, pi, do = _backward_problem(rng, B=2, H=3, N=11, dr=4, dv=3, K=6)
+    eps = 0.05
+    T = {k: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+         for k, a in dict(xq=xq, xk=xk, v=v, mu=mu, s2=s2, pi=pi).items()}
+
+    def resp(x):
+        lp = torch.distributions.Normal(T["mu"][None, :, None], T["s2"].sqrt()[None, :, None]).log_prob(
+            x[:, :, :, None, :]).sum(-1) + torch.log(T["pi"])[None, :, None]
+        return torch.softmax(lp, dim=-1)
+
+    gq, gk = resp(T["xq"]), resp(T["xk"])
+    vt = torch.cumsum(gk[..., :, None] * T["v"][..., None, :], dim=2)   # [B,H,N,K,dv]
+    z = torch.cumsum(gk, dim=2)
+    o = (gq[..., None] * vt).sum(-2) / ((gq * z).sum(-1, keepdim=True) + eps)
+    (o * torch.tensor(do)).sum().backward()
+    g = oracle.backward.backward_causal(xq, xk, v, mu, s2, pi, eps, do)
+    for key, name in (("dXQ", "xq"), ("dXK", "xk"), ("dV", "v"), ("dmu", "mu"), ("dsigma2", "s2"), ("dpi", "pi")):
+        np.testing.assert_allclose(g[key], T[name].grad.numpy(), rtol=1e-9, atol=1e-12, err_msg=key)
+
+
+def test_backward_causal_prefix_mean_closed_form():
+    """K = 1: O_i = sum_{j<=i} V_j / (i + 1 + eps), so dV_j = sum_{i>=j} dO_i / (i + 1 + eps);
+    routing vectors get no gradient."""
+    rng = np.random.default_rng(65)
+    xq, xk, v, mu, s2, pi, do = _backward_problem(rng, K=1)
+    eps = 0.5
+    g = oracle.backward.backward_causal(xq, xk, v, mu, s2, pi, eps, do)
+    N = v.shape[2]
+    w = do / (np.arange(N)[None, None, :, None] + 1 + eps)
+    ref = np.cumsum(w[:, :, ::-1], axis=2)[:, :, ::-1]
+    np.testing.assert_allclose(g["dV"], ref, rtol=1e-12)
+    assert np.abs(g["dXQ"]).max() < 1e-12 and np.abs(g["dXK"]).max() < 1e-12
+
+
+def test_backward_causal_last_row_is_bidirectional():
+    """With a gradient on the last position only, the causal and bidirectional backwards agree:
+    the last causal output is the bidirectional one (Eq. 8b at i = N is Eq. 8)."""
+    rng = np.random.default_rng(66)
+    xq, xk, v, mu, s2, pi, do = _backward_problem(rng)
+    do[:, :, :-1] = 0.0
+    a = oracle.backward.backward_causal(xq, xk, v, mu, s2, pi, 1e-3, do)
+    b = oracle.backward.backward_bidir(xq, xk, v, mu, s2, pi, 1e-3, do)
+    for key in a:
+        np.testing.assert_allclose(a[key], b[key], rtol=1e-10, atol=1e-13, err_msg=key)
