@@ -22,10 +22,11 @@ STATUS_NAMES = ["GMA_OK", "GMA_ERR_NULL_POINTER", "GMA_ERR_BAD_SHAPE", "GMA_ERR_
                 "GMA_ERR_UNSUPPORTED", "GMA_ERR_MISALIGNED", "GMA_ERR_WORKSPACE_TOO_SMALL",
                 "GMA_ERR_HIP"]
 GMA_F32, GMA_BF16 = 0, 1
-GMA_OP_RESPONSIBILITIES, GMA_OP_BIDIR, GMA_OP_CAUSAL, GMA_OP_DIAGNOSTICS, GMA_OP_BACKWARD_BIDIR = 0, 1, 2, 3, 4
+GMA_OP_RESPONSIBILITIES, GMA_OP_BIDIR, GMA_OP_CAUSAL, GMA_OP_DIAGNOSTICS = 0, 1, 2, 3
+GMA_OP_BACKWARD_BIDIR, GMA_OP_BACKWARD_CAUSAL = 4, 5
 EXPORTED = ["gma_status_string", "gma_workspace_size", "gma_responsibilities", "gma_forward_bidir",
             "gma_forward_causal", "gma_forward_causal_state", "gma_cross_workspace_size", "gma_forward_cross", "gma_responsibility_diagnostics", "gma_backward_bidir",
-            "gma_profiling",
+            "gma_backward_causal", "gma_profiling",
             "gma_profiling_collect", "gma_set_wait_limit"]
 WAIT_LIMIT_DEFAULT = 1 << 18  # GMA_WAIT_LIMIT_DEFAULT
 
@@ -89,6 +90,8 @@ def load() -> ctypes.CDLL:
             lib.gma_backward_bidir.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, shp, vp,
                                                sz, vp]
             lib.gma_backward_bidir.restype = i32
+            lib.gma_backward_causal.argtypes = lib.gma_backward_bidir.argtypes
+            lib.gma_backward_causal.restype = i32
             lib.gma_profiling.argtypes = [ctypes.c_int]
             lib.gma_profiling.restype = i32
             lib.gma_profiling_collect.argtypes = [ctypes.POINTER(KernelStat), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
@@ -253,20 +256,33 @@ def gma_backward_bidir(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, mu: 
     """Gradients of <d_o, O> for the bidirectional forward O (Sec. 4.1, Eq. 17-20), fp32:
     dXQ, dXK [B,H,N,d_r], dV [B,H,N,d_v], dmu, dsigma2 [H,K,d_r], dpi [H,K] (into `out` when given,
     a dict with those keys)."""
+    return _backward(GMA_OP_BACKWARD_BIDIR, "gma_backward_bidir", xq, xk, v, mu, sigma2, pi, d_o, eps, out,
+                     workspace, stream)
+
+
+def gma_backward_causal(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, mu: torch.Tensor,
+                        sigma2: torch.Tensor, pi: torch.Tensor, d_o: torch.Tensor, eps: float = 1e-6,
+                        out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradients of <d_o, O> for the causal forward O (Sec. 3.5 Eq. 6b, 8b; Sec. 4.1), fp32; outputs
+    as gma_backward_bidir."""
+    return _backward(GMA_OP_BACKWARD_CAUSAL, "gma_backward_causal", xq, xk, v, mu, sigma2, pi, d_o, eps, out,
+                     workspace, stream)
+
+
+def _backward(op, name, xq, xk, v, mu, sigma2, pi, d_o, eps, out, workspace, stream) -> dict:
     B, H, N, dr = xq.shape
     dv = v.shape[-1]
     K = mu.shape[1]
     io = _dtype_code(xq.dtype)
-    dev = xq.device
     if out is None:
         out = {"dXQ": torch.empty_like(xq), "dXK": torch.empty_like(xk), "dV": torch.empty_like(v),
                "dmu": torch.empty_like(mu), "dsigma2": torch.empty_like(sigma2), "dpi": torch.empty_like(pi)}
-    ws = _workspace(gma_workspace_size(GMA_OP_BACKWARD_BIDIR, B, H, N, dr, dv, K, io), dev, workspace)
-    _check(load().gma_backward_bidir(_ptr(xq), _ptr(xk), _ptr(v), io, _ptr(mu), _ptr(sigma2), _ptr(pi),
-                                     float(eps), _ptr(d_o), _ptr(out["dXQ"]), _ptr(out["dXK"]), _ptr(out["dV"]),
-                                     _ptr(out["dmu"]), _ptr(out["dsigma2"]), _ptr(out["dpi"]),
-                                     ctypes.byref(Shape(B, H, N, dr, dv, K)), _ptr(ws), ws.numel(),
-                                     _stream(stream)), "gma_backward_bidir")
+    ws = _workspace(gma_workspace_size(op, B, H, N, dr, dv, K, io), xq.device, workspace)
+    _check(getattr(load(), name)(_ptr(xq), _ptr(xk), _ptr(v), io, _ptr(mu), _ptr(sigma2), _ptr(pi),
+                                 float(eps), _ptr(d_o), _ptr(out["dXQ"]), _ptr(out["dXK"]), _ptr(out["dV"]),
+                                 _ptr(out["dmu"]), _ptr(out["dsigma2"]), _ptr(out["dpi"]),
+                                 ctypes.byref(Shape(B, H, N, dr, dv, K)), _ptr(ws), ws.numel(), _stream(stream)),
+           name)
     return out
 
 

@@ -30,7 +30,8 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 gma_status_t check_dims(gma_op_t op, const gma_shape_t& s, gma_dtype_t io) {
     if (s.B < 0 || s.H < 0 || s.N < 0) return GMA_ERR_BAD_SHAPE;
     if (s.d_r < 1 || s.K < 1) return GMA_ERR_UNSUPPORTED;
-    const bool has_values = op == GMA_OP_BIDIR || op == GMA_OP_CAUSAL || op == GMA_OP_BACKWARD_BIDIR;
+    const bool has_values = op == GMA_OP_BIDIR || op == GMA_OP_CAUSAL || op == GMA_OP_BACKWARD_BIDIR ||
+                            op == GMA_OP_BACKWARD_CAUSAL;
     if (has_values && s.d_v < 1) return GMA_ERR_UNSUPPORTED;
     if (s.K > 256) return GMA_ERR_UNSUPPORTED;
     if (io == GMA_F32) {
@@ -54,16 +55,18 @@ void layout(Plan* pl);
 
 gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_t chunk, Plan* pl) {
     if (op != GMA_OP_RESPONSIBILITIES && op != GMA_OP_BIDIR && op != GMA_OP_CAUSAL && op != GMA_OP_DIAGNOSTICS &&
-        op != GMA_OP_BACKWARD_BIDIR)
+        op != GMA_OP_BACKWARD_BIDIR && op != GMA_OP_BACKWARD_CAUSAL)
         return GMA_ERR_BAD_VALUE;
     if (io != GMA_F32 && io != GMA_BF16) return GMA_ERR_BAD_VALUE;
     gma_status_t st = check_dims(op, s, io);
     if (st != GMA_OK) return st;
-    if (op == GMA_OP_BACKWARD_BIDIR) {  // the forward's plan (fp32 only), then the gradient scratch
+    if (op == GMA_OP_BACKWARD_BIDIR || op == GMA_OP_BACKWARD_CAUSAL) {  // the forward's plan (fp32 only), then the gradient scratch
         if (io != GMA_F32) return GMA_ERR_UNSUPPORTED;
-        if ((st = make_plan(GMA_OP_BIDIR, s, io, 0, pl)) != GMA_OK) return st;
+        const bool causal = op == GMA_OP_BACKWARD_CAUSAL;
+        if ((st = make_plan(causal ? GMA_OP_CAUSAL : GMA_OP_BIDIR, s, io, causal ? 64 : 0, pl)) != GMA_OK) return st;
         pl->op = op;
-        pl->total += f32_backward_extra_bytes(*pl);
+        pl->chunk = 0;
+        pl->total += causal ? f32_backward_causal_extra_bytes(*pl) : f32_backward_extra_bytes(*pl);
         return GMA_OK;
     }
     if (op == GMA_OP_CAUSAL && chunk != 16 && chunk != 32 && chunk != 64) return GMA_ERR_UNSUPPORTED;
@@ -372,13 +375,14 @@ gma_status_t gma_responsibility_diagnostics(const void* X, gma_dtype_t x_dtype, 
                                           static_cast<char*>(workspace), stream));
 }
 
-gma_status_t gma_backward_bidir(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
-                                const float* mu, const float* sigma2, const float* pi, float eps, const void* dO,
-                                void* dXQ, void* dXK, void* dV, float* dmu, float* dsigma2, float* dpi,
-                                const gma_shape_t* shape, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+static gma_status_t backward_common(gma_op_t op, const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                                    const float* mu, const float* sigma2, const float* pi, float eps, const void* dO,
+                                    void* dXQ, void* dXK, void* dV, float* dmu, float* dsigma2, float* dpi,
+                                    const gma_shape_t* shape, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
     if (!mu || !sigma2 || !pi || !shape) return GMA_ERR_NULL_POINTER;
     Plan p;
-    gma_status_t st = gma::make_plan(GMA_OP_BACKWARD_BIDIR, *shape, io_dtype, 0, &p);
+    gma_status_t st = gma::make_plan(op, *shape, io_dtype, 0, &p);
     if (st != GMA_OK) return st;
     if ((!dmu || !dsigma2 || !dpi) && p.H > 0) return GMA_ERR_NULL_POINTER;
     if ((!XQ || !XK || !V || !dO || !dXQ || !dXK || !dV) && p.P > 0 && p.N > 0) return GMA_ERR_NULL_POINTER;
@@ -387,10 +391,31 @@ gma_status_t gma_backward_bidir(const void* XQ, const void* XK, const void* V, g
                           (const void*)dXK, (const void*)dV, (const void*)dmu, (const void*)dsigma2, (const void*)dpi})
         if (!gma::aligned16(q)) return GMA_ERR_MISALIGNED;
     if ((st = check_ws(p, workspace, workspace_bytes)) != GMA_OK) return st;
-    return launch_status(gma::f32_backward_bidir(
-        p, static_cast<const float*>(XQ), static_cast<const float*>(XK), static_cast<const float*>(V), mu, sigma2,
-        pi, eps, static_cast<const float*>(dO), static_cast<float*>(dXQ), static_cast<float*>(dXK),
-        static_cast<float*>(dV), dmu, dsigma2, dpi, static_cast<char*>(workspace), stream));
+    const float *q = static_cast<const float*>(XQ), *k = static_cast<const float*>(XK),
+                *v = static_cast<const float*>(V), *d = static_cast<const float*>(dO);
+    float *dq = static_cast<float*>(dXQ), *dk = static_cast<float*>(dXK), *dvv = static_cast<float*>(dV);
+    char* ws = static_cast<char*>(workspace);
+    if (op == GMA_OP_BACKWARD_CAUSAL)
+        return launch_status(gma::f32_backward_causal(p, q, k, v, mu, sigma2, pi, eps, d, dq, dk, dvv, dmu, dsigma2,
+                                                      dpi, ws, stream));
+    return launch_status(gma::f32_backward_bidir(p, q, k, v, mu, sigma2, pi, eps, d, dq, dk, dvv, dmu, dsigma2, dpi,
+                                                 ws, stream));
+}
+
+gma_status_t gma_backward_bidir(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                                const float* mu, const float* sigma2, const float* pi, float eps, const void* dO,
+                                void* dXQ, void* dXK, void* dV, float* dmu, float* dsigma2, float* dpi,
+                                const gma_shape_t* shape, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return backward_common(GMA_OP_BACKWARD_BIDIR, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, dO, dXQ, dXK, dV, dmu,
+                           dsigma2, dpi, shape, workspace, workspace_bytes, stream);
+}
+
+gma_status_t gma_backward_causal(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                                 const float* mu, const float* sigma2, const float* pi, float eps, const void* dO,
+                                 void* dXQ, void* dXK, void* dV, float* dmu, float* dsigma2, float* dpi,
+                                 const gma_shape_t* shape, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return backward_common(GMA_OP_BACKWARD_CAUSAL, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, dO, dXQ, dXK, dV, dmu,
+                           dsigma2, dpi, shape, workspace, workspace_bytes, stream);
 }
 
 gma_status_t gma_cross_workspace_size(const gma_cross_shape_t* shape, gma_dtype_t io_dtype, size_t* bytes_out) {

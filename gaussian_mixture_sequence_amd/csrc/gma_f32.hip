@@ -1147,4 +1147,298 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
 }
 
+// ---------------------------------------------------------------------------- causal backward
+// Gradients of <dO, O> for the causal forward (Eq. 6b, 8b).  Position i reads the prefix memory
+// Vt^(i), Z^(i) over j <= i, so with D_i = gamma^Q_i . Z^(i) + eps and a_i = dO_i . O_i
+//   g^Q_ik = (dO_i . Vt^(i)_k - a_i Z^(i)_k) / D_i,
+// and key position j receives the suffix sums of what every later (or equal) query position
+// sends to its memory:
+//   dVt_j = sum_{i>=j} gamma^Q_i dO_i^T / D_i,  dZ_j = -sum_{i>=j} gamma^Q_i a_i / D_i,
+//   dV_j = sum_k gamma^K_jk dVt_j[k],            g^K_jk = dVt_j[k] . V_j + dZ_j[k];
+// Eq. 18-20 follow as for the bidirectional backward.  Within a tile of T positions the prefix
+// (suffix) splits into the memory at the tile's start (end) and the masked T x T products
+// C_ij = gamma^Q_i . gamma^K_j and A_ij = (dO_i . V_j - a_i) / D_i for j <= i.
+namespace {
+
+size_t bwdc_lds_bytes(int T, int dr, int dv, int K) {
+    return size_t(T) * (dr + 3 * K + 2 * dv + 2 * T + 2) * sizeof(float);
+}
+
+// Causal: exclusive suffix over segments in place; segment g then holds the sum over the
+// segments after it.
+__global__ void __launch_bounds__(kThreads) f32_suffix_kernel(float* __restrict__ partials, int G, int E) {
+    const int64_t p = blockIdx.y;
+    const int e = blockIdx.x * kThreads + threadIdx.x;
+    if (e >= E) return;
+    float* src = partials + size_t(p) * G * E + e;
+    float run = 0.0f;
+    for (int g = G - 1; g >= 0; --g) {
+        const float a = src[size_t(g) * E];
+        src[size_t(g) * E] = run;
+        run += a;
+    }
+}
+
+// Grid (G segments, P).  QUERY walks the segment's tiles forward from the memory before the
+// segment (state: [Vt (K dv) | Z (K)], advanced in place), writes dX_Q, D_i and a_i of every
+// row (rowda), the segment's total of what its queries send to the memory (seg_part) and its
+// moments.  KEY walks the tiles backward from what the later segments' queries sent (state,
+// advanced in place), writes dX_K, dV and its moments.
+template <bool QUERY>
+__global__ void __launch_bounds__(kThreads)
+    f32_bwdc_kernel(const float* __restrict__ XQ, const float* __restrict__ XK, const float* __restrict__ V,
+                    const float* __restrict__ dO, int64_t N, int H, int dr, int dv, int K, int64_t seg, int G, int T,
+                    const double* c, const double* inv, const float* mu, float* state, float eps,
+                    float* __restrict__ rowda, float* __restrict__ dX, float* __restrict__ dV,
+                    float* __restrict__ seg_part, float* __restrict__ param_part) {
+    extern __shared__ float lds[];
+    const int64_t p = blockIdx.y;
+    const int gi = blockIdx.x, h = int(p % H);
+    float* xs = lds;          // T*dr: scratch of gamma_tile; left holding this side's rows
+    float* gq = xs + T * dr;  // T*K
+    float* gk = gq + T * K;   // T*K
+    float* gg = gk + T * K;   // T*K: upstream gradient, then ds
+    float* ys = gg + T * K;   // T*dv: dO
+    float* vs = ys + T * dv;  // T*dv: V
+    float* Cm = vs + T * dv;  // T*T
+    float* Am = Cm + T * T;   // T*T
+    float* dd = Am + T * T;   // T: D_i
+    float* aa = dd + T;       // T: a_i
+    const double *ch = c + size_t(h) * K, *ih = inv + size_t(h) * K * dr;
+    const float* mh = mu + size_t(h) * K * dr;
+    const int E = K * (dv + 1), PE = 2 * K * dr + K;
+    float* St = state + (size_t(p) * G + gi) * E;  // [K][dv], then Z
+    float* Zs = St + size_t(K) * dv;
+    float* sp = QUERY ? seg_part + (size_t(p) * G + gi) * E : nullptr;
+    float* pp = param_part + (size_t(p) * G + gi) * PE;
+    const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
+    const int ntiles = int((hi - lo + T - 1) / T);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    bool first = true;
+    for (int it = 0; it < ntiles; ++it) {
+        const int64_t n0 = lo + int64_t(QUERY ? it : ntiles - 1 - it) * T;
+        const int rows = int(min<int64_t>(T, hi - n0));
+        // responsibilities; the side's own rows are left in xs
+        if (QUERY) {
+            gamma_tile(XK + p * N * dr, n0, rows, T, dr, K, ch, ih, mh, xs, gk);
+            gamma_tile(XQ + p * N * dr, n0, rows, T, dr, K, ch, ih, mh, xs, gq);
+        } else {
+            gamma_tile(XQ + p * N * dr, n0, rows, T, dr, K, ch, ih, mh, xs, gq);
+            gamma_tile(XK + p * N * dr, n0, rows, T, dr, K, ch, ih, mh, xs, gk);
+        }
+        for (int i = threadIdx.x; i < T * dv; i += kThreads) {
+            const int t = i / dv;
+            ys[i] = t < rows ? dO[(p * N + n0) * dv + i] : 0.0f;
+            vs[i] = t < rows ? V[(p * N + n0) * dv + i] : 0.0f;
+        }
+        if (!QUERY)
+            for (int t = threadIdx.x; t < T; t += kThreads) {
+                dd[t] = t < rows ? rowda[(p * N + n0 + t) * 2 + 0] : 1.0f;
+                aa[t] = t < rows ? rowda[(p * N + n0 + t) * 2 + 1] : 0.0f;
+            }
+        // C_ij = gamma^Q_i . gamma^K_j (j <= i)
+        for (int e = threadIdx.x; e < T * T; e += kThreads) {
+            const int i = e / T, j = e - i * T;
+            float acc = 0.0f;
+            if (j <= i && i < rows)
+                for (int k = 0; k < K; ++k) acc = fmaf(gq[i * K + k], gk[j * K + k], acc);
+            Cm[e] = acc;
+        }
+        __syncthreads();
+        if (QUERY) {  // D_i and a_i from the memory at the tile's start and the tile's own keys
+            for (int t = wave; t < rows; t += kThreads / kWave) {
+                float d = 0.0f;
+                for (int k = lane; k < K; k += kWave) d = fmaf(gq[t * K + k], Zs[k], d);
+                for (int j = lane; j <= t; j += kWave) d += Cm[t * T + j];
+                d = wave_sum(d) + eps;
+                float a = 0.0f;
+                for (int cc = lane; cc < dv; cc += kWave) {
+                    float nn = 0.0f;
+                    for (int k = 0; k < K; ++k) nn = fmaf(gq[t * K + k], St[size_t(k) * dv + cc], nn);
+                    for (int j = 0; j <= t; ++j) nn = fmaf(Cm[t * T + j], vs[j * dv + cc], nn);
+                    a = fmaf(ys[t * dv + cc], nn / d, a);
+                }
+                a = wave_sum(a);
+                if (lane == 0) {
+                    dd[t] = d;
+                    aa[t] = a;
+                    rowda[(p * N + n0 + t) * 2 + 0] = d;
+                    rowda[(p * N + n0 + t) * 2 + 1] = a;
+                }
+            }
+            __syncthreads();
+        }
+        // A_ij = (dO_i . V_j - a_i) / D_i (j <= i)
+        for (int e = threadIdx.x; e < T * T; e += kThreads) {
+            const int i = e / T, j = e - i * T;
+            float acc = 0.0f;
+            if (j <= i && i < rows) {
+                for (int cc = 0; cc < dv; ++cc) acc = fmaf(ys[i * dv + cc], vs[j * dv + cc], acc);
+                acc = (acc - aa[i]) / dd[i];
+            }
+            Am[e] = acc;
+        }
+        __syncthreads();
+        if (QUERY) {  // g^Q
+            for (int e = threadIdx.x; e < T * K; e += kThreads) {
+                const int t = e / K, k = e - t * K;
+                float acc = 0.0f;
+                if (t < rows) {
+                    for (int cc = 0; cc < dv; ++cc) acc = fmaf(ys[t * dv + cc], St[size_t(k) * dv + cc], acc);
+                    acc = (acc - aa[t] * Zs[k]) / dd[t];
+                    for (int j = 0; j <= t; ++j) acc = fmaf(Am[t * T + j], gk[j * K + k], acc);
+                }
+                gg[e] = acc;
+            }
+        } else {  // dV and g^K from the memory gradient after the tile and the tile's own queries
+            for (int e = threadIdx.x; e < rows * dv; e += kThreads) {
+                const int j = e / dv, cc = e - j * dv;
+                float acc = 0.0f;
+                for (int k = 0; k < K; ++k) acc = fmaf(gk[j * K + k], St[size_t(k) * dv + cc], acc);
+                for (int i = j; i < rows; ++i) acc = fmaf(Cm[i * T + j], ys[i * dv + cc] / dd[i], acc);
+                dV[(p * N + n0) * dv + e] = acc;
+            }
+            for (int e = threadIdx.x; e < T * K; e += kThreads) {
+                const int j = e / K, k = e - j * K;
+                float acc = 0.0f;
+                if (j < rows) {
+                    for (int cc = 0; cc < dv; ++cc) acc = fmaf(vs[j * dv + cc], St[size_t(k) * dv + cc], acc);
+                    acc += Zs[k];
+                    for (int i = j; i < rows; ++i) acc = fmaf(Am[i * T + j], gq[i * K + k], acc);
+                }
+                gg[e] = acc;
+            }
+        }
+        __syncthreads();
+        // Eq. 18 with this side's responsibilities, one wave per row
+        const float* gm = QUERY ? gq : gk;
+        for (int t = wave; t < T; t += kThreads / kWave) {
+            float w = 0.0f;
+            for (int k = lane; k < K; k += kWave) w = fmaf(gm[t * K + k], gg[t * K + k], w);
+            w = wave_sum(w);
+            for (int k = lane; k < K; k += kWave) gg[t * K + k] = gm[t * K + k] * (gg[t * K + k] - w);
+        }
+        __syncthreads();
+        // routing-vector gradient
+        for (int i = threadIdx.x; i < rows * dr; i += kThreads) {
+            const int t = i / dr, d = i - t * dr;
+            float acc = 0.0f;
+            for (int k = 0; k < K; ++k)
+                acc = fmaf(gg[t * K + k], float((double(xs[t * dr + d]) - double(mh[size_t(k) * dr + d])) * ih[size_t(k) * dr + d]), acc);
+            dX[(p * N + n0) * dr + i] = -acc;
+        }
+        // moments of these rows
+        for (int e = threadIdx.x; e < K * dr; e += kThreads) {
+            const int k = e / dr, d = e - k * dr;
+            const double m = double(mh[e]);
+            double a1 = 0.0, a2 = 0.0;
+            for (int t = 0; t < rows; ++t) {
+                const double df = double(xs[t * dr + d]) - m, w = double(gg[t * K + k]) * df;
+                a1 += w;
+                a2 += w * df;
+            }
+            pp[e] = first ? float(a1) : pp[e] + float(a1);
+            pp[K * dr + e] = first ? float(a2) : pp[K * dr + e] + float(a2);
+        }
+        for (int k = threadIdx.x; k < K; k += kThreads) {
+            float acc = 0.0f;
+            for (int t = 0; t < rows; ++t) acc += gg[t * K + k];
+            pp[2 * K * dr + k] = first ? acc : pp[2 * K * dr + k] + acc;
+        }
+        __syncthreads();  // every read of the memory for this tile is done
+        // advance the memory past the tile: QUERY adds the tile's keys (Eq. 6b) and totals what
+        // its queries send; KEY adds what the tile's queries send
+        for (int e = threadIdx.x; e < E; e += kThreads) {
+            float qsum = 0.0f, ksum = 0.0f;
+            if (e < K * dv) {
+                const int k = e / dv, cc = e - k * dv;
+                for (int t = 0; t < rows; ++t) {
+                    qsum = fmaf(gq[t * K + k], ys[t * dv + cc] / dd[t], qsum);
+                    if (QUERY) ksum = fmaf(gk[t * K + k], vs[t * dv + cc], ksum);
+                }
+            } else {
+                const int k = e - K * dv;
+                for (int t = 0; t < rows; ++t) {
+                    qsum -= gq[t * K + k] * aa[t] / dd[t];
+                    if (QUERY) ksum += gk[t * K + k];
+                }
+            }
+            if (QUERY) {
+                St[e] += ksum;
+                sp[e] = first ? qsum : sp[e] + qsum;
+            } else {
+                St[e] += qsum;
+            }
+        }
+        first = false;
+        __syncthreads();  // the memory and the tile's LDS are ready for the next tile
+    }
+    if (first) {  // empty segment
+        for (int e = threadIdx.x; e < PE; e += kThreads) pp[e] = 0.0f;
+        if (QUERY)
+            for (int e = threadIdx.x; e < E; e += kThreads) sp[e] = 0.0f;
+    }
+}
+
+}  // namespace
+
+size_t f32_backward_causal_extra_bytes(const Plan& p) {
+    const size_t E = size_t(p.K) * size_t(p.dv + 1);
+    return round_up(size_t(p.P * p.G) * E * 4, 256) + round_up(size_t(p.P * p.N) * 2 * 4, 256) +
+           round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256);
+}
+
+hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
+                               const float* s2, const float* pi, float eps, const float* dO, float* dXQ, float* dXK,
+                               float* dV, float* dmu, float* ds2, float* dpi, char* ws, hipStream_t st) {
+    if (p.H == 0) return hipSuccess;
+    if (p.P == 0 || p.N == 0) return reduce_params(p, nullptr, 0, nullptr, pi, dmu, ds2, dpi, st);  // zero gradients
+    static const hipError_t attr = [] {
+        const void* fns[] = {(const void*)f32_bwdc_kernel<true>, (const void*)f32_bwdc_kernel<false>};
+        for (const void* f : fns) {
+            hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
+            if (r != hipSuccess) return r;
+        }
+        return hipSuccess;
+    }();
+    if (attr != hipSuccess) return attr;
+    hipError_t e = launch_params(p, s2, pi, ws, st);
+    if (e != hipSuccess) return e;
+    F32Params v = f32_params_view(p, ws);
+    float* states = reinterpret_cast<float*>(ws + p.off_partials);  // segment aggregates, then running memories
+    const size_t E = size_t(p.K) * size_t(p.dv + 1);
+    char* extra = ws + p.total - f32_backward_causal_extra_bytes(p);
+    float* seg_part = reinterpret_cast<float*>(extra);
+    float* rowda = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256));
+    float* ppart = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256) +
+                                            round_up(size_t(p.P * p.N) * 2 * 4, 256));
+    float* ppart_key = ppart + size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K);
+    const dim3 grid(unsigned(p.G), unsigned(p.P));
+    const int Ei = int(E);
+    const dim3 egrid(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P));
+    const int H = int(p.H), dr = int(p.dr), dv = int(p.dv), K = int(p.K), G = int(p.G);
+    if (p.G > 1) {  // segment aggregates of the forward memory (one segment: the prefix writes zeros)
+        const size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
+        GMA_LAUNCH("f32_bwdc_aggregate", f32_write_kernel, grid, dim3(kThreads), lds_w, st, XK, V, p.N, H, dr, dv, K,
+                   p.seg, G, v.c, v.inv, mu, states);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    GMA_LAUNCH("f32_bwdc_prefix", f32_prefix_kernel, egrid, dim3(kThreads), 0, st, states, G, Ei,
+               static_cast<const float*>(nullptr), K, dv);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    int T = kTile;
+    while (T > 8 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
+    const size_t lds = bwdc_lds_bytes(T, dr, dv, K);
+    GMA_LAUNCH("f32_bwdc_query", f32_bwdc_kernel<true>, grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N, H, dr,
+               dv, K, p.seg, G, T, v.c, v.inv, mu, states, eps, rowda, dXQ, static_cast<float*>(nullptr), seg_part,
+               ppart);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    GMA_LAUNCH("f32_bwdc_suffix", f32_suffix_kernel, egrid, dim3(kThreads), 0, st, seg_part, G, Ei);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    GMA_LAUNCH("f32_bwdc_key", f32_bwdc_kernel<false>, grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N, H, dr, dv,
+               K, p.seg, G, T, v.c, v.inv, mu, seg_part, eps, rowda, dXK, dV, static_cast<float*>(nullptr), ppart_key);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
+}
+
 }  // namespace gma

@@ -84,6 +84,12 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
                               const float* s2, const float* pi, float eps, const float* dO, float* dXQ, float* dXK,
                               float* dV, float* dmu, float* ds2, float* dpi, char* ws, hipStream_t st);
 
+// Backward of the causal forward (fp32): workspace beyond the causal plan's own, and the launcher.
+size_t f32_backward_causal_extra_bytes(const Plan& p);
+hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
+                               const float* s2, const float* pi, float eps, const float* dO, float* dXQ, float* dXK,
+                               float* dV, float* dmu, float* ds2, float* dpi, char* ws, hipStream_t st);
+
 // ---- responsibility diagnostics (gma_diag.hip) ---------------------------------
 // Workspace: Gamma [B][H][N][K] fp32, then per-block partial sums, then the responsibilities
 // plan's own workspace.

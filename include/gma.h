@@ -79,7 +79,8 @@ typedef enum {
     GMA_OP_BIDIR = 1,
     GMA_OP_CAUSAL = 2,
     GMA_OP_DIAGNOSTICS = 3,
-    GMA_OP_BACKWARD_BIDIR = 4
+    GMA_OP_BACKWARD_BIDIR = 4,
+    GMA_OP_BACKWARD_CAUSAL = 5
 } gma_op_t;
 
 /* Problem sizes: batch B, heads H, sequence length N, routing dim d_r, value dim d_v,
@@ -252,6 +253,26 @@ gma_status_t gma_backward_bidir(const void* XQ, const void* XK, const void* V, g
                                 const void* dO, void* dXQ, void* dXK, void* dV, float* dmu, float* dsigma2,
                                 float* dpi, const gma_shape_t* shape, void* workspace, size_t workspace_bytes,
                                 hipStream_t stream);
+
+/*
+ * Backward pass of the causal forward (gma_forward_causal): the gradients of <dO, O> with
+ * respect to every input, Sec. 4.1 Eq. 17-20 through the prefix memory of Sec. 3.5 Eq. 6b, 8b.
+ * Position i reads Vt^(i), Z^(i) over j <= i, so with D_i = (Gamma_Q Z^(i))_i + eps and
+ * a_i = dO_i . O_i the query side is
+ *   g^Q_ik = (dO_i . Vt^(i)_k - a_i Z^(i)_k) / D_i,
+ * and key position j receives the suffix sums over the positions that read it:
+ *   dVt_j = sum_{i>=j} Gamma_Q[i,:]^T dO_i / D_i,  dZ_j = -sum_{i>=j} Gamma_Q[i,:] a_i / D_i,
+ *   dV[j,:] = sum_k Gamma_K[j,k] dVt_j[k,:],        g^K_jk = dVt_j[k,:] . V_j + dZ_j[k];
+ * the softmax Jacobian, the routing-vector and the parameter gradients are those of
+ * gma_backward_bidir.  Shapes, dtypes (fp32 only), outputs, workspace
+ * (gma_workspace_size(GMA_OP_BACKWARD_CAUSAL, shape, GMA_F32, 0, ...), which also holds D_i and
+ * a_i of every position) and errors as for gma_backward_bidir.
+ */
+gma_status_t gma_backward_causal(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                                 const float* mu, const float* sigma2, const float* pi, float eps,
+                                 const void* dO, void* dXQ, void* dXK, void* dV, float* dmu, float* dsigma2,
+                                 float* dpi, const gma_shape_t* shape, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 /*
  * Kernel timing (optional tracing).  While enabled, every kernel the library launches is

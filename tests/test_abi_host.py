@@ -233,23 +233,25 @@ def test_diagnostics_argument_errors(lib):
     assert f(FAKE, 7, FAKE, FAKE, FAKE, sh, FAKE, FAKE, None, None, FAKE, need, None) == VALUE
 
 
-def test_backward_argument_errors(lib):
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_argument_errors(lib, causal):
     F, BF = gb.GMA_F32, gb.GMA_BF16
-    Bw = gb.GMA_OP_BACKWARD_BIDIR
+    Bw = gb.GMA_OP_BACKWARD_CAUSAL if causal else gb.GMA_OP_BACKWARD_BIDIR
+    fn = lib.gma_backward_causal if causal else lib.gma_backward_bidir
     assert ws_size(Bw, 8, 8, 4096, 64, 64, 64, F)[0] == OK
     assert ws_size(Bw, 8, 8, 4096, 64, 64, 64, BF)[0] == UNSUP   # fp32 only
     assert ws_size(Bw, 1, 1, 8, 16, 0, 8, F)[0] == UNSUP          # needs values
     assert ws_size(Bw, 1, 1, 8, 129, 32, 8, F)[0] == UNSUP
     assert ws_size(Bw, 1, -1, 8, 16, 32, 8, F)[0] == SHAPE
     # more scratch than the forward: the gradient memory and the parameter partials
-    assert ws_size(Bw, 8, 8, 4096, 64, 64, 64, F)[1] > ws_size(gb.GMA_OP_BIDIR, 8, 8, 4096, 64, 64, 64, F)[1]
+    fwd = gb.GMA_OP_CAUSAL if causal else gb.GMA_OP_BIDIR
+    assert ws_size(Bw, 8, 8, 4096, 64, 64, 64, F)[1] > ws_size(fwd, 8, 8, 4096, 64, 64, 64, F)[1]
     shape = (2, 3, 64, 16, 32, 8)
     need = ws_size(Bw, *shape, F)[1]
     sh = ctypes.byref(gb.Shape(*shape))
 
     def call(xq=FAKE, io=F, pi=FAKE, eps=1e-6, d_o=FAKE, dxk=FAKE, dmu=FAKE, dpi=FAKE, ws=FAKE, nb=need, s=sh):
-        return lib.gma_backward_bidir(xq, FAKE, FAKE, io, FAKE, FAKE, pi, eps, d_o, FAKE, dxk, FAKE, dmu, FAKE, dpi,
-                                      s, ws, nb, None)
+        return fn(xq, FAKE, FAKE, io, FAKE, FAKE, pi, eps, d_o, FAKE, dxk, FAKE, dmu, FAKE, dpi, s, ws, nb, None)
 
     assert call(xq=None) == NULLP
     assert call(d_o=None) == NULLP

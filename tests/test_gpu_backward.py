@@ -1,5 +1,6 @@
-"""GPU parity of the backward pass of the bidirectional forward (Sec. 4.1, Eq. 17-20) through
-the C ABI, against the fp64 oracle's backward on the same seeded inputs and upstream gradient.
+"""GPU parity of the backward passes of the bidirectional and causal forwards (Sec. 4.1, Eq.
+17-20; Sec. 3.5 Eq. 6b, 8b) through the C ABI, against the fp64 oracle's backward on the same
+seeded inputs and upstream gradient.
 
 Error measure: per output tensor, max |g - g*| / max |g*| (tensor-scaled).  The gradients are
 sums of responsibility-weighted terms of both signs (the centring of Eq. 18 makes every row of
@@ -139,6 +140,82 @@ def test_backward_full_size_sampled_heads():
         sl = head_slice(inp, b, h)
         ref = oracle.backward.backward_bidir(sl["xq"], sl["xk"], sl["v"], sl["mu"], sl["sigma2"], sl["pi"], w.eps,
                                              d_o[b:b + 1, h:h + 1])
+        for k in ("dXQ", "dXK", "dV"):
+            err = tensor_error(got[k][b:b + 1, h:h + 1], ref[k])
+            assert err <= TOL_BWD, (b, h, k, err)
+    for k in ("dmu", "dsigma2", "dpi"):
+        assert np.isfinite(got[k]).all(), k
+
+
+# ---------------------------------------------------------------------------- causal
+
+
+def run_gpu_causal(w: Workload, inp, d_o):
+    d = to_device(inp)
+    g = gb.gma_backward_causal(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], d_o.cuda(), w.eps)
+    torch.cuda.synchronize()
+    return {k: to_np(v) for k, v in g.items()}
+
+
+def run_oracle_causal(w: Workload, inp, d_o):
+    return oracle.backward.backward_causal(inp["xq"], inp["xk"], inp["v"], inp["mu"], inp["sigma2"], inp["pi"],
+                                           w.eps, d_o)
+
+
+CAUSAL_CASES = [
+    WORKLOADS["bidir_small_f32"].with_(causal=True),
+    case(1000, 101, B=2, H=3, d_r=7, d_v=5, K=13),       # ragged dims, 16 segments of one tile
+    case(2, 102),                                        # two positions
+    case(3000, 103, d_r=32, d_v=64, K=64),              # several tiles per segment, ragged tail
+    case(300, 104, B=1, H=1, d_r=128, d_v=128, K=256),  # maximum dims (half-height tiles)
+    case(700, 105, B=3, H=2, d_r=64, d_v=32, K=128, mu_std=1.5),
+]
+
+
+@pytest.mark.parametrize("w", CAUSAL_CASES, ids=cid)
+def test_backward_causal_parity(w):
+    inp = make_inputs(w)
+    d_o = upstream(w, w.seed + 1000)
+    got, ref = run_gpu_causal(w, inp, d_o), run_oracle_causal(w, inp, d_o)
+    for k in KEYS:
+        assert got[k].shape == ref[k].shape, k
+        assert np.isfinite(got[k]).all(), k
+        err = tensor_error(got[k], ref[k])
+        assert err <= TOL_BWD, (k, err)
+
+
+def test_backward_causal_deterministic():
+    w = case(3000, 106, B=2, H=2)
+    inp = make_inputs(w)
+    d_o = upstream(w, 1106)
+    a, b = run_gpu_causal(w, inp, d_o), run_gpu_causal(w, inp, d_o)
+    for k in KEYS:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_backward_causal_no_rows_gives_zero_parameter_gradients():
+    w = case(0, 107)
+    inp = make_inputs(w)
+    d = to_device(inp)
+    g = gb.gma_backward_causal(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"],
+                               torch.empty(w.B, w.H, 0, w.d_v, device="cuda"), w.eps)
+    torch.cuda.synchronize()
+    for k in ("dmu", "dsigma2", "dpi"):
+        assert not to_np(g[k]).any(), k
+
+
+def test_backward_causal_full_size_sampled_heads():
+    """The B=8, H=12, N=2048, d_r=d_v=64, K=32 causal dims in fp32 (five segments per problem):
+    the per-position gradients of sampled (batch, head) problems against the oracle run on that
+    problem alone."""
+    w = WORKLOADS["causal_b8h12_n2048"].with_(dtype="f32", name="bwdc_full")
+    inp = make_inputs(w)
+    d_o = upstream(w, 2002)
+    got = run_gpu_causal(w, inp, d_o)
+    for b, h in ((0, 0), (5, 7), (7, 11)):
+        sl = head_slice(inp, b, h)
+        ref = oracle.backward.backward_causal(sl["xq"], sl["xk"], sl["v"], sl["mu"], sl["sigma2"], sl["pi"], w.eps,
+                                              d_o[b:b + 1, h:h + 1])
         for k in ("dXQ", "dXK", "dV"):
             err = tensor_error(got[k][b:b + 1, h:h + 1], ref[k])
             assert err <= TOL_BWD, (b, h, k, err)
