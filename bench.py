@@ -260,6 +260,12 @@ def alg_bytes_per_token_head(w, kernel: str) -> float:
     if w.diagnostics:  # the routing vectors in; the outputs (per token, not per head) are negligible
         return e * w.d_r
     if w.backward:
+        if kernel.endswith("_bwdc_aggregate"):
+            return e * (w.d_r + w.d_v)          # X_K and V in
+        if kernel.endswith("_bwdc_query"):
+            return e * (3 * w.d_r + 2 * w.d_v)  # X_Q, X_K, V, dO in, dX_Q out
+        if kernel.endswith("_bwdc_key"):
+            return e * (3 * w.d_r + 3 * w.d_v)  # X_Q, X_K, V, dO in, dX_K and dV out
         if kernel.endswith("_bwd_write"):
             return e * (w.d_r + w.d_v)          # X_K and V in
         if kernel.endswith("_bwd_query"):
@@ -290,6 +296,13 @@ def alg_flops_per_token_head(w, kernel: str) -> float:
     if not w.backward:
         return 0.0
     K, dr, dv = w.K, w.d_r, w.d_v
+    T = 64  # positions per tile of the causal passes: the masked in-tile products cost T/2 per row
+    if kernel.endswith("_bwdc_aggregate"):
+        return 3 * K * dr + 2 * K * dv + 4 * K
+    if kernel.endswith("_bwdc_query"):  # the bidirectional query pass, the keys' scores, the memory update
+        return 15 * K * dr + 8 * K * dv + 15 * K + 2 * dv + 2 * T * K + 2 * T * dv
+    if kernel.endswith("_bwdc_key"):    # the bidirectional key pass, the queries' scores, the suffix update
+        return 15 * K * dr + 6 * K * dv + 11 * K + 2 * T * K + 2 * T * dv
     if kernel.endswith("_bwd_write"):
         return 3 * K * dr + 2 * K * dv + 4 * K
     if kernel.endswith("_bwd_query"):
@@ -303,6 +316,7 @@ KERNEL_SYMBOL = {"bf16_scan": "gma::bf::scan_kernel", "bf16_bidir": "gma::bf::bi
                  "bf16_cross": "gma::bf::bidir_kernel", "bf16_resp": "gma::bf::resp_kernel",
                  "bf16_decode": "gma::dec::decode_kernel", "bf16_diag": "gma::diag::diag_fused_kernel",
                  "f32_bwd_query": "gma::f32_bwd_tiled_kernel<1>", "f32_bwd_key": "gma::f32_bwd_tiled_kernel<2>",
+                 "f32_bwdc_query": "gma::f32_bwdc_kernel<true>", "f32_bwdc_key": "gma::f32_bwdc_kernel<false>",
                  "bf16_causal": "gma::bf::causal_kernel", "bf16_causal_aggregate": "gma::bf::write_kernel<64, 1"}
 
 
@@ -316,7 +330,8 @@ def cpu_backward_sample(cpu_inputs):
     while True:
         b, h = divmod(done % (w.B * w.H), w.H)
         sl = {k: (v[b:b + 1, h:h + 1] if k in ("xq", "xk", "v", "d_o") else v[h:h + 1]) for k, v in d.items()}
-        oracle.backward.backward_bidir(sl["xq"], sl["xk"], sl["v"], sl["mu"], sl["sigma2"], sl["pi"], w.eps, sl["d_o"])
+        fn = oracle.backward.backward_causal if w.causal else oracle.backward.backward_bidir
+        fn(sl["xq"], sl["xk"], sl["v"], sl["mu"], sl["sigma2"], sl["pi"], w.eps, sl["d_o"])
         done += 1
         cpu_s = time.perf_counter() - tc
         if cpu_s >= 10.0:
@@ -393,7 +408,8 @@ def main(args=None, probe_only=False) -> int:
         elif w.diagnostics:
             nbytes = gb.gma_workspace_size(gb.GMA_OP_DIAGNOSTICS, w.B, w.H, w.N, w.d_r, 0, w.K, io)
         elif w.backward:
-            nbytes = gb.gma_workspace_size(gb.GMA_OP_BACKWARD_BIDIR, w.B, w.H, w.N, w.d_r, w.d_v, w.K, io)
+            nbytes = gb.gma_workspace_size(gb.GMA_OP_BACKWARD_CAUSAL if w.causal else gb.GMA_OP_BACKWARD_BIDIR,
+                                           w.B, w.H, w.N, w.d_r, w.d_v, w.K, io)
         else:
             nbytes = gb.gma_workspace_size(op, w.B, w.H, 1 if w.decode else w.N, w.d_r, w.d_v, w.K, io, w.chunk)
         wss.append(torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev))
@@ -406,6 +422,9 @@ def main(args=None, probe_only=False) -> int:
             if w.diagnostics:
                 gb.gma_responsibility_diagnostics(d["xq"], d["mu"], d["sigma2"], d["pi"], workspace=wss[i],
                                                   stream=stream)
+            elif w.backward and w.causal:
+                gb.gma_backward_causal(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], d["d_o"], w.eps,
+                                       out=outs[i][s], workspace=wss[i], stream=stream)
             elif w.backward:
                 gb.gma_backward_bidir(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], d["d_o"], w.eps,
                                       out=outs[i][s], workspace=wss[i], stream=stream)
@@ -463,7 +482,9 @@ def main(args=None, probe_only=False) -> int:
     kernel_of = {}
     for w in ws_list:
         pre = "bf16" if w.dtype == "bf16" else "f32"
-        ks = ["params", "bwd_write", "bwd_combine", "bwd_query", "bwd_key", "bwd_params"] if w.backward else \
+        ks = ["params", "bwdc_aggregate", "bwdc_prefix", "bwdc_query", "bwdc_suffix", "bwdc_key", "bwd_params"] \
+            if w.backward and w.causal else \
+            ["params", "bwd_write", "bwd_combine", "bwd_query", "bwd_key", "bwd_params"] if w.backward else \
             ["diag", "resp", "params"] if w.diagnostics else \
             ["params", "scan", "causal_aggregate", "causal", "prefix", "decode"] if w.causal else \
             ["params", "cross_write", "cross_combine", "cross_read", "cross"] if w.cross else \
@@ -529,10 +550,10 @@ def main(args=None, probe_only=False) -> int:
                 "X_Q,X_K,V~N(0,1); %d rotating input sets)" % args.sets,
         "config": {
             "workload": " + ".join("%s (%s B=%d H=%d %s d_r=%d d_v=%d K=%d%s)" % (
-                w.name, "causal" if w.causal else "cross" if w.cross else "bidir backward" if w.backward else "bidir",
+                w.name, ("causal" if w.causal else "cross" if w.cross else "bidir") + (" backward" if w.backward else ""),
                 w.B, w.H,
                 "N_q=%d N_k=%d" % (w.N, w.n_ctx) if w.cross else "N=%d" % w.N, w.d_r, w.d_v, w.K,
-                ", chunk=%d" % w.chunk if w.causal else "") for w in ws_list),
+                ", chunk=%d" % w.chunk if w.causal and not w.backward else "") for w in ws_list),
             "tokens_per_step": tokens_per_step,
             "eps": 1e-6,
         },

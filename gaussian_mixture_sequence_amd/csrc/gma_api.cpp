@@ -22,6 +22,7 @@ constexpr int64_t kTokenTile = 64;      // tokens per tile in every kernel famil
 constexpr int64_t kBidirBlocks = 512;   // target workgroups for the split-N write and the read
                                         // (two resident per CU: one wave of workgroups)
 constexpr int64_t kCausalBlocks = 512;  // target workgroups for the segmented scan
+constexpr int64_t kBackwardBlocks = 2048;  // target workgroups for the causal backward's segments
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -64,6 +65,16 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
         if (io != GMA_F32) return GMA_ERR_UNSUPPORTED;
         const bool causal = op == GMA_OP_BACKWARD_CAUSAL;
         if ((st = make_plan(causal ? GMA_OP_CAUSAL : GMA_OP_BIDIR, s, io, causal ? 64 : 0, pl)) != GMA_OK) return st;
+        if (causal && pl->P > 0 && pl->N > 0) {
+            // the causal backward walks each segment's positions in order: finer segments than the
+            // forward's (about kBackwardBlocks workgroups), each a multiple of the token tile; the
+            // regions are laid out as for the causal forward with this split
+            const int64_t g = std::max<int64_t>(1, std::min(cdiv(kBackwardBlocks, pl->P), cdiv(pl->N, kTokenTile)));
+            pl->seg = round_up(size_t(cdiv(pl->N, g)), kTokenTile);
+            pl->G = cdiv(pl->N, pl->seg);
+            pl->seg_q = pl->seg;
+            layout(pl);
+        }
         pl->op = op;
         pl->chunk = 0;
         pl->total += causal ? f32_backward_causal_extra_bytes(*pl) : f32_backward_extra_bytes(*pl);

@@ -1418,15 +1418,26 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
     const dim3 egrid(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P));
     const int H = int(p.H), dr = int(p.dr), dv = int(p.dv), K = int(p.K), G = int(p.G);
     if (p.G > 1) {  // segment aggregates of the forward memory (one segment: the prefix writes zeros)
-        const size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
-        GMA_LAUNCH("f32_bwdc_aggregate", f32_write_kernel, grid, dim3(kThreads), lds_w, st, XK, V, p.N, H, dr, dv, K,
-                   p.seg, G, v.c, v.inv, mu, states);
+        if (bwd_tiled_applies(p)) {
+            if ((e = bwd_allow_lds()) != hipSuccess) return e;
+            GMA_LAUNCH("f32_bwdc_aggregate", f32_bwd_tiled_kernel<BWD_WRITE>, grid, dim3(kThreads),
+                       bwd_tiled_lds_bytes(BWD_WRITE, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv,
+                       mu, static_cast<const float*>(nullptr), eps, static_cast<float*>(nullptr),
+                       static_cast<float*>(nullptr), states, static_cast<float*>(nullptr));
+        } else {
+            const size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
+            GMA_LAUNCH("f32_bwdc_aggregate", f32_write_kernel, grid, dim3(kThreads), lds_w, st, XK, V, p.N, H, dr, dv,
+                       K, p.seg, G, v.c, v.inv, mu, states);
+        }
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     GMA_LAUNCH("f32_bwdc_prefix", f32_prefix_kernel, egrid, dim3(kThreads), 0, st, states, G, Ei,
                static_cast<const float*>(nullptr), K, dv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    // 64-position tiles when two workgroups fit a CU, else the largest tile that lets two fit
+    // (down to 32), else the largest that fits at all
     int T = kTile;
+    while (T > 32 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds / 2) T /= 2;
     while (T > 8 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
     const size_t lds = bwdc_lds_bytes(T, dr, dv, K);
     GMA_LAUNCH("f32_bwdc_query", f32_bwdc_kernel<true>, grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N, H, dr,

@@ -87,6 +87,9 @@ WORKLOADS: Dict[str, Workload] = {
     # backward of the bidirectional forward (Sec. 4.1), fp32: the B=8, H=8, N=4096 bidirectional dims
     "bwd_b8h8_n4096_f32": Workload("bwd_b8h8_n4096_f32", False, 8, 8, 4096, 64, 64, 64, "f32", seed=8,
                                    backward=True),
+    # backward of the causal forward, fp32: the B=8, H=12, N=2048 causal dims
+    "bwdc_b8h12_n2048_f32": Workload("bwdc_b8h12_n2048_f32", True, 8, 12, 2048, 64, 64, 32, "f32", seed=9,
+                                     backward=True),
     "cross_b8h8_q4096_k16384": Workload("cross_b8h8_q4096_k16384", False, 8, 8, 4096, 64, 64, 64, "bf16",
                                         seed=5, n_ctx=16384),
 }
