@@ -54,17 +54,28 @@ gma_status_t check_dims(gma_op_t op, const gma_shape_t& s, gma_dtype_t io) {
 
 void layout(Plan* pl);
 
+// fp32 copies of X_Q, X_K, V, dO (inputs) and dX_Q, dX_K, dV (outputs) for a bf16 backward, in
+// that order after the fp32 passes' regions.
+size_t backward_stage_bytes(const Plan& p) {
+    const size_t r = round_up(size_t(p.P * p.N * p.dr) * 4, 256), v = round_up(size_t(p.P * p.N * p.dv) * 4, 256);
+    return 4 * r + 3 * v;
+}
+
 gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_t chunk, Plan* pl) {
     if (op != GMA_OP_RESPONSIBILITIES && op != GMA_OP_BIDIR && op != GMA_OP_CAUSAL && op != GMA_OP_DIAGNOSTICS &&
         op != GMA_OP_BACKWARD_BIDIR && op != GMA_OP_BACKWARD_CAUSAL)
         return GMA_ERR_BAD_VALUE;
     if (io != GMA_F32 && io != GMA_BF16) return GMA_ERR_BAD_VALUE;
-    gma_status_t st = check_dims(op, s, io);
+    // the backward computes in fp32 at either I/O dtype, so it takes the fp32 size limits
+    const bool backward = op == GMA_OP_BACKWARD_BIDIR || op == GMA_OP_BACKWARD_CAUSAL;
+    gma_status_t st = check_dims(op, s, backward ? GMA_F32 : io);
     if (st != GMA_OK) return st;
-    if (op == GMA_OP_BACKWARD_BIDIR || op == GMA_OP_BACKWARD_CAUSAL) {  // the forward's plan (fp32 only), then the gradient scratch
-        if (io != GMA_F32) return GMA_ERR_UNSUPPORTED;
+    if (op == GMA_OP_BACKWARD_BIDIR || op == GMA_OP_BACKWARD_CAUSAL) {
+        // the fp32 forward's plan, then the gradient scratch; bf16 I/O adds fp32 copies of the
+        // inputs and outputs
         const bool causal = op == GMA_OP_BACKWARD_CAUSAL;
-        if ((st = make_plan(causal ? GMA_OP_CAUSAL : GMA_OP_BIDIR, s, io, causal ? 64 : 0, pl)) != GMA_OK) return st;
+        if ((st = make_plan(causal ? GMA_OP_CAUSAL : GMA_OP_BIDIR, s, GMA_F32, causal ? 64 : 0, pl)) != GMA_OK)
+            return st;
         if (causal && pl->P > 0 && pl->N > 0) {
             // the causal backward walks each segment's positions in order: finer segments than the
             // forward's (about kBackwardBlocks workgroups), each a multiple of the token tile; the
@@ -78,6 +89,11 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
         pl->op = op;
         pl->chunk = 0;
         pl->total += causal ? f32_backward_causal_extra_bytes(*pl) : f32_backward_extra_bytes(*pl);
+        pl->off_stage = pl->total;
+        if (io == GMA_BF16) {
+            pl->io = io;
+            pl->total += backward_stage_bytes(*pl);
+        }
         return GMA_OK;
     }
     if (op == GMA_OP_CAUSAL && chunk != 16 && chunk != 32 && chunk != 64) return GMA_ERR_UNSUPPORTED;
@@ -406,11 +422,30 @@ static gma_status_t backward_common(gma_op_t op, const void* XQ, const void* XK,
                 *v = static_cast<const float*>(V), *d = static_cast<const float*>(dO);
     float *dq = static_cast<float*>(dXQ), *dk = static_cast<float*>(dXK), *dvv = static_cast<float*>(dV);
     char* ws = static_cast<char*>(workspace);
+    const bool staged = io_dtype == GMA_BF16 && p.P > 0 && p.N > 0;
+    const size_t nr = size_t(p.P * p.N * p.dr), nv = size_t(p.P * p.N * p.dv);
+    hipError_t e = hipSuccess;
+    if (staged) {  // fp32 copies of the inputs; the passes write fp32 outputs next to them
+        const size_t r = gma::round_up(nr * 4, 256), vb = gma::round_up(nv * 4, 256);
+        char* sg = ws + p.off_stage;
+        float *q32 = reinterpret_cast<float*>(sg), *k32 = reinterpret_cast<float*>(sg + r),
+              *v32 = reinterpret_cast<float*>(sg + 2 * r), *d32 = reinterpret_cast<float*>(sg + 2 * r + vb);
+        dq = reinterpret_cast<float*>(sg + 2 * r + 2 * vb);
+        dk = reinterpret_cast<float*>(sg + 3 * r + 2 * vb);
+        dvv = reinterpret_cast<float*>(sg + 4 * r + 2 * vb);
+        if ((e = gma::widen_bf16(XQ, q32, nr, stream)) != hipSuccess || (e = gma::widen_bf16(XK, k32, nr, stream)) != hipSuccess ||
+            (e = gma::widen_bf16(V, v32, nv, stream)) != hipSuccess || (e = gma::widen_bf16(dO, d32, nv, stream)) != hipSuccess)
+            return launch_status(e);
+        q = q32, k = k32, v = v32, d = d32;
+    }
     if (op == GMA_OP_BACKWARD_CAUSAL)
-        return launch_status(gma::f32_backward_causal(p, q, k, v, mu, sigma2, pi, eps, d, dq, dk, dvv, dmu, dsigma2,
-                                                      dpi, ws, stream));
-    return launch_status(gma::f32_backward_bidir(p, q, k, v, mu, sigma2, pi, eps, d, dq, dk, dvv, dmu, dsigma2, dpi,
-                                                 ws, stream));
+        e = gma::f32_backward_causal(p, q, k, v, mu, sigma2, pi, eps, d, dq, dk, dvv, dmu, dsigma2, dpi, ws, stream);
+    else
+        e = gma::f32_backward_bidir(p, q, k, v, mu, sigma2, pi, eps, d, dq, dk, dvv, dmu, dsigma2, dpi, ws, stream);
+    if (e != hipSuccess || !staged) return launch_status(e);
+    if ((e = gma::narrow_to_bf16(dq, dXQ, nr, stream)) != hipSuccess || (e = gma::narrow_to_bf16(dk, dXK, nr, stream)) != hipSuccess)
+        return launch_status(e);
+    return launch_status(gma::narrow_to_bf16(dvv, dV, nv, stream));
 }
 
 gma_status_t gma_backward_bidir(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,

@@ -1096,7 +1096,7 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     float* partials = reinterpret_cast<float*>(ws + p.off_partials);
     float* memory = reinterpret_cast<float*>(ws + p.off_memory);
     const size_t E = size_t(p.K) * size_t(p.dv + 1);
-    char* extra = ws + p.total - f32_backward_extra_bytes(p);
+    char* extra = ws + p.off_stage - f32_backward_extra_bytes(p);
     float* dpart = reinterpret_cast<float*>(extra);
     float* dmem = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256));
     float* ppart = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256) + round_up(size_t(p.P) * E * 4, 256));
@@ -1407,7 +1407,7 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
     F32Params v = f32_params_view(p, ws);
     float* states = reinterpret_cast<float*>(ws + p.off_partials);  // segment aggregates, then running memories
     const size_t E = size_t(p.K) * size_t(p.dv + 1);
-    char* extra = ws + p.total - f32_backward_causal_extra_bytes(p);
+    char* extra = ws + p.off_stage - f32_backward_causal_extra_bytes(p);
     float* seg_part = reinterpret_cast<float*>(extra);
     float* rowda = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256));
     float* ppart = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256) +
@@ -1450,6 +1450,35 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
                K, p.seg, G, T, v.c, v.inv, mu, seg_part, eps, rowda, dXK, dV, static_cast<float*>(nullptr), ppart_key);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
+}
+
+// ---------------------------------------------------------------------------- bf16 staging
+namespace {
+__global__ void __launch_bounds__(kThreads) widen_bf16_kernel(const uint16_t* __restrict__ src,
+                                                              float* __restrict__ dst, size_t n) {
+    for (size_t i = size_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += size_t(gridDim.x) * kThreads)
+        dst[i] = bf16_bits_to_f32(src[i]);
+}
+__global__ void __launch_bounds__(kThreads) narrow_bf16_kernel(const float* __restrict__ src,
+                                                               uint16_t* __restrict__ dst, size_t n) {
+    for (size_t i = size_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += size_t(gridDim.x) * kThreads)
+        dst[i] = f32_to_bf16_bits(src[i]);
+}
+unsigned cast_blocks(size_t n) { return unsigned(std::min<size_t>((n + kThreads - 1) / kThreads, 8192)); }
+}  // namespace
+
+hipError_t widen_bf16(const void* src, float* dst, size_t n, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    GMA_LAUNCH("widen_bf16", widen_bf16_kernel, dim3(cast_blocks(n)), dim3(kThreads), 0, st,
+               static_cast<const uint16_t*>(src), dst, n);
+    return hipGetLastError();
+}
+
+hipError_t narrow_to_bf16(const float* src, void* dst, size_t n, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    GMA_LAUNCH("narrow_bf16", narrow_bf16_kernel, dim3(cast_blocks(n)), dim3(kThreads), 0, st, src,
+               static_cast<uint16_t*>(dst), n);
+    return hipGetLastError();
 }
 
 }  // namespace gma

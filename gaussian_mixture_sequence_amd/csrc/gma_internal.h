@@ -32,6 +32,7 @@ struct Plan {
     int32_t chunk;        // causal chunk length
     // byte offsets into the workspace
     size_t off_params, off_partials, off_memory, off_flags, total;
+    size_t off_stage;     // backward: end of the fp32 passes' regions; bf16 I/O is staged in fp32 after it
     size_t params_bytes, partials_bytes, memory_bytes, flags_bytes;
 };
 
@@ -89,6 +90,10 @@ size_t f32_backward_causal_extra_bytes(const Plan& p);
 hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
                                const float* s2, const float* pi, float eps, const float* dO, float* dXQ, float* dXK,
                                float* dV, float* dmu, float* ds2, float* dpi, char* ws, hipStream_t st);
+
+// bf16 <-> fp32 copies of n elements (the staging of the backward's bf16 I/O).
+hipError_t widen_bf16(const void* src, float* dst, size_t n, hipStream_t st);
+hipError_t narrow_to_bf16(const float* src, void* dst, size_t n, hipStream_t st);
 
 // ---- responsibility diagnostics (gma_diag.hip) ---------------------------------
 // Workspace: Gamma [B][H][N][K] fp32, then per-block partial sums, then the responsibilities

@@ -240,13 +240,16 @@ gma_status_t gma_responsibility_diagnostics(const void* X, gma_dtype_t x_dtype, 
  *   dpi[k] = sum_i ds_ik / pi_k      (pi as passed in; its parameterisation lies upstream),
  * the parameter sums running over both sides, every sequence and every position.  Also
  *   dV[j,:] = sum_k Gamma_K[j,k] dVt_k.
- *   XQ, XK, dXQ, dXK [B,H,N,d_r]; V, dO, dV [B,H,N,d_v]; mu, sigma2, dmu, dsigma2 [H,K,d_r];
- *   pi, dpi [H,K].  Every tensor fp32 (io_dtype must be GMA_F32; GMA_BF16 is
- *   GMA_ERR_UNSUPPORTED).  The gradient outputs are overwritten, not accumulated into.
- * Workspace: gma_workspace_size(GMA_OP_BACKWARD_BIDIR, shape, GMA_F32, 0, ...): the forward's
+ *   XQ, XK, dXQ, dXK [B,H,N,d_r]; V, dO, dV [B,H,N,d_v] in io_dtype (GMA_F32 or GMA_BF16);
+ *   mu, sigma2, dmu, dsigma2 [H,K,d_r] and pi, dpi [H,K] fp32.  The arithmetic is fp32 at either
+ *   I/O dtype; bf16 inputs are widened exactly and bf16 outputs rounded to nearest even.  The
+ *   gradient outputs are overwritten, not accumulated into.
+ * Workspace: gma_workspace_size(GMA_OP_BACKWARD_BIDIR, shape, io_dtype, 0, ...): the forward's
  * memory and its split partials, the same for (dVt, dZ), and per-split parameter partials,
- * reduced in a fixed order (bitwise reproducible).  Sizes, alignment and errors as for
- * gma_forward_bidir; with no rows (B N = 0) the parameter gradients are zeros.
+ * reduced in a fixed order (bitwise reproducible); with bf16 I/O also fp32 copies of the four
+ * inputs and three outputs (O(B H N (d_r + d_v)) bytes).  Sizes as for the fp32 forward (d_r, d_v
+ * <= 128, K <= 256 at either I/O dtype); alignment and errors as for gma_forward_bidir; with no
+ * rows (B N = 0) the parameter gradients are zeros.
  */
 gma_status_t gma_backward_bidir(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
                                 const float* mu, const float* sigma2, const float* pi, float eps,
@@ -264,8 +267,8 @@ gma_status_t gma_backward_bidir(const void* XQ, const void* XK, const void* V, g
  *   dVt_j = sum_{i>=j} Gamma_Q[i,:]^T dO_i / D_i,  dZ_j = -sum_{i>=j} Gamma_Q[i,:] a_i / D_i,
  *   dV[j,:] = sum_k Gamma_K[j,k] dVt_j[k,:],        g^K_jk = dVt_j[k,:] . V_j + dZ_j[k];
  * the softmax Jacobian, the routing-vector and the parameter gradients are those of
- * gma_backward_bidir.  Shapes, dtypes (fp32 only), outputs, workspace
- * (gma_workspace_size(GMA_OP_BACKWARD_CAUSAL, shape, GMA_F32, 0, ...), which also holds D_i and
+ * gma_backward_bidir.  Shapes, dtypes, outputs, workspace
+ * (gma_workspace_size(GMA_OP_BACKWARD_CAUSAL, shape, io_dtype, 0, ...), which also holds D_i and
  * a_i of every position) and errors as for gma_backward_bidir.
  */
 gma_status_t gma_backward_causal(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,

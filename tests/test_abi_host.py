@@ -239,7 +239,10 @@ def test_backward_argument_errors(lib, causal):
     Bw = gb.GMA_OP_BACKWARD_CAUSAL if causal else gb.GMA_OP_BACKWARD_BIDIR
     fn = lib.gma_backward_causal if causal else lib.gma_backward_bidir
     assert ws_size(Bw, 8, 8, 4096, 64, 64, 64, F)[0] == OK
-    assert ws_size(Bw, 8, 8, 4096, 64, 64, 64, BF)[0] == UNSUP   # fp32 only
+    # bf16 I/O: fp32 sizes (d 7 is fine), and fp32 copies of the I/O in the workspace
+    assert ws_size(Bw, 8, 8, 4096, 64, 64, 64, BF)[0] == OK
+    assert ws_size(Bw, 1, 1, 64, 7, 5, 13, BF)[0] == OK
+    assert ws_size(Bw, 8, 8, 4096, 64, 64, 64, BF)[1] >= ws_size(Bw, 8, 8, 4096, 64, 64, 64, F)[1] + 7 * 8 * 8 * 4096 * 64 * 4
     assert ws_size(Bw, 1, 1, 8, 16, 0, 8, F)[0] == UNSUP          # needs values
     assert ws_size(Bw, 1, 1, 8, 129, 32, 8, F)[0] == UNSUP
     assert ws_size(Bw, 1, -1, 8, 16, 32, 8, F)[0] == SHAPE
@@ -259,7 +262,6 @@ def test_backward_argument_errors(lib, causal):
     assert call(dmu=None) == NULLP
     assert call(pi=None) == NULLP
     assert call(ws=None) == NULLP
-    assert call(io=BF) == UNSUP
     assert call(io=9) == VALUE
     assert call(eps=0.0) == VALUE
     assert call(eps=float("nan")) == VALUE
