@@ -1179,12 +1179,64 @@ __global__ void __launch_bounds__(kThreads) f32_suffix_kernel(float* __restrict_
     }
 }
 
+// gamma_tile with fp32 tables in LDS: c [K], 1/sigma2 and mu as [K][LR] rows (LR = d_r + 1),
+// the direct-form score of Eq. 16 in fp32, then the softmax of Eq. 3b.  Same contract as gamma_tile.
+__device__ void gamma_tile_lds(const float* __restrict__ X, int64_t n0, int rows, int T, int dr, int K,
+                               const float* c_l, const float* inv_l, const float* mu_l, float* xs, float* g) {
+    const int LR = dr + 1;
+    for (int i = threadIdx.x; i < T * dr; i += kThreads) {
+        const int t = i / dr;
+        xs[i] = (t < rows) ? X[(n0 + t) * dr + (i - t * dr)] : 0.0f;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int t = wave; t < T; t += kThreads / kWave) {
+        float* gt = g + size_t(t) * K;
+        if (t >= rows) {
+            for (int k = lane; k < K; k += kWave) gt[k] = 0.0f;
+            continue;
+        }
+        const float* xt = xs + t * dr;
+        float sc[4], m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = lane + j * kWave;
+            sc[j] = -INFINITY;
+            if (k < K) {
+                const float *mk = mu_l + k * LR, *ik = inv_l + k * LR;
+                float q = 0.0f;
+                for (int d = 0; d < dr; ++d) {
+                    const float df = xt[d] - mk[d];
+                    q = fmaf(df * df, ik[d], q);
+                }
+                sc[j] = c_l[k] - 0.5f * q;
+                m = fmaxf(m, sc[j]);
+            }
+        }
+        m = wave_max(m);
+        float ev[4], sum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            ev[j] = (lane + j * kWave < K) ? expf(sc[j] - m) : 0.0f;
+            sum += ev[j];
+        }
+        sum = wave_sum(sum);
+        const float r = 1.0f / sum;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (lane + j * kWave < K) gt[lane + j * kWave] = ev[j] * r;
+    }
+    __syncthreads();
+}
+
 // Grid (G segments, P).  QUERY walks the segment's tiles forward from the memory before the
-// segment (state: [Vt (K dv) | Z (K)], advanced in place), writes dX_Q, D_i and a_i of every
-// row (rowda), the segment's total of what its queries send to the memory (seg_part) and its
-// moments.  KEY walks the tiles backward from what the later segments' queries sent (state,
-// advanced in place), writes dX_K, dV and its moments.
-template <bool QUERY>
+// segment (state: [Vt (K dv) | Z (K)]), writes dX_Q, D_i and a_i of every row (rowda), the
+// segment's total of what its queries send to the memory (seg_part) and its moments.  KEY walks
+// the tiles backward from what the later segments' queries sent (state), writes dX_K, dV and its
+// moments.  FAST: the per-head tables (fp32) and the running memory live in LDS (rows padded by
+// one element), the scores, dX and moments are fp32; otherwise they are read from the fp64 tables
+// and the running memory is advanced in place in the workspace.
+template <bool QUERY, bool FAST>
 __global__ void __launch_bounds__(kThreads)
     f32_bwdc_kernel(const float* __restrict__ XQ, const float* __restrict__ XK, const float* __restrict__ V,
                     const float* __restrict__ dO, int64_t N, int H, int dr, int dv, int K, int64_t seg, int G, int T,
@@ -1204,11 +1256,33 @@ __global__ void __launch_bounds__(kThreads)
     float* Am = Cm + T * T;   // T*T
     float* dd = Am + T * T;   // T: D_i
     float* aa = dd + T;       // T: a_i
+    const int LR = dr + 1, LV = dv + 1;
+    float* mT = aa + T;             // FAST: [K][LR] mu
+    float* iT = mT + K * LR;        // FAST: [K][LR] 1 / sigma2
+    float* cT = iT + K * LR;        // FAST: [K] score constants
+    float* Sm = cT + K;             // FAST: [K][LV] running memory (Vt or dVt)
+    float* Sz = Sm + K * LV;        // FAST: [K] its Z (or dZ)
     const double *ch = c + size_t(h) * K, *ih = inv + size_t(h) * K * dr;
     const float* mh = mu + size_t(h) * K * dr;
     const int E = K * (dv + 1), PE = 2 * K * dr + K;
-    float* St = state + (size_t(p) * G + gi) * E;  // [K][dv], then Z
-    float* Zs = St + size_t(K) * dv;
+    float* Sg = state + (size_t(p) * G + gi) * E;  // [K][dv], then Z
+    // the running memory: LDS rows of LV (FAST) or the workspace record
+    float* St = FAST ? Sm : Sg;
+    float* Zs = FAST ? Sz : Sg + size_t(K) * dv;
+    const int SL = FAST ? LV : dv;
+    if (FAST) {
+        for (int i = threadIdx.x; i < K * dr; i += kThreads) {
+            const int k = i / dr, d = i - k * dr;
+            mT[k * LR + d] = mh[i];
+            iT[k * LR + d] = float(ih[i]);
+        }
+        for (int k = threadIdx.x; k < K; k += kThreads) {
+            cT[k] = float(ch[k]);
+            Sz[k] = Sg[K * dv + k];
+        }
+        for (int i = threadIdx.x; i < K * dv; i += kThreads) Sm[(i / dv) * LV + i % dv] = Sg[i];
+        __syncthreads();
+    }
     float* sp = QUERY ? seg_part + (size_t(p) * G + gi) * E : nullptr;
     float* pp = param_part + (size_t(p) * G + gi) * PE;
     const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
@@ -1219,7 +1293,12 @@ __global__ void __launch_bounds__(kThreads)
         const int64_t n0 = lo + int64_t(QUERY ? it : ntiles - 1 - it) * T;
         const int rows = int(min<int64_t>(T, hi - n0));
         // responsibilities; the side's own rows are left in xs
-        if (QUERY) {
+        if (FAST) {
+            gamma_tile_lds(QUERY ? XK + p * N * dr : XQ + p * N * dr, n0, rows, T, dr, K, cT, iT, mT, xs,
+                           QUERY ? gk : gq);
+            gamma_tile_lds(QUERY ? XQ + p * N * dr : XK + p * N * dr, n0, rows, T, dr, K, cT, iT, mT, xs,
+                           QUERY ? gq : gk);
+        } else if (QUERY) {
             gamma_tile(XK + p * N * dr, n0, rows, T, dr, K, ch, ih, mh, xs, gk);
             gamma_tile(XQ + p * N * dr, n0, rows, T, dr, K, ch, ih, mh, xs, gq);
         } else {
@@ -1254,7 +1333,7 @@ __global__ void __launch_bounds__(kThreads)
                 float a = 0.0f;
                 for (int cc = lane; cc < dv; cc += kWave) {
                     float nn = 0.0f;
-                    for (int k = 0; k < K; ++k) nn = fmaf(gq[t * K + k], St[size_t(k) * dv + cc], nn);
+                    for (int k = 0; k < K; ++k) nn = fmaf(gq[t * K + k], St[size_t(k) * SL + cc], nn);
                     for (int j = 0; j <= t; ++j) nn = fmaf(Cm[t * T + j], vs[j * dv + cc], nn);
                     a = fmaf(ys[t * dv + cc], nn / d, a);
                 }
@@ -1284,7 +1363,7 @@ __global__ void __launch_bounds__(kThreads)
                 const int t = e / K, k = e - t * K;
                 float acc = 0.0f;
                 if (t < rows) {
-                    for (int cc = 0; cc < dv; ++cc) acc = fmaf(ys[t * dv + cc], St[size_t(k) * dv + cc], acc);
+                    for (int cc = 0; cc < dv; ++cc) acc = fmaf(ys[t * dv + cc], St[size_t(k) * SL + cc], acc);
                     acc = (acc - aa[t] * Zs[k]) / dd[t];
                     for (int j = 0; j <= t; ++j) acc = fmaf(Am[t * T + j], gk[j * K + k], acc);
                 }
@@ -1294,7 +1373,7 @@ __global__ void __launch_bounds__(kThreads)
             for (int e = threadIdx.x; e < rows * dv; e += kThreads) {
                 const int j = e / dv, cc = e - j * dv;
                 float acc = 0.0f;
-                for (int k = 0; k < K; ++k) acc = fmaf(gk[j * K + k], St[size_t(k) * dv + cc], acc);
+                for (int k = 0; k < K; ++k) acc = fmaf(gk[j * K + k], St[size_t(k) * SL + cc], acc);
                 for (int i = j; i < rows; ++i) acc = fmaf(Cm[i * T + j], ys[i * dv + cc] / dd[i], acc);
                 dV[(p * N + n0) * dv + e] = acc;
             }
@@ -1302,7 +1381,7 @@ __global__ void __launch_bounds__(kThreads)
                 const int j = e / K, k = e - j * K;
                 float acc = 0.0f;
                 if (j < rows) {
-                    for (int cc = 0; cc < dv; ++cc) acc = fmaf(vs[j * dv + cc], St[size_t(k) * dv + cc], acc);
+                    for (int cc = 0; cc < dv; ++cc) acc = fmaf(vs[j * dv + cc], St[size_t(k) * SL + cc], acc);
                     acc += Zs[k];
                     for (int i = j; i < rows; ++i) acc = fmaf(Am[i * T + j], gq[i * K + k], acc);
                 }
@@ -1323,22 +1402,39 @@ __global__ void __launch_bounds__(kThreads)
         for (int i = threadIdx.x; i < rows * dr; i += kThreads) {
             const int t = i / dr, d = i - t * dr;
             float acc = 0.0f;
-            for (int k = 0; k < K; ++k)
-                acc = fmaf(gg[t * K + k], float((double(xs[t * dr + d]) - double(mh[size_t(k) * dr + d])) * ih[size_t(k) * dr + d]), acc);
+            if (FAST) {
+                const float x = xs[t * dr + d];
+                for (int k = 0; k < K; ++k) acc = fmaf(gg[t * K + k] * iT[k * LR + d], x - mT[k * LR + d], acc);
+            } else {
+                for (int k = 0; k < K; ++k)
+                    acc = fmaf(gg[t * K + k], float((double(xs[t * dr + d]) - double(mh[size_t(k) * dr + d])) * ih[size_t(k) * dr + d]), acc);
+            }
             dX[(p * N + n0) * dr + i] = -acc;
         }
         // moments of these rows
         for (int e = threadIdx.x; e < K * dr; e += kThreads) {
             const int k = e / dr, d = e - k * dr;
-            const double m = double(mh[e]);
-            double a1 = 0.0, a2 = 0.0;
-            for (int t = 0; t < rows; ++t) {
-                const double df = double(xs[t * dr + d]) - m, w = double(gg[t * K + k]) * df;
-                a1 += w;
-                a2 += w * df;
+            float a1, a2;
+            if (FAST) {
+                const float m = mT[k * LR + d];
+                a1 = 0.0f, a2 = 0.0f;
+                for (int t = 0; t < rows; ++t) {
+                    const float df = xs[t * dr + d] - m, w = gg[t * K + k] * df;
+                    a1 += w;
+                    a2 = fmaf(w, df, a2);
+                }
+            } else {
+                const double m = double(mh[e]);
+                double b1 = 0.0, b2 = 0.0;
+                for (int t = 0; t < rows; ++t) {
+                    const double df = double(xs[t * dr + d]) - m, w = double(gg[t * K + k]) * df;
+                    b1 += w;
+                    b2 += w * df;
+                }
+                a1 = float(b1), a2 = float(b2);
             }
-            pp[e] = first ? float(a1) : pp[e] + float(a1);
-            pp[K * dr + e] = first ? float(a2) : pp[K * dr + e] + float(a2);
+            pp[e] = first ? a1 : pp[e] + a1;
+            pp[K * dr + e] = first ? a2 : pp[K * dr + e] + a2;
         }
         for (int k = threadIdx.x; k < K; k += kThreads) {
             float acc = 0.0f;
@@ -1363,11 +1459,13 @@ __global__ void __launch_bounds__(kThreads)
                     if (QUERY) ksum += gk[t * K + k];
                 }
             }
+            // element e of the [Vt | Z] record in the running memory's layout
+            float& m = e < K * dv ? St[(e / dv) * SL + e % dv] : Zs[e - K * dv];
             if (QUERY) {
-                St[e] += ksum;
+                m += ksum;
                 sp[e] = first ? qsum : sp[e] + qsum;
             } else {
-                St[e] += qsum;
+                m += qsum;
             }
         }
         first = false;
@@ -1394,7 +1492,8 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
     if (p.H == 0) return hipSuccess;
     if (p.P == 0 || p.N == 0) return reduce_params(p, nullptr, 0, nullptr, pi, dmu, ds2, dpi, st);  // zero gradients
     static const hipError_t attr = [] {
-        const void* fns[] = {(const void*)f32_bwdc_kernel<true>, (const void*)f32_bwdc_kernel<false>};
+        const void* fns[] = {(const void*)f32_bwdc_kernel<true, false>, (const void*)f32_bwdc_kernel<false, false>,
+                             (const void*)f32_bwdc_kernel<true, true>, (const void*)f32_bwdc_kernel<false, true>};
         for (const void* f : fns) {
             hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
             if (r != hipSuccess) return r;
@@ -1434,20 +1533,35 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
     GMA_LAUNCH("f32_bwdc_prefix", f32_prefix_kernel, egrid, dim3(kThreads), 0, st, states, G, Ei,
                static_cast<const float*>(nullptr), K, dv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // 64-position tiles when two workgroups fit a CU, else the largest tile that lets two fit
-    // (down to 32), else the largest that fits at all
+    // FAST (tables and running memory in LDS) with 64- or 32-position tiles when two workgroups
+    // still fit a CU; otherwise the general form: 64-position tiles when two fit, else the largest
+    // tile that lets two fit (down to 32), else the largest that fits at all
+    const size_t fast_extra = size_t(2 * K * (dr + 1) + 2 * K + K * (dv + 1)) * sizeof(float);
     int T = kTile;
-    while (T > 32 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds / 2) T /= 2;
-    while (T > 8 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
-    const size_t lds = bwdc_lds_bytes(T, dr, dv, K);
-    GMA_LAUNCH("f32_bwdc_query", f32_bwdc_kernel<true>, grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N, H, dr,
-               dv, K, p.seg, G, T, v.c, v.inv, mu, states, eps, rowda, dXQ, static_cast<float*>(nullptr), seg_part,
-               ppart);
+    bool fast = false;
+    for (int t = kTile; t >= 32 && !fast; t /= 2)
+        if (bwdc_lds_bytes(t, dr, dv, K) + fast_extra <= kMaxLds / 2) fast = true, T = t;
+    if (!fast) {
+        while (T > 32 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds / 2) T /= 2;
+        while (T > 8 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
+    }
+    const size_t lds = bwdc_lds_bytes(T, dr, dv, K) + (fast ? fast_extra : 0);
+    float* none = nullptr;
+    if (fast)
+        GMA_LAUNCH("f32_bwdc_query", (f32_bwdc_kernel<true, true>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N,
+                   H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, states, eps, rowda, dXQ, none, seg_part, ppart);
+    else
+        GMA_LAUNCH("f32_bwdc_query", (f32_bwdc_kernel<true, false>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N,
+                   H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, states, eps, rowda, dXQ, none, seg_part, ppart);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     GMA_LAUNCH("f32_bwdc_suffix", f32_suffix_kernel, egrid, dim3(kThreads), 0, st, seg_part, G, Ei);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    GMA_LAUNCH("f32_bwdc_key", f32_bwdc_kernel<false>, grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N, H, dr, dv,
-               K, p.seg, G, T, v.c, v.inv, mu, seg_part, eps, rowda, dXK, dV, static_cast<float*>(nullptr), ppart_key);
+    if (fast)
+        GMA_LAUNCH("f32_bwdc_key", (f32_bwdc_kernel<false, true>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N, H,
+                   dr, dv, K, p.seg, G, T, v.c, v.inv, mu, seg_part, eps, rowda, dXK, dV, none, ppart_key);
+    else
+        GMA_LAUNCH("f32_bwdc_key", (f32_bwdc_kernel<false, false>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N,
+                   H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, seg_part, eps, rowda, dXK, dV, none, ppart_key);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
 }
