@@ -601,21 +601,26 @@ __global__ void __launch_bounds__(kThreads)
 // so row reductions are 16-lane shuffles.
 constexpr int kBT = 64;        // rows per tile
 constexpr int kLDT = kBT + 4;  // row stride of the transposed ([L][T]) tiles
-enum { BWD_WRITE = 0, BWD_QUERY = 1, BWD_KEY = 2 };
+// BWD_CQUERY / BWD_CKEY: the causal passes (the memory a tile sees is the running prefix or
+// suffix, plus the masked in-tile products)
+enum { BWD_WRITE = 0, BWD_QUERY = 1, BWD_KEY = 2, BWD_CQUERY = 3, BWD_CKEY = 4 };
 
 bool bwd_tiled_applies(const Plan& p) {
     return p.K % 4 == 0 && p.dr % 4 == 0 && p.dv % 4 == 0 && p.K <= 64 && p.dr <= 64 && p.dv <= 64;
 }
 
 size_t bwd_tiled_lds_bytes(int mode, int K, int dr, int dv) {
-    const bool qk = mode != BWD_WRITE;
+    const bool qk = mode != BWD_WRITE, causal = mode >= BWD_CQUERY;
+    const bool qside = mode == BWD_QUERY || mode == BWD_CQUERY, kside = mode == BWD_KEY || mode == BWD_CKEY;
     size_t f = size_t(2 * dr * (K + 4) + K);                 // mu^T, (1/sigma2)^T, c
     if (qk) f += size_t(2 * K * dv + K);                     // memory (or its gradient), transposed, and Z
     if (qk) f += size_t(dr * kLDT) + size_t(K * kLDT) + size_t(kBT * K);  // X^T, gamma^T (then ds^T), gamma (then ds)
     else f += size_t(max(dr * kLDT, kBT * K));               // X^T, then gamma in the same space
-    if (mode != BWD_KEY) f += size_t(kBT * dv);              // V (write) or dO / D (query)
+    if (!kside) f += size_t(kBT * dv);                       // V (write) or dO / D (query)
     if (qk) f += size_t(dv * kLDT);                          // (dO / D)^T (query) or V^T (key)
-    if (mode == BWD_QUERY) f += 2 * kBT;                     // D, a'
+    if (qside || causal) f += 2 * kBT;                       // D, a'
+    if (causal)  // the other side's gamma in both layouts, V (query) or dO / D (key) rows, C and A
+        f += size_t(kBT * (K + 4) + K * kLDT + kBT * (dv + 4) + kBT * kLDT * (qside ? 1 : 2));
     return f * sizeof(float);
 }
 
@@ -635,19 +640,83 @@ __device__ __forceinline__ float max16(float v) {
     return v;
 }
 
+// Responsibilities of the tile in xT (rows t = r0 + i, columns k = m0 + j of thread (tr, mc)):
+// the direct-form score of Eq. 16 from the LDS tables, then the softmax of Eq. 3b over the 16
+// lanes of the row group.  Rows at or beyond `rows` get zeros.
+__device__ __forceinline__ void tile_gamma(const float* xT, const float* muT, const float* ivT, const float* cK,
+                                           int K, int dr, int LDK, int r0, int m0, int rows, float (&gam)[4][4]) {
+    float q[4][4] = {};
+    if (m0 < K) {
+#pragma unroll 4
+        for (int d = 0; d < dr; ++d) {
+            float xa[4], ma[4], ia[4];
+            unpack(lds4(xT + d * kLDT + r0), xa);
+            unpack(lds4(muT + d * LDK + m0), ma);
+            unpack(lds4(ivT + d * LDK + m0), ia);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float df = xa[i] - ma[j];
+                    q[i][j] = fmaf(df * df, ia[j], q[i][j]);
+                }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float sc[4], m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            sc[j] = m0 < K ? cK[m0 + j] - 0.5f * q[i][j] : -INFINITY;
+            m = fmaxf(m, sc[j]);
+        }
+        m = max16(m);
+        float e[4], sum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            e[j] = m0 < K ? expf(sc[j] - m) : 0.0f;
+            sum += e[j];
+        }
+        sum = sum16(sum);
+        const float r = r0 + i < rows ? 1.0f / sum : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) gam[i][j] = e[j] * r;
+    }
+}
+
+// Load rows [n0, n0 + rows) of X [.][dr] into xT [dr][kLDT] (zeros beyond `rows`).
+__device__ __forceinline__ void load_xT(const float* Xp, int64_t n0, int rows, int dr, float* xT) {
+    for (int i = threadIdx.x; i < kBT * (dr / 4); i += kThreads) {
+        const int t = i / (dr / 4), d = (i - t * (dr / 4)) * 4;
+        const float4 v = t < rows ? *reinterpret_cast<const float4*>(Xp + (n0 + t) * dr + d) : make_float4(0, 0, 0, 0);
+        xT[(d + 0) * kLDT + t] = v.x;
+        xT[(d + 1) * kLDT + t] = v.y;
+        xT[(d + 2) * kLDT + t] = v.z;
+        xT[(d + 3) * kLDT + t] = v.w;
+    }
+}
+
 // Grid (G, P), one split of one problem per workgroup.
 //   WRITE: X = X_K, Y = V; mem_part gets the split's [Vt | Z] (the forward's memory, Eq. 5-6).
 //   QUERY: X = X_Q, Y = dO, mem = [Vt | Z]; writes dX_Q, mem_part gets the split's [dVt | dZ].
 //   KEY:   X = X_K, Y = V, mem = [dVt | dZ]; writes dX_K and dY = dV.
 // QUERY and KEY write the split's moment record to param_part.
+//   CQUERY, CKEY: the causal passes over segment g of problem p.  X2 holds the other side's routing
+//   vectors (CQUERY: X_K, CKEY: X_Q) and Y2 the other side's rows (CQUERY: V, CKEY: dO); mem is the
+//   per-segment record [P][G][K (dv + 1)] of the memory before the segment (CQUERY) or of what the
+//   later segments' queries send (CKEY), advanced in LDS tile by tile.  CQUERY writes D_i and a_i
+//   of its rows to rowda and the segment's total of what its queries send to mem_part; CKEY reads
+//   rowda.
 template <int MODE>
 __global__ void __launch_bounds__(kThreads)
     f32_bwd_tiled_kernel(const float* __restrict__ X, const float* __restrict__ Y, int64_t N, int H, int dr, int dv,
                          int K, int64_t seg, int G, const double* __restrict__ c, const double* __restrict__ inv,
                          const float* __restrict__ mu, const float* __restrict__ mem, float eps,
                          float* __restrict__ dX, float* __restrict__ dY, float* __restrict__ mem_part,
-                         float* __restrict__ param_part) {
-    constexpr bool QK = MODE != BWD_WRITE;
+                         float* __restrict__ param_part, const float* __restrict__ X2 = nullptr,
+                         const float* __restrict__ Y2 = nullptr, float* __restrict__ rowda = nullptr) {
+    constexpr bool QK = MODE != BWD_WRITE, CAUSAL = MODE >= BWD_CQUERY;
+    constexpr bool QS = MODE == BWD_QUERY || MODE == BWD_CQUERY, KS = MODE == BWD_KEY || MODE == BWD_CKEY;
     extern __shared__ float lds[];
     const int64_t p = blockIdx.y;
     const int gi = blockIdx.x, h = int(p % H);
@@ -663,9 +732,15 @@ __global__ void __launch_bounds__(kThreads)
     float* gT = xT + dr * kLDT;                    // [K][kLDT] gamma^T, then ds^T
     float* g = QK ? gT + K * kLDT : xT;            // [kBT][K]  gamma, then ds (write: in the space of X^T)
     float* Yr = QK ? g + kBT * K : xT + max(dr * kLDT, kBT * K);  // [kBT][dv] V (write) or dO / D (query)
-    float* YT = Yr + (MODE != BWD_KEY ? kBT * dv : 0);  // [dv][kLDT]
+    float* YT = Yr + (!KS ? kBT * dv : 0);         // [dv][kLDT]
     float* Dv = YT + (QK ? dv * kLDT : 0);         // [kBT]
     float* Av = Dv + kBT;                          // [kBT]
+    const int LG = K + 4, LV4 = dv + 4;
+    float* Go = Av + kBT;                          // causal: [kBT][LG] the other side's gamma
+    float* GoT = Go + kBT * LG;                    // causal: [K][kLDT] the same, transposed
+    float* Rw = GoT + K * kLDT;                    // causal: [kBT][LV4] V (query) or dO / D (key) rows
+    float* Cm = Rw + kBT * LV4;                    // causal: query: C^T, then A^T; key: C ([i][j], stride kLDT)
+    float* Am = Cm + kBT * kLDT;                   // causal key: A ([i][j], stride kLDT)
 
     {   // per-head tables and (query, key) the problem's memory
         const double *ch = c + size_t(h) * K, *ih = inv + size_t(h) * K * dr;
@@ -677,7 +752,7 @@ __global__ void __launch_bounds__(kThreads)
         }
         for (int k = tid; k < K; k += kThreads) cK[k] = float(ch[k]);
         if (QK) {
-            const float* src = mem + size_t(p) * K * (dv + 1);
+            const float* src = mem + (CAUSAL ? size_t(p) * G + gi : size_t(p)) * K * (dv + 1);
             for (int i = tid; i < K * dv; i += kThreads) {
                 const int k = i / dv, cc = i - k * dv;
                 const float v = src[i];
@@ -700,21 +775,46 @@ __global__ void __launch_bounds__(kThreads)
     const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
     const float* Xp = X + size_t(p) * N * dr;
     const float* Yp = Y + size_t(p) * N * dv;
-    for (int64_t n0 = lo; n0 < hi; n0 += kBT) {
+    const int ntiles = int((hi - lo + kBT - 1) / kBT);
+    for (int it = 0; it < ntiles; ++it) {
+        const int64_t n0 = lo + int64_t(MODE == BWD_CKEY ? ntiles - 1 - it : it) * kBT;  // the key pass runs backward
         const int rows = int(min<int64_t>(kBT, hi - n0));
         __syncthreads();  // the previous tile's reads are done
-        for (int i = tid; i < kBT * (dr / 4); i += kThreads) {
-            const int t = i / (dr / 4), d = (i - t * (dr / 4)) * 4;
-            const float4 v = t < rows ? *reinterpret_cast<const float4*>(Xp + (n0 + t) * dr + d) : make_float4(0, 0, 0, 0);
-            xT[(d + 0) * kLDT + t] = v.x;
-            xT[(d + 1) * kLDT + t] = v.y;
-            xT[(d + 2) * kLDT + t] = v.z;
-            xT[(d + 3) * kLDT + t] = v.w;
+        if (CAUSAL) {  // the other side's responsibilities, in both layouts
+            load_xT(X2 + size_t(p) * N * dr, n0, rows, dr, xT);
+            __syncthreads();
+            float go[4][4];
+            tile_gamma(xT, muT, ivT, cK, K, dr, LDK, r0, m0, rows, go);
+            if (m0 < K) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) put4(Go + (r0 + i) * LG + m0, go[i][0], go[i][1], go[i][2], go[i][3]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) put4(GoT + (m0 + j) * kLDT + r0, go[0][j], go[1][j], go[2][j], go[3][j]);
+            }
+            // V rows (query) or dO / D rows with D, a' (key)
+            const float* Y2p = Y2 + size_t(p) * N * dv;
+            for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
+                const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
+                float4 v = t < rows ? *reinterpret_cast<const float4*>(Y2p + (n0 + t) * dv + cc) : make_float4(0, 0, 0, 0);
+                if (MODE == BWD_CKEY && t < rows) {
+                    const float rD = 1.0f / rowda[(size_t(p) * N + n0 + t) * 2];
+                    v.x *= rD, v.y *= rD, v.z *= rD, v.w *= rD;
+                }
+                *reinterpret_cast<float4*>(Rw + t * LV4 + cc) = v;
+            }
+            if (MODE == BWD_CKEY)
+                for (int t = tid; t < kBT; t += kThreads) {
+                    const float D = t < rows ? rowda[(size_t(p) * N + n0 + t) * 2] : 1.0f;
+                    Dv[t] = D;
+                    Av[t] = t < rows ? rowda[(size_t(p) * N + n0 + t) * 2 + 1] / D : 0.0f;
+                }
+            __syncthreads();  // xT is free again
         }
+        load_xT(Xp, n0, rows, dr, xT);
         for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
             const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
             const float4 v = t < rows ? *reinterpret_cast<const float4*>(Yp + (n0 + t) * dv + cc) : make_float4(0, 0, 0, 0);
-            if (MODE == BWD_KEY) {
+            if (KS) {
                 YT[(cc + 0) * kLDT + t] = v.x;
                 YT[(cc + 1) * kLDT + t] = v.y;
                 YT[(cc + 2) * kLDT + t] = v.z;
@@ -727,48 +827,10 @@ __global__ void __launch_bounds__(kThreads)
 
         // responsibilities (rows t, columns k): direct-form score of Eq. 16, softmax of Eq. 3b
         float gam[4][4];
-        {
-            float q[4][4] = {};
-            if (m0 < K) {
-#pragma unroll 4
-                for (int d = 0; d < dr; ++d) {
-                    float xa[4], ma[4], ia[4];
-                    unpack(lds4(xT + d * kLDT + r0), xa);
-                    unpack(lds4(muT + d * LDK + m0), ma);
-                    unpack(lds4(ivT + d * LDK + m0), ia);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const float df = xa[i] - ma[j];
-                            q[i][j] = fmaf(df * df, ia[j], q[i][j]);
-                        }
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float sc[4], m = -INFINITY;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    sc[j] = m0 < K ? cK[m0 + j] - 0.5f * q[i][j] : -INFINITY;
-                    m = fmaxf(m, sc[j]);
-                }
-                m = max16(m);
-                float e[4], sum = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    e[j] = m0 < K ? expf(sc[j] - m) : 0.0f;
-                    sum += e[j];
-                }
-                sum = sum16(sum);
-                const float r = r0 + i < rows ? 1.0f / sum : 0.0f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) gam[i][j] = e[j] * r;
-            }
-        }
+        tile_gamma(xT, muT, ivT, cK, K, dr, LDK, r0, m0, rows, gam);
         if (MODE == BWD_WRITE) __syncthreads();  // gamma overwrites X^T
         if (m0 < K) {
-            if (MODE != BWD_KEY)
+            if (!KS)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) put4(g + (r0 + i) * K + m0, gam[i][0], gam[i][1], gam[i][2], gam[i][3]);
             if (QK)
@@ -794,8 +856,64 @@ __global__ void __launch_bounds__(kThreads)
             continue;
         }
 
+        // causal: C_ij = gamma^Q_i . gamma^K_j for key j <= query i (rows i = r0.., columns j = m0..);
+        // the query pass keeps C^T and its row sums, the key pass C and A_ij = dO'_i . V_j - a'_i
+        float cs[4] = {};
+        if (CAUSAL) {
+            const float* gqT = QS ? gT : GoT;  // [K][kLDT] gamma^Q transposed
+            const float* gkT = QS ? GoT : gT;  // [K][kLDT] gamma^K transposed
+            float ca[4][4] = {}, aa[4][4] = {};
+            const bool live = m0 <= r0 + 3 && r0 < rows;  // the block has entries with j <= i
+            if (live) {
+#pragma unroll 4
+                for (int k = 0; k < K; ++k) {
+                    float qa[4], ka[4];
+                    unpack(lds4(gqT + k * kLDT + r0), qa);
+                    unpack(lds4(gkT + k * kLDT + m0), ka);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) ca[i][j] = fmaf(qa[i], ka[j], ca[i][j]);
+                }
+                if (MODE == BWD_CKEY) {
+#pragma unroll 4
+                    for (int cc = 0; cc < dv; ++cc) {
+                        float va[4], oa[4];
+                        unpack(lds4(YT + cc * kLDT + m0), va);  // V^T
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) oa[i] = Rw[(r0 + i) * LV4 + cc];  // dO'
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) aa[i][j] = fmaf(oa[i], va[j], aa[i][j]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bool in = live && m0 + j <= r0 + i && r0 + i < rows;
+                    ca[i][j] = in ? ca[i][j] : 0.0f;
+                    aa[i][j] = in ? aa[i][j] - Av[r0 + i] : 0.0f;
+                    cs[i] += ca[i][j];
+                }
+            if (QS) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) put4(Cm + (m0 + j) * kLDT + r0, ca[0][j], ca[1][j], ca[2][j], ca[3][j]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    put4(Cm + (r0 + i) * kLDT + m0, ca[i][0], ca[i][1], ca[i][2], ca[i][3]);
+                    put4(Am + (r0 + i) * kLDT + m0, aa[i][0], aa[i][1], aa[i][2], aa[i][3]);
+                }
+            }
+            __syncthreads();
+        }
+        const int tmax = min(r0 + 4, rows);  // causal: in-tile keys j <= the block's last query row
+
         float gg[4][4] = {};  // upstream gradient at the responsibilities (rows t, columns k)
-        if (MODE == BWD_QUERY) {
+        if (QS) {
             // N = gamma Vt (rows t, columns c); D = gamma Z + eps; dO . N
             float nv[4][4] = {};
             if (m0 < dv)
@@ -809,10 +927,20 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
                         for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ga[i], va[j], nv[i][j]);
                 }
+            if (CAUSAL && m0 < dv)  // + sum_{j <= t} C_tj V_j
+                for (int j = 0; j < tmax; ++j) {
+                    float ca[4], va[4];
+                    unpack(lds4(Cm + j * kLDT + r0), ca);
+                    unpack(lds4(Rw + j * LV4 + m0), va);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) nv[i][jj] = fmaf(ca[i], va[jj], nv[i][jj]);
+                }
             float Dt[4], An[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float dp = 0.0f, ap = 0.0f;
+                float dp = cs[i], ap = 0.0f;
                 if (m0 < K)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) dp = fmaf(gam[i][j], Zm[m0 + j], dp);
@@ -845,8 +973,36 @@ __global__ void __launch_bounds__(kThreads)
                 for (int i = 0; i < 4; ++i) {
                     Dv[r0 + i] = Dt[i];
                     Av[r0 + i] = An[i] / (Dt[i] * Dt[i]);
+                    if (CAUSAL && r0 + i < rows) {
+                        rowda[(size_t(p) * N + n0 + r0 + i) * 2 + 0] = Dt[i];
+                        rowda[(size_t(p) * N + n0 + r0 + i) * 2 + 1] = An[i] / Dt[i];
+                    }
                 }
             __syncthreads();
+            // causal: A^T (A_tj = dO'_t . V_j - a'_t for j <= t) over C^T, whose reads are done
+            if (CAUSAL) {
+                float aa[4][4] = {};
+                const bool live = m0 <= r0 + 3 && r0 < rows;
+                if (live)
+#pragma unroll 4
+                    for (int cc = 0; cc < dv; ++cc) {
+                        float oa[4], va[4];
+                        unpack(lds4(YT + cc * kLDT + r0), oa);  // dO'^T
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) va[j] = Rw[(m0 + j) * LV4 + cc];  // V
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) aa[i][j] = fmaf(oa[i], va[j], aa[i][j]);
+                    }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        aa[i][j] = live && m0 + j <= r0 + i && r0 + i < rows ? aa[i][j] - Av[r0 + i] : 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) put4(Cm + (m0 + j) * kLDT + r0, aa[0][j], aa[1][j], aa[2][j], aa[3][j]);
+            }
             // dVt += gamma^T dO', dZ -= gamma^T a' (rows k, columns c)
             if (r0 < K && m0 < dv)
 #pragma unroll 4
@@ -879,6 +1035,19 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(-Av[r0 + i], Zm[m0 + j], gg[i][j]);
             }
+            if (CAUSAL) {  // + sum_{j <= t} A_tj gamma^K_j
+                __syncthreads();
+                if (m0 < K)
+                    for (int j = 0; j < tmax; ++j) {
+                        float ta[4], ka[4];
+                        unpack(lds4(Cm + j * kLDT + r0), ta);
+                        unpack(lds4(Go + j * LG + m0), ka);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj) gg[i][jj] = fmaf(ta[i], ka[jj], gg[i][jj]);
+                    }
+            }
         } else {
             // dV = gamma dVt (rows t, columns c)
             if (m0 < dv) {
@@ -893,6 +1062,16 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
                         for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ga[i], va[j], nv[i][j]);
                 }
+                if (CAUSAL)  // + sum_{i >= j} C_ij dO'_i (rows j = r0.., queries i >= r0)
+                    for (int i2 = r0; i2 < rows; ++i2) {
+                        float ca[4], oa[4];
+                        unpack(lds4(Cm + i2 * kLDT + r0), ca);
+                        unpack(lds4(Rw + i2 * LV4 + m0), oa);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ca[i], oa[j], nv[i][j]);
+                    }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (r0 + i < rows)
@@ -915,6 +1094,16 @@ __global__ void __launch_bounds__(kThreads)
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) gg[i][j] += Zm[m0 + j];
+                if (CAUSAL)  // + sum_{i >= j} A_ij gamma^Q_i
+                    for (int i2 = r0; i2 < rows; ++i2) {
+                        float ta[4], qa[4];
+                        unpack(lds4(Am + i2 * kLDT + r0), ta);
+                        unpack(lds4(Go + i2 * LG + m0), qa);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(ta[i], qa[j], gg[i][j]);
+                    }
             }
         }
         // Eq. 18: ds = gamma (g - gamma . g)
@@ -980,9 +1169,37 @@ __global__ void __launch_bounds__(kThreads)
                         s2[i][j] = fmaf(w, df, s2[i][j]);
                     }
             }
+        if (CAUSAL && r0 < K && m0 < dv) {
+            // advance the memory past the tile (its last reads were before the ds barriers):
+            // query: + gamma^K^T [V | 1] (Eq. 6b); key: + gamma^Q^T [dO' | -a']
+            float ua[4][4] = {}, uz[4] = {};
+            for (int t = 0; t < rows; ++t) {
+                float ga[4], ya[4];
+                unpack(lds4(Go + t * LG + r0), ga);
+                unpack(lds4(Rw + t * LV4 + m0), ya);
+                const float zt = QS ? 1.0f : -Av[t];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uz[i] = fmaf(ga[i], zt, uz[i]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) ua[i][j] = fmaf(ga[i], ya[j], ua[i][j]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float mm[4];
+                unpack(lds4(M + (r0 + i) * dv + m0), mm);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) mm[j] += ua[i][j];
+                put4(M + (r0 + i) * dv + m0, mm[0], mm[1], mm[2], mm[3]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) MT[(m0 + j) * K + r0 + i] = mm[j];
+                if (mc == 0) Zm[r0 + i] += uz[i];
+            }
+        }
     }
     // the split's records (zeros for a split without rows)
-    if (MODE != BWD_KEY && r0 < K && m0 < dv) {
+    if (!KS && r0 < K && m0 < dv) {
         float* mp = mem_part + (size_t(p) * G + gi) * size_t(K) * (dv + 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -1066,7 +1283,8 @@ hipError_t bwd_allow_lds() {
     static const hipError_t e = [] {
         const void* fns[] = {(const void*)f32_bwd_side_kernel<true>, (const void*)f32_bwd_side_kernel<false>,
                              (const void*)f32_bwd_tiled_kernel<BWD_WRITE>, (const void*)f32_bwd_tiled_kernel<BWD_QUERY>,
-                             (const void*)f32_bwd_tiled_kernel<BWD_KEY>};
+                             (const void*)f32_bwd_tiled_kernel<BWD_KEY>, (const void*)f32_bwd_tiled_kernel<BWD_CQUERY>,
+                             (const void*)f32_bwd_tiled_kernel<BWD_CKEY>};
         for (const void* f : fns) {
             hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
             if (r != hipSuccess) return r;
@@ -1109,7 +1327,8 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
         GMA_LAUNCH("f32_bwd_write", f32_bwd_tiled_kernel<BWD_WRITE>, grid, dim3(kThreads),
                    bwd_tiled_lds_bytes(BWD_WRITE, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
                    static_cast<const float*>(nullptr), eps, static_cast<float*>(nullptr),
-                   static_cast<float*>(nullptr), partials, static_cast<float*>(nullptr));
+                   static_cast<float*>(nullptr), partials, static_cast<float*>(nullptr),
+                   static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), static_cast<float*>(nullptr));
     } else {
         const size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
         GMA_LAUNCH("f32_bwd_write", f32_write_kernel, grid, dim3(kThreads), lds_w, st, XK, V, p.N, H, dr, dv, K,
@@ -1121,7 +1340,8 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     if (bwd_tiled_applies(p)) {
         GMA_LAUNCH("f32_bwd_query", f32_bwd_tiled_kernel<BWD_QUERY>, grid, dim3(kThreads),
                    bwd_tiled_lds_bytes(BWD_QUERY, K, dr, dv), st, XQ, dO, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
-                   static_cast<const float*>(memory), eps, dXQ, static_cast<float*>(nullptr), dpart, ppart);
+                   static_cast<const float*>(memory), eps, dXQ, static_cast<float*>(nullptr), dpart, ppart,
+                   static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), static_cast<float*>(nullptr));
     } else {
         int T = kTile;
         while (T > 8 && bwd_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
@@ -1135,7 +1355,8 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     if (bwd_tiled_applies(p)) {
         GMA_LAUNCH("f32_bwd_key", f32_bwd_tiled_kernel<BWD_KEY>, grid, dim3(kThreads),
                    bwd_tiled_lds_bytes(BWD_KEY, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
-                   static_cast<const float*>(dmem), eps, dXK, dV, static_cast<float*>(nullptr), ppart_key);
+                   static_cast<const float*>(dmem), eps, dXK, dV, static_cast<float*>(nullptr), ppart_key,
+                   static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), static_cast<float*>(nullptr));
     } else {
         int T = kTile;
         while (T > 8 && bwd_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
@@ -1522,7 +1743,8 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
             GMA_LAUNCH("f32_bwdc_aggregate", f32_bwd_tiled_kernel<BWD_WRITE>, grid, dim3(kThreads),
                        bwd_tiled_lds_bytes(BWD_WRITE, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv,
                        mu, static_cast<const float*>(nullptr), eps, static_cast<float*>(nullptr),
-                       static_cast<float*>(nullptr), states, static_cast<float*>(nullptr));
+                       static_cast<float*>(nullptr), states, static_cast<float*>(nullptr),
+                   static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), static_cast<float*>(nullptr));
         } else {
             const size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
             GMA_LAUNCH("f32_bwdc_aggregate", f32_write_kernel, grid, dim3(kThreads), lds_w, st, XK, V, p.N, H, dr, dv,
@@ -1547,6 +1769,24 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
     }
     const size_t lds = bwdc_lds_bytes(T, dr, dv, K) + (fast ? fast_extra : 0);
     float* none = nullptr;
+    const float* cnone = nullptr;
+    const bool tiled = bwd_tiled_applies(p) && bwd_tiled_lds_bytes(BWD_CQUERY, K, dr, dv) <= kMaxLds &&
+                       bwd_tiled_lds_bytes(BWD_CKEY, K, dr, dv) <= kMaxLds;
+    if (tiled) {  // register-tiled passes with the running memory in LDS
+        if ((e = bwd_allow_lds()) != hipSuccess) return e;
+        GMA_LAUNCH("f32_bwdc_query", f32_bwd_tiled_kernel<BWD_CQUERY>, grid, dim3(kThreads),
+                   bwd_tiled_lds_bytes(BWD_CQUERY, K, dr, dv), st, XQ, dO, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
+                   static_cast<const float*>(states), eps, dXQ, none, seg_part, ppart, XK, V, rowda);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        GMA_LAUNCH("f32_bwdc_suffix", f32_suffix_kernel, egrid, dim3(kThreads), 0, st, seg_part, G, Ei);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        GMA_LAUNCH("f32_bwdc_key", f32_bwd_tiled_kernel<BWD_CKEY>, grid, dim3(kThreads),
+                   bwd_tiled_lds_bytes(BWD_CKEY, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
+                   static_cast<const float*>(seg_part), eps, dXK, dV, none, ppart_key, XQ, dO, rowda);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
+    }
+    (void)cnone;
     if (fast)
         GMA_LAUNCH("f32_bwdc_query", (f32_bwdc_kernel<true, true>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N,
                    H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, states, eps, rowda, dXQ, none, seg_part, ppart);

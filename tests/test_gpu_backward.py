@@ -124,7 +124,7 @@ TOL_BWD_BF16 = 5e-3
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("dims", [(1000, 7, 5, 13), (3000, 64, 64, 64), (500, 128, 128, 256)],
+@pytest.mark.parametrize("dims", [(1000, 7, 5, 13), (3000, 64, 64, 64), (500, 128, 128, 256), (1500, 64, 64, 32)],
                          ids=lambda d: "N%d-dr%d-dv%d-K%d" % d)
 def test_backward_bf16_parity(causal, dims):
     N, dr, dv, K = dims
@@ -183,6 +183,10 @@ CAUSAL_CASES = [
     case(3000, 103, d_r=32, d_v=64, K=64),              # several tiles per segment, ragged tail
     case(300, 104, B=1, H=1, d_r=128, d_v=128, K=256),  # maximum dims (half-height tiles)
     case(700, 105, B=3, H=2, d_r=64, d_v=32, K=128, mu_std=1.5),
+    # the register-tiled causal passes (K, d_r, d_v <= 64, multiples of 4, within LDS)
+    case(1000, 108, B=2, H=2, d_r=32, d_v=32, K=32),
+    case(333, 109, B=2, H=1, d_r=64, d_v=64, K=32),     # ragged tail, one tile per segment
+    case(4100, 110, B=4, H=16, d_r=64, d_v=48, K=20),   # several tiles per segment, K below a row group
 ]
 
 
