@@ -17,119 +17,10 @@
 //            the segment aggregates, i.e. each segment's starting memory (Eq. 6b)
 //   read     bidirectional: O = Gamma_Q Vt / (Gamma_Q Z + eps) (Eq. 7-8)
 //   scan     causal: chunked scan of Eq. 6b/8b inside each segment
-#include <cmath>
-#include <cstdint>
-
-#include "gma_device.h"
-#include "gma_internal.h"
+#include "gma_f32_common.h"
 
 namespace gma {
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int kTile = 64;  // tokens per tile
-constexpr size_t kMaxLds = 160 * 1024;
-
-struct F32Params {
-    const double* c;    // [H][K]
-    const double* inv;  // [H][K][dr]   1 / sigma2
-};
-
-F32Params f32_params_view(const Plan& p, char* ws) {
-    F32Params v;
-    v.c = reinterpret_cast<const double*>(ws + p.off_params);
-    v.inv = reinterpret_cast<const double*>(ws + p.off_params + round_up(size_t(p.H * p.K) * 8, 256));
-    return v;
-}
-
-// One block per head.  c_k = log pi_k - 1/2 sum_d log sigma2_kd in fp64, then shifted by
-// its maximum over k (a k-independent shift, exact in the softmax) so the fp32 value is small.
-// Each wave takes one component at a time, its lanes over d.
-__global__ void __launch_bounds__(kThreads) f32_params_kernel(const float* __restrict__ s2,
-                                                              const float* __restrict__ pi, int K,
-                                                              int dr, double* __restrict__ c_out,
-                                                              double* __restrict__ inv_out) {
-    const int h = blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    __shared__ double cd[256];
-    __shared__ double red[kThreads / kWave];
-    const float* s2h = s2 + size_t(h) * K * dr;
-    for (int k = wave; k < K; k += kThreads / kWave) {
-        double acc = 0.0;
-        for (int d = lane; d < dr; d += kWave) {
-            const double v = double(s2h[size_t(k) * dr + d]);
-            acc += log(v);
-            inv_out[(size_t(h) * K + k) * dr + d] = 1.0 / v;
-        }
-        for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-        if (lane == 0) cd[k] = log(double(pi[size_t(h) * K + k])) - 0.5 * acc;
-    }
-    __syncthreads();
-    double local_max = -INFINITY;
-    for (int k = threadIdx.x; k < K; k += kThreads) local_max = fmax(local_max, cd[k]);
-    // block max
-    for (int o = 32; o >= 1; o >>= 1) local_max = fmax(local_max, __shfl_xor(local_max, o, kWave));
-    if (lane == 0) red[wave] = local_max;
-    __syncthreads();
-    double m = red[0];
-    for (int w = 1; w < kThreads / kWave; ++w) m = fmax(m, red[w]);
-    for (int k = threadIdx.x; k < K; k += kThreads) c_out[size_t(h) * K + k] = cd[k] - m;
-}
-
-// Responsibilities of rows [n0, n0 + rows) of one problem into LDS g[T][K]; xs is LDS
-// scratch of T*dr floats.  Rows at or beyond `rows` are zero in g.  One wave owns a
-// row at a time: each lane evaluates up to K/64 <= 4 scores in fp64 registers, the
-// row maximum is subtracted in fp64, and only then is the softmax (Eq. 3b) taken in fp32.
-__device__ void gamma_tile(const float* __restrict__ X, int64_t n0, int rows, int T, int dr, int K,
-                           const double* __restrict__ c_h, const double* __restrict__ inv_h,
-                           const float* __restrict__ mu_h, float* xs, float* g) {
-    for (int i = threadIdx.x; i < T * dr; i += kThreads) {
-        int t = i / dr;
-        xs[i] = (t < rows) ? X[(n0 + t) * dr + (i - t * dr)] : 0.0f;
-    }
-    __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int t = wave; t < T; t += kThreads / kWave) {
-        float* gt = g + size_t(t) * K;
-        if (t >= rows) {
-            for (int k = lane; k < K; k += kWave) gt[k] = 0.0f;
-            continue;
-        }
-        const float* xt = xs + t * dr;
-        double sc[4];
-        double m = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int k = lane + j * kWave;
-            sc[j] = -INFINITY;
-            if (k < K) {
-                const float* mk = mu_h + size_t(k) * dr;
-                const double* ik = inv_h + size_t(k) * dr;
-                double q = 0.0;
-                for (int d = 0; d < dr; ++d) {
-                    double diff = double(xt[d]) - double(mk[d]);
-                    q = fma(diff * diff, ik[d], q);
-                }
-                sc[j] = c_h[k] - 0.5 * q;
-                m = fmax(m, sc[j]);
-            }
-        }
-        for (int o = 32; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, kWave));
-        float ev[4];
-        float sum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            ev[j] = (lane + j * kWave < K) ? expf(float(sc[j] - m)) : 0.0f;
-            sum += ev[j];
-        }
-        sum = wave_sum(sum);
-        const float r = 1.0f / sum;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (lane + j * kWave < K) gt[lane + j * kWave] = ev[j] * r;
-    }
-    __syncthreads();
-}
 
 __global__ void __launch_bounds__(kThreads) f32_resp_kernel(const float* __restrict__ X, int64_t N,
                                                             int H, int dr, int K, const double* c,
@@ -150,83 +41,6 @@ __global__ void __launch_bounds__(kThreads) f32_resp_kernel(const float* __restr
             static_cast<uint16_t*>(Gamma)[base + i] = f32_to_bf16_bits(g[i]);
         else
             static_cast<float*>(Gamma)[base + i] = g[i];
-    }
-}
-
-// Partial latent memory of one split: mem[k*dv + c] = sum_t gammaK_tk V_tc and
-// mem[K*dv + k] = sum_t gammaK_tk over tokens [g*seg, min((g+1)*seg, N)).
-__global__ void __launch_bounds__(kThreads) f32_write_kernel(const float* __restrict__ XK,
-                                                             const float* __restrict__ V, int64_t N,
-                                                             int H, int dr, int dv, int K, int64_t seg,
-                                                             int G, const double* c, const double* inv,
-                                                             const float* mu, float* partials) {
-    extern __shared__ float lds[];
-    const int64_t p = blockIdx.y;
-    const int g_idx = blockIdx.x;
-    const int h = int(p % H);
-    float* xs = lds;
-    float* g = xs + kTile * dr;
-    float* vs = g + kTile * K;
-    float* mem = partials + (size_t(p) * G + g_idx) * size_t(K) * (dv + 1);
-    const int64_t lo = int64_t(g_idx) * seg, hi = min<int64_t>(lo + seg, N);
-    const int E = K * (dv + 1);
-    bool first = true;
-    for (int64_t n0 = lo; n0 < hi; n0 += kTile) {
-        const int rows = int(min<int64_t>(kTile, hi - n0));
-        gamma_tile(XK + p * N * dr, n0, rows, kTile, dr, K, c + size_t(h) * K,
-                   inv + size_t(h) * K * dr, mu + size_t(h) * K * dr, xs, g);
-        for (int i = threadIdx.x; i < rows * dv; i += kThreads) vs[i] = V[(p * N + n0) * dv + i];
-        __syncthreads();
-        for (int e = threadIdx.x; e < E; e += kThreads) {
-            float acc = 0.0f;
-            if (e < K * dv) {
-                int k = e / dv, cc = e - k * dv;
-                for (int t = 0; t < rows; ++t) acc = fmaf(g[t * K + k], vs[t * dv + cc], acc);
-            } else {
-                int k = e - K * dv;
-                for (int t = 0; t < rows; ++t) acc += g[t * K + k];
-            }
-            mem[e] = first ? acc : mem[e] + acc;
-        }
-        first = false;
-        __syncthreads();
-    }
-    if (first)  // empty split (cannot happen with the host plan, kept for safety)
-        for (int e = threadIdx.x; e < E; e += kThreads) mem[e] = 0.0f;
-}
-
-// Bidirectional: out[p][e] = sum_g partials[p][g][e] in increasing g.
-__global__ void __launch_bounds__(kThreads) f32_combine_kernel(const float* __restrict__ partials,
-                                                               int G, int E, float* __restrict__ out) {
-    const int64_t p = blockIdx.y;
-    const int e = blockIdx.x * kThreads + threadIdx.x;
-    if (e >= E) return;
-    const float* src = partials + size_t(p) * G * E + e;
-    float acc = 0.0f;
-    for (int g = 0; g < G; ++g) acc += src[size_t(g) * E];
-    out[size_t(p) * E + e] = acc;
-}
-
-// Index of partial-layout element e (Vt [K][dv] then Z [K]) in the carried-memory layout
-// [K][dv + 1] (row k: Vt_k then Z_k).
-__device__ __forceinline__ int state_index(int e, int K, int dv) {
-    return e < K * dv ? (e / dv) * (dv + 1) + e % dv : (e - K * dv) * (dv + 1) + dv;
-}
-
-// Causal: exclusive prefix over segments in place; segment g then holds the memory
-// accumulated over all positions before it, starting from the carried memory state_in
-// ([P][K][dv+1], or zero when NULL).
-__global__ void __launch_bounds__(kThreads) f32_prefix_kernel(float* __restrict__ partials, int G, int E,
-                                                              const float* __restrict__ state_in, int K, int dv) {
-    const int64_t p = blockIdx.y;
-    const int e = blockIdx.x * kThreads + threadIdx.x;
-    if (e >= E) return;
-    float* src = partials + size_t(p) * G * E + e;
-    float run = state_in ? state_in[size_t(p) * E + state_index(e, K, dv)] : 0.0f;
-    for (int g = 0; g < G; ++g) {
-        float a = src[size_t(g) * E];
-        src[size_t(g) * E] = run;
-        run += a;
     }
 }
 
@@ -363,10 +177,7 @@ hipError_t allow_lds() {
 hipError_t launch_params(const Plan& p, const float* s2, const float* pi, char* ws, hipStream_t st) {
     hipError_t e0 = allow_lds();
     if (e0 != hipSuccess) return e0;
-    F32Params v = f32_params_view(p, ws);
-    GMA_LAUNCH("f32_params", f32_params_kernel, dim3(unsigned(p.H)), dim3(kThreads), 0, st, s2, pi, int(p.K),
-                       int(p.dr), const_cast<double*>(v.c), const_cast<double*>(v.inv));
-    return hipGetLastError();
+    return launch_param_tables(p, s2, pi, ws, st);
 }
 
 }  // namespace
@@ -441,1397 +252,6 @@ hipError_t f32_causal(const Plan& p, const float* XQ, const float* XK, const flo
                        scan_lds_bytes(C, int(p.dr), int(p.dv), int(p.K)), st, XQ, XK, V, p.N, int(p.H),
                        int(p.dr), int(p.dv), int(p.K), p.seg, int(p.G), C, v.c, v.inv, mu, partials, eps, O,
                        state_out);
-    return hipGetLastError();
-}
-
-// ============================================================================ backward
-// Gradients of <dO, O> for the bidirectional forward (Sec. 4.1 of "Gaussian Mixture
-// Attention": the softmax Jacobian of Eq. 17, the centred score gradient of Eq. 18 and the
-// chain rule of Eq. 19-20 through the direct-form score of Eq. 16), fp32.  With
-// D_i = gamma^Q_i . Z + eps, dO'_i = dO_i / D_i and a'_i = dO_i . O_i / D_i:
-//   g^Q_ik = dO'_i . Vt_k - a'_i Z_k,            dVt_k = sum_i gamma^Q_ik dO'_i,
-//   dZ_k = -sum_i gamma^Q_ik a'_i,                dV_j = sum_k gamma^K_jk dVt_k,
-//   g^K_jk = dVt_k . V_j + dZ_k,                  ds_ik = gamma_ik (g_ik - sum_l gamma_il g_il),
-//   dx_id = -sum_k ds_ik (x_id - mu_kd) / sigma2_kd.
-// The mixture parameters see every row of both sides through three moments per split,
-//   S0_k = sum_i ds_ik,  S1_kd = sum_i ds_ik (x_id - mu_kd),  S2_kd = sum_i ds_ik (x_id - mu_kd)^2,
-// kept in the direct (centred) form, from which dmu_kd = S1_kd / sigma2_kd,
-// dsigma2_kd = (S2_kd / sigma2_kd^2 - S0_k / sigma2_kd) / 2 and dpi_k = S0_k / pi_k.
-// Partial records per (problem, split): [S1 (K d_r) | S2 (K d_r) | S0 (K)].
-namespace {
-
-// ---- general sizes: one thread per output element, LDS tiles of T rows
-size_t bwd_lds_bytes(int T, int dr, int dv, int K) { return size_t(T) * (dr + 2 * K + dv + 2) * sizeof(float); }
-
-// Grid (G, P): rows [g seg, (g + 1) seg) of problem p in tiles of T.  QUERY: the query side
-// (reads the memory mem = [Vt | Z], writes dX_Q and the partial [dVt | dZ] of its rows);
-// otherwise the key side (reads dmem = [dVt | dZ], writes dV and dX_K).  Both write the
-// block's moment record pp (first tile writes, later tiles add: each entry has one owner).
-template <bool QUERY>
-__global__ void __launch_bounds__(kThreads)
-    f32_bwd_side_kernel(const float* __restrict__ X, const float* __restrict__ Y, int64_t N, int H, int dr, int dv,
-                        int K, int64_t seg, int G, int T, const double* c, const double* inv, const float* mu,
-                        const float* __restrict__ mem, float eps, float* __restrict__ dX, float* __restrict__ dY,
-                        float* __restrict__ mem_part, float* __restrict__ param_part) {
-    extern __shared__ float lds[];
-    const int64_t p = blockIdx.y;
-    const int gi = blockIdx.x, h = int(p % H);
-    float* xs = lds;          // T*dr: the tile's routing vectors (left by gamma_tile)
-    float* gm = xs + T * dr;  // T*K: responsibilities
-    float* gg = gm + T * K;   // T*K: upstream gradient, then the score gradient
-    float* ys = gg + T * K;   // T*dv: dO (query side) or V (key side)
-    float* dd = ys + T * dv;  // T: D_i
-    float* aa = dd + T;       // T: a_i
-    const double *ch = c + size_t(h) * K, *ih = inv + size_t(h) * K * dr;
-    const float* mh = mu + size_t(h) * K * dr;
-    const float* Vt = mem + size_t(p) * K * (dv + 1);  // [K][dv], then Z (or dVt, dZ)
-    const float* Z = Vt + size_t(K) * dv;
-    const int E = K * (dv + 1), PE = 2 * K * dr + K;
-    float* mp = mem_part ? mem_part + (size_t(p) * G + gi) * E : nullptr;
-    float* pp = param_part + (size_t(p) * G + gi) * PE;
-    const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    bool first = true;
-    for (int64_t n0 = lo; n0 < hi; n0 += T) {
-        const int rows = int(min<int64_t>(T, hi - n0));
-        gamma_tile(X + p * N * dr, n0, rows, T, dr, K, ch, ih, mh, xs, gm);
-        for (int i = threadIdx.x; i < T * dv; i += kThreads) {
-            const int t = i / dv;
-            ys[i] = t < rows ? Y[(p * N + n0) * dv + i] : 0.0f;
-        }
-        __syncthreads();
-        if (QUERY) {  // D_t and a_t = dO_t . O_t, one wave per row
-            for (int t = wave; t < rows; t += kThreads / kWave) {
-                float d = 0.0f;
-                for (int k = lane; k < K; k += kWave) d = fmaf(gm[t * K + k], Z[k], d);
-                d = wave_sum(d) + eps;
-                float a = 0.0f;
-                for (int cc = lane; cc < dv; cc += kWave) {
-                    float nn = 0.0f;
-                    for (int k = 0; k < K; ++k) nn = fmaf(gm[t * K + k], Vt[size_t(k) * dv + cc], nn);
-                    a = fmaf(ys[t * dv + cc], nn / d, a);
-                }
-                a = wave_sum(a);
-                if (lane == 0) {
-                    dd[t] = d;
-                    aa[t] = a;
-                }
-            }
-            __syncthreads();
-        } else {  // dV_tc = sum_k gamma^K_tk dVt_kc
-            for (int i = threadIdx.x; i < rows * dv; i += kThreads) {
-                const int t = i / dv, cc = i - t * dv;
-                float acc = 0.0f;
-                for (int k = 0; k < K; ++k) acc = fmaf(gm[t * K + k], Vt[size_t(k) * dv + cc], acc);
-                dY[(p * N + n0) * dv + i] = acc;
-            }
-        }
-        // upstream gradient at the responsibilities
-        for (int i = threadIdx.x; i < T * K; i += kThreads) {
-            const int t = i / K, k = i - t * K;
-            float acc = 0.0f;
-            if (t < rows) {
-                for (int cc = 0; cc < dv; ++cc) acc = fmaf(ys[t * dv + cc], Vt[size_t(k) * dv + cc], acc);
-                acc = QUERY ? (acc - aa[t] * Z[k]) / dd[t] : acc + Z[k];
-            }
-            gg[i] = acc;
-        }
-        __syncthreads();
-        // Eq. 18: ds = gamma (g - gamma . g), one wave per row
-        for (int t = wave; t < T; t += kThreads / kWave) {
-            float w = 0.0f;
-            for (int k = lane; k < K; k += kWave) w = fmaf(gm[t * K + k], gg[t * K + k], w);
-            w = wave_sum(w);
-            for (int k = lane; k < K; k += kWave) gg[t * K + k] = gm[t * K + k] * (gg[t * K + k] - w);
-        }
-        __syncthreads();
-        // routing-vector gradient
-        for (int i = threadIdx.x; i < rows * dr; i += kThreads) {
-            const int t = i / dr, d = i - t * dr;
-            float acc = 0.0f;
-            for (int k = 0; k < K; ++k)
-                acc = fmaf(gg[t * K + k], float((double(xs[t * dr + d]) - double(mh[size_t(k) * dr + d])) * ih[size_t(k) * dr + d]), acc);
-            dX[(p * N + n0) * dr + i] = -acc;
-        }
-        // moments of these rows
-        for (int e = threadIdx.x; e < K * dr; e += kThreads) {
-            const int k = e / dr, d = e - k * dr;
-            const double m = double(mh[e]);
-            double a1 = 0.0, a2 = 0.0;
-            for (int t = 0; t < rows; ++t) {
-                const double df = double(xs[t * dr + d]) - m, w = double(gg[t * K + k]) * df;
-                a1 += w;
-                a2 += w * df;
-            }
-            pp[e] = first ? float(a1) : pp[e] + float(a1);
-            pp[K * dr + e] = first ? float(a2) : pp[K * dr + e] + float(a2);
-        }
-        for (int k = threadIdx.x; k < K; k += kThreads) {
-            float acc = 0.0f;
-            for (int t = 0; t < rows; ++t) acc += gg[t * K + k];
-            pp[2 * K * dr + k] = first ? acc : pp[2 * K * dr + k] + acc;
-        }
-        if (QUERY) {  // partial [dVt | dZ] of these rows, in the memory's layout
-            for (int e = threadIdx.x; e < E; e += kThreads) {
-                float acc = 0.0f;
-                if (e < K * dv) {
-                    const int k = e / dv, cc = e - k * dv;
-                    for (int t = 0; t < rows; ++t) acc = fmaf(gm[t * K + k], ys[t * dv + cc] / dd[t], acc);
-                } else {
-                    const int k = e - K * dv;
-                    for (int t = 0; t < rows; ++t) acc -= gm[t * K + k] * aa[t] / dd[t];
-                }
-                mp[e] = first ? acc : mp[e] + acc;
-            }
-        }
-        first = false;
-        __syncthreads();  // the tile's LDS is free
-    }
-    if (first) {  // empty block
-        for (int e = threadIdx.x; e < PE; e += kThreads) pp[e] = 0.0f;
-        if (QUERY)
-            for (int e = threadIdx.x; e < E; e += kThreads) mp[e] = 0.0f;
-    }
-}
-
-// ---- register-tiled passes for K, d_r, d_v <= 64 (multiples of 4)
-// 256 threads as 16 row groups x 16 column groups: thread (tr, mc) owns rows r0 = 4 tr .. r0 + 3
-// and columns m0 = 4 mc .. m0 + 3 of every 64 x 64 product of a tile; operands are read from
-// LDS as 16-byte vectors.  The 16 threads of a row group are 16 adjacent lanes of one wave,
-// so row reductions are 16-lane shuffles.
-constexpr int kBT = 64;        // rows per tile
-constexpr int kLDT = kBT + 4;  // row stride of the transposed ([L][T]) tiles
-// BWD_CQUERY / BWD_CKEY: the causal passes (the memory a tile sees is the running prefix or
-// suffix, plus the masked in-tile products)
-enum { BWD_WRITE = 0, BWD_QUERY = 1, BWD_KEY = 2, BWD_CQUERY = 3, BWD_CKEY = 4 };
-
-bool bwd_tiled_applies(const Plan& p) {
-    return p.K % 4 == 0 && p.dr % 4 == 0 && p.dv % 4 == 0 && p.K <= 64 && p.dr <= 64 && p.dv <= 64;
-}
-
-size_t bwd_tiled_lds_bytes(int mode, int K, int dr, int dv) {
-    const bool qk = mode != BWD_WRITE, causal = mode >= BWD_CQUERY;
-    const bool qside = mode == BWD_QUERY || mode == BWD_CQUERY, kside = mode == BWD_KEY || mode == BWD_CKEY;
-    size_t f = size_t(2 * dr * (K + 4) + K);                 // mu^T, (1/sigma2)^T, c
-    if (qk) f += size_t(2 * K * dv + K);                     // memory (or its gradient), transposed, and Z
-    if (qk) f += size_t(dr * kLDT) + size_t(K * kLDT) + size_t(kBT * K);  // X^T, gamma^T (then ds^T), gamma (then ds)
-    else f += size_t(max(dr * kLDT, kBT * K));               // X^T, then gamma in the same space
-    if (!kside) f += size_t(kBT * dv);                       // V (write) or dO / D (query)
-    if (qk) f += size_t(dv * kLDT);                          // (dO / D)^T (query) or V^T (key)
-    if (qside || causal) f += 2 * kBT;                       // D, a'
-    if (causal)  // the other side's gamma in both layouts, V (query) or dO / D (key) rows, C and A
-        f += size_t(kBT * (K + 4) + K * kLDT + kBT * (dv + 4) + kBT * kLDT * (qside ? 1 : 2));
-    return f * sizeof(float);
-}
-
-__device__ __forceinline__ float4 lds4(const float* q) { return *reinterpret_cast<const float4*>(q); }
-__device__ __forceinline__ void put4(float* q, float a, float b, float c, float d) {
-    *reinterpret_cast<float4*>(q) = make_float4(a, b, c, d);
-}
-__device__ __forceinline__ void unpack(const float4 v, float (&a)[4]) {
-    a[0] = v.x, a[1] = v.y, a[2] = v.z, a[3] = v.w;
-}
-__device__ __forceinline__ float sum16(float v) {
-    for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 16);
-    return v;
-}
-__device__ __forceinline__ float max16(float v) {
-    for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 16));
-    return v;
-}
-
-// Responsibilities of the tile in xT (rows t = r0 + i, columns k = m0 + j of thread (tr, mc)):
-// the direct-form score of Eq. 16 from the LDS tables, then the softmax of Eq. 3b over the 16
-// lanes of the row group.  Rows at or beyond `rows` get zeros.
-__device__ __forceinline__ void tile_gamma(const float* xT, const float* muT, const float* ivT, const float* cK,
-                                           int K, int dr, int LDK, int r0, int m0, int rows, float (&gam)[4][4]) {
-    float q[4][4] = {};
-    if (m0 < K) {
-#pragma unroll 4
-        for (int d = 0; d < dr; ++d) {
-            float xa[4], ma[4], ia[4];
-            unpack(lds4(xT + d * kLDT + r0), xa);
-            unpack(lds4(muT + d * LDK + m0), ma);
-            unpack(lds4(ivT + d * LDK + m0), ia);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float df = xa[i] - ma[j];
-                    q[i][j] = fmaf(df * df, ia[j], q[i][j]);
-                }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float sc[4], m = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            sc[j] = m0 < K ? cK[m0 + j] - 0.5f * q[i][j] : -INFINITY;
-            m = fmaxf(m, sc[j]);
-        }
-        m = max16(m);
-        float e[4], sum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            e[j] = m0 < K ? expf(sc[j] - m) : 0.0f;
-            sum += e[j];
-        }
-        sum = sum16(sum);
-        const float r = r0 + i < rows ? 1.0f / sum : 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) gam[i][j] = e[j] * r;
-    }
-}
-
-// Load rows [n0, n0 + rows) of X [.][dr] into xT [dr][kLDT] (zeros beyond `rows`).
-__device__ __forceinline__ void load_xT(const float* Xp, int64_t n0, int rows, int dr, float* xT) {
-    for (int i = threadIdx.x; i < kBT * (dr / 4); i += kThreads) {
-        const int t = i / (dr / 4), d = (i - t * (dr / 4)) * 4;
-        const float4 v = t < rows ? *reinterpret_cast<const float4*>(Xp + (n0 + t) * dr + d) : make_float4(0, 0, 0, 0);
-        xT[(d + 0) * kLDT + t] = v.x;
-        xT[(d + 1) * kLDT + t] = v.y;
-        xT[(d + 2) * kLDT + t] = v.z;
-        xT[(d + 3) * kLDT + t] = v.w;
-    }
-}
-
-// Grid (G, P), one split of one problem per workgroup.
-//   WRITE: X = X_K, Y = V; mem_part gets the split's [Vt | Z] (the forward's memory, Eq. 5-6).
-//   QUERY: X = X_Q, Y = dO, mem = [Vt | Z]; writes dX_Q, mem_part gets the split's [dVt | dZ].
-//   KEY:   X = X_K, Y = V, mem = [dVt | dZ]; writes dX_K and dY = dV.
-// QUERY and KEY write the split's moment record to param_part.
-//   CQUERY, CKEY: the causal passes over segment g of problem p.  X2 holds the other side's routing
-//   vectors (CQUERY: X_K, CKEY: X_Q) and Y2 the other side's rows (CQUERY: V, CKEY: dO); mem is the
-//   per-segment record [P][G][K (dv + 1)] of the memory before the segment (CQUERY) or of what the
-//   later segments' queries send (CKEY), advanced in LDS tile by tile.  CQUERY writes D_i and a_i
-//   of its rows to rowda and the segment's total of what its queries send to mem_part; CKEY reads
-//   rowda.
-template <int MODE>
-__global__ void __launch_bounds__(kThreads)
-    f32_bwd_tiled_kernel(const float* __restrict__ X, const float* __restrict__ Y, int64_t N, int H, int dr, int dv,
-                         int K, int64_t seg, int G, const double* __restrict__ c, const double* __restrict__ inv,
-                         const float* __restrict__ mu, const float* __restrict__ mem, float eps,
-                         float* __restrict__ dX, float* __restrict__ dY, float* __restrict__ mem_part,
-                         float* __restrict__ param_part, const float* __restrict__ X2 = nullptr,
-                         const float* __restrict__ Y2 = nullptr, float* __restrict__ rowda = nullptr) {
-    constexpr bool QK = MODE != BWD_WRITE, CAUSAL = MODE >= BWD_CQUERY;
-    constexpr bool QS = MODE == BWD_QUERY || MODE == BWD_CQUERY, KS = MODE == BWD_KEY || MODE == BWD_CKEY;
-    extern __shared__ float lds[];
-    const int64_t p = blockIdx.y;
-    const int gi = blockIdx.x, h = int(p % H);
-    const int tid = threadIdx.x, tr = tid >> 4, mc = tid & 15, r0 = tr * 4, m0 = mc * 4;
-    const int LDK = K + 4;
-    float* muT = lds;                              // [dr][LDK]
-    float* ivT = muT + dr * LDK;                   // [dr][LDK]
-    float* cK = ivT + dr * LDK;                    // [K]
-    float* M = cK + K;                             // [K][dv]   Vt (query) or dVt (key)
-    float* MT = M + (QK ? K * dv : 0);             // [dv][K]
-    float* Zm = MT + (QK ? dv * K : 0);            // [K]       Z or dZ
-    float* xT = Zm + (QK ? K : 0);                 // [dr][kLDT]
-    float* gT = xT + dr * kLDT;                    // [K][kLDT] gamma^T, then ds^T
-    float* g = QK ? gT + K * kLDT : xT;            // [kBT][K]  gamma, then ds (write: in the space of X^T)
-    float* Yr = QK ? g + kBT * K : xT + max(dr * kLDT, kBT * K);  // [kBT][dv] V (write) or dO / D (query)
-    float* YT = Yr + (!KS ? kBT * dv : 0);         // [dv][kLDT]
-    float* Dv = YT + (QK ? dv * kLDT : 0);         // [kBT]
-    float* Av = Dv + kBT;                          // [kBT]
-    const int LG = K + 4, LV4 = dv + 4;
-    float* Go = Av + kBT;                          // causal: [kBT][LG] the other side's gamma
-    float* GoT = Go + kBT * LG;                    // causal: [K][kLDT] the same, transposed
-    float* Rw = GoT + K * kLDT;                    // causal: [kBT][LV4] V (query) or dO / D (key) rows
-    float* Cm = Rw + kBT * LV4;                    // causal: query: C^T, then A^T; key: C ([i][j], stride kLDT)
-    float* Am = Cm + kBT * kLDT;                   // causal key: A ([i][j], stride kLDT)
-
-    {   // per-head tables and (query, key) the problem's memory
-        const double *ch = c + size_t(h) * K, *ih = inv + size_t(h) * K * dr;
-        const float* mh = mu + size_t(h) * K * dr;
-        for (int i = tid; i < K * dr; i += kThreads) {
-            const int k = i / dr, d = i - k * dr;
-            muT[d * LDK + k] = mh[i];
-            ivT[d * LDK + k] = float(ih[i]);
-        }
-        for (int k = tid; k < K; k += kThreads) cK[k] = float(ch[k]);
-        if (QK) {
-            const float* src = mem + (CAUSAL ? size_t(p) * G + gi : size_t(p)) * K * (dv + 1);
-            for (int i = tid; i < K * dv; i += kThreads) {
-                const int k = i / dv, cc = i - k * dv;
-                const float v = src[i];
-                M[i] = v;
-                MT[cc * K + k] = v;
-            }
-            for (int k = tid; k < K; k += kThreads) Zm[k] = src[K * dv + k];
-        }
-    }
-    __syncthreads();
-    // moment accumulators (rows d = r0 + i, columns k = m0 + j) and their mu
-    float mreg[4][4], s1[4][4] = {}, s2[4][4] = {}, s0[4] = {};
-    // memory-like accumulators (rows k = r0 + i, columns c = m0 + j): Vt, Z (write) or dVt, dZ (query)
-    float mv[4][4] = {}, mz[4] = {};
-    const bool mom = QK && r0 < dr && m0 < K;
-    if (mom)
-        for (int i = 0; i < 4; ++i)
-            for (int j = 0; j < 4; ++j) mreg[i][j] = muT[(r0 + i) * LDK + m0 + j];
-
-    const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
-    const float* Xp = X + size_t(p) * N * dr;
-    const float* Yp = Y + size_t(p) * N * dv;
-    const int ntiles = int((hi - lo + kBT - 1) / kBT);
-    for (int it = 0; it < ntiles; ++it) {
-        const int64_t n0 = lo + int64_t(MODE == BWD_CKEY ? ntiles - 1 - it : it) * kBT;  // the key pass runs backward
-        const int rows = int(min<int64_t>(kBT, hi - n0));
-        __syncthreads();  // the previous tile's reads are done
-        if (CAUSAL) {  // the other side's responsibilities, in both layouts
-            load_xT(X2 + size_t(p) * N * dr, n0, rows, dr, xT);
-            __syncthreads();
-            float go[4][4];
-            tile_gamma(xT, muT, ivT, cK, K, dr, LDK, r0, m0, rows, go);
-            if (m0 < K) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) put4(Go + (r0 + i) * LG + m0, go[i][0], go[i][1], go[i][2], go[i][3]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) put4(GoT + (m0 + j) * kLDT + r0, go[0][j], go[1][j], go[2][j], go[3][j]);
-            }
-            // V rows (query) or dO / D rows with D, a' (key)
-            const float* Y2p = Y2 + size_t(p) * N * dv;
-            for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
-                const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
-                float4 v = t < rows ? *reinterpret_cast<const float4*>(Y2p + (n0 + t) * dv + cc) : make_float4(0, 0, 0, 0);
-                if (MODE == BWD_CKEY && t < rows) {
-                    const float rD = 1.0f / rowda[(size_t(p) * N + n0 + t) * 2];
-                    v.x *= rD, v.y *= rD, v.z *= rD, v.w *= rD;
-                }
-                *reinterpret_cast<float4*>(Rw + t * LV4 + cc) = v;
-            }
-            if (MODE == BWD_CKEY)
-                for (int t = tid; t < kBT; t += kThreads) {
-                    const float D = t < rows ? rowda[(size_t(p) * N + n0 + t) * 2] : 1.0f;
-                    Dv[t] = D;
-                    Av[t] = t < rows ? rowda[(size_t(p) * N + n0 + t) * 2 + 1] / D : 0.0f;
-                }
-            __syncthreads();  // xT is free again
-        }
-        load_xT(Xp, n0, rows, dr, xT);
-        for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
-            const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
-            const float4 v = t < rows ? *reinterpret_cast<const float4*>(Yp + (n0 + t) * dv + cc) : make_float4(0, 0, 0, 0);
-            if (KS) {
-                YT[(cc + 0) * kLDT + t] = v.x;
-                YT[(cc + 1) * kLDT + t] = v.y;
-                YT[(cc + 2) * kLDT + t] = v.z;
-                YT[(cc + 3) * kLDT + t] = v.w;
-            } else {
-                *reinterpret_cast<float4*>(Yr + t * dv + cc) = v;
-            }
-        }
-        __syncthreads();
-
-        // responsibilities (rows t, columns k): direct-form score of Eq. 16, softmax of Eq. 3b
-        float gam[4][4];
-        tile_gamma(xT, muT, ivT, cK, K, dr, LDK, r0, m0, rows, gam);
-        if (MODE == BWD_WRITE) __syncthreads();  // gamma overwrites X^T
-        if (m0 < K) {
-            if (!KS)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) put4(g + (r0 + i) * K + m0, gam[i][0], gam[i][1], gam[i][2], gam[i][3]);
-            if (QK)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) put4(gT + (m0 + j) * kLDT + r0, gam[0][j], gam[1][j], gam[2][j], gam[3][j]);
-        }
-        __syncthreads();
-
-        if (MODE == BWD_WRITE) {  // Vt += gamma^T V, Z += gamma^T 1 (rows k, columns c)
-            if (r0 < K && m0 < dv)
-#pragma unroll 4
-                for (int t = 0; t < rows; ++t) {
-                    float ga[4], ya[4];
-                    unpack(lds4(g + t * K + r0), ga);
-                    unpack(lds4(Yr + t * dv + m0), ya);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        mz[i] += ga[i];
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) mv[i][j] = fmaf(ga[i], ya[j], mv[i][j]);
-                    }
-                }
-            continue;
-        }
-
-        // causal: C_ij = gamma^Q_i . gamma^K_j for key j <= query i (rows i = r0.., columns j = m0..);
-        // the query pass keeps C^T and its row sums, the key pass C and A_ij = dO'_i . V_j - a'_i
-        float cs[4] = {};
-        if (CAUSAL) {
-            const float* gqT = QS ? gT : GoT;  // [K][kLDT] gamma^Q transposed
-            const float* gkT = QS ? GoT : gT;  // [K][kLDT] gamma^K transposed
-            float ca[4][4] = {}, aa[4][4] = {};
-            const bool live = m0 <= r0 + 3 && r0 < rows;  // the block has entries with j <= i
-            if (live) {
-#pragma unroll 4
-                for (int k = 0; k < K; ++k) {
-                    float qa[4], ka[4];
-                    unpack(lds4(gqT + k * kLDT + r0), qa);
-                    unpack(lds4(gkT + k * kLDT + m0), ka);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) ca[i][j] = fmaf(qa[i], ka[j], ca[i][j]);
-                }
-                if (MODE == BWD_CKEY) {
-#pragma unroll 4
-                    for (int cc = 0; cc < dv; ++cc) {
-                        float va[4], oa[4];
-                        unpack(lds4(YT + cc * kLDT + m0), va);  // V^T
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) oa[i] = Rw[(r0 + i) * LV4 + cc];  // dO'
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) aa[i][j] = fmaf(oa[i], va[j], aa[i][j]);
-                    }
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool in = live && m0 + j <= r0 + i && r0 + i < rows;
-                    ca[i][j] = in ? ca[i][j] : 0.0f;
-                    aa[i][j] = in ? aa[i][j] - Av[r0 + i] : 0.0f;
-                    cs[i] += ca[i][j];
-                }
-            if (QS) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) put4(Cm + (m0 + j) * kLDT + r0, ca[0][j], ca[1][j], ca[2][j], ca[3][j]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    put4(Cm + (r0 + i) * kLDT + m0, ca[i][0], ca[i][1], ca[i][2], ca[i][3]);
-                    put4(Am + (r0 + i) * kLDT + m0, aa[i][0], aa[i][1], aa[i][2], aa[i][3]);
-                }
-            }
-            __syncthreads();
-        }
-        const int tmax = min(r0 + 4, rows);  // causal: in-tile keys j <= the block's last query row
-
-        float gg[4][4] = {};  // upstream gradient at the responsibilities (rows t, columns k)
-        if (QS) {
-            // N = gamma Vt (rows t, columns c); D = gamma Z + eps; dO . N
-            float nv[4][4] = {};
-            if (m0 < dv)
-#pragma unroll 4
-                for (int k = 0; k < K; ++k) {
-                    float ga[4], va[4];
-                    unpack(lds4(gT + k * kLDT + r0), ga);
-                    unpack(lds4(M + k * dv + m0), va);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ga[i], va[j], nv[i][j]);
-                }
-            if (CAUSAL && m0 < dv)  // + sum_{j <= t} C_tj V_j
-                for (int j = 0; j < tmax; ++j) {
-                    float ca[4], va[4];
-                    unpack(lds4(Cm + j * kLDT + r0), ca);
-                    unpack(lds4(Rw + j * LV4 + m0), va);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) nv[i][jj] = fmaf(ca[i], va[jj], nv[i][jj]);
-                }
-            float Dt[4], An[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float dp = cs[i], ap = 0.0f;
-                if (m0 < K)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) dp = fmaf(gam[i][j], Zm[m0 + j], dp);
-                if (m0 < dv) {
-                    float ya[4];
-                    unpack(lds4(Yr + (r0 + i) * dv + m0), ya);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) ap = fmaf(ya[j], nv[i][j], ap);
-                }
-                Dt[i] = sum16(dp) + eps;
-                An[i] = sum16(ap);
-            }
-            // dO' = dO / D in both layouts (each thread rescales its own entries), D and a' = dO . N / D^2
-            float sy[4][4];
-            if (m0 < dv) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float ya[4];
-                    unpack(lds4(Yr + (r0 + i) * dv + m0), ya);
-                    const float rD = 1.0f / Dt[i];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) sy[i][j] = ya[j] * rD;
-                    put4(Yr + (r0 + i) * dv + m0, sy[i][0], sy[i][1], sy[i][2], sy[i][3]);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) put4(YT + (m0 + j) * kLDT + r0, sy[0][j], sy[1][j], sy[2][j], sy[3][j]);
-            }
-            if (mc == 0)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    Dv[r0 + i] = Dt[i];
-                    Av[r0 + i] = An[i] / (Dt[i] * Dt[i]);
-                    if (CAUSAL && r0 + i < rows) {
-                        rowda[(size_t(p) * N + n0 + r0 + i) * 2 + 0] = Dt[i];
-                        rowda[(size_t(p) * N + n0 + r0 + i) * 2 + 1] = An[i] / Dt[i];
-                    }
-                }
-            __syncthreads();
-            // causal: A^T (A_tj = dO'_t . V_j - a'_t for j <= t) over C^T, whose reads are done
-            if (CAUSAL) {
-                float aa[4][4] = {};
-                const bool live = m0 <= r0 + 3 && r0 < rows;
-                if (live)
-#pragma unroll 4
-                    for (int cc = 0; cc < dv; ++cc) {
-                        float oa[4], va[4];
-                        unpack(lds4(YT + cc * kLDT + r0), oa);  // dO'^T
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) va[j] = Rw[(m0 + j) * LV4 + cc];  // V
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) aa[i][j] = fmaf(oa[i], va[j], aa[i][j]);
-                    }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        aa[i][j] = live && m0 + j <= r0 + i && r0 + i < rows ? aa[i][j] - Av[r0 + i] : 0.0f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) put4(Cm + (m0 + j) * kLDT + r0, aa[0][j], aa[1][j], aa[2][j], aa[3][j]);
-            }
-            // dVt += gamma^T dO', dZ -= gamma^T a' (rows k, columns c)
-            if (r0 < K && m0 < dv)
-#pragma unroll 4
-                for (int t = 0; t < rows; ++t) {
-                    float ga[4], ya[4];
-                    unpack(lds4(g + t * K + r0), ga);
-                    unpack(lds4(Yr + t * dv + m0), ya);
-                    const float at = Av[t];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        mz[i] = fmaf(-ga[i], at, mz[i]);
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) mv[i][j] = fmaf(ga[i], ya[j], mv[i][j]);
-                    }
-                }
-            // g = dO' Vt^T - a' Z
-            if (m0 < K) {
-#pragma unroll 4
-                for (int cc = 0; cc < dv; ++cc) {
-                    float ya[4], va[4];
-                    unpack(lds4(YT + cc * kLDT + r0), ya);
-                    unpack(lds4(MT + cc * K + m0), va);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(ya[i], va[j], gg[i][j]);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(-Av[r0 + i], Zm[m0 + j], gg[i][j]);
-            }
-            if (CAUSAL) {  // + sum_{j <= t} A_tj gamma^K_j
-                __syncthreads();
-                if (m0 < K)
-                    for (int j = 0; j < tmax; ++j) {
-                        float ta[4], ka[4];
-                        unpack(lds4(Cm + j * kLDT + r0), ta);
-                        unpack(lds4(Go + j * LG + m0), ka);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int jj = 0; jj < 4; ++jj) gg[i][jj] = fmaf(ta[i], ka[jj], gg[i][jj]);
-                    }
-            }
-        } else {
-            // dV = gamma dVt (rows t, columns c)
-            if (m0 < dv) {
-                float nv[4][4] = {};
-#pragma unroll 4
-                for (int k = 0; k < K; ++k) {
-                    float ga[4], va[4];
-                    unpack(lds4(gT + k * kLDT + r0), ga);
-                    unpack(lds4(M + k * dv + m0), va);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ga[i], va[j], nv[i][j]);
-                }
-                if (CAUSAL)  // + sum_{i >= j} C_ij dO'_i (rows j = r0.., queries i >= r0)
-                    for (int i2 = r0; i2 < rows; ++i2) {
-                        float ca[4], oa[4];
-                        unpack(lds4(Cm + i2 * kLDT + r0), ca);
-                        unpack(lds4(Rw + i2 * LV4 + m0), oa);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ca[i], oa[j], nv[i][j]);
-                    }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (r0 + i < rows)
-                        *reinterpret_cast<float4*>(dY + (size_t(p) * N + n0 + r0 + i) * dv + m0) =
-                            make_float4(nv[i][0], nv[i][1], nv[i][2], nv[i][3]);
-            }
-            // g = V dVt^T + dZ
-            if (m0 < K) {
-#pragma unroll 4
-                for (int cc = 0; cc < dv; ++cc) {
-                    float ya[4], va[4];
-                    unpack(lds4(YT + cc * kLDT + r0), ya);
-                    unpack(lds4(MT + cc * K + m0), va);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(ya[i], va[j], gg[i][j]);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) gg[i][j] += Zm[m0 + j];
-                if (CAUSAL)  // + sum_{i >= j} A_ij gamma^Q_i
-                    for (int i2 = r0; i2 < rows; ++i2) {
-                        float ta[4], qa[4];
-                        unpack(lds4(Am + i2 * kLDT + r0), ta);
-                        unpack(lds4(Go + i2 * LG + m0), qa);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(ta[i], qa[j], gg[i][j]);
-                    }
-            }
-        }
-        // Eq. 18: ds = gamma (g - gamma . g)
-        float ds[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float w = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) w = fmaf(gam[i][j], gg[i][j], w);
-            w = sum16(w);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) ds[i][j] = gam[i][j] * (gg[i][j] - w);
-        }
-        __syncthreads();  // every read of gamma is done
-        if (m0 < K) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) put4(g + (r0 + i) * K + m0, ds[i][0], ds[i][1], ds[i][2], ds[i][3]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) put4(gT + (m0 + j) * kLDT + r0, ds[0][j], ds[1][j], ds[2][j], ds[3][j]);
-        }
-        __syncthreads();
-        // dX (rows d, columns t): dx_td = -sum_k ds_tk (x_td - mu_kd) / sigma2_kd
-        if (r0 < dr) {
-            float xa[4][4], acc[4][4] = {};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) unpack(lds4(xT + (r0 + i) * kLDT + m0), xa[i]);
-#pragma unroll 4
-            for (int k = 0; k < K; ++k) {
-                float da[4], ma[4], ia[4];
-                unpack(lds4(gT + k * kLDT + m0), da);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    ma[i] = muT[(r0 + i) * LDK + k];
-                    ia[i] = ivT[(r0 + i) * LDK + k];
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(da[j] * ia[i], xa[i][j] - ma[i], acc[i][j]);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (m0 + j < rows)
-                    *reinterpret_cast<float4*>(dX + (size_t(p) * N + n0 + m0 + j) * dr + r0) =
-                        make_float4(-acc[0][j], -acc[1][j], -acc[2][j], -acc[3][j]);
-        }
-        // moments (rows d, columns k)
-        if (mom)
-#pragma unroll 4
-            for (int t = 0; t < rows; ++t) {
-                float da[4], xa[4];
-                unpack(lds4(g + t * K + m0), da);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) xa[i] = xT[(r0 + i) * kLDT + t];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) s0[j] += da[j];
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const float df = xa[i] - mreg[i][j], w = da[j] * df;
-                        s1[i][j] += w;
-                        s2[i][j] = fmaf(w, df, s2[i][j]);
-                    }
-            }
-        if (CAUSAL && r0 < K && m0 < dv) {
-            // advance the memory past the tile (its last reads were before the ds barriers):
-            // query: + gamma^K^T [V | 1] (Eq. 6b); key: + gamma^Q^T [dO' | -a']
-            float ua[4][4] = {}, uz[4] = {};
-            for (int t = 0; t < rows; ++t) {
-                float ga[4], ya[4];
-                unpack(lds4(Go + t * LG + r0), ga);
-                unpack(lds4(Rw + t * LV4 + m0), ya);
-                const float zt = QS ? 1.0f : -Av[t];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    uz[i] = fmaf(ga[i], zt, uz[i]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) ua[i][j] = fmaf(ga[i], ya[j], ua[i][j]);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float mm[4];
-                unpack(lds4(M + (r0 + i) * dv + m0), mm);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) mm[j] += ua[i][j];
-                put4(M + (r0 + i) * dv + m0, mm[0], mm[1], mm[2], mm[3]);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) MT[(m0 + j) * K + r0 + i] = mm[j];
-                if (mc == 0) Zm[r0 + i] += uz[i];
-            }
-        }
-    }
-    // the split's records (zeros for a split without rows)
-    if (!KS && r0 < K && m0 < dv) {
-        float* mp = mem_part + (size_t(p) * G + gi) * size_t(K) * (dv + 1);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<float4*>(mp + (r0 + i) * dv + m0) = make_float4(mv[i][0], mv[i][1], mv[i][2], mv[i][3]);
-        if (mc == 0)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mp[K * dv + r0 + i] = mz[i];
-    }
-    if (mom) {
-        float* pp = param_part + (size_t(p) * G + gi) * size_t(2 * K * dr + K);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                pp[(m0 + j) * dr + r0 + i] = s1[i][j];
-                pp[K * dr + (m0 + j) * dr + r0 + i] = s2[i][j];
-            }
-        if (tr == 0)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pp[2 * K * dr + m0 + j] = s0[j];
-    }
-}
-
-// Grid (ceil((K d_r + K) / kThreads), H): the parameter gradients of head h from the moments,
-// summed in fp64 over the query and key sides, the batch and the splits in that fixed order.
-// With B == 0 it writes zeros (no rows, no gradient) and reads neither moments nor tables.
-__global__ void __launch_bounds__(kThreads)
-    f32_bwd_param_reduce_kernel(const float* __restrict__ part, int B, int H, int G, int K, int dr,
-                                const double* __restrict__ inv, const float* __restrict__ pi,
-                                float* __restrict__ dmu, float* __restrict__ ds2, float* __restrict__ dpi) {
-    const int h = blockIdx.y, PE = 2 * K * dr + K;
-    const int e = blockIdx.x * kThreads + threadIdx.x;
-    if (e >= K * dr + K) return;
-    const size_t P = size_t(B) * H;
-    const int k = e < K * dr ? e / dr : e - K * dr;
-    const int i1 = e < K * dr ? e : 2 * K * dr + k;  // S1 (or S0 for dpi)
-    // records in (side, b, g) order, loads issued eight records at a time, sums in that order
-    double s1 = 0.0, s2 = 0.0, s0 = 0.0;
-    const int R = 2 * B * G;
-    for (int r = 0; r < R; r += 8) {
-        float v1[8], v2[8], v0[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            v1[u] = v2[u] = v0[u] = 0.0f;
-            const int q = r + u;
-            if (q < R) {
-                const int side = q / (B * G), b = (q / G) % B, g = q % G;
-                const float* rec = part + ((side * P + size_t(b) * H + h) * G + g) * PE;
-                v1[u] = rec[i1];
-                if (e < K * dr) {
-                    v2[u] = rec[K * dr + e];
-                    v0[u] = rec[2 * K * dr + k];
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            s1 += double(v1[u]);
-            s2 += double(v2[u]);
-            s0 += double(v0[u]);
-        }
-    }
-    if (e < K * dr) {
-        const double iv = B > 0 ? inv[size_t(h) * K * dr + e] : 0.0;
-        dmu[size_t(h) * K * dr + e] = float(iv * s1);
-        ds2[size_t(h) * K * dr + e] = float(0.5 * (iv * iv * s2 - iv * s0));
-    } else {
-        dpi[size_t(h) * K + k] = B > 0 ? float(s1 / double(pi[size_t(h) * K + k])) : 0.0f;
-    }
-}
-
-hipError_t reduce_params(const Plan& p, const float* part, int B, const double* inv, const float* pi, float* dmu,
-                         float* ds2, float* dpi, hipStream_t st) {
-    const int n = int(p.K * p.dr + p.K);
-    GMA_LAUNCH("f32_bwd_params", f32_bwd_param_reduce_kernel, dim3(unsigned((n + kThreads - 1) / kThreads), unsigned(p.H)),
-               dim3(kThreads), 0, st, part, B, int(p.H), int(p.G), int(p.K), int(p.dr), inv, pi, dmu, ds2, dpi);
-    return hipGetLastError();
-}
-
-hipError_t bwd_allow_lds() {
-    static const hipError_t e = [] {
-        const void* fns[] = {(const void*)f32_bwd_side_kernel<true>, (const void*)f32_bwd_side_kernel<false>,
-                             (const void*)f32_bwd_tiled_kernel<BWD_WRITE>, (const void*)f32_bwd_tiled_kernel<BWD_QUERY>,
-                             (const void*)f32_bwd_tiled_kernel<BWD_KEY>, (const void*)f32_bwd_tiled_kernel<BWD_CQUERY>,
-                             (const void*)f32_bwd_tiled_kernel<BWD_CKEY>};
-        for (const void* f : fns) {
-            hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
-            if (r != hipSuccess) return r;
-        }
-        return hipSuccess;
-    }();
-    return e;
-}
-
-}  // namespace
-
-size_t f32_backward_extra_bytes(const Plan& p) {
-    const size_t E = size_t(p.K) * size_t(p.dv + 1);
-    return round_up(size_t(p.P * p.G) * E * 4, 256) + round_up(size_t(p.P) * E * 4, 256) +
-           round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256);
-}
-
-hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
-                              const float* s2, const float* pi, float eps, const float* dO, float* dXQ, float* dXK,
-                              float* dV, float* dmu, float* ds2, float* dpi, char* ws, hipStream_t st) {
-    if (p.H == 0) return hipSuccess;
-    if (p.P == 0 || p.N == 0) return reduce_params(p, nullptr, 0, nullptr, pi, dmu, ds2, dpi, st);  // zero gradients
-    hipError_t e = bwd_allow_lds();
-    if (e != hipSuccess) return e;
-    if ((e = launch_params(p, s2, pi, ws, st)) != hipSuccess) return e;
-    F32Params v = f32_params_view(p, ws);
-    float* partials = reinterpret_cast<float*>(ws + p.off_partials);
-    float* memory = reinterpret_cast<float*>(ws + p.off_memory);
-    const size_t E = size_t(p.K) * size_t(p.dv + 1);
-    char* extra = ws + p.off_stage - f32_backward_extra_bytes(p);
-    float* dpart = reinterpret_cast<float*>(extra);
-    float* dmem = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256));
-    float* ppart = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256) + round_up(size_t(p.P) * E * 4, 256));
-    float* ppart_key = ppart + size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K);
-    const dim3 grid(unsigned(p.G), unsigned(p.P));
-    const int Ei = int(E);
-    const dim3 cgrid(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P));
-    const int H = int(p.H), dr = int(p.dr), dv = int(p.dv), K = int(p.K), G = int(p.G);
-    if (bwd_tiled_applies(p)) {
-        GMA_LAUNCH("f32_bwd_write", f32_bwd_tiled_kernel<BWD_WRITE>, grid, dim3(kThreads),
-                   bwd_tiled_lds_bytes(BWD_WRITE, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
-                   static_cast<const float*>(nullptr), eps, static_cast<float*>(nullptr),
-                   static_cast<float*>(nullptr), partials, static_cast<float*>(nullptr),
-                   static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), static_cast<float*>(nullptr));
-    } else {
-        const size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
-        GMA_LAUNCH("f32_bwd_write", f32_write_kernel, grid, dim3(kThreads), lds_w, st, XK, V, p.N, H, dr, dv, K,
-                   p.seg, G, v.c, v.inv, mu, partials);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, partials, G, Ei, memory);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (bwd_tiled_applies(p)) {
-        GMA_LAUNCH("f32_bwd_query", f32_bwd_tiled_kernel<BWD_QUERY>, grid, dim3(kThreads),
-                   bwd_tiled_lds_bytes(BWD_QUERY, K, dr, dv), st, XQ, dO, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
-                   static_cast<const float*>(memory), eps, dXQ, static_cast<float*>(nullptr), dpart, ppart,
-                   static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), static_cast<float*>(nullptr));
-    } else {
-        int T = kTile;
-        while (T > 8 && bwd_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
-        GMA_LAUNCH("f32_bwd_query", f32_bwd_side_kernel<true>, grid, dim3(kThreads), bwd_lds_bytes(T, dr, dv, K), st,
-                   XQ, dO, p.N, H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, static_cast<const float*>(memory), eps, dXQ,
-                   static_cast<float*>(nullptr), dpart, ppart);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, dpart, G, Ei, dmem);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (bwd_tiled_applies(p)) {
-        GMA_LAUNCH("f32_bwd_key", f32_bwd_tiled_kernel<BWD_KEY>, grid, dim3(kThreads),
-                   bwd_tiled_lds_bytes(BWD_KEY, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
-                   static_cast<const float*>(dmem), eps, dXK, dV, static_cast<float*>(nullptr), ppart_key,
-                   static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), static_cast<float*>(nullptr));
-    } else {
-        int T = kTile;
-        while (T > 8 && bwd_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
-        GMA_LAUNCH("f32_bwd_key", f32_bwd_side_kernel<false>, grid, dim3(kThreads), bwd_lds_bytes(T, dr, dv, K), st,
-                   XK, V, p.N, H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, static_cast<const float*>(dmem), eps, dXK, dV,
-                   static_cast<float*>(nullptr), ppart_key);
-    }
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
-}
-
-// ---------------------------------------------------------------------------- causal backward
-// Gradients of <dO, O> for the causal forward (Eq. 6b, 8b).  Position i reads the prefix memory
-// Vt^(i), Z^(i) over j <= i, so with D_i = gamma^Q_i . Z^(i) + eps and a_i = dO_i . O_i
-//   g^Q_ik = (dO_i . Vt^(i)_k - a_i Z^(i)_k) / D_i,
-// and key position j receives the suffix sums of what every later (or equal) query position
-// sends to its memory:
-//   dVt_j = sum_{i>=j} gamma^Q_i dO_i^T / D_i,  dZ_j = -sum_{i>=j} gamma^Q_i a_i / D_i,
-//   dV_j = sum_k gamma^K_jk dVt_j[k],            g^K_jk = dVt_j[k] . V_j + dZ_j[k];
-// Eq. 18-20 follow as for the bidirectional backward.  Within a tile of T positions the prefix
-// (suffix) splits into the memory at the tile's start (end) and the masked T x T products
-// C_ij = gamma^Q_i . gamma^K_j and A_ij = (dO_i . V_j - a_i) / D_i for j <= i.
-namespace {
-
-size_t bwdc_lds_bytes(int T, int dr, int dv, int K) {
-    return size_t(T) * (dr + 3 * K + 2 * dv + 2 * T + 2) * sizeof(float);
-}
-
-// Causal: exclusive suffix over segments in place; segment g then holds the sum over the
-// segments after it.
-__global__ void __launch_bounds__(kThreads) f32_suffix_kernel(float* __restrict__ partials, int G, int E) {
-    const int64_t p = blockIdx.y;
-    const int e = blockIdx.x * kThreads + threadIdx.x;
-    if (e >= E) return;
-    float* src = partials + size_t(p) * G * E + e;
-    float run = 0.0f;
-    for (int g = G - 1; g >= 0; --g) {
-        const float a = src[size_t(g) * E];
-        src[size_t(g) * E] = run;
-        run += a;
-    }
-}
-
-// gamma_tile with fp32 tables in LDS: c [K], 1/sigma2 and mu as [K][LR] rows (LR = d_r + 1),
-// the direct-form score of Eq. 16 in fp32, then the softmax of Eq. 3b.  Same contract as gamma_tile.
-__device__ void gamma_tile_lds(const float* __restrict__ X, int64_t n0, int rows, int T, int dr, int K,
-                               const float* c_l, const float* inv_l, const float* mu_l, float* xs, float* g) {
-    const int LR = dr + 1;
-    for (int i = threadIdx.x; i < T * dr; i += kThreads) {
-        const int t = i / dr;
-        xs[i] = (t < rows) ? X[(n0 + t) * dr + (i - t * dr)] : 0.0f;
-    }
-    __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int t = wave; t < T; t += kThreads / kWave) {
-        float* gt = g + size_t(t) * K;
-        if (t >= rows) {
-            for (int k = lane; k < K; k += kWave) gt[k] = 0.0f;
-            continue;
-        }
-        const float* xt = xs + t * dr;
-        float sc[4], m = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int k = lane + j * kWave;
-            sc[j] = -INFINITY;
-            if (k < K) {
-                const float *mk = mu_l + k * LR, *ik = inv_l + k * LR;
-                float q = 0.0f;
-                for (int d = 0; d < dr; ++d) {
-                    const float df = xt[d] - mk[d];
-                    q = fmaf(df * df, ik[d], q);
-                }
-                sc[j] = c_l[k] - 0.5f * q;
-                m = fmaxf(m, sc[j]);
-            }
-        }
-        m = wave_max(m);
-        float ev[4], sum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            ev[j] = (lane + j * kWave < K) ? expf(sc[j] - m) : 0.0f;
-            sum += ev[j];
-        }
-        sum = wave_sum(sum);
-        const float r = 1.0f / sum;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (lane + j * kWave < K) gt[lane + j * kWave] = ev[j] * r;
-    }
-    __syncthreads();
-}
-
-// Grid (G segments, P).  QUERY walks the segment's tiles forward from the memory before the
-// segment (state: [Vt (K dv) | Z (K)]), writes dX_Q, D_i and a_i of every row (rowda), the
-// segment's total of what its queries send to the memory (seg_part) and its moments.  KEY walks
-// the tiles backward from what the later segments' queries sent (state), writes dX_K, dV and its
-// moments.  FAST: the per-head tables (fp32) and the running memory live in LDS (rows padded by
-// one element), the scores, dX and moments are fp32; otherwise they are read from the fp64 tables
-// and the running memory is advanced in place in the workspace.
-template <bool QUERY, bool FAST>
-__global__ void __launch_bounds__(kThreads)
-    f32_bwdc_kernel(const float* __restrict__ XQ, const float* __restrict__ XK, const float* __restrict__ V,
-                    const float* __restrict__ dO, int64_t N, int H, int dr, int dv, int K, int64_t seg, int G, int T,
-                    const double* c, const double* inv, const float* mu, float* state, float eps,
-                    float* __restrict__ rowda, float* __restrict__ dX, float* __restrict__ dV,
-                    float* __restrict__ seg_part, float* __restrict__ param_part) {
-    extern __shared__ float lds[];
-    const int64_t p = blockIdx.y;
-    const int gi = blockIdx.x, h = int(p % H);
-    float* xs = lds;          // T*dr: scratch of gamma_tile; left holding this side's rows
-    float* gq = xs + T * dr;  // T*K
-    float* gk = gq + T * K;   // T*K
-    float* gg = gk + T * K;   // T*K: upstream gradient, then ds
-    float* ys = gg + T * K;   // T*dv: dO
-    float* vs = ys + T * dv;  // T*dv: V
-    float* Cm = vs + T * dv;  // T*T
-    float* Am = Cm + T * T;   // T*T
-    float* dd = Am + T * T;   // T: D_i
-    float* aa = dd + T;       // T: a_i
-    const int LR = dr + 1, LV = dv + 1;
-    float* mT = aa + T;             // FAST: [K][LR] mu
-    float* iT = mT + K * LR;        // FAST: [K][LR] 1 / sigma2
-    float* cT = iT + K * LR;        // FAST: [K] score constants
-    float* Sm = cT + K;             // FAST: [K][LV] running memory (Vt or dVt)
-    float* Sz = Sm + K * LV;        // FAST: [K] its Z (or dZ)
-    const double *ch = c + size_t(h) * K, *ih = inv + size_t(h) * K * dr;
-    const float* mh = mu + size_t(h) * K * dr;
-    const int E = K * (dv + 1), PE = 2 * K * dr + K;
-    float* Sg = state + (size_t(p) * G + gi) * E;  // [K][dv], then Z
-    // the running memory: LDS rows of LV (FAST) or the workspace record
-    float* St = FAST ? Sm : Sg;
-    float* Zs = FAST ? Sz : Sg + size_t(K) * dv;
-    const int SL = FAST ? LV : dv;
-    if (FAST) {
-        for (int i = threadIdx.x; i < K * dr; i += kThreads) {
-            const int k = i / dr, d = i - k * dr;
-            mT[k * LR + d] = mh[i];
-            iT[k * LR + d] = float(ih[i]);
-        }
-        for (int k = threadIdx.x; k < K; k += kThreads) {
-            cT[k] = float(ch[k]);
-            Sz[k] = Sg[K * dv + k];
-        }
-        for (int i = threadIdx.x; i < K * dv; i += kThreads) Sm[(i / dv) * LV + i % dv] = Sg[i];
-        __syncthreads();
-    }
-    float* sp = QUERY ? seg_part + (size_t(p) * G + gi) * E : nullptr;
-    float* pp = param_part + (size_t(p) * G + gi) * PE;
-    const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
-    const int ntiles = int((hi - lo + T - 1) / T);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    bool first = true;
-    for (int it = 0; it < ntiles; ++it) {
-        const int64_t n0 = lo + int64_t(QUERY ? it : ntiles - 1 - it) * T;
-        const int rows = int(min<int64_t>(T, hi - n0));
-        // responsibilities; the side's own rows are left in xs
-        if (FAST) {
-            gamma_tile_lds(QUERY ? XK + p * N * dr : XQ + p * N * dr, n0, rows, T, dr, K, cT, iT, mT, xs,
-                           QUERY ? gk : gq);
-            gamma_tile_lds(QUERY ? XQ + p * N * dr : XK + p * N * dr, n0, rows, T, dr, K, cT, iT, mT, xs,
-                           QUERY ? gq : gk);
-        } else if (QUERY) {
-            gamma_tile(XK + p * N * dr, n0, rows, T, dr, K, ch, ih, mh, xs, gk);
-            gamma_tile(XQ + p * N * dr, n0, rows, T, dr, K, ch, ih, mh, xs, gq);
-        } else {
-            gamma_tile(XQ + p * N * dr, n0, rows, T, dr, K, ch, ih, mh, xs, gq);
-            gamma_tile(XK + p * N * dr, n0, rows, T, dr, K, ch, ih, mh, xs, gk);
-        }
-        for (int i = threadIdx.x; i < T * dv; i += kThreads) {
-            const int t = i / dv;
-            ys[i] = t < rows ? dO[(p * N + n0) * dv + i] : 0.0f;
-            vs[i] = t < rows ? V[(p * N + n0) * dv + i] : 0.0f;
-        }
-        if (!QUERY)
-            for (int t = threadIdx.x; t < T; t += kThreads) {
-                dd[t] = t < rows ? rowda[(p * N + n0 + t) * 2 + 0] : 1.0f;
-                aa[t] = t < rows ? rowda[(p * N + n0 + t) * 2 + 1] : 0.0f;
-            }
-        // C_ij = gamma^Q_i . gamma^K_j (j <= i)
-        for (int e = threadIdx.x; e < T * T; e += kThreads) {
-            const int i = e / T, j = e - i * T;
-            float acc = 0.0f;
-            if (j <= i && i < rows)
-                for (int k = 0; k < K; ++k) acc = fmaf(gq[i * K + k], gk[j * K + k], acc);
-            Cm[e] = acc;
-        }
-        __syncthreads();
-        if (QUERY) {  // D_i and a_i from the memory at the tile's start and the tile's own keys
-            for (int t = wave; t < rows; t += kThreads / kWave) {
-                float d = 0.0f;
-                for (int k = lane; k < K; k += kWave) d = fmaf(gq[t * K + k], Zs[k], d);
-                for (int j = lane; j <= t; j += kWave) d += Cm[t * T + j];
-                d = wave_sum(d) + eps;
-                float a = 0.0f;
-                for (int cc = lane; cc < dv; cc += kWave) {
-                    float nn = 0.0f;
-                    for (int k = 0; k < K; ++k) nn = fmaf(gq[t * K + k], St[size_t(k) * SL + cc], nn);
-                    for (int j = 0; j <= t; ++j) nn = fmaf(Cm[t * T + j], vs[j * dv + cc], nn);
-                    a = fmaf(ys[t * dv + cc], nn / d, a);
-                }
-                a = wave_sum(a);
-                if (lane == 0) {
-                    dd[t] = d;
-                    aa[t] = a;
-                    rowda[(p * N + n0 + t) * 2 + 0] = d;
-                    rowda[(p * N + n0 + t) * 2 + 1] = a;
-                }
-            }
-            __syncthreads();
-        }
-        // A_ij = (dO_i . V_j - a_i) / D_i (j <= i)
-        for (int e = threadIdx.x; e < T * T; e += kThreads) {
-            const int i = e / T, j = e - i * T;
-            float acc = 0.0f;
-            if (j <= i && i < rows) {
-                for (int cc = 0; cc < dv; ++cc) acc = fmaf(ys[i * dv + cc], vs[j * dv + cc], acc);
-                acc = (acc - aa[i]) / dd[i];
-            }
-            Am[e] = acc;
-        }
-        __syncthreads();
-        if (QUERY) {  // g^Q
-            for (int e = threadIdx.x; e < T * K; e += kThreads) {
-                const int t = e / K, k = e - t * K;
-                float acc = 0.0f;
-                if (t < rows) {
-                    for (int cc = 0; cc < dv; ++cc) acc = fmaf(ys[t * dv + cc], St[size_t(k) * SL + cc], acc);
-                    acc = (acc - aa[t] * Zs[k]) / dd[t];
-                    for (int j = 0; j <= t; ++j) acc = fmaf(Am[t * T + j], gk[j * K + k], acc);
-                }
-                gg[e] = acc;
-            }
-        } else {  // dV and g^K from the memory gradient after the tile and the tile's own queries
-            for (int e = threadIdx.x; e < rows * dv; e += kThreads) {
-                const int j = e / dv, cc = e - j * dv;
-                float acc = 0.0f;
-                for (int k = 0; k < K; ++k) acc = fmaf(gk[j * K + k], St[size_t(k) * SL + cc], acc);
-                for (int i = j; i < rows; ++i) acc = fmaf(Cm[i * T + j], ys[i * dv + cc] / dd[i], acc);
-                dV[(p * N + n0) * dv + e] = acc;
-            }
-            for (int e = threadIdx.x; e < T * K; e += kThreads) {
-                const int j = e / K, k = e - j * K;
-                float acc = 0.0f;
-                if (j < rows) {
-                    for (int cc = 0; cc < dv; ++cc) acc = fmaf(vs[j * dv + cc], St[size_t(k) * SL + cc], acc);
-                    acc += Zs[k];
-                    for (int i = j; i < rows; ++i) acc = fmaf(Am[i * T + j], gq[i * K + k], acc);
-                }
-                gg[e] = acc;
-            }
-        }
-        __syncthreads();
-        // Eq. 18 with this side's responsibilities, one wave per row
-        const float* gm = QUERY ? gq : gk;
-        for (int t = wave; t < T; t += kThreads / kWave) {
-            float w = 0.0f;
-            for (int k = lane; k < K; k += kWave) w = fmaf(gm[t * K + k], gg[t * K + k], w);
-            w = wave_sum(w);
-            for (int k = lane; k < K; k += kWave) gg[t * K + k] = gm[t * K + k] * (gg[t * K + k] - w);
-        }
-        __syncthreads();
-        // routing-vector gradient
-        for (int i = threadIdx.x; i < rows * dr; i += kThreads) {
-            const int t = i / dr, d = i - t * dr;
-            float acc = 0.0f;
-            if (FAST) {
-                const float x = xs[t * dr + d];
-                for (int k = 0; k < K; ++k) acc = fmaf(gg[t * K + k] * iT[k * LR + d], x - mT[k * LR + d], acc);
-            } else {
-                for (int k = 0; k < K; ++k)
-                    acc = fmaf(gg[t * K + k], float((double(xs[t * dr + d]) - double(mh[size_t(k) * dr + d])) * ih[size_t(k) * dr + d]), acc);
-            }
-            dX[(p * N + n0) * dr + i] = -acc;
-        }
-        // moments of these rows
-        for (int e = threadIdx.x; e < K * dr; e += kThreads) {
-            const int k = e / dr, d = e - k * dr;
-            float a1, a2;
-            if (FAST) {
-                const float m = mT[k * LR + d];
-                a1 = 0.0f, a2 = 0.0f;
-                for (int t = 0; t < rows; ++t) {
-                    const float df = xs[t * dr + d] - m, w = gg[t * K + k] * df;
-                    a1 += w;
-                    a2 = fmaf(w, df, a2);
-                }
-            } else {
-                const double m = double(mh[e]);
-                double b1 = 0.0, b2 = 0.0;
-                for (int t = 0; t < rows; ++t) {
-                    const double df = double(xs[t * dr + d]) - m, w = double(gg[t * K + k]) * df;
-                    b1 += w;
-                    b2 += w * df;
-                }
-                a1 = float(b1), a2 = float(b2);
-            }
-            pp[e] = first ? a1 : pp[e] + a1;
-            pp[K * dr + e] = first ? a2 : pp[K * dr + e] + a2;
-        }
-        for (int k = threadIdx.x; k < K; k += kThreads) {
-            float acc = 0.0f;
-            for (int t = 0; t < rows; ++t) acc += gg[t * K + k];
-            pp[2 * K * dr + k] = first ? acc : pp[2 * K * dr + k] + acc;
-        }
-        __syncthreads();  // every read of the memory for this tile is done
-        // advance the memory past the tile: QUERY adds the tile's keys (Eq. 6b) and totals what
-        // its queries send; KEY adds what the tile's queries send
-        for (int e = threadIdx.x; e < E; e += kThreads) {
-            float qsum = 0.0f, ksum = 0.0f;
-            if (e < K * dv) {
-                const int k = e / dv, cc = e - k * dv;
-                for (int t = 0; t < rows; ++t) {
-                    qsum = fmaf(gq[t * K + k], ys[t * dv + cc] / dd[t], qsum);
-                    if (QUERY) ksum = fmaf(gk[t * K + k], vs[t * dv + cc], ksum);
-                }
-            } else {
-                const int k = e - K * dv;
-                for (int t = 0; t < rows; ++t) {
-                    qsum -= gq[t * K + k] * aa[t] / dd[t];
-                    if (QUERY) ksum += gk[t * K + k];
-                }
-            }
-            // element e of the [Vt | Z] record in the running memory's layout
-            float& m = e < K * dv ? St[(e / dv) * SL + e % dv] : Zs[e - K * dv];
-            if (QUERY) {
-                m += ksum;
-                sp[e] = first ? qsum : sp[e] + qsum;
-            } else {
-                m += qsum;
-            }
-        }
-        first = false;
-        __syncthreads();  // the memory and the tile's LDS are ready for the next tile
-    }
-    if (first) {  // empty segment
-        for (int e = threadIdx.x; e < PE; e += kThreads) pp[e] = 0.0f;
-        if (QUERY)
-            for (int e = threadIdx.x; e < E; e += kThreads) sp[e] = 0.0f;
-    }
-}
-
-}  // namespace
-
-size_t f32_backward_causal_extra_bytes(const Plan& p) {
-    const size_t E = size_t(p.K) * size_t(p.dv + 1);
-    return round_up(size_t(p.P * p.G) * E * 4, 256) + round_up(size_t(p.P * p.N) * 2 * 4, 256) +
-           round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256);
-}
-
-hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
-                               const float* s2, const float* pi, float eps, const float* dO, float* dXQ, float* dXK,
-                               float* dV, float* dmu, float* ds2, float* dpi, char* ws, hipStream_t st) {
-    if (p.H == 0) return hipSuccess;
-    if (p.P == 0 || p.N == 0) return reduce_params(p, nullptr, 0, nullptr, pi, dmu, ds2, dpi, st);  // zero gradients
-    static const hipError_t attr = [] {
-        const void* fns[] = {(const void*)f32_bwdc_kernel<true, false>, (const void*)f32_bwdc_kernel<false, false>,
-                             (const void*)f32_bwdc_kernel<true, true>, (const void*)f32_bwdc_kernel<false, true>};
-        for (const void* f : fns) {
-            hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
-            if (r != hipSuccess) return r;
-        }
-        return hipSuccess;
-    }();
-    if (attr != hipSuccess) return attr;
-    hipError_t e = launch_params(p, s2, pi, ws, st);
-    if (e != hipSuccess) return e;
-    F32Params v = f32_params_view(p, ws);
-    float* states = reinterpret_cast<float*>(ws + p.off_partials);  // segment aggregates, then running memories
-    const size_t E = size_t(p.K) * size_t(p.dv + 1);
-    char* extra = ws + p.off_stage - f32_backward_causal_extra_bytes(p);
-    float* seg_part = reinterpret_cast<float*>(extra);
-    float* rowda = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256));
-    float* ppart = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256) +
-                                            round_up(size_t(p.P * p.N) * 2 * 4, 256));
-    float* ppart_key = ppart + size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K);
-    const dim3 grid(unsigned(p.G), unsigned(p.P));
-    const int Ei = int(E);
-    const dim3 egrid(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P));
-    const int H = int(p.H), dr = int(p.dr), dv = int(p.dv), K = int(p.K), G = int(p.G);
-    if (p.G > 1) {  // segment aggregates of the forward memory (one segment: the prefix writes zeros)
-        if (bwd_tiled_applies(p)) {
-            if ((e = bwd_allow_lds()) != hipSuccess) return e;
-            GMA_LAUNCH("f32_bwdc_aggregate", f32_bwd_tiled_kernel<BWD_WRITE>, grid, dim3(kThreads),
-                       bwd_tiled_lds_bytes(BWD_WRITE, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv,
-                       mu, static_cast<const float*>(nullptr), eps, static_cast<float*>(nullptr),
-                       static_cast<float*>(nullptr), states, static_cast<float*>(nullptr),
-                   static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), static_cast<float*>(nullptr));
-        } else {
-            const size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
-            GMA_LAUNCH("f32_bwdc_aggregate", f32_write_kernel, grid, dim3(kThreads), lds_w, st, XK, V, p.N, H, dr, dv,
-                       K, p.seg, G, v.c, v.inv, mu, states);
-        }
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    GMA_LAUNCH("f32_bwdc_prefix", f32_prefix_kernel, egrid, dim3(kThreads), 0, st, states, G, Ei,
-               static_cast<const float*>(nullptr), K, dv);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    // FAST (tables and running memory in LDS) with 64- or 32-position tiles when two workgroups
-    // still fit a CU; otherwise the general form: 64-position tiles when two fit, else the largest
-    // tile that lets two fit (down to 32), else the largest that fits at all
-    const size_t fast_extra = size_t(2 * K * (dr + 1) + 2 * K + K * (dv + 1)) * sizeof(float);
-    int T = kTile;
-    bool fast = false;
-    for (int t = kTile; t >= 32 && !fast; t /= 2)
-        if (bwdc_lds_bytes(t, dr, dv, K) + fast_extra <= kMaxLds / 2) fast = true, T = t;
-    if (!fast) {
-        while (T > 32 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds / 2) T /= 2;
-        while (T > 8 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
-    }
-    const size_t lds = bwdc_lds_bytes(T, dr, dv, K) + (fast ? fast_extra : 0);
-    float* none = nullptr;
-    const float* cnone = nullptr;
-    const bool tiled = bwd_tiled_applies(p) && bwd_tiled_lds_bytes(BWD_CQUERY, K, dr, dv) <= kMaxLds &&
-                       bwd_tiled_lds_bytes(BWD_CKEY, K, dr, dv) <= kMaxLds;
-    if (tiled) {  // register-tiled passes with the running memory in LDS
-        if ((e = bwd_allow_lds()) != hipSuccess) return e;
-        GMA_LAUNCH("f32_bwdc_query", f32_bwd_tiled_kernel<BWD_CQUERY>, grid, dim3(kThreads),
-                   bwd_tiled_lds_bytes(BWD_CQUERY, K, dr, dv), st, XQ, dO, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
-                   static_cast<const float*>(states), eps, dXQ, none, seg_part, ppart, XK, V, rowda);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        GMA_LAUNCH("f32_bwdc_suffix", f32_suffix_kernel, egrid, dim3(kThreads), 0, st, seg_part, G, Ei);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        GMA_LAUNCH("f32_bwdc_key", f32_bwd_tiled_kernel<BWD_CKEY>, grid, dim3(kThreads),
-                   bwd_tiled_lds_bytes(BWD_CKEY, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
-                   static_cast<const float*>(seg_part), eps, dXK, dV, none, ppart_key, XQ, dO, rowda);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
-    }
-    (void)cnone;
-    if (fast)
-        GMA_LAUNCH("f32_bwdc_query", (f32_bwdc_kernel<true, true>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N,
-                   H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, states, eps, rowda, dXQ, none, seg_part, ppart);
-    else
-        GMA_LAUNCH("f32_bwdc_query", (f32_bwdc_kernel<true, false>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N,
-                   H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, states, eps, rowda, dXQ, none, seg_part, ppart);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    GMA_LAUNCH("f32_bwdc_suffix", f32_suffix_kernel, egrid, dim3(kThreads), 0, st, seg_part, G, Ei);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (fast)
-        GMA_LAUNCH("f32_bwdc_key", (f32_bwdc_kernel<false, true>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N, H,
-                   dr, dv, K, p.seg, G, T, v.c, v.inv, mu, seg_part, eps, rowda, dXK, dV, none, ppart_key);
-    else
-        GMA_LAUNCH("f32_bwdc_key", (f32_bwdc_kernel<false, false>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N,
-                   H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, seg_part, eps, rowda, dXK, dV, none, ppart_key);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
-}
-
-// ---------------------------------------------------------------------------- bf16 staging
-namespace {
-__global__ void __launch_bounds__(kThreads) widen_bf16_kernel(const uint16_t* __restrict__ src,
-                                                              float* __restrict__ dst, size_t n) {
-    for (size_t i = size_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += size_t(gridDim.x) * kThreads)
-        dst[i] = bf16_bits_to_f32(src[i]);
-}
-__global__ void __launch_bounds__(kThreads) narrow_bf16_kernel(const float* __restrict__ src,
-                                                               uint16_t* __restrict__ dst, size_t n) {
-    for (size_t i = size_t(blockIdx.x) * kThreads + threadIdx.x; i < n; i += size_t(gridDim.x) * kThreads)
-        dst[i] = f32_to_bf16_bits(src[i]);
-}
-unsigned cast_blocks(size_t n) { return unsigned(std::min<size_t>((n + kThreads - 1) / kThreads, 8192)); }
-}  // namespace
-
-hipError_t widen_bf16(const void* src, float* dst, size_t n, hipStream_t st) {
-    if (n == 0) return hipSuccess;
-    GMA_LAUNCH("widen_bf16", widen_bf16_kernel, dim3(cast_blocks(n)), dim3(kThreads), 0, st,
-               static_cast<const uint16_t*>(src), dst, n);
-    return hipGetLastError();
-}
-
-hipError_t narrow_to_bf16(const float* src, void* dst, size_t n, hipStream_t st) {
-    if (n == 0) return hipSuccess;
-    GMA_LAUNCH("narrow_bf16", narrow_bf16_kernel, dim3(cast_blocks(n)), dim3(kThreads), 0, st, src,
-               static_cast<uint16_t*>(dst), n);
     return hipGetLastError();
 }
 
