@@ -239,3 +239,28 @@ def test_backward_causal_full_size_sampled_heads():
             assert err <= TOL_BWD, (b, h, k, err)
     for k in ("dmu", "dsigma2", "dpi"):
         assert np.isfinite(got[k]).all(), k
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dims", [(700, 16, 32, 8), (700, 7, 5, 13), (300, 32, 64, 64)],
+                         ids=lambda d: "N%d-dr%d-dv%d-K%d" % d)
+def test_backward_ignores_workspace_contents(causal, dims):
+    """Every scratch value (split partials, segment memories and totals, per-position D and a,
+    moments) is written before it is read: a workspace of NaN bytes, reused across calls, gives
+    the same gradients bit for bit as a fresh one."""
+    N, dr, dv, K = dims
+    w = case(N, 120 + N % 89, B=2, H=3, d_r=dr, d_v=dv, K=K, causal=causal)
+    inp = make_inputs(w)
+    d = to_device(inp)
+    d_o = upstream(w, 1120).cuda()
+    fn = gb.gma_backward_causal if causal else gb.gma_backward_bidir
+    op = gb.GMA_OP_BACKWARD_CAUSAL if causal else gb.GMA_OP_BACKWARD_BIDIR
+    nbytes = gb.gma_workspace_size(op, w.B, w.H, w.N, w.d_r, w.d_v, w.K, gb.GMA_F32)
+    args = (d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], d_o, w.eps)
+    clean = fn(*args, workspace=torch.zeros(nbytes, dtype=torch.uint8, device="cuda"))
+    dirty_ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    for _ in range(2):
+        dirty = fn(*args, workspace=dirty_ws)
+        torch.cuda.synchronize()
+        for k in KEYS:
+            assert torch.equal(clean[k], dirty[k]), k
