@@ -259,19 +259,20 @@ def alg_bytes_per_token_head(w, kernel: str) -> float:
         return e * (2 * w.d_r + 2 * w.d_v) + 2 * 4 * w.K * (w.d_v + 1)
     if w.diagnostics:  # the routing vectors in; the outputs (per token, not per head) are negligible
         return e * w.d_r
-    if w.backward:
+    if w.backward:  # the register-tiled passes keep the responsibilities (fp32, K per row) between passes
+        g = 4 * w.K
         if kernel.endswith("_bwdc_aggregate"):
-            return e * (w.d_r + w.d_v)          # X_K and V in
+            return e * (w.d_r + w.d_v) + g          # X_K and V in, Gamma_K out
         if kernel.endswith("_bwdc_query"):
-            return e * (3 * w.d_r + 2 * w.d_v)  # X_Q, X_K, V, dO in, dX_Q out
+            return e * (2 * w.d_r + 2 * w.d_v) + 2 * g  # X_Q, V, dO in, dX_Q out, Gamma_K in, Gamma_Q out
         if kernel.endswith("_bwdc_key"):
-            return e * (3 * w.d_r + 3 * w.d_v)  # X_Q, X_K, V, dO in, dX_K and dV out
+            return e * (2 * w.d_r + 3 * w.d_v) + 2 * g  # X_K, V, dO in, dX_K, dV out, Gamma_K and Gamma_Q in
         if kernel.endswith("_bwd_write"):
-            return e * (w.d_r + w.d_v)          # X_K and V in
+            return e * (w.d_r + w.d_v) + g          # X_K and V in, Gamma_K out
         if kernel.endswith("_bwd_query"):
-            return e * (2 * w.d_r + w.d_v)      # X_Q and dO in, dX_Q out
+            return e * (2 * w.d_r + w.d_v)          # X_Q and dO in, dX_Q out
         if kernel.endswith("_bwd_key"):
-            return e * (2 * w.d_r + 2 * w.d_v)  # X_K and V in, dX_K and dV out
+            return e * (2 * w.d_r + 2 * w.d_v) + g  # X_K and V in, dX_K and dV out, Gamma_K in
         if kernel == "step":
             return e * (4 * w.d_r + 3 * w.d_v)  # X_Q, X_K, V, dO in; dX_Q, dX_K, dV out
         return 0.0
@@ -292,23 +293,24 @@ F32_VALU_PEAK_TFLOPS = 78.6
 def alg_flops_per_token_head(w, kernel: str) -> float:
     """Algorithmic fp32 flops per (row, head) of the backward passes (an FMA counts 2): per (k, d)
     the direct-form score 3 (difference, then a fused square-scale-add), dX 4 and the three moments
-    5; per (k, c) each product with the memory 2; per k the softmax 3, Eq. 18 4, D / Z terms 2 each."""
+    5; per (k, c) each product with the memory 2; per k the softmax 3, Eq. 18 4, D / Z terms 2 each.
+    A pass that reads responsibilities another pass computed does no score work for them."""
     if not w.backward:
         return 0.0
     K, dr, dv = w.K, w.d_r, w.d_v
     T = 64  # positions per tile of the causal passes: the masked in-tile products cost T/2 per row
     if kernel.endswith("_bwdc_aggregate"):
         return 3 * K * dr + 2 * K * dv + 4 * K
-    if kernel.endswith("_bwdc_query"):  # the bidirectional query pass, the keys' scores, the memory update
-        return 15 * K * dr + 8 * K * dv + 15 * K + 2 * dv + 2 * T * K + 2 * T * dv
-    if kernel.endswith("_bwdc_key"):    # the bidirectional key pass, the queries' scores, the suffix update
-        return 15 * K * dr + 6 * K * dv + 11 * K + 2 * T * K + 2 * T * dv
+    if kernel.endswith("_bwdc_query"):  # the bidirectional query pass and the memory update
+        return 12 * K * dr + 8 * K * dv + 12 * K + 2 * dv + 2 * T * K + 2 * T * dv
+    if kernel.endswith("_bwdc_key"):    # the bidirectional key pass without scores, the suffix update
+        return 9 * K * dr + 6 * K * dv + 5 * K + 2 * T * K + 2 * T * dv
     if kernel.endswith("_bwd_write"):
         return 3 * K * dr + 2 * K * dv + 4 * K
     if kernel.endswith("_bwd_query"):
         return 12 * K * dr + 6 * K * dv + 12 * K + 2 * dv
-    if kernel.endswith("_bwd_key"):
-        return 12 * K * dr + 4 * K * dv + 8 * K
+    if kernel.endswith("_bwd_key"):  # Gamma_K comes from the write pass
+        return 9 * K * dr + 4 * K * dv + 5 * K
     return 0.0
 
 

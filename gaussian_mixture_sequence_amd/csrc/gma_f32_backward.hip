@@ -249,6 +249,27 @@ __device__ __forceinline__ void tile_gamma(const float* xT, const float* muT, co
     }
 }
 
+// The 4 x 4 responsibility block (rows r0.., components m0..) of the tile at n0 from a cache
+// [.][K] (zeros beyond `rows` or K), and its store.
+__device__ __forceinline__ void gamma_from(const float* Gp, int64_t n0, int rows, int K, int r0, int m0,
+                                           float (&gam)[4][4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool ok = m0 < K && r0 + i < rows;
+        const float4 v = ok ? *reinterpret_cast<const float4*>(Gp + (n0 + r0 + i) * K + m0) : make_float4(0, 0, 0, 0);
+        gam[i][0] = v.x, gam[i][1] = v.y, gam[i][2] = v.z, gam[i][3] = v.w;
+    }
+}
+__device__ __forceinline__ void gamma_to(float* Gp, int64_t n0, int rows, int K, int r0, int m0,
+                                         const float (&gam)[4][4]) {
+    if (m0 < K)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (r0 + i < rows)
+                *reinterpret_cast<float4*>(Gp + (n0 + r0 + i) * K + m0) =
+                    make_float4(gam[i][0], gam[i][1], gam[i][2], gam[i][3]);
+}
+
 // Load rows [n0, n0 + rows) of X [.][dr] into xT [dr][kLDT] (zeros beyond `rows`).
 __device__ __forceinline__ void load_xT(const float* Xp, int64_t n0, int rows, int dr, float* xT) {
     for (int i = threadIdx.x; i < kBT * (dr / 4); i += kThreads) {
@@ -272,14 +293,18 @@ __device__ __forceinline__ void load_xT(const float* Xp, int64_t n0, int rows, i
 //   later segments' queries send (CKEY), advanced in LDS tile by tile.  CQUERY writes D_i and a_i
 //   of its rows to rowda and the segment's total of what its queries send to mem_part; CKEY reads
 //   rowda.
+// Responsibility cache ([P][N][K] fp32, or NULL): gsave receives this pass's own responsibilities,
+// gload supplies them instead of the score loop, goload supplies the other side's (causal).
+// A cached value is the one the score loop would compute, so the results do not change.
 template <int MODE>
 __global__ void __launch_bounds__(kThreads)
     f32_bwd_tiled_kernel(const float* __restrict__ X, const float* __restrict__ Y, int64_t N, int H, int dr, int dv,
                          int K, int64_t seg, int G, const double* __restrict__ c, const double* __restrict__ inv,
                          const float* __restrict__ mu, const float* __restrict__ mem, float eps,
                          float* __restrict__ dX, float* __restrict__ dY, float* __restrict__ mem_part,
-                         float* __restrict__ param_part, const float* __restrict__ X2 = nullptr,
-                         const float* __restrict__ Y2 = nullptr, float* __restrict__ rowda = nullptr) {
+                         float* __restrict__ param_part, const float* __restrict__ X2, const float* __restrict__ Y2,
+                         float* __restrict__ rowda, float* __restrict__ gsave, const float* __restrict__ gload,
+                         const float* __restrict__ goload) {
     constexpr bool QK = MODE != BWD_WRITE, CAUSAL = MODE >= BWD_CQUERY;
     constexpr bool QS = MODE == BWD_QUERY || MODE == BWD_CQUERY, KS = MODE == BWD_KEY || MODE == BWD_CKEY;
     extern __shared__ float lds[];
@@ -346,10 +371,14 @@ __global__ void __launch_bounds__(kThreads)
         const int rows = int(min<int64_t>(kBT, hi - n0));
         __syncthreads();  // the previous tile's reads are done
         if (CAUSAL) {  // the other side's responsibilities, in both layouts
-            load_xT(X2 + size_t(p) * N * dr, n0, rows, dr, xT);
-            __syncthreads();
             float go[4][4];
-            tile_gamma(xT, muT, ivT, cK, K, dr, LDK, r0, m0, rows, go);
+            if (goload) {
+                gamma_from(goload + size_t(p) * N * K, n0, rows, K, r0, m0, go);
+            } else {
+                load_xT(X2 + size_t(p) * N * dr, n0, rows, dr, xT);
+                __syncthreads();
+                tile_gamma(xT, muT, ivT, cK, K, dr, LDK, r0, m0, rows, go);
+            }
             if (m0 < K) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) put4(Go + (r0 + i) * LG + m0, go[i][0], go[i][1], go[i][2], go[i][3]);
@@ -392,7 +421,11 @@ __global__ void __launch_bounds__(kThreads)
 
         // responsibilities (rows t, columns k): direct-form score of Eq. 16, softmax of Eq. 3b
         float gam[4][4];
-        tile_gamma(xT, muT, ivT, cK, K, dr, LDK, r0, m0, rows, gam);
+        if (gload)
+            gamma_from(gload + size_t(p) * N * K, n0, rows, K, r0, m0, gam);
+        else
+            tile_gamma(xT, muT, ivT, cK, K, dr, LDK, r0, m0, rows, gam);
+        if (gsave) gamma_to(gsave + size_t(p) * N * K, n0, rows, K, r0, m0, gam);
         if (MODE == BWD_WRITE) __syncthreads();  // gamma overwrites X^T
         if (m0 < K) {
             if (!KS)
@@ -862,10 +895,14 @@ hipError_t bwd_allow_lds() {
 
 }  // namespace
 
+// Responsibilities of one side, [P][N][K] fp32 (the register-tiled passes keep them between passes).
+size_t gamma_cache_bytes(const Plan& p) { return round_up(size_t(p.P * p.N) * size_t(p.K) * 4, 256); }
+
 size_t f32_backward_extra_bytes(const Plan& p) {
     const size_t E = size_t(p.K) * size_t(p.dv + 1);
     return round_up(size_t(p.P * p.G) * E * 4, 256) + round_up(size_t(p.P) * E * 4, 256) +
-           round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256);
+           round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256) +
+           (bwd_tiled_applies(p) ? gamma_cache_bytes(p) : 0);
 }
 
 hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
@@ -885,6 +922,11 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     float* dmem = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256));
     float* ppart = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256) + round_up(size_t(p.P) * E * 4, 256));
     float* ppart_key = ppart + size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K);
+    // Gamma_K from the write pass, read back by the key pass (tiled passes only)
+    float* gk_cache = reinterpret_cast<float*>(reinterpret_cast<char*>(ppart) +
+                                               round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256));
+    float* none = nullptr;
+    const float* cnone = nullptr;
     const dim3 grid(unsigned(p.G), unsigned(p.P));
     const int Ei = int(E);
     const dim3 cgrid(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P));
@@ -892,9 +934,7 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     if (bwd_tiled_applies(p)) {
         GMA_LAUNCH("f32_bwd_write", f32_bwd_tiled_kernel<BWD_WRITE>, grid, dim3(kThreads),
                    bwd_tiled_lds_bytes(BWD_WRITE, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
-                   static_cast<const float*>(nullptr), eps, static_cast<float*>(nullptr),
-                   static_cast<float*>(nullptr), partials, static_cast<float*>(nullptr),
-                   static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), static_cast<float*>(nullptr));
+                   cnone, eps, none, none, partials, none, cnone, cnone, none, gk_cache, cnone, cnone);
     } else {
         const size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
         GMA_LAUNCH("f32_bwd_write", f32_write_kernel, grid, dim3(kThreads), lds_w, st, XK, V, p.N, H, dr, dv, K,
@@ -906,8 +946,8 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     if (bwd_tiled_applies(p)) {
         GMA_LAUNCH("f32_bwd_query", f32_bwd_tiled_kernel<BWD_QUERY>, grid, dim3(kThreads),
                    bwd_tiled_lds_bytes(BWD_QUERY, K, dr, dv), st, XQ, dO, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
-                   static_cast<const float*>(memory), eps, dXQ, static_cast<float*>(nullptr), dpart, ppart,
-                   static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), static_cast<float*>(nullptr));
+                   static_cast<const float*>(memory), eps, dXQ, none, dpart, ppart, cnone, cnone, none, none, cnone,
+                   cnone);
     } else {
         int T = kTile;
         while (T > 8 && bwd_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
@@ -921,8 +961,8 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     if (bwd_tiled_applies(p)) {
         GMA_LAUNCH("f32_bwd_key", f32_bwd_tiled_kernel<BWD_KEY>, grid, dim3(kThreads),
                    bwd_tiled_lds_bytes(BWD_KEY, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
-                   static_cast<const float*>(dmem), eps, dXK, dV, static_cast<float*>(nullptr), ppart_key,
-                   static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), static_cast<float*>(nullptr));
+                   static_cast<const float*>(dmem), eps, dXK, dV, none, ppart_key, cnone, cnone, none, none,
+                   static_cast<const float*>(gk_cache), cnone);
     } else {
         int T = kTile;
         while (T > 8 && bwd_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
@@ -1267,10 +1307,18 @@ __global__ void __launch_bounds__(kThreads)
 
 }  // namespace
 
+// The causal passes take the register-tiled form where the LDS holds it.
+bool bwdc_tiled_applies(const Plan& p) {
+    const int K = int(p.K), dr = int(p.dr), dv = int(p.dv);
+    return bwd_tiled_applies(p) && bwd_tiled_lds_bytes(BWD_CQUERY, K, dr, dv) <= kMaxLds &&
+           bwd_tiled_lds_bytes(BWD_CKEY, K, dr, dv) <= kMaxLds;
+}
+
 size_t f32_backward_causal_extra_bytes(const Plan& p) {
     const size_t E = size_t(p.K) * size_t(p.dv + 1);
     return round_up(size_t(p.P * p.G) * E * 4, 256) + round_up(size_t(p.P * p.N) * 2 * 4, 256) +
-           round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256);
+           round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256) +
+           (bwdc_tiled_applies(p) ? 2 * gamma_cache_bytes(p) : 0);
 }
 
 hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
@@ -1291,7 +1339,6 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
     hipError_t e = bwd_allow_lds();
     if (e != hipSuccess) return e;
     if ((e = launch_param_tables(p, s2, pi, ws, st)) != hipSuccess) return e;
-    if (e != hipSuccess) return e;
     F32Params v = f32_params_view(p, ws);
     float* states = reinterpret_cast<float*>(ws + p.off_partials);  // segment aggregates, then running memories
     const size_t E = size_t(p.K) * size_t(p.dv + 1);
@@ -1301,23 +1348,28 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
     float* ppart = reinterpret_cast<float*>(extra + round_up(size_t(p.P * p.G) * E * 4, 256) +
                                             round_up(size_t(p.P * p.N) * 2 * 4, 256));
     float* ppart_key = ppart + size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K);
+    // Gamma_K (from the aggregate pass) and Gamma_Q (from the query pass) for the tiled passes
+    float* gk_cache = reinterpret_cast<float*>(reinterpret_cast<char*>(ppart) +
+                                               round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256));
+    float* gq_cache = reinterpret_cast<float*>(reinterpret_cast<char*>(gk_cache) + gamma_cache_bytes(p));
+    float* none = nullptr;
+    const float* cnone = nullptr;
+    const bool tiled = bwdc_tiled_applies(p);
     const dim3 grid(unsigned(p.G), unsigned(p.P));
     const int Ei = int(E);
     const dim3 egrid(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P));
     const int H = int(p.H), dr = int(p.dr), dv = int(p.dv), K = int(p.K), G = int(p.G);
-    if (p.G > 1) {  // segment aggregates of the forward memory (one segment: the prefix writes zeros)
-        if (bwd_tiled_applies(p)) {
-            if ((e = bwd_allow_lds()) != hipSuccess) return e;
-            GMA_LAUNCH("f32_bwdc_aggregate", f32_bwd_tiled_kernel<BWD_WRITE>, grid, dim3(kThreads),
-                       bwd_tiled_lds_bytes(BWD_WRITE, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv,
-                       mu, static_cast<const float*>(nullptr), eps, static_cast<float*>(nullptr),
-                       static_cast<float*>(nullptr), states, static_cast<float*>(nullptr),
-                   static_cast<const float*>(nullptr), static_cast<const float*>(nullptr), static_cast<float*>(nullptr));
-        } else {
-            const size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
-            GMA_LAUNCH("f32_bwdc_aggregate", f32_write_kernel, grid, dim3(kThreads), lds_w, st, XK, V, p.N, H, dr, dv,
-                       K, p.seg, G, v.c, v.inv, mu, states);
-        }
+    // segment aggregates of the forward memory (one segment: the prefix writes zeros); the tiled
+    // passes also take Gamma_K from this pass, so it runs for one segment too
+    if (tiled || (p.G > 1 && bwd_tiled_applies(p))) {
+        GMA_LAUNCH("f32_bwdc_aggregate", f32_bwd_tiled_kernel<BWD_WRITE>, grid, dim3(kThreads),
+                   bwd_tiled_lds_bytes(BWD_WRITE, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
+                   cnone, eps, none, none, states, none, cnone, cnone, none, tiled ? gk_cache : none, cnone, cnone);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else if (p.G > 1) {
+        const size_t lds_w = size_t(kTile) * (p.dr + p.K + p.dv) * sizeof(float);
+        GMA_LAUNCH("f32_bwdc_aggregate", f32_write_kernel, grid, dim3(kThreads), lds_w, st, XK, V, p.N, H, dr, dv, K,
+                   p.seg, G, v.c, v.inv, mu, states);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     GMA_LAUNCH("f32_bwdc_prefix", f32_prefix_kernel, egrid, dim3(kThreads), 0, st, states, G, Ei,
@@ -1336,21 +1388,18 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
         while (T > 8 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
     }
     const size_t lds = bwdc_lds_bytes(T, dr, dv, K) + (fast ? fast_extra : 0);
-    float* none = nullptr;
-    const float* cnone = nullptr;
-    const bool tiled = bwd_tiled_applies(p) && bwd_tiled_lds_bytes(BWD_CQUERY, K, dr, dv) <= kMaxLds &&
-                       bwd_tiled_lds_bytes(BWD_CKEY, K, dr, dv) <= kMaxLds;
     if (tiled) {  // register-tiled passes with the running memory in LDS
-        if ((e = bwd_allow_lds()) != hipSuccess) return e;
         GMA_LAUNCH("f32_bwdc_query", f32_bwd_tiled_kernel<BWD_CQUERY>, grid, dim3(kThreads),
                    bwd_tiled_lds_bytes(BWD_CQUERY, K, dr, dv), st, XQ, dO, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
-                   static_cast<const float*>(states), eps, dXQ, none, seg_part, ppart, XK, V, rowda);
+                   static_cast<const float*>(states), eps, dXQ, none, seg_part, ppart, XK, V, rowda, gq_cache, cnone,
+                   static_cast<const float*>(gk_cache));
         if ((e = hipGetLastError()) != hipSuccess) return e;
         GMA_LAUNCH("f32_bwdc_suffix", f32_suffix_kernel, egrid, dim3(kThreads), 0, st, seg_part, G, Ei);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         GMA_LAUNCH("f32_bwdc_key", f32_bwd_tiled_kernel<BWD_CKEY>, grid, dim3(kThreads),
                    bwd_tiled_lds_bytes(BWD_CKEY, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
-                   static_cast<const float*>(seg_part), eps, dXK, dV, none, ppart_key, XQ, dO, rowda);
+                   static_cast<const float*>(seg_part), eps, dXK, dV, none, ppart_key, XQ, dO, rowda, none,
+                   static_cast<const float*>(gk_cache), static_cast<const float*>(gq_cache));
         if ((e = hipGetLastError()) != hipSuccess) return e;
         return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
     }
