@@ -246,8 +246,9 @@ gma_status_t gma_responsibility_diagnostics(const void* X, gma_dtype_t x_dtype, 
  *   gradient outputs are overwritten, not accumulated into.
  * Workspace: gma_workspace_size(GMA_OP_BACKWARD_BIDIR, shape, io_dtype, 0, ...): the forward's
  * memory and its split partials, the same for (dVt, dZ), and per-split parameter partials,
- * reduced in a fixed order (bitwise reproducible); with bf16 I/O also fp32 copies of the four
- * inputs and three outputs (O(B H N (d_r + d_v)) bytes).  Sizes as for the fp32 forward (d_r, d_v
+ * reduced in a fixed order (bitwise reproducible); for K, d_r, d_v <= 64 (multiples of 4) the
+ * responsibilities of the keys, which the key pass reads back (B H N K fp32); with bf16 I/O also
+ * fp32 copies of the four inputs and three outputs (O(B H N (d_r + d_v)) bytes).  Sizes as for the fp32 forward (d_r, d_v
  * <= 128, K <= 256 at either I/O dtype); alignment and errors as for gma_forward_bidir; with no
  * rows (B N = 0) the parameter gradients are zeros.
  */
@@ -269,7 +270,8 @@ gma_status_t gma_backward_bidir(const void* XQ, const void* XK, const void* V, g
  * the softmax Jacobian, the routing-vector and the parameter gradients are those of
  * gma_backward_bidir.  Shapes, dtypes, outputs, workspace
  * (gma_workspace_size(GMA_OP_BACKWARD_CAUSAL, shape, io_dtype, 0, ...), which also holds D_i and
- * a_i of every position) and errors as for gma_backward_bidir.
+ * a_i of every position and, where the register-tiled passes apply, the responsibilities of both
+ * sides, 2 B H N K fp32) and errors as for gma_backward_bidir.
  */
 gma_status_t gma_backward_causal(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
                                  const float* mu, const float* sigma2, const float* pi, float eps,
