@@ -35,7 +35,8 @@ def _score_grads(x, ds, mu, s2, pi):
 
 def backward_bidir(XQ, XK, V, mu, sigma2, pi, eps, dO) -> dict:
     """Gradients of <dO, O> for the bidirectional forward O (Sec. 3.3): dXQ, dXK [B,H,N,d_r],
-    dV [B,H,N,d_v], dmu, dsigma2 [H,K,d_r], dpi [H,K]."""
+    dV [B,H,N,d_v], dmu, dsigma2 [H,K,d_r], dpi [H,K].  The same formulas give the cross-attention
+    backward (Sec. 3, "Cross-attention"): XQ, dO and dXQ then have N_q rows, XK, V, dXK, dV N_k."""
     from . import _f64, responsibilities
     XQ, XK, V, dO = (_f64(t) for t in (XQ, XK, V, dO))
     mu, s2, pi = (_f64(t) for t in (mu, sigma2, pi))

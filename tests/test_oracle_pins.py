@@ -699,3 +699,28 @@ def test_backward_causal_last_row_is_bidirectional():
     b = oracle.backward.backward_bidir(xq, xk, v, mu, s2, pi, 1e-3, do)
     for key in a:
         np.testing.assert_allclose(a[key], b[key], rtol=1e-10, atol=1e-13, err_msg=key)
+
+
+def test_backward_cross_matches_finite_differences():
+    """Cross-attention (queries of one length, context of another): the bidirectional backward's
+    formulas hold with N_q query rows and N_k context rows; <grad, u> equals the central
+    difference of <dO, O> through the cross forward oracle for every input."""
+    rng = np.random.default_rng(67)
+    B, H, Nq, Nk, dr, dv, K = 2, 2, 7, 11, 3, 4, 5
+    xq = rng.standard_normal((B, H, Nq, dr))
+    _, xk, v, mu, s2, pi = rand_problem(rng, B, H, Nk, dr, dv, K)
+    do = rng.standard_normal((B, H, Nq, dv))
+    eps = 1e-3
+    g = oracle.backward.backward_bidir(xq, xk, v, mu, s2, pi, eps, do)
+    assert g["dXQ"].shape == xq.shape and g["dXK"].shape == xk.shape and g["dV"].shape == v.shape
+    args = {"dXQ": xq, "dXK": xk, "dV": v, "dmu": mu, "dsigma2": s2, "dpi": pi}
+    order = ["dXQ", "dXK", "dV", "dmu", "dsigma2", "dpi"]
+    for key in order:
+        u = rng.standard_normal(args[key].shape)
+        h = 1e-6 * (np.abs(args[key]).max() + 1.0)
+        def loss(sign):
+            a = [args[k].copy() for k in order]
+            a[order.index(key)] = a[order.index(key)] + sign * h * u
+            return float((do * oracle.forward_cross(a[0], a[1], a[2], a[3], a[4], a[5], eps)).sum())
+        fd = (loss(1.0) - loss(-1.0)) / (2 * h)
+        np.testing.assert_allclose((g[key] * u).sum(), fd, rtol=2e-6, atol=1e-9, err_msg=key)
