@@ -26,7 +26,7 @@ GMA_OP_RESPONSIBILITIES, GMA_OP_BIDIR, GMA_OP_CAUSAL, GMA_OP_DIAGNOSTICS = 0, 1,
 GMA_OP_BACKWARD_BIDIR, GMA_OP_BACKWARD_CAUSAL = 4, 5
 EXPORTED = ["gma_status_string", "gma_workspace_size", "gma_responsibilities", "gma_forward_bidir",
             "gma_forward_causal", "gma_forward_causal_state", "gma_cross_workspace_size", "gma_forward_cross", "gma_responsibility_diagnostics", "gma_backward_bidir",
-            "gma_backward_causal", "gma_profiling",
+            "gma_backward_causal", "gma_backward_cross_workspace_size", "gma_backward_cross", "gma_profiling",
             "gma_profiling_collect", "gma_set_wait_limit"]
 WAIT_LIMIT_DEFAULT = 1 << 18  # GMA_WAIT_LIMIT_DEFAULT
 
@@ -92,6 +92,11 @@ def load() -> ctypes.CDLL:
             lib.gma_backward_bidir.restype = i32
             lib.gma_backward_causal.argtypes = lib.gma_backward_bidir.argtypes
             lib.gma_backward_causal.restype = i32
+            lib.gma_backward_cross_workspace_size.argtypes = [xshp, i32, ctypes.POINTER(sz)]
+            lib.gma_backward_cross_workspace_size.restype = i32
+            lib.gma_backward_cross.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, xshp,
+                                               vp, sz, vp]
+            lib.gma_backward_cross.restype = i32
             lib.gma_profiling.argtypes = [ctypes.c_int]
             lib.gma_profiling.restype = i32
             lib.gma_profiling_collect.argtypes = [ctypes.POINTER(KernelStat), ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
@@ -267,6 +272,35 @@ def gma_backward_causal(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, mu:
     as gma_backward_bidir."""
     return _backward(GMA_OP_BACKWARD_CAUSAL, "gma_backward_causal", xq, xk, v, mu, sigma2, pi, d_o, eps, out,
                      workspace, stream)
+
+
+def gma_backward_cross_workspace_size(B: int, H: int, N_q: int, N_k: int, d_r: int, d_v: int, K: int,
+                                      io_dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().gma_backward_cross_workspace_size(ctypes.byref(CrossShape(B, H, N_q, N_k, d_r, d_v, K)), io_dtype,
+                                                    ctypes.byref(out)), "gma_backward_cross_workspace_size")
+    return int(out.value)
+
+
+def gma_backward_cross(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, mu: torch.Tensor,
+                       sigma2: torch.Tensor, pi: torch.Tensor, d_o: torch.Tensor, eps: float = 1e-6,
+                       out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradients of <d_o, O> for the cross-attention forward O (queries xq [B,H,N_q,d_r], context
+    xk [B,H,N_k,d_r], v [B,H,N_k,d_v]; Sec. 3, Sec. 4.1); outputs as gma_backward_bidir."""
+    B, H, Nq, dr = xq.shape
+    Nk, dv = xk.shape[2], v.shape[-1]
+    K = mu.shape[1]
+    io = _dtype_code(xq.dtype)
+    if out is None:
+        out = {"dXQ": torch.empty_like(xq), "dXK": torch.empty_like(xk), "dV": torch.empty_like(v),
+               "dmu": torch.empty_like(mu), "dsigma2": torch.empty_like(sigma2), "dpi": torch.empty_like(pi)}
+    ws = _workspace(gma_backward_cross_workspace_size(B, H, Nq, Nk, dr, dv, K, io), xq.device, workspace)
+    _check(load().gma_backward_cross(_ptr(xq), _ptr(xk), _ptr(v), io, _ptr(mu), _ptr(sigma2), _ptr(pi), float(eps),
+                                     _ptr(d_o), _ptr(out["dXQ"]), _ptr(out["dXK"]), _ptr(out["dV"]), _ptr(out["dmu"]),
+                                     _ptr(out["dsigma2"]), _ptr(out["dpi"]),
+                                     ctypes.byref(CrossShape(B, H, Nq, Nk, dr, dv, K)), _ptr(ws), ws.numel(),
+                                     _stream(stream)), "gma_backward_cross")
+    return out
 
 
 def _backward(op, name, xq, xk, v, mu, sigma2, pi, d_o, eps, out, workspace, stream) -> dict:

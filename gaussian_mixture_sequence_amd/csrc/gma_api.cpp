@@ -55,11 +55,20 @@ gma_status_t check_dims(gma_op_t op, const gma_shape_t& s, gma_dtype_t io) {
 void layout(Plan* pl);
 
 // fp32 copies of X_Q, X_K, V, dO (inputs) and dX_Q, dX_K, dV (outputs) for a bf16 backward, in
-// that order after the fp32 passes' regions.
-size_t backward_stage_bytes(const Plan& p) {
-    const size_t r = round_up(size_t(p.P * p.N * p.dr) * 4, 256), v = round_up(size_t(p.P * p.N * p.dv) * 4, 256);
-    return 4 * r + 3 * v;
+// that order after the fp32 passes' regions (query-side arrays of N_q rows, key-side of N).
+struct StageLayout {
+    size_t off[7];  // XQ, XK, V, dO, dXQ, dXK, dV
+    size_t total;
+};
+StageLayout stage_layout(const Plan& p) {
+    const size_t rq = round_up(size_t(p.P * p.Nq * p.dr) * 4, 256), rk = round_up(size_t(p.P * p.N * p.dr) * 4, 256);
+    const size_t vq = round_up(size_t(p.P * p.Nq * p.dv) * 4, 256), vk = round_up(size_t(p.P * p.N * p.dv) * 4, 256);
+    const size_t sz[7] = {rq, rk, vk, vq, rq, rk, vk};
+    StageLayout l{};
+    for (int i = 0; i < 7; ++i) l.off[i] = l.total, l.total += sz[i];
+    return l;
 }
+size_t backward_stage_bytes(const Plan& p) { return stage_layout(p).total; }
 
 gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_t chunk, Plan* pl) {
     if (op != GMA_OP_RESPONSIBILITIES && op != GMA_OP_BIDIR && op != GMA_OP_CAUSAL && op != GMA_OP_DIAGNOSTICS &&
@@ -191,6 +200,22 @@ gma_status_t make_cross_plan(const gma_cross_shape_t& s, gma_dtype_t io, Plan* p
     p.G = std::max<int64_t>(1, std::max(cdiv(p.N, p.seg), cdiv(p.Nq, p.seg_q)));
     layout(&p);
     *pl = p;
+    return GMA_OK;
+}
+
+// Backward of cross-attention: the cross plan in fp32 (split partials and memory over the
+// context), then the bidirectional backward's scratch, then the bf16 staging if any.
+gma_status_t make_backward_cross_plan(const gma_cross_shape_t& s, gma_dtype_t io, Plan* pl) {
+    if (io != GMA_F32 && io != GMA_BF16) return GMA_ERR_BAD_VALUE;
+    gma_status_t st = make_cross_plan(s, GMA_F32, pl);
+    if (st != GMA_OK) return st;
+    pl->op = GMA_OP_BACKWARD_BIDIR;
+    pl->total += f32_backward_extra_bytes(*pl);
+    pl->off_stage = pl->total;
+    if (io == GMA_BF16) {
+        pl->io = io;
+        pl->total += backward_stage_bytes(*pl);
+    }
     return GMA_OK;
 }
 
@@ -402,6 +427,52 @@ gma_status_t gma_responsibility_diagnostics(const void* X, gma_dtype_t x_dtype, 
                                           static_cast<char*>(workspace), stream));
 }
 
+// Validation, bf16 staging and dispatch of the three backward entry points; `p` is their plan
+// (query-side arrays have p.Nq rows, key-side arrays p.N).
+static gma_status_t backward_run(const Plan& p, const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                                 const float* mu, const float* sigma2, const float* pi, float eps, const void* dO,
+                                 void* dXQ, void* dXK, void* dV, float* dmu, float* dsigma2, float* dpi,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if ((!dmu || !dsigma2 || !dpi) && p.H > 0) return GMA_ERR_NULL_POINTER;
+    if ((!XQ || !dO || !dXQ) && p.P > 0 && p.Nq > 0) return GMA_ERR_NULL_POINTER;  // tensors with elements
+    if ((!XK || !V || !dXK || !dV) && p.P > 0 && p.N > 0) return GMA_ERR_NULL_POINTER;
+    if (!(eps > 0.0f) || !std::isfinite(eps)) return GMA_ERR_BAD_VALUE;
+    for (const void* q : {XQ, XK, V, (const void*)mu, (const void*)sigma2, (const void*)pi, dO, (const void*)dXQ,
+                          (const void*)dXK, (const void*)dV, (const void*)dmu, (const void*)dsigma2, (const void*)dpi})
+        if (!gma::aligned16(q)) return GMA_ERR_MISALIGNED;
+    gma_status_t st = check_ws(p, workspace, workspace_bytes);
+    if (st != GMA_OK) return st;
+    const float *q = static_cast<const float*>(XQ), *k = static_cast<const float*>(XK),
+                *v = static_cast<const float*>(V), *d = static_cast<const float*>(dO);
+    float *dq = static_cast<float*>(dXQ), *dk = static_cast<float*>(dXK), *dvv = static_cast<float*>(dV);
+    char* ws = static_cast<char*>(workspace);
+    const bool staged = io_dtype == GMA_BF16 && p.P > 0 && (p.N > 0 || p.Nq > 0);
+    const size_t nrq = size_t(p.P * p.Nq * p.dr), nrk = size_t(p.P * p.N * p.dr);
+    const size_t nvq = size_t(p.P * p.Nq * p.dv), nvk = size_t(p.P * p.N * p.dv);
+    hipError_t e = hipSuccess;
+    if (staged) {  // fp32 copies of the inputs; the passes write fp32 outputs next to them
+        const gma::StageLayout l = gma::stage_layout(p);
+        char* sg = ws + p.off_stage;
+        float *q32 = reinterpret_cast<float*>(sg + l.off[0]), *k32 = reinterpret_cast<float*>(sg + l.off[1]),
+              *v32 = reinterpret_cast<float*>(sg + l.off[2]), *d32 = reinterpret_cast<float*>(sg + l.off[3]);
+        dq = reinterpret_cast<float*>(sg + l.off[4]);
+        dk = reinterpret_cast<float*>(sg + l.off[5]);
+        dvv = reinterpret_cast<float*>(sg + l.off[6]);
+        if ((e = gma::widen_bf16(XQ, q32, nrq, stream)) != hipSuccess || (e = gma::widen_bf16(XK, k32, nrk, stream)) != hipSuccess ||
+            (e = gma::widen_bf16(V, v32, nvk, stream)) != hipSuccess || (e = gma::widen_bf16(dO, d32, nvq, stream)) != hipSuccess)
+            return launch_status(e);
+        q = q32, k = k32, v = v32, d = d32;
+    }
+    if (p.op == GMA_OP_BACKWARD_CAUSAL)
+        e = gma::f32_backward_causal(p, q, k, v, mu, sigma2, pi, eps, d, dq, dk, dvv, dmu, dsigma2, dpi, ws, stream);
+    else
+        e = gma::f32_backward_bidir(p, q, k, v, mu, sigma2, pi, eps, d, dq, dk, dvv, dmu, dsigma2, dpi, ws, stream);
+    if (e != hipSuccess || !staged) return launch_status(e);
+    if ((e = gma::narrow_to_bf16(dq, dXQ, nrq, stream)) != hipSuccess || (e = gma::narrow_to_bf16(dk, dXK, nrk, stream)) != hipSuccess)
+        return launch_status(e);
+    return launch_status(gma::narrow_to_bf16(dvv, dV, nvk, stream));
+}
+
 static gma_status_t backward_common(gma_op_t op, const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
                                     const float* mu, const float* sigma2, const float* pi, float eps, const void* dO,
                                     void* dXQ, void* dXK, void* dV, float* dmu, float* dsigma2, float* dpi,
@@ -411,41 +482,8 @@ static gma_status_t backward_common(gma_op_t op, const void* XQ, const void* XK,
     Plan p;
     gma_status_t st = gma::make_plan(op, *shape, io_dtype, 0, &p);
     if (st != GMA_OK) return st;
-    if ((!dmu || !dsigma2 || !dpi) && p.H > 0) return GMA_ERR_NULL_POINTER;
-    if ((!XQ || !XK || !V || !dO || !dXQ || !dXK || !dV) && p.P > 0 && p.N > 0) return GMA_ERR_NULL_POINTER;
-    if (!(eps > 0.0f) || !std::isfinite(eps)) return GMA_ERR_BAD_VALUE;
-    for (const void* q : {XQ, XK, V, (const void*)mu, (const void*)sigma2, (const void*)pi, dO, (const void*)dXQ,
-                          (const void*)dXK, (const void*)dV, (const void*)dmu, (const void*)dsigma2, (const void*)dpi})
-        if (!gma::aligned16(q)) return GMA_ERR_MISALIGNED;
-    if ((st = check_ws(p, workspace, workspace_bytes)) != GMA_OK) return st;
-    const float *q = static_cast<const float*>(XQ), *k = static_cast<const float*>(XK),
-                *v = static_cast<const float*>(V), *d = static_cast<const float*>(dO);
-    float *dq = static_cast<float*>(dXQ), *dk = static_cast<float*>(dXK), *dvv = static_cast<float*>(dV);
-    char* ws = static_cast<char*>(workspace);
-    const bool staged = io_dtype == GMA_BF16 && p.P > 0 && p.N > 0;
-    const size_t nr = size_t(p.P * p.N * p.dr), nv = size_t(p.P * p.N * p.dv);
-    hipError_t e = hipSuccess;
-    if (staged) {  // fp32 copies of the inputs; the passes write fp32 outputs next to them
-        const size_t r = gma::round_up(nr * 4, 256), vb = gma::round_up(nv * 4, 256);
-        char* sg = ws + p.off_stage;
-        float *q32 = reinterpret_cast<float*>(sg), *k32 = reinterpret_cast<float*>(sg + r),
-              *v32 = reinterpret_cast<float*>(sg + 2 * r), *d32 = reinterpret_cast<float*>(sg + 2 * r + vb);
-        dq = reinterpret_cast<float*>(sg + 2 * r + 2 * vb);
-        dk = reinterpret_cast<float*>(sg + 3 * r + 2 * vb);
-        dvv = reinterpret_cast<float*>(sg + 4 * r + 2 * vb);
-        if ((e = gma::widen_bf16(XQ, q32, nr, stream)) != hipSuccess || (e = gma::widen_bf16(XK, k32, nr, stream)) != hipSuccess ||
-            (e = gma::widen_bf16(V, v32, nv, stream)) != hipSuccess || (e = gma::widen_bf16(dO, d32, nv, stream)) != hipSuccess)
-            return launch_status(e);
-        q = q32, k = k32, v = v32, d = d32;
-    }
-    if (op == GMA_OP_BACKWARD_CAUSAL)
-        e = gma::f32_backward_causal(p, q, k, v, mu, sigma2, pi, eps, d, dq, dk, dvv, dmu, dsigma2, dpi, ws, stream);
-    else
-        e = gma::f32_backward_bidir(p, q, k, v, mu, sigma2, pi, eps, d, dq, dk, dvv, dmu, dsigma2, dpi, ws, stream);
-    if (e != hipSuccess || !staged) return launch_status(e);
-    if ((e = gma::narrow_to_bf16(dq, dXQ, nr, stream)) != hipSuccess || (e = gma::narrow_to_bf16(dk, dXK, nr, stream)) != hipSuccess)
-        return launch_status(e);
-    return launch_status(gma::narrow_to_bf16(dvv, dV, nv, stream));
+    return backward_run(p, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, dO, dXQ, dXK, dV, dmu, dsigma2, dpi, workspace,
+                        workspace_bytes, stream);
 }
 
 gma_status_t gma_backward_bidir(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
@@ -462,6 +500,27 @@ gma_status_t gma_backward_causal(const void* XQ, const void* XK, const void* V, 
                                  const gma_shape_t* shape, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return backward_common(GMA_OP_BACKWARD_CAUSAL, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, dO, dXQ, dXK, dV, dmu,
                            dsigma2, dpi, shape, workspace, workspace_bytes, stream);
+}
+
+gma_status_t gma_backward_cross_workspace_size(const gma_cross_shape_t* shape, gma_dtype_t io_dtype, size_t* bytes_out) {
+    if (!shape || !bytes_out) return GMA_ERR_NULL_POINTER;
+    Plan p;
+    gma_status_t st = gma::make_backward_cross_plan(*shape, io_dtype, &p);
+    if (st != GMA_OK) return st;
+    *bytes_out = p.total;
+    return GMA_OK;
+}
+
+gma_status_t gma_backward_cross(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype, const float* mu,
+                                const float* sigma2, const float* pi, float eps, const void* dO, void* dXQ, void* dXK,
+                                void* dV, float* dmu, float* dsigma2, float* dpi, const gma_cross_shape_t* shape,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!mu || !sigma2 || !pi || !shape) return GMA_ERR_NULL_POINTER;
+    Plan p;
+    gma_status_t st = gma::make_backward_cross_plan(*shape, io_dtype, &p);
+    if (st != GMA_OK) return st;
+    return backward_run(p, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, dO, dXQ, dXK, dV, dmu, dsigma2, dpi, workspace,
+                        workspace_bytes, stream);
 }
 
 gma_status_t gma_cross_workspace_size(const gma_cross_shape_t* shape, gma_dtype_t io_dtype, size_t* bytes_out) {

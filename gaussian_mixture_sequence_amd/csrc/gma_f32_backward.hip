@@ -909,7 +909,9 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
                               const float* s2, const float* pi, float eps, const float* dO, float* dXQ, float* dXK,
                               float* dV, float* dmu, float* ds2, float* dpi, char* ws, hipStream_t st) {
     if (p.H == 0) return hipSuccess;
-    if (p.P == 0 || p.N == 0) return reduce_params(p, nullptr, 0, nullptr, pi, dmu, ds2, dpi, st);  // zero gradients
+    // no rows on either side: zero parameter gradients (one empty side of cross-attention runs the
+    // passes, which give the zeros of that case: an empty context leaves O = 0)
+    if (p.P == 0 || (p.N == 0 && p.Nq == 0)) return reduce_params(p, nullptr, 0, nullptr, pi, dmu, ds2, dpi, st);
     hipError_t e = bwd_allow_lds();
     if (e != hipSuccess) return e;
     if ((e = launch_param_tables(p, s2, pi, ws, st)) != hipSuccess) return e;
@@ -945,14 +947,14 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (bwd_tiled_applies(p)) {
         GMA_LAUNCH("f32_bwd_query", f32_bwd_tiled_kernel<BWD_QUERY>, grid, dim3(kThreads),
-                   bwd_tiled_lds_bytes(BWD_QUERY, K, dr, dv), st, XQ, dO, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
+                   bwd_tiled_lds_bytes(BWD_QUERY, K, dr, dv), st, XQ, dO, p.Nq, H, dr, dv, K, p.seg_q, G, v.c, v.inv, mu,
                    static_cast<const float*>(memory), eps, dXQ, none, dpart, ppart, cnone, cnone, none, none, cnone,
                    cnone);
     } else {
         int T = kTile;
         while (T > 8 && bwd_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
         GMA_LAUNCH("f32_bwd_query", f32_bwd_side_kernel<true>, grid, dim3(kThreads), bwd_lds_bytes(T, dr, dv, K), st,
-                   XQ, dO, p.N, H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, static_cast<const float*>(memory), eps, dXQ,
+                   XQ, dO, p.Nq, H, dr, dv, K, p.seg_q, G, T, v.c, v.inv, mu, static_cast<const float*>(memory), eps, dXQ,
                    static_cast<float*>(nullptr), dpart, ppart);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;

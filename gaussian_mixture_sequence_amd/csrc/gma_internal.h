@@ -62,6 +62,8 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
 // Cross-attention plan: a bidirectional plan over the context (N = N_k) whose read covers
 // N_q query rows in the same number of splits.
 gma_status_t make_cross_plan(const gma_cross_shape_t& s, gma_dtype_t io, Plan* plan);
+// Backward of cross-attention: the cross plan (fp32) with the backward's scratch and staging.
+gma_status_t make_backward_cross_plan(const gma_cross_shape_t& s, gma_dtype_t io, Plan* plan);
 
 // ---- fp32 path (gma_f32.hip) ---------------------------------------------------
 hipError_t f32_responsibilities(const Plan& p, const float* X, const float* mu, const float* s2,

@@ -280,6 +280,25 @@ gma_status_t gma_backward_causal(const void* XQ, const void* XK, const void* V, 
                                  hipStream_t stream);
 
 /*
+ * Backward pass of cross-attention (gma_forward_cross): the gradients of <dO, O> with the
+ * formulas of gma_backward_bidir, Gamma_Q taken over the N_q query rows and Gamma_K over the N_k
+ * context rows (Sec. 3 "Cross-attention"; Sec. 4.1 Eq. 17-20).
+ *   XQ, dXQ [B,H,N_q,d_r]; dO [B,H,N_q,d_v]; XK, dXK [B,H,N_k,d_r]; V, dV [B,H,N_k,d_v] in io_dtype;
+ *   mu, sigma2, pi and their gradients fp32, as for gma_backward_bidir.
+ * An empty context (N_k = 0) gives O = 0, so dXQ and the parameter gradients are zeros; no queries
+ * (N_q = 0) give zeros everywhere.  A side without rows may come without storage.
+ * Workspace: gma_backward_cross_workspace_size (same validation and errors as the call).  With
+ * N_q = N_k it equals the bidirectional backward on the same tensors.
+ */
+gma_status_t gma_backward_cross_workspace_size(const gma_cross_shape_t* shape, gma_dtype_t io_dtype,
+                                               size_t* bytes_out);
+gma_status_t gma_backward_cross(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                                const float* mu, const float* sigma2, const float* pi, float eps,
+                                const void* dO, void* dXQ, void* dXK, void* dV, float* dmu, float* dsigma2,
+                                float* dpi, const gma_cross_shape_t* shape, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Kernel timing (optional tracing).  While enabled, every kernel the library launches is
  * bracketed by a pair of hipEvents recorded on the launch stream; gma_profiling_collect
  * waits for the recorded events, adds each launch's elapsed time to a per-kernel total,

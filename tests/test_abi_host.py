@@ -271,3 +271,38 @@ def test_backward_argument_errors(lib, causal):
     # no heads: nothing to write, returns before any HIP call
     sh0 = gb.Shape(2, 0, 64, 16, 32, 8)
     assert call(s=ctypes.byref(sh0), nb=ws_size(Bw, 2, 0, 64, 16, 32, 8, F)[1], dmu=None, dpi=None) == OK
+
+
+def test_backward_cross_argument_errors(lib):
+    F, BF = gb.GMA_F32, gb.GMA_BF16
+    size = lib.gma_backward_cross_workspace_size
+
+    def ws(shape, io=F):
+        out = ctypes.c_size_t(0)
+        return size(ctypes.byref(gb.CrossShape(*shape)), io, ctypes.byref(out)), out.value
+
+    assert ws((8, 8, 4096, 16384, 64, 64, 64))[0] == OK
+    assert ws((8, 8, 4096, 16384, 64, 64, 64), BF)[0] == OK
+    assert ws((1, 1, 8, 8, 129, 32, 8))[0] == UNSUP
+    assert ws((1, 1, -1, 8, 16, 32, 8))[0] == SHAPE
+    assert ws((1, 1, 8, 8, 16, 32, 8), 5)[0] == VALUE
+    assert size(None, F, ctypes.byref(ctypes.c_size_t())) == NULLP
+    # N_q = N_k: the bidirectional backward's workspace
+    same = ctypes.c_size_t(0)
+    assert lib.gma_workspace_size(gb.GMA_OP_BACKWARD_BIDIR, ctypes.byref(gb.Shape(2, 3, 700, 16, 32, 8)), F, 0,
+                                  ctypes.byref(same)) == OK
+    assert ws((2, 3, 700, 700, 16, 32, 8))[1] == same.value
+    shape = (2, 3, 64, 100, 16, 32, 8)
+    need = ws(shape)[1]
+    sh = ctypes.byref(gb.CrossShape(*shape))
+
+    def call(xq=FAKE, xk=FAKE, d_o=FAKE, dv=FAKE, eps=1e-6, nb=need, s=sh):
+        return lib.gma_backward_cross(xq, xk, FAKE, F, FAKE, FAKE, FAKE, eps, d_o, FAKE, FAKE, dv, FAKE, FAKE, FAKE,
+                                      s, FAKE, nb, None)
+
+    assert call(xq=None) == NULLP
+    assert call(xk=None) == NULLP
+    assert call(dv=None) == NULLP
+    assert call(d_o=FAKE + 4) == MISAL
+    assert call(eps=0.0) == VALUE
+    assert call(nb=need - 1) == WS

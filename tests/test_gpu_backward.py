@@ -264,3 +264,61 @@ def test_backward_ignores_workspace_contents(causal, dims):
         torch.cuda.synchronize()
         for k in KEYS:
             assert torch.equal(clean[k], dirty[k]), k
+
+
+# ---------------------------------------------------------------------------- cross-attention
+
+
+def cross_case(Nq, Nk, seed, **kw):
+    return WORKLOADS["bidir_small_f32"].with_(name="bwdx", N=Nq, n_ctx=Nk, seed=seed, **dict(dict(B=1, H=2), **kw))
+
+
+def xid(w):
+    return "%s-q%d-k%d-dr%d-dv%d-K%d" % (w.dtype, w.N, w.n_ctx, w.d_r, w.d_v, w.K)
+
+
+CROSS_CASES = [
+    cross_case(200, 333, 131),                                   # tiled
+    cross_case(1000, 3000, 132, d_r=64, d_v=64, K=64),           # longer context, several splits
+    cross_case(3000, 700, 133, d_r=32, d_v=64, K=64),            # more queries than keys
+    cross_case(257, 100, 134, d_r=7, d_v=5, K=13),               # general kernels
+    cross_case(130, 450, 135, B=1, H=1, d_r=128, d_v=128, K=256),
+    cross_case(300, 0, 136),                                     # empty context
+    cross_case(0, 300, 137),                                     # no queries
+    cross_case(1000, 3000, 138, d_r=64, d_v=64, K=64, dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("w", CROSS_CASES, ids=xid)
+def test_backward_cross_parity(w):
+    inp = make_inputs(w)
+    d_o = upstream(w, w.seed + 1000)
+    if w.dtype == "bf16":
+        d_o = d_o.bfloat16()
+    d = to_device(inp)
+    g = gb.gma_backward_cross(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], d_o.cuda(), w.eps)
+    torch.cuda.synchronize()
+    ref = run_oracle(w, inp, d_o)
+    for k in KEYS:
+        got = to_np(g[k])
+        assert got.shape == ref[k].shape and np.isfinite(got).all(), k
+        tol = TOL_BWD_BF16 if (w.dtype == "bf16" and k in ("dXQ", "dXK", "dV")) else TOL_BWD
+        if ref[k].size == 0:
+            continue
+        if np.abs(ref[k]).max() == 0.0:
+            assert not got.any(), k   # exact zeros: an empty side
+        else:
+            assert tensor_error(got, ref[k]) <= tol, (k, tensor_error(got, ref[k]))
+
+
+def test_backward_cross_equal_lengths_is_bidir_bitwise():
+    """With N_q = N_k the cross backward runs the bidirectional backward's plan: identical bits."""
+    w = cross_case(2900, 2900, 139, B=2, H=3, d_r=32, d_v=32, K=32)
+    inp = make_inputs(w)
+    d = to_device(inp)
+    d_o = upstream(w, 1139).cuda()
+    args = (d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], d_o, w.eps)
+    a, b = gb.gma_backward_cross(*args), gb.gma_backward_bidir(*args)
+    torch.cuda.synchronize()
+    for k in KEYS:
+        assert torch.equal(a[k], b[k]), k
