@@ -1377,19 +1377,6 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
     GMA_LAUNCH("f32_bwdc_prefix", f32_prefix_kernel, egrid, dim3(kThreads), 0, st, states, G, Ei,
                static_cast<const float*>(nullptr), K, dv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // FAST (tables and running memory in LDS) with 64- or 32-position tiles when two workgroups
-    // still fit a CU; otherwise the general form: 64-position tiles when two fit, else the largest
-    // tile that lets two fit (down to 32), else the largest that fits at all
-    const size_t fast_extra = size_t(2 * K * (dr + 1) + 2 * K + K * (dv + 1)) * sizeof(float);
-    int T = kTile;
-    bool fast = false;
-    for (int t = kTile; t >= 32 && !fast; t /= 2)
-        if (bwdc_lds_bytes(t, dr, dv, K) + fast_extra <= kMaxLds / 2) fast = true, T = t;
-    if (!fast) {
-        while (T > 32 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds / 2) T /= 2;
-        while (T > 8 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
-    }
-    const size_t lds = bwdc_lds_bytes(T, dr, dv, K) + (fast ? fast_extra : 0);
     if (tiled) {  // register-tiled passes with the running memory in LDS
         GMA_LAUNCH("f32_bwdc_query", f32_bwd_tiled_kernel<BWD_CQUERY>, grid, dim3(kThreads),
                    bwd_tiled_lds_bytes(BWD_CQUERY, K, dr, dv), st, XQ, dO, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
@@ -1405,7 +1392,19 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
         if ((e = hipGetLastError()) != hipSuccess) return e;
         return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
     }
-    (void)cnone;
+    // one element per thread: FAST (tables and running memory in LDS) with 64- or 32-position tiles when two workgroups
+    // still fit a CU; otherwise the general form: 64-position tiles when two fit, else the largest
+    // tile that lets two fit (down to 32), else the largest that fits at all
+    const size_t fast_extra = size_t(2 * K * (dr + 1) + 2 * K + K * (dv + 1)) * sizeof(float);
+    int T = kTile;
+    bool fast = false;
+    for (int t = kTile; t >= 32 && !fast; t /= 2)
+        if (bwdc_lds_bytes(t, dr, dv, K) + fast_extra <= kMaxLds / 2) fast = true, T = t;
+    if (!fast) {
+        while (T > 32 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds / 2) T /= 2;
+        while (T > 8 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
+    }
+    const size_t lds = bwdc_lds_bytes(T, dr, dv, K) + (fast ? fast_extra : 0);
     if (fast)
         GMA_LAUNCH("f32_bwdc_query", (f32_bwdc_kernel<true, true>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N,
                    H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, states, eps, rowda, dXQ, none, seg_part, ppart);

@@ -66,7 +66,7 @@ def backward_bidir(XQ, XK, V, mu, sigma2, pi, eps, dO) -> dict:
     return out
 
 
-def backward_causal(XQ, XK, V, mu, sigma2, pi, eps, dO) -> dict:
+def backward_causal(XQ, XK, V, mu, sigma2, pi, eps, dO, state_in=None, dstate_out=None) -> dict:
     """Gradients of <dO, O> for the causal forward O (Sec. 3.5, Eq. 6b and 8b): position i reads
     the prefix memory Vt^(i) = sum_{j<=i} gamma^K_j V_j^T, Z^(i) = sum_{j<=i} gamma^K_j.  With
     D_i = gamma^Q_i . Z^(i) + eps and a_i = dO_i . O_i,
@@ -75,7 +75,13 @@ def backward_causal(XQ, XK, V, mu, sigma2, pi, eps, dO) -> dict:
     key position j enters every memory Vt^(i) with i >= j, so its gradients are suffix sums:
       dVt_j = sum_{i>=j} gamma^Q_i dO_i^T / D_i,  dZ_j = -sum_{i>=j} gamma^Q_i a_i / D_i,
       dV_j = sum_k gamma^K_jk dVt_j[k],            g^K_jk = dVt_j[k] . V_j + dZ_j[k].
-    The rest (Eq. 18-20) is as for the bidirectional backward.  Shapes as backward_bidir."""
+    The rest (Eq. 18-20) is as for the bidirectional backward.  Shapes as backward_bidir.
+
+    Continued from a carried memory state_in [B,H,K,d_v+1] (row k: Vt_k then Z_k; the forward of
+    forward_causal_state), every memory Vt^(i) includes state_in, and the loss may carry a gradient
+    dstate_out on the memory after the last position, which every key position enters with weight
+    one: dstate_out is added to every dVt_j, dZ_j.  The result then also holds dstate_in, the
+    gradient with respect to state_in: dstate_out plus what every query position sends."""
     from . import _f64, responsibilities
     XQ, XK, V, dO = (_f64(t) for t in (XQ, XK, V, dO))
     mu, s2, pi = (_f64(t) for t in (mu, sigma2, pi))
@@ -83,11 +89,19 @@ def backward_causal(XQ, XK, V, mu, sigma2, pi, eps, dO) -> dict:
     B, H, N, dr = XQ.shape
     out = {"dXQ": np.zeros_like(XQ), "dXK": np.zeros_like(XK), "dV": np.zeros_like(V),
            "dmu": np.zeros_like(mu), "dsigma2": np.zeros_like(s2), "dpi": np.zeros_like(pi)}
+    K, dv = mu.shape[1], V.shape[-1]
+    carried = state_in is not None or dstate_out is not None
+    sin = _f64(state_in) if state_in is not None else np.zeros((B, H, K, dv + 1))
+    dso = _f64(dstate_out) if dstate_out is not None else np.zeros((B, H, K, dv + 1))
+    if carried:
+        out["dstate_in"] = dso.copy()
     for b in range(B):
         for h in range(H):
             gq, gk, v, do = GQ[b, h], GK[b, h], V[b, h], dO[b, h]
-            vt = np.cumsum(gk[:, :, None] * v[:, None, :], axis=0)   # Vt^(i), [N,K,d_v] (Eq. 6b)
-            z = np.cumsum(gk, axis=0)                                  # Z^(i), [N,K]
+            if N == 0:
+                continue
+            vt = sin[b, h, None, :, :dv] + np.cumsum(gk[:, :, None] * v[:, None, :], axis=0)   # Vt^(i) (Eq. 6b)
+            z = sin[b, h, None, :, dv] + np.cumsum(gk, axis=0)                                  # Z^(i), [N,K]
             n_ = np.einsum("ik,ikc->ic", gq, vt)                       # Eq. 8b numerator
             d_ = np.einsum("ik,ik->i", gq, z) + eps
             o = n_ / d_[:, None]
@@ -95,6 +109,11 @@ def backward_causal(XQ, XK, V, mu, sigma2, pi, eps, dO) -> dict:
             g_q = (np.einsum("ic,ikc->ik", do, vt) - a[:, None] * z) / d_[:, None]
             dvt = np.cumsum((gq[:, :, None] * (do / d_[:, None])[:, None, :])[::-1], axis=0)[::-1]
             dz = -np.cumsum((gq * (a / d_)[:, None])[::-1], axis=0)[::-1]
+            dvt = dvt + dso[b, h, None, :, :dv]   # the memory after the call depends on every key
+            dz = dz + dso[b, h, None, :, dv]
+            if carried:  # what every position sends to the memory it read, plus dstate_out
+                out["dstate_in"][b, h, :, :dv] = dvt[0]
+                out["dstate_in"][b, h, :, dv] = dz[0]
             out["dV"][b, h] = np.einsum("jk,jkc->jc", gk, dvt)
             g_k = np.einsum("jc,jkc->jk", v, dvt) + dz
             for x, g, gam, key in ((XQ[b, h], g_q, gq, "dXQ"), (XK[b, h], g_k, gk, "dXK")):

@@ -724,3 +724,48 @@ def test_backward_cross_matches_finite_differences():
             return float((do * oracle.forward_cross(a[0], a[1], a[2], a[3], a[4], a[5], eps)).sum())
         fd = (loss(1.0) - loss(-1.0)) / (2 * h)
         np.testing.assert_allclose((g[key] * u).sum(), fd, rtol=2e-6, atol=1e-9, err_msg=key)
+
+
+def test_backward_causal_state_matches_finite_differences():
+    """A call continued from a carried memory: <grad, u> equals the central difference of
+    <dO, O> + <dS, state_out> (forward_causal_state) for every input and for state_in."""
+    rng = np.random.default_rng(68)
+    xq, xk, v, mu, s2, pi, do = _backward_problem(rng)
+    B, H, N, dv, K = v.shape[0], v.shape[1], v.shape[2], v.shape[3], mu.shape[1]
+    sin = np.abs(rng.standard_normal((B, H, K, dv + 1)))
+    sin[..., :dv] = rng.standard_normal((B, H, K, dv))
+    ds = rng.standard_normal((B, H, K, dv + 1))
+    eps = 1e-3
+    g = oracle.backward.backward_causal(xq, xk, v, mu, s2, pi, eps, do, state_in=sin, dstate_out=ds)
+    args = {"dXQ": xq, "dXK": xk, "dV": v, "dmu": mu, "dsigma2": s2, "dpi": pi, "dstate_in": sin}
+    order = ["dXQ", "dXK", "dV", "dmu", "dsigma2", "dpi", "dstate_in"]
+    for key in order:
+        u = rng.standard_normal(args[key].shape)
+        h = 1e-6 * (np.abs(args[key]).max() + 1.0)
+        def loss(sign):
+            a = [args[k].copy() for k in order]
+            a[order.index(key)] = a[order.index(key)] + sign * h * u
+            o, so = oracle.forward_causal_state(a[0], a[1], a[2], a[3], a[4], a[5], eps, a[6])
+            return float((do * o).sum() + (ds * so).sum())
+        fd = (loss(1.0) - loss(-1.0)) / (2 * h)
+        np.testing.assert_allclose((g[key] * u).sum(), fd, rtol=2e-6, atol=1e-9, err_msg=key)
+
+
+def test_backward_causal_state_piecewise_equals_whole():
+    """Backward through two chained calls (the second's dstate_in fed to the first as its
+    dstate_out) equals the backward of one call over the whole sequence."""
+    rng = np.random.default_rng(69)
+    xq, xk, v, mu, s2, pi, do = _backward_problem(rng, N=13)
+    eps = 1e-3
+    whole = oracle.backward.backward_causal(xq, xk, v, mu, s2, pi, eps, do)
+    m = 5
+    _, s1 = oracle.forward_causal_state(xq[:, :, :m], xk[:, :, :m], v[:, :, :m], mu, s2, pi, eps)
+    second = oracle.backward.backward_causal(xq[:, :, m:], xk[:, :, m:], v[:, :, m:], mu, s2, pi, eps, do[:, :, m:],
+                                             state_in=s1)
+    first = oracle.backward.backward_causal(xq[:, :, :m], xk[:, :, :m], v[:, :, :m], mu, s2, pi, eps, do[:, :, :m],
+                                            dstate_out=second["dstate_in"])
+    for key in ("dXQ", "dXK", "dV"):
+        np.testing.assert_allclose(np.concatenate([first[key], second[key]], axis=2), whole[key], rtol=1e-10,
+                                   atol=1e-13, err_msg=key)
+    for key in ("dmu", "dsigma2", "dpi"):
+        np.testing.assert_allclose(first[key] + second[key], whole[key], rtol=1e-10, atol=1e-13, err_msg=key)
