@@ -26,7 +26,7 @@ GMA_OP_RESPONSIBILITIES, GMA_OP_BIDIR, GMA_OP_CAUSAL, GMA_OP_DIAGNOSTICS = 0, 1,
 GMA_OP_BACKWARD_BIDIR, GMA_OP_BACKWARD_CAUSAL = 4, 5
 EXPORTED = ["gma_status_string", "gma_workspace_size", "gma_responsibilities", "gma_forward_bidir",
             "gma_forward_causal", "gma_forward_causal_state", "gma_cross_workspace_size", "gma_forward_cross", "gma_responsibility_diagnostics", "gma_backward_bidir",
-            "gma_backward_causal", "gma_backward_cross_workspace_size", "gma_backward_cross", "gma_profiling",
+            "gma_backward_causal", "gma_backward_causal_state", "gma_backward_cross_workspace_size", "gma_backward_cross", "gma_profiling",
             "gma_profiling_collect", "gma_set_wait_limit"]
 WAIT_LIMIT_DEFAULT = 1 << 18  # GMA_WAIT_LIMIT_DEFAULT
 
@@ -92,6 +92,9 @@ def load() -> ctypes.CDLL:
             lib.gma_backward_bidir.restype = i32
             lib.gma_backward_causal.argtypes = lib.gma_backward_bidir.argtypes
             lib.gma_backward_causal.restype = i32
+            lib.gma_backward_causal_state.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp,
+                                                      vp, vp, vp, shp, vp, sz, vp]
+            lib.gma_backward_causal_state.restype = i32
             lib.gma_backward_cross_workspace_size.argtypes = [xshp, i32, ctypes.POINTER(sz)]
             lib.gma_backward_cross_workspace_size.restype = i32
             lib.gma_backward_cross.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, vp, vp, vp, vp, vp, vp, xshp,
@@ -272,6 +275,32 @@ def gma_backward_causal(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, mu:
     as gma_backward_bidir."""
     return _backward(GMA_OP_BACKWARD_CAUSAL, "gma_backward_causal", xq, xk, v, mu, sigma2, pi, d_o, eps, out,
                      workspace, stream)
+
+
+def gma_backward_causal_state(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, mu: torch.Tensor,
+                              sigma2: torch.Tensor, pi: torch.Tensor, d_o: torch.Tensor, eps: float = 1e-6,
+                              state_in: Optional[torch.Tensor] = None, dstate_out: Optional[torch.Tensor] = None,
+                              out: Optional[dict] = None, workspace: Optional[torch.Tensor] = None,
+                              stream=None) -> dict:
+    """Gradients of <d_o, O> + <dstate_out, state_out> for a causal call continued from the carried
+    memory state_in [B,H,K,d_v+1] (Sec. 3.5 Eq. 6b as a recurrence); outputs as gma_backward_causal
+    plus dstate_in [B,H,K,d_v+1], the gradient of state_in."""
+    B, H, N, dr = xq.shape
+    dv = v.shape[-1]
+    K = mu.shape[1]
+    io = _dtype_code(xq.dtype)
+    if out is None:
+        out = {"dXQ": torch.empty_like(xq), "dXK": torch.empty_like(xk), "dV": torch.empty_like(v),
+               "dmu": torch.empty_like(mu), "dsigma2": torch.empty_like(sigma2), "dpi": torch.empty_like(pi),
+               "dstate_in": torch.empty(B, H, K, dv + 1, dtype=torch.float32, device=xq.device)}
+    ws = _workspace(gma_workspace_size(GMA_OP_BACKWARD_CAUSAL, B, H, N, dr, dv, K, io), xq.device, workspace)
+    _check(load().gma_backward_causal_state(_ptr(xq), _ptr(xk), _ptr(v), io, _ptr(mu), _ptr(sigma2), _ptr(pi),
+                                            float(eps), _ptr(d_o), _ptr(state_in), _ptr(dstate_out),
+                                            _ptr(out["dXQ"]), _ptr(out["dXK"]), _ptr(out["dV"]), _ptr(out["dmu"]),
+                                            _ptr(out["dsigma2"]), _ptr(out["dpi"]), _ptr(out["dstate_in"]),
+                                            ctypes.byref(Shape(B, H, N, dr, dv, K)), _ptr(ws), ws.numel(),
+                                            _stream(stream)), "gma_backward_causal_state")
+    return out
 
 
 def gma_backward_cross_workspace_size(B: int, H: int, N_q: int, N_k: int, d_r: int, d_v: int, K: int,

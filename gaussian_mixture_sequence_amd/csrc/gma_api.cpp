@@ -432,8 +432,20 @@ gma_status_t gma_responsibility_diagnostics(const void* X, gma_dtype_t x_dtype, 
 static gma_status_t backward_run(const Plan& p, const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
                                  const float* mu, const float* sigma2, const float* pi, float eps, const void* dO,
                                  void* dXQ, void* dXK, void* dV, float* dmu, float* dsigma2, float* dpi,
-                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                 const float* state_in = nullptr, const float* dstate_out = nullptr,
+                                 float* dstate_in = nullptr) {
     if ((!dmu || !dsigma2 || !dpi) && p.H > 0) return GMA_ERR_NULL_POINTER;
+    for (const void* q : {(const void*)state_in, (const void*)dstate_out, (const void*)dstate_in})
+        if (!gma::aligned16(q)) return GMA_ERR_MISALIGNED;
+    if (dstate_in) {  // written while the others are read: no overlap
+        const size_t sb = size_t(p.P) * size_t(p.K) * size_t(p.dv + 1) * 4;
+        const char* b = reinterpret_cast<const char*>(dstate_in);
+        for (const float* other : {state_in, dstate_out}) {
+            const char* a = reinterpret_cast<const char*>(other);
+            if (other && sb > 0 && a < b + sb && b < a + sb) return GMA_ERR_BAD_VALUE;
+        }
+    }
     if ((!XQ || !dO || !dXQ) && p.P > 0 && p.Nq > 0) return GMA_ERR_NULL_POINTER;  // tensors with elements
     if ((!XK || !V || !dXK || !dV) && p.P > 0 && p.N > 0) return GMA_ERR_NULL_POINTER;
     if (!(eps > 0.0f) || !std::isfinite(eps)) return GMA_ERR_BAD_VALUE;
@@ -464,7 +476,8 @@ static gma_status_t backward_run(const Plan& p, const void* XQ, const void* XK, 
         q = q32, k = k32, v = v32, d = d32;
     }
     if (p.op == GMA_OP_BACKWARD_CAUSAL)
-        e = gma::f32_backward_causal(p, q, k, v, mu, sigma2, pi, eps, d, dq, dk, dvv, dmu, dsigma2, dpi, ws, stream);
+        e = gma::f32_backward_causal(p, q, k, v, mu, sigma2, pi, eps, d, dq, dk, dvv, dmu, dsigma2, dpi, ws, stream,
+                                     state_in, dstate_out, dstate_in);
     else
         e = gma::f32_backward_bidir(p, q, k, v, mu, sigma2, pi, eps, d, dq, dk, dvv, dmu, dsigma2, dpi, ws, stream);
     if (e != hipSuccess || !staged) return launch_status(e);
@@ -500,6 +513,20 @@ gma_status_t gma_backward_causal(const void* XQ, const void* XK, const void* V, 
                                  const gma_shape_t* shape, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return backward_common(GMA_OP_BACKWARD_CAUSAL, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, dO, dXQ, dXK, dV, dmu,
                            dsigma2, dpi, shape, workspace, workspace_bytes, stream);
+}
+
+gma_status_t gma_backward_causal_state(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                                       const float* mu, const float* sigma2, const float* pi, float eps,
+                                       const void* dO, const float* state_in, const float* dstate_out, void* dXQ,
+                                       void* dXK, void* dV, float* dmu, float* dsigma2, float* dpi, float* dstate_in,
+                                       const gma_shape_t* shape, void* workspace, size_t workspace_bytes,
+                                       hipStream_t stream) {
+    if (!mu || !sigma2 || !pi || !shape) return GMA_ERR_NULL_POINTER;
+    Plan p;
+    gma_status_t st = gma::make_plan(GMA_OP_BACKWARD_CAUSAL, *shape, io_dtype, 0, &p);
+    if (st != GMA_OK) return st;
+    return backward_run(p, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, dO, dXQ, dXK, dV, dmu, dsigma2, dpi, workspace,
+                        workspace_bytes, stream, state_in, dstate_out, dstate_in);
 }
 
 gma_status_t gma_backward_cross_workspace_size(const gma_cross_shape_t* shape, gma_dtype_t io_dtype, size_t* bytes_out) {

@@ -994,18 +994,23 @@ size_t bwdc_lds_bytes(int T, int dr, int dv, int K) {
 }
 
 // Causal: exclusive suffix over segments in place; segment g then holds the sum over the
-// segments after it.
-__global__ void __launch_bounds__(kThreads) f32_suffix_kernel(float* __restrict__ partials, int G, int E) {
+// segments after it, starting from the gradient of the memory after the call (dstate_out,
+// [P][K][dv+1], or zero when NULL).  The total, the gradient of the memory before the call, goes
+// to dstate_in ([P][K][dv+1]) when it is not NULL.
+__global__ void __launch_bounds__(kThreads) f32_suffix_kernel(float* __restrict__ partials, int G, int E,
+                                                              const float* __restrict__ dstate_out,
+                                                              float* __restrict__ dstate_in, int K, int dv) {
     const int64_t p = blockIdx.y;
     const int e = blockIdx.x * kThreads + threadIdx.x;
     if (e >= E) return;
     float* src = partials + size_t(p) * G * E + e;
-    float run = 0.0f;
+    float run = dstate_out ? dstate_out[size_t(p) * E + state_index(e, K, dv)] : 0.0f;
     for (int g = G - 1; g >= 0; --g) {
         const float a = src[size_t(g) * E];
         src[size_t(g) * E] = run;
         run += a;
     }
+    if (dstate_in) dstate_in[size_t(p) * E + state_index(e, K, dv)] = run;
 }
 
 // gamma_tile with fp32 tables in LDS: c [K], 1/sigma2 and mu as [K][LR] rows (LR = d_r + 1),
@@ -1325,9 +1330,15 @@ size_t f32_backward_causal_extra_bytes(const Plan& p) {
 
 hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
                                const float* s2, const float* pi, float eps, const float* dO, float* dXQ, float* dXK,
-                               float* dV, float* dmu, float* ds2, float* dpi, char* ws, hipStream_t st) {
+                               float* dV, float* dmu, float* ds2, float* dpi, char* ws, hipStream_t st,
+                               const float* state_in, const float* dstate_out, float* dstate_in) {
     if (p.H == 0) return hipSuccess;
-    if (p.P == 0 || p.N == 0) return reduce_params(p, nullptr, 0, nullptr, pi, dmu, ds2, dpi, st);  // zero gradients
+    if (p.P == 0) return reduce_params(p, nullptr, 0, nullptr, pi, dmu, ds2, dpi, st);
+    if (p.N == 0) {  // no positions: zero parameter gradients, and the memory passes its gradient through
+        hipError_t e0 = reduce_params(p, nullptr, 0, nullptr, pi, dmu, ds2, dpi, st);
+        if (e0 != hipSuccess || !dstate_in) return e0;
+        return copy_state(p, dstate_out, dstate_in, st);
+    }
     static const hipError_t attr = [] {
         const void* fns[] = {(const void*)f32_bwdc_kernel<true, false>, (const void*)f32_bwdc_kernel<false, false>,
                              (const void*)f32_bwdc_kernel<true, true>, (const void*)f32_bwdc_kernel<false, true>};
@@ -1374,8 +1385,7 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
                    p.seg, G, v.c, v.inv, mu, states);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    GMA_LAUNCH("f32_bwdc_prefix", f32_prefix_kernel, egrid, dim3(kThreads), 0, st, states, G, Ei,
-               static_cast<const float*>(nullptr), K, dv);
+    GMA_LAUNCH("f32_bwdc_prefix", f32_prefix_kernel, egrid, dim3(kThreads), 0, st, states, G, Ei, state_in, K, dv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (tiled) {  // register-tiled passes with the running memory in LDS
         GMA_LAUNCH("f32_bwdc_query", f32_bwd_tiled_kernel<BWD_CQUERY>, grid, dim3(kThreads),
@@ -1383,7 +1393,8 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
                    static_cast<const float*>(states), eps, dXQ, none, seg_part, ppart, XK, V, rowda, gq_cache, cnone,
                    static_cast<const float*>(gk_cache));
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        GMA_LAUNCH("f32_bwdc_suffix", f32_suffix_kernel, egrid, dim3(kThreads), 0, st, seg_part, G, Ei);
+        GMA_LAUNCH("f32_bwdc_suffix", f32_suffix_kernel, egrid, dim3(kThreads), 0, st, seg_part, G, Ei, dstate_out,
+                   dstate_in, K, dv);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         GMA_LAUNCH("f32_bwdc_key", f32_bwd_tiled_kernel<BWD_CKEY>, grid, dim3(kThreads),
                    bwd_tiled_lds_bytes(BWD_CKEY, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
@@ -1392,9 +1403,9 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
         if ((e = hipGetLastError()) != hipSuccess) return e;
         return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
     }
-    // one element per thread: FAST (tables and running memory in LDS) with 64- or 32-position tiles when two workgroups
-    // still fit a CU; otherwise the general form: 64-position tiles when two fit, else the largest
-    // tile that lets two fit (down to 32), else the largest that fits at all
+    // one element per thread: FAST (tables and running memory in LDS) with 64- or 32-position
+    // tiles when two workgroups still fit a CU; otherwise the general form: 64-position tiles when
+    // two fit, else the largest tile that lets two fit (down to 32), else the largest that fits
     const size_t fast_extra = size_t(2 * K * (dr + 1) + 2 * K + K * (dv + 1)) * sizeof(float);
     int T = kTile;
     bool fast = false;
@@ -1412,7 +1423,8 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
         GMA_LAUNCH("f32_bwdc_query", (f32_bwdc_kernel<true, false>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N,
                    H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, states, eps, rowda, dXQ, none, seg_part, ppart);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    GMA_LAUNCH("f32_bwdc_suffix", f32_suffix_kernel, egrid, dim3(kThreads), 0, st, seg_part, G, Ei);
+    GMA_LAUNCH("f32_bwdc_suffix", f32_suffix_kernel, egrid, dim3(kThreads), 0, st, seg_part, G, Ei, dstate_out, dstate_in,
+               K, dv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (fast)
         GMA_LAUNCH("f32_bwdc_key", (f32_bwdc_kernel<false, true>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N, H,

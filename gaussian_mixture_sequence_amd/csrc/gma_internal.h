@@ -89,9 +89,13 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
 
 // Backward of the causal forward (fp32): workspace beyond the causal plan's own, and the launcher.
 size_t f32_backward_causal_extra_bytes(const Plan& p);
+// state_in: the carried memory before the call, dstate_out: the gradient of the memory after it,
+// dstate_in: the gradient of state_in (all [P][K][d_v+1] fp32, NULL for none).
 hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
                                const float* s2, const float* pi, float eps, const float* dO, float* dXQ, float* dXK,
-                               float* dV, float* dmu, float* ds2, float* dpi, char* ws, hipStream_t st);
+                               float* dV, float* dmu, float* ds2, float* dpi, char* ws, hipStream_t st,
+                               const float* state_in = nullptr, const float* dstate_out = nullptr,
+                               float* dstate_in = nullptr);
 
 // bf16 <-> fp32 copies of n elements (the staging of the backward's bf16 I/O).
 hipError_t widen_bf16(const void* src, float* dst, size_t n, hipStream_t st);

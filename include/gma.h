@@ -280,6 +280,28 @@ gma_status_t gma_backward_causal(const void* XQ, const void* XK, const void* V, 
                                  hipStream_t stream);
 
 /*
+ * Backward pass of a causal call continued from a carried memory (gma_forward_causal_state):
+ * the gradients of <dO, O> + <dstate_out, state_out>.  Every prefix memory of the call includes
+ * state_in, and the memory after the call depends on every key position with weight one, so
+ * dstate_out is added to every key position's memory gradient (dVt_j, dZ_j of
+ * gma_backward_causal), and
+ *   dstate_in[k, :d_v] = dstate_out[k, :d_v] + sum_i Gamma_Q[i,k] dO_i / D_i,
+ *   dstate_in[k, d_v]  = dstate_out[k, d_v]  - sum_i Gamma_Q[i,k] a_i / D_i
+ * (sum over every position of the call).  Chained over calls (each call's dstate_in passed as the
+ * previous call's dstate_out) this is the backward of one pass over the whole sequence.
+ *   state_in, dstate_out: [B,H,K,d_v+1] fp32 (row k: Vt_k, then Z_k), NULL for zeros;
+ *   dstate_in: [B,H,K,d_v+1] fp32 out, NULL to skip; it must not overlap state_in or dstate_out.
+ * A call without positions returns dstate_in = dstate_out and zero parameter gradients.  Other
+ * arguments, the workspace (GMA_OP_BACKWARD_CAUSAL) and errors as for gma_backward_causal.
+ */
+gma_status_t gma_backward_causal_state(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                                       const float* mu, const float* sigma2, const float* pi, float eps,
+                                       const void* dO, const float* state_in, const float* dstate_out, void* dXQ,
+                                       void* dXK, void* dV, float* dmu, float* dsigma2, float* dpi,
+                                       float* dstate_in, const gma_shape_t* shape, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Backward pass of cross-attention (gma_forward_cross): the gradients of <dO, O> with the
  * formulas of gma_backward_bidir, Gamma_Q taken over the N_q query rows and Gamma_K over the N_k
  * context rows (Sec. 3 "Cross-attention"; Sec. 4.1 Eq. 17-20).

@@ -306,3 +306,21 @@ def test_backward_cross_argument_errors(lib):
     assert call(d_o=FAKE + 4) == MISAL
     assert call(eps=0.0) == VALUE
     assert call(nb=need - 1) == WS
+
+
+def test_backward_causal_state_argument_errors(lib):
+    F = gb.GMA_F32
+    shape = (2, 3, 64, 16, 32, 8)
+    need = ws_size(gb.GMA_OP_BACKWARD_CAUSAL, *shape, F)[1]
+    sh = ctypes.byref(gb.Shape(*shape))
+    sb = 2 * 3 * 8 * 33 * 4  # bytes of one [B,H,K,d_v+1] state
+
+    def call(sin=None, dso=None, dsi=FAKE + 0x100000, xq=FAKE):
+        return lib.gma_backward_causal_state(xq, FAKE, FAKE, F, FAKE, FAKE, FAKE, 1e-6, FAKE, sin, dso, FAKE, FAKE,
+                                             FAKE, FAKE, FAKE, FAKE, dsi, sh, FAKE, need, None)
+
+    assert call(xq=None) == NULLP
+    assert call(sin=FAKE + 4) == MISAL
+    assert call(dsi=FAKE + 8) == MISAL
+    assert call(dso=FAKE + 0x100000 + sb - 16) == VALUE    # dstate_in overlaps dstate_out
+    assert call(sin=FAKE + 0x100000 - sb + 16) == VALUE    # dstate_in overlaps state_in

@@ -322,3 +322,89 @@ def test_backward_cross_equal_lengths_is_bidir_bitwise():
     torch.cuda.synchronize()
     for k in KEYS:
         assert torch.equal(a[k], b[k]), k
+
+
+# ---------------------------------------------------------------------------- carried memory
+
+
+def carried(w, seed):
+    """A carried memory (Z >= 0) and a gradient for the memory after the call, [B,H,K,d_v+1]."""
+    gen = torch.Generator().manual_seed(seed)
+    s = torch.randn(w.B, w.H, w.K, w.d_v + 1, generator=gen, dtype=torch.float32)
+    s[..., -1] = s[..., -1].abs() * 3.0
+    ds = torch.randn(w.B, w.H, w.K, w.d_v + 1, generator=gen, dtype=torch.float32)
+    return s, ds
+
+
+STATE_CASES = [
+    case(700, 141),                                         # tiled causal passes
+    case(1000, 142, B=2, H=2, d_r=64, d_v=64, K=32),
+    case(500, 143, B=2, H=3, d_r=7, d_v=5, K=13),          # one element per thread (LDS tables)
+    case(300, 144, d_r=32, d_v=64, K=64),                  # one element per thread (general)
+    case(200, 145, B=1, H=1, d_r=128, d_v=128, K=256),
+]
+
+
+@pytest.mark.parametrize("w", STATE_CASES, ids=cid)
+def test_backward_causal_state_parity(w):
+    w = w.with_(causal=True)
+    inp = make_inputs(w)
+    d_o = upstream(w, w.seed + 1000)
+    s, ds = carried(w, w.seed + 2000)
+    d = to_device(inp)
+    g = gb.gma_backward_causal_state(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], d_o.cuda(), w.eps,
+                                     state_in=s.cuda(), dstate_out=ds.cuda())
+    torch.cuda.synchronize()
+    ref = oracle.backward.backward_causal(inp["xq"], inp["xk"], inp["v"], inp["mu"], inp["sigma2"], inp["pi"], w.eps,
+                                          d_o, state_in=s, dstate_out=ds)
+    for k in KEYS + ("dstate_in",):
+        got = to_np(g[k])
+        assert got.shape == ref[k].shape and np.isfinite(got).all(), k
+        assert tensor_error(got, ref[k]) <= TOL_BWD, (k, tensor_error(got, ref[k]))
+
+
+def test_backward_causal_state_chained_calls_equal_whole_sequence():
+    """Three calls over consecutive pieces, forward state carried and dstate_in fed back as the
+    previous call's dstate_out, give the whole-sequence backward."""
+    w = case(1000, 146, B=2, H=2, d_r=32, d_v=32, K=32, causal=True)
+    inp = make_inputs(w)
+    d_o = upstream(w, 1146)
+    d = to_device(inp)
+    cuts = [0, 300, 301, 1000]
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    states = [None]
+    for a, b in zip(cuts[:-1], cuts[1:]):  # forward: the memory before each piece
+        _, so = gb.gma_forward_causal_state(sl(d["xq"], a, b), sl(d["xk"], a, b), sl(d["v"], a, b), d["mu"],
+                                            d["sigma2"], d["pi"], w.eps, state_in=states[-1])
+        states.append(so)
+    grads, dso = [None] * 3, None
+    for i in (2, 1, 0):
+        a, b = cuts[i], cuts[i + 1]
+        grads[i] = gb.gma_backward_causal_state(sl(d["xq"], a, b), sl(d["xk"], a, b), sl(d["v"], a, b), d["mu"],
+                                                d["sigma2"], d["pi"], sl(d_o, a, b).cuda(), w.eps,
+                                                state_in=states[i], dstate_out=dso)
+        dso = grads[i]["dstate_in"]
+    torch.cuda.synchronize()
+    ref = oracle.backward.backward_causal(inp["xq"], inp["xk"], inp["v"], inp["mu"], inp["sigma2"], inp["pi"], w.eps,
+                                          d_o)
+    for k in ("dXQ", "dXK", "dV"):
+        got = np.concatenate([to_np(gr[k]) for gr in grads], axis=2)
+        assert tensor_error(got, ref[k]) <= TOL_BWD, k
+    for k in ("dmu", "dsigma2", "dpi"):
+        got = sum(to_np(gr[k]) for gr in grads)
+        assert tensor_error(got, ref[k]) <= TOL_BWD, k
+
+
+def test_backward_causal_state_empty_call():
+    """No positions: dstate_in = dstate_out exactly, zero parameter gradients."""
+    w = case(0, 147, causal=True)
+    inp = make_inputs(w)
+    d = to_device(inp)
+    s, ds = carried(w, 2147)
+    g = gb.gma_backward_causal_state(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"],
+                                     torch.empty(w.B, w.H, 0, w.d_v, device="cuda"), w.eps, state_in=s.cuda(),
+                                     dstate_out=ds.cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(g["dstate_in"].cpu(), ds)
+    for k in ("dmu", "dsigma2", "dpi"):
+        assert not to_np(g[k]).any(), k
