@@ -248,9 +248,9 @@ gma_status_t gma_responsibility_diagnostics(const void* X, gma_dtype_t x_dtype, 
  * memory and its split partials, the same for (dVt, dZ), and per-split parameter partials,
  * reduced in a fixed order (bitwise reproducible); for K, d_r, d_v <= 64 (multiples of 4) the
  * responsibilities of the keys, which the key pass reads back (B H N K fp32); with bf16 I/O also
- * fp32 copies of the four inputs and three outputs (O(B H N (d_r + d_v)) bytes).  Sizes as for the fp32 forward (d_r, d_v
- * <= 128, K <= 256 at either I/O dtype); alignment and errors as for gma_forward_bidir; with no
- * rows (B N = 0) the parameter gradients are zeros.
+ * fp32 copies of the four inputs and three outputs (O(B H N (d_r + d_v)) bytes).  Sizes as for
+ * the fp32 forward (d_r, d_v <= 128, K <= 256 at either I/O dtype); alignment and errors as for
+ * gma_forward_bidir; with no rows (B N = 0) the parameter gradients are zeros.
  */
 gma_status_t gma_backward_bidir(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
                                 const float* mu, const float* sigma2, const float* pi, float eps,
