@@ -408,3 +408,28 @@ def test_backward_causal_state_empty_call():
     assert torch.equal(g["dstate_in"].cpu(), ds)
     for k in ("dmu", "dsigma2", "dpi"):
         assert not to_np(g[k]).any(), k
+
+
+# ---------------------------------------------------------------------------- autograd
+
+
+@pytest.mark.parametrize("variant", ["bidir", "causal", "cross"])
+def test_autograd_functions_match_oracle(variant):
+    """torch.autograd through gaussian_mixture_sequence_amd.autograd: the loss <dO, O> back-propagates
+    to the oracle's gradients."""
+    from gaussian_mixture_sequence_amd import autograd as ga
+    if variant == "cross":
+        w = cross_case(300, 500, 151, d_r=32, d_v=32, K=32)
+    else:
+        w = case(700, 152, B=2, H=2, d_r=32, d_v=32, K=32, causal=variant == "causal")
+    inp = make_inputs(w)
+    d_o = upstream(w, 1151)
+    leaves = {k: t.cuda().requires_grad_(True) for k, t in inp.items()}
+    fn = {"bidir": ga.gma_bidir, "causal": ga.gma_causal, "cross": ga.gma_cross}[variant]
+    out = fn(leaves["xq"], leaves["xk"], leaves["v"], leaves["mu"], leaves["sigma2"], leaves["pi"], w.eps)
+    (out * d_o.cuda()).sum().backward()
+    torch.cuda.synchronize()
+    ref_fn = oracle.backward.backward_causal if variant == "causal" else oracle.backward.backward_bidir
+    ref = ref_fn(inp["xq"], inp["xk"], inp["v"], inp["mu"], inp["sigma2"], inp["pi"], w.eps, d_o)
+    for k, name in zip(KEYS, ("xq", "xk", "v", "mu", "sigma2", "pi")):
+        assert tensor_error(to_np(leaves[name].grad), ref[k]) <= TOL_BWD, k
