@@ -25,6 +25,56 @@ namespace gma {
 // Partial records per (problem, split): [S1 (K d_r) | S2 (K d_r) | S0 (K)].
 namespace {
 
+// gamma_tile with fp32 tables in LDS: c [K], 1/sigma2 and mu as [K][LR] rows (LR = d_r + 1),
+// the direct-form score of Eq. 16 in fp32, then the softmax of Eq. 3b.  Same contract as gamma_tile.
+__device__ void gamma_tile_lds(const float* __restrict__ X, int64_t n0, int rows, int T, int dr, int K,
+                               const float* c_l, const float* inv_l, const float* mu_l, float* xs, float* g) {
+    const int LR = dr + 1;
+    for (int i = threadIdx.x; i < T * dr; i += kThreads) {
+        const int t = i / dr;
+        xs[i] = (t < rows) ? X[(n0 + t) * dr + (i - t * dr)] : 0.0f;
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int t = wave; t < T; t += kThreads / kWave) {
+        float* gt = g + size_t(t) * K;
+        if (t >= rows) {
+            for (int k = lane; k < K; k += kWave) gt[k] = 0.0f;
+            continue;
+        }
+        const float* xt = xs + t * dr;
+        float sc[4], m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = lane + j * kWave;
+            sc[j] = -INFINITY;
+            if (k < K) {
+                const float *mk = mu_l + k * LR, *ik = inv_l + k * LR;
+                float q = 0.0f;
+                for (int d = 0; d < dr; ++d) {
+                    const float df = xt[d] - mk[d];
+                    q = fmaf(df * df, ik[d], q);
+                }
+                sc[j] = c_l[k] - 0.5f * q;
+                m = fmaxf(m, sc[j]);
+            }
+        }
+        m = wave_max(m);
+        float ev[4], sum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            ev[j] = (lane + j * kWave < K) ? expf(sc[j] - m) : 0.0f;
+            sum += ev[j];
+        }
+        sum = wave_sum(sum);
+        const float r = 1.0f / sum;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (lane + j * kWave < K) gt[lane + j * kWave] = ev[j] * r;
+    }
+    __syncthreads();
+}
+
 // ---- general sizes: one thread per output element, LDS tiles of T rows
 size_t bwd_lds_bytes(int T, int dr, int dv, int K) { return size_t(T) * (dr + 2 * K + dv + 2) * sizeof(float); }
 
@@ -32,7 +82,9 @@ size_t bwd_lds_bytes(int T, int dr, int dv, int K) { return size_t(T) * (dr + 2 
 // (reads the memory mem = [Vt | Z], writes dX_Q and the partial [dVt | dZ] of its rows);
 // otherwise the key side (reads dmem = [dVt | dZ], writes dV and dX_K).  Both write the
 // block's moment record pp (first tile writes, later tiles add: each entry has one owner).
-template <bool QUERY>
+// FAST: the per-head tables (fp32) and the memory sit in LDS (rows padded by one element) and
+// the scores, dX and moments are fp32; otherwise they come from the fp64 tables in the workspace.
+template <bool QUERY, bool FAST>
 __global__ void __launch_bounds__(kThreads)
     f32_bwd_side_kernel(const float* __restrict__ X, const float* __restrict__ Y, int64_t N, int H, int dr, int dv,
                         int K, int64_t seg, int G, int T, const double* c, const double* inv, const float* mu,
@@ -47,10 +99,31 @@ __global__ void __launch_bounds__(kThreads)
     float* ys = gg + T * K;   // T*dv: dO (query side) or V (key side)
     float* dd = ys + T * dv;  // T: D_i
     float* aa = dd + T;       // T: a_i
+    const int LR = dr + 1, LV = dv + 1;
+    float* mT = aa + T;           // FAST: [K][LR] mu
+    float* iT = mT + K * LR;      // FAST: [K][LR] 1 / sigma2
+    float* cT = iT + K * LR;      // FAST: [K] score constants
+    float* Ml = cT + K;           // FAST: [K][LV] the memory (or its gradient)
+    float* Zl = Ml + K * LV;      // FAST: [K] its Z column
     const double *ch = c + size_t(h) * K, *ih = inv + size_t(h) * K * dr;
     const float* mh = mu + size_t(h) * K * dr;
-    const float* Vt = mem + size_t(p) * K * (dv + 1);  // [K][dv], then Z (or dVt, dZ)
-    const float* Z = Vt + size_t(K) * dv;
+    const float* Vg = mem + size_t(p) * K * (dv + 1);  // [K][dv], then Z (or dVt, dZ)
+    const float* Vt = FAST ? Ml : Vg;
+    const float* Z = FAST ? Zl : Vg + size_t(K) * dv;
+    const int SV = FAST ? LV : dv;
+    if (FAST) {
+        for (int i = threadIdx.x; i < K * dr; i += kThreads) {
+            const int k = i / dr, d = i - k * dr;
+            mT[k * LR + d] = mh[i];
+            iT[k * LR + d] = float(ih[i]);
+        }
+        for (int k = threadIdx.x; k < K; k += kThreads) {
+            cT[k] = float(ch[k]);
+            Zl[k] = Vg[K * dv + k];
+        }
+        for (int i = threadIdx.x; i < K * dv; i += kThreads) Ml[(i / dv) * LV + i % dv] = Vg[i];
+        __syncthreads();
+    }
     const int E = K * (dv + 1), PE = 2 * K * dr + K;
     float* mp = mem_part ? mem_part + (size_t(p) * G + gi) * E : nullptr;
     float* pp = param_part + (size_t(p) * G + gi) * PE;
@@ -59,7 +132,10 @@ __global__ void __launch_bounds__(kThreads)
     bool first = true;
     for (int64_t n0 = lo; n0 < hi; n0 += T) {
         const int rows = int(min<int64_t>(T, hi - n0));
-        gamma_tile(X + p * N * dr, n0, rows, T, dr, K, ch, ih, mh, xs, gm);
+        if (FAST)
+            gamma_tile_lds(X + p * N * dr, n0, rows, T, dr, K, cT, iT, mT, xs, gm);
+        else
+            gamma_tile(X + p * N * dr, n0, rows, T, dr, K, ch, ih, mh, xs, gm);
         for (int i = threadIdx.x; i < T * dv; i += kThreads) {
             const int t = i / dv;
             ys[i] = t < rows ? Y[(p * N + n0) * dv + i] : 0.0f;
@@ -73,7 +149,7 @@ __global__ void __launch_bounds__(kThreads)
                 float a = 0.0f;
                 for (int cc = lane; cc < dv; cc += kWave) {
                     float nn = 0.0f;
-                    for (int k = 0; k < K; ++k) nn = fmaf(gm[t * K + k], Vt[size_t(k) * dv + cc], nn);
+                    for (int k = 0; k < K; ++k) nn = fmaf(gm[t * K + k], Vt[size_t(k) * SV + cc], nn);
                     a = fmaf(ys[t * dv + cc], nn / d, a);
                 }
                 a = wave_sum(a);
@@ -87,7 +163,7 @@ __global__ void __launch_bounds__(kThreads)
             for (int i = threadIdx.x; i < rows * dv; i += kThreads) {
                 const int t = i / dv, cc = i - t * dv;
                 float acc = 0.0f;
-                for (int k = 0; k < K; ++k) acc = fmaf(gm[t * K + k], Vt[size_t(k) * dv + cc], acc);
+                for (int k = 0; k < K; ++k) acc = fmaf(gm[t * K + k], Vt[size_t(k) * SV + cc], acc);
                 dY[(p * N + n0) * dv + i] = acc;
             }
         }
@@ -96,7 +172,7 @@ __global__ void __launch_bounds__(kThreads)
             const int t = i / K, k = i - t * K;
             float acc = 0.0f;
             if (t < rows) {
-                for (int cc = 0; cc < dv; ++cc) acc = fmaf(ys[t * dv + cc], Vt[size_t(k) * dv + cc], acc);
+                for (int cc = 0; cc < dv; ++cc) acc = fmaf(ys[t * dv + cc], Vt[size_t(k) * SV + cc], acc);
                 acc = QUERY ? (acc - aa[t] * Z[k]) / dd[t] : acc + Z[k];
             }
             gg[i] = acc;
@@ -114,22 +190,39 @@ __global__ void __launch_bounds__(kThreads)
         for (int i = threadIdx.x; i < rows * dr; i += kThreads) {
             const int t = i / dr, d = i - t * dr;
             float acc = 0.0f;
-            for (int k = 0; k < K; ++k)
-                acc = fmaf(gg[t * K + k], float((double(xs[t * dr + d]) - double(mh[size_t(k) * dr + d])) * ih[size_t(k) * dr + d]), acc);
+            if (FAST) {
+                const float x = xs[t * dr + d];
+                for (int k = 0; k < K; ++k) acc = fmaf(gg[t * K + k] * iT[k * LR + d], x - mT[k * LR + d], acc);
+            } else {
+                for (int k = 0; k < K; ++k)
+                    acc = fmaf(gg[t * K + k], float((double(xs[t * dr + d]) - double(mh[size_t(k) * dr + d])) * ih[size_t(k) * dr + d]), acc);
+            }
             dX[(p * N + n0) * dr + i] = -acc;
         }
         // moments of these rows
         for (int e = threadIdx.x; e < K * dr; e += kThreads) {
             const int k = e / dr, d = e - k * dr;
-            const double m = double(mh[e]);
-            double a1 = 0.0, a2 = 0.0;
-            for (int t = 0; t < rows; ++t) {
-                const double df = double(xs[t * dr + d]) - m, w = double(gg[t * K + k]) * df;
-                a1 += w;
-                a2 += w * df;
+            float a1, a2;
+            if (FAST) {
+                const float m = mT[k * LR + d];
+                a1 = 0.0f, a2 = 0.0f;
+                for (int t = 0; t < rows; ++t) {
+                    const float df = xs[t * dr + d] - m, w = gg[t * K + k] * df;
+                    a1 += w;
+                    a2 = fmaf(w, df, a2);
+                }
+            } else {
+                const double m = double(mh[e]);
+                double b1 = 0.0, b2 = 0.0;
+                for (int t = 0; t < rows; ++t) {
+                    const double df = double(xs[t * dr + d]) - m, w = double(gg[t * K + k]) * df;
+                    b1 += w;
+                    b2 += w * df;
+                }
+                a1 = float(b1), a2 = float(b2);
             }
-            pp[e] = first ? float(a1) : pp[e] + float(a1);
-            pp[K * dr + e] = first ? float(a2) : pp[K * dr + e] + float(a2);
+            pp[e] = first ? a1 : pp[e] + a1;
+            pp[K * dr + e] = first ? a2 : pp[K * dr + e] + a2;
         }
         for (int k = threadIdx.x; k < K; k += kThreads) {
             float acc = 0.0f;
@@ -877,10 +970,27 @@ hipError_t reduce_params(const Plan& p, const float* part, int B, const double* 
     return hipGetLastError();
 }
 
+// The one-element-per-thread passes: FAST (tables and memory in LDS) with the largest tile (64
+// down to 16 positions) that fits, else the general form with the largest tile that fits.
+struct SideConfig {
+    bool fast;
+    int T;
+    size_t lds;
+};
+SideConfig side_config(int K, int dr, int dv) {
+    const size_t extra = size_t(2 * K * (dr + 1) + 2 * K + K * (dv + 1)) * sizeof(float);
+    for (int t = kTile; t >= 16; t /= 2)
+        if (bwd_lds_bytes(t, dr, dv, K) + extra <= kMaxLds) return {true, t, bwd_lds_bytes(t, dr, dv, K) + extra};
+    int T = kTile;
+    while (T > 8 && bwd_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
+    return {false, T, bwd_lds_bytes(T, dr, dv, K)};
+}
+
 hipError_t bwd_allow_lds() {
     static const hipError_t e = [] {
-        const void* fns[] = {(const void*)f32_write_kernel, (const void*)f32_bwd_side_kernel<true>,
-                             (const void*)f32_bwd_side_kernel<false>,
+        const void* fns[] = {(const void*)f32_write_kernel, (const void*)f32_bwd_side_kernel<true, false>,
+                             (const void*)f32_bwd_side_kernel<false, false>, (const void*)f32_bwd_side_kernel<true, true>,
+                             (const void*)f32_bwd_side_kernel<false, true>,
                              (const void*)f32_bwd_tiled_kernel<BWD_WRITE>, (const void*)f32_bwd_tiled_kernel<BWD_QUERY>,
                              (const void*)f32_bwd_tiled_kernel<BWD_KEY>, (const void*)f32_bwd_tiled_kernel<BWD_CQUERY>,
                              (const void*)f32_bwd_tiled_kernel<BWD_CKEY>};
@@ -933,6 +1043,7 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     const int Ei = int(E);
     const dim3 cgrid(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P));
     const int H = int(p.H), dr = int(p.dr), dv = int(p.dv), K = int(p.K), G = int(p.G);
+    const SideConfig side = side_config(K, dr, dv);
     if (bwd_tiled_applies(p)) {
         GMA_LAUNCH("f32_bwd_write", f32_bwd_tiled_kernel<BWD_WRITE>, grid, dim3(kThreads),
                    bwd_tiled_lds_bytes(BWD_WRITE, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
@@ -950,12 +1061,14 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
                    bwd_tiled_lds_bytes(BWD_QUERY, K, dr, dv), st, XQ, dO, p.Nq, H, dr, dv, K, p.seg_q, G, v.c, v.inv, mu,
                    static_cast<const float*>(memory), eps, dXQ, none, dpart, ppart, cnone, cnone, none, none, cnone,
                    cnone);
+    } else if (side.fast) {
+        GMA_LAUNCH("f32_bwd_query", (f32_bwd_side_kernel<true, true>), grid, dim3(kThreads), side.lds, st, XQ, dO, p.Nq,
+                   H, dr, dv, K, p.seg_q, G, side.T, v.c, v.inv, mu, static_cast<const float*>(memory), eps, dXQ, none,
+                   dpart, ppart);
     } else {
-        int T = kTile;
-        while (T > 8 && bwd_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
-        GMA_LAUNCH("f32_bwd_query", f32_bwd_side_kernel<true>, grid, dim3(kThreads), bwd_lds_bytes(T, dr, dv, K), st,
-                   XQ, dO, p.Nq, H, dr, dv, K, p.seg_q, G, T, v.c, v.inv, mu, static_cast<const float*>(memory), eps, dXQ,
-                   static_cast<float*>(nullptr), dpart, ppart);
+        GMA_LAUNCH("f32_bwd_query", (f32_bwd_side_kernel<true, false>), grid, dim3(kThreads), side.lds, st, XQ, dO,
+                   p.Nq, H, dr, dv, K, p.seg_q, G, side.T, v.c, v.inv, mu, static_cast<const float*>(memory), eps, dXQ,
+                   none, dpart, ppart);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, dpart, G, Ei, dmem);
@@ -965,12 +1078,14 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
                    bwd_tiled_lds_bytes(BWD_KEY, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
                    static_cast<const float*>(dmem), eps, dXK, dV, none, ppart_key, cnone, cnone, none, none,
                    static_cast<const float*>(gk_cache), cnone);
+    } else if (side.fast) {
+        GMA_LAUNCH("f32_bwd_key", (f32_bwd_side_kernel<false, true>), grid, dim3(kThreads), side.lds, st, XK, V, p.N, H,
+                   dr, dv, K, p.seg, G, side.T, v.c, v.inv, mu, static_cast<const float*>(dmem), eps, dXK, dV, none,
+                   ppart_key);
     } else {
-        int T = kTile;
-        while (T > 8 && bwd_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
-        GMA_LAUNCH("f32_bwd_key", f32_bwd_side_kernel<false>, grid, dim3(kThreads), bwd_lds_bytes(T, dr, dv, K), st,
-                   XK, V, p.N, H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, static_cast<const float*>(dmem), eps, dXK, dV,
-                   static_cast<float*>(nullptr), ppart_key);
+        GMA_LAUNCH("f32_bwd_key", (f32_bwd_side_kernel<false, false>), grid, dim3(kThreads), side.lds, st, XK, V, p.N,
+                   H, dr, dv, K, p.seg, G, side.T, v.c, v.inv, mu, static_cast<const float*>(dmem), eps, dXK, dV, none,
+                   ppart_key);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
@@ -1011,56 +1126,6 @@ __global__ void __launch_bounds__(kThreads) f32_suffix_kernel(float* __restrict_
         run += a;
     }
     if (dstate_in) dstate_in[size_t(p) * E + state_index(e, K, dv)] = run;
-}
-
-// gamma_tile with fp32 tables in LDS: c [K], 1/sigma2 and mu as [K][LR] rows (LR = d_r + 1),
-// the direct-form score of Eq. 16 in fp32, then the softmax of Eq. 3b.  Same contract as gamma_tile.
-__device__ void gamma_tile_lds(const float* __restrict__ X, int64_t n0, int rows, int T, int dr, int K,
-                               const float* c_l, const float* inv_l, const float* mu_l, float* xs, float* g) {
-    const int LR = dr + 1;
-    for (int i = threadIdx.x; i < T * dr; i += kThreads) {
-        const int t = i / dr;
-        xs[i] = (t < rows) ? X[(n0 + t) * dr + (i - t * dr)] : 0.0f;
-    }
-    __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int t = wave; t < T; t += kThreads / kWave) {
-        float* gt = g + size_t(t) * K;
-        if (t >= rows) {
-            for (int k = lane; k < K; k += kWave) gt[k] = 0.0f;
-            continue;
-        }
-        const float* xt = xs + t * dr;
-        float sc[4], m = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int k = lane + j * kWave;
-            sc[j] = -INFINITY;
-            if (k < K) {
-                const float *mk = mu_l + k * LR, *ik = inv_l + k * LR;
-                float q = 0.0f;
-                for (int d = 0; d < dr; ++d) {
-                    const float df = xt[d] - mk[d];
-                    q = fmaf(df * df, ik[d], q);
-                }
-                sc[j] = c_l[k] - 0.5f * q;
-                m = fmaxf(m, sc[j]);
-            }
-        }
-        m = wave_max(m);
-        float ev[4], sum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            ev[j] = (lane + j * kWave < K) ? expf(sc[j] - m) : 0.0f;
-            sum += ev[j];
-        }
-        sum = wave_sum(sum);
-        const float r = 1.0f / sum;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (lane + j * kWave < K) gt[lane + j * kWave] = ev[j] * r;
-    }
-    __syncthreads();
 }
 
 // Grid (G segments, P).  QUERY walks the segment's tiles forward from the memory before the
@@ -1404,13 +1469,16 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
         return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
     }
     // one element per thread: FAST (tables and running memory in LDS) with 64- or 32-position
-    // tiles when two workgroups still fit a CU; otherwise the general form: 64-position tiles when
-    // two fit, else the largest tile that lets two fit (down to 32), else the largest that fits
+    // tiles when two workgroups still fit a CU, else with the largest tile (down to 16) that fits
+    // one; otherwise the general form: 64-position tiles when two fit, else the largest tile that
+    // lets two fit (down to 32), else the largest that fits
     const size_t fast_extra = size_t(2 * K * (dr + 1) + 2 * K + K * (dv + 1)) * sizeof(float);
     int T = kTile;
     bool fast = false;
     for (int t = kTile; t >= 32 && !fast; t /= 2)
         if (bwdc_lds_bytes(t, dr, dv, K) + fast_extra <= kMaxLds / 2) fast = true, T = t;
+    for (int t = kTile; t >= 16 && !fast; t /= 2)
+        if (bwdc_lds_bytes(t, dr, dv, K) + fast_extra <= kMaxLds) fast = true, T = t;
     if (!fast) {
         while (T > 32 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds / 2) T /= 2;
         while (T > 8 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
