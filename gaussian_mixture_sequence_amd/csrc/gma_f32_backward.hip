@@ -82,14 +82,15 @@ size_t bwd_lds_bytes(int T, int dr, int dv, int K) { return size_t(T) * (dr + 2 
 // (reads the memory mem = [Vt | Z], writes dX_Q and the partial [dVt | dZ] of its rows);
 // otherwise the key side (reads dmem = [dVt | dZ], writes dV and dX_K).  Both write the
 // block's moment record pp (first tile writes, later tiles add: each entry has one owner).
-// FAST: the per-head tables (fp32) and the memory sit in LDS (rows padded by one element) and
-// the scores, dX and moments are fp32; otherwise they come from the fp64 tables in the workspace.
+// FAST: the per-head tables (fp32) sit in LDS (rows padded by one element), and the memory too
+// when mem_lds is set; the scores, dX and moments are then fp32.  Otherwise everything comes from
+// the fp64 tables and the memory in the workspace.
 template <bool QUERY, bool FAST>
 __global__ void __launch_bounds__(kThreads)
     f32_bwd_side_kernel(const float* __restrict__ X, const float* __restrict__ Y, int64_t N, int H, int dr, int dv,
                         int K, int64_t seg, int G, int T, const double* c, const double* inv, const float* mu,
                         const float* __restrict__ mem, float eps, float* __restrict__ dX, float* __restrict__ dY,
-                        float* __restrict__ mem_part, float* __restrict__ param_part) {
+                        float* __restrict__ mem_part, float* __restrict__ param_part, int mem_lds) {
     extern __shared__ float lds[];
     const int64_t p = blockIdx.y;
     const int gi = blockIdx.x, h = int(p % H);
@@ -108,9 +109,10 @@ __global__ void __launch_bounds__(kThreads)
     const double *ch = c + size_t(h) * K, *ih = inv + size_t(h) * K * dr;
     const float* mh = mu + size_t(h) * K * dr;
     const float* Vg = mem + size_t(p) * K * (dv + 1);  // [K][dv], then Z (or dVt, dZ)
-    const float* Vt = FAST ? Ml : Vg;
-    const float* Z = FAST ? Zl : Vg + size_t(K) * dv;
-    const int SV = FAST ? LV : dv;
+    const bool ML = FAST && mem_lds;
+    const float* Vt = ML ? Ml : Vg;
+    const float* Z = ML ? Zl : Vg + size_t(K) * dv;
+    const int SV = ML ? LV : dv;
     if (FAST) {
         for (int i = threadIdx.x; i < K * dr; i += kThreads) {
             const int k = i / dr, d = i - k * dr;
@@ -119,9 +121,10 @@ __global__ void __launch_bounds__(kThreads)
         }
         for (int k = threadIdx.x; k < K; k += kThreads) {
             cT[k] = float(ch[k]);
-            Zl[k] = Vg[K * dv + k];
+            if (ML) Zl[k] = Vg[K * dv + k];
         }
-        for (int i = threadIdx.x; i < K * dv; i += kThreads) Ml[(i / dv) * LV + i % dv] = Vg[i];
+        if (ML)
+            for (int i = threadIdx.x; i < K * dv; i += kThreads) Ml[(i / dv) * LV + i % dv] = Vg[i];
         __syncthreads();
     }
     const int E = K * (dv + 1), PE = 2 * K * dr + K;
@@ -972,18 +975,25 @@ hipError_t reduce_params(const Plan& p, const float* part, int B, const double* 
 
 // The one-element-per-thread passes: FAST (tables and memory in LDS) with the largest tile (64
 // down to 16 positions) that fits, else the general form with the largest tile that fits.
+// With larger K the tables alone stay in LDS (the memory is read from the workspace) and the
+// tiles shrink to 8 positions.
 struct SideConfig {
     bool fast;
+    int mem_lds;
     int T;
     size_t lds;
 };
 SideConfig side_config(int K, int dr, int dv) {
-    const size_t extra = size_t(2 * K * (dr + 1) + 2 * K + K * (dv + 1)) * sizeof(float);
+    const size_t tables = size_t(2 * K * (dr + 1) + K) * sizeof(float);
+    const size_t memory = size_t(K * (dv + 1) + K) * sizeof(float);
     for (int t = kTile; t >= 16; t /= 2)
-        if (bwd_lds_bytes(t, dr, dv, K) + extra <= kMaxLds) return {true, t, bwd_lds_bytes(t, dr, dv, K) + extra};
+        if (bwd_lds_bytes(t, dr, dv, K) + tables + memory <= kMaxLds)
+            return {true, 1, t, bwd_lds_bytes(t, dr, dv, K) + tables + memory};
+    for (int t = kTile; t >= 8; t /= 2)
+        if (bwd_lds_bytes(t, dr, dv, K) + tables <= kMaxLds) return {true, 0, t, bwd_lds_bytes(t, dr, dv, K) + tables};
     int T = kTile;
     while (T > 8 && bwd_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
-    return {false, T, bwd_lds_bytes(T, dr, dv, K)};
+    return {false, 0, T, bwd_lds_bytes(T, dr, dv, K)};
 }
 
 hipError_t bwd_allow_lds() {
@@ -1064,11 +1074,11 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     } else if (side.fast) {
         GMA_LAUNCH("f32_bwd_query", (f32_bwd_side_kernel<true, true>), grid, dim3(kThreads), side.lds, st, XQ, dO, p.Nq,
                    H, dr, dv, K, p.seg_q, G, side.T, v.c, v.inv, mu, static_cast<const float*>(memory), eps, dXQ, none,
-                   dpart, ppart);
+                   dpart, ppart, side.mem_lds);
     } else {
         GMA_LAUNCH("f32_bwd_query", (f32_bwd_side_kernel<true, false>), grid, dim3(kThreads), side.lds, st, XQ, dO,
                    p.Nq, H, dr, dv, K, p.seg_q, G, side.T, v.c, v.inv, mu, static_cast<const float*>(memory), eps, dXQ,
-                   none, dpart, ppart);
+                   none, dpart, ppart, side.mem_lds);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, dpart, G, Ei, dmem);
@@ -1081,11 +1091,11 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     } else if (side.fast) {
         GMA_LAUNCH("f32_bwd_key", (f32_bwd_side_kernel<false, true>), grid, dim3(kThreads), side.lds, st, XK, V, p.N, H,
                    dr, dv, K, p.seg, G, side.T, v.c, v.inv, mu, static_cast<const float*>(dmem), eps, dXK, dV, none,
-                   ppart_key);
+                   ppart_key, side.mem_lds);
     } else {
         GMA_LAUNCH("f32_bwd_key", (f32_bwd_side_kernel<false, false>), grid, dim3(kThreads), side.lds, st, XK, V, p.N,
                    H, dr, dv, K, p.seg, G, side.T, v.c, v.inv, mu, static_cast<const float*>(dmem), eps, dXK, dV, none,
-                   ppart_key);
+                   ppart_key, side.mem_lds);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
@@ -1132,16 +1142,16 @@ __global__ void __launch_bounds__(kThreads) f32_suffix_kernel(float* __restrict_
 // segment (state: [Vt (K dv) | Z (K)]), writes dX_Q, D_i and a_i of every row (rowda), the
 // segment's total of what its queries send to the memory (seg_part) and its moments.  KEY walks
 // the tiles backward from what the later segments' queries sent (state), writes dX_K, dV and its
-// moments.  FAST: the per-head tables (fp32) and the running memory live in LDS (rows padded by
-// one element), the scores, dX and moments are fp32; otherwise they are read from the fp64 tables
-// and the running memory is advanced in place in the workspace.
+// moments.  FAST: the per-head tables (fp32) live in LDS (rows padded by one element), and the
+// running memory too when mem_lds is set; the scores, dX and moments are fp32.  Otherwise the
+// tables are the fp64 ones, and a memory outside LDS is advanced in place in the workspace.
 template <bool QUERY, bool FAST>
 __global__ void __launch_bounds__(kThreads)
     f32_bwdc_kernel(const float* __restrict__ XQ, const float* __restrict__ XK, const float* __restrict__ V,
                     const float* __restrict__ dO, int64_t N, int H, int dr, int dv, int K, int64_t seg, int G, int T,
                     const double* c, const double* inv, const float* mu, float* state, float eps,
                     float* __restrict__ rowda, float* __restrict__ dX, float* __restrict__ dV,
-                    float* __restrict__ seg_part, float* __restrict__ param_part) {
+                    float* __restrict__ seg_part, float* __restrict__ param_part, int mem_lds) {
     extern __shared__ float lds[];
     const int64_t p = blockIdx.y;
     const int gi = blockIdx.x, h = int(p % H);
@@ -1165,10 +1175,11 @@ __global__ void __launch_bounds__(kThreads)
     const float* mh = mu + size_t(h) * K * dr;
     const int E = K * (dv + 1), PE = 2 * K * dr + K;
     float* Sg = state + (size_t(p) * G + gi) * E;  // [K][dv], then Z
-    // the running memory: LDS rows of LV (FAST) or the workspace record
-    float* St = FAST ? Sm : Sg;
-    float* Zs = FAST ? Sz : Sg + size_t(K) * dv;
-    const int SL = FAST ? LV : dv;
+    // the running memory: LDS rows of LV or the workspace record
+    const bool ML = FAST && mem_lds;
+    float* St = ML ? Sm : Sg;
+    float* Zs = ML ? Sz : Sg + size_t(K) * dv;
+    const int SL = ML ? LV : dv;
     if (FAST) {
         for (int i = threadIdx.x; i < K * dr; i += kThreads) {
             const int k = i / dr, d = i - k * dr;
@@ -1177,9 +1188,10 @@ __global__ void __launch_bounds__(kThreads)
         }
         for (int k = threadIdx.x; k < K; k += kThreads) {
             cT[k] = float(ch[k]);
-            Sz[k] = Sg[K * dv + k];
+            if (ML) Sz[k] = Sg[K * dv + k];
         }
-        for (int i = threadIdx.x; i < K * dv; i += kThreads) Sm[(i / dv) * LV + i % dv] = Sg[i];
+        if (ML)
+            for (int i = threadIdx.x; i < K * dv; i += kThreads) Sm[(i / dv) * LV + i % dv] = Sg[i];
         __syncthreads();
     }
     float* sp = QUERY ? seg_part + (size_t(p) * G + gi) * E : nullptr;
@@ -1470,36 +1482,41 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
     }
     // one element per thread: FAST (tables and running memory in LDS) with 64- or 32-position
     // tiles when two workgroups still fit a CU, else with the largest tile (down to 16) that fits
-    // one; otherwise the general form: 64-position tiles when two fit, else the largest tile that
-    // lets two fit (down to 32), else the largest that fits
-    const size_t fast_extra = size_t(2 * K * (dr + 1) + 2 * K + K * (dv + 1)) * sizeof(float);
-    int T = kTile;
+    // one; else the tables alone in LDS (tiles down to 8); otherwise the general form: 64-position
+    // tiles when two fit, else the largest tile that lets two fit (down to 32), else the largest
+    // that fits
+    const size_t tables = size_t(2 * K * (dr + 1) + K) * sizeof(float);
+    const size_t memory = size_t(K * (dv + 1) + K) * sizeof(float);
+    int T = kTile, mem_lds = 1;
     bool fast = false;
     for (int t = kTile; t >= 32 && !fast; t /= 2)
-        if (bwdc_lds_bytes(t, dr, dv, K) + fast_extra <= kMaxLds / 2) fast = true, T = t;
+        if (bwdc_lds_bytes(t, dr, dv, K) + tables + memory <= kMaxLds / 2) fast = true, T = t;
     for (int t = kTile; t >= 16 && !fast; t /= 2)
-        if (bwdc_lds_bytes(t, dr, dv, K) + fast_extra <= kMaxLds) fast = true, T = t;
+        if (bwdc_lds_bytes(t, dr, dv, K) + tables + memory <= kMaxLds) fast = true, T = t;
+    for (int t = kTile; t >= 8 && !fast; t /= 2)
+        if (bwdc_lds_bytes(t, dr, dv, K) + tables <= kMaxLds) fast = true, T = t, mem_lds = 0;
     if (!fast) {
+        mem_lds = 0;
         while (T > 32 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds / 2) T /= 2;
         while (T > 8 && bwdc_lds_bytes(T, dr, dv, K) > kMaxLds) T /= 2;
     }
-    const size_t lds = bwdc_lds_bytes(T, dr, dv, K) + (fast ? fast_extra : 0);
+    const size_t lds = bwdc_lds_bytes(T, dr, dv, K) + (fast ? tables + (mem_lds ? memory : 0) : 0);
     if (fast)
         GMA_LAUNCH("f32_bwdc_query", (f32_bwdc_kernel<true, true>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N,
-                   H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, states, eps, rowda, dXQ, none, seg_part, ppart);
+                   H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, states, eps, rowda, dXQ, none, seg_part, ppart, mem_lds);
     else
         GMA_LAUNCH("f32_bwdc_query", (f32_bwdc_kernel<true, false>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N,
-                   H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, states, eps, rowda, dXQ, none, seg_part, ppart);
+                   H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, states, eps, rowda, dXQ, none, seg_part, ppart, mem_lds);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     GMA_LAUNCH("f32_bwdc_suffix", f32_suffix_kernel, egrid, dim3(kThreads), 0, st, seg_part, G, Ei, dstate_out, dstate_in,
                K, dv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (fast)
         GMA_LAUNCH("f32_bwdc_key", (f32_bwdc_kernel<false, true>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N, H,
-                   dr, dv, K, p.seg, G, T, v.c, v.inv, mu, seg_part, eps, rowda, dXK, dV, none, ppart_key);
+                   dr, dv, K, p.seg, G, T, v.c, v.inv, mu, seg_part, eps, rowda, dXK, dV, none, ppart_key, mem_lds);
     else
         GMA_LAUNCH("f32_bwdc_key", (f32_bwdc_kernel<false, false>), grid, dim3(kThreads), lds, st, XQ, XK, V, dO, p.N,
-                   H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, seg_part, eps, rowda, dXK, dV, none, ppart_key);
+                   H, dr, dv, K, p.seg, G, T, v.c, v.inv, mu, seg_part, eps, rowda, dXK, dV, none, ppart_key, mem_lds);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
 }

@@ -65,6 +65,7 @@ CASES = [
     case(5000, 93, d_r=32, d_v=64, K=64),              # several splits per problem
     case(300, 94, B=1, H=1, d_r=128, d_v=128, K=256),  # maximum dims (half-height tiles)
     case(700, 95, B=3, H=2, d_r=64, d_v=32, K=128, mu_std=1.5),
+    case(500, 96, B=1, H=2, d_r=64, d_v=64, K=256),     # K beyond the LDS memory: tables only
 ]
 
 
@@ -187,6 +188,7 @@ CAUSAL_CASES = [
     case(1000, 108, B=2, H=2, d_r=32, d_v=32, K=32),
     case(333, 109, B=2, H=1, d_r=64, d_v=64, K=32),     # ragged tail, one tile per segment
     case(4100, 110, B=4, H=16, d_r=64, d_v=48, K=20),   # several tiles per segment, K below a row group
+    case(500, 111, B=1, H=2, d_r=64, d_v=64, K=256),
 ]
 
 
