@@ -124,3 +124,70 @@ def backward_causal(XQ, XK, V, mu, sigma2, pi, eps, dO, state_in=None, dstate_ou
                 out["dsigma2"][h] += ds2
                 out["dpi"][h] += dpi
     return out
+
+
+def backward_magnitudes(XQ, XK, V, mu, sigma2, pi, eps, dO, causal=False, state_in=None, dstate_out=None) -> dict:
+    """Per-entry scale of every gradient of backward_bidir (causal=False) or backward_causal
+    (causal=True): the formulas above (Sec. 4.1 Eq. 17-20 through Eq. 5-8, or Eq. 6b/8b) evaluated
+    on magnitudes, every input and every intermediate replaced by its absolute value and every
+    difference by a sum, e.g. for the query side
+      |g^Q|_ik = (|dO_i| . |Vt|_k + |a|_i Z_k) / D_i,  |ds|_ik = gamma_ik (|g|_ik + sum_j gamma_ij |g|_ij),
+      |dX|_id = sum_k |ds|_ik |x_id - mu_kd| / sigma2_kd.
+    Each entry bounds the sum of the absolute values of the terms that form the gradient entry (so
+    it is at least the entry's magnitude); an evaluation whose every operation carries a relative
+    error u is off by at most a modest multiple of u times it.  Same keys and shapes as the
+    gradients (dstate_in only for a carried memory)."""
+    from . import _f64, responsibilities
+    XQ, XK, V, dO = (_f64(t) for t in (XQ, XK, V, dO))
+    mu, s2, pi = (_f64(t) for t in (mu, sigma2, pi))
+    GQ, GK = responsibilities(XQ, mu, s2, pi), responsibilities(XK, mu, s2, pi)
+    B, H, N, dr = XQ.shape
+    K, dv = mu.shape[1], V.shape[-1]
+    out = {"dXQ": np.zeros_like(XQ), "dXK": np.zeros_like(XK), "dV": np.zeros_like(V),
+           "dmu": np.zeros_like(mu), "dsigma2": np.zeros_like(s2), "dpi": np.zeros_like(pi)}
+    carried = state_in is not None or dstate_out is not None
+    sin = np.abs(_f64(state_in)) if state_in is not None else np.zeros((B, H, K, dv + 1))
+    dso = np.abs(_f64(dstate_out)) if dstate_out is not None else np.zeros((B, H, K, dv + 1))
+    if carried:
+        out["dstate_in"] = dso.copy()
+    for b in range(B):
+        for h in range(H):
+            gq, gk, v, do = GQ[b, h], GK[b, h], np.abs(V[b, h]), np.abs(dO[b, h])
+            if gq.shape[0] == 0 or gk.shape[0] == 0:
+                continue
+            if causal:
+                vt = sin[b, h, None, :, :dv] + np.cumsum(gk[:, :, None] * v[:, None, :], axis=0)   # [N,K,dv]
+                z = sin[b, h, None, :, dv] + np.cumsum(gk, axis=0)                                  # [N,K]
+                d_ = np.einsum("ik,ik->i", gq, z) + eps
+                o = np.einsum("ik,ikc->ic", gq, vt) / d_[:, None]
+                a = (do * o).sum(axis=1)
+                g_q = (np.einsum("ic,ikc->ik", do, vt) + a[:, None] * z) / d_[:, None]
+                dvt = np.cumsum((gq[:, :, None] * (do / d_[:, None])[:, None, :])[::-1], axis=0)[::-1]
+                dz = np.cumsum((gq * (a / d_)[:, None])[::-1], axis=0)[::-1]
+                dvt = dvt + dso[b, h, None, :, :dv]
+                dz = dz + dso[b, h, None, :, dv]
+                if carried:
+                    out["dstate_in"][b, h, :, :dv] = dvt[0]
+                    out["dstate_in"][b, h, :, dv] = dz[0]
+                out["dV"][b, h] = np.einsum("jk,jkc->jc", gk, dvt)
+                g_k = np.einsum("jc,jkc->jk", v, dvt) + dz
+            else:
+                vt, z = gk.T @ v, gk.sum(axis=0)
+                d_ = gq @ z + eps
+                o = (gq @ vt) / d_[:, None]
+                a = (do * o).sum(axis=1)
+                g_q = (do @ vt.T + a[:, None] * z[None, :]) / d_[:, None]
+                dvt = gq.T @ (do / d_[:, None])
+                dz = gq.T @ (a / d_)
+                out["dV"][b, h] = gk @ dvt
+                g_k = v @ dvt.T + dz[None, :]
+            for x, g, gam, key in ((XQ[b, h], g_q, gq, "dXQ"), (XK[b, h], g_k, gk, "dXK")):
+                ds = gam * (g + (gam * g).sum(axis=1, keepdims=True))
+                diff = np.abs(x[:, None, :] - mu[h][None])                  # [N,K,d]
+                w = ds[:, :, None] * diff / s2[h][None]
+                out[key][b, h] = w.sum(axis=1)
+                out["dmu"][h] += w.sum(axis=0)
+                out["dsigma2"][h] += (ds[:, :, None] * 0.5 * (diff * diff / (s2[h] * s2[h])[None]
+                                                               + 1.0 / s2[h][None])).sum(axis=0)
+                out["dpi"][h] += ds.sum(axis=0) / pi[h]
+    return out

@@ -769,3 +769,144 @@ def test_backward_causal_state_piecewise_equals_whole():
                                    atol=1e-13, err_msg=key)
     for key in ("dmu", "dsigma2", "dpi"):
         np.testing.assert_allclose(first[key] + second[key], whole[key], rtol=1e-10, atol=1e-13, err_msg=key)
+
+
+# ---- magnitude evaluation of the backward formulas (the per-entry scale of the GPU tests)
+
+def _mag_cases(rng):
+    xq, xk, v, mu, s2, pi, do = _backward_problem(rng, B=2, H=2, N=13, dr=3, dv=4, K=5)
+    s = rng.standard_normal((2, 2, 5, 5))
+    s[..., -1] = np.abs(s[..., -1]) * 2
+    ds = rng.standard_normal((2, 2, 5, 5))
+    return (xq, xk, v, mu, s2, pi, do), [dict(causal=False), dict(causal=True),
+                                         dict(causal=True, state_in=s, dstate_out=ds)]
+
+
+def _grads(args, eps, causal=False, **kw):
+    xq, xk, v, mu, s2, pi, do = args
+    if causal:
+        return oracle.backward.backward_causal(xq, xk, v, mu, s2, pi, eps, do, **kw)
+    return oracle.backward.backward_bidir(xq, xk, v, mu, s2, pi, eps, do)
+
+
+def _mags(args, eps, **kw):
+    xq, xk, v, mu, s2, pi, do = args
+    return oracle.backward.backward_magnitudes(xq, xk, v, mu, s2, pi, eps, do, **kw)
+
+
+def test_backward_magnitudes_bound_every_entry():
+    """Triangle inequality: each entry's magnitude is at least the entry's absolute value, for the
+    bidirectional, causal and carried-memory backward; with a context of another length too."""
+    rng = np.random.default_rng(70)
+    args, variants = _mag_cases(rng)
+    for kw in variants:
+        g = _grads(args, 1e-3, **kw)
+        m = _mags(args, 1e-3, **kw)
+        for k in g:
+            assert (m[k] >= np.abs(g[k]) * (1 - 1e-12)).all(), (kw.get("causal"), k)
+    xq, xk, v, mu, s2, pi, do = args
+    g = oracle.backward.backward_bidir(xq[:, :, :7], xk, v, mu, s2, pi, 1e-3, do[:, :, :7])
+    m = oracle.backward.backward_magnitudes(xq[:, :, :7], xk, v, mu, s2, pi, 1e-3, do[:, :, :7])
+    for k in g:
+        assert g[k].shape == m[k].shape and (m[k] >= np.abs(g[k]) * (1 - 1e-12)).all(), k
+
+
+def test_backward_magnitudes_bound_value_and_gradient_perturbations():
+    """Every term of every gradient entry has exactly one factor from V or from the upstream
+    gradient dO, or one from each (the gradients are linear in dO and, apart from dV, linear in V
+    for fixed routing).  Perturbing each entry of V and dO by a relative amount of at most d then
+    moves each gradient entry by at most (2 d + d^2) times its magnitude."""
+    rng = np.random.default_rng(71)
+    args, variants = _mag_cases(rng)
+    xq, xk, v, mu, s2, pi, do = args
+    d = 1e-3
+    for kw in variants:
+        g = _grads(args, 1e-3, **kw)
+        m = _mags(args, 1e-3, **kw)
+        for trial in range(4):
+            pv = v * (1 + d * rng.uniform(-1, 1, v.shape))
+            pd = do * (1 + d * rng.uniform(-1, 1, do.shape))
+            kw2 = dict(kw)
+            if "dstate_out" in kw:  # the memory and its gradient enter like V and dO
+                kw2["state_in"] = kw["state_in"] * (1 + d * rng.uniform(-1, 1, kw["state_in"].shape))
+                kw2["dstate_out"] = kw["dstate_out"] * (1 + d * rng.uniform(-1, 1, kw["dstate_out"].shape))
+            gp = _grads((xq, xk, pv, mu, s2, pi, pd), 1e-3, **kw2)
+            for k in g:
+                if k == "dstate_in" or "dstate_out" in kw:
+                    continue  # D depends on the carried Z: not bilinear there
+                assert (np.abs(gp[k] - g[k]) <= (2 * d + d * d) * m[k] * (1 + 1e-9) + 1e-15).all(), (kw, k)
+
+
+def test_backward_magnitudes_exact_without_cancellation():
+    """With a nonnegative upstream gradient every term of dV (sum over k of gamma^K dVt, dVt a
+    gamma-weighted sum of dO / D) is nonnegative, so its magnitude is dV itself; magnitudes are
+    positively homogeneous in dO and do not see its sign."""
+    rng = np.random.default_rng(72)
+    args, variants = _mag_cases(rng)
+    xq, xk, v, mu, s2, pi, do = args
+    pos = (xq, xk, v, mu, s2, pi, np.abs(do))
+    for kw in variants[:2]:
+        g = _grads(pos, 1e-3, **kw)
+        m = _mags(pos, 1e-3, **kw)
+        np.testing.assert_allclose(m["dV"], g["dV"], rtol=1e-12)
+        m2 = oracle.backward.backward_magnitudes(xq, xk, v, mu, s2, pi, 1e-3, -2.5 * do, **kw)
+        m1 = _mags(args, 1e-3, **kw)
+        for k in m1:
+            np.testing.assert_allclose(m2[k], 2.5 * m1[k], rtol=1e-12)
+
+
+def _expanded_magnitudes(xq, xk, v, mu, s2, pi, eps, do, causal):
+    """The definition the magnitude evaluation stands for, on one tiny (batch, head) problem: every
+    gradient written out as a sum of signed monomials in the leaves gamma^Q, gamma^K, V, dO, x - mu,
+    1/sigma2, 1/pi, Z^(i) and D_i (Eq. 5-8 or 6b/8b, then Eq. 17-20), each monomial enumerated
+    term by term, and the absolute values of the monomials summed."""
+    A = oracle.responsibilities(xq, mu, s2, pi)[0, 0]
+    Bk = oracle.responsibilities(xk, mu, s2, pi)[0, 0]
+    X, Y, V, dO = xq[0, 0], xk[0, 0], v[0, 0], do[0, 0]
+    mu, s2, pi = mu[0], s2[0], pi[0]
+    N, K = A.shape
+    dv, dr = V.shape[1], X.shape[1]
+    M = np.tril(np.ones((N, N))) if causal else np.ones((N, N))     # M[i, j]: query i reads key j
+    Z = M @ Bk                                                      # Z^(i)_k, a positive leaf
+    D = (A * Z).sum(axis=1) + eps
+    a_mono = [[dO[i, c] * A[i, kk] * Bk[j, kk] * V[j, c] / D[i]
+               for c in range(dv) for kk in range(K) for j in range(N) if M[i, j]] for i in range(N)]
+    gq = [[[dO[i, c] * Bk[j, k] * V[j, c] / D[i] for c in range(dv) for j in range(N) if M[i, j]]
+           + [-m * Z[i, k] / D[i] for m in a_mono[i]] for k in range(K)] for i in range(N)]
+    dvt = [[[[A[i, k] * dO[i, c] / D[i] for i in range(N) if M[i, j]] for c in range(dv)] for k in range(K)]
+           for j in range(N)]
+    dz = [[[-A[i, k] * m / D[i] for i in range(N) if M[i, j] for m in a_mono[i]] for k in range(K)] for j in range(N)]
+    gk = [[[V[j, c] * m for c in range(dv) for m in dvt[j][k][c]] + dz[j][k] for k in range(K)] for j in range(N)]
+    out = {"dV": np.array([[sum(abs(Bk[j, k] * m) for k in range(K) for m in dvt[j][k][c]) for c in range(dv)]
+                           for j in range(N)]),
+           "dmu": np.zeros((K, dr)), "dsigma2": np.zeros((K, dr)), "dpi": np.zeros(K)}
+    for x, g, gam, key in ((X, gq, A, "dXQ"), (Y, gk, Bk, "dXK")):
+        dx = np.zeros((N, dr))
+        for i in range(N):
+            for k in range(K):
+                ds = [gam[i, k] * m for m in g[i][k]] + [-gam[i, k] * gam[i, l] * m for l in range(K) for m in g[i][l]]
+                tot = sum(abs(m) for m in ds)
+                for d in range(dr):
+                    diff = abs(x[i, d] - mu[k, d])
+                    dx[i, d] += tot * diff / s2[k, d]
+                    out["dmu"][k, d] += tot * diff / s2[k, d]
+                    out["dsigma2"][k, d] += tot * 0.5 * (diff * diff / s2[k, d] ** 2 + 1.0 / s2[k, d])
+                out["dpi"][k] += tot / pi[k]
+        out[key] = dx
+    return out
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_magnitudes_equal_expanded_monomial_sums(causal):
+    """The nested magnitude evaluation equals the sum of |monomial| over the fully expanded
+    gradients, enumerated term by term (a dropped term, a lost factor or a sign kept where it
+    should not be makes them differ)."""
+    rng = np.random.default_rng(73 + causal)
+    xq, xk, v, mu, s2, pi = rand_problem(rng, 1, 1, 4, 2, 2, 3)
+    do = rng.standard_normal((1, 1, 4, 2))
+    m = oracle.backward.backward_magnitudes(xq, xk, v, mu, s2, pi, 0.01, do, causal=causal)
+    ref = _expanded_magnitudes(xq, xk, v, mu, s2, pi, 0.01, do, causal)
+    for k in ("dXQ", "dXK", "dV"):
+        np.testing.assert_allclose(m[k][0, 0], ref[k], rtol=1e-11, err_msg=k)
+    for k in ("dmu", "dsigma2", "dpi"):
+        np.testing.assert_allclose(m[k][0], ref[k], rtol=1e-11, err_msg=k)
