@@ -20,14 +20,16 @@ LIB_PATH = os.path.join(_PKG, "libgma.so")
 GMA_OK = 0
 STATUS_NAMES = ["GMA_OK", "GMA_ERR_NULL_POINTER", "GMA_ERR_BAD_SHAPE", "GMA_ERR_BAD_VALUE",
                 "GMA_ERR_UNSUPPORTED", "GMA_ERR_MISALIGNED", "GMA_ERR_WORKSPACE_TOO_SMALL",
-                "GMA_ERR_HIP"]
+                "GMA_ERR_HIP", "GMA_ERR_TIMEOUT"]
+GMA_ERR_TIMEOUT = 8
 GMA_F32, GMA_BF16 = 0, 1
 GMA_OP_RESPONSIBILITIES, GMA_OP_BIDIR, GMA_OP_CAUSAL, GMA_OP_DIAGNOSTICS = 0, 1, 2, 3
 GMA_OP_BACKWARD_BIDIR, GMA_OP_BACKWARD_CAUSAL = 4, 5
 EXPORTED = ["gma_status_string", "gma_workspace_size", "gma_responsibilities", "gma_forward_bidir",
             "gma_forward_causal", "gma_forward_causal_state", "gma_cross_workspace_size", "gma_forward_cross", "gma_responsibility_diagnostics", "gma_backward_bidir",
             "gma_backward_causal", "gma_backward_causal_state", "gma_backward_cross_workspace_size", "gma_backward_cross", "gma_profiling",
-            "gma_profiling_collect", "gma_set_wait_limit"]
+            "gma_profiling_collect", "gma_set_wait_limit", "gma_device_status", "gma_set_single_launch",
+            "gma_plan_info"]
 WAIT_LIMIT_DEFAULT = 1 << 18  # GMA_WAIT_LIMIT_DEFAULT
 
 
@@ -45,6 +47,11 @@ class KernelStat(ctypes.Structure):
 class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("N", ctypes.c_int64),
                 ("d_r", ctypes.c_int64), ("d_v", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("splits", "rows_per_split", "workgroups", "threads_per_workgroup",
+                                              "lds_bytes", "waits_on_all_splits", "resident_bound")]
 
 
 class CrossShape(ctypes.Structure):
@@ -106,6 +113,12 @@ def load() -> ctypes.CDLL:
             lib.gma_profiling_collect.restype = i32
             lib.gma_set_wait_limit.argtypes = [ctypes.c_uint32]
             lib.gma_set_wait_limit.restype = i32
+            lib.gma_device_status.argtypes = [vp]
+            lib.gma_device_status.restype = i32
+            lib.gma_set_single_launch.argtypes = [ctypes.c_int]
+            lib.gma_set_single_launch.restype = i32
+            lib.gma_plan_info.argtypes = [i32, shp, i32, i32, ctypes.POINTER(PlanInfo)]
+            lib.gma_plan_info.restype = i32
             _lib = lib
     return _lib
 
@@ -392,3 +405,25 @@ def gma_profiling_collect(capacity: int = 64):
 def gma_set_wait_limit(polls: int) -> None:
     """Bound on the hand-off waits of the single-launch bf16 forwards (see gma.h)."""
     _check(load().gma_set_wait_limit(int(polls)), "gma_set_wait_limit")
+
+
+def gma_device_status(stream=None) -> int:
+    """Waits for the stream and returns (and clears) the device's status: GMA_OK, or GMA_ERR_TIMEOUT
+    when a single-launch forward's hand-off wait ran out since the last query."""
+    st = load().gma_device_status(_stream(stream))
+    if st not in (GMA_OK, GMA_ERR_TIMEOUT):
+        raise GmaError(st, "gma_device_status")
+    return st
+
+
+def gma_set_single_launch(enable: bool) -> None:
+    """Allow (default) or forbid the bf16 forwards' single launches with in-launch hand-offs."""
+    _check(load().gma_set_single_launch(1 if enable else 0), "gma_set_single_launch")
+
+
+def gma_plan_info(op: int, B: int, H: int, N: int, d_r: int, d_v: int, K: int, io_dtype: int, chunk: int = 0) -> dict:
+    """The device-independent split of a forward (see gma_plan_info in gma.h) as a dict."""
+    info = PlanInfo()
+    _check(load().gma_plan_info(op, ctypes.byref(Shape(B, H, N, d_r, d_v, K)), io_dtype, chunk, ctypes.byref(info)),
+           "gma_plan_info")
+    return {n: getattr(info, n) for n, _ in PlanInfo._fields_}

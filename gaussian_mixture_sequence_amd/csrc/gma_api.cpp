@@ -23,10 +23,18 @@ constexpr int64_t kBidirBlocks = 512;   // target workgroups for the split-N wri
                                         // (two resident per CU: one wave of workgroups)
 constexpr int64_t kCausalBlocks = 512;  // target workgroups for the segmented scan
 constexpr int64_t kBackwardBlocks = 2048;  // target workgroups for the causal backward's segments
+constexpr int64_t kDeviceCUs = 256;        // compute units of an MI355X (planning is device-independent)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tiles of 32 components the bf16 kernels are compiled for: the smallest of 1, 2, 4, 8 that
+// holds K (K <= 256 is checked before).
+int64_t bf16_component_tiles(int64_t K) {
+    const int64_t t = cdiv(std::max<int64_t>(K, 1), 32);
+    return t <= 1 ? 1 : t <= 2 ? 2 : t <= 4 ? 4 : 8;
+}
 
 gma_status_t check_dims(gma_op_t op, const gma_shape_t& s, gma_dtype_t io) {
     if (s.B < 0 || s.H < 0 || s.N < 0) return GMA_ERR_BAD_SHAPE;
@@ -53,6 +61,16 @@ gma_status_t check_dims(gma_op_t op, const gma_shape_t& s, gma_dtype_t io) {
 }  // namespace
 
 void layout(Plan* pl);
+
+// Workgroups the bidirectional split aims at.  The bf16 forward runs as one launch whose
+// workgroups wait on every other workgroup of their problem, so there the whole grid must be
+// resident at once: P G stays within what the kernel's LDS and declared waves let every CU
+// of a 256-CU MI355X hold (for P beyond that, one split per problem, which waits on nothing
+// else).  The fp32 forward runs its phases as separate launches and takes two per CU.
+int64_t bidir_split_target(const Plan& p) {
+    if (p.io != GMA_BF16) return kBidirBlocks;
+    return kDeviceCUs * bf16_bidir_per_cu(p.dr, p.Kp / 32, p.dv / 32);
+}
 
 // fp32 copies of X_Q, X_K, V, dO (inputs) and dX_Q, dX_K, dV (outputs) for a bf16 backward, in
 // that order after the fp32 passes' regions (query-side arrays of N_q rows, key-side of N).
@@ -114,7 +132,9 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
     p.dv = (op == GMA_OP_BIDIR || op == GMA_OP_CAUSAL) ? s.d_v : 0;
     p.K = s.K;
     p.P = s.B * s.H;
-    p.Kp = (io == GMA_BF16) ? round_up(size_t(s.K), 32) : s.K;
+    // bf16: K padded to 1, 2, 4 or 8 tiles of 32 components (the compiled MFMA tilings);
+    // padded components get a score of -inf and so a responsibility of exactly 0
+    p.Kp = (io == GMA_BF16) ? 32 * bf16_component_tiles(s.K) : s.K;
     p.chunk = (op == GMA_OP_CAUSAL) ? chunk : 0;
 
     // parameter tables: the fp32 path keeps 1/sigma2 and the score constant in fp64; the bf16
@@ -127,7 +147,7 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
     p.G = 1;
     p.seg = round_up(size_t(std::max<int64_t>(p.N, 1)), kTokenTile);
     if (op == GMA_OP_BIDIR && p.P > 0 && p.N > 0) {
-        int64_t g = std::min(cdiv(kBidirBlocks, p.P), cdiv(p.N, 512));
+        int64_t g = std::min(bidir_split_target(p) / p.P, cdiv(p.N, 512));
         g = std::max<int64_t>(g, 1);
         p.seg = round_up(size_t(cdiv(p.N, g)), kTokenTile);
         p.G = cdiv(p.N, p.seg);
@@ -192,7 +212,7 @@ gma_status_t make_cross_plan(const gma_cross_shape_t& s, gma_dtype_t io, Plan* p
     p.G = 1;
     if (p.P > 0) {
         const int64_t n = std::max(p.N, p.Nq);
-        p.G = std::max<int64_t>(1, std::min(cdiv(kBidirBlocks, p.P), cdiv(std::max<int64_t>(n, 1), 512)));
+        p.G = std::max<int64_t>(1, std::min(bidir_split_target(p) / p.P, cdiv(std::max<int64_t>(n, 1), 512)));
     }
     p.seg = round_up(size_t(cdiv(std::max<int64_t>(p.N, 1), p.G)), kTokenTile);
     p.seg_q = round_up(size_t(cdiv(std::max<int64_t>(p.Nq, 1), p.G)), kTokenTile);
@@ -237,9 +257,81 @@ uint64_t launch_token() {
 
 namespace {
 std::atomic<uint32_t> g_wait_limit{GMA_WAIT_LIMIT_DEFAULT};
+std::atomic<int> g_single_launch{1};
 }  // namespace
 
 uint32_t wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
+bool single_launch_enabled() { return g_single_launch.load(std::memory_order_relaxed) != 0; }
+
+// ---- per-device error word ----------------------------------------------------------
+// Kernels OR kDevErrTimeout into d_error_word when a hand-off wait runs out;
+// gma_device_status moves it into d_error_taken (an atomic exchange on the device, so no
+// bit raised meanwhile is lost) and copies that to the host.  Each device has its own
+// copy of both words; their addresses are resolved once per device, with it current.
+__device__ uint32_t d_error_word;
+__device__ uint32_t d_error_taken;
+
+__global__ void take_error_kernel(uint32_t* word, uint32_t* taken) {
+    if (threadIdx.x == 0) *taken = atomicExch(word, 0u);
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+struct DeviceWords {
+    std::once_flag once;
+    hipError_t status = hipSuccess;
+    uint32_t* word = nullptr;
+    uint32_t* taken = nullptr;
+};
+DeviceWords g_words[kMaxDevices];
+
+hipError_t device_words(DeviceWords** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    DeviceWords& w = g_words[dev];
+    std::call_once(w.once, [&w] {
+        w.status = hipGetSymbolAddress(reinterpret_cast<void**>(&w.word), HIP_SYMBOL(d_error_word));
+        if (w.status == hipSuccess)
+            w.status = hipGetSymbolAddress(reinterpret_cast<void**>(&w.taken), HIP_SYMBOL(d_error_taken));
+    });
+    *out = &w;
+    return w.status;
+}
+
+std::mutex g_resident_mu;
+std::map<std::pair<int, const void*>, int64_t> g_resident;
+}  // namespace
+
+hipError_t device_error_word(uint32_t** word) {
+    DeviceWords* w = nullptr;
+    hipError_t e = device_words(&w);
+    *word = e == hipSuccess ? w->word : nullptr;
+    return e;
+}
+
+hipError_t resident_workgroups(const void* kernel, int threads, int64_t* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    {
+        std::lock_guard<std::mutex> lk(g_resident_mu);
+        auto it = g_resident.find({dev, kernel});
+        if (it != g_resident.end()) {
+            *out = it->second;
+            return hipSuccess;
+        }
+    }
+    int per_cu = 0, cus = 0;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    const int64_t n = int64_t(std::max(per_cu, 0)) * int64_t(std::max(cus, 0));
+    std::lock_guard<std::mutex> lk(g_resident_mu);
+    g_resident[{dev, kernel}] = n;
+    *out = n;
+    return hipSuccess;
+}
 
 // ---- kernel timing ----------------------------------------------------------------
 
@@ -302,6 +394,7 @@ const char* gma_status_string(gma_status_t s) {
         case GMA_ERR_MISALIGNED: return "GMA_ERR_MISALIGNED";
         case GMA_ERR_WORKSPACE_TOO_SMALL: return "GMA_ERR_WORKSPACE_TOO_SMALL";
         case GMA_ERR_HIP: return "GMA_ERR_HIP";
+        case GMA_ERR_TIMEOUT: return "GMA_ERR_TIMEOUT";
     }
     return "GMA_ERR_UNKNOWN";
 }
@@ -581,6 +674,46 @@ gma_status_t gma_forward_cross(const void* XQ, const void* XK, const void* V, gm
                                             static_cast<const float*>(V), mu, sigma2, pi, eps, static_cast<float*>(O),
                                             ws, stream));
     return launch_status(gma::bf16_bidir(p, XQ, XK, V, mu, sigma2, pi, eps, O, ws, stream));
+}
+
+gma_status_t gma_set_single_launch(int enable) {
+    gma::g_single_launch.store(enable != 0 ? 1 : 0, std::memory_order_relaxed);
+    return GMA_OK;
+}
+
+gma_status_t gma_device_status(hipStream_t stream) {
+    gma::DeviceWords* w = nullptr;
+    if (gma::device_words(&w) != hipSuccess) return GMA_ERR_HIP;
+    hipLaunchKernelGGL(gma::take_error_kernel, dim3(1), dim3(64), 0, stream, w->word, w->taken);
+    if (hipGetLastError() != hipSuccess) return GMA_ERR_HIP;
+    uint32_t bits = 0;
+    if (hipMemcpyAsync(&bits, w->taken, sizeof(bits), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return GMA_ERR_HIP;
+    return (bits & gma::kDevErrTimeout) ? GMA_ERR_TIMEOUT : GMA_OK;
+}
+
+gma_status_t gma_plan_info(gma_op_t op, const gma_shape_t* shape, gma_dtype_t io_dtype, int32_t chunk,
+                           gma_plan_info_t* info) {
+    if (!shape || !info) return GMA_ERR_NULL_POINTER;
+    if (op != GMA_OP_BIDIR && op != GMA_OP_CAUSAL) return GMA_ERR_BAD_VALUE;
+    Plan p;
+    gma_status_t st = gma::make_plan(op, *shape, io_dtype, chunk, &p);
+    if (st != GMA_OK) return st;
+    *info = gma_plan_info_t{};
+    info->splits = p.G;
+    info->rows_per_split = int64_t(p.seg);
+    info->workgroups = p.P * p.G;
+    if (op == GMA_OP_BIDIR && io_dtype == GMA_BF16) {
+        int threads = 0;
+        int64_t lds = 0;
+        gma::bf16_bidir_geometry(p.dr, p.Kp / 32, p.dv / 32, &threads, &lds);
+        info->threads_per_workgroup = threads;
+        info->lds_bytes = lds;
+        info->waits_on_all_splits = p.G > 1 ? 1 : 0;
+        info->resident_bound = gma::kDeviceCUs * gma::bf16_bidir_per_cu(p.dr, p.Kp / 32, p.dv / 32);
+    }
+    return GMA_OK;
 }
 
 gma_status_t gma_set_wait_limit(uint32_t polls) {

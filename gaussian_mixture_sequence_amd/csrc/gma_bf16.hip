@@ -126,7 +126,7 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(WriteLds<DR, KT, VT>::bytes))))
     constexpr int Kp = KT * 32, DV = VT * 32;
     const int64_t p = blockIdx.y;
     const int g = blockIdx.x;
-    const int64_t lo = int64_t(g) * seg, hi = min<int64_t>(lo + seg, N);
+    const int64_t lo = min<int64_t>(int64_t(g) * seg, N), hi = min<int64_t>(lo + seg, N);
     WaveParams<DR, Split<DR, KT>::CTW> P;
     write_body<DR, KT, VT, true>(smem, XK, V, N, p, int(p % H), lo, hi, mx, P,
                                  partials + (size_t(p) * G + g) * size_t(Kp) * (DV + 1));
@@ -207,9 +207,10 @@ struct ReadLds {
     using gs_t = uint16_t[S::ROUND * LDG];
     using ms_t = uint16_t[MS_LDS ? 2 * DV * LDM : 8];
     using dn_t = float[2][S::ROUND];
+    using vote_t = int[S::NW];  // per-wave votes of the fused kernel's hand-off (workgroup_all)
     static constexpr size_t o_st = 0, o_xt = lds_align(o_st + sizeof(st_t)), o_gs = lds_align(o_xt + sizeof(xt_t)),
                             o_ms = lds_align(o_gs + sizeof(gs_t)), o_dn = lds_align(o_ms + sizeof(ms_t)),
-                            bytes = lds_align(o_dn + sizeof(dn_t));
+                            o_vote = lds_align(o_dn + sizeof(dn_t)), bytes = lds_align(o_vote + sizeof(vote_t));
 };
 
 // Rows [lo, hi) of problem p (head h): O = Gamma_Q Vt / (Gamma_Q Z + eps) from the problem's
@@ -423,20 +424,29 @@ __device__ __forceinline__ void read_body(char* __restrict__ smem, const uint16_
 //      scores issued, which need no memory;
 //   3. after all G partials of p are published: combine 1/G of p's memory (fixed order);
 //   4. after all G slices are published: the rest of the read phase.
+// Steps 3 and 4 wait on every workgroup of the problem, so the host launches this kernel
+// only when its whole grid can be resident at once (otherwise the three phases run as
+// separate launches: write_kernel, combine_kernel, read_kernel).
 // flags: [P][2][G] words (partials ready, memory slice ready), compared with `token`.  A
-// workgroup whose wait times out writes NaN over its output rows.
+// workgroup whose first wait times out neither combines nor publishes its slice, so no
+// workgroup ever reads a memory summed from incomplete partials; every workgroup of the
+// problem then times out in turn, writes NaN over its output rows and raises
+// kDevErrTimeout in `err`.
+template <int DR, int KT, int VT>
+constexpr size_t bidir_lds_bytes() {
+    return WriteLds<DR, KT, VT>::bytes > ReadLds<DR, KT, VT>::bytes ? WriteLds<DR, KT, VT>::bytes
+                                                                     : ReadLds<DR, KT, VT>::bytes;
+}
+
 template <int DR, int KT, int VT>
 __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
-__attribute__((amdgpu_waves_per_eu(waves_for_lds(WriteLds<DR, KT, VT>::bytes > ReadLds<DR, KT, VT>::bytes
-                                                      ? WriteLds<DR, KT, VT>::bytes
-                                                      : ReadLds<DR, KT, VT>::bytes))))
+__attribute__((amdgpu_waves_per_eu(waves_for_lds(bidir_lds_bytes<DR, KT, VT>()))))
     bidir_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
                  int64_t N, int64_t Nq, int H, int64_t seg, int64_t seg_q, int G, Mixture mx, float* __restrict__ partials,
                  uint16_t* __restrict__ memory, uint64_t* __restrict__ flags, uint64_t token,
-                 uint32_t wait_limit, float eps, uint16_t* __restrict__ O) {
-    using WL = WriteLds<DR, KT, VT>;
+                 uint32_t wait_limit, float eps, uint16_t* __restrict__ O, uint32_t* __restrict__ err) {
     using RL = ReadLds<DR, KT, VT>;
-    __shared__ __attribute__((aligned(16))) char smem[WL::bytes > RL::bytes ? WL::bytes : RL::bytes];
+    __shared__ __attribute__((aligned(16))) char smem[bidir_lds_bytes<DR, KT, VT>()];
     constexpr int Kp = KT * 32, DV = VT * 32, E = Kp * (DV + 1), NT = Split<DR, KT>::NW * 64;
     const int64_t p = blockIdx.y;
     const int g = blockIdx.x, h = int(p % H);
@@ -451,21 +461,54 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(WriteLds<DR, KT, VT>::bytes > R
     publish_token(fl + g, token);  // its barrier also frees the write phase's LDS
     bool ok = true;
     read_body<DR, KT, VT, false>(smem, XQ, Nq, p, h, lo_q, hi_q, mx, P, mem, eps, O, [&] {
-        // behind the read phase's first tiles and scores: complete the memory
-        ok = wait_tokens(fl, G, token, wait_limit);
-        const int per = (E / 4 + G - 1) / G;  // 16-byte groups per slice
-        combine_range(part, G, E, Kp, DV, min(g * per, E / 4), min((g + 1) * per, E / 4), mem, NT);
-        publish_token(fl + G + g, token);
-        ok = wait_tokens(fl + G, G, token, wait_limit) && ok;
+        // behind the read phase's first tiles and scores: complete the memory.  The waves
+        // poll on their own and agree before the combine, which needs every wave.
+        ok = workgroup_all(wait_tokens(fl, G, token, wait_limit), reinterpret_cast<int*>(smem + RL::o_vote));
+        if (ok) {
+            const int per = (E / 4 + G - 1) / G;  // 16-byte groups per slice
+            combine_range(part, G, E, Kp, DV, min(g * per, E / 4), min((g + 1) * per, E / 4), mem, NT);
+            publish_token(fl + G + g, token);
+            ok = wait_tokens(fl + G, G, token, wait_limit);
+        }
     });
-    // waves poll on their own: agree on the outcome before acting on it
     ok = workgroup_all(ok, reinterpret_cast<int*>(smem));
-    if (!ok) {  // the memory was never complete: make that visible in the output
+    if (!ok) {  // the memory was never complete: make that visible in the output and to the host
         __builtin_amdgcn_s_waitcnt(0);  // the phase's own stores of these rows land first
         __syncthreads();
         uint16_t* op = O + (size_t(p) * Nq + lo_q) * DV;
         for (int64_t e = threadIdx.x; e < (hi_q - lo_q) * DV; e += NT) op[e] = 0x7fc0u;
+        if (threadIdx.x == 0) atomicOr(err, kDevErrTimeout);
     }
+}
+
+// The bidirectional forward as three launches with no waits between workgroups (used when
+// the single launch's grid cannot be resident at once, or when the caller asks for it):
+// write_kernel (partials), combine_kernel (the memory, slice g of problem p per workgroup,
+// the same fixed order as the single launch), read_kernel.
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ partials, int G, int Kp, int DV,
+                                                      uint16_t* __restrict__ memory) {
+    const int E = Kp * (DV + 1);
+    const int64_t p = blockIdx.y;
+    const int g = blockIdx.x;
+    const int per = (E / 4 + G - 1) / G;
+    combine_range(partials + size_t(p) * G * E, G, E, Kp, DV, min(g * per, E / 4), min((g + 1) * per, E / 4),
+                  memory + size_t(p) * E * 2, 256);
+}
+
+template <int DR, int KT, int VT>
+__global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
+__attribute__((amdgpu_waves_per_eu(waves_for_lds(ReadLds<DR, KT, VT>::bytes))))
+    read_kernel(const uint16_t* __restrict__ XQ, int64_t Nq, int H, int64_t seg_q, Mixture mx,
+                const uint16_t* __restrict__ memory, float eps, uint16_t* __restrict__ O) {
+    __shared__ __attribute__((aligned(16))) char smem[ReadLds<DR, KT, VT>::bytes];
+    constexpr int Kp = KT * 32, DV = VT * 32, E = Kp * (DV + 1);
+    const int64_t p = blockIdx.y;
+    const int g = blockIdx.x;
+    const int64_t lo_q = min<int64_t>(int64_t(g) * seg_q, Nq), hi_q = min<int64_t>(lo_q + seg_q, Nq);
+    if (lo_q >= hi_q) return;  // uniform over the workgroup
+    WaveParams<DR, Split<DR, KT>::CTW> P;
+    read_body<DR, KT, VT, true>(smem, XQ, Nq, p, int(p % H), lo_q, hi_q, mx, P, memory + size_t(p) * E * 2, eps, O,
+                                [] {});
 }
 
 // ---------------------------------------------------------------------------- dispatch
@@ -532,23 +575,77 @@ hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, con
     });
 }
 
+void bf16_bidir_geometry(int64_t dr, int64_t kt, int64_t vt, int* threads, int64_t* lds_bytes) {
+    *threads = 0;
+    *lds_bytes = 0;
+    (void)bf::with_dr_kt(int(dr), int(kt), [&](auto D, auto T) {
+        constexpr int DR = decltype(D)::value, KT = decltype(T)::value;
+        return bf::with_vt(int(vt), [&](auto VV) {
+            constexpr int VT = decltype(VV)::value;
+            *threads = bf::Split<DR, KT>::NW * 64;
+            *lds_bytes = int64_t(bf::bidir_lds_bytes<DR, KT, VT>());
+            return hipSuccess;
+        });
+    });
+}
+
+int64_t bf16_bidir_per_cu(int64_t dr, int64_t kt, int64_t vt) {
+    int threads = 0;
+    int64_t lds = 0;
+    bf16_bidir_geometry(dr, kt, vt, &threads, &lds);
+    if (threads <= 0 || lds <= 0) return 1;
+    // LDS: 160 KiB per CU; waves: the kernels declare the waves per SIMD their LDS allows
+    // (bf::waves_for_lds), so the registers of that many waves of every SIMD are guaranteed
+    const int64_t by_lds = (160 * 1024) / lds;
+    const int64_t by_waves = (int64_t(bf::waves_for_lds(size_t(lds))) * 4 * 64) / threads;
+    return std::max<int64_t>(1, std::min(by_lds, by_waves));
+}
+
 hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu, const float* s2,
                       const float* pi, float eps, void* O, char* ws, hipStream_t st) {
     const bf::Mixture mx{mu, s2, pi, int(p.K)};
     float* partials = reinterpret_cast<float*>(ws + p.off_partials);
     uint16_t* memory = reinterpret_cast<uint16_t*>(ws + p.off_memory);
     uint64_t* flags = reinterpret_cast<uint64_t*>(ws + p.off_flags);
-    const uint64_t token = launch_token();
+    uint32_t* err = nullptr;
+    hipError_t e = device_error_word(&err);
+    if (e != hipSuccess) return e;
     return bf::with_dr_kt(int(p.dr), kt_of(p), [&](auto D, auto T) {
         constexpr int DR = decltype(D)::value, KT = decltype(T)::value;
-        return bf::with_vt(int(p.dv / 32), [&](auto VV) {
+        return bf::with_vt(int(p.dv / 32), [&](auto VV) -> hipError_t {
             constexpr int VT = decltype(VV)::value;
             using S = bf::Split<DR, KT>;
-            GMA_LAUNCH(p.cross ? "bf16_cross" : "bf16_bidir", (bf::bidir_kernel<DR, KT, VT>), dim3(unsigned(p.G), unsigned(p.P)),
-                       dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
-                       static_cast<const uint16_t*>(V), p.N, p.Nq, int(p.H), p.seg, p.seg_q, int(p.G), mx, partials,
-                       memory, flags,
-                       token, wait_limit(), eps, static_cast<uint16_t*>(O));
+            constexpr int NT = S::NW * 64;
+            const dim3 grid(unsigned(p.G), unsigned(p.P));
+            // the single launch waits on every workgroup of a problem: only when the whole grid
+            // is resident at once on this device (with one split per problem nothing waits on
+            // another workgroup)
+            bool single = single_launch_enabled();
+            if (single && p.G > 1) {
+                int64_t resident = 0;
+                hipError_t r = resident_workgroups(reinterpret_cast<const void*>(&bf::bidir_kernel<DR, KT, VT>), NT,
+                                                   &resident);
+                if (r != hipSuccess) return r;
+                single = p.P * p.G <= resident;
+            }
+            if (single) {
+                GMA_LAUNCH(p.cross ? "bf16_cross" : "bf16_bidir", (bf::bidir_kernel<DR, KT, VT>), grid, dim3(NT), 0, st,
+                           static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
+                           static_cast<const uint16_t*>(V), p.N, p.Nq, int(p.H), p.seg, p.seg_q, int(p.G), mx, partials,
+                           memory, flags, launch_token(), wait_limit(), eps, static_cast<uint16_t*>(O), err);
+                return hipGetLastError();
+            }
+            GMA_LAUNCH(p.cross ? "bf16_cross_write" : "bf16_write", (bf::write_kernel<DR, KT, VT>), grid, dim3(NT), 0, st,
+                       static_cast<const uint16_t*>(XK), static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G),
+                       mx, partials);
+            hipError_t r = hipGetLastError();
+            if (r != hipSuccess) return r;
+            GMA_LAUNCH(p.cross ? "bf16_cross_combine" : "bf16_combine", bf::combine_kernel, grid, dim3(256), 0, st,
+                       partials, int(p.G), KT * 32, VT * 32, memory);
+            if ((r = hipGetLastError()) != hipSuccess) return r;
+            GMA_LAUNCH(p.cross ? "bf16_cross_read" : "bf16_read", (bf::read_kernel<DR, KT, VT>), grid, dim3(NT), 0, st,
+                       static_cast<const uint16_t*>(XQ), p.Nq, int(p.H), p.seg_q, mx, memory, eps,
+                       static_cast<uint16_t*>(O));
             return hipGetLastError();
         });
     });

@@ -478,46 +478,66 @@ struct WaveParams {
     //   c = log2 pi - (sum_d log2 sigma2 + log2(e) mu^2 / sigma2) / 2   (fp32).
     // Padded components get zero planes (sigma2 taken as +inf) and c = -inf, so their
     // responsibility is exactly 0.  sigma2 must be a positive normal float.
+    // Bitwise the same planes and constants as PlaneBuilder::build, so that kernels (and the
+    // workgroups of one kernel) that build them either way agree exactly: the same operations per
+    // (component, dim), and the constant's sum taken over 4-dim chunks combined in the same tree.
     __device__ __forceinline__ void build(const Raw& r, int K, int ct0) {
         const float L2E = 1.4426950408889634f;
+        constexpr int KS = DR / 16, CPR = DR / 4;  // 4-dim chunks per component row
         const int l = threadIdx.x & 63, lh = l >> 5;
 #pragma unroll
         for (int ct = 0; ct < CTW; ++ct) {
             const bool valid = (ct0 + ct) * 32 + (l & 31) < K;
-            float csum = 0.0f;
+            float part[2 * KS];  // this lane's chunks: chunk 4 ks + 2 lh + h4 at index 2 ks + h4
 #pragma unroll
-            for (int ks = 0; ks < DR / 16; ++ks) {
-                const float m[8] = {r.m[ct][ks][0].x, r.m[ct][ks][0].y, r.m[ct][ks][0].z, r.m[ct][ks][0].w,
-                                    r.m[ct][ks][1].x, r.m[ct][ks][1].y, r.m[ct][ks][1].z, r.m[ct][ks][1].w};
-                const float v[8] = {r.v[ct][ks][0].x, r.v[ct][ks][0].y, r.v[ct][ks][0].z, r.v[ct][ks][0].w,
-                                    r.v[ct][ks][1].x, r.v[ct][ks][1].y, r.v[ct][ks][1].z, r.v[ct][ks][1].w};
+            for (int ks = 0; ks < KS; ++ks) {
                 u32x4 ah, al, bh, bl;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    float a2[2], b2[2];
+                for (int h4 = 0; h4 < 2; ++h4) {
+                    const float4 mv = r.m[ct][ks][h4], vv4 = r.v[ct][ks][h4];
+                    const float mm[4] = {mv.x, mv.y, mv.z, mv.w};
+                    const float vv[4] = {vv4.x, vv4.y, vv4.z, vv4.w};
+                    float a[4], b[4], csum = 0.0f;
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const float vv = v[2 * q + e];
-                        const float inv = __builtin_amdgcn_rcpf(valid ? vv : INFINITY);
-                        const float mi = m[2 * q + e] * inv;
-                        a2[e] = mi * L2E;
-                        b2[e] = (-0.5f * L2E) * inv;
-                        csum += __builtin_amdgcn_logf(vv) + mi * m[2 * q + e] * L2E;
+                    for (int e = 0; e < 4; ++e) {
+                        const float inv2 = __builtin_amdgcn_rcpf(valid ? vv[e] : INFINITY) * L2E;
+                        a[e] = mm[e] * inv2;
+                        b[e] = -0.5f * inv2;
+                        csum += __builtin_amdgcn_logf(vv[e]) + mm[e] * a[e];
                     }
-                    ah[q] = pack_bf16x2(a2[0], a2[1]);
-                    bh[q] = pack_bf16x2(b2[0], b2[1]);
-                    al[q] = pack_bf16x2(a2[0] - __uint_as_float(ah[q] << 16), a2[1] - __uint_as_float(ah[q] & 0xffff0000u));
-                    bl[q] = pack_bf16x2(b2[0] - __uint_as_float(bh[q] << 16), b2[1] - __uint_as_float(bh[q] & 0xffff0000u));
+                    part[2 * ks + h4] = csum;
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const uint32_t hi_a = pack_bf16x2(a[2 * q], a[2 * q + 1]);
+                        const uint32_t hi_b = pack_bf16x2(b[2 * q], b[2 * q + 1]);
+                        ah[2 * h4 + q] = hi_a;
+                        al[2 * h4 + q] = pack_bf16x2(a[2 * q] - __uint_as_float(hi_a << 16),
+                                                     a[2 * q + 1] - __uint_as_float(hi_a & 0xffff0000u));
+                        bh[2 * h4 + q] = hi_b;
+                        bl[2 * h4 + q] = pack_bf16x2(b[2 * q] - __uint_as_float(hi_b << 16),
+                                                     b[2 * q + 1] - __uint_as_float(hi_b & 0xffff0000u));
+                    }
                 }
                 w[ct][ks][0] = __builtin_bit_cast(bf16x8, ah);
                 w[ct][ks][1] = __builtin_bit_cast(bf16x8, al);
                 w[ct][ks][2] = __builtin_bit_cast(bf16x8, bh);
                 w[ct][ks][3] = __builtin_bit_cast(bf16x8, bl);
             }
-            // the two halves of component k's dims sit in lanes j and j + 32
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(csum), __float_as_uint(csum), false, false);
-            const float ctot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-            const float ck = valid ? __builtin_amdgcn_logf(r.pk[ct]) - 0.5f * ctot : -INFINITY;
+            // all CPR chunk sums of component k: lanes j and j + 32 hold the two halves
+            float chunk[CPR];
+#pragma unroll
+            for (int i = 0; i < 2 * KS; ++i) {
+                const float mine = part[i], other = __shfl_xor(part[i], 32, kWave);
+                const int ks = i >> 1, h4 = i & 1;
+                chunk[4 * ks + 0 + h4] = lh == 0 ? mine : other;
+                chunk[4 * ks + 2 + h4] = lh == 0 ? other : mine;
+            }
+            // the tree of PlaneBuilder's butterfly: level o adds chunk i + o into chunk i
+#pragma unroll
+            for (int o = CPR / 2; o >= 1; o >>= 1)
+#pragma unroll
+                for (int i = 0; i < o; ++i) chunk[i] = chunk[i] + chunk[i + o];
+            const float ck = valid ? __builtin_amdgcn_logf(r.pk[ct]) - 0.5f * chunk[0] : -INFINITY;
             // D rows of this lane: components 8 q + 4 lh + i of the tile
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -622,13 +642,17 @@ __device__ __forceinline__ void local_softmax(f32x16 (&acc)[CTW], const float (&
 #pragma unroll
         for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[ct][r]);
     m = xmax32(m);
+    // a wave whose components are all padding (score -inf) has m = -inf: subtract 0 instead, so
+    // that its terms are exp2(-inf) = 0 (and L = 0) rather than NaN; the combine across waves
+    // then weighs it by exp2(-inf - m_total) = 0
+    const float mref = m == -INFINITY ? 0.0f : m;
     L = 0.0f;
     D = 0.0f;
 #pragma unroll
     for (int ct = 0; ct < CTW; ++ct)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            float e = __builtin_amdgcn_exp2f(acc[ct][r] - m);
+            float e = __builtin_amdgcn_exp2f(acc[ct][r] - mref);
             acc[ct][r] = e;
             L += e;
             if (WITH_Z) D = fmaf(e, zr[ct][r], D);

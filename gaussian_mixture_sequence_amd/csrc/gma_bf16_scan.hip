@@ -535,10 +535,14 @@ __device__ __forceinline__ void scan_body(char* __restrict__ smem, const uint16_
 // ---- the causal forward in one launch (shapes of the pipelined scan).  Grid (G, P);
 // workgroup (s, p) owns segment s of problem p.  Segments 0 .. G-2 first write their
 // aggregate (write_body over the segment) and publish it; every segment then waits for the
-// aggregates of the segments before it (only earlier-dispatched workgroups), sums them in
-// increasing order and scans.  The last segment's aggregate is never needed, so its
-// workgroup builds its operand planes and goes straight to the wait.  flags: [P][G] words
-// compared with `token`; a workgroup whose wait times out writes NaN over its positions.
+// aggregates of the segments before it (only lower-numbered workgroups, dispatched no later
+// than itself, so the launch needs no co-residency), sums them in increasing order and
+// scans.  The last segment's aggregate is never needed, so its workgroup builds its operand
+// planes and goes straight to the wait.  flags: [P][G] words compared with `token`.  With
+// `aggregated` set, the aggregates are already in place (written by an earlier launch,
+// write_kernel): no segment writes one and nothing waits.  A workgroup whose wait times out
+// writes NaN over its positions (and over state_out if it is the last segment) and raises
+// kDevErrTimeout in `err`.
 template <int DR, int KT, int VT, int CH_REQ>
 constexpr size_t causal_lds_bytes() {
     constexpr size_t w = WriteLds<DR, KT, VT>::bytes;
@@ -551,8 +555,9 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64))
 __attribute__((amdgpu_waves_per_eu(waves_for_lds(causal_lds_bytes<DR, KT, VT, CH_REQ>()))))
     causal_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
                   int64_t N, int H, int64_t seg, int G, Mixture mx, float* __restrict__ aggregates,
-                  uint64_t* __restrict__ flags, uint64_t token, uint32_t wait_limit, float eps,
-                  uint16_t* __restrict__ O, const float* __restrict__ state_in, float* __restrict__ state_out) {
+                  uint64_t* __restrict__ flags, uint64_t token, uint32_t wait_limit, int aggregated, float eps,
+                  uint16_t* __restrict__ O, const float* __restrict__ state_in, float* __restrict__ state_out,
+                  uint32_t* __restrict__ err) {
     __shared__ __attribute__((aligned(16))) char smem[causal_lds_bytes<DR, KT, VT, CH_REQ>()];
     using S = Split<DR, KT>;
     constexpr int Kp = KT * 32, DV = VT * 32, E = Kp * (DV + 1), NT = S::NW * 64;
@@ -562,7 +567,7 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(causal_lds_bytes<DR, KT, VT, CH
     float* agg = aggregates + size_t(p) * G * E;
     uint64_t* fl = flags + size_t(p) * G;
     WaveParams<DR, S::CTW> P;
-    if (s + 1 < G) {
+    if (s + 1 < G && !aggregated) {
         write_body<DR, KT, VT, true>(smem, XK, V, N, p, h, lo, hi, mx, P, agg + size_t(s) * E);
         publish_token(fl + s, token);  // its barrier also frees the write phase's LDS
     } else if constexpr (PlaneBuilder<DR, Kp, NT>::LDS_BYTES <= sizeof(smem)) {  // the whole buffer is free here
@@ -577,17 +582,22 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(causal_lds_bytes<DR, KT, VT, CH
     }
     bool ok = true;
     const size_t SE = size_t(mx.K) * (DV + 1);  // one problem's carried memory
+    float* so = (state_out && s == G - 1) ? state_out + p * SE : nullptr;
     scan_body<DR, KT, VT, CH_REQ, false>(smem, XQ, XK, V, N, p, h, s, lo, hi, mx, P, agg, eps, O,
-                                         [&] { ok = wait_tokens(fl, s, token, wait_limit); },
-                                         state_in ? state_in + p * SE : nullptr,
-                                         (state_out && s == G - 1) ? state_out + p * SE : nullptr);
+                                         [&] {
+                                             if (!aggregated) ok = wait_tokens(fl, s, token, wait_limit);
+                                         },
+                                         state_in ? state_in + p * SE : nullptr, so);
     // waves poll on their own: agree on the outcome before acting on it
     ok = workgroup_all(ok, reinterpret_cast<int*>(smem));
-    if (!ok) {  // the starting memory was never complete: make that visible in the output
+    if (!ok) {  // the starting memory was never complete: make that visible in the outputs and to the host
         __builtin_amdgcn_s_waitcnt(0);  // the phase's own stores of these rows land first
         __syncthreads();
         uint16_t* op = O + (size_t(p) * N + lo) * DV;
         for (int64_t e = threadIdx.x; e < (hi - lo) * DV; e += NT) op[e] = 0x7fc0u;
+        if (so)
+            for (size_t e = threadIdx.x; e < SE; e += NT) so[e] = __builtin_nanf("");
+        if (threadIdx.x == 0) atomicOr(err, kDevErrTimeout);
     }
 }
 
@@ -987,16 +997,27 @@ hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void
     float* aggregates = reinterpret_cast<float*>(ws + p.off_partials);
     uint64_t* flags = reinterpret_cast<uint64_t*>(ws + p.off_flags);
     const int ch = p.chunk < 32 ? 32 : p.chunk;
+    uint32_t* err = nullptr;
+    hipError_t de = device_error_word(&err);
+    if (de != hipSuccess) return de;
     return bf::with_all(int(p.dr), int(p.Kp / 32), int(p.dv / 32), ch, [&](auto D, auto T, auto W, auto C) {
         constexpr int DR = decltype(D)::value, KT = decltype(T)::value, VT = decltype(W)::value,
                       CH = decltype(C)::value;
         using S = bf::Split<DR, KT>;
         // pipelined scan where its registers suffice (up to 4 component tiles and d_r * K <= 8192)
         if constexpr (KT <= 4 && DR * KT <= 256) {
+            // one launch; without the in-launch hand-off (single launch disabled) the aggregates
+            // come from a launch of their own first
+            const bool single = single_launch_enabled();
+            if (!single && p.G > 1) {
+                hipError_t e = bf16_write_partials(p, XK, V, mu, s2, pi, ws, st, p.G - 1);
+                if (e != hipSuccess) return e;
+            }
             GMA_LAUNCH("bf16_causal", (bf::causal_kernel<DR, KT, VT, CH>), dim3(unsigned(p.G), unsigned(p.P)),
                        dim3(S::NW * 64), 0, st, static_cast<const uint16_t*>(XQ), static_cast<const uint16_t*>(XK),
                        static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg, int(p.G), mx, aggregates, flags,
-                       launch_token(), wait_limit(), eps, static_cast<uint16_t*>(O), state_in, state_out);
+                       launch_token(), wait_limit(), single ? 0 : 1, eps, static_cast<uint16_t*>(O), state_in,
+                       state_out, err);
         } else {
             // aggregates of segments 0 .. G-2 (the last segment's aggregate is never read)
             if (p.G > 1) {

@@ -44,6 +44,19 @@ uint64_t launch_token();
 // (gma_set_wait_limit).
 uint32_t wait_limit();
 
+// Bits of the per-device error word that kernels raise (atomic OR) and gma_device_status
+// takes: a hand-off wait of a single-launch forward ran out.
+constexpr uint32_t kDevErrTimeout = 1u;
+// Address of the error word on the current device (resolved once per device).
+hipError_t device_error_word(uint32_t** word);
+
+// Whether the bf16 forwards may hand data between workgroups inside one launch
+// (gma_set_single_launch).
+bool single_launch_enabled();
+// Workgroups of `kernel` (launched with `threads` threads and no dynamic LDS) that the current
+// device keeps resident at once: the runtime's occupancy per CU times the CU count (cached).
+hipError_t resident_workgroups(const void* kernel, int threads, int64_t* out);
+
 // Kernel timing hooks (see gma_profiling in gma.h).  Launchers bracket each launch with
 // trace_begin / trace_end; both are no-ops unless profiling is enabled.
 void trace_begin(hipStream_t st, const char* name);
@@ -123,6 +136,12 @@ hipError_t causal_decode(const Plan& p, const void* XQ, const void* XK, const vo
 hipError_t bf16_responsibilities(const Plan& p, const void* X, const float* mu, const float* s2,
                                  const float* pi, void* Gamma, gma_dtype_t gamma_dtype, char* ws,
                                  hipStream_t st);
+// Threads and static LDS bytes of one workgroup of the single-launch bidirectional kernel for
+// these dims (d_r, component tiles of 32, value tiles of 32); zeros for unsupported dims.
+void bf16_bidir_geometry(int64_t dr, int64_t kt, int64_t vt, int* threads, int64_t* lds_bytes);
+// Workgroups of that kernel a CU keeps resident by its LDS and its declared waves per SIMD
+// (every MI355X CU has 160 KiB of LDS and 4 SIMDs); at least 1.
+int64_t bf16_bidir_per_cu(int64_t dr, int64_t kt, int64_t vt);
 hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void* V,
                       const float* mu, const float* s2, const float* pi, float eps, void* O,
                       char* ws, hipStream_t st);

@@ -24,14 +24,24 @@
  *             parameters mu, sigma2, pi are always fp32.  eps is fp32.
  * Memory      Every pointer is a device pointer (HBM) owned by the caller.  The library
  *             never allocates or frees device memory and keeps no state between calls
- *             (apart from the optional kernel-timing record, gma_profiling); scratch
- *             space is the caller's workspace (size from gma_workspace_size).
+ *             apart from the optional kernel-timing record (gma_profiling) and one
+ *             device error word per device (gma_device_status); scratch space is the
+ *             caller's workspace (size from gma_workspace_size).
  *             O and Gamma must not overlap any input or the workspace.
  * Alignment   Tensor pointers and the workspace must be 16-byte aligned
  *             (GMA_ERR_MISALIGNED otherwise).
  * Streams     Work is enqueued on `stream` (NULL = the device's null stream) and the call
- *             returns without waiting.  Calls on different streams may run concurrently
- *             if they use different workspaces.
+ *             returns without waiting.  Calls on different streams must use different
+ *             workspaces.  The single-launch bf16 forwards (gma_forward_bidir,
+ *             gma_forward_cross, gma_forward_causal and gma_forward_causal_state) hand data
+ *             between the workgroups of one launch and rely on the device dispatching them
+ *             (bidirectional: all of the launch's workgroups resident at once; the host
+ *             checks the grid against the device's occupancy and otherwise runs the phases
+ *             as separate launches).  A kernel running concurrently on another stream can
+ *             hold the compute units those workgroups need; a hand-off wait then runs out
+ *             after a bounded time, the affected output rows are NaN and gma_device_status
+ *             reports GMA_ERR_TIMEOUT.  Callers that run forwards concurrently on one device
+ *             turn the single launches off with gma_set_single_launch(0).
  * Pointers    A tensor pointer may be NULL when the tensor has no elements (e.g. N = 0);
  *             the parameters, the shape and a workspace of nonzero size may not.
  * Errors      Arguments are validated on the host before any HIP call; a non-OK status
@@ -69,7 +79,9 @@ typedef enum {
     GMA_ERR_UNSUPPORTED = 4,         /* d_r, d_v, K or chunk outside the supported set    */
     GMA_ERR_MISALIGNED = 5,          /* pointer not 16-byte aligned                       */
     GMA_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes < gma_workspace_size(...)         */
-    GMA_ERR_HIP = 7                  /* a HIP runtime call or kernel launch failed        */
+    GMA_ERR_HIP = 7,                 /* a HIP runtime call or kernel launch failed        */
+    GMA_ERR_TIMEOUT = 8              /* gma_device_status: a hand-off wait inside a
+                                        single-launch forward ran out (see there)         */
 } gma_status_t;
 
 typedef enum { GMA_F32 = 0, GMA_BF16 = 1 } gma_dtype_t;
@@ -346,14 +358,61 @@ gma_status_t gma_profiling_collect(gma_kernel_stat_t* stats, int capacity, int* 
  * launch publish (the split partials and memory slices of a bidirectional problem; the
  * aggregates of the earlier segments of a causal problem).  The waits poll at most `polls`
  * times (each poll is a device-wide load followed by a short sleep).  A workgroup whose
- * wait exceeds the bound stops waiting and writes NaN over its output rows, so a launch
- * always terminates.  The default, GMA_WAIT_LIMIT_DEFAULT polls, is far above any wait of
+ * wait exceeds the bound stops waiting, publishes nothing further, writes NaN over its
+ * output rows (and the carried memory, if it produces it) and raises the device error that
+ * gma_device_status reports, so a launch always terminates and a failure is never silent.  The default, GMA_WAIT_LIMIT_DEFAULT polls, is far above any wait of
  * a healthy launch (well under a second in total).  0 makes every such wait fail at
  * once.  That setting exists so that tests can exercise the failure path.  The value is
  * process-wide and read when a forward is enqueued.
  */
 #define GMA_WAIT_LIMIT_DEFAULT (1u << 18)
 gma_status_t gma_set_wait_limit(uint32_t polls);
+
+/*
+ * Device-side failures of earlier calls on the current device.  Waits for `stream`, then
+ * returns GMA_ERR_TIMEOUT if, since the previous gma_device_status on this device, a
+ * single-launch forward's hand-off wait ran out (gma_set_wait_limit; its output rows, and
+ * the carried memory of a causal call, were then written as NaN), GMA_OK if not, and
+ * GMA_ERR_HIP if the query itself failed.  Taking the status clears it.  The library keeps
+ * one error word per device (a static device variable, the only state it keeps besides the
+ * profiling record); kernels raise it with an atomic OR, and this call exchanges it with
+ * zero on the device, so a failure raised meanwhile by work on another stream is reported
+ * by this call or the next one, never lost.
+ */
+gma_status_t gma_device_status(hipStream_t stream);
+
+/*
+ * Whether the bf16 forwards may run as single launches whose workgroups hand data to one
+ * another (1, the default) or must run their phases as separate launches in which no
+ * workgroup waits for another (0): bidirectional and cross-attention forwards as write,
+ * combine and read launches; causal forwards as the segment aggregates followed by the
+ * scan.  Results are bitwise identical in both modes.  0 is for callers that run several
+ * forwards concurrently on one device (see Streams above).  Process-wide, read when a
+ * forward is enqueued.
+ */
+gma_status_t gma_set_single_launch(int enable);
+
+/*
+ * How a forward of `op` (GMA_OP_BIDIR or GMA_OP_CAUSAL) on `shape` is split, for inspection
+ * and tests; device-independent, like the workspace size.  Same validation and errors as
+ * gma_workspace_size.
+ *   splits                 sequence splits (bidirectional) or segments (causal) per problem
+ *   rows_per_split         positions per split (the last may be shorter)
+ *   workgroups             B H splits: the grid of the single launch
+ *   threads_per_workgroup  }  bf16 bidirectional only (0 otherwise): the single-launch
+ *   lds_bytes              }  kernel's workgroup size and static LDS,
+ *   waits_on_all_splits    }  1 if its workgroups wait on every split of their problem,
+ *   resident_bound         }  and the workgroups that the kernel's LDS and declared waves
+ *                              per SIMD let a 256-CU MI355X keep resident at once
+ *                              (workgroups <= resident_bound whenever waits_on_all_splits)
+ */
+typedef struct {
+    int64_t splits, rows_per_split, workgroups;
+    int64_t threads_per_workgroup, lds_bytes, waits_on_all_splits, resident_bound;
+} gma_plan_info_t;
+
+gma_status_t gma_plan_info(gma_op_t op, const gma_shape_t* shape, gma_dtype_t io_dtype, int32_t chunk,
+                           gma_plan_info_t* info);
 
 #ifdef __cplusplus
 }

@@ -324,3 +324,44 @@ def test_backward_causal_state_argument_errors(lib):
     assert call(dsi=FAKE + 8) == MISAL
     assert call(dso=FAKE + 0x100000 + sb - 16) == VALUE    # dstate_in overlaps dstate_out
     assert call(sin=FAKE + 0x100000 - sb + 16) == VALUE    # dstate_in overlaps state_in
+
+
+BF16_DIMS = [(dr, K, dv) for dr in (16, 32, 64, 128) for K in (8, 32, 50, 64, 100, 128, 200, 256) for dv in (32, 64, 128)]
+
+
+@pytest.mark.parametrize("dr,K,dv", BF16_DIMS, ids=lambda x: str(x))
+def test_bidir_single_launch_grid_fits_resident_bound(lib, dr, K, dv):
+    """The single-launch bf16 bidirectional forward makes each workgroup wait for every split of
+    its problem, so its grid must be resident at once.  For every supported dim set, and problem
+    counts from one head up to thousands at sequences up to 2^20 positions, the planned grid stays
+    within what 256 CUs hold by the kernel's own LDS (160 KiB per CU) and by the two waves per SIMD
+    its register budget guarantees, or uses one split per problem (no cross-workgroup wait)."""
+    for B, H in ((1, 1), (1, 3), (8, 8), (4, 4), (2, 16), (40, 25)):
+        for N in (1, 1000, 4096, 65536, 262144, 1 << 20):
+            info = gb.gma_plan_info(gb.GMA_OP_BIDIR, B, H, N, dr, dv, K, gb.GMA_BF16)
+            assert info["workgroups"] == B * H * info["splits"]
+            assert info["splits"] * info["rows_per_split"] >= N
+            assert 0 < info["lds_bytes"] <= 160 * 1024
+            assert info["threads_per_workgroup"] in (256, 512)
+            per_cu = min((160 * 1024) // info["lds_bytes"], (4 * 2 * 64) // info["threads_per_workgroup"])
+            assert info["resident_bound"] <= 256 * max(per_cu, 1)
+            if info["splits"] > 1:
+                assert info["waits_on_all_splits"] == 1
+                assert info["workgroups"] <= 256 * per_cu, (B, H, N, info)
+            else:
+                assert info["waits_on_all_splits"] == 0
+
+
+def test_plan_info_validation(lib):
+    info = gb.PlanInfo()
+    sh = gb.Shape(1, 1, 8, 16, 32, 8)
+    assert lib.gma_plan_info(gb.GMA_OP_BIDIR, None, gb.GMA_BF16, 0, ctypes.byref(info)) == NULLP
+    assert lib.gma_plan_info(gb.GMA_OP_BIDIR, ctypes.byref(sh), gb.GMA_BF16, 0, None) == NULLP
+    assert lib.gma_plan_info(gb.GMA_OP_RESPONSIBILITIES, ctypes.byref(sh), gb.GMA_BF16, 0, ctypes.byref(info)) == VALUE
+    assert lib.gma_plan_info(gb.GMA_OP_CAUSAL, ctypes.byref(sh), gb.GMA_BF16, 24, ctypes.byref(info)) == UNSUP
+    assert lib.gma_plan_info(gb.GMA_OP_BIDIR, ctypes.byref(gb.Shape(1, 1, 8, 24, 32, 8)), gb.GMA_BF16, 0,
+                             ctypes.byref(info)) == UNSUP
+    c = gb.gma_plan_info(gb.GMA_OP_CAUSAL, 8, 12, 2048, 64, 64, 32, gb.GMA_BF16, 64)
+    assert c["threads_per_workgroup"] == 0 and c["workgroups"] == 96 * c["splits"]
+    f = gb.gma_plan_info(gb.GMA_OP_BIDIR, 8, 8, 4096, 64, 64, 64, gb.GMA_F32)
+    assert f["lds_bytes"] == 0 and f["waits_on_all_splits"] == 0

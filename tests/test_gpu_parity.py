@@ -116,6 +116,9 @@ BF16_BIDIR_CASES = [
     bf16_case(B=1, H=3, N=1, seed=45),                                      # single token
     bf16_case(B=1, H=1, N=129, d_r=64, d_v=32, K=50, seed=46),              # ragged everything
     bf16_case(B=1, H=2, N=5000, d_r=64, d_v=128, K=256, seed=47),           # several splits
+    bf16_case(B=1, H=2, N=900, d_r=32, d_v=64, K=100, seed=140),            # K padded 100 -> 128
+    bf16_case(B=1, H=1, N=700, d_r=64, d_v=32, K=150, seed=141),            # K padded 150 -> 256
+    bf16_case(B=2, H=1, N=500, d_r=16, d_v=128, K=200, seed=142),           # K padded 200 -> 256
 ]
 
 
@@ -169,6 +172,9 @@ BF16_CAUSAL_CASES = [
     bf16_case(causal=True, B=2, H=1, N=3001, d_r=32, d_v=64, K=128, chunk=64, seed=55),  # several segments
     bf16_case(causal=True, B=1, H=1, N=260, d_r=128, d_v=128, K=256, seed=56),          # maximum dims
     bf16_case(causal=True, B=1, H=1, N=777, d_r=64, d_v=32, K=50, chunk=16, seed=57),   # ragged, chunk 16
+    bf16_case(causal=True, B=1, H=2, N=900, d_r=32, d_v=64, K=100, seed=143),           # K padded 100 -> 128
+    bf16_case(causal=True, B=1, H=1, N=700, d_r=32, d_v=64, K=150, seed=144),           # K padded 150 -> 256
+    bf16_case(causal=True, B=2, H=1, N=500, d_r=16, d_v=128, K=200, seed=145),          # K padded 200 -> 256
 ]
 
 
@@ -253,15 +259,69 @@ def test_bf16_workspace_reuse_and_garbage(causal):
 @pytest.mark.parametrize("causal", [False, True], ids=["bidir", "causal"])
 def test_bf16_wait_timeout_gives_nan(causal):
     """Failure path of the in-launch hand-off, forced from the host: with a wait bound of 0
-    every workgroup's wait fails at once, the launch still ends, and every output row is
-    NaN.  Restoring the default bound gives the normal result again."""
+    every workgroup's wait fails at once, the launch still ends, every output row is NaN (and
+    so is the carried memory of a causal call), and gma_device_status reports the timeout once.
+    Restoring the default bound gives the normal result again, with no error reported."""
     w = bf16_case(causal=causal, B=1, H=2, N=1500, seed=63)
     inp = make_inputs(w)
     ref = to_np(run_gpu(w, inp))
+    assert gb.gma_device_status() == gb.GMA_OK
+    state = None
     try:
         gb.gma_set_wait_limit(0)
-        out = to_np(run_gpu(w, inp))
+        if causal:
+            d = to_device(inp)
+            state = torch.zeros(w.B, w.H, w.K, w.d_v + 1, dtype=torch.float32, device="cuda")
+            out, _ = gb.gma_forward_causal_state(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps,
+                                                 chunk=w.chunk, state_out=state)
+            torch.cuda.synchronize()
+            out = to_np(out)
+        else:
+            out = to_np(run_gpu(w, inp))
     finally:
         gb.gma_set_wait_limit(gb.WAIT_LIMIT_DEFAULT)
     assert np.isnan(out).all()
+    if causal:
+        assert torch.isnan(state).all()
+    assert gb.gma_device_status() == gb.GMA_ERR_TIMEOUT
+    assert gb.gma_device_status() == gb.GMA_OK  # taking the status clears it
     assert np.array_equal(to_np(run_gpu(w, inp)), ref)
+    assert gb.gma_device_status() == gb.GMA_OK
+
+
+BF16_SPLIT_LAUNCH_CASES = [
+    bf16_case(B=2, H=3, N=2900, seed=64),
+    bf16_case(B=1, H=1, N=70000, d_r=32, d_v=64, K=128, mu_std=1.5, seed=65),
+    bf16_case(causal=True, B=2, H=3, N=2900, seed=66),
+    bf16_case(causal=True, B=1, H=2, N=3001, d_r=32, d_v=64, K=128, seed=67),
+    bf16_case(causal=True, B=1, H=1, N=1100, d_r=64, d_v=128, K=256, seed=68),
+]
+
+
+@pytest.mark.parametrize("w", BF16_SPLIT_LAUNCH_CASES, ids=case_id)
+def test_bf16_single_launch_off_is_bitwise_equal(w):
+    """gma_set_single_launch(0) runs every phase as its own launch (no workgroup waits for another):
+    the same arithmetic in the same order, so the outputs are bit-identical."""
+    inp = make_inputs(w)
+    a = to_np(run_gpu(w, inp))
+    try:
+        gb.gma_set_single_launch(False)
+        b = to_np(run_gpu(w, inp))
+    finally:
+        gb.gma_set_single_launch(True)
+    assert np.array_equal(a, b)
+    assert gb.gma_device_status() == gb.GMA_OK
+
+
+def test_bf16_bidir_one_head_long_sequence():
+    """One problem (B = H = 1) of 262144 positions at the largest per-workgroup LDS (d_r 64, d_v 128,
+    K 256): the split count is bounded by the workgroups the device keeps resident, so the
+    single-launch hand-off completes; every row against the oracle."""
+    w = bf16_case(B=1, H=1, N=262144, d_r=64, d_v=128, K=256, seed=69)
+    info = gb.gma_plan_info(gb.GMA_OP_BIDIR, w.B, w.H, w.N, w.d_r, w.d_v, w.K, gb.GMA_BF16)
+    assert info["workgroups"] <= info["resident_bound"]
+    inp = make_inputs(w)
+    out = run_gpu(w, inp)
+    assert gb.gma_device_status() == gb.GMA_OK
+    err = row_scaled_error(to_np(out), run_oracle(w, inp))
+    assert err <= TOL["bf16"], err
