@@ -29,7 +29,8 @@ EXPORTED = ["gma_status_string", "gma_workspace_size", "gma_responsibilities", "
             "gma_forward_causal", "gma_forward_causal_state", "gma_cross_workspace_size", "gma_forward_cross", "gma_responsibility_diagnostics", "gma_backward_bidir",
             "gma_backward_causal", "gma_backward_causal_state", "gma_backward_cross_workspace_size", "gma_backward_cross", "gma_profiling",
             "gma_profiling_collect", "gma_set_wait_limit", "gma_device_status", "gma_set_single_launch",
-            "gma_plan_info"]
+            "gma_plan_info", "gma_forward_bidir_noalloc"]
+STATIC_SCRATCH_BYTES = 32 << 20  # GMA_STATIC_SCRATCH_BYTES
 WAIT_LIMIT_DEFAULT = 1 << 18  # GMA_WAIT_LIMIT_DEFAULT
 
 
@@ -119,6 +120,8 @@ def load() -> ctypes.CDLL:
             lib.gma_set_single_launch.restype = i32
             lib.gma_plan_info.argtypes = [i32, shp, i32, i32, ctypes.POINTER(PlanInfo)]
             lib.gma_plan_info.restype = i32
+            lib.gma_forward_bidir_noalloc.argtypes = [vp, vp, vp, i32, vp, vp, vp, f32, vp, shp, vp]
+            lib.gma_forward_bidir_noalloc.restype = i32
             _lib = lib
     return _lib
 
@@ -427,3 +430,17 @@ def gma_plan_info(op: int, B: int, H: int, N: int, d_r: int, d_v: int, K: int, i
     _check(load().gma_plan_info(op, ctypes.byref(Shape(B, H, N, d_r, d_v, K)), io_dtype, chunk, ctypes.byref(info)),
            "gma_plan_info")
     return {n: getattr(info, n) for n, _ in PlanInfo._fields_}
+
+
+def gma_forward_bidir_noalloc(xq: torch.Tensor, xk: torch.Tensor, v: torch.Tensor, mu: torch.Tensor,
+                              sigma2: torch.Tensor, pi: torch.Tensor, eps: float, out: torch.Tensor,
+                              stream=None) -> torch.Tensor:
+    """gma_forward_bidir on the library's static scratch: no workspace, and the caller provides `out`
+    (so that nothing is allocated)."""
+    B, H, N, dr = xq.shape
+    dv = v.shape[-1]
+    K = mu.shape[1]
+    _check(load().gma_forward_bidir_noalloc(_ptr(xq), _ptr(xk), _ptr(v), _dtype_code(xq.dtype), _ptr(mu), _ptr(sigma2),
+                                            _ptr(pi), float(eps), _ptr(out), ctypes.byref(Shape(B, H, N, dr, dv, K)),
+                                            _stream(stream)), "gma_forward_bidir_noalloc")
+    return out

@@ -271,6 +271,12 @@ bool single_launch_enabled() { return g_single_launch.load(std::memory_order_rel
 __device__ uint32_t d_error_word;
 __device__ uint32_t d_error_taken;
 
+// Scratch of gma_forward_bidir_noalloc (the workspace it does not take): one per device, held
+// until the process ends.  In host code the name is only a handle for hipGetSymbolAddress;
+// kernels receive the device address it resolves to.
+constexpr size_t kStaticScratchBytes = size_t(GMA_STATIC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
 __global__ void take_error_kernel(uint32_t* word, uint32_t* taken) {
     if (threadIdx.x == 0) *taken = atomicExch(word, 0u);
 }
@@ -282,6 +288,7 @@ struct DeviceWords {
     hipError_t status = hipSuccess;
     uint32_t* word = nullptr;
     uint32_t* taken = nullptr;
+    void* scratch = nullptr;  // this device's copy of `scratch`
 };
 DeviceWords g_words[kMaxDevices];
 
@@ -295,6 +302,7 @@ hipError_t device_words(DeviceWords** out) {
         w.status = hipGetSymbolAddress(reinterpret_cast<void**>(&w.word), HIP_SYMBOL(d_error_word));
         if (w.status == hipSuccess)
             w.status = hipGetSymbolAddress(reinterpret_cast<void**>(&w.taken), HIP_SYMBOL(d_error_taken));
+        if (w.status == hipSuccess) w.status = hipGetSymbolAddress(&w.scratch, HIP_SYMBOL(scratch));
     });
     *out = &w;
     return w.status;
@@ -483,6 +491,21 @@ gma_status_t gma_forward_bidir(const void* XQ, const void* XK, const void* V, gm
                                size_t workspace_bytes, hipStream_t stream) {
     return forward_common(GMA_OP_BIDIR, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, O, shape, 0,
                           workspace, workspace_bytes, stream);
+}
+
+gma_status_t gma_forward_bidir_noalloc(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                                       const float* mu, const float* sigma2, const float* pi, float eps, void* O,
+                                       const gma_shape_t* shape, hipStream_t stream) {
+    if (!shape) return GMA_ERR_NULL_POINTER;
+    size_t need = 0;
+    gma_status_t st = gma_workspace_size(GMA_OP_BIDIR, shape, io_dtype, 0, &need);
+    if (st != GMA_OK) return st;
+    if (need > gma::kStaticScratchBytes) return GMA_ERR_WORKSPACE_TOO_SMALL;  // before any HIP call
+    if (!mu || !sigma2 || !pi) return GMA_ERR_NULL_POINTER;
+    gma::DeviceWords* w = nullptr;
+    if (gma::device_words(&w) != hipSuccess) return GMA_ERR_HIP;
+    return forward_common(GMA_OP_BIDIR, XQ, XK, V, io_dtype, mu, sigma2, pi, eps, O, shape, 0, w->scratch,
+                          gma::kStaticScratchBytes, stream);
 }
 
 gma_status_t gma_forward_causal(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,

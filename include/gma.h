@@ -146,6 +146,24 @@ gma_status_t gma_forward_bidir(const void* XQ, const void* XK, const void* V,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * gma_forward_bidir without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  It makes no allocation of any kind: its scratch is a static device array of
+ * GMA_STATIC_SCRATCH_BYTES inside the library, one per device, resolved when the first call on
+ * that device (or gma_device_status) runs there and held until the process ends.  Shapes whose
+ * workspace (gma_workspace_size(GMA_OP_BIDIR, ...)) exceeds that size are rejected with
+ * GMA_ERR_WORKSPACE_TOO_SMALL before any HIP call.  Every call on a device shares that device's
+ * array and the kernels leave their contents in it: calls that overlap on one device (several
+ * streams, several host threads) race and must be serialised by the caller.  The kernels never
+ * read scratch they did not write in the same call, so no clearing is needed.  Arguments, results
+ * (bitwise those of gma_forward_bidir), dtypes and errors otherwise as for gma_forward_bidir.
+ */
+#define GMA_STATIC_SCRATCH_BYTES (32u << 20)
+gma_status_t gma_forward_bidir_noalloc(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
+                                       const float* mu, const float* sigma2, const float* pi, float eps, void* O,
+                                       const gma_shape_t* shape, hipStream_t stream);
+
+/*
  * Causal GMA forward, Sec. 3.5 Eq. 6b and 8b:
  *   Vt^(i) = sum_{j<=i} gammaK_j V_j^T,  Z^(i) = sum_{j<=i} gammaK_j   (inclusive of i)
  *   O_i    = gammaQ_i Vt^(i) / (gammaQ_i Z^(i) + eps)
