@@ -33,78 +33,6 @@
 namespace gma {
 namespace bf {
 
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// 16x16x32 fragment with k down a column of a row-major LDS tile:
-// lane (g, i) gets tile[row0 + 8 g + v][col0 + i], v = 0..7.  Within each 16-lane group
-// the transposing read hands output lane q, element v, the value at offset q % 4 of the
-// 8 bytes addressed by source lane 4 v + q / 4; source lane m therefore addresses row
-// (m / 4), columns 4 (m % 4) .. + 3.
-__device__ __forceinline__ bf16x8 read_colfrag16(const uint16_t* tile, int ld, int row0, int col0) {
-    const int l = threadIdx.x & 63;
-    const int g = l >> 4, m = l & 15;
-    const uint16_t* base = tile + (row0 + 8 * g + (m >> 2)) * ld + col0 + 4 * (m & 3);
-    i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
-    i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 4 * ld));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-struct ScanStats {
-    float m, L, D;
-};
-
-// The scans keep the memory as 16x16 MFMA accumulators: mem[cc][kt] holds Vt[k][c] for value
-// column c = 16 (wave + cc NW) + l % 16 and components k = 16 kt + 4 (l / 16) + r, r = 0..3
-// (Vt^T's D layout), and Z in LDS.  The carried memory of gma_forward_causal_state is
-// [K][DV + 1] fp32 (row k: Vt_k then Z_k); components k >= K (padding) are zero.  Thread t
-// initialises Z entries ZV t .. ZV t + ZV - 1 (+ ZV NT, ...): the same entries it later adds
-// the earlier segments' aggregates to, so no barrier is needed in between.
-template <int CPW, int KT16, int NW, int DV, int ZV>
-__device__ __forceinline__ void init_memory(f32x4 (&mem)[CPW][KT16], float* Zs, int Kp, int NT,
-                                            const float* __restrict__ state, int K) {
-    const int l = threadIdx.x & 63, g4 = l >> 4, i16 = l & 15, wave = wave_id();
-#pragma unroll
-    for (int cc = 0; cc < CPW; ++cc)
-#pragma unroll
-        for (int kt = 0; kt < KT16; ++kt) {
-            const int c = (wave + cc * NW) * 16 + i16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int k = kt * 16 + 4 * g4 + r;
-                mem[cc][kt][r] = (state && c < DV && k < K) ? state[size_t(k) * (DV + 1) + c] : 0.0f;
-            }
-        }
-    for (int k0 = threadIdx.x * ZV; k0 < Kp; k0 += NT * ZV)
-#pragma unroll
-        for (int r = 0; r < ZV; ++r) {
-            const int k = k0 + r;
-            Zs[k] = (state && k < K) ? state[size_t(k) * (DV + 1) + DV] : 0.0f;
-        }
-}
-
-// Writes the memory back in the carried layout; Zs must be complete (after a barrier).
-template <int CPW, int KT16, int NW, int DV>
-__device__ __forceinline__ void store_memory(const f32x4 (&mem)[CPW][KT16], const float* Zs, float* __restrict__ state,
-                                             int K) {
-    const int l = threadIdx.x & 63, g4 = l >> 4, i16 = l & 15, wave = wave_id();
-#pragma unroll
-    for (int cc = 0; cc < CPW; ++cc)
-#pragma unroll
-        for (int kt = 0; kt < KT16; ++kt) {
-            const int c = (wave + cc * NW) * 16 + i16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int k = kt * 16 + 4 * g4 + r;
-                if (c < DV && k < K) state[size_t(k) * (DV + 1) + c] = mem[cc][kt][r];
-            }
-        }
-    for (int k = threadIdx.x; k < K; k += int(blockDim.x)) state[size_t(k) * (DV + 1) + DV] = Zs[k];
-}
-
 template <int DR, int KT, int CH>
 constexpr int scan_jpw() {  // 32-position score jobs per wave and chunk (query and key)
     return (2 * (CH / 32) + Split<DR, KT>::TS - 1) / Split<DR, KT>::TS;
@@ -976,8 +904,9 @@ hipError_t with_all(int dr, int kt, int vt, int ch, F&& f) {
         return f(std::integral_constant<int, D>(), std::integral_constant<int, T>(), std::integral_constant<int, W>(), \
                  std::integral_constant<int, 64>());
 #define GMA_SCAN_VT(D, T) GMA_SCAN_CH(D, T, 1) GMA_SCAN_CH(D, T, 2) GMA_SCAN_CH(D, T, 4)
-#define GMA_SCAN_KT(D) GMA_SCAN_VT(D, 1) GMA_SCAN_VT(D, 2) GMA_SCAN_VT(D, 4) GMA_SCAN_VT(D, 8)
-    GMA_SCAN_KT(16) GMA_SCAN_KT(32) GMA_SCAN_KT(64) GMA_SCAN_KT(128)
+#define GMA_SCAN_KT(D) GMA_SCAN_VT(D, 1) GMA_SCAN_VT(D, 2) GMA_SCAN_VT(D, 4)
+    // 8 component tiles with d_r <= 64 take the wide scan (gma_bf16_wide.hip)
+    GMA_SCAN_KT(16) GMA_SCAN_KT(32) GMA_SCAN_KT(64) GMA_SCAN_KT(128) GMA_SCAN_VT(128, 8)
 #undef GMA_SCAN_KT
 #undef GMA_SCAN_VT
 #undef GMA_SCAN_CH
@@ -993,6 +922,8 @@ hipError_t with_all(int dr, int kt, int vt, int ch, F&& f) {
 hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu, const float* s2,
                        const float* pi, float eps, void* O, char* ws, hipStream_t st, const float* state_in,
                        float* state_out) {
+    if (bf16_causal_wide_applies(p))
+        return bf16_causal_wide(p, XQ, XK, V, mu, s2, pi, eps, O, ws, st, state_in, state_out);
     const bf::Mixture mx{mu, s2, pi, int(p.K)};
     float* aggregates = reinterpret_cast<float*>(ws + p.off_partials);
     uint64_t* flags = reinterpret_cast<uint64_t*>(ws + p.off_flags);

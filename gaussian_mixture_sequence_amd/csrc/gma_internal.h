@@ -148,6 +148,12 @@ hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void*
 hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void* V,
                        const float* mu, const float* s2, const float* pi, float eps, void* O,
                        char* ws, hipStream_t st, const float* state_in, float* state_out);
+// Causal forward for 256 padded components with d_r <= 64 (gma_bf16_wide.hip): one launch of
+// 8-wave workgroups, the memory spread over the waves' registers.
+bool bf16_causal_wide_applies(const Plan& p);
+hipError_t bf16_causal_wide(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu,
+                            const float* s2, const float* pi, float eps, void* O, char* ws, hipStream_t st,
+                            const float* state_in, float* state_out);
 // Segment aggregates (the first `splits` segments) into the partials region: the first
 // launch of the causal path for shapes the fused causal kernel does not take.
 hipError_t bf16_write_partials(const Plan& p, const void* XK, const void* V, const float* mu, const float* s2,
