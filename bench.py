@@ -1,16 +1,19 @@
 #!/usr/bin/env python3
 """Throughput benchmark of the GMA forward (bidirectional and causal) on one MI355X.
 
-One step = one pass of the whole hot path over one batch of synthetic input: the
-bidirectional forward on the B=8, H=8, N=4096 workload (d_r=64, d_v=64, K=64) and the
-causal forward on the B=8, H=12, N=2048 workload (d_r=64, d_v=64, K=32, chunk 64), both
-bf16 I/O with fp32 accumulation.  Inputs are resident in HBM before timing starts and
+One step = one pass of the whole hot path over one batch of synthetic input of each bf16
+workload: the bidirectional forward at B=8, H=8, N=4096 (d_r=64, d_v=64, K=64), the causal
+forward at B=8, H=12, N=2048 (d_r=64, d_v=64, K=32, chunk 64), the long-context
+bidirectional forward at B=4, H=4, N=65536 (d_r=32, d_v=64, K=128) and the long causal
+forward at B=2, H=16, N=32768 (d_r=64, d_v=128, K=256), all bf16 I/O with fp32
+accumulation.  Inputs are resident in HBM before timing starts and
 rotate over several independent input sets (more bytes than the 256 MB Infinity Cache)
 so that every step reads from HBM.
 
-Output: one JSON line with the whole-step throughput (tokens/s), the roofline fraction
-of the dominant kernel (per-kernel times from the library's hipEvent hooks, taken in a
-second pass over the same steps) and the oracle timed on the host cores.
+Output: one JSON line with the whole-step throughput (tokens/s), each workload's kernel
+against its roofline (HBM or bf16 MFMA, whichever bounds it at peak; per-kernel times from
+the library's hipEvent hooks, taken in a second pass over the same steps, one workload at a
+time), the step's dominant kernel as `roofline`, and the oracle timed on the host cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sets S] [--no-cpu-baseline]
 """
@@ -29,7 +32,7 @@ if ROOT not in sys.path:
 METRIC = "GMA forward tokens/s (bidir & causal) + achieved HBM GB/s / MFMA % of peak"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
-DEFAULT_STEP = ["bidir_b8h8_n4096", "causal_b8h12_n2048"]
+DEFAULT_STEP = ["bidir_b8h8_n4096", "causal_b8h12_n2048", "bidir_long_n65536", "causal_long_n32768"]
 
 
 def parse():
@@ -51,6 +54,12 @@ def parse():
                          "(CSV output under DIR) into --trace-out")
     ap.add_argument("--trace-out", metavar="FILE", default=None)
     ap.add_argument("--trace-command", default=None, help="the command that produced DIR, recorded in the summary")
+    ap.add_argument("--memory-sweep", action="store_true",
+                    help="peak device memory of the bidirectional forward at the long-context dims (B=4, H=4, d_r=32, "
+                         "d_v=64, K=128, bf16) for N = 4096 .. 65536, with a linear fit; JSON to stdout (and --trace-out)")
+    ap.add_argument("--hip-trace-summarize", metavar="DIR", default=None,
+                    help="count the HIP API calls made while the library runs, from a rocprofv3 --hip-trace "
+                         "--kernel-trace run of --traffic-probe step (CSV output under DIR), into --trace-out")
     ap.add_argument("--counters-summarize", metavar="DIR", default=None,
                     help="summarise rocprofv3 --pmc runs of --traffic-probe step (one subdirectory per pass under DIR) "
                          "into utilisation figures per library kernel, written to --trace-out")
@@ -233,6 +242,92 @@ def counters_summarize(d: str, out: str, workloads: str, command: str) -> int:
     return 0
 
 
+def memory_sweep(out: str) -> int:
+    """Device memory of one forward at the long-context dims for growing N: what the caller
+    allocates (inputs, output and the library's workspace; torch.cuda.memory_allocated) and the
+    peak while the call runs (torch.cuda.max_memory_allocated, which stays at the former: the
+    library allocates nothing).  A least-squares line in N fits it; the quadratic term of a second
+    fit is reported relative to the largest value (Sec. 5.1: memory grows linearly in N)."""
+    import numpy as np
+    import torch
+    from gaussian_mixture_sequence_amd import binding as gb
+    from gaussian_mixture_sequence_amd.inputs import WORKLOADS, make_inputs
+    gb.load()
+    res = {"command": "python bench.py --memory-sweep", "variants": {}}
+    for causal in (False, True):
+        base = WORKLOADS["bidir_long_n65536"].with_(causal=causal)
+        rows = []
+        for n in (4096, 8192, 16384, 32768, 49152, 65536):
+            w = base.with_(N=n)
+            torch.cuda.empty_cache()
+            torch.cuda.synchronize()
+            before = torch.cuda.memory_allocated()
+            d = {k: v.cuda() for k, v in make_inputs(w).items()}
+            op = gb.GMA_OP_CAUSAL if causal else gb.GMA_OP_BIDIR
+            ws_bytes = gb.gma_workspace_size(op, w.B, w.H, w.N, w.d_r, w.d_v, w.K, gb.GMA_BF16, w.chunk if causal else 0)
+            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+            o = torch.empty(w.B, w.H, w.N, w.d_v, dtype=torch.bfloat16, device="cuda")
+            torch.cuda.synchronize()
+            held = torch.cuda.memory_allocated()
+            torch.cuda.reset_peak_memory_stats()
+            if causal:
+                gb.gma_forward_causal(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps, chunk=w.chunk,
+                                      out=o, workspace=ws)
+            else:
+                gb.gma_forward_bidir(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps, out=o, workspace=ws)
+            torch.cuda.synchronize()
+            peak = torch.cuda.max_memory_allocated()
+            rows.append({"N": n, "call_bytes": int(held - before), "peak_during_call_minus_held": int(peak - held),
+                         "workspace_bytes": int(ws_bytes),
+                         "gamma_fp32_bytes_if_materialised": int(2 * w.B * w.H * n * w.K * 4)})
+            del d, ws, o
+        ns = np.array([r["N"] for r in rows], float)
+        pk = np.array([r["call_bytes"] for r in rows], float)
+        b, a = np.polyfit(ns, pk, 1)
+        q = np.polyfit(ns, pk, 2)
+        res["variants"]["causal" if causal else "bidirectional"] = {
+            "workload": "%s forward, B=4 H=4 d_r=32 d_v=64 K=128 bf16" % ("causal" if causal else "bidirectional"),
+            "rows": rows,
+            "linear_fit": {"bytes_per_position": b, "intercept_bytes": a,
+                           "max_abs_residual_rel": float(np.abs(pk - (a + b * ns)).max() / pk.max())},
+            "quadratic_term_rel": float(abs(q[0]) * ns.max() ** 2 / pk.max())}
+    text = json.dumps(res, indent=1)
+    print(text)
+    if out:
+        with open(out, "w") as f:
+            f.write(text + "\n")
+    return 0
+
+
+def hip_trace_summarize(d: str, out: str, command: str) -> int:
+    """HIP API calls from the first library kernel launch on, by function name, from the CSVs of a
+    rocprofv3 --hip-trace --kernel-trace run of `--traffic-probe step` (every buffer is allocated
+    before that launch).  Allocation calls in that window would be the library's."""
+    import csv
+    import glob
+    kt = [r for f in glob.glob(os.path.join(d, "**", "*_kernel_trace.csv"), recursive=True) for r in csv.DictReader(open(f))]
+    api = [r for f in glob.glob(os.path.join(d, "**", "*_hip_api_trace.csv"), recursive=True) for r in csv.DictReader(open(f))]
+    gma = [r for r in kt if "gma::" in r["Kernel_Name"]]
+    if not gma or not api:
+        print("no library kernels or no HIP API records under %s" % d, file=sys.stderr)
+        return 1
+    first_corr = min(int(r["Correlation_Id"]) for r in gma)
+    start = min(int(r["Start_Timestamp"]) for r in api if int(r["Correlation_Id"]) == first_corr)
+    counts = {}
+    for r in api:
+        if int(r["Start_Timestamp"]) >= start:
+            counts[r["Function"]] = counts.get(r["Function"], 0) + 1
+    alloc = {k: v for k, v in counts.items() if "alloc" in k.lower() or "free" in k.lower()}
+    lines = ["# HIP API calls from the first library kernel launch on (%d library kernel dispatches)" % len(gma),
+             "# command (run from the repository root on one MI355X):", "#   " + (command or "?"),
+             "allocation or free calls in the window: %d %s" % (sum(alloc.values()), json.dumps(alloc))]
+    lines += ["%-40s %8d" % kv for kv in sorted(counts.items(), key=lambda kv: -kv[1])]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+    return 0
+
+
 def measured_traffic(kernel_symbol_prefix: str, workloads: str):
     """HBM bytes per launch of the kernel, from the workload set's traffic record when that record
     was taken on the current kernel sources."""
@@ -314,6 +409,130 @@ def alg_flops_per_token_head(w, kernel: str) -> float:
     return 0.0
 
 
+def alg_mfma_flops_per_token_head(w, kernel: str) -> float:
+    """Algorithmic flops per (token, head) of a bf16 forward kernel: the score contractions of both
+    sides, 2 x 2 K d_r MACs (Sec. 3.4, Eq. 12's 2 N K d_r term), the write and the read,
+    2 x K (d_v + 1) MACs, and for the chunked causal form the in-chunk products, C (K + d_v + 1)
+    MACs for a chunk of C positions (an FMA counts 2 flops)."""
+    if w.backward or w.diagnostics or w.dtype != "bf16":
+        return 0.0
+    K, dr, dv = w.K, w.d_r, w.d_v
+    full = 8 * K * dr + 4 * K * (dv + 1)
+    if kernel.endswith("_write") or kernel.endswith("_causal_aggregate"):
+        return 4 * K * dr + 2 * K * (dv + 1)
+    if kernel.endswith("_read"):
+        return 4 * K * dr + 2 * K * (dv + 1)
+    if kernel.endswith("_causal") or kernel.endswith("_scan"):
+        return full + 2 * w.chunk * (K + dv + 1)
+    if kernel.endswith("_bidir") or kernel.endswith("_cross"):
+        return full
+    return 0.0
+
+
+def component_tiles(K: int) -> int:
+    """32-component tiles the bf16 kernels are compiled for (K padded to 1, 2, 4 or 8 tiles)."""
+    t = (K + 31) // 32
+    return 1 if t <= 1 else 2 if t <= 2 else 4 if t <= 4 else 8
+
+
+def kernel_symbol(w, name: str) -> str:
+    """The demangled symbol (up to its argument list) of the kernel a bench name stands for."""
+    if w.dtype == "bf16" and not w.backward and not w.diagnostics and not w.decode:
+        kt, vt = component_tiles(w.K), w.d_v // 32
+        if name.endswith("_bidir") or name.endswith("_cross"):
+            return "gma::bf::bidir_kernel<%d, %d, %d>" % (w.d_r, kt, vt)
+        if name.endswith("_causal"):
+            if kt == 8 and w.d_r <= 64:
+                return "gma::bf::wide_causal_kernel<%d, %d>" % (w.d_r, vt)
+            if kt <= 4 and w.d_r * kt <= 256:
+                return "gma::bf::causal_kernel<%d, %d, %d, %d>" % (w.d_r, kt, vt, max(32, w.chunk))
+    return KERNEL_SYMBOL.get(name, "?")
+
+
+def kernel_roofline(w, name: str, entry: dict, workloads: str, steps: int):
+    """A kernel's algorithmic rate against its roofline: the bf16 forwards against HBM and bf16
+    MFMA peaks (bound = whichever would take longer at peak), the fp32 backward passes against the
+    fp32 vector peak."""
+    avg_us = entry["avg_us"]
+    sym = kernel_symbol(w, name)
+    base = {"kernel": "%s/%s" % (w.name, name), "symbol": sym, "avg_us": avg_us,
+            "launches_per_step": entry["launches"] / max(steps, 1),
+            "traffic": measured_traffic(sym, workloads)}
+    if "alg_TFLOPs" in entry:  # the fp32 backward: bound by vector ALU issue
+        ach = entry["alg_TFLOPs"]
+        return dict(base, bound="alu", achieved=ach, peak=F32_VALU_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach / F32_VALU_PEAK_TFLOPS, 4), alg_flops_per_launch=entry["alg_flops_per_launch"],
+                    alg_bytes_per_launch=entry.get("alg_bytes_per_launch"))
+    if "alg_GBps" not in entry:
+        return None
+    hbm_frac = entry["alg_GBps"] / HBM_PEAK_GBPS
+    r = dict(base, alg_bytes_per_launch=entry["alg_bytes_per_launch"], hbm_frac=round(hbm_frac, 4))
+    t_hbm = entry["alg_bytes_per_launch"] / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = entry.get("alg_mfma_flops_per_launch", 0) / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+    if "alg_mfma_TFLOPs" in entry:
+        r["alg_mfma_flops_per_launch"] = entry["alg_mfma_flops_per_launch"]
+        r["mfma_frac"] = round(entry["alg_mfma_TFLOPs"] / BF16_MFMA_PEAK_TFLOPS, 4)
+    if t_mfma > t_hbm:
+        ach = entry["alg_mfma_TFLOPs"]
+        r.update(bound="mfma", achieved=ach, peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                 frac=round(ach / BF16_MFMA_PEAK_TFLOPS, 4))
+    else:
+        ach = entry["alg_GBps"]
+        r.update(bound="hbm", achieved=ach, peak=HBM_PEAK_GBPS, unit="GB/s", frac=round(hbm_frac, 4))
+    return r
+
+
+def cpu_baseline(ws_list) -> dict:
+    """The oracle (fp64 C with OpenMP over (batch, head) problems) on a bounded sample of every
+    workload of the step: the first batch entries of each workload, as many whole sequences as
+    there are threads (all heads of a sequence at once), timed on the host cores; then, on one
+    thread, the first 2048 positions of one (batch, head) problem of each workload.  The method
+    is linear in the sequence length, so a workload's rate is its sample's token rate, and the
+    step's is its tokens over the summed estimated times of its workloads."""
+    import oracle
+    from gaussian_mixture_sequence_amd.inputs import make_inputs
+    if any(w.backward for w in ws_list):
+        cpu_inputs = [(w, {k: oracle._f64(v) for k, v in make_inputs(w).items()}) for w in ws_list if w.backward]
+        return cpu_backward_sample(cpu_inputs)
+    threads = oracle.num_threads()
+
+    def run(w, inp, b1, h1, n1):
+        sl = {k: (v[:b1, :h1, :n1].contiguous() if k in ("xq", "xk", "v") else v[:h1].contiguous())
+              for k, v in inp.items()}
+        if w.diagnostics:
+            t0 = time.perf_counter()
+            oracle.diagnostics.diagnostics(sl["xq"], sl["mu"], sl["sigma2"], sl["pi"])
+            return time.perf_counter() - t0
+        fn = oracle.forward_causal if w.causal else oracle.forward_cross if w.cross else oracle.forward_bidir
+        t0 = time.perf_counter()
+        fn(sl["xq"], sl["xk"], sl["v"], sl["mu"], sl["sigma2"], sl["pi"], w.eps)
+        return time.perf_counter() - t0
+
+    samples, est_s, est_1_s = [], 0.0, 0.0
+    for w in ws_list:
+        inp = make_inputs(w)
+        bs = max(1, min(w.B, threads // max(w.H, 1)))
+        dt = run(w, inp, bs, w.H, w.N)
+        rate = bs * w.N / dt  # tokens (all heads) per second
+        est_s += w.B * w.N / rate
+        samples.append("%s: %d sequence(s) x %d heads x %d positions in %.2f s" % (w.name, bs, w.H, w.N, dt))
+    oracle.set_num_threads(1)
+    try:
+        for w in ws_list:
+            inp = make_inputs(w)
+            n1 = min(w.N, 2048)
+            dt = run(w, inp, 1, 1, n1)
+            est_1_s += w.B * w.N * w.H / (n1 / dt)  # one head-row per position per second
+    finally:
+        oracle.set_num_threads(threads)
+    tokens = sum(w.B * w.N for w in ws_list)
+    return {"value": round(tokens / est_s, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "; ".join(samples) + "; fp64 C oracle, OpenMP over (batch, head); step time estimated "
+                      "from each workload's sample rate",
+            "single_thread": {"value": round(tokens / est_1_s, 1), "unit": "tokens/s", "cores": 1,
+                              "sample": "first 2048 positions of (batch 0, head 0) of each workload, one thread"}}
+
+
 KERNEL_SYMBOL = {"bf16_scan": "gma::bf::scan_kernel", "bf16_bidir": "gma::bf::bidir_kernel",
                  "bf16_cross": "gma::bf::bidir_kernel", "bf16_resp": "gma::bf::resp_kernel",
                  "bf16_decode": "gma::dec::decode_kernel", "bf16_diag": "gma::diag::diag_fused_kernel",
@@ -355,6 +574,10 @@ def main(args=None, probe_only=False) -> int:
         return traffic_summarize(args.traffic_summarize, args.workloads)
     if args.trace_summarize:
         return trace_summarize(args.trace_summarize, args.trace_out, args.workloads, args.trace_command)
+    if args.memory_sweep:
+        return memory_sweep(args.trace_out)
+    if args.hip_trace_summarize:
+        return hip_trace_summarize(args.hip_trace_summarize, args.trace_out, args.trace_command)
     if args.counters_summarize:
         return counters_summarize(args.counters_summarize, args.trace_out, args.workloads, args.trace_command)
     if args.traffic_probe and not probe_only:
@@ -418,8 +641,13 @@ def main(args=None, probe_only=False) -> int:
     stream = torch.cuda.current_stream()
 
     def step(k: int) -> None:
+        for i in range(len(ws_list)):
+            step_one(k, i)
+
+    def step_one(k: int, i: int) -> None:
         s = k % args.sets
-        for i, w in enumerate(ws_list):
+        w = ws_list[i]
+        if True:
             d = sets[s][i]
             if w.diagnostics:
                 gb.gma_responsibility_diagnostics(d["xq"], d["mu"], d["sigma2"], d["pi"], workspace=wss[i],
@@ -469,37 +697,26 @@ def main(args=None, probe_only=False) -> int:
     tokens_per_step = sum(w.B * (1 if w.decode else w.N) for w in ws_list)
     value = tokens_per_step * args.steps / wall
 
-    # ---- per-kernel durations: the same steps again with the library's hipEvent hooks
-    gb.gma_profiling(True)
-    torch.cuda.synchronize()
-    tp0 = time.perf_counter()
-    for k in range(args.steps):
-        step(k)
-    torch.cuda.synchronize()
-    prof_wall = time.perf_counter() - tp0
-    kstats = gb.gma_profiling_collect()
-    gb.gma_profiling(False)
+    # ---- per-kernel durations: the same steps again, one workload at a time, with the library's
+    # hipEvent hooks (events recorded on the launch stream around every library launch)
+    per_wl = []
+    prof_ms = 0.0
+    for i in range(len(ws_list)):
+        gb.gma_profiling(True)
+        torch.cuda.synchronize()
+        tp0 = time.perf_counter()
+        for k in range(args.steps):
+            step_one(k, i)
+        torch.cuda.synchronize()
+        prof_ms += 1000.0 * (time.perf_counter() - tp0)
+        per_wl.append(gb.gma_profiling_collect())
+        gb.gma_profiling(False)
 
-    # which workload launches which kernel (names are unique per op)
-    kernel_of = {}
-    for w in ws_list:
-        pre = "bf16" if w.dtype == "bf16" else "f32"
-        ks = ["params", "bwdc_aggregate", "bwdc_prefix", "bwdc_query", "bwdc_suffix", "bwdc_key", "bwd_params"] \
-            if w.backward and w.causal else \
-            ["params", "bwd_write", "bwd_combine", "bwd_query", "bwd_key", "bwd_params"] if w.backward else \
-            ["diag", "resp", "params"] if w.diagnostics else \
-            ["params", "scan", "causal_aggregate", "causal", "prefix", "decode"] if w.causal else \
-            ["params", "cross_write", "cross_combine", "cross_read", "cross"] if w.cross else \
-            ["params", "write", "combine", "read", "bidir"]
-        for k in ks:
-            kernel_of.setdefault("%s_%s" % (pre, k), []).append(w)
-    kernels = {}
-    for name, (launches, total_ms) in kstats.items():
-        avg_us = 1000.0 * total_ms / max(launches, 1)
-        entry = {"launches": launches, "avg_us": round(avg_us, 3)}
-        owners = kernel_of.get(name, [])
-        if len(owners) == 1:
-            w = owners[0]
+    kernels, rooflines = {}, []
+    for w, kstats in zip(ws_list, per_wl):
+        for name, (launches, total_ms) in kstats.items():
+            avg_us = 1000.0 * total_ms / max(launches, 1)
+            entry = {"launches": launches, "avg_us": round(avg_us, 3)}
             per_launch = alg_bytes_per_token_head(w, name) * w.B * w.H * (1 if w.decode else w.N)
             if per_launch:
                 entry["alg_bytes_per_launch"] = int(per_launch)
@@ -508,24 +725,20 @@ def main(args=None, probe_only=False) -> int:
             if flops:
                 entry["alg_flops_per_launch"] = int(flops)
                 entry["alg_TFLOPs"] = round(flops / (avg_us * 1e-6) / 1e12, 2)
-        kernels[name] = entry
-    dominant = max(kstats.items(), key=lambda kv: kv[1][1])[0] if kstats else None
+            mflops = alg_mfma_flops_per_token_head(w, name) * w.B * w.H * (1 if w.decode else w.N)
+            if mflops:
+                entry["alg_mfma_flops_per_launch"] = int(mflops)
+                entry["alg_mfma_TFLOPs"] = round(mflops / (avg_us * 1e-6) / 1e12, 2)
+            kernels["%s/%s" % (w.name, name)] = entry
+        if kstats:  # the workload's dominant kernel against its roofline
+            name = max(kstats.items(), key=lambda kv: kv[1][1])[0]
+            r = kernel_roofline(w, name, kernels["%s/%s" % (w.name, name)], args.workloads, args.steps)
+            if r:
+                rooflines.append(r)
+    # the step's dominant kernel (largest share of the step's time)
     roofline = None
-    if dominant and "alg_TFLOPs" in kernels[dominant]:  # the fp32 backward: bound by vector ALU issue
-        ach = kernels[dominant]["alg_TFLOPs"]
-        traffic = measured_traffic(KERNEL_SYMBOL.get(dominant, "?"), args.workloads)
-        roofline = {"kernel": dominant, "bound": "alu", "achieved": ach, "peak": F32_VALU_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(ach / F32_VALU_PEAK_TFLOPS, 4), "traffic": traffic,
-                    "avg_us": kernels[dominant]["avg_us"],
-                    "alg_flops_per_launch": kernels[dominant]["alg_flops_per_launch"],
-                    "alg_bytes_per_launch": kernels[dominant].get("alg_bytes_per_launch")}
-    elif dominant and "alg_GBps" in kernels[dominant]:
-        ach = kernels[dominant]["alg_GBps"]
-        traffic = measured_traffic(KERNEL_SYMBOL.get(dominant, "?"), args.workloads)
-        roofline = {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                    "avg_us": kernels[dominant]["avg_us"],
-                    "alg_bytes_per_launch": kernels[dominant]["alg_bytes_per_launch"]}
+    if rooflines:
+        roofline = max(rooflines, key=lambda r: r["avg_us"] * r["launches_per_step"])
 
     # ---- sanity: outputs finite
     for i in range(len(ws_list)):
@@ -548,7 +761,7 @@ def main(args=None, probe_only=False) -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if any(w.dtype == "bf16" for w in ws_list) else "f32",
-        "data": "synthetic (seeded; mu~N(0,1), sigma2=softplus(N(0,1))+1e-3, pi=softmax(N(0,1)), "
+        "data": "synthetic (seeded; mu~N(0,mu_std), sigma2=softplus(N(0,1))+1e-3, pi=softmax(N(0,1)), "
                 "X_Q,X_K,V~N(0,1); %d rotating input sets)" % args.sets,
         "config": {
             "workload": " + ".join("%s (%s B=%d H=%d %s d_r=%d d_v=%d K=%d%s)" % (
@@ -563,42 +776,14 @@ def main(args=None, probe_only=False) -> int:
         "step_alg_hbm_GBps": round(step_bytes / (wall / args.steps) / 1e9, 1),
         "step_alg_hbm_frac": round(step_bytes / (wall / args.steps) / 1e9 / HBM_PEAK_GBPS, 4),
         "roofline": roofline,
+        "rooflines": rooflines,
         "kernels": kernels,
-        "profiled_ms_per_step": round(1000.0 * prof_wall / args.steps, 4),
+        "profiled_ms_per_step": round(prof_ms / args.steps, 4),
     }
 
-    # ---- the oracle on the host cores, same workload (first input set), fp64
+    # ---- the oracle on the host cores, same workloads (first input set), fp64
     if not args.no_cpu_baseline:
-        import oracle
-        cpu_inputs = []
-        for w in ws_list:
-            inp = make_inputs(w)
-            cpu_inputs.append((w, {k: oracle._f64(v) for k, v in inp.items()}))
-        # the oracle over every position of every workload (for decoding: all N positions, which
-        # equals N one-position steps with the memory carried), repeated until about 10 s of CPU
-        # work have been timed
-        if any(w.backward for w in ws_list):
-            result["cpu_baseline"] = cpu_backward_sample([c for c in cpu_inputs if c[0].backward])
-        else:
-            cpu_tokens = sum(w.B * w.N for w in ws_list)
-            reps = 0
-            tc = time.perf_counter()
-            while True:
-                for w, d in cpu_inputs:
-                    if w.diagnostics:
-                        oracle.diagnostics.diagnostics(d["xq"], d["mu"], d["sigma2"], d["pi"])
-                        continue
-                    fn = oracle.forward_causal if w.causal else oracle.forward_cross if w.cross else oracle.forward_bidir
-                    fn(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], w.eps)
-                reps += 1
-                cpu_s = time.perf_counter() - tc
-                if cpu_s >= 10.0 or reps >= 100000:
-                    break
-            result["cpu_baseline"] = {
-                "value": round(cpu_tokens * reps / cpu_s, 1), "unit": "tokens/s", "cores": oracle.num_threads(),
-                "kind": "oracle",
-                "sample": "the whole workload (%d tokens: every position of every sequence) %d times, fp64 C oracle "
-                          "with OpenMP over (batch, head); %.2f s wall" % (cpu_tokens, reps, cpu_s)}
+        result["cpu_baseline"] = cpu_baseline(ws_list)
     print(json.dumps(result))
     return 0
 

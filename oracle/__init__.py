@@ -70,6 +70,8 @@ def _load():
                 f.restype = ctypes.c_int
             lib.oracle_num_threads.restype = ctypes.c_int
             lib.oracle_num_threads.argtypes = []
+            lib.oracle_set_num_threads.restype = None
+            lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
             _lib = lib
     return _lib
 
@@ -100,6 +102,11 @@ def _params(mu, sigma2, pi):
 def num_threads() -> int:
     """Threads the oracle's OpenMP loops use."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the oracle's OpenMP loops from now on (n >= 1)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def log_scores(X, mu, sigma2, pi) -> np.ndarray:

@@ -330,3 +330,12 @@ int oracle_num_threads(void) {
     return 1;
 #endif
 }
+
+/* Threads for the parallel loops above from now on (n >= 1; ignored without OpenMP). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
