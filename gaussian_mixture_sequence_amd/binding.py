@@ -52,7 +52,7 @@ class Shape(ctypes.Structure):
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("splits", "rows_per_split", "workgroups", "threads_per_workgroup",
-                                              "lds_bytes", "waits_on_all_splits", "resident_bound")]
+                                              "lds_bytes", "waits_on_all_splits", "resident_bound", "chunk_used")]
 
 
 class CrossShape(ctypes.Structure):

@@ -123,7 +123,9 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
         }
         return GMA_OK;
     }
-    if (op == GMA_OP_CAUSAL && chunk != 16 && chunk != 32 && chunk != 64) return GMA_ERR_UNSUPPORTED;
+    // causal chunk lengths 16, 32, 64 and 128; the bf16 scans form scores on 32-position subtiles
+    if (op == GMA_OP_CAUSAL && chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128) return GMA_ERR_UNSUPPORTED;
+    if (op == GMA_OP_CAUSAL && io == GMA_BF16 && chunk == 16) return GMA_ERR_UNSUPPORTED;
 
     Plan p{};
     p.op = op;
@@ -727,6 +729,7 @@ gma_status_t gma_plan_info(gma_op_t op, const gma_shape_t* shape, gma_dtype_t io
     info->splits = p.G;
     info->rows_per_split = int64_t(p.seg);
     info->workgroups = p.P * p.G;
+    if (op == GMA_OP_CAUSAL) info->chunk_used = io_dtype == GMA_BF16 ? gma::bf16_causal_chunk(p) : gma::f32_causal_chunk(p);
     if (op == GMA_OP_BIDIR && io_dtype == GMA_BF16) {
         int threads = 0;
         int64_t lds = 0;

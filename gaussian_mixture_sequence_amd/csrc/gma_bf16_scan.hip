@@ -915,10 +915,29 @@ hipError_t with_all(int dr, int kt, int vt, int ch, F&& f) {
 
 }  // namespace bf
 
-// The bf16 scan works on 32-position score subtiles, so a requested chunk of 16
-// positions runs as 32 (the chunk length only changes the order of the sums).  Shapes
-// whose registers fit the pipelined scan run the fused causal kernel; the others run the
-// segment aggregates (write kernel) and then the serial scan.
+// The chunk the bf16 scans run: the requested one (32, 64 or 128 positions; the scans form their
+// scores on 32-position subtiles, so 16 is refused when the call is validated), capped at 64,
+// the largest compiled, and halved where the chunk's tiles do not fit (scan_chunk,
+// serial_scan_chunk); the scan of 256 components takes 32.  The chunk length only changes the
+// order of the sums.
+int64_t bf16_causal_chunk(const Plan& p) {
+    if (bf16_causal_wide_applies(p)) return 32;
+    int64_t used = 0;
+    (void)bf::with_all(int(p.dr), int(p.Kp / 32), int(p.dv / 32), p.chunk >= 64 ? 64 : 32,
+                       [&](auto D, auto T, auto W, auto C) {
+                           constexpr int DR = decltype(D)::value, KT = decltype(T)::value,
+                                         VT = decltype(W)::value, CH = decltype(C)::value;
+                           if constexpr (KT <= 4 && DR * KT <= 256)
+                               used = bf::scan_chunk<DR, KT, VT, CH>();
+                           else
+                               used = bf::serial_scan_chunk<DR, KT, VT, CH>();
+                           return hipSuccess;
+                       });
+    return used;
+}
+
+// Shapes whose registers fit the pipelined scan run the fused causal kernel; 256 components with
+// d_r <= 64 the wide scan; the others the segment aggregates (write kernel) and then the serial scan.
 hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void* V, const float* mu, const float* s2,
                        const float* pi, float eps, void* O, char* ws, hipStream_t st, const float* state_in,
                        float* state_out) {
@@ -927,7 +946,7 @@ hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void
     const bf::Mixture mx{mu, s2, pi, int(p.K)};
     float* aggregates = reinterpret_cast<float*>(ws + p.off_partials);
     uint64_t* flags = reinterpret_cast<uint64_t*>(ws + p.off_flags);
-    const int ch = p.chunk < 32 ? 32 : p.chunk;
+    const int ch = p.chunk >= 64 ? 64 : 32;  // the compiled request; the kernels may halve it
     uint32_t* err = nullptr;
     hipError_t de = device_error_word(&err);
     if (de != hipSuccess) return de;

@@ -225,6 +225,13 @@ hipError_t copy_state(const Plan& p, const float* state_in, float* state_out, hi
     return hipGetLastError();
 }
 
+// The chunk length is a tiling choice: the requested one, halved until the chunk's tiles fit in LDS.
+int64_t f32_causal_chunk(const Plan& p) {
+    int C = p.chunk;
+    while (C > 8 && scan_lds_bytes(C, int(p.dr), int(p.dv), int(p.K)) > kMaxLds) C /= 2;
+    return C;
+}
+
 hipError_t f32_causal(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
                       const float* s2, const float* pi, float eps, float* O, char* ws, hipStream_t st,
                       const float* state_in, float* state_out) {
@@ -245,9 +252,7 @@ hipError_t f32_causal(const Plan& p, const float* XQ, const float* XK, const flo
     GMA_LAUNCH("f32_prefix", f32_prefix_kernel, dim3(unsigned((E + kThreads - 1) / kThreads), unsigned(p.P)),
                        dim3(kThreads), 0, st, partials, int(p.G), E, state_in, int(p.K), int(p.dv));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // The chunk length is a tiling choice; halve it until the chunk's tiles fit in LDS.
-    int C = p.chunk;
-    while (C > 8 && scan_lds_bytes(C, int(p.dr), int(p.dv), int(p.K)) > kMaxLds) C /= 2;
+    const int C = int(f32_causal_chunk(p));
     GMA_LAUNCH("f32_scan", f32_scan_kernel, dim3(unsigned(p.G), unsigned(p.P)), dim3(kThreads),
                        scan_lds_bytes(C, int(p.dr), int(p.dv), int(p.K)), st, XQ, XK, V, p.N, int(p.H),
                        int(p.dr), int(p.dv), int(p.K), p.seg, int(p.G), C, v.c, v.inv, mu, partials, eps, O,

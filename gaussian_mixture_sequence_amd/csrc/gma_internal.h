@@ -86,6 +86,8 @@ hipError_t f32_bidir(const Plan& p, const float* XQ, const float* XK, const floa
                      const float* mu, const float* s2, const float* pi, float eps, float* O,
                      char* ws, hipStream_t st);
 // state_in / state_out: [P][K][d_v+1] fp32 carried memory (gma_forward_causal_state), or NULL.
+// Positions per chunk the fp32 causal scan runs for the plan's requested chunk.
+int64_t f32_causal_chunk(const Plan& p);
 hipError_t f32_causal(const Plan& p, const float* XQ, const float* XK, const float* V,
                       const float* mu, const float* s2, const float* pi, float eps, float* O,
                       char* ws, hipStream_t st, const float* state_in, float* state_out);
@@ -145,6 +147,8 @@ int64_t bf16_bidir_per_cu(int64_t dr, int64_t kt, int64_t vt);
 hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void* V,
                       const float* mu, const float* s2, const float* pi, float eps, void* O,
                       char* ws, hipStream_t st);
+// Positions per chunk the bf16 causal scan runs for the plan's requested chunk.
+int64_t bf16_causal_chunk(const Plan& p);
 hipError_t bf16_causal(const Plan& p, const void* XQ, const void* XK, const void* V,
                        const float* mu, const float* s2, const float* pi, float eps, void* O,
                        char* ws, hipStream_t st, const float* state_in, float* state_out);

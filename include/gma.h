@@ -170,7 +170,11 @@ gma_status_t gma_forward_bidir_noalloc(const void* XQ, const void* XK, const voi
  * computed as a chunked scan: the sequence is cut into chunks of `chunk` positions;
  * inside a chunk the masked product (Gamma_Q Gamma_K^T restricted to j <= i) is formed
  * on chip and the K x (d_v+1) running memory carries the prefix across chunks.
- * `chunk` must be 16, 32 or 64 (GMA_ERR_UNSUPPORTED otherwise).  Output row i depends
+ * `chunk` must be 16, 32, 64 or 128 (GMA_ERR_UNSUPPORTED otherwise; with bf16 I/O 16 is
+ * unsupported too, as the bf16 scans form their scores on 32-position tiles).  It is the most
+ * positions a step takes on chip: each kernel runs the largest power of two not above it that
+ * its tiles allow in LDS and registers (64 at most on the bf16 path, 32 for 256 components);
+ * gma_plan_info reports the length used.  Only the order of the sums depends on it.  Output row i depends
  * only on inputs at positions <= i.  Arguments as for gma_forward_bidir.  With bf16 I/O
  * and K <= 128 (d_r * K <= 8192) the forward is one launch: each segment's workgroup
  * publishes its segment aggregate in the workspace and waits for those of the segments
@@ -423,10 +427,13 @@ gma_status_t gma_set_single_launch(int enable);
  *   resident_bound         }  and the workgroups that the kernel's LDS and declared waves
  *                              per SIMD let a 256-CU MI355X keep resident at once
  *                              (workgroups <= resident_bound whenever waits_on_all_splits)
+ *   chunk_used             causal only (0 otherwise): the positions per chunk the scan runs for
+ *                          the requested `chunk` (see gma_forward_causal)
  */
 typedef struct {
     int64_t splits, rows_per_split, workgroups;
     int64_t threads_per_workgroup, lds_bytes, waits_on_all_splits, resident_bound;
+    int64_t chunk_used;
 } gma_plan_info_t;
 
 gma_status_t gma_plan_info(gma_op_t op, const gma_shape_t* shape, gma_dtype_t io_dtype, int32_t chunk,

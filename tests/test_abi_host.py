@@ -65,7 +65,11 @@ def test_workspace_size_validation(lib):
     assert ws_size(Bd, 1, 1, 8, 16, 48, 8, BF)[0] == UNSUP      # bf16 d_v set
     assert ws_size(R, 1, 1, 8, 16, 0, 8, BF)[0] == OK            # d_v ignored
     assert ws_size(C, 1, 1, 8, 16, 32, 8, F, chunk=24)[0] == UNSUP
-    assert ws_size(C, 1, 1, 8, 16, 32, 8, F, chunk=128)[0] == UNSUP
+    for ch in (16, 32, 64, 128):  # the chunk set of the causal scan
+        assert ws_size(C, 1, 1, 8, 16, 32, 8, F, chunk=ch)[0] == OK, ch
+        assert ws_size(C, 1, 1, 8, 16, 32, 8, BF, chunk=ch)[0] == (UNSUP if ch == 16 else OK), ch
+    for ch in (0, 8, 24, 48, 96, 256):
+        assert ws_size(C, 1, 1, 8, 16, 32, 8, F, chunk=ch)[0] == UNSUP, ch
     assert ws_size(7, 1, 1, 8, 16, 32, 8, F)[0] == VALUE
     assert ws_size(Bd, 1, 1, 8, 16, 32, 8, 5)[0] == VALUE
     assert gb.load().gma_workspace_size(Bd, None, F, 64, ctypes.byref(ctypes.c_size_t())) == NULLP
@@ -365,3 +369,24 @@ def test_plan_info_validation(lib):
     assert c["threads_per_workgroup"] == 0 and c["workgroups"] == 96 * c["splits"]
     f = gb.gma_plan_info(gb.GMA_OP_BIDIR, 8, 8, 4096, 64, 64, 64, gb.GMA_F32)
     assert f["lds_bytes"] == 0 and f["waits_on_all_splits"] == 0
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_causal_chunk_used(lib, io):
+    """The scan runs the largest power of two not above the requested chunk that its tiles allow:
+    never more than requested, at least 32 with bf16 (its 32-position score tiles), at most 64 on
+    the bf16 path and 32 for 256 padded components with d_r <= 64."""
+    dt = gb.GMA_BF16 if io == "bf16" else gb.GMA_F32
+    for dr, dv, K in ((64, 64, 32), (16, 32, 8), (32, 64, 128), (64, 128, 256), (128, 128, 256), (64, 32, 50)):
+        used = {}
+        for ch in (16, 32, 64, 128):
+            if io == "bf16" and ch == 16:
+                continue
+            u = gb.gma_plan_info(gb.GMA_OP_CAUSAL, 2, 3, 1000, dr, dv, K, dt, ch)["chunk_used"]
+            assert u <= ch and u & (u - 1) == 0, (dr, dv, K, ch, u)
+            if io == "bf16":
+                assert 32 <= u <= 64 and (u == 32 if (K > 128 and dr <= 64) else True), (dr, dv, K, ch, u)
+            used[ch] = u
+        vals = [used[c] for c in sorted(used)]
+        assert vals == sorted(vals), used  # a longer request never runs a shorter chunk
+    assert gb.gma_plan_info(gb.GMA_OP_BIDIR, 1, 1, 100, 64, 64, 64, dt)["chunk_used"] == 0

@@ -171,7 +171,7 @@ BF16_CAUSAL_CASES = [
     bf16_case(causal=True, B=1, H=1, N=1, seed=54),                                     # single token
     bf16_case(causal=True, B=2, H=1, N=3001, d_r=32, d_v=64, K=128, chunk=64, seed=55),  # several segments
     bf16_case(causal=True, B=1, H=1, N=260, d_r=128, d_v=128, K=256, seed=56),          # maximum dims
-    bf16_case(causal=True, B=1, H=1, N=777, d_r=64, d_v=32, K=50, chunk=16, seed=57),   # ragged, chunk 16
+    bf16_case(causal=True, B=1, H=1, N=777, d_r=64, d_v=32, K=50, chunk=32, seed=57),   # ragged, chunk 32
     bf16_case(causal=True, B=1, H=2, N=900, d_r=32, d_v=64, K=100, seed=143),           # K padded 100 -> 128
     bf16_case(causal=True, B=1, H=1, N=700, d_r=32, d_v=64, K=150, seed=144),           # K padded 150 -> 256
     bf16_case(causal=True, B=2, H=1, N=500, d_r=16, d_v=128, K=200, seed=145),          # K padded 200 -> 256
@@ -222,6 +222,21 @@ def test_bf16_causal_chunk_invariance():
     a = to_np(run_gpu(w, inp, chunk=32))
     b = to_np(run_gpu(w, inp, chunk=64))
     assert row_scaled_error(a, b) <= 1e-2
+
+
+@pytest.mark.parametrize("w", [small("bidir_small_f32", causal=True, B=1, H=2, N=1000, seed=146),
+                               bf16_case(causal=True, B=1, H=2, N=1000, seed=147),
+                               bf16_case(causal=True, B=1, H=1, N=700, d_r=64, d_v=128, K=256, seed=148)],
+                         ids=lambda w: "%s-K%d" % (w.dtype, w.K))
+def test_causal_chunk_128(w):
+    """Chunk 128, the longest of the chunk set: parity with the oracle, and the same bits as the
+    request whose chunk length the scan actually runs (gma_plan_info's chunk_used)."""
+    io = gb.GMA_BF16 if w.dtype == "bf16" else gb.GMA_F32
+    used = gb.gma_plan_info(gb.GMA_OP_CAUSAL, w.B, w.H, w.N, w.d_r, w.d_v, w.K, io, 128)["chunk_used"]
+    inp = make_inputs(w)
+    a = to_np(run_gpu(w, inp, chunk=128))
+    assert row_scaled_error(a, run_oracle(w, inp)) <= TOL[w.dtype]
+    assert np.array_equal(a, to_np(run_gpu(w, inp, chunk=used)))
 
 
 def test_bf16_causal_last_row_matches_bidir():
