@@ -14,23 +14,24 @@
 //      Vc:  S = Gq Gk^T kept for key j <= query i,  num = S Vc + Gq Vt,  den = S 1 + Gq Z + eps,
 //      then Vt += Gk^T Vc, Z += Gk^T 1.
 //
-// Work split over the 8 waves: wave w holds the score operands of component tile w (the 5-term
-// split-operand scores of gma_bf16_common.h), so the softmax over the 256 components combines
-// the waves' statistics through LDS; wave w owns value columns 16 w .. 16 w + 15 of the fp32
-// memory, kept in registers as sixteen 16x16 MFMA accumulators (Vt^T's D layout,
-// init_memory), and computes those columns of the outputs; Z lives in LDS.
-//
-// Software pipeline, two barriers per chunk c (buffers b = c % 2 hold chunk c):
-//   region 1: S(c) tiles (3 waves), partial sums of Gq(c) Z, scores of chunk c+1 (x tiles of
-//             c+1 in LDS) and their per-wave softmax statistics                   -> B_Q
-//   region 2: Gq, Gk of chunk c+1 into the other buffers (statistics combined); inter part
-//             Vt^T Gq(c)^T over the memory before chunk c (split into hi + lo bf16), memory
-//             update with chunk c, intra part V(c)^T S(c)^T, outputs of chunk c divided and
-//             stored, Z advanced; V(c+1) and the x tiles of c+2 committed, loads of V(c+2)
-//             and x(c+3) issued                                                  -> B_P
-// (the scores live across B_Q only until they are stored, so the memory's products in region 2
-// have the registers the scores had)
-// The aggregate phase runs the same loop on the key side alone.
+// Two kinds of waves.  Waves w and w + 4 of a workgroup run on the same SIMD, so every SIMD holds
+// one of each and the matrix cores of one overlap the vector work of the other:
+//   score waves 0..3:  wave s holds the score operands of component tiles 2s, 2s + 1 (the 5-term
+//                      split-operand scores of gma_bf16_common.h) and turns the x tiles of the next
+//                      chunk into its responsibilities (softmax statistics combined over the four
+//                      waves through LDS);
+//   memory waves 4..7: wave 4 + m holds the fp32 memory of value-column tiles m (and m + 4 for
+//                      d_v = 128) as sixteen 16x16 MFMA accumulators each (Vt^T's D layout) and
+//                      computes the chunk's S tiles, outputs and memory update; Z lives in LDS.
+// Each kind runs its own loop; both pass the same barriers, two per chunk c (buffers b = c % 2
+// hold chunk c):
+//   part 1: score waves: scores of chunk c+1 (x tiles in LDS) and their statistics; memory waves:
+//           S(c) tiles, partial sums of Gq(c) Z, inter part Vt^T Gq(c)^T (memory before chunk c,
+//           split into hi + lo bf16)                                              -> B_Q
+//   part 2: score waves: Gq, Gk of chunk c+1 into the other buffers, x tiles of c+2 committed;
+//           memory waves: memory update with chunk c, intra part V(c)^T S(c)^T, outputs of chunk c
+//           divided and stored, Z advanced, V(c+1) committed                       -> B_P
+// The aggregate phase runs the same loops on the key side alone.
 #include <cstdint>
 #include <type_traits>
 
@@ -42,25 +43,57 @@ namespace bf {
 
 template <int DR, int VT>
 struct WideLds {
-    static constexpr int KT = 8, Kp = 256, DV = VT * 32, CH = 32, NW = 8, NT = NW * 64;
-    static constexpr int LDG = Kp + 8, LDV = DV + 8, LDSS = CH + 8, DPARTS = 16;
-    using XT = XTile<DR, CH, NT>;
+    static constexpr int KT = 8, Kp = 256, DV = VT * 32, CH = 32, NW = 8, NS = 4, NT = NW * 64, HT = NT / 2;
+    static constexpr int LDG = Kp + 8, LDV = DV + 8, LDSS = CH + 8, DPARTS = 8;
+    using XT = XTile<DR, CH, HT>;  // staged by the score waves' 256 threads
     using g_t = uint16_t[2][CH * LDG];
     using v_t = uint16_t[2][CH * LDV];
     using s_t = uint16_t[CH * LDSS];
     using x_t = u32x4[XT::LDS_BYTES / 16];
-    using st_t = float[2][NW][CH][2];   // (m, L) per job (0: keys, 1: queries), wave, position
-    using di_t = float[DPARTS][CH];     // partial sums of Gq Z over 16 components each
+    using st_t = float[2][NS][CH][2];   // (m, L) per job (0: keys, 1: queries), score wave, position
+    using di_t = float[DPARTS][CH];     // partial sums of Gq Z over 32 components each
     using dp_t = float[2][CH];          // S row sums of key block 0 and 1
     using z_t = float[Kp];
+    using c_t = float[Kp];              // score constants c_k (log2 units)
     using vote_t = int[NW];
     static constexpr size_t o_gq = 0, o_gk = lds_align(o_gq + sizeof(g_t)), o_vs = lds_align(o_gk + sizeof(g_t)),
                             o_ss = lds_align(o_vs + sizeof(v_t)), o_xq = lds_align(o_ss + sizeof(s_t)),
                             o_xk = lds_align(o_xq + sizeof(x_t)), o_st = lds_align(o_xk + sizeof(x_t)),
                             o_di = lds_align(o_st + sizeof(st_t)), o_dp = lds_align(o_di + sizeof(di_t)),
-                            o_zs = lds_align(o_dp + sizeof(dp_t)), o_vote = lds_align(o_zs + sizeof(z_t)),
-                            bytes = lds_align(o_vote + sizeof(vote_t));
+                            o_zs = lds_align(o_dp + sizeof(dp_t)), o_cs = lds_align(o_zs + sizeof(z_t)),
+                            o_vote = lds_align(o_cs + sizeof(c_t)), bytes = lds_align(o_vote + sizeof(vote_t));
 };
+
+// Scores of one 32-token subtile for component tiles ct0, ct0 + 1 from an XTile in LDS, the
+// accumulators starting at the score constants (in LDS, [Kp] fp32).
+template <int DR>
+__device__ __forceinline__ void wide_scores(const WaveParams<DR, 2>& P, const float* cst, int ct0, const u32x4* xt,
+                                            f32x16 (&acc)[2]) {
+    const int lh = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 cv = *reinterpret_cast<const float4*>(cst + (ct0 + ct) * 32 + 8 * q + 4 * lh);
+            acc[ct][4 * q + 0] = cv.x;
+            acc[ct][4 * q + 1] = cv.y;
+            acc[ct][4 * q + 2] = cv.z;
+            acc[ct][4 * q + 3] = cv.w;
+        }
+#pragma unroll
+    for (int ks = 0; ks < DR / 16; ++ks) {
+        bf16x8 x, x2h, x2l;
+        xtile_frags<DR>(xt, 0, ks, x, x2h, x2l);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+            acc[ct] = mfma(P.w[ct][ks][0], x, acc[ct]);
+            acc[ct] = mfma(P.w[ct][ks][1], x, acc[ct]);
+            acc[ct] = mfma(P.w[ct][ks][2], x2h, acc[ct]);
+            acc[ct] = mfma(P.w[ct][ks][3], x2h, acc[ct]);
+            acc[ct] = mfma(P.w[ct][ks][2], x2l, acc[ct]);
+        }
+    }
+}
 
 // mode 0: the whole forward (segments 0 .. G-2 aggregate and publish first, every segment
 // waits for the aggregates before it, then scans); mode 1: aggregates only (grid G-1 segments);
@@ -73,13 +106,14 @@ __global__ void __launch_bounds__(512)
                        uint16_t* __restrict__ O, const float* __restrict__ state_in, float* __restrict__ state_out,
                        uint32_t* __restrict__ err) {
     using LY = WideLds<DR, VT>;
-    constexpr int Kp = LY::Kp, DV = LY::DV, CH = LY::CH, NW = LY::NW, NT = LY::NT;
+    constexpr int Kp = LY::Kp, DV = LY::DV, CH = LY::CH, NS = LY::NS, HT = LY::HT;
     constexpr int LDG = LY::LDG, LDV = LY::LDV, LDSS = LY::LDSS;
-    constexpr int KT16 = Kp / 16;   // 16-row component tiles of the memory
-    constexpr int C16 = DV / 16;    // 16-wide value column tiles: wave w < C16 owns tile w
+    constexpr int KT16 = Kp / 16;          // 16-row component tiles of the memory
+    constexpr int C16 = DV / 16;           // 16-wide value-column tiles
+    constexpr int CPW = (C16 + 3) / 4;     // column tiles per memory wave: tiles m, m + 4
     constexpr int E = Kp * (DV + 1);
-    constexpr int VCHUNKS = CH * DV / 8, VCH = (VCHUNKS + NT - 1) / NT;
-    constexpr bool VEVEN = VCHUNKS % NT == 0;
+    constexpr int VCHUNKS = CH * DV / 8, VCH = (VCHUNKS + HT - 1) / HT;
+    constexpr bool VEVEN = VCHUNKS % HT == 0;
     using XT = typename LY::XT;
     __shared__ __attribute__((aligned(16))) char smem[LY::bytes];
     typename LY::g_t& Gq = *reinterpret_cast<typename LY::g_t*>(smem + LY::o_gq);
@@ -92,217 +126,285 @@ __global__ void __launch_bounds__(512)
     typename LY::di_t& den_ip = *reinterpret_cast<typename LY::di_t*>(smem + LY::o_di);
     typename LY::dp_t& den_part = *reinterpret_cast<typename LY::dp_t*>(smem + LY::o_dp);
     float* Zs = reinterpret_cast<float*>(smem + LY::o_zs);
+    float* cst = reinterpret_cast<float*>(smem + LY::o_cs);
     int* vote = reinterpret_cast<int*>(smem + LY::o_vote);
 
     const int wave = wave_id(), l = threadIdx.x & 63, lh = l >> 5, j = l & 31, g4 = l >> 4, i16 = l & 15;
+    const bool scorer = wave < NS;
+    const int ht = int(threadIdx.x) & (HT - 1);  // thread index within its half (score or memory waves)
     const int64_t p = blockIdx.y;
     const int s = blockIdx.x, h = int(p % H);
     const int64_t lo = int64_t(s) * seg, hi = min<int64_t>(lo + seg, N), rows = hi - lo;
+    const int64_t C = (rows + CH - 1) / CH;  // chunks of the segment
     float* agg = aggregates + size_t(p) * G * E;
     uint64_t* fl = flags + size_t(p) * G;
     const size_t SE = size_t(mx.K) * (DV + 1);  // one problem's carried memory
-    const bool owns_cols = wave < C16;
-
-    WaveParams<DR, 1> P;  // component tile `wave`
-    P.compute(mx, h, wave);
+    const bool aggregate = mode == 1 || (mode == 0 && s + 1 < G);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(XQ + (size_t(p) * N + lo) * DR, rows * DR * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(XK + (size_t(p) * N + lo) * DR, rows * DR * 2);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t(p) * N + lo) * DV, rows * DV * 2);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + (size_t(p) * N + lo) * DV, rows * DV * 2);
-    // S tile (query block 0, key block 1) lies above the diagonal: zero for good
-    for (int c = threadIdx.x; c < CH * LDSS / 8; c += NT) reinterpret_cast<u32x4*>(Ss)[c] = u32x4{0u, 0u, 0u, 0u};
+    bool ok = true;
 
-    f32x4 mem[KT16];
-    u32x4 vr[VCH];
-    auto load_v = [&](int64_t row0) {
+    if (scorer) {
+        // ================================================================ score waves
+        const int ct0 = 2 * wave;
+        WaveParams<DR, 2> P;
+        P.compute(mx, h, ct0);
+        if (j == 0)  // the constants of tiles ct0, ct0 + 1 into LDS (lanes 0 and 32 hold both halves)
 #pragma unroll
-        for (int u = 0; u < VCH; ++u) {
-            const int c = threadIdx.x + u * NT;
-            vr[u] = (VEVEN || c < VCHUNKS) ? buf_load16(rv, uint32_t((row0 * DV + int64_t(c) * 8) * 2))
-                                           : u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    auto commit_v = [&](uint16_t* dst) {
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int u = 0; u < VCH; ++u) {
-            const int c = threadIdx.x + u * NT;
-            if (VEVEN || c < VCHUNKS) {
-                const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
-                *reinterpret_cast<u32x4*>(dst + row * LDV + col) = vr[u];
-            }
-        }
-    };
-    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) cst[(ct0 + ct) * 32 + 8 * q + 4 * lh + i] = P.c[ct][4 * q + i];
+        // S tile (query block 0, key block 1) lies above the diagonal: zero for good
+        for (int c = ht; c < CH * LDSS / 8; c += HT) reinterpret_cast<u32x4*>(Ss)[c] = u32x4{0u, 0u, 0u, 0u};
+        __syncthreads();  // B_init: constants and the zero tile visible
 
-    // The chunk loop over the segment.  AGG: the key side alone (aggregate); otherwise the scan.
-    // pre() runs once the first loads are in flight, before anything reads the memory.
-    auto run = [&](auto agg_tag, auto&& pre) __attribute__((always_inline)) {
-        constexpr bool AGG = decltype(agg_tag)::value;
-        constexpr int JOBS = AGG ? 1 : 2;  // score jobs: 0 keys, 1 queries
-        const int64_t C = (rows + CH - 1) / CH;
-        XT xq, xk;
-        f32x16 acc[2][1];
-        float zdummy[1][16];
-        float sm_m[2], sm_L[2];
-        auto scores_next = [&]() __attribute__((always_inline)) {  // from the x tiles in LDS
-            scores_lds<DR, 1>(P, XtK, 0, acc[0]);
-            if (!AGG) scores_lds<DR, 1>(P, XtQ, 0, acc[1]);
-        };
-        auto softmax_local = [&]() __attribute__((always_inline)) {
+        auto run = [&](auto agg_tag) __attribute__((always_inline)) {
+            constexpr bool AGG = decltype(agg_tag)::value;
+            constexpr int JOBS = AGG ? 1 : 2;  // 0 keys, 1 queries
+            XT xq, xk;
+            f32x16 acc[2][2];
+            float sm_m[2], sm_L[2];
+            auto scores_next = [&]() __attribute__((always_inline)) {
+                wide_scores<DR>(P, cst, ct0, XtK, acc[0]);
+                if (!AGG) wide_scores<DR>(P, cst, ct0, XtQ, acc[1]);
 #pragma unroll
-            for (int jb = 0; jb < JOBS; ++jb) {
-                float D;
-                local_softmax<1, false>(acc[jb], zdummy, sm_m[jb], sm_L[jb], D);
-                if (lh == 0) {
-                    st[jb][wave][j][0] = sm_m[jb];
-                    st[jb][wave][j][1] = sm_L[jb];
-                }
-            }
-        };
-        // responsibilities of the chunk starting at row0 into buffer b (after the statistics)
-        auto store_gamma = [&](int64_t row0, int b) __attribute__((always_inline)) {
-            const bool valid = row0 + j < rows;
-#pragma unroll
-            for (int jb = 0; jb < JOBS; ++jb) {
-                float mm = -INFINITY;
-#pragma unroll
-                for (int w = 0; w < NW; ++w) mm = fmaxf(mm, st[jb][w][j][0]);
-                float Lt = 0.0f;
-#pragma unroll
-                for (int w = 0; w < NW; ++w) Lt = fmaf(st[jb][w][j][1], __builtin_amdgcn_exp2f(st[jb][w][j][0] - mm), Lt);
-                float scale = __builtin_amdgcn_exp2f(sm_m[jb] - mm) * __builtin_amdgcn_rcpf(Lt);
-                if (!valid) scale = 0.0f;  // positions past the segment: no responsibility
-                store_gamma_lds<1>(acc[jb], scale, jb == 0 ? Gk[b] : Gq[b], LDG, j, wave);
-            }
-        };
-
-        // ---- prologue: V(0) and x(0) loaded, pre(), V(0) and x(0) into LDS, responsibilities
-        // of chunk 0 into buffer 0, x(1) into LDS; V(1) and x(2) in flight
-        load_v(0);
-        if (!AGG) xq.load(rq, 0);
-        xk.load(rk, 0);
-        pre();
-        commit_v(Vs[0]);
-        load_v(CH);
-        if (!AGG) xq.commit(XtQ);
-        xk.commit(XtK);
-        if (!AGG) xq.load(rq, CH);
-        xk.load(rk, CH);
-        __syncthreads();
-        scores_next();
-        softmax_local();
-        __syncthreads();  // statistics published; x(0) consumed
-        store_gamma(0, 0);
-        if (!AGG) xq.commit(XtQ);
-        xk.commit(XtK);
-        if (!AGG) xq.load(rq, 2 * CH);
-        xk.load(rk, 2 * CH);
-        __syncthreads();
-
-        auto chunk = [&](const int64_t c, const int b) __attribute__((always_inline)) {
-            const int64_t nc = c * CH;
-            // ================= region 1
-            __builtin_amdgcn_s_setprio(1);
-            f32x4 o[2];
-            if constexpr (!AGG) {
-                // S^T tiles (rows keys, columns queries) of blocks (q, k) = (0,0), (1,0), (1,1)
-                if (wave >= NW - 3) {
-                    const int t = wave - (NW - 3), qb = t > 0 ? 1 : 0, kb = t > 1 ? 1 : 0;
-                    f32x4 sacc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                    for (int ks = 0; ks < Kp / 32; ++ks)
-                        sacc = mfma16(*reinterpret_cast<const bf16x8*>(Gk[b] + (kb * 16 + i16) * LDG + 32 * ks + 8 * g4),
-                                      *reinterpret_cast<const bf16x8*>(Gq[b] + (qb * 16 + i16) * LDG + 32 * ks + 8 * g4),
-                                      sacc);
-                    float rs = 0.0f;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if (kb * 16 + 4 * g4 + r > qb * 16 + i16) sacc[r] = 0.0f;  // key after query
-                        rs += sacc[r];
+                for (int jb = 0; jb < JOBS; ++jb) {
+                    float D, zdummy[2][16];
+                    local_softmax<2, false>(acc[jb], zdummy, sm_m[jb], sm_L[jb], D);
+                    if (lh == 0) {
+                        st[jb][wave][j][0] = sm_m[jb];
+                        st[jb][wave][j][1] = sm_L[jb];
                     }
-                    rs += __shfl_xor(rs, 16, kWave);
-                    rs += __shfl_xor(rs, 32, kWave);
-                    if (g4 == 0) den_part[kb][qb * 16 + i16] = rs;
-                    *reinterpret_cast<u32x2*>(Ss + (qb * 16 + i16) * LDSS + kb * 16 + 4 * g4) =
-                        u32x2{pack_bf16x2(sacc[0], sacc[1]), pack_bf16x2(sacc[2], sacc[3])};
                 }
-                {  // partial sums of Gq(c) Z over components 16 part .. + 15
-                    const int row = threadIdx.x & 31, part = threadIdx.x >> 5;
-                    const u32x4* gr = reinterpret_cast<const u32x4*>(Gq[b] + row * LDG + 16 * part);
-                    float d = 0.0f;
+            };
+            auto store_gamma = [&](int64_t row0, int b) __attribute__((always_inline)) {
+                const bool valid = row0 + j < rows;
 #pragma unroll
-                    for (int h2 = 0; h2 < 2; ++h2) {
-                        const u32x4 gv = gr[h2];
-                        const float4 z0 = *reinterpret_cast<const float4*>(Zs + 16 * part + 8 * h2);
-                        const float4 z1 = *reinterpret_cast<const float4*>(Zs + 16 * part + 8 * h2 + 4);
-                        d = fmaf(__uint_as_float(gv[0] << 16), z0.x, d);
-                        d = fmaf(__uint_as_float(gv[0] & 0xffff0000u), z0.y, d);
-                        d = fmaf(__uint_as_float(gv[1] << 16), z0.z, d);
-                        d = fmaf(__uint_as_float(gv[1] & 0xffff0000u), z0.w, d);
-                        d = fmaf(__uint_as_float(gv[2] << 16), z1.x, d);
-                        d = fmaf(__uint_as_float(gv[2] & 0xffff0000u), z1.y, d);
-                        d = fmaf(__uint_as_float(gv[3] << 16), z1.z, d);
-                        d = fmaf(__uint_as_float(gv[3] & 0xffff0000u), z1.w, d);
-                    }
-                    den_ip[part][row] = d;
+                for (int jb = 0; jb < JOBS; ++jb) {
+                    float mm = -INFINITY;
+#pragma unroll
+                    for (int w = 0; w < NS; ++w) mm = fmaxf(mm, st[jb][w][j][0]);
+                    float Lt = 0.0f;
+#pragma unroll
+                    for (int w = 0; w < NS; ++w)
+                        Lt = fmaf(st[jb][w][j][1], __builtin_amdgcn_exp2f(st[jb][w][j][0] - mm), Lt);
+                    float scale = __builtin_amdgcn_exp2f(sm_m[jb] - mm) * __builtin_amdgcn_rcpf(Lt);
+                    if (!valid) scale = 0.0f;  // positions past the segment: no responsibility
+                    store_gamma_lds<2>(acc[jb], scale, jb == 0 ? Gk[b] : Gq[b], LDG, j, ct0);
+                }
+            };
+            // prologue (barriers P0, P1, P2)
+            if (!AGG) xq.load(rq, 0);
+            xk.load(rk, 0);
+            if (!AGG) xq.commit(XtQ);
+            xk.commit(XtK);
+            if (!AGG) xq.load(rq, CH);
+            xk.load(rk, CH);
+            __syncthreads();  // P0: x(0) in LDS
+            scores_next();
+            __syncthreads();  // P1: statistics of chunk 0; x(0) consumed
+            store_gamma(0, 0);
+            if (!AGG) xq.commit(XtQ);
+            xk.commit(XtK);
+            if (!AGG) xq.load(rq, 2 * CH);
+            xk.load(rk, 2 * CH);
+            __syncthreads();  // P2: Gamma(0) and x(1) in LDS
+            for (int64_t c = 0; c < C; ++c) {
+                const int b = int(c & 1);
+                __builtin_amdgcn_s_setprio(1);
+                scores_next();  // chunk c+1
+                __builtin_amdgcn_s_setprio(0);
+                __syncthreads();  // B_Q
+                store_gamma((c + 1) * CH, b ^ 1);
+                if (!AGG) xq.commit(XtQ);  // x(c+2)
+                xk.commit(XtK);
+                if (!AGG) xq.load(rq, (c + 3) * CH);
+                xk.load(rk, (c + 3) * CH);
+                __syncthreads();  // B_P
+            }
+        };
+        if (aggregate) {
+            run(std::true_type());
+            publish_token(fl + s, token);  // after the memory waves' stores of the aggregate
+            if (mode == 1) return;
+        }
+        run(std::false_type());
+    } else {
+        // ================================================================ memory waves
+        const int m = wave - NS;
+        const bool has_cols = m < C16;
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + (size_t(p) * N + lo) * DV, rows * DV * 2);
+        const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + (size_t(p) * N + lo) * DV, rows * DV * 2);
+        const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+        f32x4 mem[CPW][KT16];
+        u32x4 vr[VCH];
+        auto load_v = [&](int64_t row0) {
+#pragma unroll
+            for (int u = 0; u < VCH; ++u) {
+                const int c = ht + u * HT;
+                vr[u] = (VEVEN || c < VCHUNKS) ? buf_load16(rv, uint32_t((row0 * DV + int64_t(c) * 8) * 2))
+                                               : u32x4{0u, 0u, 0u, 0u};
+            }
+        };
+        auto commit_v = [&](uint16_t* dst) {
+#pragma unroll
+            for (int u = 0; u < VCH; ++u) {
+                const int c = ht + u * HT;
+                if (VEVEN || c < VCHUNKS) {
+                    const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
+                    *reinterpret_cast<u32x4*>(dst + row * LDV + col) = vr[u];
                 }
             }
-            scores_next();  // chunk c+1 (x tiles in LDS)
-            softmax_local();
-            __builtin_amdgcn_s_setprio(0);
-            __syncthreads();  // B_Q
-            // ================= region 2
-            store_gamma(nc + CH, b ^ 1);
-            if constexpr (!AGG) {
-                // inter part: O^T = Vt^T Gq^T over the memory before this chunk (hi + lo bf16)
-                if (owns_cols) {
-                    o[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                    o[1] = o[0];
+        };
+        auto owns = [&](int cc) { return has_cols && m + 4 * cc < C16; };
+        // in the chunk loop: with d_v a multiple of 64 a wave that owns its first column tile
+        // owns all CPW of them (known at compile time; the loops then carry no branches)
+        constexpr bool ALL = C16 % 4 == 0;
+        auto owns_next = [&](int cc) { return ALL || owns(cc); };
+        __syncthreads();  // B_init
+
+        // pre(): after the first V load is in flight, before the memory is read
+        auto run = [&](auto agg_tag, auto&& pre) __attribute__((always_inline)) {
+            constexpr bool AGG = decltype(agg_tag)::value;
+            // prologue (barriers P0, P1, P2)
+            load_v(0);
+            pre();
+            commit_v(Vs[0]);
+            load_v(CH);
+            __syncthreads();  // P0
+            __syncthreads();  // P1
+            __syncthreads();  // P2
+            for (int64_t c = 0; c < C; ++c) {
+                const int b = int(c & 1);
+                const int64_t nc = c * CH;
+                f32x4 o[CPW][2];
+                // ---- part 1
+                if constexpr (!AGG) {
+                    __builtin_amdgcn_s_setprio(1);
+                    // S^T tiles (rows keys, columns queries) of blocks (q, k) = (0,0), (1,0), (1,1)
+                    if (m < 3) {
+                        const int qb = m > 0 ? 1 : 0, kb = m > 1 ? 1 : 0;
+                        f32x4 sacc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                    for (int m2 = 0; m2 < Kp / 32; ++m2) {
-                        u32x4 ah, al;
+                        for (int ks = 0; ks < Kp / 32; ++ks)
+                            sacc = mfma16(
+                                *reinterpret_cast<const bf16x8*>(Gk[b] + (kb * 16 + i16) * LDG + 32 * ks + 8 * g4),
+                                *reinterpret_cast<const bf16x8*>(Gq[b] + (qb * 16 + i16) * LDG + 32 * ks + 8 * g4), sacc);
+                        float rs = 0.0f;
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int v0 = 2 * q, v1 = 2 * q + 1;
-                            const float x0 = mem[2 * m2 + (v0 >> 2)][v0 & 3];
-                            const float x1 = mem[2 * m2 + (v1 >> 2)][v1 & 3];
-                            const uint32_t hb = pack_bf16x2(x0, x1);
-                            ah[q] = hb;
-                            al[q] = pack_bf16x2(x0 - __uint_as_float(hb << 16), x1 - __uint_as_float(hb & 0xffff0000u));
+                        for (int r = 0; r < 4; ++r) {
+                            if (kb * 16 + 4 * g4 + r > qb * 16 + i16) sacc[r] = 0.0f;  // key after query
+                            rs += sacc[r];
                         }
+                        rs += __shfl_xor(rs, 16, kWave);
+                        rs += __shfl_xor(rs, 32, kWave);
+                        if (g4 == 0) den_part[kb][qb * 16 + i16] = rs;
+                        *reinterpret_cast<u32x2*>(Ss + (qb * 16 + i16) * LDSS + kb * 16 + 4 * g4) =
+                            u32x2{pack_bf16x2(sacc[0], sacc[1]), pack_bf16x2(sacc[2], sacc[3])};
+                    }
+                    {  // partial sums of Gq(c) Z over components 32 part .. + 31
+                        const int row = ht & 31, part = ht >> 5;
+                        const u32x4* gr = reinterpret_cast<const u32x4*>(Gq[b] + row * LDG + 32 * part);
+                        float d = 0.0f;
+#pragma unroll
+                        for (int h4 = 0; h4 < 4; ++h4) {
+                            const u32x4 gv = gr[h4];
+                            const float4 z0 = *reinterpret_cast<const float4*>(Zs + 32 * part + 8 * h4);
+                            const float4 z1 = *reinterpret_cast<const float4*>(Zs + 32 * part + 8 * h4 + 4);
+                            d = fmaf(__uint_as_float(gv[0] << 16), z0.x, d);
+                            d = fmaf(__uint_as_float(gv[0] & 0xffff0000u), z0.y, d);
+                            d = fmaf(__uint_as_float(gv[1] << 16), z0.z, d);
+                            d = fmaf(__uint_as_float(gv[1] & 0xffff0000u), z0.w, d);
+                            d = fmaf(__uint_as_float(gv[2] << 16), z1.x, d);
+                            d = fmaf(__uint_as_float(gv[2] & 0xffff0000u), z1.y, d);
+                            d = fmaf(__uint_as_float(gv[3] << 16), z1.z, d);
+                            d = fmaf(__uint_as_float(gv[3] & 0xffff0000u), z1.w, d);
+                        }
+                        den_ip[part][row] = d;
+                    }
+                    // inter part: O^T = Vt^T Gq^T over the memory before this chunk (hi + lo bf16);
+                    // each 32-component step reads its two Gq fragments once for both column
+                    // tiles and issues the four hi products before the four lo ones
+#pragma unroll
+                    for (int cc = 0; cc < CPW; ++cc) o[cc][0] = o[cc][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    auto gq_frags = [&](int m2, bf16x8(&bq)[2]) {
 #pragma unroll
                         for (int t16 = 0; t16 < 2; ++t16) {
                             const uint16_t* gq = Gq[b] + (t16 * 16 + i16) * LDG + 32 * m2 + 4 * g4;
                             const u32x2 b0 = *reinterpret_cast<const u32x2*>(gq);
                             const u32x2 b1 = *reinterpret_cast<const u32x2*>(gq + 16);
-                            const bf16x8 bb = __builtin_bit_cast(bf16x8, u32x4{b0[0], b0[1], b1[0], b1[1]});
-                            o[t16] = mfma16(__builtin_bit_cast(bf16x8, ah), bb, o[t16]);
-                            o[t16] = mfma16(__builtin_bit_cast(bf16x8, al), bb, o[t16]);
+                            bq[t16] = __builtin_bit_cast(bf16x8, u32x4{b0[0], b0[1], b1[0], b1[1]});
+                        }
+                    };
+                    if (owns(0)) {
+#pragma unroll
+                        for (int m2 = 0; m2 < Kp / 32; ++m2) {
+                            // the split below covers the latency of these reads
+                            bf16x8 bq[2];
+                            gq_frags(m2, bq);
+#pragma unroll
+                            for (int cc = 0; cc < CPW; ++cc) {
+                                if (!owns_next(cc)) continue;
+                                u32x4 ah, al;
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) {
+                                    const int v0 = 2 * q, v1 = 2 * q + 1;
+                                    const float x0 = mem[cc][2 * m2 + (v0 >> 2)][v0 & 3];
+                                    const float x1 = mem[cc][2 * m2 + (v1 >> 2)][v1 & 3];
+                                    const uint32_t hb = pack_bf16x2(x0, x1);
+                                    ah[q] = hb;
+                                    al[q] = pack_bf16x2(x0 - __uint_as_float(hb << 16),
+                                                        x1 - __uint_as_float(hb & 0xffff0000u));
+                                }
+#pragma unroll
+                                for (int t16 = 0; t16 < 2; ++t16)
+                                    o[cc][t16] = mfma16(__builtin_bit_cast(bf16x8, ah), bq[t16], o[cc][t16]);
+#pragma unroll
+                                for (int t16 = 0; t16 < 2; ++t16)
+                                    o[cc][t16] = mfma16(__builtin_bit_cast(bf16x8, al), bq[t16], o[cc][t16]);
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
                         }
                     }
+                    __builtin_amdgcn_s_setprio(0);
                 }
-            }
-            // memory update with chunk c: Vt += Gk^T Vc (own columns), Z += Gk^T 1 (tiles wave, wave + 8)
-            f32x4 zt[2];
-            {
-                if (owns_cols) {
-                    const bf16x8 bv = read_colfrag16(Vs[b], LDV, 0, 16 * wave);
+                __syncthreads();  // B_Q
+                // ---- part 2: memory update with chunk c (own columns), Z += Gk^T 1 (tiles 4 m .. 4 m + 3)
+                bf16x8 bv[CPW];  // V(c) column fragments: memory update and intra part
 #pragma unroll
-                    for (int kt = 0; kt < KT16; ++kt) mem[kt] = mfma16(read_colfrag16(Gk[b], LDG, 0, 16 * kt), bv, mem[kt]);
-                }
+                for (int cc = 0; cc < CPW; ++cc)
+                    bv[cc] = owns_next(cc) ? read_colfrag16(Vs[b], LDV, 0, 16 * (m + 4 * cc)) : bf16x8{};
+                if (owns(0)) {
+                    // two steps of look-ahead on the Gk fragment reads
+                    bf16x8 a0 = read_colfrag16(Gk[b], LDG, 0, 0), a1 = read_colfrag16(Gk[b], LDG, 0, 16);
 #pragma unroll
-                for (int zi = 0; zi < 2; ++zi)
-                    zt[zi] = mfma16(read_colfrag16(Gk[b], LDG, 0, 16 * (wave + NW * zi)), ones,
-                                    f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-            }
-            if constexpr (!AGG) {
-                if (owns_cols) {
-                    const bf16x8 av = read_colfrag16(Vs[b], LDV, 0, 16 * wave);
+                    for (int kt = 0; kt < KT16; ++kt) {
+                        const bf16x8 a = a0;
+                        a0 = a1;
+                        if (kt + 2 < KT16) a1 = read_colfrag16(Gk[b], LDG, 0, 16 * (kt + 2));
 #pragma unroll
-                    for (int t16 = 0; t16 < 2; ++t16) {
-                        const bf16x8 bb = *reinterpret_cast<const bf16x8*>(Ss + (t16 * 16 + i16) * LDSS + 8 * g4);
-                        o[t16] = mfma16(av, bb, o[t16]);
+                        for (int cc = 0; cc < CPW; ++cc)
+                            if (owns_next(cc)) mem[cc][kt] = mfma16(a, bv[cc], mem[cc][kt]);
+                        __builtin_amdgcn_sched_barrier(0);
                     }
+                }
+                {  // Zs is read again only after B_P
+                    bf16x8 az[4];
+                    f32x4 zt[4];
+#pragma unroll
+                    for (int zi = 0; zi < 4; ++zi) az[zi] = read_colfrag16(Gk[b], LDG, 0, 16 * (4 * m + zi));
+#pragma unroll
+                    for (int zi = 0; zi < 4; ++zi) zt[zi] = mfma16(az[zi], ones, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+                    if (i16 == 0)
+#pragma unroll
+                        for (int zi = 0; zi < 4; ++zi)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) Zs[16 * (4 * m + zi) + 4 * g4 + r] += zt[zi][r];
+                }
+                if constexpr (!AGG) {
+                    float rden[2];
 #pragma unroll
                     for (int t16 = 0; t16 < 2; ++t16) {
                         const int q = t16 * 16 + i16;
@@ -310,122 +412,139 @@ __global__ void __launch_bounds__(512)
                         if (t16 == 1) den += den_part[1][q];
 #pragma unroll
                         for (int pt = 0; pt < LY::DPARTS; ++pt) den += den_ip[pt][q];
-                        const float rden = __builtin_amdgcn_rcpf(den);
-                        // positions past the segment fall outside the resource and are dropped
-                        buf_store8(ro, uint32_t(((nc + q) * DV + 16 * wave + 4 * g4) * 2),
-                                   u32x2{pack_bf16x2(o[t16][0] * rden, o[t16][1] * rden),
-                                         pack_bf16x2(o[t16][2] * rden, o[t16][3] * rden)});
+                        rden[t16] = __builtin_amdgcn_rcpf(den);
+                    }
+#pragma unroll
+                    for (int cc = 0; cc < CPW; ++cc) {
+                        if (!owns_next(cc)) continue;
+                        const int c16 = m + 4 * cc;
+#pragma unroll
+                        for (int t16 = 0; t16 < 2; ++t16) {
+                            const bf16x8 bb = *reinterpret_cast<const bf16x8*>(Ss + (t16 * 16 + i16) * LDSS + 8 * g4);
+                            o[cc][t16] = mfma16(bv[cc], bb, o[cc][t16]);
+                        }
+#pragma unroll
+                        for (int t16 = 0; t16 < 2; ++t16) {
+                            const int q = t16 * 16 + i16;
+                            const float rd = rden[t16];
+                            // positions past the segment fall outside the resource and are dropped
+                            buf_store8(ro, uint32_t(((nc + q) * DV + 16 * c16 + 4 * g4) * 2),
+                                       u32x2{pack_bf16x2(o[cc][t16][0] * rd, o[cc][t16][1] * rd),
+                                             pack_bf16x2(o[cc][t16][2] * rd, o[cc][t16][3] * rd)});
+                        }
                     }
                 }
+                commit_v(Vs[b ^ 1]);  // V(c+1)
+                load_v(nc + 2 * CH);
+                __syncthreads();  // B_P
             }
-            if (i16 == 0)
-#pragma unroll
-                for (int zi = 0; zi < 2; ++zi)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) Zs[16 * (wave + NW * zi) + 4 * g4 + r] += zt[zi][r];
-            commit_v(Vs[b ^ 1]);  // V(c+1)
-            load_v(nc + 2 * CH);
-            if (!AGG) xq.commit(XtQ);  // x(c+2)
-            xk.commit(XtK);
-            if (!AGG) xq.load(rq, nc + 3 * CH);
-            xk.load(rk, nc + 3 * CH);
-            __syncthreads();  // B_P
         };
-        for (int64_t c = 0; c < C; ++c) chunk(c, int(c & 1));
-    };
 
-    // ---- 1. the segment's aggregate (not needed for the last segment)
-    const bool aggregate = mode == 1 || (mode == 0 && s + 1 < G);
-    if (aggregate) {
+        if (aggregate) {
 #pragma unroll
-        for (int kt = 0; kt < KT16; ++kt) mem[kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int k = threadIdx.x; k < Kp; k += NT) Zs[k] = 0.0f;
-        run(std::true_type(), [] {});
-        // VtT [DV][Kp] then Z [Kp], device-coherent for the consumers in this launch
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(agg + size_t(s) * E, int64_t(E) * 4);
-        if (owns_cols)
+            for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
-            for (int kt = 0; kt < KT16; ++kt)
-                buf_store16_dev(ra, uint32_t(((16 * wave + i16) * Kp + 16 * kt + 4 * g4) * 4),
-                                u32x4{__float_as_uint(mem[kt][0]), __float_as_uint(mem[kt][1]),
-                                      __float_as_uint(mem[kt][2]), __float_as_uint(mem[kt][3])});
-        if (threadIdx.x < Kp / 4) {
-            const float4 z = *reinterpret_cast<const float4*>(Zs + 4 * threadIdx.x);
-            buf_store16_dev(ra, uint32_t((Kp * DV + 4 * threadIdx.x) * 4),
-                            u32x4{__float_as_uint(z.x), __float_as_uint(z.y), __float_as_uint(z.z), __float_as_uint(z.w)});
-        }
-        publish_token(fl + s, token);  // its barrier also ends every use of the aggregate's LDS
-        if (mode == 1) return;
-    }
-
-    // ---- 2. + 3. the starting memory, then the scan
-    bool ok = true;
-    {  // the carried memory [K][DV + 1] (row k: Vt_k then Z_k) or zeros; rows k >= K lie past the
-       // resource's end and read as zero
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(state_in ? state_in + p * SE : nullptr,
-                                                    state_in ? int64_t(SE) * 4 : 0);
+                for (int kt = 0; kt < KT16; ++kt) mem[cc][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int k = ht; k < Kp; k += HT) Zs[k] = 0.0f;
+            run(std::true_type(), [] {});
+            // VtT [DV][Kp] then Z [Kp], device-coherent for the consumers in this launch
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(agg + size_t(s) * E, int64_t(E) * 4);
 #pragma unroll
-        for (int kt = 0; kt < KT16; ++kt) mem[kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-        if (state_in && owns_cols)
+            for (int cc = 0; cc < CPW; ++cc)
+                if (owns(cc))
 #pragma unroll
-            for (int kt = 0; kt < KT16; ++kt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    mem[kt][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                        rs, uint32_t(((16 * kt + 4 * g4 + r) * (DV + 1) + 16 * wave + i16) * 4), 0, 0));
-        if (threadIdx.x < Kp / 4)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                Zs[4 * threadIdx.x + r] =
-                    state_in ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                                   rs, uint32_t(((4 * threadIdx.x + r) * (DV + 1) + DV) * 4), 0, 0))
-                             : 0.0f;
-    }
-    run(std::false_type(), [&] {
-        if (mode == 0) ok = wait_tokens(fl, s, token, wait_limit);
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc(agg, int64_t(s) * int64_t(E) * 4);
-        for (int gs = 0; gs < s; ++gs) {  // increasing segment order
-            const uint32_t a = uint32_t(size_t(gs) * E * 4);
-            if (owns_cols)
-#pragma unroll
-                for (int kt = 0; kt < KT16; ++kt) {
-                    const u32x4 v = buf_load16_dev(ra, a + uint32_t(((16 * wave + i16) * Kp + 16 * kt + 4 * g4) * 4));
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) mem[kt][r] += __uint_as_float(v[r]);
-                }
-            if (threadIdx.x < Kp / 4) {
-                const u32x4 v = buf_load16_dev(ra, a + uint32_t((Kp * DV + 4 * threadIdx.x) * 4));
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Zs[4 * threadIdx.x + r] += __uint_as_float(v[r]);
+                    for (int kt = 0; kt < KT16; ++kt)
+                        buf_store16_dev(ra, uint32_t(((16 * (m + 4 * cc) + i16) * Kp + 16 * kt + 4 * g4) * 4),
+                                        u32x4{__float_as_uint(mem[cc][kt][0]), __float_as_uint(mem[cc][kt][1]),
+                                              __float_as_uint(mem[cc][kt][2]), __float_as_uint(mem[cc][kt][3])});
+            if (ht < Kp / 4) {
+                const float4 z = *reinterpret_cast<const float4*>(Zs + 4 * ht);
+                buf_store16_dev(ra, uint32_t((Kp * DV + 4 * ht) * 4),
+                                u32x4{__float_as_uint(z.x), __float_as_uint(z.y), __float_as_uint(z.z), __float_as_uint(z.w)});
             }
+            publish_token(fl + s, token);  // its barrier pairs with the score waves' publish
+            if (mode == 1) return;
         }
-    });
-    float* so = (state_out && s == G - 1) ? state_out + p * SE : nullptr;
-    if (so) {  // the memory after the last position, same layout; rows k >= K are dropped
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(so, int64_t(SE) * 4);
-        if (owns_cols)
+
+        // the starting memory: the carried memory [K][DV + 1] (row k: Vt_k then Z_k) or zeros
+        // (rows k >= K lie past the resource's end and read as zero), then the earlier aggregates
+        {
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(state_in ? state_in + p * SE : nullptr,
+                                                        state_in ? int64_t(SE) * 4 : 0);
 #pragma unroll
-            for (int kt = 0; kt < KT16; ++kt)
+            for (int cc = 0; cc < CPW; ++cc)
+#pragma unroll
+                for (int kt = 0; kt < KT16; ++kt) mem[cc][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (state_in)
+#pragma unroll
+                for (int cc = 0; cc < CPW; ++cc)
+                    if (owns(cc))
+#pragma unroll
+                        for (int kt = 0; kt < KT16; ++kt)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                mem[cc][kt][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                    rs, uint32_t(((16 * kt + 4 * g4 + r) * (DV + 1) + 16 * (m + 4 * cc) + i16) * 4), 0, 0));
+            if (ht < Kp / 4)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(mem[kt][r]), rs,
-                                                          uint32_t(((16 * kt + 4 * g4 + r) * (DV + 1) + 16 * wave + i16) * 4),
-                                                          0, 0);
-        if (threadIdx.x < Kp / 4)  // Zs is complete after B_P of the last chunk
+                    Zs[4 * ht + r] = state_in ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                                    rs, uint32_t(((4 * ht + r) * (DV + 1) + DV) * 4), 0, 0))
+                                              : 0.0f;
+        }
+        run(std::false_type(), [&] {
+            if (mode == 0) ok = wait_tokens(fl, s, token, wait_limit);
+            const __amdgpu_buffer_rsrc_t ra = make_rsrc(agg, int64_t(s) * int64_t(E) * 4);
+            for (int gs = 0; gs < s; ++gs) {  // increasing segment order
+                const uint32_t a = uint32_t(size_t(gs) * E * 4);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Zs[4 * threadIdx.x + r]), rs,
-                                                      uint32_t(((4 * threadIdx.x + r) * (DV + 1) + DV) * 4), 0, 0);
+                for (int cc = 0; cc < CPW; ++cc)
+                    if (owns(cc))
+#pragma unroll
+                        for (int kt = 0; kt < KT16; ++kt) {
+                            const u32x4 v =
+                                buf_load16_dev(ra, a + uint32_t(((16 * (m + 4 * cc) + i16) * Kp + 16 * kt + 4 * g4) * 4));
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) mem[cc][kt][r] += __uint_as_float(v[r]);
+                            if (kt % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bounds the loads in flight
+                        }
+                if (ht < Kp / 4) {
+                    const u32x4 v = buf_load16_dev(ra, a + uint32_t((Kp * DV + 4 * ht) * 4));
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) Zs[4 * ht + r] += __uint_as_float(v[r]);
+                }
+            }
+        });
+        float* so = (state_out && s == G - 1) ? state_out + p * SE : nullptr;
+        if (so) {  // the memory after the last position, same layout; rows k >= K are dropped
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(so, int64_t(SE) * 4);
+#pragma unroll
+            for (int cc = 0; cc < CPW; ++cc)
+                if (owns(cc))
+#pragma unroll
+                    for (int kt = 0; kt < KT16; ++kt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            __builtin_amdgcn_raw_buffer_store_b32(
+                                __float_as_uint(mem[cc][kt][r]), rs,
+                                uint32_t(((16 * kt + 4 * g4 + r) * (DV + 1) + 16 * (m + 4 * cc) + i16) * 4), 0, 0);
+            if (ht < Kp / 4)  // Zs is complete after B_P of the last chunk
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Zs[4 * ht + r]), rs,
+                                                          uint32_t(((4 * ht + r) * (DV + 1) + DV) * 4), 0, 0);
+        }
     }
+
     // waves poll on their own: agree on the outcome before acting on it
     ok = workgroup_all(ok, vote);
     if (!ok) {  // the starting memory was never complete: make that visible in the outputs and to the host
         __builtin_amdgcn_s_waitcnt(0);  // the scan's own stores of these rows land first
         __syncthreads();
         uint16_t* op = O + (size_t(p) * N + lo) * DV;
-        for (int64_t e = threadIdx.x; e < rows * DV; e += NT) op[e] = 0x7fc0u;
-        if (so)
-            for (size_t e = threadIdx.x; e < SE; e += NT) so[e] = __builtin_nanf("");
+        for (int64_t e = threadIdx.x; e < rows * DV; e += 512) op[e] = 0x7fc0u;
+        if (state_out && s == G - 1)
+            for (size_t e = threadIdx.x; e < SE; e += 512) state_out[p * SE + e] = __builtin_nanf("");
         if (threadIdx.x == 0) atomicOr(err, kDevErrTimeout);
     }
 }
