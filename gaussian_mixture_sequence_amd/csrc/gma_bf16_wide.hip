@@ -44,14 +44,14 @@ namespace bf {
 template <int DR, int VT>
 struct WideLds {
     static constexpr int KT = 8, Kp = 256, DV = VT * 32, CH = 32, NW = 8, NS = 4, NT = NW * 64, HT = NT / 2;
-    static constexpr int LDG = Kp + 8, LDV = DV + 8, LDSS = CH + 8, DPARTS = 8;
+    static constexpr int LDG = Kp + 8, LDV = DV + 8, LDSS = CH + 8;
     using XT = XTile<DR, CH, HT>;  // staged by the score waves' 256 threads
     using g_t = uint16_t[2][CH * LDG];
     using v_t = uint16_t[2][CH * LDV];
     using s_t = uint16_t[CH * LDSS];
     using x_t = u32x4[XT::LDS_BYTES / 16];
     using st_t = float[2][NS][CH][2];   // (m, L) per job (0: keys, 1: queries), score wave, position
-    using di_t = float[DPARTS][CH];     // partial sums of Gq Z over 32 components each
+    using di_t = float[CH];             // Gq Z per query
     using dp_t = float[2][CH];          // S row sums of key block 0 and 1
     using z_t = float[Kp];
     using c_t = float[Kp];              // score constants c_k (log2 units)
@@ -213,6 +213,55 @@ __global__ void __launch_bounds__(512)
             __syncthreads();  // P2: Gamma(0) and x(1) in LDS
             for (int64_t c = 0; c < C; ++c) {
                 const int b = int(c & 1);
+                if constexpr (!AGG) {
+                    // S^T tiles of chunk c (rows keys, columns queries), blocks (q, k) = (0,0), (1,0),
+                    // (1,1) on waves 0, 1, 2, with their masked row sums
+                    if (wave < 3) {
+                        const int qb = wave > 0 ? 1 : 0, kb = wave > 1 ? 1 : 0;
+                        f32x4 sacc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                        for (int ks = 0; ks < Kp / 32; ++ks)
+                            sacc = mfma16(
+                                *reinterpret_cast<const bf16x8*>(Gk[b] + (kb * 16 + i16) * LDG + 32 * ks + 8 * g4),
+                                *reinterpret_cast<const bf16x8*>(Gq[b] + (qb * 16 + i16) * LDG + 32 * ks + 8 * g4), sacc);
+                        float rs = 0.0f;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            if (kb * 16 + 4 * g4 + r > qb * 16 + i16) sacc[r] = 0.0f;  // key after query
+                            rs += sacc[r];
+                        }
+                        rs += __shfl_xor(rs, 16, kWave);
+                        rs += __shfl_xor(rs, 32, kWave);
+                        if (g4 == 0) den_part[kb][qb * 16 + i16] = rs;
+                        *reinterpret_cast<u32x2*>(Ss + (qb * 16 + i16) * LDSS + kb * 16 + 4 * g4) =
+                            u32x2{pack_bf16x2(sacc[0], sacc[1]), pack_bf16x2(sacc[2], sacc[3])};
+                    }
+                    {  // Gq(c) Z (memory before chunk c): thread (row, part) sums components
+                       // 32 part .. + 31, then the eight parts of a row are summed across lanes
+                        const int row = ht >> 3, part = ht & 7;
+                        const uint16_t* gr = Gq[b] + row * LDG + 32 * part;
+                        float d = 0.0f;
+#pragma unroll
+                        for (int h4 = 0; h4 < 4; ++h4) {
+                            const int hh = (h4 + part) & 3;  // staggered: fewer bank conflicts on Zs
+                            const u32x4 gv = *reinterpret_cast<const u32x4*>(gr + 8 * hh);
+                            const float4 z0 = *reinterpret_cast<const float4*>(Zs + 32 * part + 8 * hh);
+                            const float4 z1 = *reinterpret_cast<const float4*>(Zs + 32 * part + 8 * hh + 4);
+                            d = fmaf(__uint_as_float(gv[0] << 16), z0.x, d);
+                            d = fmaf(__uint_as_float(gv[0] & 0xffff0000u), z0.y, d);
+                            d = fmaf(__uint_as_float(gv[1] << 16), z0.z, d);
+                            d = fmaf(__uint_as_float(gv[1] & 0xffff0000u), z0.w, d);
+                            d = fmaf(__uint_as_float(gv[2] << 16), z1.x, d);
+                            d = fmaf(__uint_as_float(gv[2] & 0xffff0000u), z1.y, d);
+                            d = fmaf(__uint_as_float(gv[3] << 16), z1.z, d);
+                            d = fmaf(__uint_as_float(gv[3] & 0xffff0000u), z1.w, d);
+                        }
+                        d += __shfl_xor(d, 1, kWave);
+                        d += __shfl_xor(d, 2, kWave);
+                        d += __shfl_xor(d, 4, kWave);
+                        if (part == 0) den_ip[row] = d;
+                    }
+                }
                 __builtin_amdgcn_s_setprio(1);
                 scores_next();  // chunk c+1
                 __builtin_amdgcn_s_setprio(0);
@@ -263,6 +312,44 @@ __global__ void __launch_bounds__(512)
         // owns all CPW of them (known at compile time; the loops then carry no branches)
         constexpr bool ALL = C16 % 4 == 0;
         auto owns_next = [&](int cc) { return ALL || owns(cc); };
+        // V(c) column fragments of the wave's own column tiles
+        auto load_bv = [&](int bb, bf16x8(&bv)[CPW]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int cc = 0; cc < CPW; ++cc)
+                bv[cc] = owns_next(cc) ? read_colfrag16(Vs[bb], LDV, 0, 16 * (m + 4 * cc)) : bf16x8{};
+        };
+        // memory += Gk(c)^T V(c) (own columns), Z += Gk(c)^T 1 (tiles 4 m .. 4 m + 3)
+        auto update_memory = [&](int bb, const bf16x8(&bv)[CPW]) __attribute__((always_inline)) {
+            __builtin_amdgcn_s_setprio(1);  // matrix-core work: ahead of the score waves' vector work
+            if (owns(0)) {
+                // two steps of look-ahead on the Gk fragment reads
+                bf16x8 a0 = read_colfrag16(Gk[bb], LDG, 0, 0), a1 = read_colfrag16(Gk[bb], LDG, 0, 16);
+#pragma unroll
+                for (int kt = 0; kt < KT16; ++kt) {
+                    const bf16x8 a = a0;
+                    a0 = a1;
+                    if (kt + 2 < KT16) a1 = read_colfrag16(Gk[bb], LDG, 0, 16 * (kt + 2));
+#pragma unroll
+                    for (int cc = 0; cc < CPW; ++cc)
+                        if (owns_next(cc)) mem[cc][kt] = mfma16(a, bv[cc], mem[cc][kt]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            __builtin_amdgcn_s_setprio(0);
+            {  // Zs is read again only after B_P
+                bf16x8 az[4];
+                f32x4 zt[4];
+#pragma unroll
+                for (int zi = 0; zi < 4; ++zi) az[zi] = read_colfrag16(Gk[bb], LDG, 0, 16 * (4 * m + zi));
+#pragma unroll
+                for (int zi = 0; zi < 4; ++zi) zt[zi] = mfma16(az[zi], ones, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+                if (i16 == 0)
+#pragma unroll
+                    for (int zi = 0; zi < 4; ++zi)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) Zs[16 * (4 * m + zi) + 4 * g4 + r] += zt[zi][r];
+            }
+        };
         __syncthreads();  // B_init
 
         // pre(): after the first V load is in flight, before the memory is read
@@ -280,50 +367,12 @@ __global__ void __launch_bounds__(512)
                 const int b = int(c & 1);
                 const int64_t nc = c * CH;
                 f32x4 o[CPW][2];
-                // ---- part 1
-                if constexpr (!AGG) {
-                    __builtin_amdgcn_s_setprio(1);
-                    // S^T tiles (rows keys, columns queries) of blocks (q, k) = (0,0), (1,0), (1,1)
-                    if (m < 3) {
-                        const int qb = m > 0 ? 1 : 0, kb = m > 1 ? 1 : 0;
-                        f32x4 sacc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                        for (int ks = 0; ks < Kp / 32; ++ks)
-                            sacc = mfma16(
-                                *reinterpret_cast<const bf16x8*>(Gk[b] + (kb * 16 + i16) * LDG + 32 * ks + 8 * g4),
-                                *reinterpret_cast<const bf16x8*>(Gq[b] + (qb * 16 + i16) * LDG + 32 * ks + 8 * g4), sacc);
-                        float rs = 0.0f;
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            if (kb * 16 + 4 * g4 + r > qb * 16 + i16) sacc[r] = 0.0f;  // key after query
-                            rs += sacc[r];
-                        }
-                        rs += __shfl_xor(rs, 16, kWave);
-                        rs += __shfl_xor(rs, 32, kWave);
-                        if (g4 == 0) den_part[kb][qb * 16 + i16] = rs;
-                        *reinterpret_cast<u32x2*>(Ss + (qb * 16 + i16) * LDSS + kb * 16 + 4 * g4) =
-                            u32x2{pack_bf16x2(sacc[0], sacc[1]), pack_bf16x2(sacc[2], sacc[3])};
-                    }
-                    {  // partial sums of Gq(c) Z over components 32 part .. + 31
-                        const int row = ht & 31, part = ht >> 5;
-                        const u32x4* gr = reinterpret_cast<const u32x4*>(Gq[b] + row * LDG + 32 * part);
-                        float d = 0.0f;
-#pragma unroll
-                        for (int h4 = 0; h4 < 4; ++h4) {
-                            const u32x4 gv = gr[h4];
-                            const float4 z0 = *reinterpret_cast<const float4*>(Zs + 32 * part + 8 * h4);
-                            const float4 z1 = *reinterpret_cast<const float4*>(Zs + 32 * part + 8 * h4 + 4);
-                            d = fmaf(__uint_as_float(gv[0] << 16), z0.x, d);
-                            d = fmaf(__uint_as_float(gv[0] & 0xffff0000u), z0.y, d);
-                            d = fmaf(__uint_as_float(gv[1] << 16), z0.z, d);
-                            d = fmaf(__uint_as_float(gv[1] & 0xffff0000u), z0.w, d);
-                            d = fmaf(__uint_as_float(gv[2] << 16), z1.x, d);
-                            d = fmaf(__uint_as_float(gv[2] & 0xffff0000u), z1.y, d);
-                            d = fmaf(__uint_as_float(gv[3] << 16), z1.z, d);
-                            d = fmaf(__uint_as_float(gv[3] & 0xffff0000u), z1.w, d);
-                        }
-                        den_ip[part][row] = d;
-                    }
+                // ---- part 1 (aggregates: the memory update, beside the score waves' products)
+                if constexpr (AGG) {
+                    bf16x8 bv[CPW];
+                    load_bv(b, bv);
+                    update_memory(b, bv);
+                } else {
                     // inter part: O^T = Vt^T Gq^T over the memory before this chunk (hi + lo bf16);
                     // each 32-component step reads its two Gq fragments once for both column
                     // tiles and issues the four hi products before the four lo ones
@@ -368,50 +417,22 @@ __global__ void __launch_bounds__(512)
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     }
-                    __builtin_amdgcn_s_setprio(0);
                 }
                 __syncthreads();  // B_Q
-                // ---- part 2: memory update with chunk c (own columns), Z += Gk^T 1 (tiles 4 m .. 4 m + 3)
-                bf16x8 bv[CPW];  // V(c) column fragments: memory update and intra part
-#pragma unroll
-                for (int cc = 0; cc < CPW; ++cc)
-                    bv[cc] = owns_next(cc) ? read_colfrag16(Vs[b], LDV, 0, 16 * (m + 4 * cc)) : bf16x8{};
-                if (owns(0)) {
-                    // two steps of look-ahead on the Gk fragment reads
-                    bf16x8 a0 = read_colfrag16(Gk[b], LDG, 0, 0), a1 = read_colfrag16(Gk[b], LDG, 0, 16);
-#pragma unroll
-                    for (int kt = 0; kt < KT16; ++kt) {
-                        const bf16x8 a = a0;
-                        a0 = a1;
-                        if (kt + 2 < KT16) a1 = read_colfrag16(Gk[b], LDG, 0, 16 * (kt + 2));
-#pragma unroll
-                        for (int cc = 0; cc < CPW; ++cc)
-                            if (owns_next(cc)) mem[cc][kt] = mfma16(a, bv[cc], mem[cc][kt]);
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                }
-                {  // Zs is read again only after B_P
-                    bf16x8 az[4];
-                    f32x4 zt[4];
-#pragma unroll
-                    for (int zi = 0; zi < 4; ++zi) az[zi] = read_colfrag16(Gk[b], LDG, 0, 16 * (4 * m + zi));
-#pragma unroll
-                    for (int zi = 0; zi < 4; ++zi) zt[zi] = mfma16(az[zi], ones, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
-                    if (i16 == 0)
-#pragma unroll
-                        for (int zi = 0; zi < 4; ++zi)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) Zs[16 * (4 * m + zi) + 4 * g4 + r] += zt[zi][r];
-                }
+                // ---- part 2: V(c+1) into the free buffer first (its wait then covers no output
+                // stores); scans: memory update with chunk c, outputs of chunk c
+                commit_v(Vs[b ^ 1]);
+                load_v(nc + 2 * CH);
                 if constexpr (!AGG) {
+                    bf16x8 bv[CPW];  // V(c) column fragments: memory update and intra part
+                    load_bv(b, bv);
+                    update_memory(b, bv);
                     float rden[2];
 #pragma unroll
                     for (int t16 = 0; t16 < 2; ++t16) {
                         const int q = t16 * 16 + i16;
-                        float den = eps + den_part[0][q];
+                        float den = eps + den_ip[q] + den_part[0][q];
                         if (t16 == 1) den += den_part[1][q];
-#pragma unroll
-                        for (int pt = 0; pt < LY::DPARTS; ++pt) den += den_ip[pt][q];
                         rden[t16] = __builtin_amdgcn_rcpf(den);
                     }
 #pragma unroll
@@ -434,8 +455,6 @@ __global__ void __launch_bounds__(512)
                         }
                     }
                 }
-                commit_v(Vs[b ^ 1]);  // V(c+1)
-                load_v(nc + 2 * CH);
                 __syncthreads();  // B_P
             }
         };
