@@ -259,7 +259,7 @@ template <int DR, int KT>
 struct Split {
     // register-resident planes <= 64 VGPRs per wave, and at most 2 component tiles per wave
     // (the pipelined kernels hold two rounds of scores)
-    static constexpr int CS0 = (KT * DR) / 64 > KT / 2 ? (KT * DR) / 64 : KT / 2;
+    static constexpr int CS0 = KT;
     static constexpr int CS = CS0 < 1 ? 1 : (CS0 > KT ? KT : CS0);
     static constexpr int CTW = KT / CS;         // component tiles per wave
     static constexpr int NW = CS > 4 ? CS : 4;  // waves per workgroup

@@ -498,7 +498,10 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(causal_lds_bytes<DR, KT, VT, CH
     if (s + 1 < G && !aggregated) {
         write_body<DR, KT, VT, true>(smem, XK, V, N, p, h, lo, hi, mx, P, agg + size_t(s) * E);
         publish_token(fl + s, token);  // its barrier also frees the write phase's LDS
-    } else if constexpr (PlaneBuilder<DR, Kp, NT>::LDS_BYTES <= sizeof(smem)) {  // the whole buffer is free here
+    }
+    // the scan's planes are built the same way in every workgroup and either launch mode (not
+    // taken over from the write phase), so the outputs do not depend on the launch mode
+    if constexpr (PlaneBuilder<DR, Kp, NT>::LDS_BYTES <= sizeof(smem)) {  // the whole buffer is free here
         PlaneBuilder<DR, Kp, NT> pb;
         pb.load(mx, h);
         pb.build(smem, mx.K);
