@@ -199,15 +199,17 @@ struct ReadLds {
     using XT = XTile<DR, S::ROUND, NT>;
     // VtT hi/lo staged in LDS when it fits; otherwise read from L2
     static constexpr bool MS_LDS = (2 * DV * LDM + S::ROUND * LDG) * 2 + XT::LDS_BYTES <= 150 * 1024;
-    static constexpr int BASE = S::TS * S::CS * 32 * 12 + S::ROUND * LDG * 2 + (MS_LDS ? 2 * DV * LDM * 2 : 0) +
-                                2 * S::ROUND * 4;
-    static constexpr int XB = (BASE + 2 * XT::LDS_BYTES <= 80 * 1024) ? 2 : 1;  // keep two workgroups per CU
     using st_t = Stats[S::CS > 1 ? S::TS * S::CS * 32 : 1];  // unused with one component group
-    using xt_t = u32x4[XB][XT::LDS_BYTES / 16];
     using gs_t = uint16_t[S::ROUND * LDG];
     using ms_t = uint16_t[MS_LDS ? 2 * DV * LDM : 8];
     using dn_t = float[2][S::ROUND];
     using vote_t = int[S::NW];  // per-wave votes of the fused kernel's hand-off (workgroup_all)
+    // everything but the x tiles, as laid out below; two x buffers only if the whole still
+    // keeps two workgroups per CU
+    static constexpr size_t REST = lds_align(sizeof(st_t)) + lds_align(sizeof(gs_t)) + lds_align(sizeof(ms_t)) +
+                                   lds_align(sizeof(dn_t)) + lds_align(sizeof(vote_t));
+    static constexpr int XB = (REST + 2 * size_t(XT::LDS_BYTES) <= 80 * 1024) ? 2 : 1;
+    using xt_t = u32x4[XB][XT::LDS_BYTES / 16];
     static constexpr size_t o_st = 0, o_xt = lds_align(o_st + sizeof(st_t)), o_gs = lds_align(o_xt + sizeof(xt_t)),
                             o_ms = lds_align(o_gs + sizeof(gs_t)), o_dn = lds_align(o_ms + sizeof(ms_t)),
                             o_vote = lds_align(o_dn + sizeof(dn_t)), bytes = lds_align(o_vote + sizeof(vote_t));

@@ -70,9 +70,14 @@ template <int DR, int KT, int VT>
 struct WriteLds {
     using S = Split<DR, KT>;
     static constexpr int NT = S::NW * 64, Kp = KT * 32, DV = VT * 32, LDG = Kp + 8, LDV = DV + 8;
-    using XT = XTile<DR, S::ROUND, NT>;
     static constexpr int ZSPLIT = S::NW / gcd_i(KT, S::NW);
     static constexpr int BASE = S::TS * S::CS * 32 * 12 + S::ROUND * (LDG + LDV) * 2;
+    // x is staged with its square split (XTile), except where one wave reads each token
+    // subtile, the split tile would leave room for only one workgroup per CU and the wave's
+    // registers have room to split its own fragments: then raw (RawTile, a third of the LDS)
+    static constexpr bool RAW = S::CS == 1 && BASE + XTile<DR, S::ROUND, NT>::LDS_BYTES > 80 * 1024 &&
+                                BASE + RawTile<DR, S::ROUND, NT>::LDS_BYTES <= 80 * 1024 && DR * VT <= 128;
+    using XT = typename std::conditional<RAW, RawTile<DR, S::ROUND, NT>, XTile<DR, S::ROUND, NT>>::type;
     static constexpr int XB = (BASE + 2 * XT::LDS_BYTES <= 80 * 1024) ? 2 : 1;  // keep two workgroups per CU
     using st_t = Stats[S::CS > 1 ? S::TS * S::CS * 32 : 1];  // unused with one component group
     using xt_t = u32x4[XB][XT::LDS_BYTES / 16];
@@ -102,7 +107,7 @@ __device__ __forceinline__ void write_body(char* __restrict__ smem, const uint16
     constexpr int NW = S::NW, NT = NW * 64;
     constexpr int Kp = KT * 32, DV = VT * 32;
     constexpr int LDG = Kp + 8, LDV = DV + 8;
-    using XT = XTile<DR, S::ROUND, NT>;
+    using XT = typename LY::XT;
     constexpr int VCHUNKS = S::ROUND * DV / 8;
     constexpr int VCH = (VCHUNKS + NT - 1) / NT;
     constexpr bool VEVEN = VCHUNKS % NT == 0;
@@ -127,6 +132,15 @@ __device__ __forceinline__ void write_body(char* __restrict__ smem, const uint16
     const int cs = wave % S::CS, ts = wave / S::CS;
     const int64_t rows = hi - lo;
     const int64_t R = (rows + S::ROUND - 1) / S::ROUND;  // rounds of this split
+    auto scores_tile = [&](const u32x4* xtile, f32x16 (&acc)[S::CTW]) __attribute__((always_inline)) {
+        if constexpr (!LY::RAW) {
+            scores_lds<DR, S::CTW>(P, xtile, ts, acc);
+        } else {
+            bf16x8 xs[S::KS];
+            raw_frags<DR>(xtile, ts, xs);
+            scores_x<DR, S::CTW>(P, xs, acc);
+        }
+    };
     // operand planes built by the whole workgroup in the x tile buffer when it is large
     // enough, else by every wave for itself
     using PB = PlaneBuilder<DR, Kp, NT>;
@@ -204,14 +218,14 @@ __device__ __forceinline__ void write_body(char* __restrict__ smem, const uint16
         if (XB == 2) xt1.commit(Xt[XB - 1]);
         __syncthreads();
         if (XB == 1) {
-            scores_lds<DR, S::CTW>(P, Xt[0], ts, acc_a_init);
+            scores_tile(Xt[0], acc_a_init);
             __syncthreads();  // x tile 0 consumed by every wave
             xt1.commit(Xt[0]);
             __syncthreads();
         }
     }
     f32x16 acc_a[S::CTW], acc_b[S::CTW];
-    if (XB == 2) scores_lds<DR, S::CTW>(P, Xt[0], ts, acc_a);
+    if (XB == 2) scores_tile(Xt[0], acc_a);
     else
 #pragma unroll
         for (int ct = 0; ct < S::CTW; ++ct) acc_a[ct] = acc_a_init[ct];
@@ -226,7 +240,7 @@ __device__ __forceinline__ void write_body(char* __restrict__ smem, const uint16
         // fills the VALU around it rather than competing for issue.
         __builtin_amdgcn_s_setprio(1);
         accumulate();
-        scores_lds<DR, S::CTW>(P, Xt[xb1], ts, nxt);
+        scores_tile(Xt[xb1], nxt);
         if (XB == 2) {
             xt.commit(Xt[xb1 ^ 1]);  // x tile r+2 into the buffer x tile r left
             xt.load(rx, r0 + 3 * S::ROUND);
