@@ -973,6 +973,521 @@ hipError_t reduce_params(const Plan& p, const float* part, int B, const double* 
     return hipGetLastError();
 }
 
+// ---- K-blocked passes of the bidirectional backward (64 < K <= 256; d_r, d_v <= 64, multiples
+// of 4): the same 16 x 16 thread grid of 4 x 4 register blocks, the components taken in blocks
+// of 64.  Row passes (one workgroup per split) compute each side's responsibilities for all K
+// from the LDS tables of one block at a time, cache them ([P][N][K] fp32) and form the per-row
+// sums over every component; block passes (one workgroup per split and component block) read
+// the cached responsibilities and produce what each component owns: the moments, the memory
+// gradient and the block's share of dX, summed over the blocks afterwards in block order.
+// The sums over all components that Eq. 18 needs reduce to per-row closed forms:
+//   query: sum_k gamma_ik g_ik = dO'_i . N_i - a'_i (D_i - eps) = eps a'_i,
+//   key:   sum_k gamma_jk g_jk = V_j . dV_j + sum_k gamma_jk dZ_k,
+// with N_i = gamma^Q_i Vt, D_i = gamma^Q_i Z + eps, dO'_i = dO_i / D_i and a'_i = dO_i . N_i / D_i^2.
+constexpr int kKB = 64;          // components per block
+constexpr int kLB = kKB + 4;     // row stride of [.][block] LDS arrays
+
+int kb_blocks(int64_t K) { return int((K + kKB - 1) / kKB); }
+
+// Responsibilities of rows [n0, n0 + rows) of one problem for all K components: the direct-form
+// score of Eq. 16 from fp32 tables of one block at a time, then the softmax of Eq. 3b over all
+// blocks (row maximum and sum over the 16 lanes of the row group).  Into S ([64][LK], zero past
+// `rows` and K) and the cache rows gc ([.][K] of this problem).  LDS: xT [dr][kLDT], muT and ivT
+// [dr][kLB], cB [kKB].
+template <int KB>
+__device__ void kb_gamma(const float* Xp, int64_t n0, int rows, int dr, int K, const double* ch, const double* ih,
+                         const float* mh, float* xT, float* muT, float* ivT, float* cB, float* S, int LK, float* gc) {
+    const int tid = threadIdx.x, r0 = (tid >> 4) * 4, m0 = (tid & 15) * 4;
+    load_xT(Xp, n0, rows, dr, xT);
+    float mrow[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        __syncthreads();  // the previous block's tables are consumed (and xT is in place)
+        for (int i = tid; i < kKB * dr; i += kThreads) {
+            const int kl = i / dr, d = i - kl * dr, k = kb * kKB + kl;
+            muT[d * kLB + kl] = k < K ? mh[size_t(k) * dr + d] : 0.0f;
+            ivT[d * kLB + kl] = k < K ? float(ih[size_t(k) * dr + d]) : 0.0f;
+        }
+        for (int kl = tid; kl < kKB; kl += kThreads) cB[kl] = kb * kKB + kl < K ? float(ch[kb * kKB + kl]) : -INFINITY;
+        __syncthreads();
+        float q[4][4] = {};
+#pragma unroll 4
+        for (int d = 0; d < dr; ++d) {
+            float xa[4], ma[4], ia[4];
+            unpack(lds4(xT + d * kLDT + r0), xa);
+            unpack(lds4(muT + d * kLB + m0), ma);
+            unpack(lds4(ivT + d * kLB + m0), ia);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float df = xa[i] - ma[j];
+                    q[i][j] = fmaf(df * df, ia[j], q[i][j]);
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float s[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                s[j] = cB[m0 + j] - 0.5f * q[i][j];
+                mrow[i] = fmaxf(mrow[i], s[j]);
+            }
+            put4(S + (r0 + i) * LK + kb * kKB + m0, s[0], s[1], s[2], s[3]);
+        }
+    }
+    // each thread reads back only what it wrote: no barrier
+    float rr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        mrow[i] = max16(mrow[i]);
+        float l = 0.0f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            float* sp = S + (r0 + i) * LK + kb * kKB + m0;
+            float s[4];
+            unpack(lds4(sp), s);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                s[j] = expf(s[j] - mrow[i]);
+                l += s[j];
+            }
+            put4(sp, s[0], s[1], s[2], s[3]);
+        }
+        rr[i] = r0 + i < rows ? 1.0f / sum16(l) : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            float* sp = S + (r0 + i) * LK + kb * kKB + m0;
+            float s[4];
+            unpack(lds4(sp), s);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                s[j] *= rr[i];
+                const int k = kb * kKB + m0 + j;
+                if (r0 + i < rows && k < K) gc[(n0 + r0 + i) * K + k] = s[j];
+            }
+            put4(sp, s[0], s[1], s[2], s[3]);
+        }
+    __syncthreads();
+}
+
+template <int KB>
+size_t kb_rows_lds_bytes(int dr, int dv) {
+    return size_t(dr * kLDT + 2 * dr * kLB + kKB + kBT * (KB * kKB + 4) + kKB * (dv + 4) + kKB + kBT * (dv + 4)) *
+           sizeof(float);
+}
+
+// Row passes, grid (G, P): rows [g seg, (g + 1) seg) of problem p in tiles of 64.
+//   QUERY = false (key side): responsibilities of X = X_K into the cache gc, and the split's
+//     partial [Vt | Z] (Eq. 5-6) of Y = V into mem_part;
+//   QUERY = true: responsibilities of X = X_Q into gc; with the memory mem = [Vt | Z] and Y = dO,
+//     D_i and a'_i of every row into rowda ([.][2] per problem).
+template <int KB, bool QUERY>
+__global__ void __launch_bounds__(kThreads)
+    f32_bwd_kb_rows_kernel(const float* __restrict__ X, const float* __restrict__ Y, int64_t N, int H, int dr, int dv,
+                           int K, int64_t seg, int G, const double* __restrict__ c, const double* __restrict__ inv,
+                           const float* __restrict__ mu, const float* __restrict__ mem, float eps,
+                           float* __restrict__ gcache, float* __restrict__ mem_part, float* __restrict__ rowda) {
+    extern __shared__ float lds[];
+    const int64_t p = blockIdx.y;
+    const int gi = blockIdx.x, h = int(p % H);
+    const int tid = threadIdx.x, r0 = (tid >> 4) * 4, m0 = (tid & 15) * 4;
+    const int LK = KB * kKB + 4, LY = dv + 4;
+    float* xT = lds;                   // [dr][kLDT]
+    float* muT = xT + dr * kLDT;       // [dr][kLB]
+    float* ivT = muT + dr * kLB;       // [dr][kLB]
+    float* cB = ivT + dr * kLB;        // [kKB]
+    float* S = cB + kKB;               // [64][LK] responsibilities
+    float* Mb = S + kBT * LK;          // [kKB][dv + 4] a block of Vt (query)
+    float* Zb = Mb + kKB * LY;         // [kKB]
+    float* Yr = Zb + kKB;              // [64][dv + 4] V (key) or dO (query) rows
+    const double *ch = c + size_t(h) * K, *ih = inv + size_t(h) * K * dr;
+    const float* mh = mu + size_t(h) * K * dr;
+    const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
+    const float* Xp = X + size_t(p) * N * dr;
+    const float* Yp = Y + size_t(p) * N * dv;
+    float* gc = gcache + size_t(p) * N * K;
+    float mv[KB][4][4] = {}, mz[KB][4] = {};  // key side: Vt rows k = kb 64 + r0.., columns c = m0..
+    for (int64_t n0 = lo; n0 < hi; n0 += kBT) {
+        const int rows = int(min<int64_t>(kBT, hi - n0));
+        __syncthreads();  // the previous tile's reads are done
+        for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
+            const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
+            const float4 v = t < rows ? *reinterpret_cast<const float4*>(Yp + (n0 + t) * dv + cc) : make_float4(0, 0, 0, 0);
+            *reinterpret_cast<float4*>(Yr + t * LY + cc) = v;
+        }
+        kb_gamma<KB>(Xp, n0, rows, dr, K, ch, ih, mh, xT, muT, ivT, cB, S, LK, gc);
+        if (!QUERY) {
+            if (m0 < dv)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll 4
+                    for (int t = 0; t < rows; ++t) {
+                        float ga[4], ya[4];
+                        unpack(lds4(S + t * LK + kb * kKB + r0), ga);
+                        unpack(lds4(Yr + t * LY + m0), ya);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            mz[kb][i] += ga[i];
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) mv[kb][i][j] = fmaf(ga[i], ya[j], mv[kb][i][j]);
+                        }
+                    }
+            continue;
+        }
+        // query: N_t = gamma_t Vt (rows t = r0.., columns c = m0..) and gamma_t Z, block by block
+        float nv[4][4] = {}, dz[4] = {};
+        const float* mp = mem + size_t(p) * K * (dv + 1);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            __syncthreads();  // the previous block of the memory is consumed
+            for (int i = tid; i < kKB * (dv / 4); i += kThreads) {
+                const int kl = i / (dv / 4), cc = (i - kl * (dv / 4)) * 4, k = kb * kKB + kl;
+                float4 v = make_float4(0, 0, 0, 0);
+                if (k < K) v = make_float4(mp[size_t(k) * dv + cc], mp[size_t(k) * dv + cc + 1], mp[size_t(k) * dv + cc + 2],
+                                           mp[size_t(k) * dv + cc + 3]);
+                *reinterpret_cast<float4*>(Mb + kl * LY + cc) = v;
+            }
+            for (int kl = tid; kl < kKB; kl += kThreads) Zb[kl] = kb * kKB + kl < K ? mp[size_t(K) * dv + kb * kKB + kl] : 0.0f;
+            __syncthreads();
+#pragma unroll 4
+            for (int kl = 0; kl < kKB; ++kl) {
+                float ga[4], va[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ga[i] = S[(r0 + i) * LK + kb * kKB + kl];
+                unpack(lds4(Mb + kl * LY + (m0 < dv ? m0 : 0)), va);
+                const float z = Zb[kl];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dz[i] = fmaf(ga[i], z, dz[i]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ga[i], va[j], nv[i][j]);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float dot = 0.0f;
+            if (m0 < dv) {
+                float oa[4];
+                unpack(lds4(Yr + (r0 + i) * LY + m0), oa);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dot = fmaf(oa[j], nv[i][j], dot);
+            }
+            dot = sum16(dot);
+            const float D = dz[i] + eps;
+            if ((tid & 15) == 0 && r0 + i < rows) {
+                rowda[(size_t(p) * N + n0 + r0 + i) * 2] = D;
+                rowda[(size_t(p) * N + n0 + r0 + i) * 2 + 1] = dot / (D * D);
+            }
+        }
+    }
+    if (!QUERY) {  // the split's partial [Vt | Z]
+        float* out = mem_part + (size_t(p) * G + gi) * size_t(K) * (dv + 1);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int k = kb * kKB + r0 + i;
+                if (k >= K) continue;
+                if (m0 < dv)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) out[size_t(k) * dv + m0 + j] = mv[kb][i][j];
+                if (m0 == 0) out[size_t(K) * dv + k] = mz[kb][i];
+            }
+    }
+}
+
+size_t kb_block_lds_bytes(int dr, int dv) {
+    return size_t(2 * kBT * kLB + kBT * (dv + 4) + dv * kLB + kKB + 3 * kBT + kBT * (dr + 4) + 2 * kKB * (dr + 4)) *
+           sizeof(float);
+}
+
+// Block passes, grid (G, P, KB): component block kb = blockIdx.z of split g of problem p.
+//   QUERY: Y = dO, mem = [Vt | Z], rowda = (D, a') per row; g_ik = (dO_i . Vt_k) / D_i - a'_i Z_k and
+//     ds = gamma (g - eps a'); the block's rows of the partial [dVt | dZ] into mem_part;
+//   key: Y = V, mem = [dVt | dZ], rowda = w per row (the key-side closed form); g_jk = V_j . dVt_k + dZ_k.
+// Both: the block's entries of the moment record (S1, S2, S0) into param_part, and the block's
+// share of dX (-sum_k ds_ik (x_id - mu_kd) / sigma2_kd over its components) into dX_part[kb].
+template <bool QUERY>
+__global__ void __launch_bounds__(kThreads)
+    f32_bwd_kb_block_kernel(const float* __restrict__ X, const float* __restrict__ Y, int64_t N, int H, int dr, int dv,
+                            int K, int64_t seg, int G, const double* __restrict__ inv, const float* __restrict__ mu,
+                            const float* __restrict__ mem, float eps, const float* __restrict__ gcache,
+                            const float* __restrict__ rowda, float* __restrict__ mem_part,
+                            float* __restrict__ param_part, float* __restrict__ dX_part) {
+    extern __shared__ float lds[];
+    const int64_t p = blockIdx.y;
+    const int gi = blockIdx.x, kb = blockIdx.z, h = int(p % H);
+    const int tid = threadIdx.x, r0 = (tid >> 4) * 4, m0 = (tid & 15) * 4;
+    const int LY = dv + 4, LX = dr + 4, k0 = kb * kKB;
+    float* Gb = lds;                  // [64][kLB] responsibilities of the block
+    float* Db = Gb + kBT * kLB;       // [64][kLB] ds
+    float* Yr = Db + kBT * kLB;       // [64][dv + 4] dO / D (query) or V (key) rows
+    float* MT = Yr + kBT * LY;        // [dv][kLB] the block of Vt (query) or dVt (key), transposed
+    float* Zb = MT + dv * kLB;        // [kKB] Z or dZ
+    float* Av = Zb + kKB;             // [64] a' (query)
+    float* Wv = Av + kBT;             // [64] sum_k gamma g of the row
+    float* Dv = Wv + kBT;             // [64] D (query)
+    float* Xr = Dv + kBT;             // [64][dr + 4] x rows
+    float* muR = Xr + kBT * LX;       // [kKB][dr + 4] mu of the block
+    float* ivR = muR + kKB * LX;      // [kKB][dr + 4] 1 / sigma2 of the block
+    const double* ih = inv + size_t(h) * K * dr;
+    const float* mh = mu + size_t(h) * K * dr;
+    const float* mp = mem + size_t(p) * K * (dv + 1);
+    for (int i = tid; i < kKB * dr; i += kThreads) {
+        const int kl = i / dr, d = i - kl * dr, k = k0 + kl;
+        muR[kl * LX + d] = k < K ? mh[size_t(k) * dr + d] : 0.0f;
+        ivR[kl * LX + d] = k < K ? float(ih[size_t(k) * dr + d]) : 0.0f;
+    }
+    for (int i = tid; i < kKB * dv; i += kThreads) {
+        const int kl = i / dv, cc = i - kl * dv, k = k0 + kl;
+        MT[cc * kLB + kl] = k < K ? mp[size_t(k) * dv + cc] : 0.0f;
+    }
+    for (int kl = tid; kl < kKB; kl += kThreads) Zb[kl] = k0 + kl < K ? mp[size_t(K) * dv + k0 + kl] : 0.0f;
+    __syncthreads();
+    // moment accumulators (rows d = r0.., columns k = m0..) with their mu; memory-gradient
+    // accumulators (query: rows k = r0.., columns c = m0..)
+    const bool mom = r0 < dr;
+    float mreg[4][4], s1[4][4] = {}, s2[4][4] = {}, s0[4] = {}, mv[4][4] = {}, mz[4] = {};
+    if (mom)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mreg[i][j] = muR[(m0 + j) * LX + r0 + i];
+    const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
+    const float* Xp = X + size_t(p) * N * dr;
+    const float* Yp = Y + size_t(p) * N * dv;
+    const float* gc = gcache + size_t(p) * N * K;
+    float* dXp = dX_part + (size_t(kb) * gridDim.y + p) * N * dr;
+    for (int64_t n0 = lo; n0 < hi; n0 += kBT) {
+        const int rows = int(min<int64_t>(kBT, hi - n0));
+        __syncthreads();  // the previous tile's reads are done
+        for (int i = tid; i < kBT * kKB; i += kThreads) {
+            const int t = i / kKB, kl = i - t * kKB;
+            Gb[t * kLB + kl] = (t < rows && k0 + kl < K) ? gc[(n0 + t) * K + k0 + kl] : 0.0f;
+        }
+        for (int t = tid; t < kBT; t += kThreads) {
+            if (QUERY) {
+                const float D = t < rows ? rowda[(size_t(p) * N + n0 + t) * 2] : 1.0f;
+                const float a = t < rows ? rowda[(size_t(p) * N + n0 + t) * 2 + 1] : 0.0f;
+                Dv[t] = D;
+                Av[t] = a;
+                Wv[t] = eps * a;
+            } else {
+                Wv[t] = t < rows ? rowda[size_t(p) * N + n0 + t] : 0.0f;
+            }
+        }
+        for (int i = tid; i < kBT * (dr / 4); i += kThreads) {
+            const int t = i / (dr / 4), d = (i - t * (dr / 4)) * 4;
+            *reinterpret_cast<float4*>(Xr + t * LX + d) =
+                t < rows ? *reinterpret_cast<const float4*>(Xp + (n0 + t) * dr + d) : make_float4(0, 0, 0, 0);
+        }
+        __syncthreads();  // Dv before the scaled rows
+        for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
+            const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
+            float4 v = t < rows ? *reinterpret_cast<const float4*>(Yp + (n0 + t) * dv + cc) : make_float4(0, 0, 0, 0);
+            if (QUERY) {
+                const float rD = 1.0f / Dv[t];
+                v.x *= rD, v.y *= rD, v.z *= rD, v.w *= rD;
+            }
+            *reinterpret_cast<float4*>(Yr + t * LY + cc) = v;
+        }
+        __syncthreads();
+        {   // g (rows t = r0.., components k = m0..), then ds = gamma (g - w_t) into Db
+            float gg[4][4] = {};
+#pragma unroll 4
+            for (int cc = 0; cc < dv; ++cc) {
+                float ya[4], ma[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ya[i] = Yr[(r0 + i) * LY + cc];
+                unpack(lds4(MT + cc * kLB + m0), ma);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(ya[i], ma[j], gg[i][j]);
+            }
+            float za[4];
+            unpack(lds4(Zb + m0), za);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float ga[4], ds[4];
+                unpack(lds4(Gb + (r0 + i) * kLB + m0), ga);
+                const float w = Wv[r0 + i];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float g = QUERY ? gg[i][j] - Av[r0 + i] * za[j] : gg[i][j] + za[j];
+                    ds[j] = ga[j] * (g - w);
+                }
+                put4(Db + (r0 + i) * kLB + m0, ds[0], ds[1], ds[2], ds[3]);
+            }
+        }
+        if (QUERY && m0 < dv)  // dVt (rows k = r0.., columns c = m0..), dZ
+#pragma unroll 4
+            for (int t = 0; t < rows; ++t) {
+                float ga[4], ya[4];
+                unpack(lds4(Gb + t * kLB + r0), ga);
+                unpack(lds4(Yr + t * LY + m0), ya);
+                const float a = Av[t];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    mz[i] = fmaf(-ga[i], a, mz[i]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) mv[i][j] = fmaf(ga[i], ya[j], mv[i][j]);
+                }
+            }
+        __syncthreads();  // ds in Db
+        if (mom)  // moments (rows d = r0.., columns k = m0..), direct (centred) form
+#pragma unroll 4
+            for (int t = 0; t < rows; ++t) {
+                float xa[4], da[4];
+                unpack(lds4(Xr + t * LX + r0), xa);
+                unpack(lds4(Db + t * kLB + m0), da);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    s0[j] += da[j];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float df = xa[i] - mreg[i][j], w = da[j] * df;
+                        s1[i][j] += w;
+                        s2[i][j] = fmaf(w, df, s2[i][j]);
+                    }
+                }
+            }
+        if (m0 < dr) {  // this block's share of dX (rows t = r0.., columns d = m0..)
+            float xa[4][4], acc[4][4] = {};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) unpack(lds4(Xr + (r0 + i) * LX + m0), xa[i]);
+            const int kn = min(kKB, K - k0);
+#pragma unroll 4
+            for (int kl = 0; kl < kn; ++kl) {
+                float ma[4], ia[4], da[4];
+                unpack(lds4(muR + kl * LX + m0), ma);
+                unpack(lds4(ivR + kl * LX + m0), ia);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) da[i] = Db[(r0 + i) * kLB + kl];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(da[i] * ia[j], xa[i][j] - ma[j], acc[i][j]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (r0 + i < rows)
+                    *reinterpret_cast<float4*>(dXp + (n0 + r0 + i) * dr + m0) =
+                        make_float4(-acc[i][0], -acc[i][1], -acc[i][2], -acc[i][3]);
+        }
+    }
+    // the block's entries of the moment record [S1 (K dr) | S2 (K dr) | S0 (K)]
+    float* pp = param_part + (size_t(p) * G + gi) * size_t(2 * K * dr + K);
+    if (mom)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = k0 + m0 + j;
+            if (k >= K) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pp[size_t(k) * dr + r0 + i] = s1[i][j];
+                pp[size_t(K) * dr + size_t(k) * dr + r0 + i] = s2[i][j];
+            }
+            if (r0 == 0) pp[2 * size_t(K) * dr + k] = s0[j];
+        }
+    if (QUERY) {  // the block's rows of the partial [dVt | dZ]
+        float* out = mem_part + (size_t(p) * G + gi) * size_t(K) * (dv + 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int k = k0 + r0 + i;
+            if (k >= K) continue;
+            if (m0 < dv)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) out[size_t(k) * dv + m0 + j] = mv[i][j];
+            if (m0 == 0) out[size_t(K) * dv + k] = mz[i];
+        }
+    }
+}
+
+// Key rows, grid (G, P): dV_j = gamma^K_j dVt (an output) and w_j = V_j . dV_j + gamma^K_j . dZ from
+// the cached responsibilities and dmem = [dVt | dZ].
+template <int KB>
+__global__ void __launch_bounds__(kThreads)
+    f32_bwd_kb_keyrows_kernel(const float* __restrict__ V, int64_t N, int dv, int K, int64_t seg,
+                              const float* __restrict__ dmem, const float* __restrict__ gcache,
+                              float* __restrict__ dV, float* __restrict__ roww) {
+    extern __shared__ float lds[];
+    const int64_t p = blockIdx.y;
+    const int gi = blockIdx.x;
+    const int tid = threadIdx.x, r0 = (tid >> 4) * 4, m0 = (tid & 15) * 4;
+    const int LY = dv + 4;
+    float* Gb = lds;               // [64][kLB]
+    float* Mb = Gb + kBT * kLB;    // [kKB][dv + 4] a block of dVt
+    float* Zb = Mb + kKB * LY;     // [kKB]
+    const float* mp = dmem + size_t(p) * K * (dv + 1);
+    const float* gc = gcache + size_t(p) * N * K;
+    const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
+    for (int64_t n0 = lo; n0 < hi; n0 += kBT) {
+        const int rows = int(min<int64_t>(kBT, hi - n0));
+        float nv[4][4] = {}, ez[4] = {};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int k0 = kb * kKB;
+            __syncthreads();  // the previous block is consumed
+            for (int i = tid; i < kBT * kKB; i += kThreads) {
+                const int t = i / kKB, kl = i - t * kKB;
+                Gb[t * kLB + kl] = (t < rows && k0 + kl < K) ? gc[(n0 + t) * K + k0 + kl] : 0.0f;
+            }
+            for (int i = tid; i < kKB * dv; i += kThreads) {
+                const int kl = i / dv, cc = i - kl * dv, k = k0 + kl;
+                Mb[kl * LY + cc] = k < K ? mp[size_t(k) * dv + cc] : 0.0f;
+            }
+            for (int kl = tid; kl < kKB; kl += kThreads) Zb[kl] = k0 + kl < K ? mp[size_t(K) * dv + k0 + kl] : 0.0f;
+            __syncthreads();
+#pragma unroll 4
+            for (int kl = 0; kl < kKB; ++kl) {
+                float ga[4], va[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ga[i] = Gb[(r0 + i) * kLB + kl];
+                unpack(lds4(Mb + kl * LY + (m0 < dv ? m0 : 0)), va);
+                const float z = Zb[kl];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ez[i] = fmaf(ga[i], z, ez[i]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ga[i], va[j], nv[i][j]);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t n = n0 + r0 + i;
+            float dot = 0.0f;
+            if (m0 < dv && r0 + i < rows) {
+                const float4 v = *reinterpret_cast<const float4*>(V + (size_t(p) * N + n) * dv + m0);
+                dot = v.x * nv[i][0] + v.y * nv[i][1] + v.z * nv[i][2] + v.w * nv[i][3];
+                *reinterpret_cast<float4*>(dV + (size_t(p) * N + n) * dv + m0) =
+                    make_float4(nv[i][0], nv[i][1], nv[i][2], nv[i][3]);
+            }
+            dot = sum16(dot);
+            if ((tid & 15) == 0 && r0 + i < rows) roww[size_t(p) * N + n] = dot + ez[i];
+        }
+    }
+}
+
+// dX = sum over the component blocks of their shares, in block order.
+__global__ void __launch_bounds__(kThreads) f32_bwd_kb_sum_kernel(const float* __restrict__ part, int KB, size_t n,
+                                                                  float* __restrict__ dX) {
+    const size_t i = (size_t(blockIdx.x) * kThreads + threadIdx.x) * 4;
+    if (i >= n) return;
+    float4 s = *reinterpret_cast<const float4*>(part + i);
+    for (int kb = 1; kb < KB; ++kb) {
+        const float4 v = *reinterpret_cast<const float4*>(part + size_t(kb) * n + i);
+        s.x += v.x, s.y += v.y, s.z += v.z, s.w += v.w;
+    }
+    *reinterpret_cast<float4*>(dX + i) = s;
+}
+
 // The one-element-per-thread passes: FAST (tables and memory in LDS) with the largest tile (64
 // down to 16 positions) that fits, else the general form with the largest tile that fits.
 // With larger K the tables alone stay in LDS (the memory is read from the workspace) and the
@@ -1003,7 +1518,13 @@ hipError_t bwd_allow_lds() {
                              (const void*)f32_bwd_side_kernel<false, true>,
                              (const void*)f32_bwd_tiled_kernel<BWD_WRITE>, (const void*)f32_bwd_tiled_kernel<BWD_QUERY>,
                              (const void*)f32_bwd_tiled_kernel<BWD_KEY>, (const void*)f32_bwd_tiled_kernel<BWD_CQUERY>,
-                             (const void*)f32_bwd_tiled_kernel<BWD_CKEY>};
+                             (const void*)f32_bwd_tiled_kernel<BWD_CKEY>,
+                             (const void*)f32_bwd_kb_rows_kernel<2, false>, (const void*)f32_bwd_kb_rows_kernel<2, true>,
+                             (const void*)f32_bwd_kb_rows_kernel<3, false>, (const void*)f32_bwd_kb_rows_kernel<3, true>,
+                             (const void*)f32_bwd_kb_rows_kernel<4, false>, (const void*)f32_bwd_kb_rows_kernel<4, true>,
+                             (const void*)f32_bwd_kb_block_kernel<true>, (const void*)f32_bwd_kb_block_kernel<false>,
+                             (const void*)f32_bwd_kb_keyrows_kernel<2>, (const void*)f32_bwd_kb_keyrows_kernel<3>,
+                             (const void*)f32_bwd_kb_keyrows_kernel<4>};
         for (const void* f : fns) {
             hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
             if (r != hipSuccess) return r;
@@ -1018,12 +1539,102 @@ hipError_t bwd_allow_lds() {
 // Responsibilities of one side, [P][N][K] fp32 (the register-tiled passes keep them between passes).
 size_t gamma_cache_bytes(const Plan& p) { return round_up(size_t(p.P * p.N) * size_t(p.K) * 4, 256); }
 
+bool bwd_kb_applies(const Plan& p) {
+    return p.K > 64 && p.K <= 256 && p.dr % 4 == 0 && p.dv % 4 == 0 && p.dr <= 64 && p.dv <= 64 && p.N > 0 &&
+           p.Nq > 0;
+}
+
+// The K-blocked passes' buffers: the responsibilities of both sides ([P][Nq][K], [P][N][K]),
+// (D, a') per query row, w per key row and the blocks' shares of dX ([KB][P][max(N, Nq)][dr]).
+struct KbBuffers {
+    float *gq, *gk, *rowq, *roww, *dxpart;
+};
+size_t kb_bytes(const Plan& p, KbBuffers* b, char* base) {
+    const size_t P = size_t(p.P), K = size_t(p.K), nmax = size_t(std::max(p.N, p.Nq));
+    const size_t sizes[5] = {round_up(P * size_t(p.Nq) * K * 4, 256), round_up(P * size_t(p.N) * K * 4, 256),
+                             round_up(P * size_t(p.Nq) * 2 * 4, 256), round_up(P * size_t(p.N) * 4, 256),
+                             round_up(size_t(kb_blocks(p.K)) * P * nmax * size_t(p.dr) * 4, 256)};
+    size_t off = 0;
+    float** outs[5] = {b ? &b->gq : nullptr, b ? &b->gk : nullptr, b ? &b->rowq : nullptr, b ? &b->roww : nullptr,
+                       b ? &b->dxpart : nullptr};
+    for (int i = 0; i < 5; ++i) {
+        if (b) *outs[i] = reinterpret_cast<float*>(base + off);
+        off += sizes[i];
+    }
+    return off;
+}
+
 size_t f32_backward_extra_bytes(const Plan& p) {
     const size_t E = size_t(p.K) * size_t(p.dv + 1);
     return round_up(size_t(p.P * p.G) * E * 4, 256) + round_up(size_t(p.P) * E * 4, 256) +
            round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256) +
-           (bwd_tiled_applies(p) ? gamma_cache_bytes(p) : 0);
+           (bwd_tiled_applies(p) ? gamma_cache_bytes(p) : 0) + (bwd_kb_applies(p) ? kb_bytes(p, nullptr, nullptr) : 0);
 }
+
+namespace {
+
+template <typename F>
+hipError_t with_kb(int KB, F&& f) {
+    if (KB == 2) return f(std::integral_constant<int, 2>());
+    if (KB == 3) return f(std::integral_constant<int, 3>());
+    if (KB == 4) return f(std::integral_constant<int, 4>());
+    return hipErrorNotSupported;
+}
+
+// The bidirectional backward in K-blocked passes (see f32_bwd_kb_rows_kernel).
+hipError_t f32_backward_bidir_kb(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
+                                 const float* pi, float eps, const float* dO, float* dXQ, float* dXK, float* dV,
+                                 float* dmu, float* ds2, float* dpi, const F32Params& v, float* partials, float* memory,
+                                 float* dpart, float* dmem, float* ppart, float* ppart_key, char* kbase, hipStream_t st) {
+    KbBuffers b{};
+    kb_bytes(p, &b, kbase);
+    const int H = int(p.H), dr = int(p.dr), dv = int(p.dv), K = int(p.K), G = int(p.G), KB = kb_blocks(p.K);
+    const int Ei = int(size_t(p.K) * size_t(p.dv + 1));
+    const dim3 grid(unsigned(p.G), unsigned(p.P)), bgrid(unsigned(p.G), unsigned(p.P), unsigned(KB));
+    const dim3 cgrid(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P));
+    const float* cnone = nullptr;
+    float* none = nullptr;
+    const size_t blds = kb_block_lds_bytes(dr, dv);
+    auto sum_dx = [&](int64_t N, float* dX) {
+        const size_t n = size_t(p.P) * size_t(N) * size_t(dr);
+        GMA_LAUNCH("f32_bwd_dx_sum", f32_bwd_kb_sum_kernel, dim3(unsigned((n / 4 + kThreads - 1) / kThreads)),
+                   dim3(kThreads), 0, st, static_cast<const float*>(b.dxpart), KB, n, dX);
+        return hipGetLastError();
+    };
+    return with_kb(KB, [&](auto KBc) -> hipError_t {
+        constexpr int KBT = decltype(KBc)::value;
+        const size_t rlds = kb_rows_lds_bytes<KBT>(dr, dv);
+        hipError_t e;
+        GMA_LAUNCH("f32_bwd_write", (f32_bwd_kb_rows_kernel<KBT, false>), grid, dim3(kThreads), rlds, st, XK, V, p.N, H,
+                   dr, dv, K, p.seg, G, v.c, v.inv, mu, cnone, eps, b.gk, partials, none);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, partials, G, Ei, memory);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        GMA_LAUNCH("f32_bwd_query_rows", (f32_bwd_kb_rows_kernel<KBT, true>), grid, dim3(kThreads), rlds, st, XQ, dO,
+                   p.Nq, H, dr, dv, K, p.seg_q, G, v.c, v.inv, mu, static_cast<const float*>(memory), eps, b.gq, none,
+                   b.rowq);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        GMA_LAUNCH("f32_bwd_query", f32_bwd_kb_block_kernel<true>, bgrid, dim3(kThreads), blds, st, XQ, dO, p.Nq, H,
+                   dr, dv, K, p.seg_q, G, v.inv, mu, static_cast<const float*>(memory), eps,
+                   static_cast<const float*>(b.gq), static_cast<const float*>(b.rowq), dpart, ppart, b.dxpart);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = sum_dx(p.Nq, dXQ)) != hipSuccess) return e;
+        GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, dpart, G, Ei, dmem);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        GMA_LAUNCH("f32_bwd_key_rows", f32_bwd_kb_keyrows_kernel<KBT>, grid, dim3(kThreads),
+                   size_t(kBT * kLB + kKB * (dv + 4) + kKB) * sizeof(float), st, V, p.N, dv, K, p.seg,
+                   static_cast<const float*>(dmem), static_cast<const float*>(b.gk), dV, b.roww);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        GMA_LAUNCH("f32_bwd_key", f32_bwd_kb_block_kernel<false>, bgrid, dim3(kThreads), blds, st, XK, V, p.N, H, dr,
+                   dv, K, p.seg, G, v.inv, mu, static_cast<const float*>(dmem), eps, static_cast<const float*>(b.gk),
+                   static_cast<const float*>(b.roww), none, ppart_key, b.dxpart);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = sum_dx(p.N, dXK)) != hipSuccess) return e;
+        return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
+    });
+}
+
+}  // namespace
 
 hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
                               const float* s2, const float* pi, float eps, const float* dO, float* dXQ, float* dXK,
@@ -1049,6 +1660,12 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
                                                round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256));
     float* none = nullptr;
     const float* cnone = nullptr;
+    if (bwd_kb_applies(p))
+        return f32_backward_bidir_kb(p, XQ, XK, V, mu, pi, eps, dO, dXQ, dXK, dV, dmu, ds2, dpi, v, partials, memory,
+                                     dpart, dmem, ppart, ppart_key,
+                                     reinterpret_cast<char*>(ppart) +
+                                         round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256),
+                                     st);
     const dim3 grid(unsigned(p.G), unsigned(p.P));
     const int Ei = int(E);
     const dim3 cgrid(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P));

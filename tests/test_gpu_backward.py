@@ -98,7 +98,10 @@ CASES = [
     case(5000, 93, d_r=32, d_v=64, K=64),              # several splits per problem
     case(300, 94, B=1, H=1, d_r=128, d_v=128, K=256),  # maximum dims (half-height tiles)
     case(700, 95, B=3, H=2, d_r=64, d_v=32, K=128, mu_std=1.5),
-    case(500, 96, B=1, H=2, d_r=64, d_v=64, K=256),     # K beyond the LDS memory: tables only
+    case(500, 96, B=1, H=2, d_r=64, d_v=64, K=256),     # K-blocked passes: four full blocks
+    # K-blocked passes: a ragged last block and tail, several splits, small dims
+    case(1500, 97, B=2, H=2, d_r=32, d_v=48, K=200),
+    case(6000, 98, B=1, H=3, d_r=16, d_v=16, K=100, mu_std=1.5),
 ]
 
 
@@ -313,6 +316,8 @@ CROSS_CASES = [
     cross_case(3000, 700, 133, d_r=32, d_v=64, K=64),            # more queries than keys
     cross_case(257, 100, 134, d_r=7, d_v=5, K=13),               # general kernels
     cross_case(130, 450, 135, B=1, H=1, d_r=128, d_v=128, K=256),
+    cross_case(700, 1900, 140, d_r=64, d_v=64, K=128),          # K-blocked passes, longer context
+    cross_case(2100, 300, 141, d_r=32, d_v=32, K=192),          # K-blocked passes, more queries
     cross_case(300, 0, 136),                                     # empty context
     cross_case(0, 300, 137),                                     # no queries
     cross_case(1000, 3000, 138, d_r=64, d_v=64, K=64, dtype="bf16"),
