@@ -194,7 +194,7 @@ __device__ __forceinline__ void combine_range(const float* __restrict__ part, in
 // LDS of read_body, carved in this order out of one workgroup buffer.
 template <int DR, int KT, int VT>
 struct ReadLds {
-    using S = Split<DR, KT>;
+    using S = Split<DR, KT, true>;
     static constexpr int NT = S::NW * 64, Kp = KT * 32, DV = VT * 32, LDG = Kp + 8, LDM = Kp + 8;
     using XT = XTile<DR, S::ROUND, NT>;
     // VtT hi/lo staged in LDS when it fits; otherwise read from L2
@@ -223,9 +223,9 @@ struct ReadLds {
 template <int DR, int KT, int VT, bool BUILD, typename WaitF>
 __device__ __forceinline__ void read_body(char* __restrict__ smem, const uint16_t* __restrict__ XQ, int64_t N,
                                           int64_t p, int h, int64_t lo, int64_t hi, const Mixture& mx,
-                                          WaveParams<DR, Split<DR, KT>::CTW>& P, const uint16_t* mp, float eps,
+                                          WaveParams<DR, Split<DR, KT, true>::CTW>& P, const uint16_t* mp, float eps,
                                           uint16_t* __restrict__ O, WaitF&& wait) {
-    using S = Split<DR, KT>;
+    using S = Split<DR, KT, true>;
     using LY = ReadLds<DR, KT, VT>;
     constexpr int NW = S::NW, NT = NW * 64;
     constexpr int Kp = KT * 32, DV = VT * 32;
@@ -462,7 +462,7 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(bidir_lds_bytes<DR, KT, VT>()))
     write_body<DR, KT, VT, true>(smem, XK, V, N, p, h, lo, hi, mx, P, part + size_t(g) * E);
     publish_token(fl + g, token);  // its barrier also frees the write phase's LDS
     bool ok = true;
-    read_body<DR, KT, VT, false>(smem, XQ, Nq, p, h, lo_q, hi_q, mx, P, mem, eps, O, [&] {
+    auto complete = [&] {
         // behind the read phase's first tiles and scores: complete the memory.  The waves
         // poll on their own and agree before the combine, which needs every wave.
         ok = workgroup_all(wait_tokens(fl, G, token, wait_limit), reinterpret_cast<int*>(smem + RL::o_vote));
@@ -472,7 +472,13 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(bidir_lds_bytes<DR, KT, VT>()))
             publish_token(fl + G + g, token);
             ok = wait_tokens(fl + G, G, token, wait_limit);
         }
-    });
+    };
+    if constexpr (Split<DR, KT, true>::CTW == Split<DR, KT>::CTW) {  // the write phase's planes serve
+        read_body<DR, KT, VT, false>(smem, XQ, Nq, p, h, lo_q, hi_q, mx, P, mem, eps, O, complete);
+    } else {  // the read phase's own split: its planes are built again
+        WaveParams<DR, Split<DR, KT, true>::CTW> PR;
+        read_body<DR, KT, VT, true>(smem, XQ, Nq, p, h, lo_q, hi_q, mx, PR, mem, eps, O, complete);
+    }
     ok = workgroup_all(ok, reinterpret_cast<int*>(smem));
     if (!ok) {  // the memory was never complete: make that visible in the output and to the host
         __builtin_amdgcn_s_waitcnt(0);  // the phase's own stores of these rows land first
@@ -508,7 +514,7 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(ReadLds<DR, KT, VT>::bytes))))
     const int g = blockIdx.x;
     const int64_t lo_q = min<int64_t>(int64_t(g) * seg_q, Nq), hi_q = min<int64_t>(lo_q + seg_q, Nq);
     if (lo_q >= hi_q) return;  // uniform over the workgroup
-    WaveParams<DR, Split<DR, KT>::CTW> P;
+    WaveParams<DR, Split<DR, KT, true>::CTW> P;
     read_body<DR, KT, VT, true>(smem, XQ, Nq, p, int(p % H), lo_q, hi_q, mx, P, memory + size_t(p) * E * 2, eps, O,
                                 [] {});
 }

@@ -253,16 +253,18 @@ __device__ __forceinline__ bf16x8 read_rowfrag(const uint16_t* tile, int ld, int
 }
 
 // Wave-level work split of the score computation: CS waves share the components of one
-// token subtile (each holds KT / CS component tiles of the parameter planes in
-// registers), TS = NW / CS token subtiles of 32 tokens are processed side by side.
-template <int DR, int KT>
+// token subtile (each holds KT / CS component tiles of the parameter planes in registers),
+// TS = NW / CS token subtiles of 32 tokens are processed side by side.  NW = max(KT, 4) waves
+// per workgroup in either phase.  The write phase (and the scan, the responsibilities) take
+// one component tile per wave: its accumulators for the memory leave no registers for a
+// second.  The read phase (READ) takes two per wave where d_r <= 32 (the planes of two tiles
+// then fit in 64 VGPRs), which halves its rounds' fixed costs.
+template <int DR, int KT, bool READ = false>
 struct Split {
-    // register-resident planes <= 64 VGPRs per wave, and at most 2 component tiles per wave
-    // (the pipelined kernels hold two rounds of scores)
-    static constexpr int CS0 = KT;
-    static constexpr int CS = CS0 < 1 ? 1 : (CS0 > KT ? KT : CS0);
+    static constexpr int NW = KT > 4 ? KT : 4;  // waves per workgroup
+    static constexpr int CSR0 = (KT * DR) / 64 > KT / 2 ? (KT * DR) / 64 : KT / 2;
+    static constexpr int CS = READ ? (CSR0 < 1 ? 1 : (CSR0 > KT ? KT : CSR0)) : KT;
     static constexpr int CTW = KT / CS;         // component tiles per wave
-    static constexpr int NW = CS > 4 ? CS : 4;  // waves per workgroup
     static constexpr int TS = NW / CS;          // token subtiles per round
     static constexpr int ROUND = 32 * TS;       // tokens per round
     static constexpr int KS = DR / 16;          // k-steps of the d contraction
