@@ -736,7 +736,7 @@ gma_status_t gma_plan_info(gma_op_t op, const gma_shape_t* shape, gma_dtype_t io
         gma::bf16_bidir_geometry(p.dr, p.Kp / 32, p.dv / 32, &threads, &lds);
         info->threads_per_workgroup = threads;
         info->lds_bytes = lds;
-        info->waits_on_all_splits = p.G > 1 ? 1 : 0;
+        info->waits_on_all_splits = p.G > 1 && p.G <= gma::kBidirSingleMaxSplits ? 1 : 0;
         info->resident_bound = gma::kDeviceCUs * gma::bf16_bidir_per_cu(p.dr, p.Kp / 32, p.dv / 32);
     }
     return GMA_OK;

@@ -628,7 +628,7 @@ hipError_t bf16_bidir(const Plan& p, const void* XQ, const void* XK, const void*
             // the single launch waits on every workgroup of a problem: only when the whole grid
             // is resident at once on this device (with one split per problem nothing waits on
             // another workgroup)
-            bool single = single_launch_enabled();
+            bool single = single_launch_enabled() && p.G <= kBidirSingleMaxSplits;
             if (single && p.G > 1) {
                 int64_t resident = 0;
                 hipError_t r = resident_workgroups(reinterpret_cast<const void*>(&bf::bidir_kernel<DR, KT, VT>), NT,

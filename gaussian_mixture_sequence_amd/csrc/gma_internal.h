@@ -46,6 +46,10 @@ uint32_t wait_limit();
 
 // Bits of the per-device error word that kernels raise (atomic OR) and gma_device_status
 // takes: a hand-off wait of a single-launch forward ran out.
+// Splits per problem up to which the bf16 bidirectional forward runs as one launch; beyond,
+// its write, combine and read launches measure faster (the single launch waits on more
+// workgroups per problem and holds both phases' registers).
+constexpr int64_t kBidirSingleMaxSplits = 8;
 constexpr uint32_t kDevErrTimeout = 1u;
 // Address of the error word on the current device (resolved once per device).
 hipError_t device_error_word(uint32_t** word);

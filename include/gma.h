@@ -37,7 +37,8 @@
  *             between the workgroups of one launch and rely on the device dispatching them
  *             (bidirectional: all of the launch's workgroups resident at once; the host
  *             checks the grid against the device's occupancy and otherwise runs the phases
- *             as separate launches).  A kernel running concurrently on another stream can
+ *             as separate launches, as it also does with more than 8 splits per problem,
+ *             where the separate launches measure faster).  A kernel running concurrently on another stream can
  *             hold the compute units those workgroups need; a hand-off wait then runs out
  *             after a bounded time, the affected output rows are NaN and gma_device_status
  *             reports GMA_ERR_TIMEOUT.  Callers that run forwards concurrently on one device
@@ -423,7 +424,8 @@ gma_status_t gma_set_single_launch(int enable);
  *   workgroups             B H splits: the grid of the single launch
  *   threads_per_workgroup  }  bf16 bidirectional only (0 otherwise): the single-launch
  *   lds_bytes              }  kernel's workgroup size and static LDS,
- *   waits_on_all_splits    }  1 if its workgroups wait on every split of their problem,
+ *   waits_on_all_splits    }  1 if the single launch is planned (2 to 8 splits per problem)
+ *                              and its workgroups wait on every split of their problem,
  *   resident_bound         }  and the workgroups that the kernel's LDS and declared waves
  *                              per SIMD let a 256-CU MI355X keep resident at once
  *                              (workgroups <= resident_bound whenever waits_on_all_splits)

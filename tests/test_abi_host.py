@@ -349,10 +349,10 @@ def test_bidir_single_launch_grid_fits_resident_bound(lib, dr, K, dv):
             assert info["threads_per_workgroup"] in (256, 512)
             per_cu = min((160 * 1024) // info["lds_bytes"], (4 * 2 * 64) // info["threads_per_workgroup"])
             assert info["resident_bound"] <= 256 * max(per_cu, 1)
-            if info["splits"] > 1:
+            if 1 < info["splits"] <= 8:  # the single launch: every workgroup resident
                 assert info["waits_on_all_splits"] == 1
                 assert info["workgroups"] <= 256 * per_cu, (B, H, N, info)
-            else:
+            else:  # one split per problem, or the write, combine and read launches
                 assert info["waits_on_all_splits"] == 0
 
 

@@ -330,11 +330,12 @@ def test_bf16_single_launch_off_is_bitwise_equal(w):
 
 def test_bf16_bidir_one_head_long_sequence():
     """One problem (B = H = 1) of 262144 positions at the largest per-workgroup LDS (d_r 64, d_v 128,
-    K 256): the split count is bounded by the workgroups the device keeps resident, so the
-    single-launch hand-off completes; every row against the oracle."""
+    K 256): the split count is bounded by the workgroups the device keeps resident, and with more
+    than 8 splits the phases run as their own launches; every row against the oracle."""
     w = bf16_case(B=1, H=1, N=262144, d_r=64, d_v=128, K=256, seed=69)
     info = gb.gma_plan_info(gb.GMA_OP_BIDIR, w.B, w.H, w.N, w.d_r, w.d_v, w.K, gb.GMA_BF16)
     assert info["workgroups"] <= info["resident_bound"]
+    assert info["waits_on_all_splits"] == (1 if 1 < info["splits"] <= 8 else 0)
     inp = make_inputs(w)
     out = run_gpu(w, inp)
     assert gb.gma_device_status() == gb.GMA_OK
