@@ -441,6 +441,10 @@ def kernel_symbol(w, name: str) -> str:
         kt, vt = component_tiles(w.K), w.d_v // 32
         if name.endswith("_bidir") or name.endswith("_cross"):
             return "gma::bf::bidir_kernel<%d, %d, %d>" % (w.d_r, kt, vt)
+        if name.endswith("_write") or name.endswith("_read"):  # the phases as their own launches
+            return "gma::bf::%s_kernel<%d, %d, %d>" % (name.rsplit("_", 1)[1], w.d_r, kt, vt)
+        if name.endswith("_combine"):
+            return "gma::bf::combine_kernel"
         if name.endswith("_causal"):
             if kt == 8 and w.d_r <= 64:
                 return "gma::bf::wide_causal_kernel<%d, %d>" % (w.d_r, vt)
