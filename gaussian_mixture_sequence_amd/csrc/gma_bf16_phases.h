@@ -93,6 +93,15 @@ struct WriteLds {
                             bytes = lds_align(o_zr + sizeof(zr_t));
 };
 
+// Whether write_body builds its operand planes with the whole workgroup (PlaneBuilder, in its x
+// tile buffer) rather than each wave for itself: the same planes a later PlaneBuilder build
+// gives, bit for bit.
+template <int DR, int KT, int VT>
+constexpr bool write_planes_cooperative() {
+    using LY = WriteLds<DR, KT, VT>;
+    return sizeof(typename LY::xt_t) >= PlaneBuilder<DR, KT * 32, LY::NT>::LDS_BYTES;
+}
+
 // Rows [lo, hi) of problem p (head h) into the fp32 partial `mem` ([DV][Kp] Vt^T, then
 // [Kp] Z), written with device-coherent stores for a consumer in the same launch.
 // BUILD: the operand planes P are built here (overlapping the first loads); otherwise P
@@ -144,7 +153,7 @@ __device__ __forceinline__ void write_body(char* __restrict__ smem, const uint16
     // operand planes built by the whole workgroup in the x tile buffer when it is large
     // enough, else by every wave for itself
     using PB = PlaneBuilder<DR, Kp, NT>;
-    constexpr bool COOP = sizeof(Xt) >= PB::LDS_BYTES;
+    constexpr bool COOP = write_planes_cooperative<DR, KT, VT>();
     typename WaveParams<DR, S::CTW>::Raw praw;
     PB pb;
     if constexpr (BUILD) {

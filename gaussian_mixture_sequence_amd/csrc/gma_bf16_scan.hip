@@ -495,21 +495,25 @@ __attribute__((amdgpu_waves_per_eu(waves_for_lds(causal_lds_bytes<DR, KT, VT, CH
     float* agg = aggregates + size_t(p) * G * E;
     uint64_t* fl = flags + size_t(p) * G;
     WaveParams<DR, S::CTW> P;
-    if (s + 1 < G && !aggregated) {
+    const bool aggregate = s + 1 < G && !aggregated;
+    if (aggregate) {
         write_body<DR, KT, VT, true>(smem, XK, V, N, p, h, lo, hi, mx, P, agg + size_t(s) * E);
         publish_token(fl + s, token);  // its barrier also frees the write phase's LDS
     }
-    // the scan's planes are built the same way in every workgroup and either launch mode (not
-    // taken over from the write phase), so the outputs do not depend on the launch mode
-    if constexpr (PlaneBuilder<DR, Kp, NT>::LDS_BYTES <= sizeof(smem)) {  // the whole buffer is free here
-        PlaneBuilder<DR, Kp, NT> pb;
-        pb.load(mx, h);
-        pb.build(smem, mx.K);
-        __syncthreads();
-        P.template read_planes<Kp>(smem, (wave_id() % S::CS) * S::CTW);
-        __syncthreads();
-    } else {
-        P.compute(mx, h, (wave_id() % S::CS) * S::CTW);
+    // the scan's planes are the same bits in every workgroup and either launch mode, so the
+    // outputs do not depend on the launch mode: the write phase's when it built them with the
+    // whole workgroup, else built here (uniform over the workgroup)
+    if (!(aggregate && write_planes_cooperative<DR, KT, VT>())) {
+        if constexpr (PlaneBuilder<DR, Kp, NT>::LDS_BYTES <= sizeof(smem)) {  // the whole buffer is free here
+            PlaneBuilder<DR, Kp, NT> pb;
+            pb.load(mx, h);
+            pb.build(smem, mx.K);
+            __syncthreads();
+            P.template read_planes<Kp>(smem, (wave_id() % S::CS) * S::CTW);
+            __syncthreads();
+        } else {
+            P.compute(mx, h, (wave_id() % S::CS) * S::CTW);
+        }
     }
     bool ok = true;
     const size_t SE = size_t(mx.K) * (DV + 1);  // one problem's carried memory
