@@ -1074,6 +1074,25 @@ __device__ void kb_gamma(const float* Xp, int64_t n0, int rows, int dr, int K, c
     __syncthreads();
 }
 
+// Responsibilities [t][k0 .. k0 + 63] of the tile's rows from the cache rows gc ([.][K]) into Gb
+// ([64][kLB]), zero past `rows` and K; 16-byte loads when K is a multiple of 4.
+__device__ __forceinline__ void load_gamma_block(const float* __restrict__ gc, int64_t n0, int rows, int K, int k0,
+                                                 float* Gb) {
+    if ((K & 3) == 0) {
+        for (int i = threadIdx.x; i < kBT * (kKB / 4); i += kThreads) {
+            const int t = i / (kKB / 4), kq = (i - t * (kKB / 4)) * 4;
+            const float4 v = (t < rows && k0 + kq < K) ? *reinterpret_cast<const float4*>(gc + (n0 + t) * K + k0 + kq)
+                                                       : make_float4(0, 0, 0, 0);
+            *reinterpret_cast<float4*>(Gb + t * kLB + kq) = v;
+        }
+    } else {
+        for (int i = threadIdx.x; i < kBT * kKB; i += kThreads) {
+            const int t = i / kKB, kl = i - t * kKB;
+            Gb[t * kLB + kl] = (t < rows && k0 + kl < K) ? gc[(n0 + t) * K + k0 + kl] : 0.0f;
+        }
+    }
+}
+
 template <int KB>
 size_t kb_rows_lds_bytes(int dr, int dv) {
     return size_t(dr * kLDT + 2 * dr * kLB + kKB + kBT * (KB * kKB + 4) + kKB * (dv + 4) + kKB + kBT * (dv + 4)) *
@@ -1146,10 +1165,8 @@ __global__ void __launch_bounds__(kThreads)
             __syncthreads();  // the previous block of the memory is consumed
             for (int i = tid; i < kKB * (dv / 4); i += kThreads) {
                 const int kl = i / (dv / 4), cc = (i - kl * (dv / 4)) * 4, k = kb * kKB + kl;
-                float4 v = make_float4(0, 0, 0, 0);
-                if (k < K) v = make_float4(mp[size_t(k) * dv + cc], mp[size_t(k) * dv + cc + 1], mp[size_t(k) * dv + cc + 2],
-                                           mp[size_t(k) * dv + cc + 3]);
-                *reinterpret_cast<float4*>(Mb + kl * LY + cc) = v;
+                *reinterpret_cast<float4*>(Mb + kl * LY + cc) =
+                    k < K ? *reinterpret_cast<const float4*>(mp + size_t(k) * dv + cc) : make_float4(0, 0, 0, 0);
             }
             for (int kl = tid; kl < kKB; kl += kThreads) Zb[kl] = kb * kKB + kl < K ? mp[size_t(K) * dv + kb * kKB + kl] : 0.0f;
             __syncthreads();
@@ -1266,10 +1283,7 @@ __global__ void __launch_bounds__(kThreads)
     for (int64_t n0 = lo; n0 < hi; n0 += kBT) {
         const int rows = int(min<int64_t>(kBT, hi - n0));
         __syncthreads();  // the previous tile's reads are done
-        for (int i = tid; i < kBT * kKB; i += kThreads) {
-            const int t = i / kKB, kl = i - t * kKB;
-            Gb[t * kLB + kl] = (t < rows && k0 + kl < K) ? gc[(n0 + t) * K + k0 + kl] : 0.0f;
-        }
+        load_gamma_block(gc, n0, rows, K, k0, Gb);
         for (int t = tid; t < kBT; t += kThreads) {
             if (QUERY) {
                 const float D = t < rows ? rowda[(size_t(p) * N + n0 + t) * 2] : 1.0f;
@@ -1434,13 +1448,11 @@ __global__ void __launch_bounds__(kThreads)
         for (int kb = 0; kb < KB; ++kb) {
             const int k0 = kb * kKB;
             __syncthreads();  // the previous block is consumed
-            for (int i = tid; i < kBT * kKB; i += kThreads) {
-                const int t = i / kKB, kl = i - t * kKB;
-                Gb[t * kLB + kl] = (t < rows && k0 + kl < K) ? gc[(n0 + t) * K + k0 + kl] : 0.0f;
-            }
-            for (int i = tid; i < kKB * dv; i += kThreads) {
-                const int kl = i / dv, cc = i - kl * dv, k = k0 + kl;
-                Mb[kl * LY + cc] = k < K ? mp[size_t(k) * dv + cc] : 0.0f;
+            load_gamma_block(gc, n0, rows, K, k0, Gb);
+            for (int i = tid; i < kKB * (dv / 4); i += kThreads) {
+                const int kl = i / (dv / 4), cc = (i - kl * (dv / 4)) * 4, k = k0 + kl;
+                *reinterpret_cast<float4*>(Mb + kl * LY + cc) =
+                    k < K ? *reinterpret_cast<const float4*>(mp + size_t(k) * dv + cc) : make_float4(0, 0, 0, 0);
             }
             for (int kl = tid; kl < kKB; kl += kThreads) Zb[kl] = k0 + kl < K ? mp[size_t(K) * dv + k0 + kl] : 0.0f;
             __syncthreads();

@@ -90,6 +90,14 @@ WORKLOADS: Dict[str, Workload] = {
     # backward of the causal forward, fp32: the B=8, H=12, N=2048 causal dims
     "bwdc_b8h12_n2048_f32": Workload("bwdc_b8h12_n2048_f32", True, 8, 12, 2048, 64, 64, 32, "f32", seed=9,
                                      backward=True),
+    # the bidirectional backward at the component counts of the paper's language models (K = 128 and
+    # 256; Sec. 5, experimental setup, and Sec. 5.3) beside K = 64: B=8, H=8, N=1024, d_r=d_v=64, fp32
+    "bwd_b8h8_n1024_k64_f32": Workload("bwd_b8h8_n1024_k64_f32", False, 8, 8, 1024, 64, 64, 64, "f32", seed=10,
+                                       backward=True),
+    "bwd_b8h8_n1024_k128_f32": Workload("bwd_b8h8_n1024_k128_f32", False, 8, 8, 1024, 64, 64, 128, "f32", seed=11,
+                                        backward=True),
+    "bwd_b8h8_n1024_k256_f32": Workload("bwd_b8h8_n1024_k256_f32", False, 8, 8, 1024, 64, 64, 256, "f32", seed=12,
+                                        backward=True),
     "cross_b8h8_q4096_k16384": Workload("cross_b8h8_q4096_k16384", False, 8, 8, 4096, 64, 64, 64, "bf16",
                                         seed=5, n_ctx=16384),
 }
