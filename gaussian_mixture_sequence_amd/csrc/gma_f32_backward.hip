@@ -2111,9 +2111,9 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
     }
     // one element per thread: FAST (tables and running memory in LDS) with 64- or 32-position
     // tiles when two workgroups still fit a CU, else with the largest tile (down to 16) that fits
-    // one; else the tables alone in LDS (tiles down to 8); otherwise the general form: 64-position
-    // tiles when two fit, else the largest tile that lets two fit (down to 32), else the largest
-    // that fits
+    // one; else the tables alone in LDS (tiles down to 4: K = 256 at d_r = 64 fits with 4);
+    // otherwise the general form: 64-position tiles when two fit, else the largest tile that lets
+    // two fit (down to 32), else the largest that fits
     const size_t tables = size_t(2 * K * (dr + 1) + K) * sizeof(float);
     const size_t memory = size_t(K * (dv + 1) + K) * sizeof(float);
     int T = kTile, mem_lds = 1;
@@ -2122,7 +2122,7 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
         if (bwdc_lds_bytes(t, dr, dv, K) + tables + memory <= kMaxLds / 2) fast = true, T = t;
     for (int t = kTile; t >= 16 && !fast; t /= 2)
         if (bwdc_lds_bytes(t, dr, dv, K) + tables + memory <= kMaxLds) fast = true, T = t;
-    for (int t = kTile; t >= 8 && !fast; t /= 2)
+    for (int t = kTile; t >= 4 && !fast; t /= 2)
         if (bwdc_lds_bytes(t, dr, dv, K) + tables <= kMaxLds) fast = true, T = t, mem_lds = 0;
     if (!fast) {
         mem_lds = 0;
