@@ -41,11 +41,11 @@
 namespace gma {
 namespace bf {
 
-template <int DR, int VT>
+template <int DR, int VT, int NW>
 struct WideLds {
-    static constexpr int KT = 8, Kp = 256, DV = VT * 32, CH = 32, NW = 8, NS = 4, NT = NW * 64, HT = NT / 2;
+    static constexpr int KT = 8, Kp = 256, DV = VT * 32, CH = 32, NS = NW / 2, NT = NW * 64, HT = NT / 2;
     static constexpr int LDG = Kp + 8, LDV = DV + 8, LDSS = CH + 8;
-    using XT = XTile<DR, CH, HT>;  // staged by the score waves' 256 threads
+    using XT = XTile<DR, CH, HT>;  // staged by the score waves' threads
     using g_t = uint16_t[2][CH * LDG];
     using v_t = uint16_t[2][CH * LDV];
     using s_t = uint16_t[CH * LDSS];
@@ -64,14 +64,14 @@ struct WideLds {
                             o_vote = lds_align(o_cs + sizeof(c_t)), bytes = lds_align(o_vote + sizeof(vote_t));
 };
 
-// Scores of one 32-token subtile for component tiles ct0, ct0 + 1 from an XTile in LDS, the
-// accumulators starting at the score constants (in LDS, [Kp] fp32).
-template <int DR>
-__device__ __forceinline__ void wide_scores(const WaveParams<DR, 2>& P, const float* cst, int ct0, const u32x4* xt,
-                                            f32x16 (&acc)[2]) {
+// Scores of one 32-token subtile for component tiles ct0 .. ct0 + CTW - 1 from an XTile in LDS,
+// the accumulators starting at the score constants (in LDS, [Kp] fp32).
+template <int DR, int CTW>
+__device__ __forceinline__ void wide_scores(const WaveParams<DR, CTW>& P, const float* cst, int ct0, const u32x4* xt,
+                                            f32x16 (&acc)[CTW]) {
     const int lh = (threadIdx.x & 63) >> 5;
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+    for (int ct = 0; ct < CTW; ++ct)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const float4 cv = *reinterpret_cast<const float4*>(cst + (ct0 + ct) * 32 + 8 * q + 4 * lh);
@@ -85,7 +85,7 @@ __device__ __forceinline__ void wide_scores(const WaveParams<DR, 2>& P, const fl
         bf16x8 x, x2h, x2l;
         xtile_frags<DR>(xt, 0, ks, x, x2h, x2l);
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
+        for (int ct = 0; ct < CTW; ++ct) {
             acc[ct] = mfma(P.w[ct][ks][0], x, acc[ct]);
             acc[ct] = mfma(P.w[ct][ks][1], x, acc[ct]);
             acc[ct] = mfma(P.w[ct][ks][2], x2h, acc[ct]);
@@ -98,19 +98,22 @@ __device__ __forceinline__ void wide_scores(const WaveParams<DR, 2>& P, const fl
 // mode 0: the whole forward (segments 0 .. G-2 aggregate and publish first, every segment
 // waits for the aggregates before it, then scans); mode 1: aggregates only (grid G-1 segments);
 // mode 2: scans only, the aggregates written by an earlier launch (no waits).
-template <int DR, int VT>
-__global__ void __launch_bounds__(512)
+template <int DR, int VT, int NW>
+__global__ void __launch_bounds__(NW * 64)
     wide_causal_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
                        int64_t N, int H, int64_t seg, int G, Mixture mx, float* __restrict__ aggregates,
                        uint64_t* __restrict__ flags, uint64_t token, uint32_t wait_limit, int mode, float eps,
                        uint16_t* __restrict__ O, const float* __restrict__ state_in, float* __restrict__ state_out,
                        uint32_t* __restrict__ err) {
-    using LY = WideLds<DR, VT>;
-    constexpr int Kp = LY::Kp, DV = LY::DV, CH = LY::CH, NS = LY::NS, HT = LY::HT;
+    using LY = WideLds<DR, VT, NW>;
+    constexpr int Kp = LY::Kp, DV = LY::DV, CH = LY::CH, NS = LY::NS, HT = LY::HT, NT = LY::NT;
+    constexpr int CTS = LY::KT / NS;       // component tiles per score wave
+    constexpr int NM = NW - NS;            // memory waves
     constexpr int LDG = LY::LDG, LDV = LY::LDV, LDSS = LY::LDSS;
     constexpr int KT16 = Kp / 16;          // 16-row component tiles of the memory
     constexpr int C16 = DV / 16;           // 16-wide value-column tiles
-    constexpr int CPW = (C16 + 3) / 4;     // column tiles per memory wave: tiles m, m + 4
+    constexpr int CPW = (C16 + NM - 1) / NM;  // column tiles per memory wave: tiles m, m + NM, ..
+    constexpr int ZPW = KT16 / NM;         // Z tiles per memory wave: ZPW m ..
     constexpr int E = Kp * (DV + 1);
     constexpr int VCHUNKS = CH * DV / 8, VCH = (VCHUNKS + HT - 1) / HT;
     constexpr bool VEVEN = VCHUNKS % HT == 0;
@@ -146,12 +149,12 @@ __global__ void __launch_bounds__(512)
 
     if (scorer) {
         // ================================================================ score waves
-        const int ct0 = 2 * wave;
-        WaveParams<DR, 2> P;
+        const int ct0 = CTS * wave;
+        WaveParams<DR, CTS> P;
         P.compute(mx, h, ct0);
-        if (j == 0)  // the constants of tiles ct0, ct0 + 1 into LDS (lanes 0 and 32 hold both halves)
+        if (j == 0)  // the constants of the wave's tiles into LDS (lanes 0 and 32 hold both halves)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < CTS; ++ct)
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
 #pragma unroll
@@ -164,15 +167,15 @@ __global__ void __launch_bounds__(512)
             constexpr bool AGG = decltype(agg_tag)::value;
             constexpr int JOBS = AGG ? 1 : 2;  // 0 keys, 1 queries
             XT xq, xk;
-            f32x16 acc[2][2];
+            f32x16 acc[2][CTS];
             float sm_m[2], sm_L[2];
             auto scores_next = [&]() __attribute__((always_inline)) {
-                wide_scores<DR>(P, cst, ct0, XtK, acc[0]);
-                if (!AGG) wide_scores<DR>(P, cst, ct0, XtQ, acc[1]);
+                wide_scores<DR, CTS>(P, cst, ct0, XtK, acc[0]);
+                if (!AGG) wide_scores<DR, CTS>(P, cst, ct0, XtQ, acc[1]);
 #pragma unroll
                 for (int jb = 0; jb < JOBS; ++jb) {
-                    float D, zdummy[2][16];
-                    local_softmax<2, false>(acc[jb], zdummy, sm_m[jb], sm_L[jb], D);
+                    float D, zdummy[CTS][16];
+                    local_softmax<CTS, false>(acc[jb], zdummy, sm_m[jb], sm_L[jb], D);
                     if (lh == 0) {
                         st[jb][wave][j][0] = sm_m[jb];
                         st[jb][wave][j][1] = sm_L[jb];
@@ -192,7 +195,7 @@ __global__ void __launch_bounds__(512)
                         Lt = fmaf(st[jb][w][j][1], __builtin_amdgcn_exp2f(st[jb][w][j][0] - mm), Lt);
                     float scale = __builtin_amdgcn_exp2f(sm_m[jb] - mm) * __builtin_amdgcn_rcpf(Lt);
                     if (!valid) scale = 0.0f;  // positions past the segment: no responsibility
-                    store_gamma_lds<2>(acc[jb], scale, jb == 0 ? Gk[b] : Gq[b], LDG, j, ct0);
+                    store_gamma_lds<CTS>(acc[jb], scale, jb == 0 ? Gk[b] : Gq[b], LDG, j, ct0);
                 }
             };
             // prologue (barriers P0, P1, P2)
@@ -237,16 +240,17 @@ __global__ void __launch_bounds__(512)
                             u32x2{pack_bf16x2(sacc[0], sacc[1]), pack_bf16x2(sacc[2], sacc[3])};
                     }
                     {  // Gq(c) Z (memory before chunk c): thread (row, part) sums components
-                       // 32 part .. + 31, then the eight parts of a row are summed across lanes
-                        const int row = ht >> 3, part = ht & 7;
-                        const uint16_t* gr = Gq[b] + row * LDG + 32 * part;
+                       // CPP part .. + CPP - 1, then the PARTS parts of a row are summed across lanes
+                        constexpr int PARTS = HT / CH, CPP = Kp / PARTS, NH = CPP / 8;
+                        const int row = ht / PARTS, part = ht % PARTS;
+                        const uint16_t* gr = Gq[b] + row * LDG + CPP * part;
                         float d = 0.0f;
 #pragma unroll
-                        for (int h4 = 0; h4 < 4; ++h4) {
-                            const int hh = (h4 + part) & 3;  // staggered: fewer bank conflicts on Zs
+                        for (int h4 = 0; h4 < NH; ++h4) {
+                            const int hh = (h4 + part) % NH;  // staggered: fewer bank conflicts on Zs
                             const u32x4 gv = *reinterpret_cast<const u32x4*>(gr + 8 * hh);
-                            const float4 z0 = *reinterpret_cast<const float4*>(Zs + 32 * part + 8 * hh);
-                            const float4 z1 = *reinterpret_cast<const float4*>(Zs + 32 * part + 8 * hh + 4);
+                            const float4 z0 = *reinterpret_cast<const float4*>(Zs + CPP * part + 8 * hh);
+                            const float4 z1 = *reinterpret_cast<const float4*>(Zs + CPP * part + 8 * hh + 4);
                             d = fmaf(__uint_as_float(gv[0] << 16), z0.x, d);
                             d = fmaf(__uint_as_float(gv[0] & 0xffff0000u), z0.y, d);
                             d = fmaf(__uint_as_float(gv[1] << 16), z0.z, d);
@@ -256,9 +260,8 @@ __global__ void __launch_bounds__(512)
                             d = fmaf(__uint_as_float(gv[3] << 16), z1.z, d);
                             d = fmaf(__uint_as_float(gv[3] & 0xffff0000u), z1.w, d);
                         }
-                        d += __shfl_xor(d, 1, kWave);
-                        d += __shfl_xor(d, 2, kWave);
-                        d += __shfl_xor(d, 4, kWave);
+#pragma unroll
+                        for (int o = 1; o < PARTS; o <<= 1) d += __shfl_xor(d, o, kWave);
                         if (part == 0) den_ip[row] = d;
                     }
                 }
@@ -307,16 +310,16 @@ __global__ void __launch_bounds__(512)
                 }
             }
         };
-        auto owns = [&](int cc) { return has_cols && m + 4 * cc < C16; };
+        auto owns = [&](int cc) { return has_cols && m + NM * cc < C16; };
         // in the chunk loop: with d_v a multiple of 64 a wave that owns its first column tile
         // owns all CPW of them (known at compile time; the loops then carry no branches)
-        constexpr bool ALL = C16 % 4 == 0;
+        constexpr bool ALL = C16 % NM == 0;
         auto owns_next = [&](int cc) { return ALL || owns(cc); };
         // V(c) column fragments of the wave's own column tiles
         auto load_bv = [&](int bb, bf16x8(&bv)[CPW]) __attribute__((always_inline)) {
 #pragma unroll
             for (int cc = 0; cc < CPW; ++cc)
-                bv[cc] = owns_next(cc) ? read_colfrag16(Vs[bb], LDV, 0, 16 * (m + 4 * cc)) : bf16x8{};
+                bv[cc] = owns_next(cc) ? read_colfrag16(Vs[bb], LDV, 0, 16 * (m + NM * cc)) : bf16x8{};
         };
         // memory += Gk(c)^T V(c) (own columns), Z += Gk(c)^T 1 (tiles 4 m .. 4 m + 3)
         auto update_memory = [&](int bb, const bf16x8(&bv)[CPW]) __attribute__((always_inline)) {
@@ -337,17 +340,17 @@ __global__ void __launch_bounds__(512)
             }
             __builtin_amdgcn_s_setprio(0);
             {  // Zs is read again only after B_P
-                bf16x8 az[4];
-                f32x4 zt[4];
+                bf16x8 az[ZPW];
+                f32x4 zt[ZPW];
 #pragma unroll
-                for (int zi = 0; zi < 4; ++zi) az[zi] = read_colfrag16(Gk[bb], LDG, 0, 16 * (4 * m + zi));
+                for (int zi = 0; zi < ZPW; ++zi) az[zi] = read_colfrag16(Gk[bb], LDG, 0, 16 * (ZPW * m + zi));
 #pragma unroll
-                for (int zi = 0; zi < 4; ++zi) zt[zi] = mfma16(az[zi], ones, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+                for (int zi = 0; zi < ZPW; ++zi) zt[zi] = mfma16(az[zi], ones, f32x4{0.0f, 0.0f, 0.0f, 0.0f});
                 if (i16 == 0)
 #pragma unroll
-                    for (int zi = 0; zi < 4; ++zi)
+                    for (int zi = 0; zi < ZPW; ++zi)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) Zs[16 * (4 * m + zi) + 4 * g4 + r] += zt[zi][r];
+                        for (int r = 0; r < 4; ++r) Zs[16 * (ZPW * m + zi) + 4 * g4 + r] += zt[zi][r];
             }
         };
         __syncthreads();  // B_init
@@ -438,7 +441,7 @@ __global__ void __launch_bounds__(512)
 #pragma unroll
                     for (int cc = 0; cc < CPW; ++cc) {
                         if (!owns_next(cc)) continue;
-                        const int c16 = m + 4 * cc;
+                        const int c16 = m + NM * cc;
 #pragma unroll
                         for (int t16 = 0; t16 < 2; ++t16) {
                             const bf16x8 bb = *reinterpret_cast<const bf16x8*>(Ss + (t16 * 16 + i16) * LDSS + 8 * g4);
@@ -473,7 +476,7 @@ __global__ void __launch_bounds__(512)
                 if (owns(cc))
 #pragma unroll
                     for (int kt = 0; kt < KT16; ++kt)
-                        buf_store16_dev(ra, uint32_t(((16 * (m + 4 * cc) + i16) * Kp + 16 * kt + 4 * g4) * 4),
+                        buf_store16_dev(ra, uint32_t(((16 * (m + NM * cc) + i16) * Kp + 16 * kt + 4 * g4) * 4),
                                         u32x4{__float_as_uint(mem[cc][kt][0]), __float_as_uint(mem[cc][kt][1]),
                                               __float_as_uint(mem[cc][kt][2]), __float_as_uint(mem[cc][kt][3])});
             if (ht < Kp / 4) {
@@ -503,7 +506,7 @@ __global__ void __launch_bounds__(512)
 #pragma unroll
                             for (int r = 0; r < 4; ++r)
                                 mem[cc][kt][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-                                    rs, uint32_t(((16 * kt + 4 * g4 + r) * (DV + 1) + 16 * (m + 4 * cc) + i16) * 4), 0, 0));
+                                    rs, uint32_t(((16 * kt + 4 * g4 + r) * (DV + 1) + 16 * (m + NM * cc) + i16) * 4), 0, 0));
             if (ht < Kp / 4)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -522,7 +525,7 @@ __global__ void __launch_bounds__(512)
 #pragma unroll
                         for (int kt = 0; kt < KT16; ++kt) {
                             const u32x4 v =
-                                buf_load16_dev(ra, a + uint32_t(((16 * (m + 4 * cc) + i16) * Kp + 16 * kt + 4 * g4) * 4));
+                                buf_load16_dev(ra, a + uint32_t(((16 * (m + NM * cc) + i16) * Kp + 16 * kt + 4 * g4) * 4));
 #pragma unroll
                             for (int r = 0; r < 4; ++r) mem[cc][kt][r] += __uint_as_float(v[r]);
                             if (kt % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // bounds the loads in flight
@@ -546,7 +549,7 @@ __global__ void __launch_bounds__(512)
                         for (int r = 0; r < 4; ++r)
                             __builtin_amdgcn_raw_buffer_store_b32(
                                 __float_as_uint(mem[cc][kt][r]), rs,
-                                uint32_t(((16 * kt + 4 * g4 + r) * (DV + 1) + 16 * (m + 4 * cc) + i16) * 4), 0, 0);
+                                uint32_t(((16 * kt + 4 * g4 + r) * (DV + 1) + 16 * (m + NM * cc) + i16) * 4), 0, 0);
             if (ht < Kp / 4)  // Zs is complete after B_P of the last chunk
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
@@ -561,12 +564,16 @@ __global__ void __launch_bounds__(512)
         __builtin_amdgcn_s_waitcnt(0);  // the scan's own stores of these rows land first
         __syncthreads();
         uint16_t* op = O + (size_t(p) * N + lo) * DV;
-        for (int64_t e = threadIdx.x; e < rows * DV; e += 512) op[e] = 0x7fc0u;
+        for (int64_t e = threadIdx.x; e < rows * DV; e += NT) op[e] = 0x7fc0u;
         if (state_out && s == G - 1)
-            for (size_t e = threadIdx.x; e < SE; e += 512) state_out[p * SE + e] = __builtin_nanf("");
+            for (size_t e = threadIdx.x; e < SE; e += NT) state_out[p * SE + e] = __builtin_nanf("");
         if (threadIdx.x == 0) atomicOr(err, kDevErrTimeout);
     }
 }
+
+// Waves per workgroup.  Sixteen (one component tile per score wave, one column tile per memory
+// wave) leave 128 registers per wave, which d_r = 64 exceeds: 79 spilled VGPRs and twice the time.
+constexpr int kWideWaves = 8;
 
 template <typename F>
 hipError_t with_wide(int dr, int vt, F&& f) {
@@ -597,8 +604,8 @@ hipError_t bf16_causal_wide(const Plan& p, const void* XQ, const void* XK, const
         const bool single = single_launch_enabled();
         const uint64_t token = launch_token();
         auto launch = [&](unsigned grid_x, int mode) {
-            GMA_LAUNCH(mode == 1 ? "bf16_causal_aggregate" : "bf16_causal", (bf::wide_causal_kernel<DR, VT>),
-                       dim3(grid_x, unsigned(p.P)), dim3(512), 0, st, static_cast<const uint16_t*>(XQ),
+            GMA_LAUNCH(mode == 1 ? "bf16_causal_aggregate" : "bf16_causal", (bf::wide_causal_kernel<DR, VT, bf::kWideWaves>),
+                       dim3(grid_x, unsigned(p.P)), dim3(bf::kWideWaves * 64), 0, st, static_cast<const uint16_t*>(XQ),
                        static_cast<const uint16_t*>(XK), static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg,
                        int(p.G), mx, aggregates, flags, token, wait_limit(), mode, eps, static_cast<uint16_t*>(O),
                        state_in, state_out, err);
