@@ -1100,16 +1100,19 @@ size_t kb_rows_lds_bytes(int dr, int dv) {
 }
 
 // Row passes, grid (G, P): rows [g seg, (g + 1) seg) of problem p in tiles of 64.
-//   QUERY = false (key side): responsibilities of X = X_K into the cache gc, and the split's
-//     partial [Vt | Z] (Eq. 5-6) of Y = V into mem_part;
-//   QUERY = true: responsibilities of X = X_Q into gc; with the memory mem = [Vt | Z] and Y = dO,
-//     D_i and a'_i of every row into rowda ([.][2] per problem).
-template <int KB, bool QUERY>
+//   KB_KEY: responsibilities of X = X_K into the cache gc, and the split's partial [Vt | Z]
+//     (Eq. 5-6) of Y = V into mem_part;
+//   KB_QUERY: responsibilities of X = X_Q into gc; with the memory mem = [Vt | Z] and Y = dO,
+//     D_i and a'_i of every row into rowda ([.][2] per problem);
+//   KB_GAMMA: the responsibilities of X into gc only.
+enum { KB_KEY = 0, KB_QUERY = 1, KB_GAMMA = 2 };
+template <int KB, int MODE>
 __global__ void __launch_bounds__(kThreads)
     f32_bwd_kb_rows_kernel(const float* __restrict__ X, const float* __restrict__ Y, int64_t N, int H, int dr, int dv,
                            int K, int64_t seg, int G, const double* __restrict__ c, const double* __restrict__ inv,
                            const float* __restrict__ mu, const float* __restrict__ mem, float eps,
                            float* __restrict__ gcache, float* __restrict__ mem_part, float* __restrict__ rowda) {
+    constexpr bool QUERY = MODE == KB_QUERY;
     extern __shared__ float lds[];
     const int64_t p = blockIdx.y;
     const int gi = blockIdx.x, h = int(p % H);
@@ -1133,12 +1136,15 @@ __global__ void __launch_bounds__(kThreads)
     for (int64_t n0 = lo; n0 < hi; n0 += kBT) {
         const int rows = int(min<int64_t>(kBT, hi - n0));
         __syncthreads();  // the previous tile's reads are done
-        for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
-            const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
-            const float4 v = t < rows ? *reinterpret_cast<const float4*>(Yp + (n0 + t) * dv + cc) : make_float4(0, 0, 0, 0);
-            *reinterpret_cast<float4*>(Yr + t * LY + cc) = v;
-        }
+        if (MODE != KB_GAMMA)
+            for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
+                const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
+                const float4 v =
+                    t < rows ? *reinterpret_cast<const float4*>(Yp + (n0 + t) * dv + cc) : make_float4(0, 0, 0, 0);
+                *reinterpret_cast<float4*>(Yr + t * LY + cc) = v;
+            }
         kb_gamma<KB>(Xp, n0, rows, dr, K, ch, ih, mh, xT, muT, ivT, cB, S, LK, gc);
+        if (MODE == KB_GAMMA) continue;
         if (!QUERY) {
             if (m0 < dv)
 #pragma unroll
@@ -1202,7 +1208,7 @@ __global__ void __launch_bounds__(kThreads)
             }
         }
     }
-    if (!QUERY) {  // the split's partial [Vt | Z]
+    if (MODE == KB_KEY) {  // the split's partial [Vt | Z]
         float* out = mem_part + (size_t(p) * G + gi) * size_t(K) * (dv + 1);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -1531,9 +1537,9 @@ hipError_t bwd_allow_lds() {
                              (const void*)f32_bwd_tiled_kernel<BWD_WRITE>, (const void*)f32_bwd_tiled_kernel<BWD_QUERY>,
                              (const void*)f32_bwd_tiled_kernel<BWD_KEY>, (const void*)f32_bwd_tiled_kernel<BWD_CQUERY>,
                              (const void*)f32_bwd_tiled_kernel<BWD_CKEY>,
-                             (const void*)f32_bwd_kb_rows_kernel<2, false>, (const void*)f32_bwd_kb_rows_kernel<2, true>,
-                             (const void*)f32_bwd_kb_rows_kernel<3, false>, (const void*)f32_bwd_kb_rows_kernel<3, true>,
-                             (const void*)f32_bwd_kb_rows_kernel<4, false>, (const void*)f32_bwd_kb_rows_kernel<4, true>,
+                             (const void*)f32_bwd_kb_rows_kernel<2, KB_KEY>, (const void*)f32_bwd_kb_rows_kernel<2, KB_QUERY>,
+                             (const void*)f32_bwd_kb_rows_kernel<3, KB_KEY>, (const void*)f32_bwd_kb_rows_kernel<3, KB_QUERY>,
+                             (const void*)f32_bwd_kb_rows_kernel<4, KB_KEY>, (const void*)f32_bwd_kb_rows_kernel<4, KB_QUERY>,
                              (const void*)f32_bwd_kb_block_kernel<true>, (const void*)f32_bwd_kb_block_kernel<false>,
                              (const void*)f32_bwd_kb_keyrows_kernel<2>, (const void*)f32_bwd_kb_keyrows_kernel<3>,
                              (const void*)f32_bwd_kb_keyrows_kernel<4>};
@@ -1617,12 +1623,12 @@ hipError_t f32_backward_bidir_kb(const Plan& p, const float* XQ, const float* XK
         constexpr int KBT = decltype(KBc)::value;
         const size_t rlds = kb_rows_lds_bytes<KBT>(dr, dv);
         hipError_t e;
-        GMA_LAUNCH("f32_bwd_write", (f32_bwd_kb_rows_kernel<KBT, false>), grid, dim3(kThreads), rlds, st, XK, V, p.N, H,
+        GMA_LAUNCH("f32_bwd_write", (f32_bwd_kb_rows_kernel<KBT, KB_KEY>), grid, dim3(kThreads), rlds, st, XK, V, p.N, H,
                    dr, dv, K, p.seg, G, v.c, v.inv, mu, cnone, eps, b.gk, partials, none);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, partials, G, Ei, memory);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        GMA_LAUNCH("f32_bwd_query_rows", (f32_bwd_kb_rows_kernel<KBT, true>), grid, dim3(kThreads), rlds, st, XQ, dO,
+        GMA_LAUNCH("f32_bwd_query_rows", (f32_bwd_kb_rows_kernel<KBT, KB_QUERY>), grid, dim3(kThreads), rlds, st, XQ, dO,
                    p.Nq, H, dr, dv, K, p.seg_q, G, v.c, v.inv, mu, static_cast<const float*>(memory), eps, b.gq, none,
                    b.rowq);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1765,6 +1771,532 @@ __global__ void __launch_bounds__(kThreads) f32_suffix_kernel(float* __restrict_
         run += a;
     }
     if (dstate_in) dstate_in[size_t(p) * E + state_index(e, K, dv)] = run;
+}
+
+// ---- K-blocked passes of the causal backward (K <= 256; d_r, d_v <= 64, multiples of 4) where
+// the register-tiled causal passes do not fit.  The tile of 64 positions is the unit of the
+// prefix and suffix: a row pass over the key side gives every tile's aggregate gamma_K^T [V | 1]
+// (then an exclusive prefix from state_in: the memory before each tile); the causal query rows
+// give D_i and a'_i from that memory and the masked in-tile products C_ij = gamma^Q_i . gamma^K_j
+// (j <= i, all components), keep C, and give every tile's aggregate of what its queries send,
+// gamma^Q_i [dO'_i | -a'_i] (then an exclusive suffix from dstate_out: what the later tiles'
+// queries send).  Block passes then need, per tile, only the memory block and
+// A_ij = dO'_i . V_j - a'_i (j <= i):
+//   query: g_ik = dO'_i . Vt_k - a'_i Z_k + sum_{j <= i} A_ij gamma^K_jk  (memory before the tile),
+//   key:   g_jk = V_j . dVt_k + dZ_k + sum_{i >= j} A_ij gamma^Q_ik     (what later tiles send);
+// the closed forms of the bidirectional passes give w (eps a'_i on the query side).
+
+// Causal query rows, grid (G, P): per tile of rows [g seg, (g + 1) seg) of problem p: C (into
+// cbuf [P][NT][64][64]), D_i and a'_i (into rowq), and the tile's aggregate of what its queries
+// send (into tsend [P][NT][K (dv + 1)]).  tmem [P][NT][K (dv + 1)]: the memory before each tile.
+template <int KB>
+__global__ void __launch_bounds__(kThreads)
+    f32_bwdc_kb_qrows_kernel(const float* __restrict__ V, const float* __restrict__ dO, int64_t N, int dv, int K,
+                             int64_t seg, const float* __restrict__ gq, const float* __restrict__ gk,
+                             const float* __restrict__ tmem, float eps, float* __restrict__ cbuf,
+                             float* __restrict__ rowq, float* __restrict__ tsend) {
+    extern __shared__ float lds[];
+    const int64_t p = blockIdx.y;
+    const int gi = blockIdx.x;
+    const int tid = threadIdx.x, r0 = (tid >> 4) * 4, m0 = (tid & 15) * 4;
+    const int LY = dv + 4, NT = int((N + kBT - 1) / kBT);
+    const size_t E = size_t(K) * (dv + 1);
+    float* Gq = lds;                // [64][kLB] gamma^Q of a block, rows i
+    float* GkT = Gq + kBT * kLB;    // [kKB][kLB] gamma^K of a block, transposed: [k][j]
+    float* Cm = GkT + kKB * kLB;    // [64][kLB] C (rows i, columns j)
+    float* Mb = Cm + kBT * kLB;     // [kKB][dv + 4] a block of the memory before the tile
+    float* Zb = Mb + kKB * LY;      // [kKB]
+    float* Yr = Zb + kKB;           // [64][dv + 4] dO rows
+    float* Vr = Yr + kBT * LY;      // [64][dv + 4] V rows
+    float* Dv = Vr + kBT * LY;      // [64] D
+    float* Av = Dv + kBT;           // [64] a'
+    const float* gqp = gq + size_t(p) * N * K;
+    const float* gkp = gk + size_t(p) * N * K;
+    const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
+    for (int64_t n0 = lo; n0 < hi; n0 += kBT) {
+        const int rows = int(min<int64_t>(kBT, hi - n0)), tile = int(n0 / kBT);
+        const float* mp = tmem + (size_t(p) * NT + tile) * E;
+        __syncthreads();  // the previous tile's reads are done
+        for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
+            const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
+            const bool ok = t < rows;
+            const size_t off = (size_t(p) * N + n0 + t) * dv + cc;
+            *reinterpret_cast<float4*>(Yr + t * LY + cc) = ok ? *reinterpret_cast<const float4*>(dO + off) : make_float4(0, 0, 0, 0);
+            *reinterpret_cast<float4*>(Vr + t * LY + cc) = ok ? *reinterpret_cast<const float4*>(V + off) : make_float4(0, 0, 0, 0);
+        }
+        float cc4[4][4] = {}, nv[4][4] = {}, dz[4] = {};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int k0 = kb * kKB;
+            __syncthreads();  // the previous block is consumed
+            load_gamma_block(gqp, n0, rows, K, k0, Gq);
+            for (int i = tid; i < kBT * kKB; i += kThreads) {  // gamma^K rows j, transposed
+                const int t = i / kKB, kl = i - t * kKB;
+                GkT[kl * kLB + t] = (t < rows && k0 + kl < K) ? gkp[(n0 + t) * K + k0 + kl] : 0.0f;
+            }
+            for (int i = tid; i < kKB * (dv / 4); i += kThreads) {
+                const int kl = i / (dv / 4), cc = (i - kl * (dv / 4)) * 4, k = k0 + kl;
+                *reinterpret_cast<float4*>(Mb + kl * LY + cc) =
+                    k < K ? *reinterpret_cast<const float4*>(mp + size_t(k) * dv + cc) : make_float4(0, 0, 0, 0);
+            }
+            for (int kl = tid; kl < kKB; kl += kThreads) Zb[kl] = k0 + kl < K ? mp[size_t(K) * dv + k0 + kl] : 0.0f;
+            __syncthreads();
+#pragma unroll 4
+            for (int kl = 0; kl < kKB; ++kl) {
+                float qa[4], ka[4], ma[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) qa[i] = Gq[(r0 + i) * kLB + kl];
+                unpack(lds4(GkT + kl * kLB + m0), ka);
+                unpack(lds4(Mb + kl * LY + (m0 < dv ? m0 : 0)), ma);
+                const float z = Zb[kl];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dz[i] = fmaf(qa[i], z, dz[i]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        cc4[i][j] = fmaf(qa[i], ka[j], cc4[i][j]);
+                        nv[i][j] = fmaf(qa[i], ma[j], nv[i][j]);
+                    }
+                }
+            }
+        }
+        // C masked to j <= i; its row sums join D
+        float cs[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float rsum = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (m0 + j > r0 + i) cc4[i][j] = 0.0f;
+                rsum += cc4[i][j];
+            }
+            cs[i] = sum16(rsum);
+            put4(Cm + (r0 + i) * kLB + m0, cc4[i][0], cc4[i][1], cc4[i][2], cc4[i][3]);
+            if (r0 + i < rows)
+                *reinterpret_cast<float4*>(cbuf + ((size_t(p) * NT + tile) * kBT + r0 + i) * kBT + m0) =
+                    make_float4(cc4[i][0], cc4[i][1], cc4[i][2], cc4[i][3]);
+        }
+        __syncthreads();  // C in LDS
+        if (m0 < dv)  // N_i += sum_{j <= i} C_ij V_j
+#pragma unroll 4
+            for (int jj = 0; jj < rows; ++jj) {
+                float ca[4], va[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ca[i] = Cm[(r0 + i) * kLB + jj];
+                unpack(lds4(Vr + jj * LY + m0), va);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ca[i], va[j], nv[i][j]);
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float dot = 0.0f;
+            if (m0 < dv) {
+                float oa[4];
+                unpack(lds4(Yr + (r0 + i) * LY + m0), oa);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) dot = fmaf(oa[j], nv[i][j], dot);
+            }
+            dot = sum16(dot);
+            const float D = dz[i] + cs[i] + eps, a = dot / (D * D);
+            if ((tid & 15) == 0) {
+                Dv[r0 + i] = D;
+                Av[r0 + i] = r0 + i < rows ? a : 0.0f;
+                if (r0 + i < rows) {
+                    rowq[(size_t(p) * N + n0 + r0 + i) * 2] = D;
+                    rowq[(size_t(p) * N + n0 + r0 + i) * 2 + 1] = a;
+                }
+            }
+        }
+        // what the tile's queries send: gamma^Q_i dO_i / D_i and -gamma^Q_i a'_i (rows k, columns c)
+        float* out = tsend + (size_t(p) * NT + tile) * E;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int k0 = kb * kKB;
+            __syncthreads();  // Dv, Av visible; the previous block is consumed
+            load_gamma_block(gqp, n0, rows, K, k0, Gq);
+            __syncthreads();
+            float bv[4][4] = {}, bz[4] = {};
+#pragma unroll 4
+            for (int t = 0; t < rows; ++t) {
+                float ga[4], ya[4];
+                unpack(lds4(Gq + t * kLB + r0), ga);
+                unpack(lds4(Yr + t * LY + (m0 < dv ? m0 : 0)), ya);
+                const float rD = 1.0f / Dv[t], a = Av[t];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bz[i] = fmaf(-ga[i], a, bz[i]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bv[i][j] = fmaf(ga[i], ya[j] * rD, bv[i][j]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int k = k0 + r0 + i;
+                if (k >= K) continue;
+                if (m0 < dv)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) out[size_t(k) * dv + m0 + j] = bv[i][j];
+                if (m0 == 0) out[size_t(K) * dv + k] = bz[i];
+            }
+        }
+    }
+}
+
+template <int KB>
+size_t kbc_qrows_lds_bytes(int dv) {
+    return size_t(2 * kBT * kLB + kKB * kLB + kKB * (dv + 4) + kKB + 2 * kBT * (dv + 4) + 2 * kBT) * sizeof(float);
+}
+
+// Causal key rows, grid (G, P): dV_j = gamma^K_j . S + sum_{i >= j} C_ij dO'_i (an output) and
+// w_j = V_j . dV_j + gamma^K_j . S_Z - sum_{i >= j} C_ij a'_i, S = tsend of the tile (what the
+// later tiles' queries send).
+template <int KB>
+__global__ void __launch_bounds__(kThreads)
+    f32_bwdc_kb_krows_kernel(const float* __restrict__ V, const float* __restrict__ dO, int64_t N, int dv, int K,
+                             int64_t seg, const float* __restrict__ gk, const float* __restrict__ tsend,
+                             const float* __restrict__ cbuf, const float* __restrict__ rowq, float* __restrict__ dV,
+                             float* __restrict__ roww) {
+    extern __shared__ float lds[];
+    const int64_t p = blockIdx.y;
+    const int gi = blockIdx.x;
+    const int tid = threadIdx.x, r0 = (tid >> 4) * 4, m0 = (tid & 15) * 4;
+    const int LY = dv + 4, NT = int((N + kBT - 1) / kBT);
+    const size_t E = size_t(K) * (dv + 1);
+    float* Gk = lds;                // [64][kLB] gamma^K of a block, rows j
+    float* Sb = Gk + kBT * kLB;     // [kKB][dv + 4] a block of S
+    float* Zb = Sb + kKB * LY;      // [kKB]
+    float* Cm = Zb + kKB;           // [64][kLB] C of the tile (rows i, columns j)
+    float* Yr = Cm + kBT * kLB;     // [64][dv + 4] dO' rows
+    float* Av = Yr + kBT * LY;      // [64] a'
+    const float* gkp = gk + size_t(p) * N * K;
+    const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
+    for (int64_t n0 = lo; n0 < hi; n0 += kBT) {
+        const int rows = int(min<int64_t>(kBT, hi - n0)), tile = int(n0 / kBT);
+        const float* sp = tsend + (size_t(p) * NT + tile) * E;
+        __syncthreads();
+        for (int i = tid; i < kBT * (kBT / 4); i += kThreads) {
+            const int t = i / (kBT / 4), jq = (i - t * (kBT / 4)) * 4;
+            *reinterpret_cast<float4*>(Cm + t * kLB + jq) =
+                t < rows ? *reinterpret_cast<const float4*>(cbuf + ((size_t(p) * NT + tile) * kBT + t) * kBT + jq)
+                         : make_float4(0, 0, 0, 0);
+        }
+        for (int t = tid; t < kBT; t += kThreads) Av[t] = t < rows ? rowq[(size_t(p) * N + n0 + t) * 2 + 1] : 0.0f;
+        for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
+            const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
+            float4 v = make_float4(0, 0, 0, 0);
+            if (t < rows) {
+                v = *reinterpret_cast<const float4*>(dO + (size_t(p) * N + n0 + t) * dv + cc);
+                const float rD = 1.0f / rowq[(size_t(p) * N + n0 + t) * 2];
+                v.x *= rD, v.y *= rD, v.z *= rD, v.w *= rD;
+            }
+            *reinterpret_cast<float4*>(Yr + t * LY + cc) = v;
+        }
+        float nv[4][4] = {}, ez[4] = {};
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int k0 = kb * kKB;
+            __syncthreads();  // the previous block is consumed (and the tile's rows are in place)
+            load_gamma_block(gkp, n0, rows, K, k0, Gk);
+            for (int i = tid; i < kKB * (dv / 4); i += kThreads) {
+                const int kl = i / (dv / 4), cc = (i - kl * (dv / 4)) * 4, k = k0 + kl;
+                *reinterpret_cast<float4*>(Sb + kl * LY + cc) =
+                    k < K ? *reinterpret_cast<const float4*>(sp + size_t(k) * dv + cc) : make_float4(0, 0, 0, 0);
+            }
+            for (int kl = tid; kl < kKB; kl += kThreads) Zb[kl] = k0 + kl < K ? sp[size_t(K) * dv + k0 + kl] : 0.0f;
+            __syncthreads();
+#pragma unroll 4
+            for (int kl = 0; kl < kKB; ++kl) {
+                float ga[4], sa[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ga[i] = Gk[(r0 + i) * kLB + kl];
+                unpack(lds4(Sb + kl * LY + (m0 < dv ? m0 : 0)), sa);
+                const float z = Zb[kl];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ez[i] = fmaf(ga[i], z, ez[i]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ga[i], sa[j], nv[i][j]);
+                }
+            }
+        }
+        // the tile's own queries (i >= j): rows j = r0.. of C's columns
+#pragma unroll 4
+        for (int i = 0; i < rows; ++i) {
+            float ca[4], ya[4];
+            unpack(lds4(Cm + i * kLB + r0), ca);
+            unpack(lds4(Yr + i * LY + (m0 < dv ? m0 : 0)), ya);
+            const float a = Av[i];
+#pragma unroll
+            for (int jr = 0; jr < 4; ++jr) {
+                ez[jr] = fmaf(-ca[jr], a, ez[jr]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) nv[jr][c] = fmaf(ca[jr], ya[c], nv[jr][c]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t n = n0 + r0 + i;
+            float dot = 0.0f;
+            if (m0 < dv && r0 + i < rows) {
+                const float4 v = *reinterpret_cast<const float4*>(V + (size_t(p) * N + n) * dv + m0);
+                dot = v.x * nv[i][0] + v.y * nv[i][1] + v.z * nv[i][2] + v.w * nv[i][3];
+                *reinterpret_cast<float4*>(dV + (size_t(p) * N + n) * dv + m0) =
+                    make_float4(nv[i][0], nv[i][1], nv[i][2], nv[i][3]);
+            }
+            dot = sum16(dot);
+            if ((tid & 15) == 0 && r0 + i < rows) roww[size_t(p) * N + n] = dot + ez[i];
+        }
+    }
+}
+
+template <int KB>
+size_t kbc_krows_lds_bytes(int dv) {
+    return size_t(kBT * kLB + kKB * (dv + 4) + kKB + kBT * kLB + kBT * (dv + 4) + kBT) * sizeof(float);
+}
+
+size_t kbc_block_lds_bytes(int dr, int dv) {
+    return size_t(2 * kBT * kLB + kBT * (dv + 4) + kBT * kLB + kBT * kLB + dv * kLB + kKB + kBT * (dr + 4) +
+                  2 * kKB * (dr + 4) + 3 * kBT) *
+           sizeof(float);
+}
+
+// Causal block passes, grid (G, P, KB): component block kb = blockIdx.z of split g of problem p.
+//   QUERY: X = X_Q; own responsibilities gown = gamma^Q, other = gamma^K; tstate: the memory before
+//     each tile; w = eps a';
+//   key: X = X_K; gown = gamma^K, other = gamma^Q; tstate: what the later tiles' queries send;
+//     w = roww.
+// Both: the block's entries of the moment record and its share of dX (as the bidirectional pass).
+template <bool QUERY>
+__global__ void __launch_bounds__(kThreads)
+    f32_bwdc_kb_block_kernel(const float* __restrict__ X, const float* __restrict__ V, const float* __restrict__ dO,
+                             int64_t N, int H, int dr, int dv, int K, int64_t seg, int G, const double* __restrict__ inv,
+                             const float* __restrict__ mu, const float* __restrict__ tstate, float eps,
+                             const float* __restrict__ gown, const float* __restrict__ gother,
+                             const float* __restrict__ rowq, const float* __restrict__ roww,
+                             float* __restrict__ param_part, float* __restrict__ dX_part) {
+    extern __shared__ float lds[];
+    const int64_t p = blockIdx.y;
+    const int gi = blockIdx.x, kb = blockIdx.z, h = int(p % H);
+    const int tid = threadIdx.x, r0 = (tid >> 4) * 4, m0 = (tid & 15) * 4;
+    const int LY = dv + 4, LX = dr + 4, k0 = kb * kKB, NT = int((N + kBT - 1) / kBT);
+    const size_t E = size_t(K) * (dv + 1);
+    float* Gb = lds;                  // [64][kLB] own responsibilities of the block
+    float* Go = Gb + kBT * kLB;       // [64][kLB] the other side's, same positions
+    float* Yr = Go + kBT * kLB;       // [64][dv + 4] dO' rows
+    float* VD = Yr + kBT * LY;        // [64][kLB]: V^T ([dv][.]) until g is formed, then ds
+    float* Am = VD + kBT * kLB;       // [64][kLB] A (rows i, columns j)
+    float* MT = Am + kBT * kLB;       // [dv][kLB] the tile's state block, transposed
+    float* Zb = MT + dv * kLB;        // [kKB]
+    float* Xr = Zb + kKB;             // [64][dr + 4] x rows
+    float* muR = Xr + kBT * LX;       // [kKB][dr + 4] mu of the block
+    float* ivR = muR + kKB * LX;      // [kKB][dr + 4] 1 / sigma2 of the block
+    float* Av = ivR + kKB * LX;       // [64] a'
+    float* Wv = Av + kBT;             // [64] w
+    float* Dv = Wv + kBT;             // [64] D
+    const double* ih = inv + size_t(h) * K * dr;
+    const float* mh = mu + size_t(h) * K * dr;
+    for (int i = tid; i < kKB * dr; i += kThreads) {
+        const int kl = i / dr, d = i - kl * dr, k = k0 + kl;
+        muR[kl * LX + d] = k < K ? mh[size_t(k) * dr + d] : 0.0f;
+        ivR[kl * LX + d] = k < K ? float(ih[size_t(k) * dr + d]) : 0.0f;
+    }
+    __syncthreads();
+    const bool mom = r0 < dr;
+    float mreg[4][4], s1[4][4] = {}, s2[4][4] = {}, s0[4] = {};
+    if (mom)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mreg[i][j] = muR[(m0 + j) * LX + r0 + i];
+    const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
+    const float* Xp = X + size_t(p) * N * dr;
+    const float* gop = gown + size_t(p) * N * K;
+    const float* gtp = gother + size_t(p) * N * K;
+    float* dXp = dX_part + (size_t(kb) * gridDim.y + p) * N * dr;
+    for (int64_t n0 = lo; n0 < hi; n0 += kBT) {
+        const int rows = int(min<int64_t>(kBT, hi - n0)), tile = int(n0 / kBT);
+        const float* mp = tstate + (size_t(p) * NT + tile) * E;
+        __syncthreads();  // the previous tile's reads are done
+        load_gamma_block(gop, n0, rows, K, k0, Gb);
+        load_gamma_block(gtp, n0, rows, K, k0, Go);
+        for (int t = tid; t < kBT; t += kThreads) {
+            const float D = t < rows ? rowq[(size_t(p) * N + n0 + t) * 2] : 1.0f;
+            const float a = t < rows ? rowq[(size_t(p) * N + n0 + t) * 2 + 1] : 0.0f;
+            Dv[t] = D;
+            Av[t] = a;
+            Wv[t] = QUERY ? eps * a : (t < rows ? roww[size_t(p) * N + n0 + t] : 0.0f);
+        }
+        for (int i = tid; i < kBT * (dr / 4); i += kThreads) {
+            const int t = i / (dr / 4), d = (i - t * (dr / 4)) * 4;
+            *reinterpret_cast<float4*>(Xr + t * LX + d) =
+                t < rows ? *reinterpret_cast<const float4*>(Xp + (n0 + t) * dr + d) : make_float4(0, 0, 0, 0);
+        }
+        for (int i = tid; i < kKB * dv; i += kThreads) {
+            const int kl = i / dv, cc = i - kl * dv, k = k0 + kl;
+            MT[cc * kLB + kl] = k < K ? mp[size_t(k) * dv + cc] : 0.0f;
+        }
+        for (int kl = tid; kl < kKB; kl += kThreads) Zb[kl] = k0 + kl < K ? mp[size_t(K) * dv + k0 + kl] : 0.0f;
+        __syncthreads();  // Dv before the scaled rows
+        for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
+            const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
+            float4 o = make_float4(0, 0, 0, 0), v = o;
+            if (t < rows) {
+                const size_t off = (size_t(p) * N + n0 + t) * dv + cc;
+                o = *reinterpret_cast<const float4*>(dO + off);
+                v = *reinterpret_cast<const float4*>(V + off);
+                const float rD = 1.0f / Dv[t];
+                o.x *= rD, o.y *= rD, o.z *= rD, o.w *= rD;
+            }
+            *reinterpret_cast<float4*>(Yr + t * LY + cc) = o;
+            VD[(cc + 0) * kLB + t] = v.x;
+            VD[(cc + 1) * kLB + t] = v.y;
+            VD[(cc + 2) * kLB + t] = v.z;
+            VD[(cc + 3) * kLB + t] = v.w;
+        }
+        __syncthreads();
+        {   // A_ij = dO'_i . V_j - a'_i for j <= i (rows i = r0.., columns j = m0..)
+            float aa[4][4] = {};
+#pragma unroll 4
+            for (int cc = 0; cc < dv; ++cc) {
+                float ya[4], va[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ya[i] = Yr[(r0 + i) * LY + cc];
+                unpack(lds4(VD + cc * kLB + m0), va);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) aa[i][j] = fmaf(ya[i], va[j], aa[i][j]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[j] = (m0 + j <= r0 + i && r0 + i < rows && m0 + j < rows) ? aa[i][j] - Av[r0 + i] : 0.0f;
+                put4(Am + (r0 + i) * kLB + m0, o[0], o[1], o[2], o[3]);
+            }
+        }
+        __syncthreads();  // A in LDS
+        float gg[4][4] = {};
+        if (QUERY) {  // rows i = r0.., components k = m0..
+#pragma unroll 4
+            for (int cc = 0; cc < dv; ++cc) {
+                float ya[4], ma[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ya[i] = Yr[(r0 + i) * LY + cc];
+                unpack(lds4(MT + cc * kLB + m0), ma);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(ya[i], ma[j], gg[i][j]);
+            }
+#pragma unroll 4
+            for (int jj = 0; jj < rows; ++jj) {  // sum_{j <= i} A_ij gamma^K_jk
+                float aa[4], ka[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) aa[i] = Am[(r0 + i) * kLB + jj];
+                unpack(lds4(Go + jj * kLB + m0), ka);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(aa[i], ka[j], gg[i][j]);
+            }
+        } else {  // rows j = r0.., components k = m0..
+#pragma unroll 4
+            for (int cc = 0; cc < dv; ++cc) {
+                float va[4], ma[4];
+                unpack(lds4(VD + cc * kLB + r0), va);
+                unpack(lds4(MT + cc * kLB + m0), ma);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(va[i], ma[j], gg[i][j]);
+            }
+#pragma unroll 4
+            for (int ii = 0; ii < rows; ++ii) {  // sum_{i >= j} A_ij gamma^Q_ik
+                float aa[4], qa[4];
+                unpack(lds4(Am + ii * kLB + r0), aa);
+                unpack(lds4(Go + ii * kLB + m0), qa);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(aa[i], qa[j], gg[i][j]);
+            }
+        }
+        float za[4];
+        unpack(lds4(Zb + m0), za);
+        float ds[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float ga[4];
+            unpack(lds4(Gb + (r0 + i) * kLB + m0), ga);
+            const float w = Wv[r0 + i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float g = QUERY ? gg[i][j] - Av[r0 + i] * za[j] : gg[i][j] + za[j];
+                ds[i][j] = ga[j] * (g - w);
+            }
+        }
+        __syncthreads();  // V^T is consumed: ds takes its place
+#pragma unroll
+        for (int i = 0; i < 4; ++i) put4(VD + (r0 + i) * kLB + m0, ds[i][0], ds[i][1], ds[i][2], ds[i][3]);
+        __syncthreads();  // ds in LDS
+        if (mom)  // moments (rows d = r0.., columns k = m0..), direct (centred) form
+#pragma unroll 4
+            for (int t = 0; t < rows; ++t) {
+                float xa[4], da[4];
+                unpack(lds4(Xr + t * LX + r0), xa);
+                unpack(lds4(VD + t * kLB + m0), da);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    s0[j] += da[j];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float df = xa[i] - mreg[i][j], w = da[j] * df;
+                        s1[i][j] += w;
+                        s2[i][j] = fmaf(w, df, s2[i][j]);
+                    }
+                }
+            }
+        if (m0 < dr) {  // this block's share of dX (rows t = r0.., columns d = m0..)
+            float xa[4][4], acc[4][4] = {};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) unpack(lds4(Xr + (r0 + i) * LX + m0), xa[i]);
+            const int kn = min(kKB, K - k0);
+#pragma unroll 4
+            for (int kl = 0; kl < kn; ++kl) {
+                float ma[4], ia[4], da[4];
+                unpack(lds4(muR + kl * LX + m0), ma);
+                unpack(lds4(ivR + kl * LX + m0), ia);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) da[i] = VD[(r0 + i) * kLB + kl];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(da[i] * ia[j], xa[i][j] - ma[j], acc[i][j]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (r0 + i < rows)
+                    *reinterpret_cast<float4*>(dXp + (n0 + r0 + i) * dr + m0) =
+                        make_float4(-acc[i][0], -acc[i][1], -acc[i][2], -acc[i][3]);
+        }
+    }
+    float* pp = param_part + (size_t(p) * G + gi) * size_t(2 * K * dr + K);
+    if (mom)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int k = k0 + m0 + j;
+            if (k >= K) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                pp[size_t(k) * dr + r0 + i] = s1[i][j];
+                pp[size_t(K) * dr + size_t(k) * dr + r0 + i] = s2[i][j];
+            }
+            if (r0 == 0) pp[2 * size_t(K) * dr + k] = s0[j];
+        }
 }
 
 // Grid (G segments, P).  QUERY walks the segment's tiles forward from the memory before the
@@ -2027,11 +2559,145 @@ bool bwdc_tiled_applies(const Plan& p) {
            bwd_tiled_lds_bytes(BWD_CKEY, K, dr, dv) <= kMaxLds;
 }
 
+// The K-blocked causal passes where the register-tiled ones do not fit.
+bool bwdc_kb_applies(const Plan& p) {
+    return !bwdc_tiled_applies(p) && p.K <= 256 && p.dr % 4 == 0 && p.dv % 4 == 0 && p.dr <= 64 && p.dv <= 64 &&
+           p.N > 0;
+}
+
+namespace {
+
+// The K-blocked causal passes' buffers: per tile of 64 positions the memory before it and what
+// the later tiles' queries send ([P][NT][K (dv + 1)] each, NT = ceil(N / 64)) and C
+// ([P][NT][64][64]); the responsibilities of both sides ([P][N][K]), (D, a') per row, w per key
+// row and the blocks' shares of dX ([KB][P][N][dr]).
+struct KbcBuffers {
+    float *tmem, *tsend, *cbuf, *gq, *gk, *rowq, *roww, *dxpart;
+};
+size_t kbc_bytes(const Plan& p, KbcBuffers* b, char* base) {
+    const size_t P = size_t(p.P), K = size_t(p.K), N = size_t(p.N), NT = (N + kBT - 1) / kBT;
+    const size_t E = K * size_t(p.dv + 1);
+    const size_t sizes[8] = {round_up(P * NT * E * 4, 256),         round_up(P * NT * E * 4, 256),
+                             round_up(P * NT * kBT * kBT * 4, 256), round_up(P * N * K * 4, 256),
+                             round_up(P * N * K * 4, 256),          round_up(P * N * 2 * 4, 256),
+                             round_up(P * N * 4, 256),
+                             round_up(size_t(kb_blocks(p.K)) * P * N * size_t(p.dr) * 4, 256)};
+    float** outs[8] = {b ? &b->tmem : nullptr, b ? &b->tsend : nullptr, b ? &b->cbuf : nullptr,
+                       b ? &b->gq : nullptr,   b ? &b->gk : nullptr,    b ? &b->rowq : nullptr,
+                       b ? &b->roww : nullptr, b ? &b->dxpart : nullptr};
+    size_t off = 0;
+    for (int i = 0; i < 8; ++i) {
+        if (b) *outs[i] = reinterpret_cast<float*>(base + off);
+        off += sizes[i];
+    }
+    return off;
+}
+
+template <typename F>
+hipError_t with_kbc(int KB, F&& f) {
+    if (KB == 1) return f(std::integral_constant<int, 1>());
+    return with_kb(KB, f);
+}
+
+template <int KB>
+hipError_t kbc_allow_lds_for() {
+    const void* fns[] = {(const void*)f32_bwd_kb_rows_kernel<KB, KB_KEY>, (const void*)f32_bwd_kb_rows_kernel<KB, KB_GAMMA>,
+                         (const void*)f32_bwdc_kb_qrows_kernel<KB>, (const void*)f32_bwdc_kb_krows_kernel<KB>};
+    for (const void* f : fns) {
+        hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
+        if (r != hipSuccess) return r;
+    }
+    return hipSuccess;
+}
+
+hipError_t kbc_allow_lds() {
+    static const hipError_t e = [] {
+        hipError_t r;
+        if ((r = kbc_allow_lds_for<1>()) != hipSuccess || (r = kbc_allow_lds_for<2>()) != hipSuccess ||
+            (r = kbc_allow_lds_for<3>()) != hipSuccess || (r = kbc_allow_lds_for<4>()) != hipSuccess)
+            return r;
+        const void* fns[] = {(const void*)f32_bwdc_kb_block_kernel<true>, (const void*)f32_bwdc_kb_block_kernel<false>};
+        for (const void* f : fns)
+            if ((r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds))) != hipSuccess)
+                return r;
+        return hipSuccess;
+    }();
+    return e;
+}
+
+// The causal backward in K-blocked passes: tile aggregates of the key side (and Gamma_K), their
+// exclusive prefix from state_in, Gamma_Q, the causal query rows (C, D, a', what each tile's
+// queries send), its exclusive suffix from dstate_out (the total into dstate_in), the query
+// blocks, the key rows (dV, w) and the key blocks.
+hipError_t f32_backward_causal_kb(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
+                                  const float* pi, float eps, const float* dO, float* dXQ, float* dXK, float* dV,
+                                  float* dmu, float* ds2, float* dpi, const F32Params& v, float* ppart,
+                                  float* ppart_key, char* kbase, hipStream_t st, const float* state_in,
+                                  const float* dstate_out, float* dstate_in) {
+    hipError_t e = kbc_allow_lds();
+    if (e != hipSuccess) return e;
+    KbcBuffers b{};
+    kbc_bytes(p, &b, kbase);
+    const int H = int(p.H), dr = int(p.dr), dv = int(p.dv), K = int(p.K), G = int(p.G), KB = kb_blocks(p.K);
+    const int NT = int((p.N + kBT - 1) / kBT), Ei = int(size_t(p.K) * size_t(p.dv + 1));
+    const int64_t tseg = kBT;
+    const dim3 tgrid(unsigned(NT), unsigned(p.P)), bgrid(unsigned(p.G), unsigned(p.P), unsigned(KB));
+    const dim3 egrid(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P));
+    const float* cnone = nullptr;
+    float* none = nullptr;
+    const size_t blds = kbc_block_lds_bytes(dr, dv);
+    auto sum_dx = [&](float* dX) {
+        const size_t n = size_t(p.P) * size_t(p.N) * size_t(dr);
+        GMA_LAUNCH("f32_bwd_dx_sum", f32_bwd_kb_sum_kernel, dim3(unsigned((n / 4 + kThreads - 1) / kThreads)),
+                   dim3(kThreads), 0, st, static_cast<const float*>(b.dxpart), KB, n, dX);
+        return hipGetLastError();
+    };
+    return with_kbc(KB, [&](auto KBc) -> hipError_t {
+        constexpr int KBT = decltype(KBc)::value;
+        const size_t rlds = kb_rows_lds_bytes<KBT>(dr, dv);
+        hipError_t r;
+        GMA_LAUNCH("f32_bwdc_aggregate", (f32_bwd_kb_rows_kernel<KBT, KB_KEY>), tgrid, dim3(kThreads), rlds, st, XK, V,
+                   p.N, H, dr, dv, K, tseg, NT, v.c, v.inv, mu, cnone, eps, b.gk, b.tmem, none);
+        if ((r = hipGetLastError()) != hipSuccess) return r;
+        GMA_LAUNCH("f32_bwdc_prefix", f32_prefix_kernel, egrid, dim3(kThreads), 0, st, b.tmem, NT, Ei, state_in, K, dv);
+        if ((r = hipGetLastError()) != hipSuccess) return r;
+        GMA_LAUNCH("f32_bwdc_query_gamma", (f32_bwd_kb_rows_kernel<KBT, KB_GAMMA>), tgrid, dim3(kThreads), rlds, st,
+                   XQ, cnone, p.N, H, dr, dv, K, tseg, NT, v.c, v.inv, mu, cnone, eps, b.gq, none, none);
+        if ((r = hipGetLastError()) != hipSuccess) return r;
+        GMA_LAUNCH("f32_bwdc_query_rows", f32_bwdc_kb_qrows_kernel<KBT>, tgrid, dim3(kThreads),
+                   kbc_qrows_lds_bytes<KBT>(dv), st, V, dO, p.N, dv, K, tseg, static_cast<const float*>(b.gq),
+                   static_cast<const float*>(b.gk), static_cast<const float*>(b.tmem), eps, b.cbuf, b.rowq, b.tsend);
+        if ((r = hipGetLastError()) != hipSuccess) return r;
+        GMA_LAUNCH("f32_bwdc_suffix", f32_suffix_kernel, egrid, dim3(kThreads), 0, st, b.tsend, NT, Ei, dstate_out,
+                   dstate_in, K, dv);
+        if ((r = hipGetLastError()) != hipSuccess) return r;
+        GMA_LAUNCH("f32_bwdc_query", f32_bwdc_kb_block_kernel<true>, bgrid, dim3(kThreads), blds, st, XQ, V, dO, p.N,
+                   H, dr, dv, K, p.seg, G, v.inv, mu, static_cast<const float*>(b.tmem), eps,
+                   static_cast<const float*>(b.gq), static_cast<const float*>(b.gk), static_cast<const float*>(b.rowq),
+                   cnone, ppart, b.dxpart);
+        if ((r = hipGetLastError()) != hipSuccess) return r;
+        if ((r = sum_dx(dXQ)) != hipSuccess) return r;
+        GMA_LAUNCH("f32_bwdc_key_rows", f32_bwdc_kb_krows_kernel<KBT>, tgrid, dim3(kThreads), kbc_krows_lds_bytes<KBT>(dv),
+                   st, V, dO, p.N, dv, K, tseg, static_cast<const float*>(b.gk), static_cast<const float*>(b.tsend),
+                   static_cast<const float*>(b.cbuf), static_cast<const float*>(b.rowq), dV, b.roww);
+        if ((r = hipGetLastError()) != hipSuccess) return r;
+        GMA_LAUNCH("f32_bwdc_key", f32_bwdc_kb_block_kernel<false>, bgrid, dim3(kThreads), blds, st, XK, V, dO, p.N,
+                   H, dr, dv, K, p.seg, G, v.inv, mu, static_cast<const float*>(b.tsend), eps,
+                   static_cast<const float*>(b.gk), static_cast<const float*>(b.gq), static_cast<const float*>(b.rowq),
+                   static_cast<const float*>(b.roww), ppart_key, b.dxpart);
+        if ((r = hipGetLastError()) != hipSuccess) return r;
+        if ((r = sum_dx(dXK)) != hipSuccess) return r;
+        return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
+    });
+}
+
+}  // namespace
+
 size_t f32_backward_causal_extra_bytes(const Plan& p) {
     const size_t E = size_t(p.K) * size_t(p.dv + 1);
     return round_up(size_t(p.P * p.G) * E * 4, 256) + round_up(size_t(p.P * p.N) * 2 * 4, 256) +
            round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256) +
-           (bwdc_tiled_applies(p) ? 2 * gamma_cache_bytes(p) : 0);
+           (bwdc_tiled_applies(p) ? 2 * gamma_cache_bytes(p) : 0) + (bwdc_kb_applies(p) ? kbc_bytes(p, nullptr, nullptr) : 0);
 }
 
 hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, const float* V, const float* mu,
@@ -2071,6 +2737,9 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
     float* gk_cache = reinterpret_cast<float*>(reinterpret_cast<char*>(ppart) +
                                                round_up(2 * size_t(p.P * p.G) * size_t(2 * p.K * p.dr + p.K) * 4, 256));
     float* gq_cache = reinterpret_cast<float*>(reinterpret_cast<char*>(gk_cache) + gamma_cache_bytes(p));
+    if (bwdc_kb_applies(p))
+        return f32_backward_causal_kb(p, XQ, XK, V, mu, pi, eps, dO, dXQ, dXK, dV, dmu, ds2, dpi, v, ppart, ppart_key,
+                                      reinterpret_cast<char*>(gk_cache), st, state_in, dstate_out, dstate_in);
     float* none = nullptr;
     const float* cnone = nullptr;
     const bool tiled = bwdc_tiled_applies(p);

@@ -233,6 +233,11 @@ CAUSAL_CASES = [
     case(333, 109, B=2, H=1, d_r=64, d_v=64, K=32),     # ragged tail, one tile per segment
     case(4100, 110, B=4, H=16, d_r=64, d_v=48, K=20),   # several tiles per segment, K below a row group
     case(500, 111, B=1, H=2, d_r=64, d_v=64, K=256),
+    # the K-blocked causal passes (K <= 256; d_r, d_v <= 64, multiples of 4)
+    case(1500, 113, B=2, H=2, d_r=32, d_v=48, K=200),    # a partial last component block
+    case(130, 114, B=1, H=3, d_r=16, d_v=16, K=66),      # K not a multiple of 4, ragged tail
+    case(1000, 115, B=1, H=2, d_r=64, d_v=64, K=64),     # one component block
+    case(4500, 112, B=2, H=16, d_r=16, d_v=16, K=72),    # two tiles per segment, ragged tail
 ]
 
 
@@ -377,8 +382,9 @@ STATE_CASES = [
     case(700, 141),                                         # tiled causal passes
     case(1000, 142, B=2, H=2, d_r=64, d_v=64, K=32),
     case(500, 143, B=2, H=3, d_r=7, d_v=5, K=13),          # one element per thread (LDS tables)
-    case(300, 144, d_r=32, d_v=64, K=64),                  # one element per thread (general)
-    case(200, 145, B=1, H=1, d_r=128, d_v=128, K=256),
+    case(300, 144, d_r=32, d_v=64, K=64),                  # K-blocked, one component block
+    case(200, 145, B=1, H=1, d_r=128, d_v=128, K=256),     # one element per thread (general)
+    case(260, 147, B=1, H=2, d_r=64, d_v=64, K=200),       # K-blocked, four component blocks
 ]
 
 
@@ -398,10 +404,13 @@ def test_backward_causal_state_parity(w):
     check_all({k: to_np(v) for k, v in g.items()}, ref, mag, keys=KEYS + ("dstate_in",), where="state-" + cid(w))
 
 
-def test_backward_causal_state_chained_calls_equal_whole_sequence():
+@pytest.mark.parametrize("dims", [(32, 32, 32), (32, 32, 128)], ids=lambda d: "dr%d-dv%d-K%d" % d)
+def test_backward_causal_state_chained_calls_equal_whole_sequence(dims):
     """Three calls over consecutive pieces, forward state carried and dstate_in fed back as the
-    previous call's dstate_out, give the whole-sequence backward."""
-    w = case(1000, 146, B=2, H=2, d_r=32, d_v=32, K=32, causal=True)
+    previous call's dstate_out, give the whole-sequence backward (register-tiled passes at K = 32,
+    K-blocked at K = 128)."""
+    dr, dv, K = dims
+    w = case(1000, 146, B=2, H=2, d_r=dr, d_v=dv, K=K, causal=True)
     inp = make_inputs(w)
     d_o = upstream(w, 1146)
     d = to_device(inp)
