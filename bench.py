@@ -356,6 +356,24 @@ def alg_bytes_per_token_head(w, kernel: str) -> float:
         return e * w.d_r
     if w.backward:  # the register-tiled passes keep the responsibilities (fp32, K per row) between passes
         g = 4 * w.K
+        T = 64  # positions per tile of the causal K-blocked passes (C: T fp32 per row)
+        # the K-blocked passes cache both sides' responsibilities; the block passes read them back
+        if kernel.endswith("_kb_write") or kernel.endswith("_kb_aggregate"):
+            return e * (w.d_r + w.d_v) + g              # X_K and V in, Gamma_K out
+        if kernel.endswith("_kb_query_gamma"):
+            return e * w.d_r + g                        # X_Q in, Gamma_Q out
+        if kernel.endswith("_bwd_kb_query_rows"):
+            return e * (w.d_r + w.d_v) + g + 8          # X_Q and dO in, Gamma_Q and (D, a') out
+        if kernel.endswith("_bwdc_kb_query_rows"):
+            return 2 * e * w.d_v + 2 * g + 8 + 4 * T    # V and dO in, both Gammas in, (D, a') and C out
+        if kernel.endswith("_bwd_kb_key_rows"):
+            return 2 * e * w.d_v + g + 4                # V in, dV out, Gamma_K in, w out
+        if kernel.endswith("_bwdc_kb_key_rows"):
+            return 3 * e * w.d_v + g + 4 + 4 * T        # V and dO in, dV out, Gamma_K and C in, w out
+        if kernel.endswith("_bwd_kb_query") or kernel.endswith("_bwd_kb_key"):
+            return e * (2 * w.d_r + w.d_v) + g          # X and dO (or V) in, dX out, Gamma in
+        if kernel.endswith("_bwdc_kb_query") or kernel.endswith("_bwdc_kb_key"):
+            return e * (2 * w.d_r + 2 * w.d_v) + 2 * g  # X, V and dO in, dX out, both Gammas in
         if kernel.endswith("_bwdc_aggregate"):
             return e * (w.d_r + w.d_v) + g          # X_K and V in, Gamma_K out
         if kernel.endswith("_bwdc_query"):
@@ -394,6 +412,26 @@ def alg_flops_per_token_head(w, kernel: str) -> float:
         return 0.0
     K, dr, dv = w.K, w.d_r, w.d_v
     T = 64  # positions per tile of the causal passes: the masked in-tile products cost T/2 per row
+    # the K-blocked passes: row passes form the responsibilities and the per-row sums, block
+    # passes (one component block each) the score gradient, moments and dX shares
+    if kernel.endswith("_kb_write") or kernel.endswith("_kb_aggregate"):
+        return 3 * K * dr + 2 * K * dv + 4 * K
+    if kernel.endswith("_kb_query_gamma"):
+        return 3 * K * dr + 3 * K
+    if kernel.endswith("_bwd_kb_query_rows"):     # scores, N_i and D_i, a'_i
+        return 3 * K * dr + 2 * K * dv + 6 * K + 2 * dv
+    if kernel.endswith("_bwdc_kb_query_rows"):    # C, N_i and D_i, C V, a'_i, what the row sends
+        return 4 * K * dv + T * K + T * dv + 4 * K + 2 * dv
+    if kernel.endswith("_bwd_kb_key_rows"):       # dV_j and w_j
+        return 2 * K * dv + 2 * K + 2 * dv
+    if kernel.endswith("_bwdc_kb_key_rows"):      # dV_j and w_j with the in-tile queries
+        return 2 * K * dv + T * dv + 2 * K + T + 2 * dv
+    if kernel.endswith("_bwd_kb_query"):          # g, ds, moments, dX, the memory gradient
+        return 9 * K * dr + 4 * K * dv + 5 * K
+    if kernel.endswith("_bwd_kb_key"):
+        return 9 * K * dr + 2 * K * dv + 4 * K
+    if kernel.endswith("_bwdc_kb_query") or kernel.endswith("_bwdc_kb_key"):  # A, g, ds, moments, dX
+        return 9 * K * dr + 2 * K * dv + T * K + T * dv + 4 * K
     if kernel.endswith("_bwdc_aggregate"):
         return 3 * K * dr + 2 * K * dv + 4 * K
     if kernel.endswith("_bwdc_query"):  # the bidirectional query pass and the memory update
@@ -542,6 +580,10 @@ KERNEL_SYMBOL = {"bf16_scan": "gma::bf::scan_kernel", "bf16_bidir": "gma::bf::bi
                  "bf16_decode": "gma::dec::decode_kernel", "bf16_diag": "gma::diag::diag_fused_kernel",
                  "f32_bwd_query": "gma::f32_bwd_tiled_kernel<1>", "f32_bwd_key": "gma::f32_bwd_tiled_kernel<2>",
                  "f32_bwdc_query": "gma::f32_bwd_tiled_kernel<3>", "f32_bwdc_key": "gma::f32_bwd_tiled_kernel<4>",
+                 "f32_bwd_kb_query": "gma::f32_bwd_kb_block_kernel<true>",
+                 "f32_bwd_kb_key": "gma::f32_bwd_kb_block_kernel<false>",
+                 "f32_bwdc_kb_query": "gma::f32_bwdc_kb_block_kernel<true>",
+                 "f32_bwdc_kb_key": "gma::f32_bwdc_kb_block_kernel<false>",
                  "bf16_causal": "gma::bf::causal_kernel", "bf16_causal_aggregate": "gma::bf::write_kernel<64, 1"}
 
 

@@ -1623,27 +1623,27 @@ hipError_t f32_backward_bidir_kb(const Plan& p, const float* XQ, const float* XK
         constexpr int KBT = decltype(KBc)::value;
         const size_t rlds = kb_rows_lds_bytes<KBT>(dr, dv);
         hipError_t e;
-        GMA_LAUNCH("f32_bwd_write", (f32_bwd_kb_rows_kernel<KBT, KB_KEY>), grid, dim3(kThreads), rlds, st, XK, V, p.N, H,
+        GMA_LAUNCH("f32_bwd_kb_write", (f32_bwd_kb_rows_kernel<KBT, KB_KEY>), grid, dim3(kThreads), rlds, st, XK, V, p.N, H,
                    dr, dv, K, p.seg, G, v.c, v.inv, mu, cnone, eps, b.gk, partials, none);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, partials, G, Ei, memory);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        GMA_LAUNCH("f32_bwd_query_rows", (f32_bwd_kb_rows_kernel<KBT, KB_QUERY>), grid, dim3(kThreads), rlds, st, XQ, dO,
+        GMA_LAUNCH("f32_bwd_kb_query_rows", (f32_bwd_kb_rows_kernel<KBT, KB_QUERY>), grid, dim3(kThreads), rlds, st, XQ, dO,
                    p.Nq, H, dr, dv, K, p.seg_q, G, v.c, v.inv, mu, static_cast<const float*>(memory), eps, b.gq, none,
                    b.rowq);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        GMA_LAUNCH("f32_bwd_query", f32_bwd_kb_block_kernel<true>, bgrid, dim3(kThreads), blds, st, XQ, dO, p.Nq, H,
+        GMA_LAUNCH("f32_bwd_kb_query", f32_bwd_kb_block_kernel<true>, bgrid, dim3(kThreads), blds, st, XQ, dO, p.Nq, H,
                    dr, dv, K, p.seg_q, G, v.inv, mu, static_cast<const float*>(memory), eps,
                    static_cast<const float*>(b.gq), static_cast<const float*>(b.rowq), dpart, ppart, b.dxpart);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = sum_dx(p.Nq, dXQ)) != hipSuccess) return e;
         GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, dpart, G, Ei, dmem);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        GMA_LAUNCH("f32_bwd_key_rows", f32_bwd_kb_keyrows_kernel<KBT>, grid, dim3(kThreads),
+        GMA_LAUNCH("f32_bwd_kb_key_rows", f32_bwd_kb_keyrows_kernel<KBT>, grid, dim3(kThreads),
                    size_t(kBT * kLB + kKB * (dv + 4) + kKB) * sizeof(float), st, V, p.N, dv, K, p.seg,
                    static_cast<const float*>(dmem), static_cast<const float*>(b.gk), dV, b.roww);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        GMA_LAUNCH("f32_bwd_key", f32_bwd_kb_block_kernel<false>, bgrid, dim3(kThreads), blds, st, XK, V, p.N, H, dr,
+        GMA_LAUNCH("f32_bwd_kb_key", f32_bwd_kb_block_kernel<false>, bgrid, dim3(kThreads), blds, st, XK, V, p.N, H, dr,
                    dv, K, p.seg, G, v.inv, mu, static_cast<const float*>(dmem), eps, static_cast<const float*>(b.gk),
                    static_cast<const float*>(b.roww), none, ppart_key, b.dxpart);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -2656,32 +2656,32 @@ hipError_t f32_backward_causal_kb(const Plan& p, const float* XQ, const float* X
         constexpr int KBT = decltype(KBc)::value;
         const size_t rlds = kb_rows_lds_bytes<KBT>(dr, dv);
         hipError_t r;
-        GMA_LAUNCH("f32_bwdc_aggregate", (f32_bwd_kb_rows_kernel<KBT, KB_KEY>), tgrid, dim3(kThreads), rlds, st, XK, V,
+        GMA_LAUNCH("f32_bwdc_kb_aggregate", (f32_bwd_kb_rows_kernel<KBT, KB_KEY>), tgrid, dim3(kThreads), rlds, st, XK, V,
                    p.N, H, dr, dv, K, tseg, NT, v.c, v.inv, mu, cnone, eps, b.gk, b.tmem, none);
         if ((r = hipGetLastError()) != hipSuccess) return r;
         GMA_LAUNCH("f32_bwdc_prefix", f32_prefix_kernel, egrid, dim3(kThreads), 0, st, b.tmem, NT, Ei, state_in, K, dv);
         if ((r = hipGetLastError()) != hipSuccess) return r;
-        GMA_LAUNCH("f32_bwdc_query_gamma", (f32_bwd_kb_rows_kernel<KBT, KB_GAMMA>), tgrid, dim3(kThreads), rlds, st,
+        GMA_LAUNCH("f32_bwdc_kb_query_gamma", (f32_bwd_kb_rows_kernel<KBT, KB_GAMMA>), tgrid, dim3(kThreads), rlds, st,
                    XQ, cnone, p.N, H, dr, dv, K, tseg, NT, v.c, v.inv, mu, cnone, eps, b.gq, none, none);
         if ((r = hipGetLastError()) != hipSuccess) return r;
-        GMA_LAUNCH("f32_bwdc_query_rows", f32_bwdc_kb_qrows_kernel<KBT>, tgrid, dim3(kThreads),
+        GMA_LAUNCH("f32_bwdc_kb_query_rows", f32_bwdc_kb_qrows_kernel<KBT>, tgrid, dim3(kThreads),
                    kbc_qrows_lds_bytes<KBT>(dv), st, V, dO, p.N, dv, K, tseg, static_cast<const float*>(b.gq),
                    static_cast<const float*>(b.gk), static_cast<const float*>(b.tmem), eps, b.cbuf, b.rowq, b.tsend);
         if ((r = hipGetLastError()) != hipSuccess) return r;
         GMA_LAUNCH("f32_bwdc_suffix", f32_suffix_kernel, egrid, dim3(kThreads), 0, st, b.tsend, NT, Ei, dstate_out,
                    dstate_in, K, dv);
         if ((r = hipGetLastError()) != hipSuccess) return r;
-        GMA_LAUNCH("f32_bwdc_query", f32_bwdc_kb_block_kernel<true>, bgrid, dim3(kThreads), blds, st, XQ, V, dO, p.N,
+        GMA_LAUNCH("f32_bwdc_kb_query", f32_bwdc_kb_block_kernel<true>, bgrid, dim3(kThreads), blds, st, XQ, V, dO, p.N,
                    H, dr, dv, K, p.seg, G, v.inv, mu, static_cast<const float*>(b.tmem), eps,
                    static_cast<const float*>(b.gq), static_cast<const float*>(b.gk), static_cast<const float*>(b.rowq),
                    cnone, ppart, b.dxpart);
         if ((r = hipGetLastError()) != hipSuccess) return r;
         if ((r = sum_dx(dXQ)) != hipSuccess) return r;
-        GMA_LAUNCH("f32_bwdc_key_rows", f32_bwdc_kb_krows_kernel<KBT>, tgrid, dim3(kThreads), kbc_krows_lds_bytes<KBT>(dv),
+        GMA_LAUNCH("f32_bwdc_kb_key_rows", f32_bwdc_kb_krows_kernel<KBT>, tgrid, dim3(kThreads), kbc_krows_lds_bytes<KBT>(dv),
                    st, V, dO, p.N, dv, K, tseg, static_cast<const float*>(b.gk), static_cast<const float*>(b.tsend),
                    static_cast<const float*>(b.cbuf), static_cast<const float*>(b.rowq), dV, b.roww);
         if ((r = hipGetLastError()) != hipSuccess) return r;
-        GMA_LAUNCH("f32_bwdc_key", f32_bwdc_kb_block_kernel<false>, bgrid, dim3(kThreads), blds, st, XK, V, dO, p.N,
+        GMA_LAUNCH("f32_bwdc_kb_key", f32_bwdc_kb_block_kernel<false>, bgrid, dim3(kThreads), blds, st, XK, V, dO, p.N,
                    H, dr, dv, K, p.seg, G, v.inv, mu, static_cast<const float*>(b.tsend), eps,
                    static_cast<const float*>(b.gk), static_cast<const float*>(b.gq), static_cast<const float*>(b.rowq),
                    static_cast<const float*>(b.roww), ppart_key, b.dxpart);

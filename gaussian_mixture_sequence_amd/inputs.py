@@ -98,6 +98,13 @@ WORKLOADS: Dict[str, Workload] = {
                                         backward=True),
     "bwd_b8h8_n1024_k256_f32": Workload("bwd_b8h8_n1024_k256_f32", False, 8, 8, 1024, 64, 64, 256, "f32", seed=12,
                                         backward=True),
+    # the causal backward at the same dims and component counts
+    "bwdc_b8h8_n1024_k64_f32": Workload("bwdc_b8h8_n1024_k64_f32", True, 8, 8, 1024, 64, 64, 64, "f32", seed=13,
+                                        backward=True),
+    "bwdc_b8h8_n1024_k128_f32": Workload("bwdc_b8h8_n1024_k128_f32", True, 8, 8, 1024, 64, 64, 128, "f32",
+                                         seed=14, backward=True),
+    "bwdc_b8h8_n1024_k256_f32": Workload("bwdc_b8h8_n1024_k256_f32", True, 8, 8, 1024, 64, 64, 256, "f32",
+                                         seed=15, backward=True),
     "cross_b8h8_q4096_k16384": Workload("cross_b8h8_q4096_k16384", False, 8, 8, 4096, 64, 64, 64, "bf16",
                                         seed=5, n_ctx=16384),
 }
