@@ -197,7 +197,12 @@ void layout(Plan* pl) {
     if (io == GMA_BF16 && op == GMA_OP_CAUSAL) p.flags_bytes = round_up(size_t(p.P * p.G) * 8, 256);
     p.off_memory = p.off_partials + p.partials_bytes;
     p.off_flags = p.off_memory + p.memory_bytes;
-    p.total = p.off_flags + p.flags_bytes;
+    // the 256-component causal scan reads back the keys' responsibilities of its key pass
+    p.gk_bytes = (io == GMA_BF16 && op == GMA_OP_CAUSAL && bf16_causal_wide_applies(p))
+                     ? round_up(size_t(p.P) * size_t(p.N) * size_t(p.Kp) * 2, 256)
+                     : 0;
+    p.off_gk = p.off_flags + p.flags_bytes;
+    p.total = p.off_gk + p.gk_bytes;
 }
 
 gma_status_t make_cross_plan(const gma_cross_shape_t& s, gma_dtype_t io, Plan* pl) {

@@ -5,33 +5,39 @@
 // (Eq. 8b): Vt^(i) = sum_{j<=i} gamma^K_j V_j^T, Z^(i) = sum_{j<=i} gamma^K_j,
 // O_i = gamma^Q_i Vt^(i) / (gamma^Q_i Z^(i) + eps), the sums running along the sequence.  The
 // sequence of each (batch, head) problem is cut into G segments; workgroup (s, p) owns segment s:
-//   1. aggregate (segments 0 .. G-2): the segment's own memory, sum over its positions of
-//      gamma^K_j [V_j | 1], chunk by chunk; published for the later segments;
+//   1. key pass: the keys' responsibilities of the segment, chunk by chunk, into the workspace
+//      ([N][256] bf16 per problem), and (segments 0 .. G-2) the segment's own memory, sum over its
+//      positions of gamma^K_j [V_j | 1], published for the later segments;
 //   2. once the aggregates of segments 0 .. s-1 are published (only lower-numbered workgroups,
 //      dispatched no later than this one, so the launch needs no co-residency), the starting
 //      memory is the carried memory plus those aggregates in increasing order;
-//   3. scan: chunks of CH = 32 positions with responsibilities Gq, Gk (bf16, in LDS) and values
-//      Vc:  S = Gq Gk^T kept for key j <= query i,  num = S Vc + Gq Vt,  den = S 1 + Gq Z + eps,
-//      then Vt += Gk^T Vc, Z += Gk^T 1.
+//   3. scan: chunks of CH = 32 positions with responsibilities Gq (scored here), Gk (read back
+//      from the key pass; bf16, in LDS) and values Vc:  S = Gq Gk^T kept for key j <= query i,
+//      num = S Vc + Gq Vt,  den = S 1 + Gq Z + eps, then Vt += Gk^T Vc, Z += Gk^T 1.
+// Each side's scores are formed once: the key pass writes 512 bytes per position and the scan
+// reads them back, in place of a second set of key-side score products and softmax.
 //
 // Two kinds of waves.  Waves w and w + 4 of a workgroup run on the same SIMD, so every SIMD holds
 // one of each and the matrix cores of one overlap the vector work of the other:
 //   score waves 0..3:  wave s holds the score operands of component tiles 2s, 2s + 1 (the 5-term
 //                      split-operand scores of gma_bf16_common.h) and turns the x tiles of the next
 //                      chunk into its responsibilities (softmax statistics combined over the four
-//                      waves through LDS);
+//                      waves through LDS); in the scan they also form the chunk's S tiles and the
+//                      partial sums of Gq Z;
 //   memory waves 4..7: wave 4 + m holds the fp32 memory of value-column tiles m (and m + 4 for
 //                      d_v = 128) as sixteen 16x16 MFMA accumulators each (Vt^T's D layout) and
-//                      computes the chunk's S tiles, outputs and memory update; Z lives in LDS.
+//                      computes the outputs and memory update; Z lives in LDS.
 // Each kind runs its own loop; both pass the same barriers, two per chunk c (buffers b = c % 2
 // hold chunk c):
-//   part 1: score waves: scores of chunk c+1 (x tiles in LDS) and their statistics; memory waves:
-//           S(c) tiles, partial sums of Gq(c) Z, inter part Vt^T Gq(c)^T (memory before chunk c,
-//           split into hi + lo bf16)                                              -> B_Q
-//   part 2: score waves: Gq, Gk of chunk c+1 into the other buffers, x tiles of c+2 committed;
-//           memory waves: memory update with chunk c, intra part V(c)^T S(c)^T, outputs of chunk c
-//           divided and stored, Z advanced, V(c+1) committed                       -> B_P
-// The aggregate phase runs the same loops on the key side alone.
+//   part 1: score waves: S(c) tiles, partial sums of Gq(c) Z, scores of chunk c+1 (x tiles in
+//           LDS) and their statistics; memory waves: inter part Vt^T Gq(c)^T (memory before
+//           chunk c, split into hi + lo bf16)                                     -> B_Q
+//   part 2: score waves: Gq of chunk c+1 into the other buffer, x tile of c+2 committed;
+//           memory waves: Gk(c+1) and V(c+1) committed, memory update with chunk c, intra part
+//           V(c)^T S(c)^T, outputs of chunk c divided and stored, Z advanced       -> B_P
+// The key pass runs the same loops on the key side alone: the memory waves update the memory
+// with chunk c and write Gk(c) to the workspace in part 1, the score waves turn the next chunk's
+// keys into Gk.
 #include <cstdint>
 #include <type_traits>
 
@@ -95,16 +101,17 @@ __device__ __forceinline__ void wide_scores(const WaveParams<DR, CTW>& P, const 
     }
 }
 
-// mode 0: the whole forward (segments 0 .. G-2 aggregate and publish first, every segment
-// waits for the aggregates before it, then scans); mode 1: aggregates only (grid G-1 segments);
-// mode 2: scans only, the aggregates written by an earlier launch (no waits).
+// mode 0: the whole forward (every segment runs its key pass, segments 0 .. G-2 publish their
+// aggregates, every segment waits for the aggregates before it, then scans); mode 1: key passes
+// only (grid G segments); mode 2: scans only, the key passes run by an earlier launch (no waits).
+// gk_cache: [P][N][256] bf16 workspace for the keys' responsibilities.
 template <int DR, int VT, int NW>
 __global__ void __launch_bounds__(NW * 64)
     wide_causal_kernel(const uint16_t* __restrict__ XQ, const uint16_t* __restrict__ XK, const uint16_t* __restrict__ V,
                        int64_t N, int H, int64_t seg, int G, Mixture mx, float* __restrict__ aggregates,
                        uint64_t* __restrict__ flags, uint64_t token, uint32_t wait_limit, int mode, float eps,
                        uint16_t* __restrict__ O, const float* __restrict__ state_in, float* __restrict__ state_out,
-                       uint32_t* __restrict__ err) {
+                       uint16_t* __restrict__ gk_cache, uint32_t* __restrict__ err) {
     using LY = WideLds<DR, VT, NW>;
     constexpr int Kp = LY::Kp, DV = LY::DV, CH = LY::CH, NS = LY::NS, HT = LY::HT, NT = LY::NT;
     constexpr int CTS = LY::KT / NS;       // component tiles per score wave
@@ -142,7 +149,7 @@ __global__ void __launch_bounds__(NW * 64)
     float* agg = aggregates + size_t(p) * G * E;
     uint64_t* fl = flags + size_t(p) * G;
     const size_t SE = size_t(mx.K) * (DV + 1);  // one problem's carried memory
-    const bool aggregate = mode == 1 || (mode == 0 && s + 1 < G);
+    const bool keypass = mode != 2, publish = s + 1 < G;  // the last segment's aggregate has no reader
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(XQ + (size_t(p) * N + lo) * DR, rows * DR * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(XK + (size_t(p) * N + lo) * DR, rows * DR * 2);
     bool ok = true;
@@ -163,56 +170,47 @@ __global__ void __launch_bounds__(NW * 64)
         for (int c = ht; c < CH * LDSS / 8; c += HT) reinterpret_cast<u32x4*>(Ss)[c] = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();  // B_init: constants and the zero tile visible
 
+        // one side per phase: the keys in the key pass, the queries in the scan
         auto run = [&](auto agg_tag) __attribute__((always_inline)) {
             constexpr bool AGG = decltype(agg_tag)::value;
-            constexpr int JOBS = AGG ? 1 : 2;  // 0 keys, 1 queries
-            XT xq, xk;
-            f32x16 acc[2][CTS];
-            float sm_m[2], sm_L[2];
+            constexpr int JB = AGG ? 0 : 1;  // statistics slot: 0 keys, 1 queries
+            const __amdgpu_buffer_rsrc_t rx = AGG ? rk : rq;
+            typename LY::x_t& Xt = AGG ? XtK : XtQ;
+            XT xt;
+            f32x16 acc[CTS];
+            float sm_m, sm_L;
             auto scores_next = [&]() __attribute__((always_inline)) {
-                wide_scores<DR, CTS>(P, cst, ct0, XtK, acc[0]);
-                if (!AGG) wide_scores<DR, CTS>(P, cst, ct0, XtQ, acc[1]);
-#pragma unroll
-                for (int jb = 0; jb < JOBS; ++jb) {
-                    float D, zdummy[CTS][16];
-                    local_softmax<CTS, false>(acc[jb], zdummy, sm_m[jb], sm_L[jb], D);
-                    if (lh == 0) {
-                        st[jb][wave][j][0] = sm_m[jb];
-                        st[jb][wave][j][1] = sm_L[jb];
-                    }
+                wide_scores<DR, CTS>(P, cst, ct0, Xt, acc);
+                float D, zdummy[CTS][16];
+                local_softmax<CTS, false>(acc, zdummy, sm_m, sm_L, D);
+                if (lh == 0) {
+                    st[JB][wave][j][0] = sm_m;
+                    st[JB][wave][j][1] = sm_L;
                 }
             };
             auto store_gamma = [&](int64_t row0, int b) __attribute__((always_inline)) {
                 const bool valid = row0 + j < rows;
+                float mm = -INFINITY;
 #pragma unroll
-                for (int jb = 0; jb < JOBS; ++jb) {
-                    float mm = -INFINITY;
+                for (int w = 0; w < NS; ++w) mm = fmaxf(mm, st[JB][w][j][0]);
+                float Lt = 0.0f;
 #pragma unroll
-                    for (int w = 0; w < NS; ++w) mm = fmaxf(mm, st[jb][w][j][0]);
-                    float Lt = 0.0f;
-#pragma unroll
-                    for (int w = 0; w < NS; ++w)
-                        Lt = fmaf(st[jb][w][j][1], __builtin_amdgcn_exp2f(st[jb][w][j][0] - mm), Lt);
-                    float scale = __builtin_amdgcn_exp2f(sm_m[jb] - mm) * __builtin_amdgcn_rcpf(Lt);
-                    if (!valid) scale = 0.0f;  // positions past the segment: no responsibility
-                    store_gamma_lds<CTS>(acc[jb], scale, jb == 0 ? Gk[b] : Gq[b], LDG, j, ct0);
-                }
+                for (int w = 0; w < NS; ++w)
+                    Lt = fmaf(st[JB][w][j][1], __builtin_amdgcn_exp2f(st[JB][w][j][0] - mm), Lt);
+                float scale = __builtin_amdgcn_exp2f(sm_m - mm) * __builtin_amdgcn_rcpf(Lt);
+                if (!valid) scale = 0.0f;  // positions past the segment: no responsibility
+                store_gamma_lds<CTS>(acc, scale, AGG ? Gk[b] : Gq[b], LDG, j, ct0);
             };
             // prologue (barriers P0, P1, P2)
-            if (!AGG) xq.load(rq, 0);
-            xk.load(rk, 0);
-            if (!AGG) xq.commit(XtQ);
-            xk.commit(XtK);
-            if (!AGG) xq.load(rq, CH);
-            xk.load(rk, CH);
+            xt.load(rx, 0);
+            xt.commit(Xt);
+            xt.load(rx, CH);
             __syncthreads();  // P0: x(0) in LDS
             scores_next();
             __syncthreads();  // P1: statistics of chunk 0; x(0) consumed
             store_gamma(0, 0);
-            if (!AGG) xq.commit(XtQ);
-            xk.commit(XtK);
-            if (!AGG) xq.load(rq, 2 * CH);
-            xk.load(rk, 2 * CH);
+            xt.commit(Xt);
+            xt.load(rx, 2 * CH);
             __syncthreads();  // P2: Gamma(0) and x(1) in LDS
             for (int64_t c = 0; c < C; ++c) {
                 const int b = int(c & 1);
@@ -270,16 +268,14 @@ __global__ void __launch_bounds__(NW * 64)
                 __builtin_amdgcn_s_setprio(0);
                 __syncthreads();  // B_Q
                 store_gamma((c + 1) * CH, b ^ 1);
-                if (!AGG) xq.commit(XtQ);  // x(c+2)
-                xk.commit(XtK);
-                if (!AGG) xq.load(rq, (c + 3) * CH);
-                xk.load(rk, (c + 3) * CH);
+                xt.commit(Xt);  // x(c+2)
+                xt.load(rx, (c + 3) * CH);
                 __syncthreads();  // B_P
             }
         };
-        if (aggregate) {
+        if (keypass) {
             run(std::true_type());
-            publish_token(fl + s, token);  // after the memory waves' stores of the aggregate
+            if (publish) publish_token(fl + s, token);  // after the memory waves' stores of the aggregate
             if (mode == 1) return;
         }
         run(std::false_type());
@@ -308,6 +304,33 @@ __global__ void __launch_bounds__(NW * 64)
                     const int row = c / (DV / 8), col = (c - row * (DV / 8)) * 8;
                     *reinterpret_cast<u32x4*>(dst + row * LDV + col) = vr[u];
                 }
+            }
+        };
+        // the keys' responsibilities of the segment in the workspace, [rows][Kp] bf16: chunk c's
+        // rows go out in the key pass (from Gk) and come back in the scan (into Gk); rows past
+        // the segment fall outside the resource (stores dropped, loads zero)
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(gk_cache + (size_t(p) * N + lo) * Kp, rows * Kp * 2);
+        constexpr int GCHUNKS = CH * Kp / 8, GCH = GCHUNKS / HT;  // 16-byte pieces of a chunk's Gk
+        static_assert(GCHUNKS % HT == 0, "whole pieces per memory-wave thread");
+        u32x4 gr[GCH];
+        auto load_g = [&](int64_t row0) {
+#pragma unroll
+            for (int u = 0; u < GCH; ++u)
+                gr[u] = buf_load16(rg, uint32_t((row0 * Kp + int64_t(ht + u * HT) * 8) * 2));
+        };
+        auto commit_g = [&](uint16_t* dst) {
+#pragma unroll
+            for (int u = 0; u < GCH; ++u) {
+                const int c = ht + u * HT, row = c / (Kp / 8), col = (c - row * (Kp / 8)) * 8;
+                *reinterpret_cast<u32x4*>(dst + row * LDG + col) = gr[u];
+            }
+        };
+        auto store_g = [&](const uint16_t* src, int64_t row0) {
+#pragma unroll
+            for (int u = 0; u < GCH; ++u) {
+                const int c = ht + u * HT, row = c / (Kp / 8), col = (c - row * (Kp / 8)) * 8;
+                buf_store16(rg, uint32_t((row0 * Kp + int64_t(c) * 8) * 2),
+                            *reinterpret_cast<const u32x4*>(src + row * LDG + col));
             }
         };
         auto owns = [&](int cc) { return has_cols && m + NM * cc < C16; };
@@ -360,9 +383,12 @@ __global__ void __launch_bounds__(NW * 64)
             constexpr bool AGG = decltype(agg_tag)::value;
             // prologue (barriers P0, P1, P2)
             load_v(0);
+            if (!AGG) load_g(0);
             pre();
             commit_v(Vs[0]);
+            if (!AGG) commit_g(Gk[0]);
             load_v(CH);
+            if (!AGG) load_g(CH);
             __syncthreads();  // P0
             __syncthreads();  // P1
             __syncthreads();  // P2
@@ -370,11 +396,13 @@ __global__ void __launch_bounds__(NW * 64)
                 const int b = int(c & 1);
                 const int64_t nc = c * CH;
                 f32x4 o[CPW][2];
-                // ---- part 1 (aggregates: the memory update, beside the score waves' products)
+                // ---- part 1 (key pass: the memory update and Gk(c) to the workspace, beside the
+                // score waves' products)
                 if constexpr (AGG) {
                     bf16x8 bv[CPW];
                     load_bv(b, bv);
                     update_memory(b, bv);
+                    store_g(Gk[b], nc);
                 } else {
                     // inter part: O^T = Vt^T Gq^T over the memory before this chunk (hi + lo bf16);
                     // each 32-component step reads its two Gq fragments once for both column
@@ -422,10 +450,15 @@ __global__ void __launch_bounds__(NW * 64)
                     }
                 }
                 __syncthreads();  // B_Q
-                // ---- part 2: V(c+1) into the free buffer first (its wait then covers no output
-                // stores); scans: memory update with chunk c, outputs of chunk c
+                // ---- part 2: V(c+1) (and, in the scan, Gk(c+1)) into the free buffers first
+                // (their waits then cover no output stores); scans: memory update with chunk c,
+                // outputs of chunk c
                 commit_v(Vs[b ^ 1]);
                 load_v(nc + 2 * CH);
+                if constexpr (!AGG) {
+                    commit_g(Gk[b ^ 1]);
+                    load_g(nc + 2 * CH);
+                }
                 if constexpr (!AGG) {
                     bf16x8 bv[CPW];  // V(c) column fragments: memory update and intra part
                     load_bv(b, bv);
@@ -462,13 +495,15 @@ __global__ void __launch_bounds__(NW * 64)
             }
         };
 
-        if (aggregate) {
+        if (keypass) {
 #pragma unroll
             for (int cc = 0; cc < CPW; ++cc)
 #pragma unroll
                 for (int kt = 0; kt < KT16; ++kt) mem[cc][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             for (int k = ht; k < Kp; k += HT) Zs[k] = 0.0f;
             run(std::true_type(), [] {});
+        }
+        if (keypass && publish) {
             // VtT [DV][Kp] then Z [Kp], device-coherent for the consumers in this launch
             const __amdgpu_buffer_rsrc_t ra = make_rsrc(agg + size_t(s) * E, int64_t(E) * 4);
 #pragma unroll
@@ -485,8 +520,8 @@ __global__ void __launch_bounds__(NW * 64)
                                 u32x4{__float_as_uint(z.x), __float_as_uint(z.y), __float_as_uint(z.z), __float_as_uint(z.w)});
             }
             publish_token(fl + s, token);  // its barrier pairs with the score waves' publish
-            if (mode == 1) return;
         }
+        if (mode == 1) return;
 
         // the starting memory: the carried memory [K][DV + 1] (row k: Vt_k then Z_k) or zeros
         // (rows k >= K lie past the resource's end and read as zero), then the earlier aggregates
@@ -596,6 +631,7 @@ hipError_t bf16_causal_wide(const Plan& p, const void* XQ, const void* XK, const
     const bf::Mixture mx{mu, s2, pi, int(p.K)};
     float* aggregates = reinterpret_cast<float*>(ws + p.off_partials);
     uint64_t* flags = reinterpret_cast<uint64_t*>(ws + p.off_flags);
+    uint16_t* gk_cache = reinterpret_cast<uint16_t*>(ws + p.off_gk);
     uint32_t* err = nullptr;
     hipError_t e = device_error_word(&err);
     if (e != hipSuccess) return e;
@@ -608,14 +644,13 @@ hipError_t bf16_causal_wide(const Plan& p, const void* XQ, const void* XK, const
                        dim3(grid_x, unsigned(p.P)), dim3(bf::kWideWaves * 64), 0, st, static_cast<const uint16_t*>(XQ),
                        static_cast<const uint16_t*>(XK), static_cast<const uint16_t*>(V), p.N, int(p.H), p.seg,
                        int(p.G), mx, aggregates, flags, token, wait_limit(), mode, eps, static_cast<uint16_t*>(O),
-                       state_in, state_out, err);
+                       state_in, state_out, gk_cache, err);
             return hipGetLastError();
         };
         if (single) return launch(unsigned(p.G), 0);
-        if (p.G > 1) {  // the aggregates in a launch of their own, then the scans without waits
-            hipError_t r = launch(unsigned(p.G - 1), 1);
-            if (r != hipSuccess) return r;
-        }
+        // the key passes in a launch of their own, then the scans without waits
+        hipError_t r = launch(unsigned(p.G), 1);
+        if (r != hipSuccess) return r;
         return launch(unsigned(p.G), 2);
     });
 }

@@ -31,9 +31,10 @@ struct Plan {
     int64_t seg_q;        // query rows per split of the read (seg, except for cross-attention)
     int32_t chunk;        // causal chunk length
     // byte offsets into the workspace
-    size_t off_params, off_partials, off_memory, off_flags, total;
+    size_t off_params, off_partials, off_memory, off_flags, off_gk, total;
     size_t off_stage;     // backward: end of the fp32 passes' regions; bf16 I/O is staged in fp32 after it
     size_t params_bytes, partials_bytes, memory_bytes, flags_bytes;
+    size_t gk_bytes;      // bf16 causal with 256 components: the keys' responsibilities [P][N][256] bf16
 };
 
 // A fresh 64-bit value per launch that hands data between workgroups (bf16 fused kernels):
