@@ -170,17 +170,20 @@ __global__ void __launch_bounds__(NW * 64)
         for (int c = ht; c < CH * LDSS / 8; c += HT) reinterpret_cast<u32x4*>(Ss)[c] = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();  // B_init: constants and the zero tile visible
 
-        // one side per phase: the keys in the key pass, the queries in the scan
+        // one side per phase: the keys in the key pass, the queries in the scan.  The score
+        // products run two chunks ahead of the Gamma stores, so a wave's softmax of chunk c+1
+        // has the products of chunk c+2 to overlap; the x tiles of even and odd chunks use the
+        // two x buffers in turn.
         auto run = [&](auto agg_tag) __attribute__((always_inline)) {
             constexpr bool AGG = decltype(agg_tag)::value;
             constexpr int JB = AGG ? 0 : 1;  // statistics slot: 0 keys, 1 queries
             const __amdgpu_buffer_rsrc_t rx = AGG ? rk : rq;
-            typename LY::x_t& Xt = AGG ? XtK : XtQ;
+            u32x4* Xb[2] = {XtQ, XtK};
             XT xt;
-            f32x16 acc[CTS];
+            f32x16 acc0[CTS], acc1[CTS];
             float sm_m, sm_L;
-            auto scores_next = [&]() __attribute__((always_inline)) {
-                wide_scores<DR, CTS>(P, cst, ct0, Xt, acc);
+            // the statistics of one chunk's raw scores (acc then holds the exponentials)
+            auto softmax = [&](f32x16(&acc)[CTS]) __attribute__((always_inline)) {
                 float D, zdummy[CTS][16];
                 local_softmax<CTS, false>(acc, zdummy, sm_m, sm_L, D);
                 if (lh == 0) {
@@ -188,7 +191,7 @@ __global__ void __launch_bounds__(NW * 64)
                     st[JB][wave][j][1] = sm_L;
                 }
             };
-            auto store_gamma = [&](int64_t row0, int b) __attribute__((always_inline)) {
+            auto store_gamma = [&](const f32x16(&acc)[CTS], int64_t row0, int b) __attribute__((always_inline)) {
                 const bool valid = row0 + j < rows;
                 float mm = -INFINITY;
 #pragma unroll
@@ -201,18 +204,23 @@ __global__ void __launch_bounds__(NW * 64)
                 if (!valid) scale = 0.0f;  // positions past the segment: no responsibility
                 store_gamma_lds<CTS>(acc, scale, AGG ? Gk[b] : Gq[b], LDG, j, ct0);
             };
-            // prologue (barriers P0, P1, P2)
+            // prologue (barriers P0, P1, P2): Gamma(0), the raw scores of chunk 1, x(2) in LDS
             xt.load(rx, 0);
-            xt.commit(Xt);
+            xt.commit(Xb[0]);
             xt.load(rx, CH);
             __syncthreads();  // P0: x(0) in LDS
-            scores_next();
-            __syncthreads();  // P1: statistics of chunk 0; x(0) consumed
-            store_gamma(0, 0);
-            xt.commit(Xt);
+            wide_scores<DR, CTS>(P, cst, ct0, Xb[0], acc0);
+            softmax(acc0);
+            xt.commit(Xb[1]);  // x(1)
             xt.load(rx, 2 * CH);
-            __syncthreads();  // P2: Gamma(0) and x(1) in LDS
-            for (int64_t c = 0; c < C; ++c) {
+            __syncthreads();  // P1: statistics of chunk 0, x(1) in LDS, x(0) consumed
+            store_gamma(acc0, 0, 0);
+            wide_scores<DR, CTS>(P, cst, ct0, Xb[1], acc1);
+            xt.commit(Xb[0]);  // x(2)
+            xt.load(rx, 3 * CH);
+            __syncthreads();  // P2: Gamma(0) and x(2) in LDS
+            // chunk c: cur holds the raw scores of chunk c+1, nxt receives those of chunk c+2
+            auto chunk = [&](int64_t c, f32x16(&cur)[CTS], f32x16(&nxt)[CTS]) __attribute__((always_inline)) {
                 const int b = int(c & 1);
                 if constexpr (!AGG) {
                     // S^T tiles of chunk c (rows keys, columns queries), blocks (q, k) = (0,0), (1,0),
@@ -264,13 +272,18 @@ __global__ void __launch_bounds__(NW * 64)
                     }
                 }
                 __builtin_amdgcn_s_setprio(1);
-                scores_next();  // chunk c+1
+                wide_scores<DR, CTS>(P, cst, ct0, Xb[b], nxt);  // chunk c+2: x(c+2) is in buffer b
+                softmax(cur);                                   // chunk c+1
                 __builtin_amdgcn_s_setprio(0);
                 __syncthreads();  // B_Q
-                store_gamma((c + 1) * CH, b ^ 1);
-                xt.commit(Xt);  // x(c+2)
-                xt.load(rx, (c + 3) * CH);
+                store_gamma(cur, (c + 1) * CH, b ^ 1);
+                xt.commit(Xb[b ^ 1]);  // x(c+3): x(c+1) was consumed in chunk c-1
+                xt.load(rx, (c + 4) * CH);
                 __syncthreads();  // B_P
+            };
+            for (int64_t c = 0; c < C; c += 2) {
+                chunk(c, acc1, acc0);
+                if (c + 1 < C) chunk(c + 1, acc0, acc1);
             }
         };
         if (keypass) {
