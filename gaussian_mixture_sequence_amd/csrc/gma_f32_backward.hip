@@ -1591,6 +1591,36 @@ size_t f32_backward_extra_bytes(const Plan& p) {
 
 namespace {
 
+// Splits of the K-blocked block passes.  Each workgroup walks its split's tiles for one component
+// block; its prologue (the block's tables and memory) and its moment record are per workgroup,
+// so the block passes take coarser splits than the row passes: about 256 workgroups in all
+// (one round of one workgroup per CU; measured faster than 512, 1024 or 4096 at B8 H8 N1024).
+// The moment records of the block passes and the memory-gradient partials then follow this
+// split (the workspace holds the plan's finer one).
+struct BlockSplit {
+    int G;
+    int64_t seg, seg_q;
+};
+BlockSplit block_split(const Plan& p, int KB) {
+    const int64_t per = std::max<int64_t>(1, (256 + p.P * KB - 1) / (p.P * KB));
+    const int64_t g = std::min<int64_t>(p.G, per);
+    auto tiles = [&](int64_t n) { return int64_t(round_up(size_t((std::max<int64_t>(n, 1) + g - 1) / g), kBT)); };
+    BlockSplit b{};
+    b.seg = tiles(p.N);
+    b.seg_q = tiles(p.Nq);
+    b.G = int(std::max<int64_t>(1, std::max((p.N + b.seg - 1) / b.seg, (p.Nq + b.seg_q - 1) / b.seg_q)));
+    return b;
+}
+
+// The parameter gradients from moment records of G splits per problem (query side, then key side
+// after P G records).
+hipError_t reduce_params_split(const Plan& p, int G, const float* part, const double* inv, const float* pi,
+                               float* dmu, float* ds2, float* dpi, hipStream_t st) {
+    Plan q = p;
+    q.G = G;
+    return reduce_params(q, part, int(p.B), inv, pi, dmu, ds2, dpi, st);
+}
+
 template <typename F>
 hipError_t with_kb(int KB, F&& f) {
     if (KB == 2) return f(std::integral_constant<int, 2>());
@@ -1607,12 +1637,15 @@ hipError_t f32_backward_bidir_kb(const Plan& p, const float* XQ, const float* XK
     KbBuffers b{};
     kb_bytes(p, &b, kbase);
     const int H = int(p.H), dr = int(p.dr), dv = int(p.dv), K = int(p.K), G = int(p.G), KB = kb_blocks(p.K);
+    const BlockSplit bs = block_split(p, KB);
     const int Ei = int(size_t(p.K) * size_t(p.dv + 1));
-    const dim3 grid(unsigned(p.G), unsigned(p.P)), bgrid(unsigned(p.G), unsigned(p.P), unsigned(KB));
+    const dim3 grid(unsigned(p.G), unsigned(p.P)), bgrid(unsigned(bs.G), unsigned(p.P), unsigned(KB));
     const dim3 cgrid(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P));
     const float* cnone = nullptr;
     float* none = nullptr;
     const size_t blds = kb_block_lds_bytes(dr, dv);
+    // the key side's moment records follow the query side's P bs.G ones
+    ppart_key = ppart + size_t(p.P) * size_t(bs.G) * size_t(2 * p.K * p.dr + p.K);
     auto sum_dx = [&](int64_t N, float* dX) {
         const size_t n = size_t(p.P) * size_t(N) * size_t(dr);
         GMA_LAUNCH("f32_bwd_dx_sum", f32_bwd_kb_sum_kernel, dim3(unsigned((n / 4 + kThreads - 1) / kThreads)),
@@ -1633,22 +1666,22 @@ hipError_t f32_backward_bidir_kb(const Plan& p, const float* XQ, const float* XK
                    b.rowq);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         GMA_LAUNCH("f32_bwd_kb_query", f32_bwd_kb_block_kernel<true>, bgrid, dim3(kThreads), blds, st, XQ, dO, p.Nq, H,
-                   dr, dv, K, p.seg_q, G, v.inv, mu, static_cast<const float*>(memory), eps,
+                   dr, dv, K, bs.seg_q, bs.G, v.inv, mu, static_cast<const float*>(memory), eps,
                    static_cast<const float*>(b.gq), static_cast<const float*>(b.rowq), dpart, ppart, b.dxpart);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = sum_dx(p.Nq, dXQ)) != hipSuccess) return e;
-        GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, dpart, G, Ei, dmem);
+        GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, dpart, bs.G, Ei, dmem);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         GMA_LAUNCH("f32_bwd_kb_key_rows", f32_bwd_kb_keyrows_kernel<KBT>, grid, dim3(kThreads),
                    size_t(kBT * kLB + kKB * (dv + 4) + kKB) * sizeof(float), st, V, p.N, dv, K, p.seg,
                    static_cast<const float*>(dmem), static_cast<const float*>(b.gk), dV, b.roww);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         GMA_LAUNCH("f32_bwd_kb_key", f32_bwd_kb_block_kernel<false>, bgrid, dim3(kThreads), blds, st, XK, V, p.N, H, dr,
-                   dv, K, p.seg, G, v.inv, mu, static_cast<const float*>(dmem), eps, static_cast<const float*>(b.gk),
+                   dv, K, bs.seg, bs.G, v.inv, mu, static_cast<const float*>(dmem), eps, static_cast<const float*>(b.gk),
                    static_cast<const float*>(b.roww), none, ppart_key, b.dxpart);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = sum_dx(p.N, dXK)) != hipSuccess) return e;
-        return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
+        return reduce_params_split(p, bs.G, ppart, v.inv, pi, dmu, ds2, dpi, st);
     });
 }
 
@@ -2638,10 +2671,13 @@ hipError_t f32_backward_causal_kb(const Plan& p, const float* XQ, const float* X
     if (e != hipSuccess) return e;
     KbcBuffers b{};
     kbc_bytes(p, &b, kbase);
-    const int H = int(p.H), dr = int(p.dr), dv = int(p.dv), K = int(p.K), G = int(p.G), KB = kb_blocks(p.K);
+    const int H = int(p.H), dr = int(p.dr), dv = int(p.dv), K = int(p.K), KB = kb_blocks(p.K);
     const int NT = int((p.N + kBT - 1) / kBT), Ei = int(size_t(p.K) * size_t(p.dv + 1));
     const int64_t tseg = kBT;
-    const dim3 tgrid(unsigned(NT), unsigned(p.P)), bgrid(unsigned(p.G), unsigned(p.P), unsigned(KB));
+    const BlockSplit bs = block_split(p, KB);
+    const dim3 tgrid(unsigned(NT), unsigned(p.P)), bgrid(unsigned(bs.G), unsigned(p.P), unsigned(KB));
+    // the key side's moment records follow the query side's P bs.G ones
+    ppart_key = ppart + size_t(p.P) * size_t(bs.G) * size_t(2 * p.K * p.dr + p.K);
     const dim3 egrid(unsigned((Ei + kThreads - 1) / kThreads), unsigned(p.P));
     const float* cnone = nullptr;
     float* none = nullptr;
@@ -2672,7 +2708,7 @@ hipError_t f32_backward_causal_kb(const Plan& p, const float* XQ, const float* X
                    dstate_in, K, dv);
         if ((r = hipGetLastError()) != hipSuccess) return r;
         GMA_LAUNCH("f32_bwdc_kb_query", f32_bwdc_kb_block_kernel<true>, bgrid, dim3(kThreads), blds, st, XQ, V, dO, p.N,
-                   H, dr, dv, K, p.seg, G, v.inv, mu, static_cast<const float*>(b.tmem), eps,
+                   H, dr, dv, K, bs.seg, bs.G, v.inv, mu, static_cast<const float*>(b.tmem), eps,
                    static_cast<const float*>(b.gq), static_cast<const float*>(b.gk), static_cast<const float*>(b.rowq),
                    cnone, ppart, b.dxpart);
         if ((r = hipGetLastError()) != hipSuccess) return r;
@@ -2682,12 +2718,12 @@ hipError_t f32_backward_causal_kb(const Plan& p, const float* XQ, const float* X
                    static_cast<const float*>(b.cbuf), static_cast<const float*>(b.rowq), dV, b.roww);
         if ((r = hipGetLastError()) != hipSuccess) return r;
         GMA_LAUNCH("f32_bwdc_kb_key", f32_bwdc_kb_block_kernel<false>, bgrid, dim3(kThreads), blds, st, XK, V, dO, p.N,
-                   H, dr, dv, K, p.seg, G, v.inv, mu, static_cast<const float*>(b.tsend), eps,
+                   H, dr, dv, K, bs.seg, bs.G, v.inv, mu, static_cast<const float*>(b.tsend), eps,
                    static_cast<const float*>(b.gk), static_cast<const float*>(b.gq), static_cast<const float*>(b.rowq),
                    static_cast<const float*>(b.roww), ppart_key, b.dxpart);
         if ((r = hipGetLastError()) != hipSuccess) return r;
         if ((r = sum_dx(dXK)) != hipSuccess) return r;
-        return reduce_params(p, ppart, int(p.B), v.inv, pi, dmu, ds2, dpi, st);
+        return reduce_params_split(p, bs.G, ppart, v.inv, pi, dmu, ds2, dpi, st);
     });
 }
 
