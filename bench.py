@@ -484,8 +484,8 @@ def kernel_symbol(w, name: str) -> str:
         if name.endswith("_combine"):
             return "gma::bf::combine_kernel"
         if name.endswith("_causal"):
-            if kt == 8 and w.d_r <= 64:
-                return "gma::bf::wide_causal_kernel<%d, %d>" % (w.d_r, vt)
+            if kt == 8 and w.d_r <= 64:  # the third argument is the kernel's wave count
+                return "gma::bf::wide_causal_kernel<%d, %d, " % (w.d_r, vt)
             if kt <= 4 and w.d_r * kt <= 256:
                 return "gma::bf::causal_kernel<%d, %d, %d, %d>" % (w.d_r, kt, vt, max(32, w.chunk))
     return KERNEL_SYMBOL.get(name, "?")
