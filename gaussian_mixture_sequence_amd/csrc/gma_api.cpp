@@ -22,7 +22,8 @@ constexpr int64_t kTokenTile = 64;      // tokens per tile in every kernel famil
 constexpr int64_t kBidirBlocks = 512;   // target workgroups for the split-N write and the read
                                         // (two resident per CU: one wave of workgroups)
 constexpr int64_t kCausalBlocks = 512;  // target workgroups for the segmented scan
-constexpr int64_t kBackwardBlocks = 2048;  // target workgroups for the backward passes' splits
+constexpr int64_t kBackwardBlocks = 2048;       // target workgroups of the causal backward's segments
+constexpr int64_t kBackwardBidirBlocks = 512;   // ... and of the bidirectional backward's splits
 constexpr int64_t kDeviceCUs = 256;        // compute units of an MI355X (planning is device-independent)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -63,14 +64,15 @@ gma_status_t check_dims(gma_op_t op, const gma_shape_t& s, gma_dtype_t io) {
 void layout(Plan* pl);
 
 // Splits of the backward passes, which walk each split's rows in tiles of kTokenTile and keep
-// one workgroup per split (and component block): about kBackwardBlocks workgroups in all, each
-// split a multiple of the tile (the forwards' splits follow their own kernels' occupancy, and
-// at B8 H8 N1024 the bidirectional one left half the CUs idle).  Both sides take the same
-// count of splits; the regions are laid out again for it.
-void backward_split(Plan* pl) {
+// one workgroup per split (and component block): about `blocks` workgroups in all, each split a
+// multiple of the tile (the forwards' splits follow their own kernels' occupancy, and at B8 H8
+// N1024 the bidirectional one left half the CUs idle).  The causal passes walk their segments
+// in order and take finer ones; each bidirectional split also writes partial records, so those
+// stay coarser.  Both sides take the same count of splits; the regions are laid out again.
+void backward_split(Plan* pl, int64_t blocks) {
     const int64_t n = std::max(pl->N, pl->Nq);
     if (pl->P <= 0 || n <= 0) return;
-    const int64_t g = std::max<int64_t>(1, std::min(cdiv(kBackwardBlocks, pl->P), cdiv(n, kTokenTile)));
+    const int64_t g = std::max<int64_t>(1, std::min(cdiv(blocks, pl->P), cdiv(n, kTokenTile)));
     pl->seg = round_up(size_t(cdiv(std::max<int64_t>(pl->N, 1), g)), kTokenTile);
     pl->seg_q = round_up(size_t(cdiv(std::max<int64_t>(pl->Nq, 1), g)), kTokenTile);
     pl->G = std::max<int64_t>(1, std::max(cdiv(pl->N, pl->seg), cdiv(pl->Nq, pl->seg_q)));
@@ -118,7 +120,7 @@ gma_status_t make_plan(gma_op_t op, const gma_shape_t& s, gma_dtype_t io, int32_
         const bool causal = op == GMA_OP_BACKWARD_CAUSAL;
         if ((st = make_plan(causal ? GMA_OP_CAUSAL : GMA_OP_BIDIR, s, GMA_F32, causal ? 64 : 0, pl)) != GMA_OK)
             return st;
-        backward_split(pl);
+        backward_split(pl, causal ? kBackwardBlocks : kBackwardBidirBlocks);
         pl->op = op;
         pl->chunk = 0;
         pl->total += causal ? f32_backward_causal_extra_bytes(*pl) : f32_backward_extra_bytes(*pl);
@@ -242,7 +244,7 @@ gma_status_t make_backward_cross_plan(const gma_cross_shape_t& s, gma_dtype_t io
     if (io != GMA_F32 && io != GMA_BF16) return GMA_ERR_BAD_VALUE;
     gma_status_t st = make_cross_plan(s, GMA_F32, pl);
     if (st != GMA_OK) return st;
-    backward_split(pl);
+    backward_split(pl, kBackwardBidirBlocks);
     pl->op = GMA_OP_BACKWARD_BIDIR;
     pl->total += f32_backward_extra_bytes(*pl);
     pl->off_stage = pl->total;
