@@ -41,7 +41,8 @@ CASES = [
     (case("f32", B=1, H=2, N=700, seed=91), [0, 300, 301, 700]),
     (case("bf16", B=1, H=2, N=2500, seed=92), [0, 900, 2500]),                            # fused scan, segments
     (case("bf16", B=2, H=1, N=1300, d_r=32, d_v=64, K=128, seed=93), [0, 64, 65, 1300]),  # K = 128
-    (case("bf16", B=1, H=1, N=600, d_r=64, d_v=128, K=256, seed=94), [0, 250, 600]),      # serial scan
+    (case("bf16", B=1, H=1, N=600, d_r=64, d_v=128, K=256, seed=94), [0, 250, 600]),      # 256 components
+    (case("bf16", B=1, H=1, N=300, d_r=128, d_v=128, K=256, seed=89), [0, 130, 300]),     # serial scan
     (case("bf16", B=1, H=2, N=300, d_r=16, d_v=32, K=8, chunk=32, seed=95), [0, 31, 300]),  # padded K
 ]
 
@@ -117,6 +118,7 @@ SHORT = [
     ("f32", dict(d_r=16, d_v=32, K=8)), ("f32", dict(d_r=7, d_v=5, K=13)), ("f32", dict(d_r=128, d_v=128, K=256)),
     ("bf16", dict(d_r=64, d_v=64, K=32)), ("bf16", dict(d_r=32, d_v=64, K=128)), ("bf16", dict(d_r=128, d_v=128, K=256)),
     ("bf16", dict(d_r=16, d_v=32, K=1)), ("bf16", dict(d_r=64, d_v=32, K=50)),
+    ("bf16", dict(d_r=64, d_v=128, K=256)), ("bf16", dict(d_r=32, d_v=64, K=200)),  # the 256-component scan
 ]
 
 
