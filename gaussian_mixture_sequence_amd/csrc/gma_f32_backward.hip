@@ -1648,6 +1648,7 @@ hipError_t f32_backward_bidir_kb(const Plan& p, const float* XQ, const float* XK
     ppart_key = ppart + size_t(p.P) * size_t(bs.G) * size_t(2 * p.K * p.dr + p.K);
     auto sum_dx = [&](int64_t N, float* dX) {
         const size_t n = size_t(p.P) * size_t(N) * size_t(dr);
+        if (n == 0) return hipSuccess;  // an empty side of cross-attention: no rows, no launch
         GMA_LAUNCH("f32_bwd_dx_sum", f32_bwd_kb_sum_kernel, dim3(unsigned((n / 4 + kThreads - 1) / kThreads)),
                    dim3(kThreads), 0, st, static_cast<const float*>(b.dxpart), KB, n, dX);
         return hipGetLastError();

@@ -325,6 +325,8 @@ CROSS_CASES = [
     cross_case(2100, 300, 141, d_r=32, d_v=32, K=192),          # K-blocked passes, more queries
     cross_case(300, 0, 136),                                     # empty context
     cross_case(0, 300, 137),                                     # no queries
+    cross_case(300, 0, 142, d_r=32, d_v=32, K=128),              # empty context, K-blocked passes
+    cross_case(0, 300, 143, d_r=32, d_v=32, K=128),              # no queries, K-blocked passes
     cross_case(1000, 3000, 138, d_r=64, d_v=64, K=64, dtype="bf16"),
 ]
 
