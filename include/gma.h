@@ -176,10 +176,12 @@ gma_status_t gma_forward_bidir_noalloc(const void* XQ, const void* XK, const voi
  * positions a step takes on chip: each kernel runs the largest power of two not above it that
  * its tiles allow in LDS and registers (64 at most on the bf16 path, 32 for 256 components);
  * gma_plan_info reports the length used.  Only the order of the sums depends on it.  Output row i depends
- * only on inputs at positions <= i.  Arguments as for gma_forward_bidir.  With bf16 I/O
- * and K <= 128 (d_r * K <= 8192) the forward is one launch: each segment's workgroup
- * publishes its segment aggregate in the workspace and waits for those of the segments
- * before it (same flag scheme as gma_forward_bidir); other shapes take two launches.
+ * only on inputs at positions <= i.  Arguments as for gma_forward_bidir.  With bf16 I/O,
+ * K <= 128 (d_r * K <= 8192) or 256 padded components with d_r <= 64, the forward is one
+ * launch: each segment's workgroup publishes its segment aggregate in the workspace and
+ * waits for those of the segments before it (same flag scheme as gma_forward_bidir); other
+ * shapes take two launches.  The 256-component form also keeps the keys' responsibilities
+ * of every position in the workspace (B*H*N*512 bytes) between its key pass and its scan.
  */
 gma_status_t gma_forward_causal(const void* XQ, const void* XK, const void* V,
                                 gma_dtype_t io_dtype,
