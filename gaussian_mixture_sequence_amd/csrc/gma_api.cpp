@@ -735,9 +735,10 @@ gma_status_t gma_device_status(hipStream_t stream) {
 gma_status_t gma_plan_info(gma_op_t op, const gma_shape_t* shape, gma_dtype_t io_dtype, int32_t chunk,
                            gma_plan_info_t* info) {
     if (!shape || !info) return GMA_ERR_NULL_POINTER;
-    if (op != GMA_OP_BIDIR && op != GMA_OP_CAUSAL) return GMA_ERR_BAD_VALUE;
+    const bool backward = op == GMA_OP_BACKWARD_BIDIR || op == GMA_OP_BACKWARD_CAUSAL;
+    if (op != GMA_OP_BIDIR && op != GMA_OP_CAUSAL && !backward) return GMA_ERR_BAD_VALUE;
     Plan p;
-    gma_status_t st = gma::make_plan(op, *shape, io_dtype, chunk, &p);
+    gma_status_t st = gma::make_plan(op, *shape, io_dtype, backward ? 0 : chunk, &p);
     if (st != GMA_OK) return st;
     *info = gma_plan_info_t{};
     info->splits = p.G;

@@ -420,10 +420,11 @@ gma_status_t gma_set_single_launch(int enable);
 /*
  * How a forward of `op` (GMA_OP_BIDIR or GMA_OP_CAUSAL) on `shape` is split, for inspection
  * and tests; device-independent, like the workspace size.  Same validation and errors as
- * gma_workspace_size.
+ * gma_workspace_size.  GMA_OP_BACKWARD_BIDIR and GMA_OP_BACKWARD_CAUSAL give the backward's
+ * splits (`chunk` ignored; the fields below the first three are then 0).
  *   splits                 sequence splits (bidirectional) or segments (causal) per problem
  *   rows_per_split         positions per split (the last may be shorter)
- *   workgroups             B H splits: the grid of the single launch
+ *   workgroups             B H splits: the grid of the single launch (backward: of the row passes)
  *   threads_per_workgroup  }  bf16 bidirectional only (0 otherwise): the single-launch
  *   lds_bytes              }  kernel's workgroup size and static LDS,
  *   waits_on_all_splits    }  1 if the single launch is planned (2 to 8 splits per problem)

@@ -356,6 +356,30 @@ def test_bidir_single_launch_grid_fits_resident_bound(lib, dr, K, dv):
                 assert info["waits_on_all_splits"] == 0
 
 
+def test_backward_splits(lib):
+    """The backward's own split rule: splits of whole 64-position tiles, about 512 workgroups for
+    the bidirectional passes and about 2048 for the causal ones (the forward's rule left half the
+    CUs idle at B8 H8 N1024)."""
+    F = gb.GMA_F32
+    info = lambda op, *sh: gb.gma_plan_info(op, *sh, F)
+    b = info(gb.GMA_OP_BACKWARD_BIDIR, 8, 8, 1024, 64, 64, 64)
+    assert (b["splits"], b["rows_per_split"], b["workgroups"]) == (8, 128, 512)
+    b = info(gb.GMA_OP_BACKWARD_BIDIR, 8, 8, 4096, 64, 64, 64)
+    assert (b["splits"], b["rows_per_split"], b["workgroups"]) == (8, 512, 512)
+    c = info(gb.GMA_OP_BACKWARD_CAUSAL, 8, 8, 1024, 64, 64, 256)
+    assert (c["splits"], c["rows_per_split"], c["workgroups"]) == (16, 64, 1024)
+    c = info(gb.GMA_OP_BACKWARD_CAUSAL, 8, 12, 2048, 64, 64, 32)
+    assert (c["splits"], c["rows_per_split"]) == (16, 128)
+    for op in (gb.GMA_OP_BACKWARD_BIDIR, gb.GMA_OP_BACKWARD_CAUSAL):
+        for sh in [(1, 1, 1, 16, 32, 8), (2, 3, 700, 16, 32, 8), (1, 2, 100000, 32, 32, 64), (64, 64, 300, 16, 16, 8)]:
+            r = info(op, *sh)
+            N = sh[2]
+            assert r["rows_per_split"] % 64 == 0 and r["splits"] * r["rows_per_split"] >= N
+            assert (r["splits"] - 1) * r["rows_per_split"] < N            # no empty split
+            assert r["workgroups"] == sh[0] * sh[1] * r["splits"]
+            assert r["threads_per_workgroup"] == r["lds_bytes"] == r["chunk_used"] == 0
+
+
 def test_plan_info_validation(lib):
     info = gb.PlanInfo()
     sh = gb.Shape(1, 1, 8, 16, 32, 8)
