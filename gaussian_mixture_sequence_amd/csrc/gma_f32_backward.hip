@@ -1835,15 +1835,20 @@ __global__ void __launch_bounds__(kThreads)
     const int tid = threadIdx.x, r0 = (tid >> 4) * 4, m0 = (tid & 15) * 4;
     const int LY = dv + 4, NT = int((N + kBT - 1) / kBT);
     const size_t E = size_t(K) * (dv + 1);
+    // C and the V rows take the places of gamma^K and the memory block once the blocks are
+    // done (kBT = kKB), which keeps the workgroup within 80 KB: two per CU
     float* Gq = lds;                // [64][kLB] gamma^Q of a block, rows i
     float* GkT = Gq + kBT * kLB;    // [kKB][kLB] gamma^K of a block, transposed: [k][j]
-    float* Cm = GkT + kKB * kLB;    // [64][kLB] C (rows i, columns j)
-    float* Mb = Cm + kBT * kLB;     // [kKB][dv + 4] a block of the memory before the tile
+    float* Cm = GkT;                // [64][kLB] C (rows i, columns j), after the blocks
+    float* Mb = GkT + kKB * kLB;    // [kKB][dv + 4] a block of the memory before the tile
+    float* Vr = Mb;                 // [64][dv + 4] V rows, after the blocks
     float* Zb = Mb + kKB * LY;      // [kKB]
     float* Yr = Zb + kKB;           // [64][dv + 4] dO rows
-    float* Vr = Yr + kBT * LY;      // [64][dv + 4] V rows
-    float* Dv = Vr + kBT * LY;      // [64] D
+    float* Dv = Yr + kBT * LY;      // [64] D
     float* Av = Dv + kBT;           // [64] a'
+    static_assert(kBT == kKB, "C and the V rows reuse the block arrays");
+    constexpr int VPT = kBT * 16 / kThreads;  // float4 pieces of the V rows per thread (d_v <= 64)
+    float4 vreg[VPT];
     const float* gqp = gq + size_t(p) * N * K;
     const float* gkp = gk + size_t(p) * N * K;
     const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
@@ -1856,7 +1861,13 @@ __global__ void __launch_bounds__(kThreads)
             const bool ok = t < rows;
             const size_t off = (size_t(p) * N + n0 + t) * dv + cc;
             *reinterpret_cast<float4*>(Yr + t * LY + cc) = ok ? *reinterpret_cast<const float4*>(dO + off) : make_float4(0, 0, 0, 0);
-            *reinterpret_cast<float4*>(Vr + t * LY + cc) = ok ? *reinterpret_cast<const float4*>(V + off) : make_float4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {  // V rows into registers, into LDS after the blocks
+            const int i = tid + u * kThreads, t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
+            vreg[u] = (i < kBT * (dv / 4) && t < rows)
+                          ? *reinterpret_cast<const float4*>(V + (size_t(p) * N + n0 + t) * dv + cc)
+                          : make_float4(0, 0, 0, 0);
         }
         float cc4[4][4] = {}, nv[4][4] = {}, dz[4] = {};
 #pragma unroll
@@ -1893,6 +1904,12 @@ __global__ void __launch_bounds__(kThreads)
                     }
                 }
             }
+        }
+        __syncthreads();  // gamma^K and the memory block are consumed: C and V take their places
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            const int i = tid + u * kThreads, t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
+            if (i < kBT * (dv / 4)) *reinterpret_cast<float4*>(Vr + t * LY + cc) = vreg[u];
         }
         // C masked to j <= i; its row sums join D
         float cs[4];
@@ -1980,7 +1997,7 @@ __global__ void __launch_bounds__(kThreads)
 
 template <int KB>
 size_t kbc_qrows_lds_bytes(int dv) {
-    return size_t(2 * kBT * kLB + kKB * kLB + kKB * (dv + 4) + kKB + 2 * kBT * (dv + 4) + 2 * kBT) * sizeof(float);
+    return size_t(kBT * kLB + kKB * kLB + kKB * (dv + 4) + kKB + kBT * (dv + 4) + 2 * kBT) * sizeof(float);
 }
 
 // Causal key rows, grid (G, P): dV_j = gamma^K_j . S + sum_{i >= j} C_ij dO'_i (an output) and
