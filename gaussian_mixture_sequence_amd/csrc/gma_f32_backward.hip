@@ -1224,10 +1224,49 @@ __global__ void __launch_bounds__(kThreads)
     }
 }
 
+
+// Responsibilities [t][k0 .. k0 + 63] of the tile's rows into Gb ([64][kLB]) as load_gamma_block,
+// for a workgroup of NTH threads.
+template <int NTH>
+__device__ __forceinline__ void load_gamma_block_n(const float* __restrict__ gc, int64_t n0, int rows, int K, int k0,
+                                                   float* Gb) {
+    if ((K & 3) == 0) {
+        for (int i = threadIdx.x; i < kBT * (kKB / 4); i += NTH) {
+            const int t = i / (kKB / 4), kq = (i - t * (kKB / 4)) * 4;
+            const float4 v = (t < rows && k0 + kq < K) ? *reinterpret_cast<const float4*>(gc + (n0 + t) * K + k0 + kq)
+                                                       : make_float4(0, 0, 0, 0);
+            *reinterpret_cast<float4*>(Gb + t * kLB + kq) = v;
+        }
+    } else {
+        for (int i = threadIdx.x; i < kBT * kKB; i += NTH) {
+            const int t = i / kKB, kl = i - t * kKB;
+            Gb[t * kLB + kl] = (t < rows && k0 + kl < K) ? gc[(n0 + t) * K + k0 + kl] : 0.0f;
+        }
+    }
+}
+
+// TW columns of a row read from LDS (TW = 2 or 4, 8- or 16-byte aligned).
+template <int TW>
+__device__ __forceinline__ void ldsw(const float* q, float (&a)[TW]) {
+    if constexpr (TW == 4) {
+        const float4 v = *reinterpret_cast<const float4*>(q);
+        a[0] = v.x, a[1] = v.y, a[2] = v.z, a[3] = v.w;
+    } else {
+        const float2 v = *reinterpret_cast<const float2*>(q);
+        a[0] = v.x, a[1] = v.y;
+    }
+}
+template <int TW>
+__device__ __forceinline__ void stsw(float* q, const float (&a)[TW]) {
+    if constexpr (TW == 4) *reinterpret_cast<float4*>(q) = make_float4(a[0], a[1], a[2], a[3]);
+    else *reinterpret_cast<float2*>(q) = make_float2(a[0], a[1]);
+}
+
 size_t kb_block_lds_bytes(int dr, int dv) {
     return size_t(2 * kBT * kLB + kBT * (dv + 4) + dv * kLB + kKB + 3 * kBT + kBT * (dr + 4) + 2 * kKB * (dr + 4)) *
            sizeof(float);
 }
+constexpr int kBlockTW = 2;  // register tile width of the bidirectional block passes (eight waves)
 
 // Block passes, grid (G, P, KB): component block kb = blockIdx.z of split g of problem p.
 //   QUERY: Y = dO, mem = [Vt | Z], rowda = (D, a') per row; g_ik = (dO_i . Vt_k) / D_i - a'_i Z_k and
@@ -1235,17 +1274,20 @@ size_t kb_block_lds_bytes(int dr, int dv) {
 //   key: Y = V, mem = [dVt | dZ], rowda = w per row (the key-side closed form); g_jk = V_j . dVt_k + dZ_k.
 // Both: the block's entries of the moment record (S1, S2, S0) into param_part, and the block's
 // share of dX (-sum_k ds_ik (x_id - mu_kd) / sigma2_kd over its components) into dX_part[kb].
-template <bool QUERY>
-__global__ void __launch_bounds__(kThreads)
+// Each thread holds 4 x TW register tiles of the 64 x 64 products: 1024 / TW threads, so TW = 2
+// gives eight waves (two per SIMD) where the 123 KB of LDS allow one workgroup per CU.
+template <bool QUERY, int TW>
+__global__ void __launch_bounds__(1024 / TW)
     f32_bwd_kb_block_kernel(const float* __restrict__ X, const float* __restrict__ Y, int64_t N, int H, int dr, int dv,
                             int K, int64_t seg, int G, const double* __restrict__ inv, const float* __restrict__ mu,
                             const float* __restrict__ mem, float eps, const float* __restrict__ gcache,
                             const float* __restrict__ rowda, float* __restrict__ mem_part,
                             float* __restrict__ param_part, float* __restrict__ dX_part) {
+    constexpr int NTH = 1024 / TW, CG = 64 / TW;  // threads; column groups of a row group
     extern __shared__ float lds[];
     const int64_t p = blockIdx.y;
     const int gi = blockIdx.x, kb = blockIdx.z, h = int(p % H);
-    const int tid = threadIdx.x, r0 = (tid >> 4) * 4, m0 = (tid & 15) * 4;
+    const int tid = threadIdx.x, r0 = (tid / CG) * 4, m0 = (tid % CG) * TW;
     const int LY = dv + 4, LX = dr + 4, k0 = kb * kKB;
     float* Gb = lds;                  // [64][kLB] responsibilities of the block
     float* Db = Gb + kBT * kLB;       // [64][kLB] ds
@@ -1261,24 +1303,24 @@ __global__ void __launch_bounds__(kThreads)
     const double* ih = inv + size_t(h) * K * dr;
     const float* mh = mu + size_t(h) * K * dr;
     const float* mp = mem + size_t(p) * K * (dv + 1);
-    for (int i = tid; i < kKB * dr; i += kThreads) {
+    for (int i = tid; i < kKB * dr; i += NTH) {
         const int kl = i / dr, d = i - kl * dr, k = k0 + kl;
         muR[kl * LX + d] = k < K ? mh[size_t(k) * dr + d] : 0.0f;
         ivR[kl * LX + d] = k < K ? float(ih[size_t(k) * dr + d]) : 0.0f;
     }
-    for (int i = tid; i < kKB * dv; i += kThreads) {
+    for (int i = tid; i < kKB * dv; i += NTH) {
         const int kl = i / dv, cc = i - kl * dv, k = k0 + kl;
         MT[cc * kLB + kl] = k < K ? mp[size_t(k) * dv + cc] : 0.0f;
     }
-    for (int kl = tid; kl < kKB; kl += kThreads) Zb[kl] = k0 + kl < K ? mp[size_t(K) * dv + k0 + kl] : 0.0f;
+    for (int kl = tid; kl < kKB; kl += NTH) Zb[kl] = k0 + kl < K ? mp[size_t(K) * dv + k0 + kl] : 0.0f;
     __syncthreads();
     // moment accumulators (rows d = r0.., columns k = m0..) with their mu; memory-gradient
     // accumulators (query: rows k = r0.., columns c = m0..)
     const bool mom = r0 < dr;
-    float mreg[4][4], s1[4][4] = {}, s2[4][4] = {}, s0[4] = {}, mv[4][4] = {}, mz[4] = {};
+    float mreg[4][TW], s1[4][TW] = {}, s2[4][TW] = {}, s0[TW] = {}, mv[4][TW] = {}, mz[4] = {};
     if (mom)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TW; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mreg[i][j] = muR[(m0 + j) * LX + r0 + i];
     const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
@@ -1289,8 +1331,8 @@ __global__ void __launch_bounds__(kThreads)
     for (int64_t n0 = lo; n0 < hi; n0 += kBT) {
         const int rows = int(min<int64_t>(kBT, hi - n0));
         __syncthreads();  // the previous tile's reads are done
-        load_gamma_block(gc, n0, rows, K, k0, Gb);
-        for (int t = tid; t < kBT; t += kThreads) {
+        load_gamma_block_n<NTH>(gc, n0, rows, K, k0, Gb);
+        for (int t = tid; t < kBT; t += NTH) {
             if (QUERY) {
                 const float D = t < rows ? rowda[(size_t(p) * N + n0 + t) * 2] : 1.0f;
                 const float a = t < rows ? rowda[(size_t(p) * N + n0 + t) * 2 + 1] : 0.0f;
@@ -1301,13 +1343,13 @@ __global__ void __launch_bounds__(kThreads)
                 Wv[t] = t < rows ? rowda[size_t(p) * N + n0 + t] : 0.0f;
             }
         }
-        for (int i = tid; i < kBT * (dr / 4); i += kThreads) {
+        for (int i = tid; i < kBT * (dr / 4); i += NTH) {
             const int t = i / (dr / 4), d = (i - t * (dr / 4)) * 4;
             *reinterpret_cast<float4*>(Xr + t * LX + d) =
                 t < rows ? *reinterpret_cast<const float4*>(Xp + (n0 + t) * dr + d) : make_float4(0, 0, 0, 0);
         }
         __syncthreads();  // Dv before the scaled rows
-        for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
+        for (int i = tid; i < kBT * (dv / 4); i += NTH) {
             const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
             float4 v = t < rows ? *reinterpret_cast<const float4*>(Yp + (n0 + t) * dv + cc) : make_float4(0, 0, 0, 0);
             if (QUERY) {
@@ -1318,56 +1360,56 @@ __global__ void __launch_bounds__(kThreads)
         }
         __syncthreads();
         {   // g (rows t = r0.., components k = m0..), then ds = gamma (g - w_t) into Db
-            float gg[4][4] = {};
+            float gg[4][TW] = {};
 #pragma unroll 4
             for (int cc = 0; cc < dv; ++cc) {
-                float ya[4], ma[4];
+                float ya[4], ma[TW];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ya[i] = Yr[(r0 + i) * LY + cc];
-                unpack(lds4(MT + cc * kLB + m0), ma);
+                ldsw<TW>(MT + cc * kLB + m0, ma);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(ya[i], ma[j], gg[i][j]);
+                    for (int j = 0; j < TW; ++j) gg[i][j] = fmaf(ya[i], ma[j], gg[i][j]);
             }
-            float za[4];
-            unpack(lds4(Zb + m0), za);
+            float za[TW];
+            ldsw<TW>(Zb + m0, za);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float ga[4], ds[4];
-                unpack(lds4(Gb + (r0 + i) * kLB + m0), ga);
+                float ga[TW], ds[TW];
+                ldsw<TW>(Gb + (r0 + i) * kLB + m0, ga);
                 const float w = Wv[r0 + i];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < TW; ++j) {
                     const float g = QUERY ? gg[i][j] - Av[r0 + i] * za[j] : gg[i][j] + za[j];
                     ds[j] = ga[j] * (g - w);
                 }
-                put4(Db + (r0 + i) * kLB + m0, ds[0], ds[1], ds[2], ds[3]);
+                stsw<TW>(Db + (r0 + i) * kLB + m0, ds);
             }
         }
         if (QUERY && m0 < dv)  // dVt (rows k = r0.., columns c = m0..), dZ
 #pragma unroll 4
             for (int t = 0; t < rows; ++t) {
-                float ga[4], ya[4];
+                float ga[4], ya[TW];
                 unpack(lds4(Gb + t * kLB + r0), ga);
-                unpack(lds4(Yr + t * LY + m0), ya);
+                ldsw<TW>(Yr + t * LY + m0, ya);
                 const float a = Av[t];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    mz[i] = fmaf(-ga[i], a, mz[i]);
+                    if (m0 == 0) mz[i] = fmaf(-ga[i], a, mz[i]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) mv[i][j] = fmaf(ga[i], ya[j], mv[i][j]);
+                    for (int j = 0; j < TW; ++j) mv[i][j] = fmaf(ga[i], ya[j], mv[i][j]);
                 }
             }
         __syncthreads();  // ds in Db
         if (mom)  // moments (rows d = r0.., columns k = m0..), direct (centred) form
 #pragma unroll 4
             for (int t = 0; t < rows; ++t) {
-                float xa[4], da[4];
+                float xa[4], da[TW];
                 unpack(lds4(Xr + t * LX + r0), xa);
-                unpack(lds4(Db + t * kLB + m0), da);
+                ldsw<TW>(Db + t * kLB + m0, da);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < TW; ++j) {
                     s0[j] += da[j];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -1378,34 +1420,37 @@ __global__ void __launch_bounds__(kThreads)
                 }
             }
         if (m0 < dr) {  // this block's share of dX (rows t = r0.., columns d = m0..)
-            float xa[4][4], acc[4][4] = {};
+            float xa[4][TW], acc[4][TW] = {};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) unpack(lds4(Xr + (r0 + i) * LX + m0), xa[i]);
+            for (int i = 0; i < 4; ++i) ldsw<TW>(Xr + (r0 + i) * LX + m0, xa[i]);
             const int kn = min(kKB, K - k0);
 #pragma unroll 4
             for (int kl = 0; kl < kn; ++kl) {
-                float ma[4], ia[4], da[4];
-                unpack(lds4(muR + kl * LX + m0), ma);
-                unpack(lds4(ivR + kl * LX + m0), ia);
+                float ma[TW], ia[TW], da[4];
+                ldsw<TW>(muR + kl * LX + m0, ma);
+                ldsw<TW>(ivR + kl * LX + m0, ia);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) da[i] = Db[(r0 + i) * kLB + kl];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(da[i] * ia[j], xa[i][j] - ma[j], acc[i][j]);
+                    for (int j = 0; j < TW; ++j) acc[i][j] = fmaf(da[i] * ia[j], xa[i][j] - ma[j], acc[i][j]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (r0 + i < rows)
-                    *reinterpret_cast<float4*>(dXp + (n0 + r0 + i) * dr + m0) =
-                        make_float4(-acc[i][0], -acc[i][1], -acc[i][2], -acc[i][3]);
+                if (r0 + i < rows) {
+                    float o[TW];
+#pragma unroll
+                    for (int j = 0; j < TW; ++j) o[j] = -acc[i][j];
+                    stsw<TW>(dXp + (n0 + r0 + i) * dr + m0, o);
+                }
         }
     }
     // the block's entries of the moment record [S1 (K dr) | S2 (K dr) | S0 (K)]
     float* pp = param_part + (size_t(p) * G + gi) * size_t(2 * K * dr + K);
     if (mom)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < TW; ++j) {
             const int k = k0 + m0 + j;
             if (k >= K) continue;
 #pragma unroll
@@ -1423,7 +1468,7 @@ __global__ void __launch_bounds__(kThreads)
             if (k >= K) continue;
             if (m0 < dv)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) out[size_t(k) * dv + m0 + j] = mv[i][j];
+                for (int j = 0; j < TW; ++j) out[size_t(k) * dv + m0 + j] = mv[i][j];
             if (m0 == 0) out[size_t(K) * dv + k] = mz[i];
         }
     }
@@ -1540,7 +1585,7 @@ hipError_t bwd_allow_lds() {
                              (const void*)f32_bwd_kb_rows_kernel<2, KB_KEY>, (const void*)f32_bwd_kb_rows_kernel<2, KB_QUERY>,
                              (const void*)f32_bwd_kb_rows_kernel<3, KB_KEY>, (const void*)f32_bwd_kb_rows_kernel<3, KB_QUERY>,
                              (const void*)f32_bwd_kb_rows_kernel<4, KB_KEY>, (const void*)f32_bwd_kb_rows_kernel<4, KB_QUERY>,
-                             (const void*)f32_bwd_kb_block_kernel<true>, (const void*)f32_bwd_kb_block_kernel<false>,
+                             (const void*)f32_bwd_kb_block_kernel<true, kBlockTW>, (const void*)f32_bwd_kb_block_kernel<false, kBlockTW>,
                              (const void*)f32_bwd_kb_keyrows_kernel<2>, (const void*)f32_bwd_kb_keyrows_kernel<3>,
                              (const void*)f32_bwd_kb_keyrows_kernel<4>};
         for (const void* f : fns) {
@@ -1666,7 +1711,7 @@ hipError_t f32_backward_bidir_kb(const Plan& p, const float* XQ, const float* XK
                    p.Nq, H, dr, dv, K, p.seg_q, G, v.c, v.inv, mu, static_cast<const float*>(memory), eps, b.gq, none,
                    b.rowq);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        GMA_LAUNCH("f32_bwd_kb_query", f32_bwd_kb_block_kernel<true>, bgrid, dim3(kThreads), blds, st, XQ, dO, p.Nq, H,
+        GMA_LAUNCH("f32_bwd_kb_query", (f32_bwd_kb_block_kernel<true, kBlockTW>), bgrid, dim3(1024 / kBlockTW), blds, st, XQ, dO, p.Nq, H,
                    dr, dv, K, bs.seg_q, bs.G, v.inv, mu, static_cast<const float*>(memory), eps,
                    static_cast<const float*>(b.gq), static_cast<const float*>(b.rowq), dpart, ppart, b.dxpart);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1677,7 +1722,7 @@ hipError_t f32_backward_bidir_kb(const Plan& p, const float* XQ, const float* XK
                    size_t(kBT * kLB + kKB * (dv + 4) + kKB) * sizeof(float), st, V, p.N, dv, K, p.seg,
                    static_cast<const float*>(dmem), static_cast<const float*>(b.gk), dV, b.roww);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        GMA_LAUNCH("f32_bwd_kb_key", f32_bwd_kb_block_kernel<false>, bgrid, dim3(kThreads), blds, st, XK, V, p.N, H, dr,
+        GMA_LAUNCH("f32_bwd_kb_key", (f32_bwd_kb_block_kernel<false, kBlockTW>), bgrid, dim3(1024 / kBlockTW), blds, st, XK, V, p.N, H, dr,
                    dv, K, bs.seg, bs.G, v.inv, mu, static_cast<const float*>(dmem), eps, static_cast<const float*>(b.gk),
                    static_cast<const float*>(b.roww), none, ppart_key, b.dxpart);
         if ((e = hipGetLastError()) != hipSuccess) return e;
