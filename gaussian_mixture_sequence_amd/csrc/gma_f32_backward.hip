@@ -2164,18 +2164,20 @@ size_t kbc_block_lds_bytes(int dr, int dv) {
 //   key: X = X_K; gown = gamma^K, other = gamma^Q; tstate: what the later tiles' queries send;
 //     w = roww.
 // Both: the block's entries of the moment record and its share of dX (as the bidirectional pass).
-template <bool QUERY>
-__global__ void __launch_bounds__(kThreads)
+// 4 x TW register tiles over 1024 / TW threads, as the bidirectional block passes.
+template <bool QUERY, int TW>
+__global__ void __launch_bounds__(1024 / TW)
     f32_bwdc_kb_block_kernel(const float* __restrict__ X, const float* __restrict__ V, const float* __restrict__ dO,
                              int64_t N, int H, int dr, int dv, int K, int64_t seg, int G, const double* __restrict__ inv,
                              const float* __restrict__ mu, const float* __restrict__ tstate, float eps,
                              const float* __restrict__ gown, const float* __restrict__ gother,
                              const float* __restrict__ rowq, const float* __restrict__ roww,
                              float* __restrict__ param_part, float* __restrict__ dX_part) {
+    constexpr int NTH = 1024 / TW, CG = 64 / TW;  // threads; column groups of a row group
     extern __shared__ float lds[];
     const int64_t p = blockIdx.y;
     const int gi = blockIdx.x, kb = blockIdx.z, h = int(p % H);
-    const int tid = threadIdx.x, r0 = (tid >> 4) * 4, m0 = (tid & 15) * 4;
+    const int tid = threadIdx.x, r0 = (tid / CG) * 4, m0 = (tid % CG) * TW;
     const int LY = dv + 4, LX = dr + 4, k0 = kb * kKB, NT = int((N + kBT - 1) / kBT);
     const size_t E = size_t(K) * (dv + 1);
     float* Gb = lds;                  // [64][kLB] own responsibilities of the block
@@ -2193,17 +2195,17 @@ __global__ void __launch_bounds__(kThreads)
     float* Dv = Wv + kBT;             // [64] D
     const double* ih = inv + size_t(h) * K * dr;
     const float* mh = mu + size_t(h) * K * dr;
-    for (int i = tid; i < kKB * dr; i += kThreads) {
+    for (int i = tid; i < kKB * dr; i += NTH) {
         const int kl = i / dr, d = i - kl * dr, k = k0 + kl;
         muR[kl * LX + d] = k < K ? mh[size_t(k) * dr + d] : 0.0f;
         ivR[kl * LX + d] = k < K ? float(ih[size_t(k) * dr + d]) : 0.0f;
     }
     __syncthreads();
     const bool mom = r0 < dr;
-    float mreg[4][4], s1[4][4] = {}, s2[4][4] = {}, s0[4] = {};
+    float mreg[4][TW], s1[4][TW] = {}, s2[4][TW] = {}, s0[TW] = {};
     if (mom)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TW; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mreg[i][j] = muR[(m0 + j) * LX + r0 + i];
     const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
@@ -2215,27 +2217,27 @@ __global__ void __launch_bounds__(kThreads)
         const int rows = int(min<int64_t>(kBT, hi - n0)), tile = int(n0 / kBT);
         const float* mp = tstate + (size_t(p) * NT + tile) * E;
         __syncthreads();  // the previous tile's reads are done
-        load_gamma_block(gop, n0, rows, K, k0, Gb);
-        load_gamma_block(gtp, n0, rows, K, k0, Go);
-        for (int t = tid; t < kBT; t += kThreads) {
+        load_gamma_block_n<NTH>(gop, n0, rows, K, k0, Gb);
+        load_gamma_block_n<NTH>(gtp, n0, rows, K, k0, Go);
+        for (int t = tid; t < kBT; t += NTH) {
             const float D = t < rows ? rowq[(size_t(p) * N + n0 + t) * 2] : 1.0f;
             const float a = t < rows ? rowq[(size_t(p) * N + n0 + t) * 2 + 1] : 0.0f;
             Dv[t] = D;
             Av[t] = a;
             Wv[t] = QUERY ? eps * a : (t < rows ? roww[size_t(p) * N + n0 + t] : 0.0f);
         }
-        for (int i = tid; i < kBT * (dr / 4); i += kThreads) {
+        for (int i = tid; i < kBT * (dr / 4); i += NTH) {
             const int t = i / (dr / 4), d = (i - t * (dr / 4)) * 4;
             *reinterpret_cast<float4*>(Xr + t * LX + d) =
                 t < rows ? *reinterpret_cast<const float4*>(Xp + (n0 + t) * dr + d) : make_float4(0, 0, 0, 0);
         }
-        for (int i = tid; i < kKB * dv; i += kThreads) {
+        for (int i = tid; i < kKB * dv; i += NTH) {
             const int kl = i / dv, cc = i - kl * dv, k = k0 + kl;
             MT[cc * kLB + kl] = k < K ? mp[size_t(k) * dv + cc] : 0.0f;
         }
-        for (int kl = tid; kl < kKB; kl += kThreads) Zb[kl] = k0 + kl < K ? mp[size_t(K) * dv + k0 + kl] : 0.0f;
+        for (int kl = tid; kl < kKB; kl += NTH) Zb[kl] = k0 + kl < K ? mp[size_t(K) * dv + k0 + kl] : 0.0f;
         __syncthreads();  // Dv before the scaled rows
-        for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
+        for (int i = tid; i < kBT * (dv / 4); i += NTH) {
             const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
             float4 o = make_float4(0, 0, 0, 0), v = o;
             if (t < rows) {
@@ -2253,100 +2255,100 @@ __global__ void __launch_bounds__(kThreads)
         }
         __syncthreads();
         {   // A_ij = dO'_i . V_j - a'_i for j <= i (rows i = r0.., columns j = m0..)
-            float aa[4][4] = {};
+            float aa[4][TW] = {};
 #pragma unroll 4
             for (int cc = 0; cc < dv; ++cc) {
-                float ya[4], va[4];
+                float ya[4], va[TW];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ya[i] = Yr[(r0 + i) * LY + cc];
-                unpack(lds4(VD + cc * kLB + m0), va);
+                ldsw<TW>(VD + cc * kLB + m0, va);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) aa[i][j] = fmaf(ya[i], va[j], aa[i][j]);
+                    for (int j = 0; j < TW; ++j) aa[i][j] = fmaf(ya[i], va[j], aa[i][j]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float o[4];
+                float o[TW];
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < TW; ++j)
                     o[j] = (m0 + j <= r0 + i && r0 + i < rows && m0 + j < rows) ? aa[i][j] - Av[r0 + i] : 0.0f;
-                put4(Am + (r0 + i) * kLB + m0, o[0], o[1], o[2], o[3]);
+                stsw<TW>(Am + (r0 + i) * kLB + m0, o);
             }
         }
         __syncthreads();  // A in LDS
-        float gg[4][4] = {};
+        float gg[4][TW] = {};
         if (QUERY) {  // rows i = r0.., components k = m0..
 #pragma unroll 4
             for (int cc = 0; cc < dv; ++cc) {
-                float ya[4], ma[4];
+                float ya[4], ma[TW];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ya[i] = Yr[(r0 + i) * LY + cc];
-                unpack(lds4(MT + cc * kLB + m0), ma);
+                ldsw<TW>(MT + cc * kLB + m0, ma);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(ya[i], ma[j], gg[i][j]);
+                    for (int j = 0; j < TW; ++j) gg[i][j] = fmaf(ya[i], ma[j], gg[i][j]);
             }
 #pragma unroll 4
             for (int jj = 0; jj < rows; ++jj) {  // sum_{j <= i} A_ij gamma^K_jk
-                float aa[4], ka[4];
+                float aa[4], ka[TW];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) aa[i] = Am[(r0 + i) * kLB + jj];
-                unpack(lds4(Go + jj * kLB + m0), ka);
+                ldsw<TW>(Go + jj * kLB + m0, ka);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(aa[i], ka[j], gg[i][j]);
+                    for (int j = 0; j < TW; ++j) gg[i][j] = fmaf(aa[i], ka[j], gg[i][j]);
             }
         } else {  // rows j = r0.., components k = m0..
 #pragma unroll 4
             for (int cc = 0; cc < dv; ++cc) {
-                float va[4], ma[4];
+                float va[4], ma[TW];
                 unpack(lds4(VD + cc * kLB + r0), va);
-                unpack(lds4(MT + cc * kLB + m0), ma);
+                ldsw<TW>(MT + cc * kLB + m0, ma);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(va[i], ma[j], gg[i][j]);
+                    for (int j = 0; j < TW; ++j) gg[i][j] = fmaf(va[i], ma[j], gg[i][j]);
             }
 #pragma unroll 4
             for (int ii = 0; ii < rows; ++ii) {  // sum_{i >= j} A_ij gamma^Q_ik
-                float aa[4], qa[4];
+                float aa[4], qa[TW];
                 unpack(lds4(Am + ii * kLB + r0), aa);
-                unpack(lds4(Go + ii * kLB + m0), qa);
+                ldsw<TW>(Go + ii * kLB + m0, qa);
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(aa[i], qa[j], gg[i][j]);
+                    for (int j = 0; j < TW; ++j) gg[i][j] = fmaf(aa[i], qa[j], gg[i][j]);
             }
         }
-        float za[4];
-        unpack(lds4(Zb + m0), za);
-        float ds[4][4];
+        float za[TW];
+        ldsw<TW>(Zb + m0, za);
+        float ds[4][TW];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float ga[4];
-            unpack(lds4(Gb + (r0 + i) * kLB + m0), ga);
+            float ga[TW];
+            ldsw<TW>(Gb + (r0 + i) * kLB + m0, ga);
             const float w = Wv[r0 + i];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < TW; ++j) {
                 const float g = QUERY ? gg[i][j] - Av[r0 + i] * za[j] : gg[i][j] + za[j];
                 ds[i][j] = ga[j] * (g - w);
             }
         }
         __syncthreads();  // V^T is consumed: ds takes its place
 #pragma unroll
-        for (int i = 0; i < 4; ++i) put4(VD + (r0 + i) * kLB + m0, ds[i][0], ds[i][1], ds[i][2], ds[i][3]);
+        for (int i = 0; i < 4; ++i) stsw<TW>(VD + (r0 + i) * kLB + m0, ds[i]);
         __syncthreads();  // ds in LDS
         if (mom)  // moments (rows d = r0.., columns k = m0..), direct (centred) form
 #pragma unroll 4
             for (int t = 0; t < rows; ++t) {
-                float xa[4], da[4];
+                float xa[4], da[TW];
                 unpack(lds4(Xr + t * LX + r0), xa);
-                unpack(lds4(VD + t * kLB + m0), da);
+                ldsw<TW>(VD + t * kLB + m0, da);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < TW; ++j) {
                     s0[j] += da[j];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -2357,33 +2359,36 @@ __global__ void __launch_bounds__(kThreads)
                 }
             }
         if (m0 < dr) {  // this block's share of dX (rows t = r0.., columns d = m0..)
-            float xa[4][4], acc[4][4] = {};
+            float xa[4][TW], acc[4][TW] = {};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) unpack(lds4(Xr + (r0 + i) * LX + m0), xa[i]);
+            for (int i = 0; i < 4; ++i) ldsw<TW>(Xr + (r0 + i) * LX + m0, xa[i]);
             const int kn = min(kKB, K - k0);
 #pragma unroll 4
             for (int kl = 0; kl < kn; ++kl) {
-                float ma[4], ia[4], da[4];
-                unpack(lds4(muR + kl * LX + m0), ma);
-                unpack(lds4(ivR + kl * LX + m0), ia);
+                float ma[TW], ia[TW], da[4];
+                ldsw<TW>(muR + kl * LX + m0, ma);
+                ldsw<TW>(ivR + kl * LX + m0, ia);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) da[i] = VD[(r0 + i) * kLB + kl];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(da[i] * ia[j], xa[i][j] - ma[j], acc[i][j]);
+                    for (int j = 0; j < TW; ++j) acc[i][j] = fmaf(da[i] * ia[j], xa[i][j] - ma[j], acc[i][j]);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (r0 + i < rows)
-                    *reinterpret_cast<float4*>(dXp + (n0 + r0 + i) * dr + m0) =
-                        make_float4(-acc[i][0], -acc[i][1], -acc[i][2], -acc[i][3]);
+                if (r0 + i < rows) {
+                    float o[TW];
+#pragma unroll
+                    for (int j = 0; j < TW; ++j) o[j] = -acc[i][j];
+                    stsw<TW>(dXp + (n0 + r0 + i) * dr + m0, o);
+                }
         }
     }
     float* pp = param_part + (size_t(p) * G + gi) * size_t(2 * K * dr + K);
     if (mom)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < TW; ++j) {
             const int k = k0 + m0 + j;
             if (k >= K) continue;
 #pragma unroll
@@ -2712,7 +2717,8 @@ hipError_t kbc_allow_lds() {
         if ((r = kbc_allow_lds_for<1>()) != hipSuccess || (r = kbc_allow_lds_for<2>()) != hipSuccess ||
             (r = kbc_allow_lds_for<3>()) != hipSuccess || (r = kbc_allow_lds_for<4>()) != hipSuccess)
             return r;
-        const void* fns[] = {(const void*)f32_bwdc_kb_block_kernel<true>, (const void*)f32_bwdc_kb_block_kernel<false>};
+        const void* fns[] = {(const void*)f32_bwdc_kb_block_kernel<true, kBlockTW>,
+                             (const void*)f32_bwdc_kb_block_kernel<false, kBlockTW>};
         for (const void* f : fns)
             if ((r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds))) != hipSuccess)
                 return r;
@@ -2770,7 +2776,7 @@ hipError_t f32_backward_causal_kb(const Plan& p, const float* XQ, const float* X
         GMA_LAUNCH("f32_bwdc_suffix", f32_suffix_kernel, egrid, dim3(kThreads), 0, st, b.tsend, NT, Ei, dstate_out,
                    dstate_in, K, dv);
         if ((r = hipGetLastError()) != hipSuccess) return r;
-        GMA_LAUNCH("f32_bwdc_kb_query", f32_bwdc_kb_block_kernel<true>, bgrid, dim3(kThreads), blds, st, XQ, V, dO, p.N,
+        GMA_LAUNCH("f32_bwdc_kb_query", (f32_bwdc_kb_block_kernel<true, kBlockTW>), bgrid, dim3(1024 / kBlockTW), blds, st, XQ, V, dO, p.N,
                    H, dr, dv, K, bs.seg, bs.G, v.inv, mu, static_cast<const float*>(b.tmem), eps,
                    static_cast<const float*>(b.gq), static_cast<const float*>(b.gk), static_cast<const float*>(b.rowq),
                    cnone, ppart, b.dxpart);
@@ -2780,7 +2786,7 @@ hipError_t f32_backward_causal_kb(const Plan& p, const float* XQ, const float* X
                    st, V, dO, p.N, dv, K, tseg, static_cast<const float*>(b.gk), static_cast<const float*>(b.tsend),
                    static_cast<const float*>(b.cbuf), static_cast<const float*>(b.rowq), dV, b.roww);
         if ((r = hipGetLastError()) != hipSuccess) return r;
-        GMA_LAUNCH("f32_bwdc_kb_key", f32_bwdc_kb_block_kernel<false>, bgrid, dim3(kThreads), blds, st, XK, V, dO, p.N,
+        GMA_LAUNCH("f32_bwdc_kb_key", (f32_bwdc_kb_block_kernel<false, kBlockTW>), bgrid, dim3(1024 / kBlockTW), blds, st, XK, V, dO, p.N,
                    H, dr, dv, K, bs.seg, bs.G, v.inv, mu, static_cast<const float*>(b.tsend), eps,
                    static_cast<const float*>(b.gk), static_cast<const float*>(b.gq), static_cast<const float*>(b.rowq),
                    static_cast<const float*>(b.roww), ppart_key, b.dxpart);
