@@ -292,12 +292,42 @@ __device__ __forceinline__ void put4(float* q, float a, float b, float c, float 
 __device__ __forceinline__ void unpack(const float4 v, float (&a)[4]) {
     a[0] = v.x, a[1] = v.y, a[2] = v.z, a[3] = v.w;
 }
+// TW columns of a row read from LDS (TW = 2 or 4, 8- or 16-byte aligned).
+template <int TW>
+__device__ __forceinline__ void ldsw(const float* q, float (&a)[TW]) {
+    if constexpr (TW == 4) {
+        const float4 v = *reinterpret_cast<const float4*>(q);
+        a[0] = v.x, a[1] = v.y, a[2] = v.z, a[3] = v.w;
+    } else {
+        const float2 v = *reinterpret_cast<const float2*>(q);
+        a[0] = v.x, a[1] = v.y;
+    }
+}
+template <int TW>
+__device__ __forceinline__ void stsw(float* q, const float (&a)[TW]) {
+    if constexpr (TW == 4) *reinterpret_cast<float4*>(q) = make_float4(a[0], a[1], a[2], a[3]);
+    else *reinterpret_cast<float2*>(q) = make_float2(a[0], a[1]);
+}
+
 __device__ __forceinline__ float sum16(float v) {
     for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 16);
     return v;
 }
 __device__ __forceinline__ float max16(float v) {
     for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 16));
+    return v;
+}
+// Sum and maximum over the W consecutive lanes of a row group (W = 16 or 32).
+template <int W>
+__device__ __forceinline__ float sum_lanes(float v) {
+#pragma unroll
+    for (int o = W / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, W);
+    return v;
+}
+template <int W>
+__device__ __forceinline__ float max_lanes(float v) {
+#pragma unroll
+    for (int o = W / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, W));
     return v;
 }
 
@@ -366,9 +396,10 @@ __device__ __forceinline__ void gamma_to(float* Gp, int64_t n0, int rows, int K,
                     make_float4(gam[i][0], gam[i][1], gam[i][2], gam[i][3]);
 }
 
-// Load rows [n0, n0 + rows) of X [.][dr] into xT [dr][kLDT] (zeros beyond `rows`).
+// Load rows [n0, n0 + rows) of X [.][dr] into xT [dr][kLDT] (zeros beyond `rows`) with NTH threads.
+template <int NTH = kThreads>
 __device__ __forceinline__ void load_xT(const float* Xp, int64_t n0, int rows, int dr, float* xT) {
-    for (int i = threadIdx.x; i < kBT * (dr / 4); i += kThreads) {
+    for (int i = threadIdx.x; i < kBT * (dr / 4); i += NTH) {
         const int t = i / (dr / 4), d = (i - t * (dr / 4)) * 4;
         const float4 v = t < rows ? *reinterpret_cast<const float4*>(Xp + (n0 + t) * dr + d) : make_float4(0, 0, 0, 0);
         xT[(d + 0) * kLDT + t] = v.x;
@@ -974,8 +1005,9 @@ hipError_t reduce_params(const Plan& p, const float* part, int B, const double* 
 }
 
 // ---- K-blocked passes of the bidirectional backward (64 < K <= 256; d_r, d_v <= 64, multiples
-// of 4): the same 16 x 16 thread grid of 4 x 4 register blocks, the components taken in blocks
-// of 64.  Row passes (one workgroup per split) compute each side's responsibilities for all K
+// of 4): 64 x 64 products over 16 row groups of 4 x TW register blocks (1024 / TW threads; TW = 2
+// keeps two waves per SIMD where the LDS allows one workgroup per CU), the components taken in
+// blocks of 64.  Row passes (one workgroup per split) compute each side's responsibilities for all K
 // from the LDS tables of one block at a time, cache them ([P][N][K] fp32) and form the per-row
 // sums over every component; block passes (one workgroup per split and component block) read
 // the cached responsibilities and produce what each component owns: the moments, the memory
@@ -994,82 +1026,89 @@ int kb_blocks(int64_t K) { return int((K + kKB - 1) / kKB); }
 // blocks (row maximum and sum over the 16 lanes of the row group).  Into S ([64][LK], zero past
 // `rows` and K) and the cache rows gc ([.][K] of this problem).  LDS: xT [dr][kLDT], muT and ivT
 // [dr][kLB], cB [kKB].
-template <int KB>
+template <int KB, int TW>
 __device__ void kb_gamma(const float* Xp, int64_t n0, int rows, int dr, int K, const double* ch, const double* ih,
                          const float* mh, float* xT, float* muT, float* ivT, float* cB, float* S, int LK, float* gc) {
-    const int tid = threadIdx.x, r0 = (tid >> 4) * 4, m0 = (tid & 15) * 4;
-    load_xT(Xp, n0, rows, dr, xT);
+    constexpr int NTH = 1024 / TW, CG = 64 / TW;
+    const int tid = threadIdx.x, r0 = (tid / CG) * 4, m0 = (tid % CG) * TW;
+    load_xT<NTH>(Xp, n0, rows, dr, xT);
     float mrow[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
         __syncthreads();  // the previous block's tables are consumed (and xT is in place)
-        for (int i = tid; i < kKB * dr; i += kThreads) {
+        for (int i = tid; i < kKB * dr; i += NTH) {
             const int kl = i / dr, d = i - kl * dr, k = kb * kKB + kl;
             muT[d * kLB + kl] = k < K ? mh[size_t(k) * dr + d] : 0.0f;
             ivT[d * kLB + kl] = k < K ? float(ih[size_t(k) * dr + d]) : 0.0f;
         }
-        for (int kl = tid; kl < kKB; kl += kThreads) cB[kl] = kb * kKB + kl < K ? float(ch[kb * kKB + kl]) : -INFINITY;
+        for (int kl = tid; kl < kKB; kl += NTH) cB[kl] = kb * kKB + kl < K ? float(ch[kb * kKB + kl]) : -INFINITY;
         __syncthreads();
-        float q[4][4] = {};
+        float q[4][TW] = {};
 #pragma unroll 4
         for (int d = 0; d < dr; ++d) {
-            float xa[4], ma[4], ia[4];
+            float xa[4], ma[TW], ia[TW];
             unpack(lds4(xT + d * kLDT + r0), xa);
-            unpack(lds4(muT + d * kLB + m0), ma);
-            unpack(lds4(ivT + d * kLB + m0), ia);
+            ldsw<TW>(muT + d * kLB + m0, ma);
+            ldsw<TW>(ivT + d * kLB + m0, ia);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < TW; ++j) {
                     const float df = xa[i] - ma[j];
                     q[i][j] = fmaf(df * df, ia[j], q[i][j]);
                 }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float s[4];
+            float s[TW];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < TW; ++j) {
                 s[j] = cB[m0 + j] - 0.5f * q[i][j];
                 mrow[i] = fmaxf(mrow[i], s[j]);
             }
-            put4(S + (r0 + i) * LK + kb * kKB + m0, s[0], s[1], s[2], s[3]);
+            stsw<TW>(S + (r0 + i) * LK + kb * kKB + m0, s);
         }
     }
     // each thread reads back only what it wrote: no barrier
     float rr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        mrow[i] = max16(mrow[i]);
+        mrow[i] = max_lanes<CG>(mrow[i]);
         float l = 0.0f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             float* sp = S + (r0 + i) * LK + kb * kKB + m0;
-            float s[4];
-            unpack(lds4(sp), s);
+            float s[TW];
+            ldsw<TW>(sp, s);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < TW; ++j) {
                 s[j] = expf(s[j] - mrow[i]);
                 l += s[j];
             }
-            put4(sp, s[0], s[1], s[2], s[3]);
+            stsw<TW>(sp, s);
         }
-        rr[i] = r0 + i < rows ? 1.0f / sum16(l) : 0.0f;
+        rr[i] = r0 + i < rows ? 1.0f / sum_lanes<CG>(l) : 0.0f;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             float* sp = S + (r0 + i) * LK + kb * kKB + m0;
-            float s[4];
-            unpack(lds4(sp), s);
+            float s[TW];
+            ldsw<TW>(sp, s);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                s[j] *= rr[i];
-                const int k = kb * kKB + m0 + j;
-                if (r0 + i < rows && k < K) gc[(n0 + r0 + i) * K + k] = s[j];
+            for (int j = 0; j < TW; ++j) s[j] *= rr[i];
+            const int k = kb * kKB + m0;
+            if (r0 + i < rows) {
+                if (K % TW == 0) {  // k < K covers the TW columns
+                    if (k < K) stsw<TW>(gc + (n0 + r0 + i) * K + k, s);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < TW; ++j)
+                        if (k + j < K) gc[(n0 + r0 + i) * K + k + j] = s[j];
+                }
             }
-            put4(sp, s[0], s[1], s[2], s[3]);
+            stsw<TW>(sp, s);
         }
     __syncthreads();
 }
@@ -1106,17 +1145,19 @@ size_t kb_rows_lds_bytes(int dr, int dv) {
 //     D_i and a'_i of every row into rowda ([.][2] per problem);
 //   KB_GAMMA: the responsibilities of X into gc only.
 enum { KB_KEY = 0, KB_QUERY = 1, KB_GAMMA = 2 };
-template <int KB, int MODE>
-__global__ void __launch_bounds__(kThreads)
+constexpr int kRowsTW = 2;  // register tile width of the row passes (eight waves)
+template <int KB, int MODE, int TW>
+__global__ void __launch_bounds__(1024 / TW)
     f32_bwd_kb_rows_kernel(const float* __restrict__ X, const float* __restrict__ Y, int64_t N, int H, int dr, int dv,
                            int K, int64_t seg, int G, const double* __restrict__ c, const double* __restrict__ inv,
                            const float* __restrict__ mu, const float* __restrict__ mem, float eps,
                            float* __restrict__ gcache, float* __restrict__ mem_part, float* __restrict__ rowda) {
     constexpr bool QUERY = MODE == KB_QUERY;
+    constexpr int NTH = 1024 / TW, CG = 64 / TW;  // threads; column groups of a row group
     extern __shared__ float lds[];
     const int64_t p = blockIdx.y;
     const int gi = blockIdx.x, h = int(p % H);
-    const int tid = threadIdx.x, r0 = (tid >> 4) * 4, m0 = (tid & 15) * 4;
+    const int tid = threadIdx.x, r0 = (tid / CG) * 4, m0 = (tid % CG) * TW;
     const int LK = KB * kKB + 4, LY = dv + 4;
     float* xT = lds;                   // [dr][kLDT]
     float* muT = xT + dr * kLDT;       // [dr][kLB]
@@ -1132,18 +1173,18 @@ __global__ void __launch_bounds__(kThreads)
     const float* Xp = X + size_t(p) * N * dr;
     const float* Yp = Y + size_t(p) * N * dv;
     float* gc = gcache + size_t(p) * N * K;
-    float mv[KB][4][4] = {}, mz[KB][4] = {};  // key side: Vt rows k = kb 64 + r0.., columns c = m0..
+    float mv[KB][4][TW] = {}, mz[KB][4] = {};  // key side: Vt rows k = kb 64 + r0.., columns c = m0..
     for (int64_t n0 = lo; n0 < hi; n0 += kBT) {
         const int rows = int(min<int64_t>(kBT, hi - n0));
         __syncthreads();  // the previous tile's reads are done
         if (MODE != KB_GAMMA)
-            for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
+            for (int i = tid; i < kBT * (dv / 4); i += NTH) {
                 const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
                 const float4 v =
                     t < rows ? *reinterpret_cast<const float4*>(Yp + (n0 + t) * dv + cc) : make_float4(0, 0, 0, 0);
                 *reinterpret_cast<float4*>(Yr + t * LY + cc) = v;
             }
-        kb_gamma<KB>(Xp, n0, rows, dr, K, ch, ih, mh, xT, muT, ivT, cB, S, LK, gc);
+        kb_gamma<KB, TW>(Xp, n0, rows, dr, K, ch, ih, mh, xT, muT, ivT, cB, S, LK, gc);
         if (MODE == KB_GAMMA) continue;
         if (!QUERY) {
             if (m0 < dv)
@@ -1151,43 +1192,43 @@ __global__ void __launch_bounds__(kThreads)
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll 4
                     for (int t = 0; t < rows; ++t) {
-                        float ga[4], ya[4];
+                        float ga[4], ya[TW];
                         unpack(lds4(S + t * LK + kb * kKB + r0), ga);
-                        unpack(lds4(Yr + t * LY + m0), ya);
+                        ldsw<TW>(Yr + t * LY + m0, ya);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             mz[kb][i] += ga[i];
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) mv[kb][i][j] = fmaf(ga[i], ya[j], mv[kb][i][j]);
+                            for (int j = 0; j < TW; ++j) mv[kb][i][j] = fmaf(ga[i], ya[j], mv[kb][i][j]);
                         }
                     }
             continue;
         }
         // query: N_t = gamma_t Vt (rows t = r0.., columns c = m0..) and gamma_t Z, block by block
-        float nv[4][4] = {}, dz[4] = {};
+        float nv[4][TW] = {}, dz[4] = {};
         const float* mp = mem + size_t(p) * K * (dv + 1);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             __syncthreads();  // the previous block of the memory is consumed
-            for (int i = tid; i < kKB * (dv / 4); i += kThreads) {
+            for (int i = tid; i < kKB * (dv / 4); i += NTH) {
                 const int kl = i / (dv / 4), cc = (i - kl * (dv / 4)) * 4, k = kb * kKB + kl;
                 *reinterpret_cast<float4*>(Mb + kl * LY + cc) =
                     k < K ? *reinterpret_cast<const float4*>(mp + size_t(k) * dv + cc) : make_float4(0, 0, 0, 0);
             }
-            for (int kl = tid; kl < kKB; kl += kThreads) Zb[kl] = kb * kKB + kl < K ? mp[size_t(K) * dv + kb * kKB + kl] : 0.0f;
+            for (int kl = tid; kl < kKB; kl += NTH) Zb[kl] = kb * kKB + kl < K ? mp[size_t(K) * dv + kb * kKB + kl] : 0.0f;
             __syncthreads();
 #pragma unroll 4
             for (int kl = 0; kl < kKB; ++kl) {
-                float ga[4], va[4];
+                float ga[4], va[TW];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ga[i] = S[(r0 + i) * LK + kb * kKB + kl];
-                unpack(lds4(Mb + kl * LY + (m0 < dv ? m0 : 0)), va);
+                ldsw<TW>(Mb + kl * LY + (m0 < dv ? m0 : 0), va);
                 const float z = Zb[kl];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     dz[i] = fmaf(ga[i], z, dz[i]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ga[i], va[j], nv[i][j]);
+                    for (int j = 0; j < TW; ++j) nv[i][j] = fmaf(ga[i], va[j], nv[i][j]);
                 }
             }
         }
@@ -1195,14 +1236,14 @@ __global__ void __launch_bounds__(kThreads)
         for (int i = 0; i < 4; ++i) {
             float dot = 0.0f;
             if (m0 < dv) {
-                float oa[4];
-                unpack(lds4(Yr + (r0 + i) * LY + m0), oa);
+                float oa[TW];
+                ldsw<TW>(Yr + (r0 + i) * LY + m0, oa);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) dot = fmaf(oa[j], nv[i][j], dot);
+                for (int j = 0; j < TW; ++j) dot = fmaf(oa[j], nv[i][j], dot);
             }
-            dot = sum16(dot);
+            dot = sum_lanes<CG>(dot);
             const float D = dz[i] + eps;
-            if ((tid & 15) == 0 && r0 + i < rows) {
+            if (m0 == 0 && r0 + i < rows) {
                 rowda[(size_t(p) * N + n0 + r0 + i) * 2] = D;
                 rowda[(size_t(p) * N + n0 + r0 + i) * 2 + 1] = dot / (D * D);
             }
@@ -1218,7 +1259,7 @@ __global__ void __launch_bounds__(kThreads)
                 if (k >= K) continue;
                 if (m0 < dv)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) out[size_t(k) * dv + m0 + j] = mv[kb][i][j];
+                    for (int j = 0; j < TW; ++j) out[size_t(k) * dv + m0 + j] = mv[kb][i][j];
                 if (m0 == 0) out[size_t(K) * dv + k] = mz[kb][i];
             }
     }
@@ -1243,23 +1284,6 @@ __device__ __forceinline__ void load_gamma_block_n(const float* __restrict__ gc,
             Gb[t * kLB + kl] = (t < rows && k0 + kl < K) ? gc[(n0 + t) * K + k0 + kl] : 0.0f;
         }
     }
-}
-
-// TW columns of a row read from LDS (TW = 2 or 4, 8- or 16-byte aligned).
-template <int TW>
-__device__ __forceinline__ void ldsw(const float* q, float (&a)[TW]) {
-    if constexpr (TW == 4) {
-        const float4 v = *reinterpret_cast<const float4*>(q);
-        a[0] = v.x, a[1] = v.y, a[2] = v.z, a[3] = v.w;
-    } else {
-        const float2 v = *reinterpret_cast<const float2*>(q);
-        a[0] = v.x, a[1] = v.y;
-    }
-}
-template <int TW>
-__device__ __forceinline__ void stsw(float* q, const float (&a)[TW]) {
-    if constexpr (TW == 4) *reinterpret_cast<float4*>(q) = make_float4(a[0], a[1], a[2], a[3]);
-    else *reinterpret_cast<float2*>(q) = make_float2(a[0], a[1]);
 }
 
 size_t kb_block_lds_bytes(int dr, int dv) {
@@ -1582,9 +1606,9 @@ hipError_t bwd_allow_lds() {
                              (const void*)f32_bwd_tiled_kernel<BWD_WRITE>, (const void*)f32_bwd_tiled_kernel<BWD_QUERY>,
                              (const void*)f32_bwd_tiled_kernel<BWD_KEY>, (const void*)f32_bwd_tiled_kernel<BWD_CQUERY>,
                              (const void*)f32_bwd_tiled_kernel<BWD_CKEY>,
-                             (const void*)f32_bwd_kb_rows_kernel<2, KB_KEY>, (const void*)f32_bwd_kb_rows_kernel<2, KB_QUERY>,
-                             (const void*)f32_bwd_kb_rows_kernel<3, KB_KEY>, (const void*)f32_bwd_kb_rows_kernel<3, KB_QUERY>,
-                             (const void*)f32_bwd_kb_rows_kernel<4, KB_KEY>, (const void*)f32_bwd_kb_rows_kernel<4, KB_QUERY>,
+                             (const void*)f32_bwd_kb_rows_kernel<2, KB_KEY, kRowsTW>, (const void*)f32_bwd_kb_rows_kernel<2, KB_QUERY, kRowsTW>,
+                             (const void*)f32_bwd_kb_rows_kernel<3, KB_KEY, kRowsTW>, (const void*)f32_bwd_kb_rows_kernel<3, KB_QUERY, kRowsTW>,
+                             (const void*)f32_bwd_kb_rows_kernel<4, KB_KEY, kRowsTW>, (const void*)f32_bwd_kb_rows_kernel<4, KB_QUERY, kRowsTW>,
                              (const void*)f32_bwd_kb_block_kernel<true, kBlockTW>, (const void*)f32_bwd_kb_block_kernel<false, kBlockTW>,
                              (const void*)f32_bwd_kb_keyrows_kernel<2>, (const void*)f32_bwd_kb_keyrows_kernel<3>,
                              (const void*)f32_bwd_kb_keyrows_kernel<4>};
@@ -1702,12 +1726,12 @@ hipError_t f32_backward_bidir_kb(const Plan& p, const float* XQ, const float* XK
         constexpr int KBT = decltype(KBc)::value;
         const size_t rlds = kb_rows_lds_bytes<KBT>(dr, dv);
         hipError_t e;
-        GMA_LAUNCH("f32_bwd_kb_write", (f32_bwd_kb_rows_kernel<KBT, KB_KEY>), grid, dim3(kThreads), rlds, st, XK, V, p.N, H,
+        GMA_LAUNCH("f32_bwd_kb_write", (f32_bwd_kb_rows_kernel<KBT, KB_KEY, kRowsTW>), grid, dim3(1024 / kRowsTW), rlds, st, XK, V, p.N, H,
                    dr, dv, K, p.seg, G, v.c, v.inv, mu, cnone, eps, b.gk, partials, none);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, partials, G, Ei, memory);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        GMA_LAUNCH("f32_bwd_kb_query_rows", (f32_bwd_kb_rows_kernel<KBT, KB_QUERY>), grid, dim3(kThreads), rlds, st, XQ, dO,
+        GMA_LAUNCH("f32_bwd_kb_query_rows", (f32_bwd_kb_rows_kernel<KBT, KB_QUERY, kRowsTW>), grid, dim3(1024 / kRowsTW), rlds, st, XQ, dO,
                    p.Nq, H, dr, dv, K, p.seg_q, G, v.c, v.inv, mu, static_cast<const float*>(memory), eps, b.gq, none,
                    b.rowq);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -2702,7 +2726,7 @@ hipError_t with_kbc(int KB, F&& f) {
 
 template <int KB>
 hipError_t kbc_allow_lds_for() {
-    const void* fns[] = {(const void*)f32_bwd_kb_rows_kernel<KB, KB_KEY>, (const void*)f32_bwd_kb_rows_kernel<KB, KB_GAMMA>,
+    const void* fns[] = {(const void*)f32_bwd_kb_rows_kernel<KB, KB_KEY, kRowsTW>, (const void*)f32_bwd_kb_rows_kernel<KB, KB_GAMMA, kRowsTW>,
                          (const void*)f32_bwdc_kb_qrows_kernel<KB>, (const void*)f32_bwdc_kb_krows_kernel<KB>};
     for (const void* f : fns) {
         hipError_t r = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, int(kMaxLds));
@@ -2761,12 +2785,12 @@ hipError_t f32_backward_causal_kb(const Plan& p, const float* XQ, const float* X
         constexpr int KBT = decltype(KBc)::value;
         const size_t rlds = kb_rows_lds_bytes<KBT>(dr, dv);
         hipError_t r;
-        GMA_LAUNCH("f32_bwdc_kb_aggregate", (f32_bwd_kb_rows_kernel<KBT, KB_KEY>), tgrid, dim3(kThreads), rlds, st, XK, V,
+        GMA_LAUNCH("f32_bwdc_kb_aggregate", (f32_bwd_kb_rows_kernel<KBT, KB_KEY, kRowsTW>), tgrid, dim3(1024 / kRowsTW), rlds, st, XK, V,
                    p.N, H, dr, dv, K, tseg, NT, v.c, v.inv, mu, cnone, eps, b.gk, b.tmem, none);
         if ((r = hipGetLastError()) != hipSuccess) return r;
         GMA_LAUNCH("f32_bwdc_prefix", f32_prefix_kernel, egrid, dim3(kThreads), 0, st, b.tmem, NT, Ei, state_in, K, dv);
         if ((r = hipGetLastError()) != hipSuccess) return r;
-        GMA_LAUNCH("f32_bwdc_kb_query_gamma", (f32_bwd_kb_rows_kernel<KBT, KB_GAMMA>), tgrid, dim3(kThreads), rlds, st,
+        GMA_LAUNCH("f32_bwdc_kb_query_gamma", (f32_bwd_kb_rows_kernel<KBT, KB_GAMMA, kRowsTW>), tgrid, dim3(1024 / kRowsTW), rlds, st,
                    XQ, cnone, p.N, H, dr, dv, K, tseg, NT, v.c, v.inv, mu, cnone, eps, b.gq, none, none);
         if ((r = hipGetLastError()) != hipSuccess) return r;
         GMA_LAUNCH("f32_bwdc_kb_query_rows", f32_bwdc_kb_qrows_kernel<KBT>, tgrid, dim3(kThreads),
