@@ -578,8 +578,8 @@ def cpu_baseline(ws_list) -> dict:
 KERNEL_SYMBOL = {"bf16_scan": "gma::bf::scan_kernel", "bf16_bidir": "gma::bf::bidir_kernel",
                  "bf16_cross": "gma::bf::bidir_kernel", "bf16_resp": "gma::bf::resp_kernel",
                  "bf16_decode": "gma::dec::decode_kernel", "bf16_diag": "gma::diag::diag_fused_kernel",
-                 "f32_bwd_query": "gma::f32_bwd_tiled_kernel<1>", "f32_bwd_key": "gma::f32_bwd_tiled_kernel<2>",
-                 "f32_bwdc_query": "gma::f32_bwd_tiled_kernel<3>", "f32_bwdc_key": "gma::f32_bwd_tiled_kernel<4>",
+                 "f32_bwd_query": "gma::f32_bwd_tiled_kernel<1, ", "f32_bwd_key": "gma::f32_bwd_tiled_kernel<2, ",
+                 "f32_bwdc_query": "gma::f32_bwd_tiled_kernel<3, ", "f32_bwdc_key": "gma::f32_bwd_tiled_kernel<4, ",
                  "f32_bwd_kb_query": "gma::f32_bwd_kb_block_kernel<true, ",
                  "f32_bwd_kb_key": "gma::f32_bwd_kb_block_kernel<false, ",
                  "f32_bwdc_kb_query": "gma::f32_bwdc_kb_block_kernel<true, ",

@@ -256,15 +256,17 @@ __global__ void __launch_bounds__(kThreads)
 }
 
 // ---- register-tiled passes for K, d_r, d_v <= 64 (multiples of 4)
-// 256 threads as 16 row groups x 16 column groups: thread (tr, mc) owns rows r0 = 4 tr .. r0 + 3
-// and columns m0 = 4 mc .. m0 + 3 of every 64 x 64 product of a tile; operands are read from
-// LDS as 16-byte vectors.  The 16 threads of a row group are 16 adjacent lanes of one wave,
-// so row reductions are 16-lane shuffles.
+// 16 row groups of 64 / TW threads: a thread owns rows r0 .. r0 + 3 and columns m0 .. m0 + TW - 1
+// of every 64 x 64 product of a tile (1024 / TW threads; TW = 2 gives eight waves, two per SIMD
+// where the LDS allows one workgroup per CU).  Row operands are read from LDS as 16-byte vectors,
+// column operands as TW-wide ones.  The threads of a row group are adjacent lanes of one wave, so
+// row reductions are shuffles within the group.
 constexpr int kBT = 64;        // rows per tile
 constexpr int kLDT = kBT + 4;  // row stride of the transposed ([L][T]) tiles
 // BWD_CQUERY / BWD_CKEY: the causal passes (the memory a tile sees is the running prefix or
 // suffix, plus the masked in-tile products)
 enum { BWD_WRITE = 0, BWD_QUERY = 1, BWD_KEY = 2, BWD_CQUERY = 3, BWD_CKEY = 4 };
+constexpr int kTiledTW = 2;  // register tile width of these passes (eight waves)
 
 bool bwd_tiled_applies(const Plan& p) {
     return p.K % 4 == 0 && p.dr % 4 == 0 && p.dv % 4 == 0 && p.K <= 64 && p.dr <= 64 && p.dv <= 64;
@@ -331,23 +333,25 @@ __device__ __forceinline__ float max_lanes(float v) {
     return v;
 }
 
-// Responsibilities of the tile in xT (rows t = r0 + i, columns k = m0 + j of thread (tr, mc)):
-// the direct-form score of Eq. 16 from the LDS tables, then the softmax of Eq. 3b over the 16
-// lanes of the row group.  Rows at or beyond `rows` get zeros.
+// Responsibilities of the tile in xT (rows t = r0 + i, columns k = m0 + j, j < TW):
+// the direct-form score of Eq. 16 from the LDS tables, then the softmax of Eq. 3b over the
+// 64 / TW lanes of the row group.  Rows at or beyond `rows` get zeros.
+template <int TW>
 __device__ __forceinline__ void tile_gamma(const float* xT, const float* muT, const float* ivT, const float* cK,
-                                           int K, int dr, int LDK, int r0, int m0, int rows, float (&gam)[4][4]) {
-    float q[4][4] = {};
+                                           int K, int dr, int LDK, int r0, int m0, int rows, float (&gam)[4][TW]) {
+    constexpr int CG = 64 / TW;
+    float q[4][TW] = {};
     if (m0 < K) {
 #pragma unroll 4
         for (int d = 0; d < dr; ++d) {
-            float xa[4], ma[4], ia[4];
+            float xa[4], ma[TW], ia[TW];
             unpack(lds4(xT + d * kLDT + r0), xa);
-            unpack(lds4(muT + d * LDK + m0), ma);
-            unpack(lds4(ivT + d * LDK + m0), ia);
+            ldsw<TW>(muT + d * LDK + m0, ma);
+            ldsw<TW>(ivT + d * LDK + m0, ia);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < TW; ++j) {
                     const float df = xa[i] - ma[j];
                     q[i][j] = fmaf(df * df, ia[j], q[i][j]);
                 }
@@ -355,45 +359,47 @@ __device__ __forceinline__ void tile_gamma(const float* xT, const float* muT, co
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float sc[4], m = -INFINITY;
+        float sc[TW], m = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < TW; ++j) {
             sc[j] = m0 < K ? cK[m0 + j] - 0.5f * q[i][j] : -INFINITY;
             m = fmaxf(m, sc[j]);
         }
-        m = max16(m);
-        float e[4], sum = 0.0f;
+        m = max_lanes<CG>(m);
+        float e[TW], sum = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < TW; ++j) {
             e[j] = m0 < K ? expf(sc[j] - m) : 0.0f;
             sum += e[j];
         }
-        sum = sum16(sum);
+        sum = sum_lanes<CG>(sum);
         const float r = r0 + i < rows ? 1.0f / sum : 0.0f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) gam[i][j] = e[j] * r;
+        for (int j = 0; j < TW; ++j) gam[i][j] = e[j] * r;
     }
 }
 
-// The 4 x 4 responsibility block (rows r0.., components m0..) of the tile at n0 from a cache
+// The 4 x TW responsibility block (rows r0.., components m0..) of the tile at n0 from a cache
 // [.][K] (zeros beyond `rows` or K), and its store.
+template <int TW>
 __device__ __forceinline__ void gamma_from(const float* Gp, int64_t n0, int rows, int K, int r0, int m0,
-                                           float (&gam)[4][4]) {
+                                           float (&gam)[4][TW]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const bool ok = m0 < K && r0 + i < rows;
-        const float4 v = ok ? *reinterpret_cast<const float4*>(Gp + (n0 + r0 + i) * K + m0) : make_float4(0, 0, 0, 0);
-        gam[i][0] = v.x, gam[i][1] = v.y, gam[i][2] = v.z, gam[i][3] = v.w;
+        if (ok) ldsw<TW>(Gp + (n0 + r0 + i) * K + m0, gam[i]);
+        else
+#pragma unroll
+            for (int j = 0; j < TW; ++j) gam[i][j] = 0.0f;
     }
 }
+template <int TW>
 __device__ __forceinline__ void gamma_to(float* Gp, int64_t n0, int rows, int K, int r0, int m0,
-                                         const float (&gam)[4][4]) {
+                                         const float (&gam)[4][TW]) {
     if (m0 < K)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            if (r0 + i < rows)
-                *reinterpret_cast<float4*>(Gp + (n0 + r0 + i) * K + m0) =
-                    make_float4(gam[i][0], gam[i][1], gam[i][2], gam[i][3]);
+            if (r0 + i < rows) stsw<TW>(Gp + (n0 + r0 + i) * K + m0, gam[i]);
 }
 
 // Load rows [n0, n0 + rows) of X [.][dr] into xT [dr][kLDT] (zeros beyond `rows`) with NTH threads.
@@ -423,8 +429,8 @@ __device__ __forceinline__ void load_xT(const float* Xp, int64_t n0, int rows, i
 // Responsibility cache ([P][N][K] fp32, or NULL): gsave receives this pass's own responsibilities,
 // gload supplies them instead of the score loop, goload supplies the other side's (causal).
 // A cached value is the one the score loop would compute, so the results do not change.
-template <int MODE>
-__global__ void __launch_bounds__(kThreads)
+template <int MODE, int TW>
+__global__ void __launch_bounds__(1024 / TW)
     f32_bwd_tiled_kernel(const float* __restrict__ X, const float* __restrict__ Y, int64_t N, int H, int dr, int dv,
                          int K, int64_t seg, int G, const double* __restrict__ c, const double* __restrict__ inv,
                          const float* __restrict__ mu, const float* __restrict__ mem, float eps,
@@ -434,10 +440,11 @@ __global__ void __launch_bounds__(kThreads)
                          const float* __restrict__ goload) {
     constexpr bool QK = MODE != BWD_WRITE, CAUSAL = MODE >= BWD_CQUERY;
     constexpr bool QS = MODE == BWD_QUERY || MODE == BWD_CQUERY, KS = MODE == BWD_KEY || MODE == BWD_CKEY;
+    constexpr int NTH = 1024 / TW, CG = 64 / TW;  // threads; column groups of a row group
     extern __shared__ float lds[];
     const int64_t p = blockIdx.y;
     const int gi = blockIdx.x, h = int(p % H);
-    const int tid = threadIdx.x, tr = tid >> 4, mc = tid & 15, r0 = tr * 4, m0 = mc * 4;
+    const int tid = threadIdx.x, r0 = (tid / CG) * 4, m0 = (tid % CG) * TW;
     const int LDK = K + 4;
     float* muT = lds;                              // [dr][LDK]
     float* ivT = muT + dr * LDK;                   // [dr][LDK]
@@ -462,32 +469,32 @@ __global__ void __launch_bounds__(kThreads)
     {   // per-head tables and (query, key) the problem's memory
         const double *ch = c + size_t(h) * K, *ih = inv + size_t(h) * K * dr;
         const float* mh = mu + size_t(h) * K * dr;
-        for (int i = tid; i < K * dr; i += kThreads) {
+        for (int i = tid; i < K * dr; i += NTH) {
             const int k = i / dr, d = i - k * dr;
             muT[d * LDK + k] = mh[i];
             ivT[d * LDK + k] = float(ih[i]);
         }
-        for (int k = tid; k < K; k += kThreads) cK[k] = float(ch[k]);
+        for (int k = tid; k < K; k += NTH) cK[k] = float(ch[k]);
         if (QK) {
             const float* src = mem + (CAUSAL ? size_t(p) * G + gi : size_t(p)) * K * (dv + 1);
-            for (int i = tid; i < K * dv; i += kThreads) {
+            for (int i = tid; i < K * dv; i += NTH) {
                 const int k = i / dv, cc = i - k * dv;
                 const float v = src[i];
                 M[i] = v;
                 MT[cc * K + k] = v;
             }
-            for (int k = tid; k < K; k += kThreads) Zm[k] = src[K * dv + k];
+            for (int k = tid; k < K; k += NTH) Zm[k] = src[K * dv + k];
         }
     }
     __syncthreads();
     // moment accumulators (rows d = r0 + i, columns k = m0 + j) and their mu
-    float mreg[4][4], s1[4][4] = {}, s2[4][4] = {}, s0[4] = {};
+    float mreg[4][TW], s1[4][TW] = {}, s2[4][TW] = {}, s0[TW] = {};
     // memory-like accumulators (rows k = r0 + i, columns c = m0 + j): Vt, Z (write) or dVt, dZ (query)
-    float mv[4][4] = {}, mz[4] = {};
+    float mv[4][TW] = {}, mz[4] = {};
     const bool mom = QK && r0 < dr && m0 < K;
     if (mom)
         for (int i = 0; i < 4; ++i)
-            for (int j = 0; j < 4; ++j) mreg[i][j] = muT[(r0 + i) * LDK + m0 + j];
+            for (int j = 0; j < TW; ++j) mreg[i][j] = muT[(r0 + i) * LDK + m0 + j];
 
     const int64_t lo = int64_t(gi) * seg, hi = min<int64_t>(lo + seg, N);
     const float* Xp = X + size_t(p) * N * dr;
@@ -498,23 +505,23 @@ __global__ void __launch_bounds__(kThreads)
         const int rows = int(min<int64_t>(kBT, hi - n0));
         __syncthreads();  // the previous tile's reads are done
         if (CAUSAL) {  // the other side's responsibilities, in both layouts
-            float go[4][4];
+            float go[4][TW];
             if (goload) {
-                gamma_from(goload + size_t(p) * N * K, n0, rows, K, r0, m0, go);
+                gamma_from<TW>(goload + size_t(p) * N * K, n0, rows, K, r0, m0, go);
             } else {
-                load_xT(X2 + size_t(p) * N * dr, n0, rows, dr, xT);
+                load_xT<NTH>(X2 + size_t(p) * N * dr, n0, rows, dr, xT);
                 __syncthreads();
-                tile_gamma(xT, muT, ivT, cK, K, dr, LDK, r0, m0, rows, go);
+                tile_gamma<TW>(xT, muT, ivT, cK, K, dr, LDK, r0, m0, rows, go);
             }
             if (m0 < K) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) put4(Go + (r0 + i) * LG + m0, go[i][0], go[i][1], go[i][2], go[i][3]);
+                for (int i = 0; i < 4; ++i) stsw<TW>(Go + (r0 + i) * LG + m0, go[i]);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) put4(GoT + (m0 + j) * kLDT + r0, go[0][j], go[1][j], go[2][j], go[3][j]);
+                for (int j = 0; j < TW; ++j) put4(GoT + (m0 + j) * kLDT + r0, go[0][j], go[1][j], go[2][j], go[3][j]);
             }
             // V rows (query) or dO / D rows with D, a' (key)
             const float* Y2p = Y2 + size_t(p) * N * dv;
-            for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
+            for (int i = tid; i < kBT * (dv / 4); i += NTH) {
                 const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
                 float4 v = t < rows ? *reinterpret_cast<const float4*>(Y2p + (n0 + t) * dv + cc) : make_float4(0, 0, 0, 0);
                 if (MODE == BWD_CKEY && t < rows) {
@@ -524,15 +531,15 @@ __global__ void __launch_bounds__(kThreads)
                 *reinterpret_cast<float4*>(Rw + t * LV4 + cc) = v;
             }
             if (MODE == BWD_CKEY)
-                for (int t = tid; t < kBT; t += kThreads) {
+                for (int t = tid; t < kBT; t += NTH) {
                     const float D = t < rows ? rowda[(size_t(p) * N + n0 + t) * 2] : 1.0f;
                     Dv[t] = D;
                     Av[t] = t < rows ? rowda[(size_t(p) * N + n0 + t) * 2 + 1] / D : 0.0f;
                 }
             __syncthreads();  // xT is free again
         }
-        load_xT(Xp, n0, rows, dr, xT);
-        for (int i = tid; i < kBT * (dv / 4); i += kThreads) {
+        load_xT<NTH>(Xp, n0, rows, dr, xT);
+        for (int i = tid; i < kBT * (dv / 4); i += NTH) {
             const int t = i / (dv / 4), cc = (i - t * (dv / 4)) * 4;
             const float4 v = t < rows ? *reinterpret_cast<const float4*>(Yp + (n0 + t) * dv + cc) : make_float4(0, 0, 0, 0);
             if (KS) {
@@ -547,20 +554,20 @@ __global__ void __launch_bounds__(kThreads)
         __syncthreads();
 
         // responsibilities (rows t, columns k): direct-form score of Eq. 16, softmax of Eq. 3b
-        float gam[4][4];
+        float gam[4][TW];
         if (gload)
-            gamma_from(gload + size_t(p) * N * K, n0, rows, K, r0, m0, gam);
+            gamma_from<TW>(gload + size_t(p) * N * K, n0, rows, K, r0, m0, gam);
         else
-            tile_gamma(xT, muT, ivT, cK, K, dr, LDK, r0, m0, rows, gam);
-        if (gsave) gamma_to(gsave + size_t(p) * N * K, n0, rows, K, r0, m0, gam);
+            tile_gamma<TW>(xT, muT, ivT, cK, K, dr, LDK, r0, m0, rows, gam);
+        if (gsave) gamma_to<TW>(gsave + size_t(p) * N * K, n0, rows, K, r0, m0, gam);
         if (MODE == BWD_WRITE) __syncthreads();  // gamma overwrites X^T
         if (m0 < K) {
             if (!KS)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) put4(g + (r0 + i) * K + m0, gam[i][0], gam[i][1], gam[i][2], gam[i][3]);
+                for (int i = 0; i < 4; ++i) stsw<TW>(g + (r0 + i) * K + m0, gam[i]);
             if (QK)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) put4(gT + (m0 + j) * kLDT + r0, gam[0][j], gam[1][j], gam[2][j], gam[3][j]);
+                for (int j = 0; j < TW; ++j) put4(gT + (m0 + j) * kLDT + r0, gam[0][j], gam[1][j], gam[2][j], gam[3][j]);
         }
         __syncthreads();
 
@@ -568,14 +575,14 @@ __global__ void __launch_bounds__(kThreads)
             if (r0 < K && m0 < dv)
 #pragma unroll 4
                 for (int t = 0; t < rows; ++t) {
-                    float ga[4], ya[4];
+                    float ga[4], ya[TW];
                     unpack(lds4(g + t * K + r0), ga);
-                    unpack(lds4(Yr + t * dv + m0), ya);
+                    ldsw<TW>(Yr + t * dv + m0, ya);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         mz[i] += ga[i];
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) mv[i][j] = fmaf(ga[i], ya[j], mv[i][j]);
+                        for (int j = 0; j < TW; ++j) mv[i][j] = fmaf(ga[i], ya[j], mv[i][j]);
                     }
                 }
             continue;
@@ -587,37 +594,37 @@ __global__ void __launch_bounds__(kThreads)
         if (CAUSAL) {
             const float* gqT = QS ? gT : GoT;  // [K][kLDT] gamma^Q transposed
             const float* gkT = QS ? GoT : gT;  // [K][kLDT] gamma^K transposed
-            float ca[4][4] = {}, aa[4][4] = {};
+            float ca[4][TW] = {}, aa[4][TW] = {};
             const bool live = m0 <= r0 + 3 && r0 < rows;  // the block has entries with j <= i
             if (live) {
 #pragma unroll 4
                 for (int k = 0; k < K; ++k) {
-                    float qa[4], ka[4];
+                    float qa[4], ka[TW];
                     unpack(lds4(gqT + k * kLDT + r0), qa);
-                    unpack(lds4(gkT + k * kLDT + m0), ka);
+                    ldsw<TW>(gkT + k * kLDT + m0, ka);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) ca[i][j] = fmaf(qa[i], ka[j], ca[i][j]);
+                        for (int j = 0; j < TW; ++j) ca[i][j] = fmaf(qa[i], ka[j], ca[i][j]);
                 }
                 if (MODE == BWD_CKEY) {
 #pragma unroll 4
                     for (int cc = 0; cc < dv; ++cc) {
-                        float va[4], oa[4];
-                        unpack(lds4(YT + cc * kLDT + m0), va);  // V^T
+                        float va[TW], oa[4];
+                        ldsw<TW>(YT + cc * kLDT + m0, va);  // V^T
 #pragma unroll
                         for (int i = 0; i < 4; ++i) oa[i] = Rw[(r0 + i) * LV4 + cc];  // dO'
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) aa[i][j] = fmaf(oa[i], va[j], aa[i][j]);
+                            for (int j = 0; j < TW; ++j) aa[i][j] = fmaf(oa[i], va[j], aa[i][j]);
                     }
                 }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < TW; ++j) {
                     const bool in = live && m0 + j <= r0 + i && r0 + i < rows;
                     ca[i][j] = in ? ca[i][j] : 0.0f;
                     aa[i][j] = in ? aa[i][j] - Av[r0 + i] : 0.0f;
@@ -625,42 +632,42 @@ __global__ void __launch_bounds__(kThreads)
                 }
             if (QS) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) put4(Cm + (m0 + j) * kLDT + r0, ca[0][j], ca[1][j], ca[2][j], ca[3][j]);
+                for (int j = 0; j < TW; ++j) put4(Cm + (m0 + j) * kLDT + r0, ca[0][j], ca[1][j], ca[2][j], ca[3][j]);
             } else {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    put4(Cm + (r0 + i) * kLDT + m0, ca[i][0], ca[i][1], ca[i][2], ca[i][3]);
-                    put4(Am + (r0 + i) * kLDT + m0, aa[i][0], aa[i][1], aa[i][2], aa[i][3]);
+                    stsw<TW>(Cm + (r0 + i) * kLDT + m0, ca[i]);
+                    stsw<TW>(Am + (r0 + i) * kLDT + m0, aa[i]);
                 }
             }
             __syncthreads();
         }
         const int tmax = min(r0 + 4, rows);  // causal: in-tile keys j <= the block's last query row
 
-        float gg[4][4] = {};  // upstream gradient at the responsibilities (rows t, columns k)
+        float gg[4][TW] = {};  // upstream gradient at the responsibilities (rows t, columns k)
         if (QS) {
             // N = gamma Vt (rows t, columns c); D = gamma Z + eps; dO . N
-            float nv[4][4] = {};
+            float nv[4][TW] = {};
             if (m0 < dv)
 #pragma unroll 4
                 for (int k = 0; k < K; ++k) {
-                    float ga[4], va[4];
+                    float ga[4], va[TW];
                     unpack(lds4(gT + k * kLDT + r0), ga);
-                    unpack(lds4(M + k * dv + m0), va);
+                    ldsw<TW>(M + k * dv + m0, va);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ga[i], va[j], nv[i][j]);
+                        for (int j = 0; j < TW; ++j) nv[i][j] = fmaf(ga[i], va[j], nv[i][j]);
                 }
             if (CAUSAL && m0 < dv)  // + sum_{j <= t} C_tj V_j
                 for (int j = 0; j < tmax; ++j) {
-                    float ca[4], va[4];
+                    float ca[4], va[TW];
                     unpack(lds4(Cm + j * kLDT + r0), ca);
-                    unpack(lds4(Rw + j * LV4 + m0), va);
+                    ldsw<TW>(Rw + j * LV4 + m0, va);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) nv[i][jj] = fmaf(ca[i], va[jj], nv[i][jj]);
+                        for (int jj = 0; jj < TW; ++jj) nv[i][jj] = fmaf(ca[i], va[jj], nv[i][jj]);
                 }
             float Dt[4], An[4];
 #pragma unroll
@@ -668,32 +675,32 @@ __global__ void __launch_bounds__(kThreads)
                 float dp = cs[i], ap = 0.0f;
                 if (m0 < K)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) dp = fmaf(gam[i][j], Zm[m0 + j], dp);
+                    for (int j = 0; j < TW; ++j) dp = fmaf(gam[i][j], Zm[m0 + j], dp);
                 if (m0 < dv) {
-                    float ya[4];
-                    unpack(lds4(Yr + (r0 + i) * dv + m0), ya);
+                    float ya[TW];
+                    ldsw<TW>(Yr + (r0 + i) * dv + m0, ya);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) ap = fmaf(ya[j], nv[i][j], ap);
+                    for (int j = 0; j < TW; ++j) ap = fmaf(ya[j], nv[i][j], ap);
                 }
-                Dt[i] = sum16(dp) + eps;
-                An[i] = sum16(ap);
+                Dt[i] = sum_lanes<CG>(dp) + eps;
+                An[i] = sum_lanes<CG>(ap);
             }
             // dO' = dO / D in both layouts (each thread rescales its own entries), D and a' = dO . N / D^2
-            float sy[4][4];
+            float sy[4][TW];
             if (m0 < dv) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    float ya[4];
-                    unpack(lds4(Yr + (r0 + i) * dv + m0), ya);
+                    float ya[TW];
+                    ldsw<TW>(Yr + (r0 + i) * dv + m0, ya);
                     const float rD = 1.0f / Dt[i];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) sy[i][j] = ya[j] * rD;
-                    put4(Yr + (r0 + i) * dv + m0, sy[i][0], sy[i][1], sy[i][2], sy[i][3]);
+                    for (int j = 0; j < TW; ++j) sy[i][j] = ya[j] * rD;
+                    stsw<TW>(Yr + (r0 + i) * dv + m0, sy[i]);
                 }
 #pragma unroll
-                for (int j = 0; j < 4; ++j) put4(YT + (m0 + j) * kLDT + r0, sy[0][j], sy[1][j], sy[2][j], sy[3][j]);
+                for (int j = 0; j < TW; ++j) put4(YT + (m0 + j) * kLDT + r0, sy[0][j], sy[1][j], sy[2][j], sy[3][j]);
             }
-            if (mc == 0)
+            if (m0 == 0)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     Dv[r0 + i] = Dt[i];
@@ -706,7 +713,7 @@ __global__ void __launch_bounds__(kThreads)
             __syncthreads();
             // causal: A^T (A_tj = dO'_t . V_j - a'_t for j <= t) over C^T, whose reads are done
             if (CAUSAL) {
-                float aa[4][4] = {};
+                float aa[4][TW] = {};
                 const bool live = m0 <= r0 + 3 && r0 < rows;
                 if (live)
 #pragma unroll 4
@@ -714,151 +721,150 @@ __global__ void __launch_bounds__(kThreads)
                         float oa[4], va[4];
                         unpack(lds4(YT + cc * kLDT + r0), oa);  // dO'^T
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) va[j] = Rw[(m0 + j) * LV4 + cc];  // V
+                        for (int j = 0; j < TW; ++j) va[j] = Rw[(m0 + j) * LV4 + cc];  // V
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) aa[i][j] = fmaf(oa[i], va[j], aa[i][j]);
+                            for (int j = 0; j < TW; ++j) aa[i][j] = fmaf(oa[i], va[j], aa[i][j]);
                     }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < TW; ++j)
                         aa[i][j] = live && m0 + j <= r0 + i && r0 + i < rows ? aa[i][j] - Av[r0 + i] : 0.0f;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) put4(Cm + (m0 + j) * kLDT + r0, aa[0][j], aa[1][j], aa[2][j], aa[3][j]);
+                for (int j = 0; j < TW; ++j) put4(Cm + (m0 + j) * kLDT + r0, aa[0][j], aa[1][j], aa[2][j], aa[3][j]);
             }
             // dVt += gamma^T dO', dZ -= gamma^T a' (rows k, columns c)
             if (r0 < K && m0 < dv)
 #pragma unroll 4
                 for (int t = 0; t < rows; ++t) {
-                    float ga[4], ya[4];
+                    float ga[4], ya[TW];
                     unpack(lds4(g + t * K + r0), ga);
-                    unpack(lds4(Yr + t * dv + m0), ya);
+                    ldsw<TW>(Yr + t * dv + m0, ya);
                     const float at = Av[t];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         mz[i] = fmaf(-ga[i], at, mz[i]);
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) mv[i][j] = fmaf(ga[i], ya[j], mv[i][j]);
+                        for (int j = 0; j < TW; ++j) mv[i][j] = fmaf(ga[i], ya[j], mv[i][j]);
                     }
                 }
             // g = dO' Vt^T - a' Z
             if (m0 < K) {
 #pragma unroll 4
                 for (int cc = 0; cc < dv; ++cc) {
-                    float ya[4], va[4];
+                    float ya[4], va[TW];
                     unpack(lds4(YT + cc * kLDT + r0), ya);
-                    unpack(lds4(MT + cc * K + m0), va);
+                    ldsw<TW>(MT + cc * K + m0, va);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(ya[i], va[j], gg[i][j]);
+                        for (int j = 0; j < TW; ++j) gg[i][j] = fmaf(ya[i], va[j], gg[i][j]);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(-Av[r0 + i], Zm[m0 + j], gg[i][j]);
+                    for (int j = 0; j < TW; ++j) gg[i][j] = fmaf(-Av[r0 + i], Zm[m0 + j], gg[i][j]);
             }
             if (CAUSAL) {  // + sum_{j <= t} A_tj gamma^K_j
                 __syncthreads();
                 if (m0 < K)
                     for (int j = 0; j < tmax; ++j) {
-                        float ta[4], ka[4];
+                        float ta[4], ka[TW];
                         unpack(lds4(Cm + j * kLDT + r0), ta);
-                        unpack(lds4(Go + j * LG + m0), ka);
+                        ldsw<TW>(Go + j * LG + m0, ka);
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
 #pragma unroll
-                            for (int jj = 0; jj < 4; ++jj) gg[i][jj] = fmaf(ta[i], ka[jj], gg[i][jj]);
+                            for (int jj = 0; jj < TW; ++jj) gg[i][jj] = fmaf(ta[i], ka[jj], gg[i][jj]);
                     }
             }
         } else {
             // dV = gamma dVt (rows t, columns c)
             if (m0 < dv) {
-                float nv[4][4] = {};
+                float nv[4][TW] = {};
 #pragma unroll 4
                 for (int k = 0; k < K; ++k) {
-                    float ga[4], va[4];
+                    float ga[4], va[TW];
                     unpack(lds4(gT + k * kLDT + r0), ga);
-                    unpack(lds4(M + k * dv + m0), va);
+                    ldsw<TW>(M + k * dv + m0, va);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ga[i], va[j], nv[i][j]);
+                        for (int j = 0; j < TW; ++j) nv[i][j] = fmaf(ga[i], va[j], nv[i][j]);
                 }
                 if (CAUSAL)  // + sum_{i >= j} C_ij dO'_i (rows j = r0.., queries i >= r0)
                     for (int i2 = r0; i2 < rows; ++i2) {
-                        float ca[4], oa[4];
+                        float ca[4], oa[TW];
                         unpack(lds4(Cm + i2 * kLDT + r0), ca);
-                        unpack(lds4(Rw + i2 * LV4 + m0), oa);
+                        ldsw<TW>(Rw + i2 * LV4 + m0, oa);
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) nv[i][j] = fmaf(ca[i], oa[j], nv[i][j]);
+                            for (int j = 0; j < TW; ++j) nv[i][j] = fmaf(ca[i], oa[j], nv[i][j]);
                     }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (r0 + i < rows)
-                        *reinterpret_cast<float4*>(dY + (size_t(p) * N + n0 + r0 + i) * dv + m0) =
-                            make_float4(nv[i][0], nv[i][1], nv[i][2], nv[i][3]);
+                        stsw<TW>(dY + (size_t(p) * N + n0 + r0 + i) * dv + m0, nv[i]);
             }
             // g = V dVt^T + dZ
             if (m0 < K) {
 #pragma unroll 4
                 for (int cc = 0; cc < dv; ++cc) {
-                    float ya[4], va[4];
+                    float ya[4], va[TW];
                     unpack(lds4(YT + cc * kLDT + r0), ya);
-                    unpack(lds4(MT + cc * K + m0), va);
+                    ldsw<TW>(MT + cc * K + m0, va);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(ya[i], va[j], gg[i][j]);
+                        for (int j = 0; j < TW; ++j) gg[i][j] = fmaf(ya[i], va[j], gg[i][j]);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) gg[i][j] += Zm[m0 + j];
+                    for (int j = 0; j < TW; ++j) gg[i][j] += Zm[m0 + j];
                 if (CAUSAL)  // + sum_{i >= j} A_ij gamma^Q_i
                     for (int i2 = r0; i2 < rows; ++i2) {
-                        float ta[4], qa[4];
+                        float ta[4], qa[TW];
                         unpack(lds4(Am + i2 * kLDT + r0), ta);
-                        unpack(lds4(Go + i2 * LG + m0), qa);
+                        ldsw<TW>(Go + i2 * LG + m0, qa);
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) gg[i][j] = fmaf(ta[i], qa[j], gg[i][j]);
+                            for (int j = 0; j < TW; ++j) gg[i][j] = fmaf(ta[i], qa[j], gg[i][j]);
                     }
             }
         }
         // Eq. 18: ds = gamma (g - gamma . g)
-        float ds[4][4];
+        float ds[4][TW];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float w = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) w = fmaf(gam[i][j], gg[i][j], w);
-            w = sum16(w);
+            for (int j = 0; j < TW; ++j) w = fmaf(gam[i][j], gg[i][j], w);
+            w = sum_lanes<CG>(w);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) ds[i][j] = gam[i][j] * (gg[i][j] - w);
+            for (int j = 0; j < TW; ++j) ds[i][j] = gam[i][j] * (gg[i][j] - w);
         }
         __syncthreads();  // every read of gamma is done
         if (m0 < K) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) put4(g + (r0 + i) * K + m0, ds[i][0], ds[i][1], ds[i][2], ds[i][3]);
+            for (int i = 0; i < 4; ++i) stsw<TW>(g + (r0 + i) * K + m0, ds[i]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) put4(gT + (m0 + j) * kLDT + r0, ds[0][j], ds[1][j], ds[2][j], ds[3][j]);
+            for (int j = 0; j < TW; ++j) put4(gT + (m0 + j) * kLDT + r0, ds[0][j], ds[1][j], ds[2][j], ds[3][j]);
         }
         __syncthreads();
         // dX (rows d, columns t): dx_td = -sum_k ds_tk (x_td - mu_kd) / sigma2_kd
         if (r0 < dr) {
-            float xa[4][4], acc[4][4] = {};
+            float xa[4][TW], acc[4][TW] = {};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) unpack(lds4(xT + (r0 + i) * kLDT + m0), xa[i]);
+            for (int i = 0; i < 4; ++i) ldsw<TW>(xT + (r0 + i) * kLDT + m0, xa[i]);
 #pragma unroll 4
             for (int k = 0; k < K; ++k) {
-                float da[4], ma[4], ia[4];
-                unpack(lds4(gT + k * kLDT + m0), da);
+                float da[TW], ma[4], ia[4];
+                ldsw<TW>(gT + k * kLDT + m0, da);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     ma[i] = muT[(r0 + i) * LDK + k];
@@ -867,10 +873,10 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(da[j] * ia[i], xa[i][j] - ma[i], acc[i][j]);
+                    for (int j = 0; j < TW; ++j) acc[i][j] = fmaf(da[j] * ia[i], xa[i][j] - ma[i], acc[i][j]);
             }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < TW; ++j)
                 if (m0 + j < rows)
                     *reinterpret_cast<float4*>(dX + (size_t(p) * N + n0 + m0 + j) * dr + r0) =
                         make_float4(-acc[0][j], -acc[1][j], -acc[2][j], -acc[3][j]);
@@ -879,16 +885,16 @@ __global__ void __launch_bounds__(kThreads)
         if (mom)
 #pragma unroll 4
             for (int t = 0; t < rows; ++t) {
-                float da[4], xa[4];
-                unpack(lds4(g + t * K + m0), da);
+                float da[TW], xa[4];
+                ldsw<TW>(g + t * K + m0, da);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) xa[i] = xT[(r0 + i) * kLDT + t];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) s0[j] += da[j];
+                for (int j = 0; j < TW; ++j) s0[j] += da[j];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
+                    for (int j = 0; j < TW; ++j) {
                         const float df = xa[i] - mreg[i][j], w = da[j] * df;
                         s1[i][j] += w;
                         s2[i][j] = fmaf(w, df, s2[i][j]);
@@ -897,29 +903,29 @@ __global__ void __launch_bounds__(kThreads)
         if (CAUSAL && r0 < K && m0 < dv) {
             // advance the memory past the tile (its last reads were before the ds barriers):
             // query: + gamma^K^T [V | 1] (Eq. 6b); key: + gamma^Q^T [dO' | -a']
-            float ua[4][4] = {}, uz[4] = {};
+            float ua[4][TW] = {}, uz[4] = {};
             for (int t = 0; t < rows; ++t) {
-                float ga[4], ya[4];
+                float ga[4], ya[TW];
                 unpack(lds4(Go + t * LG + r0), ga);
-                unpack(lds4(Rw + t * LV4 + m0), ya);
+                ldsw<TW>(Rw + t * LV4 + m0, ya);
                 const float zt = QS ? 1.0f : -Av[t];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     uz[i] = fmaf(ga[i], zt, uz[i]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) ua[i][j] = fmaf(ga[i], ya[j], ua[i][j]);
+                    for (int j = 0; j < TW; ++j) ua[i][j] = fmaf(ga[i], ya[j], ua[i][j]);
                 }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float mm[4];
-                unpack(lds4(M + (r0 + i) * dv + m0), mm);
+                float mm[TW];
+                ldsw<TW>(M + (r0 + i) * dv + m0, mm);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) mm[j] += ua[i][j];
-                put4(M + (r0 + i) * dv + m0, mm[0], mm[1], mm[2], mm[3]);
+                for (int j = 0; j < TW; ++j) mm[j] += ua[i][j];
+                stsw<TW>(M + (r0 + i) * dv + m0, mm);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) MT[(m0 + j) * K + r0 + i] = mm[j];
-                if (mc == 0) Zm[r0 + i] += uz[i];
+                for (int j = 0; j < TW; ++j) MT[(m0 + j) * K + r0 + i] = mm[j];
+                if (m0 == 0) Zm[r0 + i] += uz[i];
             }
         }
     }
@@ -928,8 +934,8 @@ __global__ void __launch_bounds__(kThreads)
         float* mp = mem_part + (size_t(p) * G + gi) * size_t(K) * (dv + 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<float4*>(mp + (r0 + i) * dv + m0) = make_float4(mv[i][0], mv[i][1], mv[i][2], mv[i][3]);
-        if (mc == 0)
+            stsw<TW>(mp + (r0 + i) * dv + m0, mv[i]);
+        if (m0 == 0)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mp[K * dv + r0 + i] = mz[i];
     }
@@ -938,13 +944,13 @@ __global__ void __launch_bounds__(kThreads)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < TW; ++j) {
                 pp[(m0 + j) * dr + r0 + i] = s1[i][j];
                 pp[K * dr + (m0 + j) * dr + r0 + i] = s2[i][j];
             }
-        if (tr == 0)
+        if (r0 == 0)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) pp[2 * K * dr + m0 + j] = s0[j];
+            for (int j = 0; j < TW; ++j) pp[2 * K * dr + m0 + j] = s0[j];
     }
 }
 
@@ -1023,7 +1029,7 @@ int kb_blocks(int64_t K) { return int((K + kKB - 1) / kKB); }
 
 // Responsibilities of rows [n0, n0 + rows) of one problem for all K components: the direct-form
 // score of Eq. 16 from fp32 tables of one block at a time, then the softmax of Eq. 3b over all
-// blocks (row maximum and sum over the 16 lanes of the row group).  Into S ([64][LK], zero past
+// blocks (row maximum and sum over the lanes of the row group).  Into S ([64][LK], zero past
 // `rows` and K) and the cache rows gc ([.][K] of this problem).  LDS: xT [dr][kLDT], muT and ivT
 // [dr][kLB], cB [kKB].
 template <int KB, int TW>
@@ -1603,9 +1609,9 @@ hipError_t bwd_allow_lds() {
         const void* fns[] = {(const void*)f32_write_kernel, (const void*)f32_bwd_side_kernel<true, false>,
                              (const void*)f32_bwd_side_kernel<false, false>, (const void*)f32_bwd_side_kernel<true, true>,
                              (const void*)f32_bwd_side_kernel<false, true>,
-                             (const void*)f32_bwd_tiled_kernel<BWD_WRITE>, (const void*)f32_bwd_tiled_kernel<BWD_QUERY>,
-                             (const void*)f32_bwd_tiled_kernel<BWD_KEY>, (const void*)f32_bwd_tiled_kernel<BWD_CQUERY>,
-                             (const void*)f32_bwd_tiled_kernel<BWD_CKEY>,
+                             (const void*)f32_bwd_tiled_kernel<BWD_WRITE, kTiledTW>, (const void*)f32_bwd_tiled_kernel<BWD_QUERY, kTiledTW>,
+                             (const void*)f32_bwd_tiled_kernel<BWD_KEY, kTiledTW>, (const void*)f32_bwd_tiled_kernel<BWD_CQUERY, kTiledTW>,
+                             (const void*)f32_bwd_tiled_kernel<BWD_CKEY, kTiledTW>,
                              (const void*)f32_bwd_kb_rows_kernel<2, KB_KEY, kRowsTW>, (const void*)f32_bwd_kb_rows_kernel<2, KB_QUERY, kRowsTW>,
                              (const void*)f32_bwd_kb_rows_kernel<3, KB_KEY, kRowsTW>, (const void*)f32_bwd_kb_rows_kernel<3, KB_QUERY, kRowsTW>,
                              (const void*)f32_bwd_kb_rows_kernel<4, KB_KEY, kRowsTW>, (const void*)f32_bwd_kb_rows_kernel<4, KB_QUERY, kRowsTW>,
@@ -1793,7 +1799,7 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     const int H = int(p.H), dr = int(p.dr), dv = int(p.dv), K = int(p.K), G = int(p.G);
     const SideConfig side = side_config(K, dr, dv);
     if (bwd_tiled_applies(p)) {
-        GMA_LAUNCH("f32_bwd_write", f32_bwd_tiled_kernel<BWD_WRITE>, grid, dim3(kThreads),
+        GMA_LAUNCH("f32_bwd_write", (f32_bwd_tiled_kernel<BWD_WRITE, kTiledTW>), grid, dim3(1024 / kTiledTW),
                    bwd_tiled_lds_bytes(BWD_WRITE, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
                    cnone, eps, none, none, partials, none, cnone, cnone, none, gk_cache, cnone, cnone);
     } else {
@@ -1805,7 +1811,7 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, partials, G, Ei, memory);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (bwd_tiled_applies(p)) {
-        GMA_LAUNCH("f32_bwd_query", f32_bwd_tiled_kernel<BWD_QUERY>, grid, dim3(kThreads),
+        GMA_LAUNCH("f32_bwd_query", (f32_bwd_tiled_kernel<BWD_QUERY, kTiledTW>), grid, dim3(1024 / kTiledTW),
                    bwd_tiled_lds_bytes(BWD_QUERY, K, dr, dv), st, XQ, dO, p.Nq, H, dr, dv, K, p.seg_q, G, v.c, v.inv, mu,
                    static_cast<const float*>(memory), eps, dXQ, none, dpart, ppart, cnone, cnone, none, none, cnone,
                    cnone);
@@ -1822,7 +1828,7 @@ hipError_t f32_backward_bidir(const Plan& p, const float* XQ, const float* XK, c
     GMA_LAUNCH("f32_bwd_combine", f32_combine_kernel, cgrid, dim3(kThreads), 0, st, dpart, G, Ei, dmem);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (bwd_tiled_applies(p)) {
-        GMA_LAUNCH("f32_bwd_key", f32_bwd_tiled_kernel<BWD_KEY>, grid, dim3(kThreads),
+        GMA_LAUNCH("f32_bwd_key", (f32_bwd_tiled_kernel<BWD_KEY, kTiledTW>), grid, dim3(1024 / kTiledTW),
                    bwd_tiled_lds_bytes(BWD_KEY, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
                    static_cast<const float*>(dmem), eps, dXK, dV, none, ppart_key, cnone, cnone, none, none,
                    static_cast<const float*>(gk_cache), cnone);
@@ -2879,7 +2885,7 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
     // segment aggregates of the forward memory (one segment: the prefix writes zeros); the tiled
     // passes also take Gamma_K from this pass, so it runs for one segment too
     if (tiled || (p.G > 1 && bwd_tiled_applies(p))) {
-        GMA_LAUNCH("f32_bwdc_aggregate", f32_bwd_tiled_kernel<BWD_WRITE>, grid, dim3(kThreads),
+        GMA_LAUNCH("f32_bwdc_aggregate", (f32_bwd_tiled_kernel<BWD_WRITE, kTiledTW>), grid, dim3(1024 / kTiledTW),
                    bwd_tiled_lds_bytes(BWD_WRITE, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
                    cnone, eps, none, none, states, none, cnone, cnone, none, tiled ? gk_cache : none, cnone, cnone);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -2892,7 +2898,7 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
     GMA_LAUNCH("f32_bwdc_prefix", f32_prefix_kernel, egrid, dim3(kThreads), 0, st, states, G, Ei, state_in, K, dv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (tiled) {  // register-tiled passes with the running memory in LDS
-        GMA_LAUNCH("f32_bwdc_query", f32_bwd_tiled_kernel<BWD_CQUERY>, grid, dim3(kThreads),
+        GMA_LAUNCH("f32_bwdc_query", (f32_bwd_tiled_kernel<BWD_CQUERY, kTiledTW>), grid, dim3(1024 / kTiledTW),
                    bwd_tiled_lds_bytes(BWD_CQUERY, K, dr, dv), st, XQ, dO, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
                    static_cast<const float*>(states), eps, dXQ, none, seg_part, ppart, XK, V, rowda, gq_cache, cnone,
                    static_cast<const float*>(gk_cache));
@@ -2900,7 +2906,7 @@ hipError_t f32_backward_causal(const Plan& p, const float* XQ, const float* XK, 
         GMA_LAUNCH("f32_bwdc_suffix", f32_suffix_kernel, egrid, dim3(kThreads), 0, st, seg_part, G, Ei, dstate_out,
                    dstate_in, K, dv);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        GMA_LAUNCH("f32_bwdc_key", f32_bwd_tiled_kernel<BWD_CKEY>, grid, dim3(kThreads),
+        GMA_LAUNCH("f32_bwdc_key", (f32_bwd_tiled_kernel<BWD_CKEY, kTiledTW>), grid, dim3(1024 / kTiledTW),
                    bwd_tiled_lds_bytes(BWD_CKEY, K, dr, dv), st, XK, V, p.N, H, dr, dv, K, p.seg, G, v.c, v.inv, mu,
                    static_cast<const float*>(seg_part), eps, dXK, dV, none, ppart_key, XQ, dO, rowda, none,
                    static_cast<const float*>(gk_cache), static_cast<const float*>(gq_cache));
