@@ -31,38 +31,40 @@ F32Params f32_params_view(const Plan& p, char* ws) {
     return v;
 }
 
-// One block per head.  c_k = log pi_k - 1/2 sum_d log sigma2_kd in fp64, then shifted by
-// its maximum over k (a k-independent shift, exact in the softmax) so the fp32 value is small.
-// Each wave takes one component at a time, its lanes over d.
+// Grid (H, ceil(K / 4)): wave w of block (h, b) takes component k = 4 b + w of head h, its lanes
+// over d: c_k = log pi_k - 1/2 sum_d log sigma2_kd in fp64 and the table of 1 / sigma2_kd.
 __global__ void __launch_bounds__(kThreads) f32_params_kernel(const float* __restrict__ s2,
                                                               const float* __restrict__ pi, int K,
                                                               int dr, double* __restrict__ c_out,
                                                               double* __restrict__ inv_out) {
     const int h = blockIdx.x;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    __shared__ double cd[256];
-    __shared__ double red[kThreads / kWave];
-    const float* s2h = s2 + size_t(h) * K * dr;
-    for (int k = wave; k < K; k += kThreads / kWave) {
-        double acc = 0.0;
-        for (int d = lane; d < dr; d += kWave) {
-            const double v = double(s2h[size_t(k) * dr + d]);
-            acc += log(v);
-            inv_out[(size_t(h) * K + k) * dr + d] = 1.0 / v;
-        }
-        for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
-        if (lane == 0) cd[k] = log(double(pi[size_t(h) * K + k])) - 0.5 * acc;
+    const int lane = threadIdx.x & 63, k = blockIdx.y * (kThreads / kWave) + (threadIdx.x >> 6);
+    if (k >= K) return;  // the whole wave
+    const float* s2k = s2 + (size_t(h) * K + k) * dr;
+    double acc = 0.0;
+    for (int d = lane; d < dr; d += kWave) {
+        const double v = double(s2k[d]);
+        acc += log(v);
+        inv_out[(size_t(h) * K + k) * dr + d] = 1.0 / v;
     }
+    for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, kWave);
+    if (lane == 0) c_out[size_t(h) * K + k] = log(double(pi[size_t(h) * K + k])) - 0.5 * acc;
+}
+
+// Grid (H): c_k of head h shifted by its maximum over k (a k-independent shift, exact in the
+// softmax), so the fp32 value the score loops take is small.
+__global__ void __launch_bounds__(kThreads) f32_params_shift_kernel(int K, double* __restrict__ c) {
+    __shared__ double red[kThreads / kWave];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    double* ch = c + size_t(blockIdx.x) * K;
+    double m = -INFINITY;
+    for (int k = threadIdx.x; k < K; k += kThreads) m = fmax(m, ch[k]);
+    for (int o = 32; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, kWave));
+    if (lane == 0) red[wave] = m;
     __syncthreads();
-    double local_max = -INFINITY;
-    for (int k = threadIdx.x; k < K; k += kThreads) local_max = fmax(local_max, cd[k]);
-    // block max
-    for (int o = 32; o >= 1; o >>= 1) local_max = fmax(local_max, __shfl_xor(local_max, o, kWave));
-    if (lane == 0) red[wave] = local_max;
-    __syncthreads();
-    double m = red[0];
+    m = red[0];
     for (int w = 1; w < kThreads / kWave; ++w) m = fmax(m, red[w]);
-    for (int k = threadIdx.x; k < K; k += kThreads) c_out[size_t(h) * K + k] = cd[k] - m;
+    for (int k = threadIdx.x; k < K; k += kThreads) ch[k] -= m;
 }
 
 // Responsibilities of rows [n0, n0 + rows) of one problem into LDS g[T][K]; xs is LDS
@@ -197,11 +199,16 @@ __global__ void __launch_bounds__(kThreads) f32_prefix_kernel(float* __restrict_
     }
 }
 
-// The score tables of every head (f32_params_kernel) into the workspace, one launch.
+// The score tables of every head (f32_params_kernel, then the shift of c) into the workspace.
 inline hipError_t launch_param_tables(const Plan& p, const float* s2, const float* pi, char* ws, hipStream_t st) {
     F32Params v = f32_params_view(p, ws);
-    GMA_LAUNCH("f32_params", f32_params_kernel, dim3(unsigned(p.H)), dim3(kThreads), 0, st, s2, pi, int(p.K),
-               int(p.dr), const_cast<double*>(v.c), const_cast<double*>(v.inv));
+    GMA_LAUNCH("f32_params", f32_params_kernel,
+               dim3(unsigned(p.H), unsigned((p.K + kThreads / kWave - 1) / (kThreads / kWave))), dim3(kThreads), 0, st,
+               s2, pi, int(p.K), int(p.dr), const_cast<double*>(v.c), const_cast<double*>(v.inv));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    GMA_LAUNCH("f32_params_shift", f32_params_shift_kernel, dim3(unsigned(p.H)), dim3(kThreads), 0, st, int(p.K),
+               const_cast<double*>(v.c));
     return hipGetLastError();
 }
 
