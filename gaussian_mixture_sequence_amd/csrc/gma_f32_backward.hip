@@ -1032,23 +1032,64 @@ int kb_blocks(int64_t K) { return int((K + kKB - 1) / kKB); }
 // blocks (row maximum and sum over the lanes of the row group).  Into S ([64][LK], zero past
 // `rows` and K) and the cache rows gc ([.][K] of this problem).  LDS: xT [dr][kLDT], muT and ivT
 // [dr][kLB], cB [kKB].
+// One component block's score tables (mu and 1 / sigma2 of components k0 .. k0 + 63, d_r <= 64)
+// on their way from the head's rows to LDS ([dr][kLB], transposed): each thread issues all its
+// 16-byte loads before any is needed, so the loads of the next block can be in flight while the
+// current block is scored.
+template <int NTH>
+struct KbTables {
+    static constexpr int PER = kKB * 64 / 4 / NTH;  // 4-element groups per thread at d_r = 64
+    float4 m[PER];
+    double2 v[PER][2];
+    __device__ __forceinline__ void load(const float* __restrict__ mh, const double* __restrict__ ih, int K, int dr,
+                                         int k0) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = 4 * (int(threadIdx.x) + u * NTH), kl = e / dr, d = e - kl * dr, k = k0 + kl;
+            if (e < kKB * dr && k < K) {
+                m[u] = *reinterpret_cast<const float4*>(mh + size_t(k) * dr + d);
+                v[u][0] = *reinterpret_cast<const double2*>(ih + size_t(k) * dr + d);
+                v[u][1] = *reinterpret_cast<const double2*>(ih + size_t(k) * dr + d + 2);
+            } else {
+                m[u] = make_float4(0, 0, 0, 0);
+                v[u][0] = v[u][1] = make_double2(0, 0);
+            }
+        }
+    }
+    __device__ __forceinline__ void store(float* muT, float* ivT, int dr) const {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = 4 * (int(threadIdx.x) + u * NTH), kl = e / dr, d = e - kl * dr;
+            if (e < kKB * dr) {
+                muT[(d + 0) * kLB + kl] = m[u].x;
+                muT[(d + 1) * kLB + kl] = m[u].y;
+                muT[(d + 2) * kLB + kl] = m[u].z;
+                muT[(d + 3) * kLB + kl] = m[u].w;
+                ivT[(d + 0) * kLB + kl] = float(v[u][0].x);
+                ivT[(d + 1) * kLB + kl] = float(v[u][0].y);
+                ivT[(d + 2) * kLB + kl] = float(v[u][1].x);
+                ivT[(d + 3) * kLB + kl] = float(v[u][1].y);
+            }
+        }
+    }
+};
+
 template <int KB, int TW>
 __device__ void kb_gamma(const float* Xp, int64_t n0, int rows, int dr, int K, const double* ch, const double* ih,
                          const float* mh, float* xT, float* muT, float* ivT, float* cB, float* S, int LK, float* gc) {
     constexpr int NTH = 1024 / TW, CG = 64 / TW;
     const int tid = threadIdx.x, r0 = (tid / CG) * 4, m0 = (tid % CG) * TW;
+    KbTables<NTH> tb;
+    tb.load(mh, ih, K, dr, 0);
     load_xT<NTH>(Xp, n0, rows, dr, xT);
     float mrow[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
         __syncthreads();  // the previous block's tables are consumed (and xT is in place)
-        for (int i = tid; i < kKB * dr; i += NTH) {
-            const int kl = i / dr, d = i - kl * dr, k = kb * kKB + kl;
-            muT[d * kLB + kl] = k < K ? mh[size_t(k) * dr + d] : 0.0f;
-            ivT[d * kLB + kl] = k < K ? float(ih[size_t(k) * dr + d]) : 0.0f;
-        }
+        tb.store(muT, ivT, dr);
         for (int kl = tid; kl < kKB; kl += NTH) cB[kl] = kb * kKB + kl < K ? float(ch[kb * kKB + kl]) : -INFINITY;
         __syncthreads();
+        if (kb + 1 < KB) tb.load(mh, ih, K, dr, (kb + 1) * kKB);  // in flight while this block is scored
         float q[4][TW] = {};
 #pragma unroll 4
         for (int d = 0; d < dr; ++d) {
