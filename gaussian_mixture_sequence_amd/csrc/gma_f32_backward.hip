@@ -1074,6 +1074,34 @@ struct KbTables {
     }
 };
 
+// One component block of a memory [Vt (K x dv) | Z (K)] (rows k0 .. k0 + 63, dv <= 64) on its way
+// to LDS (Mb [64][dv + 4], Zb [64]), loaded ahead of its use as KbTables.
+template <int NTH>
+struct KbMemBlock {
+    static constexpr int PER = kKB * 64 / 4 / NTH;  // 4-element groups per thread at dv = 64
+    float4 m[PER];
+    float z;
+    __device__ __forceinline__ void load(const float* __restrict__ mp, int K, int dv, int k0) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = 4 * (int(threadIdx.x) + u * NTH), kl = e / dv, cc = e - kl * dv, k = k0 + kl;
+            m[u] = (e < kKB * dv && k < K) ? *reinterpret_cast<const float4*>(mp + size_t(k) * dv + cc)
+                                           : make_float4(0, 0, 0, 0);
+        }
+        const int k = k0 + int(threadIdx.x);
+        z = (threadIdx.x < kKB && k < K) ? mp[size_t(K) * dv + k] : 0.0f;
+    }
+    __device__ __forceinline__ void store(float* Mb, float* Zb, int dv) const {
+        const int LY = dv + 4;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = 4 * (int(threadIdx.x) + u * NTH), kl = e / dv, cc = e - kl * dv;
+            if (e < kKB * dv) *reinterpret_cast<float4*>(Mb + kl * LY + cc) = m[u];
+        }
+        if (threadIdx.x < kKB) Zb[threadIdx.x] = z;
+    }
+};
+
 template <int KB, int TW>
 __device__ void kb_gamma(const float* Xp, int64_t n0, int rows, int dr, int K, const double* ch, const double* ih,
                          const float* mh, float* xT, float* muT, float* ivT, float* cB, float* S, int LK, float* gc) {
@@ -1231,6 +1259,8 @@ __global__ void __launch_bounds__(1024 / TW)
                     t < rows ? *reinterpret_cast<const float4*>(Yp + (n0 + t) * dv + cc) : make_float4(0, 0, 0, 0);
                 *reinterpret_cast<float4*>(Yr + t * LY + cc) = v;
             }
+        KbMemBlock<NTH> mb;  // query: the memory's first block, in flight while the tile is scored
+        if (QUERY) mb.load(mem + size_t(p) * K * (dv + 1), K, dv, 0);
         kb_gamma<KB, TW>(Xp, n0, rows, dr, K, ch, ih, mh, xT, muT, ivT, cB, S, LK, gc);
         if (MODE == KB_GAMMA) continue;
         if (!QUERY) {
@@ -1257,13 +1287,9 @@ __global__ void __launch_bounds__(1024 / TW)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             __syncthreads();  // the previous block of the memory is consumed
-            for (int i = tid; i < kKB * (dv / 4); i += NTH) {
-                const int kl = i / (dv / 4), cc = (i - kl * (dv / 4)) * 4, k = kb * kKB + kl;
-                *reinterpret_cast<float4*>(Mb + kl * LY + cc) =
-                    k < K ? *reinterpret_cast<const float4*>(mp + size_t(k) * dv + cc) : make_float4(0, 0, 0, 0);
-            }
-            for (int kl = tid; kl < kKB; kl += NTH) Zb[kl] = kb * kKB + kl < K ? mp[size_t(K) * dv + kb * kKB + kl] : 0.0f;
+            mb.store(Mb, Zb, dv);
             __syncthreads();
+            if (kb + 1 < KB) mb.load(mp, K, dv, (kb + 1) * kKB);  // in flight during this block's products
 #pragma unroll 4
             for (int kl = 0; kl < kKB; ++kl) {
                 float ga[4], va[TW];
