@@ -102,6 +102,9 @@ CASES = [
     # K-blocked passes: a ragged last block and tail, several splits, small dims
     case(1500, 97, B=2, H=2, d_r=32, d_v=48, K=200),
     case(6000, 98, B=1, H=3, d_r=16, d_v=16, K=100, mu_std=1.5),
+    # K-blocked passes with K not a multiple of 4 (per-element responsibility loads; the memory
+    # rows of every problem after the first start off a 16-byte boundary), ragged tail
+    case(900, 99, B=2, H=2, d_r=32, d_v=16, K=66),
 ]
 
 
@@ -323,6 +326,7 @@ CROSS_CASES = [
     cross_case(130, 450, 135, B=1, H=1, d_r=128, d_v=128, K=256),
     cross_case(700, 1900, 140, d_r=64, d_v=64, K=128),          # K-blocked passes, longer context
     cross_case(2100, 300, 141, d_r=32, d_v=32, K=192),          # K-blocked passes, more queries
+    cross_case(500, 800, 148, d_r=16, d_v=32, K=130),           # K-blocked, K not a multiple of 4
     cross_case(300, 0, 136),                                     # empty context
     cross_case(0, 300, 137),                                     # no queries
     cross_case(300, 0, 142, d_r=32, d_v=32, K=128),              # empty context, K-blocked passes
