@@ -282,6 +282,19 @@ def test_backward_causal_full_size_sampled_heads():
     full_size_check(w, got, inp, d_o, (0, 11), causal=True)
 
 
+@pytest.mark.parametrize("name,head", [("bwd_b8h8_n1024_k256_f32", 3), ("bwdc_b8h8_n1024_k256_f32", 6)],
+                         ids=["bidir", "causal"])
+def test_backward_kblocked_full_size_sampled_head(name, head):
+    """B=8, H=8, N=1024, d_r=d_v=64 with K=256 components (the language-model setting of the
+    paper's experiments), fp32, in the split plan the bench times (the K-blocked passes): every
+    gradient of one head, all eight sequences, against the oracle."""
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    d_o = upstream(w, 2003)
+    got = (run_gpu_causal if w.causal else run_gpu)(w, inp, d_o)
+    full_size_check(w, got, inp, d_o, (head,), causal=w.causal)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("dims", [(700, 16, 32, 8), (700, 7, 5, 13), (300, 32, 64, 64)],
                          ids=lambda d: "N%d-dr%d-dv%d-K%d" % d)
