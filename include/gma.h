@@ -284,7 +284,10 @@ gma_status_t gma_responsibility_diagnostics(const void* X, gma_dtype_t x_dtype, 
  * Workspace: gma_workspace_size(GMA_OP_BACKWARD_BIDIR, shape, io_dtype, 0, ...): the forward's
  * memory and its split partials, the same for (dVt, dZ), and per-split parameter partials,
  * reduced in a fixed order (bitwise reproducible); for K, d_r, d_v <= 64 (multiples of 4) the
- * responsibilities of the keys, which the key pass reads back (B H N K fp32); with bf16 I/O also
+ * responsibilities of the keys, which the key pass reads back (B H N K fp32); for 64 < K <= 256
+ * with d_r, d_v <= 64 (multiples of 4) the responsibilities of both sides (2 B H N K fp32), three
+ * fp32 values per row and the component blocks' shares of dX (ceil(K / 64) B H N d_r fp32); with
+ * bf16 I/O also
  * fp32 copies of the four inputs and three outputs (O(B H N (d_r + d_v)) bytes).  Sizes as for
  * the fp32 forward (d_r, d_v <= 128, K <= 256 at either I/O dtype); alignment and errors as for
  * gma_forward_bidir; with no rows (B N = 0) the parameter gradients are zeros.
@@ -308,7 +311,11 @@ gma_status_t gma_backward_bidir(const void* XQ, const void* XK, const void* V, g
  * gma_backward_bidir.  Shapes, dtypes, outputs, workspace
  * (gma_workspace_size(GMA_OP_BACKWARD_CAUSAL, shape, io_dtype, 0, ...), which also holds D_i and
  * a_i of every position and, where the register-tiled passes apply, the responsibilities of both
- * sides, 2 B H N K fp32) and errors as for gma_backward_bidir.
+ * sides, 2 B H N K fp32; where the K-blocked causal passes apply (K <= 256, d_r, d_v <= 64, not
+ * within the register-tiled passes' LDS), the same, the memory before and what the later
+ * positions send for every tile of 64 positions (2 B H ceil(N / 64) K (d_v + 1) fp32), the
+ * in-tile products (B H ceil(N / 64) 64 64 fp32), three fp32 values per row and the component
+ * blocks' shares of dX (ceil(K / 64) B H N d_r fp32)) and errors as for gma_backward_bidir.
  */
 gma_status_t gma_backward_causal(const void* XQ, const void* XK, const void* V, gma_dtype_t io_dtype,
                                  const float* mu, const float* sigma2, const float* pi, float eps,
