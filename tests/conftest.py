@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests are only meaningful where a GPU is visible; elsewhere they are skipped
-    # (the driver selects them explicitly with -m gpu on a GPU machine).
+    # (on a GPU machine they are selected with -m gpu).
     try:
         import torch
         has_gpu = torch.cuda.is_available()
