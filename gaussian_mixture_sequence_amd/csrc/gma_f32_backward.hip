@@ -2017,9 +2017,21 @@ __global__ void __launch_bounds__(kThreads)
             const int k0 = kb * kKB;
             __syncthreads();  // the previous block is consumed
             load_gamma_block(gqp, n0, rows, K, k0, Gq);
-            for (int i = tid; i < kBT * kKB; i += kThreads) {  // gamma^K rows j, transposed
-                const int t = i / kKB, kl = i - t * kKB;
-                GkT[kl * kLB + t] = (t < rows && k0 + kl < K) ? gkp[(n0 + t) * K + k0 + kl] : 0.0f;
+            if ((K & 3) == 0) {  // gamma^K rows j, transposed; 16-byte rows
+                for (int i = tid; i < kBT * (kKB / 4); i += kThreads) {
+                    const int t = i / (kKB / 4), kq = (i - t * (kKB / 4)) * 4;
+                    const float4 v = (t < rows && k0 + kq < K) ? *reinterpret_cast<const float4*>(gkp + (n0 + t) * K + k0 + kq)
+                                                             : make_float4(0, 0, 0, 0);
+                    GkT[(kq + 0) * kLB + t] = v.x;
+                    GkT[(kq + 1) * kLB + t] = v.y;
+                    GkT[(kq + 2) * kLB + t] = v.z;
+                    GkT[(kq + 3) * kLB + t] = v.w;
+                }
+            } else {
+                for (int i = tid; i < kBT * kKB; i += kThreads) {
+                    const int t = i / kKB, kl = i - t * kKB;
+                    GkT[kl * kLB + t] = (t < rows && k0 + kl < K) ? gkp[(n0 + t) * K + k0 + kl] : 0.0f;
+                }
             }
             for (int i = tid; i < kKB * (dv / 4); i += kThreads) {
                 const int kl = i / (dv / 4), cc = (i - kl * (dv / 4)) * 4, k = k0 + kl;
