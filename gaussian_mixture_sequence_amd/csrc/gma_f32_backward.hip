@@ -1359,6 +1359,28 @@ __device__ __forceinline__ void load_gamma_block_n(const float* __restrict__ gc,
     }
 }
 
+// The block of a memory [Vt (K x dv) | ...] with rows k0 .. k0 + 63 into MT ([dv][kLB], transposed,
+// zero past K), by NTH threads: 16-byte row reads when the memory's rows start on 16-byte
+// boundaries (K a multiple of 4), else one element at a time.
+template <int NTH>
+__device__ __forceinline__ void load_mem_block_t(const float* __restrict__ mp, int K, int dv, int k0, float* MT) {
+    if ((K & 3) == 0) {
+        for (int i = threadIdx.x; i < kKB * (dv / 4); i += NTH) {
+            const int kl = i / (dv / 4), cc = (i - kl * (dv / 4)) * 4, k = k0 + kl;
+            const float4 v = k < K ? *reinterpret_cast<const float4*>(mp + size_t(k) * dv + cc) : make_float4(0, 0, 0, 0);
+            MT[(cc + 0) * kLB + kl] = v.x;
+            MT[(cc + 1) * kLB + kl] = v.y;
+            MT[(cc + 2) * kLB + kl] = v.z;
+            MT[(cc + 3) * kLB + kl] = v.w;
+        }
+    } else {
+        for (int i = threadIdx.x; i < kKB * dv; i += NTH) {
+            const int kl = i / dv, cc = i - kl * dv, k = k0 + kl;
+            MT[cc * kLB + kl] = k < K ? mp[size_t(k) * dv + cc] : 0.0f;
+        }
+    }
+}
+
 size_t kb_block_lds_bytes(int dr, int dv) {
     return size_t(2 * kBT * kLB + kBT * (dv + 4) + dv * kLB + kKB + 3 * kBT + kBT * (dr + 4) + 2 * kKB * (dr + 4)) *
            sizeof(float);
@@ -1405,10 +1427,7 @@ __global__ void __launch_bounds__(1024 / TW)
         muR[kl * LX + d] = k < K ? mh[size_t(k) * dr + d] : 0.0f;
         ivR[kl * LX + d] = k < K ? float(ih[size_t(k) * dr + d]) : 0.0f;
     }
-    for (int i = tid; i < kKB * dv; i += NTH) {
-        const int kl = i / dv, cc = i - kl * dv, k = k0 + kl;
-        MT[cc * kLB + kl] = k < K ? mp[size_t(k) * dv + cc] : 0.0f;
-    }
+    load_mem_block_t<NTH>(mp, K, dv, k0, MT);
     for (int kl = tid; kl < kKB; kl += NTH) Zb[kl] = k0 + kl < K ? mp[size_t(K) * dv + k0 + kl] : 0.0f;
     __syncthreads();
     // moment accumulators (rows d = r0.., columns k = m0..) with their mu; memory-gradient
@@ -2340,10 +2359,7 @@ __global__ void __launch_bounds__(1024 / TW)
             *reinterpret_cast<float4*>(Xr + t * LX + d) =
                 t < rows ? *reinterpret_cast<const float4*>(Xp + (n0 + t) * dr + d) : make_float4(0, 0, 0, 0);
         }
-        for (int i = tid; i < kKB * dv; i += NTH) {
-            const int kl = i / dv, cc = i - kl * dv, k = k0 + kl;
-            MT[cc * kLB + kl] = k < K ? mp[size_t(k) * dv + cc] : 0.0f;
-        }
+        load_mem_block_t<NTH>(mp, K, dv, k0, MT);
         for (int kl = tid; kl < kKB; kl += NTH) Zb[kl] = k0 + kl < K ? mp[size_t(K) * dv + k0 + kl] : 0.0f;
         __syncthreads();  // Dv before the scaled rows
         for (int i = tid; i < kBT * (dv / 4); i += NTH) {
