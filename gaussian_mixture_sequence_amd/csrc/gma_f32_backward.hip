@@ -466,25 +466,51 @@ __global__ void __launch_bounds__(1024 / TW)
     float* Cm = Rw + kBT * LV4;                    // causal: query: C^T, then A^T; key: C ([i][j], stride kLDT)
     float* Am = Cm + kBT * kLDT;                   // causal key: A ([i][j], stride kLDT)
 
-    {   // per-head tables and (query, key) the problem's memory
+    {   // per-head tables and (query, key) the problem's memory: each thread's 16-byte loads are
+        // issued together, then stored (K, d_r, d_v <= 64 and multiples of 4, so every 4-element
+        // group lies in one row and starts on a 16-byte boundary)
+        constexpr int PER = 64 * 64 / 4 / NTH;  // 4-element groups per thread at K = d = 64
         const double *ch = c + size_t(h) * K, *ih = inv + size_t(h) * K * dr;
         const float* mh = mu + size_t(h) * K * dr;
-        for (int i = tid; i < K * dr; i += NTH) {
-            const int k = i / dr, d = i - k * dr;
-            muT[d * LDK + k] = mh[i];
-            ivT[d * LDK + k] = float(ih[i]);
+        const float* src = QK ? mem + (CAUSAL ? size_t(p) * G + gi : size_t(p)) * K * (dv + 1) : nullptr;
+        float4 tm[PER], tmem[PER];
+        double2 tv[PER][2];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = 4 * (tid + u * NTH);
+            if (e < K * dr) {
+                tm[u] = *reinterpret_cast<const float4*>(mh + e);
+                tv[u][0] = *reinterpret_cast<const double2*>(ih + e);
+                tv[u][1] = *reinterpret_cast<const double2*>(ih + e + 2);
+            }
+            if (QK && e < K * dv) tmem[u] = *reinterpret_cast<const float4*>(src + e);
+        }
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = 4 * (tid + u * NTH);
+            if (e < K * dr) {
+                const int k = e / dr, d = e - k * dr;
+                muT[(d + 0) * LDK + k] = tm[u].x;
+                muT[(d + 1) * LDK + k] = tm[u].y;
+                muT[(d + 2) * LDK + k] = tm[u].z;
+                muT[(d + 3) * LDK + k] = tm[u].w;
+                ivT[(d + 0) * LDK + k] = float(tv[u][0].x);
+                ivT[(d + 1) * LDK + k] = float(tv[u][0].y);
+                ivT[(d + 2) * LDK + k] = float(tv[u][1].x);
+                ivT[(d + 3) * LDK + k] = float(tv[u][1].y);
+            }
+            if (QK && e < K * dv) {
+                const int k = e / dv, cc = e - k * dv;
+                *reinterpret_cast<float4*>(M + e) = tmem[u];
+                MT[(cc + 0) * K + k] = tmem[u].x;
+                MT[(cc + 1) * K + k] = tmem[u].y;
+                MT[(cc + 2) * K + k] = tmem[u].z;
+                MT[(cc + 3) * K + k] = tmem[u].w;
+            }
         }
         for (int k = tid; k < K; k += NTH) cK[k] = float(ch[k]);
-        if (QK) {
-            const float* src = mem + (CAUSAL ? size_t(p) * G + gi : size_t(p)) * K * (dv + 1);
-            for (int i = tid; i < K * dv; i += NTH) {
-                const int k = i / dv, cc = i - k * dv;
-                const float v = src[i];
-                M[i] = v;
-                MT[cc * K + k] = v;
-            }
+        if (QK)
             for (int k = tid; k < K; k += NTH) Zm[k] = src[K * dv + k];
-        }
     }
     __syncthreads();
     // moment accumulators (rows d = r0 + i, columns k = m0 + j) and their mu
