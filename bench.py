@@ -354,6 +354,8 @@ def alg_bytes_per_token_head(w, kernel: str) -> float:
         return e * (2 * w.d_r + 2 * w.d_v) + 2 * 4 * w.K * (w.d_v + 1)
     if w.diagnostics:  # the routing vectors in; the outputs (per token, not per head) are negligible
         return e * w.d_r
+    if w.responsibilities:  # the routing vectors in, Gamma out, both in the I/O dtype
+        return e * (w.d_r + w.K)
     if w.backward:  # the register-tiled passes keep the responsibilities (fp32, K per row) between passes
         g = 4 * w.K
         T = 64  # positions per tile of the causal K-blocked passes (C: T fp32 per row)
@@ -455,6 +457,8 @@ def alg_mfma_flops_per_token_head(w, kernel: str) -> float:
     if w.backward or w.diagnostics or w.dtype != "bf16":
         return 0.0
     K, dr, dv = w.K, w.d_r, w.d_v
+    if w.responsibilities:  # one side's score contraction
+        return 4 * K * dr if kernel.endswith("_resp") else 0.0
     full = 8 * K * dr + 4 * K * (dv + 1)
     if kernel.endswith("_write") or kernel.endswith("_causal_aggregate"):
         return 4 * K * dr + 2 * K * (dv + 1)
@@ -544,6 +548,10 @@ def cpu_baseline(ws_list) -> dict:
         if w.diagnostics:
             t0 = time.perf_counter()
             oracle.diagnostics.diagnostics(sl["xq"], sl["mu"], sl["sigma2"], sl["pi"])
+            return time.perf_counter() - t0
+        if w.responsibilities:
+            t0 = time.perf_counter()
+            oracle.responsibilities(sl["xq"], sl["mu"], sl["sigma2"], sl["pi"])
             return time.perf_counter() - t0
         fn = oracle.forward_causal if w.causal else oracle.forward_cross if w.cross else oracle.forward_bidir
         t0 = time.perf_counter()
@@ -669,6 +677,8 @@ def main(args=None, probe_only=False) -> int:
                           "dV": torch.empty_like(d0["v"]), "dmu": torch.empty_like(d0["mu"]),
                           "dsigma2": torch.empty_like(d0["sigma2"]), "dpi": torch.empty_like(d0["pi"])}
                          for _ in range(args.sets)])
+        elif w.responsibilities:
+            outs.append([torch.empty(w.B, w.H, w.N, w.K, dtype=dt, device=dev) for _ in range(args.sets)])
         else:
             outs.append([torch.empty(w.B, w.H, 1 if w.decode else w.N, w.d_v, dtype=dt, device=dev)
                          for _ in range(args.sets)])
@@ -678,6 +688,8 @@ def main(args=None, probe_only=False) -> int:
             nbytes = gb.gma_cross_workspace_size(w.B, w.H, w.N, w.n_ctx, w.d_r, w.d_v, w.K, io)
         elif w.diagnostics:
             nbytes = gb.gma_workspace_size(gb.GMA_OP_DIAGNOSTICS, w.B, w.H, w.N, w.d_r, 0, w.K, io)
+        elif w.responsibilities:
+            nbytes = gb.gma_workspace_size(gb.GMA_OP_RESPONSIBILITIES, w.B, w.H, w.N, w.d_r, 1, w.K, io)
         elif w.backward:
             nbytes = gb.gma_workspace_size(gb.GMA_OP_BACKWARD_CAUSAL if w.causal else gb.GMA_OP_BACKWARD_BIDIR,
                                            w.B, w.H, w.N, w.d_r, w.d_v, w.K, io)
@@ -698,6 +710,9 @@ def main(args=None, probe_only=False) -> int:
             if w.diagnostics:
                 gb.gma_responsibility_diagnostics(d["xq"], d["mu"], d["sigma2"], d["pi"], workspace=wss[i],
                                                   stream=stream)
+            elif w.responsibilities:
+                gb.gma_responsibilities(d["xq"], d["mu"], d["sigma2"], d["pi"], out=outs[i][s], workspace=wss[i],
+                                        stream=stream)
             elif w.backward and w.causal:
                 gb.gma_backward_causal(d["xq"], d["xk"], d["v"], d["mu"], d["sigma2"], d["pi"], d["d_o"], w.eps,
                                        out=outs[i][s], workspace=wss[i], stream=stream)
@@ -811,7 +826,8 @@ def main(args=None, probe_only=False) -> int:
                 "X_Q,X_K,V~N(0,1); %d rotating input sets)" % args.sets,
         "config": {
             "workload": " + ".join("%s (%s B=%d H=%d %s d_r=%d d_v=%d K=%d%s)" % (
-                w.name, ("causal" if w.causal else "cross" if w.cross else "bidir") + (" backward" if w.backward else ""),
+                w.name, ("responsibilities" if w.responsibilities else "diagnostics" if w.diagnostics else
+                         "causal" if w.causal else "cross" if w.cross else "bidir") + (" backward" if w.backward else ""),
                 w.B, w.H,
                 "N_q=%d N_k=%d" % (w.N, w.n_ctx) if w.cross else "N=%d" % w.N, w.d_r, w.d_v, w.K,
                 ", chunk=%d" % w.chunk if w.causal and not w.backward else "") for w in ws_list),

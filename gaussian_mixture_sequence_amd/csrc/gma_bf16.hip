@@ -63,12 +63,21 @@ __global__ void __launch_bounds__((Split<DR, KT>::NW * 64)) resp_kernel(const ui
     }
     const uint16_t* Xp = X + size_t(p) * N * DR;
     const bool vec = (K & 3) == 0;  // whole groups of 4 components: 16- or 8-byte stores
+    // the wave's x fragments are loaded one round ahead of their scores
+    auto first_row = [&](int r) { return (int64_t(blockIdx.x) * RPW + r) * S::ROUND + ts * 32; };
+    auto rows_of = [&](int64_t n0) { return int(max<int64_t>(0, min<int64_t>(32, N - n0))); };
+    bf16x8 xs[DR / 16];
+    load_x<DR>(Xp, first_row(0), rows_of(first_row(0)), xs);
     for (int r = 0; r < RPW; ++r) {
-        const int64_t n0 = (int64_t(blockIdx.x) * RPW + r) * S::ROUND + ts * 32;
+        const int64_t n0 = first_row(r);
         if (n0 - ts * 32 >= N) break;  // uniform over the workgroup
-        const int valid = int(max<int64_t>(0, min<int64_t>(32, N - n0)));
+        const int valid = rows_of(n0);
+        bf16x8 xn[DR / 16];
+        load_x<DR>(Xp, first_row(r + 1), r + 1 < RPW ? rows_of(first_row(r + 1)) : 0, xn);
         f32x16 acc[S::CTW];
-        scores<DR, S::CTW>(P, Xp, n0, valid, acc);
+        scores_x<DR, S::CTW>(P, xs, acc);
+#pragma unroll
+        for (int ks = 0; ks < DR / 16; ++ks) xs[ks] = xn[ks];
         float m, L, D;
         float zr[S::CTW][16];
         local_softmax<S::CTW, false>(acc, zr, m, L, D);
@@ -555,9 +564,10 @@ hipError_t bf16_responsibilities(const Plan& p, const void* X, const float* mu, 
     return bf::with_dr_kt(int(p.dr), kt_of(p), [&](auto D, auto T) {
         constexpr int DR = decltype(D)::value, KT = decltype(T)::value;
         using S = bf::Split<DR, KT>;
-        // rounds per workgroup: about 2048 workgroups in all (several waves of them on 256 CUs)
+        // rounds per workgroup: about 512 workgroups in all, so each one's operand build serves
+        // several rounds (measured: 2048 workgroups of two rounds took 13% longer at B8 H8 N4096)
         const int64_t rounds = (p.N + S::ROUND - 1) / S::ROUND;
-        const int64_t rpw = std::max<int64_t>(1, (p.P * rounds + 2047) / 2048);
+        const int64_t rpw = std::max<int64_t>(1, (p.P * rounds + 511) / 512);
         dim3 grid(unsigned((rounds + rpw - 1) / rpw), unsigned(p.P));
         GMA_LAUNCH("bf16_resp", (bf::resp_kernel<DR, KT>), grid, dim3(S::NW * 64), 0, st,
                            static_cast<const uint16_t*>(X), p.N, int(p.H), int(rpw), mx, Gamma,

@@ -44,6 +44,7 @@ class Workload:
     decode: bool = False  # causal decoding: one position per call, carrying the memory between calls
     diagnostics: bool = False  # responsibility diagnostics of X_Q (Sec. 5.4); V and X_K unused
     backward: bool = False  # backward pass of the bidirectional forward for a seeded upstream gradient dO
+    responsibilities: bool = False  # Gamma of X_Q alone (Eq. 3), written out in the I/O dtype; V, X_K unused
 
     @property
     def tokens(self) -> int:
@@ -107,6 +108,10 @@ WORKLOADS: Dict[str, Workload] = {
                                          seed=15, backward=True),
     "cross_b8h8_q4096_k16384": Workload("cross_b8h8_q4096_k16384", False, 8, 8, 4096, 64, 64, 64, "bf16",
                                         seed=5, n_ctx=16384),
+    # the responsibilities alone (gma_responsibilities) at the B=8, H=8, N=4096, d_r=64, K=64
+    # bidirectional dims, bf16 routing vectors in and bf16 Gamma out
+    "resp_b8h8_n4096": Workload("resp_b8h8_n4096", False, 8, 8, 4096, 64, 64, 64, "bf16", seed=16,
+                                responsibilities=True),
 }
 WORKLOAD_ORDER = ["bidir_small_f32", "bidir_b8h8_n4096", "causal_b8h12_n2048",
                   "bidir_long_n65536", "causal_long_n32768"]
