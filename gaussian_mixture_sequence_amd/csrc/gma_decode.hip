@@ -93,7 +93,19 @@ __global__ void __launch_bounds__(kDecodeThreads)
         if (t < dv) rvv = load_io(V, (size_t(p) * N + i) * dv + t);
     };
     fetch(0);
-    for (int e = t; e < E; e += blockDim.x) mem[e] = state_in ? state_in[size_t(p) * E + e] : 0.0f;
+    // the carried memory: 16-byte pieces, eight of a thread's loads in flight before the first is
+    // stored, where the problem's memory starts on a 16-byte boundary (E a multiple of 4)
+    const bool vec = (E & 3) == 0;
+    if (!state_in) {
+        for (int e = t; e < E; e += kDecodeThreads) mem[e] = 0.0f;
+    } else if (vec) {
+        const float4* sp = reinterpret_cast<const float4*>(state_in + size_t(p) * E);
+#pragma unroll 8
+        for (int e4 = t; e4 < E / 4; e4 += kDecodeThreads) reinterpret_cast<float4*>(mem)[e4] = sp[e4];
+    } else {
+#pragma unroll 8
+        for (int e = t; e < E; e += kDecodeThreads) mem[e] = state_in[size_t(p) * E + e];
+    }
 
     // component k = t / TPC; its lane j = t % TPC takes dims j, j + TPC, ... (the first MAXD of
     // them kept in registers)
@@ -230,8 +242,14 @@ __global__ void __launch_bounds__(kDecodeThreads)
         if (t < dv) store_io(O, rv + t, num / den[0]);  // rv: this position's output row
     }
     __syncthreads();
-    if (state_out)
-        for (int e = t; e < E; e += blockDim.x) state_out[size_t(p) * E + e] = mem[e];
+    if (state_out) {
+        if (vec) {
+            float4* sp = reinterpret_cast<float4*>(state_out + size_t(p) * E);
+            for (int e4 = t; e4 < E / 4; e4 += kDecodeThreads) sp[e4] = reinterpret_cast<const float4*>(mem)[e4];
+        } else {
+            for (int e = t; e < E; e += kDecodeThreads) state_out[size_t(p) * E + e] = mem[e];
+        }
+    }
 }
 
 size_t decode_lds_bytes(const Plan& p) {
